@@ -1,0 +1,227 @@
+"""CPU oracle for the log-linear (Fenwick-tree) token mixer, in fp64.
+
+TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the
+CPU-baseline leg of the benchmark may import this module; the product path
+never does, and this module imports nothing from the product package.
+
+Two independent forms of the same output are provided:
+
+* Form A -- the materialised mask.  "Log-linear attention, and what a logarithm
+  buys", section 1 writes every variant as P = A (.) M, O = P V with A = Q K^T;
+  section 2 gives the Fenwick buckets (greedily take the largest power of two
+  that fits in what remains; bucket l >= 1 holds 2^(l-1) tokens, plus a
+  size-one sentinel) and the per-level weights lambda_t^(l); section 3 composes
+  the Mamba-2 scalar-decay mask with the level mask by an elementwise product.
+  So M[t, s] = lambda_t^(level(t, s)) * exp(A_t - A_s) for s <= t, where
+  A_t = a_0 + ... + a_t, and the level of s comes from enumerating the buckets
+  greedily (not from a closed-form bit formula).
+* Form B -- the token-by-token Fenwick recurrence of section 2, in C
+  (loglin_oracle.c), which also serves decode.
+
+Readings of points the page leaves open (positions 0-indexed, oldest tokens in
+the largest bucket, lambda indexed by the query, the decay convention) are
+listed with the reasons in the design notes at the repository root.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "loglin_oracle.c")
+_LIB = os.path.join(_HERE, "liblloracle.so")
+
+LLO_OK, LLO_EARG, LLO_ECAP, LLO_ELIVE, LLO_ENOMEM = 0, 1, 2, 3, 4
+
+
+def build(force: bool = False) -> str:
+    """Compile the C part of the oracle with gcc (plain -O2, no tuning)."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp"
+        subprocess.check_call(
+            ["gcc", "-O2", "-std=c99", "-shared", "-fPIC", _SRC, "-o", tmp, "-lm", "-lpthread"]
+        )
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+_lib = None
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        _lib = ctypes.CDLL(build())
+        dp = ctypes.POINTER(ctypes.c_double)
+        ip = ctypes.POINTER(ctypes.c_int64)
+        _lib.llo_fwd_recurrent.argtypes = [dp, dp, dp, dp, dp, dp, dp, ctypes.c_long, ctypes.c_long,
+                                           ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        _lib.llo_fwd_recurrent.restype = ctypes.c_int
+        _lib.llo_decode.argtypes = [dp, ip, dp, dp, dp, dp, dp, dp, ctypes.c_long, ctypes.c_int,
+                                    ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
+        _lib.llo_decode.restype = ctypes.c_int
+    return _lib
+
+
+def _f64(x) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(x, dtype=np.float64))
+
+
+def _ptr(x: np.ndarray, ctype=ctypes.c_double):
+    return x.ctypes.data_as(ctypes.POINTER(ctype))
+
+
+def default_threads() -> int:
+    return max(1, len(os.sched_getaffinity(0)))
+
+
+# --------------------------------------------------------------------------
+# Fenwick buckets by greedy enumeration (section 2)
+
+def fenwick_buckets(t: int):
+    """Buckets of the prefix seen by the query at 0-indexed position t.
+
+    Returns a list of (level, start, stop) half-open token ranges.  The t
+    earlier tokens 0..t-1 are cut greedily: take the largest power of two 2^p
+    that fits in what remains, oldest tokens first; that bucket gets level
+    p + 1 and holds 2^p tokens.  Token t itself is the size-one sentinel at
+    level 0.
+    """
+    if t < 0:
+        raise ValueError("t must be >= 0")
+    out = []
+    rem, start = t, 0
+    while rem > 0:
+        p = 0
+        while (1 << (p + 1)) <= rem:
+            p += 1
+        out.append((p + 1, start, start + (1 << p)))
+        start += 1 << p
+        rem -= 1 << p
+    out.append((0, t, t + 1))
+    return out
+
+
+def level_row(t: int, length: int | None = None) -> np.ndarray:
+    """int8 row: level of key s for query t (s <= t), -1 for s > t."""
+    n = t + 1 if length is None else length
+    row = np.full(n, -1, dtype=np.int8)
+    for lev, a, b in fenwick_buckets(t):
+        row[a:min(b, n)] = lev
+    return row
+
+
+def level_map(T: int) -> np.ndarray:
+    """int8 [T, T] level map, -1 above the diagonal."""
+    m = np.full((T, T), -1, dtype=np.int8)
+    for t in range(T):
+        m[t, : t + 1] = level_row(t)
+    return m
+
+
+def bucket_bound(t: int) -> int:
+    """The page's bound on the number of buckets: ceil(log2 t + 1) + 1."""
+    return int(np.ceil(np.log2(float(t)) + 1.0)) + 1
+
+
+# --------------------------------------------------------------------------
+# Form A: materialised mask
+
+def form_a(q, k, v, a, lam) -> np.ndarray:
+    """O = ((Q K^T) (.) M) V with the mask written out, per (batch, head) slice.
+
+    q, k [..., T, dk]; v [..., T, dv]; a [..., T]; lam [..., T, L].
+    Leading dimensions are flattened into slices.  Meant for T up to a few
+    thousand (it allocates T x T per slice).
+    """
+    q, k, v, a, lam = map(_f64, (q, k, v, a, lam))
+    lead = q.shape[:-2]
+    T, dk = q.shape[-2:]
+    dv = v.shape[-1]
+    L = lam.shape[-1]
+    lev = level_map(T).astype(np.int64)
+    tri = lev >= 0
+    if T > 0 and lev.max() >= L:
+        raise ValueError(f"lambda has {L} levels; T={T} needs {lev.max() + 1}")
+    qf, kf, vf = q.reshape(-1, T, dk), k.reshape(-1, T, dk), v.reshape(-1, T, dv)
+    af, lf = a.reshape(-1, T), lam.reshape(-1, T, L)
+    out = np.zeros((qf.shape[0], T, dv))
+    rows = np.arange(T)[:, None]
+    for i in range(qf.shape[0]):
+        A = np.cumsum(af[i])
+        decay = np.where(tri, np.exp(np.where(tri, A[:, None] - A[None, :], 0.0)), 0.0)
+        lvl = np.where(tri, lf[i][rows, np.maximum(lev, 0)], 0.0)
+        M = decay * lvl
+        out[i] = ((qf[i] @ kf[i].T) * M) @ vf[i]
+    return out.reshape(*lead, T, dv)
+
+
+def form_a_rows(q, k, v, a, lam, rows) -> np.ndarray:
+    """Form A for selected query rows of one (batch, head) slice.
+
+    q, k [T, dk]; v [T, dv]; a [T]; lam [T, L]; rows: iterable of positions.
+    Returns [len(rows), dv].  Each row costs O(t (dk + dv)).
+    """
+    a = np.asarray(a, dtype=np.float64)
+    A = np.cumsum(a)
+    rows = [int(r) for r in rows]
+    out = np.zeros((len(rows), v.shape[-1]))
+    for n, t in enumerate(rows):
+        lev = level_row(t).astype(np.int64)
+        w = np.asarray(lam[t], dtype=np.float64)[lev] * np.exp(A[t] - A[: t + 1])
+        scores = np.asarray(k[: t + 1], dtype=np.float64) @ np.asarray(q[t], dtype=np.float64)
+        out[n] = (scores * w) @ np.asarray(v[: t + 1], dtype=np.float64)
+    return out
+
+
+# --------------------------------------------------------------------------
+# Form B: the Fenwick recurrence (C)
+
+def form_b(q, k, v, a, lam, nthreads: int | None = None, return_states: bool = False):
+    """Token-by-token Fenwick recurrence over whole sequences (fp64).
+
+    Shapes as in form_a.  With return_states, also returns the level states
+    after the last token, [..., L, dk, dv] (S = sum k v^T orientation).
+    """
+    q, k, v, a, lam = map(_f64, (q, k, v, a, lam))
+    lead = q.shape[:-2]
+    T, dk = q.shape[-2:]
+    dv = v.shape[-1]
+    L = lam.shape[-1]
+    BH = int(np.prod(lead)) if lead else 1
+    out = np.zeros((BH, T, dv))
+    st = np.zeros((BH, L, dk, dv)) if return_states else None
+    rc = _load().llo_fwd_recurrent(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(lam), _ptr(out),
+                                   _ptr(st) if st is not None else None, BH, T, dk, dv, L,
+                                   nthreads or default_threads())
+    if rc != LLO_OK:
+        raise RuntimeError(f"oracle recurrence failed with code {rc}")
+    out = out.reshape(*lead, T, dv)
+    if return_states:
+        return out, st.reshape(*lead, L, dk, dv)
+    return out
+
+
+def decode(states, pos, q, k, v, a, lam, nthreads: int | None = None):
+    """Continue P independent (sequence, head) pairs by `steps` tokens.
+
+    states [P, L, dk, dv]; pos [P] next positions; q, k [steps, P, dk];
+    v [steps, P, dv]; a [steps, P]; lam [steps, P, L].
+    Returns (out [steps, P, dv], states_after, pos_after).
+    """
+    st = _f64(states).copy()
+    ps = np.ascontiguousarray(np.asarray(pos, dtype=np.int64)).copy()
+    q, k, v, a, lam = map(_f64, (q, k, v, a, lam))
+    steps, P, dk = q.shape
+    dv = v.shape[-1]
+    L = st.shape[1]
+    out = np.zeros((steps, P, dv))
+    rc = _load().llo_decode(_ptr(st), _ptr(ps, ctypes.c_int64), _ptr(q), _ptr(k), _ptr(v),
+                            _ptr(a), _ptr(lam), _ptr(out), P, steps, dk, dv, L,
+                            nthreads or default_threads())
+    if rc != LLO_OK:
+        raise RuntimeError(f"oracle decode failed with code {rc}")
+    return out, st, ps
