@@ -1,0 +1,265 @@
+#!/usr/bin/env python3
+"""Benchmark of the log-linear (Fenwick) token mixer on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--no-cpu-baseline]
+
+A step is one chunked forward over the fwd8k batch (B=4, H=16, T=8192,
+dk=128, dv=64, bf16 inputs, C=64, L=15) with inputs already resident in HBM;
+`value` is forward tokens/s (B*T tokens per step).  In the same run the
+Fenwick decode step is timed on the decode workload (128 sequences x 32
+heads, 17 levels of 128 x 128 fp32 states, 256 steps) and reported under
+"decode".  Each kernel is also timed alone with HIP events on the stream it
+is launched on; "roofline" is the one with the largest share of the step.
+The fp64 CPU oracle is timed on a bounded sample of the same workload
+("cpu_baseline").  Prints exactly one JSON line on stdout; progress goes to
+stderr.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+from log_linear_token_amd import inputs as I  # noqa: E402
+from log_linear_token_amd import loglin as LL  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
+BF16_PEAK_TFLOPS = 2500.0    # dense bf16 MFMA, TFLOP/s
+
+
+def log(msg: str) -> None:
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def timed(fn, reps: int, stream) -> float:
+    """Average milliseconds of fn() over reps launches, HIP events on `stream`."""
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(reps):
+        fn()
+    end.record(stream)
+    torch.cuda.synchronize()
+    return start.elapsed_time(end) / reps
+
+
+# --------------------------------------------------------------------- byte and flop models
+
+def fwd_models(cfg) -> dict:
+    """Algorithmic bytes / flops per launch of each forward kernel (bf16 inputs)."""
+    B, H, T, dk, dv, C, L = cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv, cfg.C, cfg.L
+    BH = B * H
+    N = -(-T // C)
+    st = dk * dv * 4                      # one fp32 state
+    qk = BH * T * dk * 2
+    vv = BH * T * dv * 2
+    a = BH * T * 4
+    lam = BH * T * L * 4
+    o = BH * T * dv * 4
+    nodes = BH * (N - 1) * st             # distinct Fenwick nodes ever read
+    nw = C // 16
+    tiles = nw * (nw + 1) // 2            # causal 16 x 16 tiles per chunk
+    intra_flops = BH * N * tiles * 2 * 16 * 16 * (dk + dv)
+    pops = sum(bin(i).count("1") for i in range(N))
+    inter_flops = BH * pops * 2 * C * dk * dv
+    state_flops = BH * N * 2 * C * dk * dv
+    return {
+        "chunk_state": {"bytes": qk + vv + a + BH * N * (st + 4), "flops": state_flops},
+        "fenwick_scan": {"bytes": BH * N * (st + 4) + nodes + BH * N * 8, "flops": 0},
+        "chunk_output": {"bytes": 2 * qk + vv + a + lam + nodes + BH * N * 8 + o,
+                         "flops": intra_flops + inter_flops},
+    }
+
+
+def decode_bytes(pos0: np.ndarray, H: int, dk: int, dv: int, Lmax: int, steps: int) -> float:
+    """Average algorithmic bytes per decode step: each (sequence, head) reads the
+    1 + popcount(t-1) live states of position t-1 and writes the 1 + popcount(t)
+    of position t (fp32 d_k x d_v each), plus q, k, v (bf16), a, lambda, out."""
+    st = dk * dv * 4
+    small = (2 * dk + dv) * 2 + 4 + Lmax * 4 + dv * 4
+    tot = 0.0
+    for s in range(steps):
+        t = pos0 + s
+        pc = np.array([bin(int(x)).count("1") for x in t])
+        pcm = np.array([bin(int(x) - 1).count("1") if x >= 1 else -1 for x in t])
+        tot += float(np.sum((1 + pcm) + (1 + pc))) * st * H + len(t) * H * small
+    return tot / steps
+
+
+# --------------------------------------------------------------------- CPU baseline
+
+def cpu_baseline(cfg, d) -> dict:
+    """The fp64 oracle recurrence on a bounded sample of the same workload."""
+    from oracle import reference as ref
+    threads = ref.default_threads()
+    nslices = max(1, min(threads, cfg.B * cfg.H))
+    idx = [(s // cfg.H, s % cfg.H) for s in range(nslices)]
+    pick = lambda x: np.stack([x[b, h] for b, h in idx])  # noqa: E731
+    q, k, v, a, lam = (pick(d[n]) for n in ("q", "k", "v", "a", "lam"))
+    log(f"cpu baseline: oracle recurrence on {nslices} of {cfg.B * cfg.H} (batch, head) slices, "
+        f"{threads} threads")
+    t0 = time.perf_counter()
+    ref.form_b(q, k, v, a, lam, nthreads=threads)
+    dt = time.perf_counter() - t0
+    # a token of the workload is one position of one sequence across all H heads
+    toks = nslices * cfg.T / cfg.H
+    return {"value": toks / dt, "unit": "tokens/s", "cores": min(threads, nslices),
+            "kind": "oracle",
+            "sample": f"fp64 Fenwick recurrence over {nslices} of the {cfg.B * cfg.H} "
+                      f"(batch, head) slices of fwd8k, all {cfg.T} positions each "
+                      f"({dt:.1f} s wall); tokens counted as slices*T/H",
+            "cpu_model": _cpu_model()}
+
+
+def _cpu_model() -> str:
+    try:
+        with open("/proc/cpuinfo") as f:
+            for ln in f:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+# --------------------------------------------------------------------- main
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=256)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-decode", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+              f"(asked for --gpus {args.gpus})", file=sys.stderr)
+        return 2
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 2
+
+    cfg = I.CONFIGS["fwd8k"]
+    log(f"generating fwd8k inputs (B={cfg.B} H={cfg.H} T={cfg.T} dk={cfg.dk} dv={cfg.dv})")
+    d = I.make_fwd(cfg, "base")
+    dev = lambda x, dt=torch.float32: torch.from_numpy(x).to("cuda").to(dt).contiguous()  # noqa
+    q, k, v = (dev(d[n], torch.bfloat16) for n in ("q", "k", "v"))
+    a, lam = dev(d["a"]), dev(d["lam"])
+    out = torch.empty((cfg.B, cfg.H, cfg.T, cfg.dv), device="cuda")
+    ws = torch.empty(LL.loglin_fwd_workspace_bytes(cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv, cfg.C),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def fwd(mask=LL.STAGE_ALL):
+        LL.loglin_fwd_chunked_stages(q, k, v, a, lam, cfg.C, mask, out=out, workspace=ws)
+
+    for _ in range(args.warmup):
+        fwd()
+    torch.cuda.synchronize()
+    log(f"timing {args.steps} forward steps")
+    t0 = time.perf_counter()
+    ms = timed(fwd, args.steps, stream)
+    wall = time.perf_counter() - t0
+    tokens = cfg.B * cfg.T
+    value = tokens / (ms / 1e3)
+    log(f"forward: {ms:.3f} ms/step ({value:.3e} tokens/s; wall {wall:.2f} s)")
+
+    # per-kernel timing, each launched alone on the same stream
+    models = fwd_models(cfg)
+    kernels = {}
+    for name, mask in (("chunk_state", LL.STAGE_CHUNK_STATE), ("fenwick_scan", LL.STAGE_SCAN),
+                       ("chunk_output", LL.STAGE_OUTPUT)):
+        fwd(mask)
+        kms = timed(lambda: fwd(mask), max(5, args.steps), stream)
+        m = models[name]
+        kernels[name] = {"ms": kms, "GB/s": m["bytes"] / (kms / 1e3) / 1e9,
+                         "TFLOP/s": m["flops"] / (kms / 1e3) / 1e12,
+                         "alg_bytes": m["bytes"], "alg_flops": m["flops"]}
+        log(f"  {name}: {kms:.3f} ms, {kernels[name]['GB/s']:.0f} GB/s, "
+            f"{kernels[name]['TFLOP/s']:.1f} TFLOP/s")
+    fwd()  # leave a complete output behind
+    dom = max(kernels, key=lambda n: kernels[n]["ms"])
+    km = kernels[dom]
+    roof = {"kernel": dom, "bound": "hbm", "achieved": round(km["GB/s"], 1),
+            "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(km["GB/s"] / HBM_PEAK_GBS, 4),
+            "traffic": None}
+
+    result = {
+        "metric": "fwd tokens/s + MFMA util, log-linear mixer T=8192; decode steps/s",
+        "value": value, "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": "fwd8k", "B": cfg.B, "H": cfg.H, "T": cfg.T, "dk": cfg.dk,
+                   "dv": cfg.dv, "C": cfg.C, "L": cfg.L, "parallelism": "none"},
+        "roofline": roof,
+        "kernels": {n: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
+                        for kk, vv in m.items()} for n, m in kernels.items()},
+        "mfma_util_chunk_output": round(kernels["chunk_output"]["TFLOP/s"] / BF16_PEAK_TFLOPS, 4),
+    }
+    del q, k, v, a, lam, out, ws
+    torch.cuda.empty_cache()
+
+    if not args.no_decode:
+        result["decode"] = bench_decode(args.decode_steps)
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(cfg, d)
+    print(json.dumps(result), flush=True)
+    return 0
+
+
+def bench_decode(steps: int) -> dict:
+    cfg = I.CONFIGS["decode"]
+    log(f"decode: {cfg.nseq} sequences x {cfg.H} heads, Lmax={cfg.Lmax}, {steps} steps")
+    d = I.make_decode(cfg.scaled(steps=steps), "base", fill=False)
+    pos = d["pos"]
+    # synthetic pre-filled states drawn on the device: N(0, 1/dk) in live slots, zero elsewhere
+    g = torch.Generator(device="cuda")
+    g.manual_seed(cfg.seed)
+    levels = torch.randn((cfg.nseq, cfg.H, cfg.Lmax, cfg.dk, cfg.dv), device="cuda",
+                         generator=g) * (1.0 / np.sqrt(cfg.dk))
+    live = np.zeros((cfg.nseq, cfg.Lmax), bool)
+    for s, n in enumerate(pos):
+        live[s, I.live_levels(int(n))] = True
+    levels *= torch.from_numpy(live).to("cuda")[:, None, :, None, None]
+    st = LL.loglin_state_init(cfg.nseq, cfg.H, cfg.dk, cfg.dv, cfg.Lmax)
+    LL.loglin_state_load(st, pos, levels)
+    del levels
+    q, k, v = (torch.from_numpy(d[n]).to("cuda").to(torch.bfloat16) for n in ("q", "k", "v"))
+    a, lam = torch.from_numpy(d["a"]).to("cuda"), torch.from_numpy(d["lam"]).to("cuda")
+    out = torch.empty((cfg.nseq, cfg.H, cfg.dv), device="cuda")
+    stream = torch.cuda.current_stream()
+    it = iter(range(steps))
+
+    def step():
+        s = next(it)
+        LL.loglin_decode_step(st, q[s], k[s], v[s], a[s], lam[s], out=out)
+
+    ms = timed(step, steps, stream)
+    LL.loglin_state_free(st)
+    sps = 1e3 / ms
+    byts = decode_bytes(pos, cfg.H, cfg.dk, cfg.dv, cfg.Lmax, steps)
+    gbs = byts / (ms / 1e3) / 1e9
+    log(f"decode: {ms:.3f} ms/step, {sps:.1f} steps/s, {gbs:.0f} GB/s")
+    return {"steps_per_s": sps, "tokens_per_s": sps * cfg.nseq, "ms_per_step": ms,
+            "steps": steps, "config": {"workload": "decode", "nseq": cfg.nseq, "H": cfg.H,
+                                       "dk": cfg.dk, "dv": cfg.dv, "Lmax": cfg.Lmax},
+            "roofline": {"kernel": "decode_step", "bound": "hbm", "achieved": round(gbs, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "alg_bytes_per_step": byts}}
+
+
+if __name__ == "__main__":
+    sys.exit(main())

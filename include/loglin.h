@@ -1,0 +1,177 @@
+/*
+ * loglin.h -- C ABI of libloglin.so, the log-linear (Fenwick-tree) token mixer
+ * on AMD Instinct MI355X (gfx950).
+ *
+ * The operation ("Log-linear attention, and what a logarithm buys"):
+ *   section 1 writes a family of mixers as O = (Q K^T (.) M) V with a causal
+ *   mask M; section 2 cuts the prefix of query t into Fenwick buckets
+ *   (greedily the largest power of two first, bucket l >= 1 of 2^(l-1)
+ *   tokens plus the query itself at level 0), gives each bucket a state
+ *   S_t^(l) and reads o_t = sum_l lambda_t^(l) q_t^T S_t^(l); section 3
+ *   composes this level mask elementwise with the Mamba-2 scalar-decay mask.
+ * With 0-indexed positions, A_t = a_0 + ... + a_t and
+ *   level(t, s) = 0 if s == t, else floor(log2(t XOR s)) + 1,
+ * the mask is M[t, s] = lambda_t^(level(t, s)) * exp(A_t - A_s) for s <= t.
+ *
+ * Conventions for every entry point
+ *  - Tensors are dense, row-major, caller-owned, and live in device memory
+ *    unless a comment says "host".  The library never frees caller memory.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    All device work is enqueued on it and returns without waiting.
+ *  - Every argument is checked on the host before anything is enqueued; a
+ *    call that returns an error has enqueued nothing and changed nothing.
+ *    The text of the last error of the calling thread is loglin_last_error().
+ *  - Documented but not checked: lambda >= 0 and log_decay <= 0 (other values
+ *    are computed as written, with the overflow that implies).
+ */
+#ifndef LOGLIN_H
+#define LOGLIN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#if defined(__GNUC__)
+#define LOGLIN_API __attribute__((visibility("default")))
+#else
+#define LOGLIN_API
+#endif
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    LOGLIN_OK = 0,
+    LOGLIN_EINVAL = 1,       /* bad pointer, size, dtype or workspace */
+    LOGLIN_EUNSUPPORTED = 2, /* chunk size or head dim not in {16,32,64,128}; too many chunks */
+    LOGLIN_ENOMEM = 3,       /* device allocation failed (state init only) */
+    LOGLIN_ECAPACITY = 4,    /* a position needs a level index >= the number of levels */
+    LOGLIN_EHIP = 5          /* the HIP runtime reported an error (see loglin_last_error) */
+} loglin_status;
+
+typedef enum { LOGLIN_F32 = 0, LOGLIN_BF16 = 1 } loglin_dtype;
+
+typedef struct loglin_state loglin_state; /* opaque, owned by the library */
+
+/*
+ * Bytes of device workspace loglin_fwd_chunked needs for these sizes
+ * (0 when T <= C: a single chunk needs no inter-chunk state).  Returns
+ * (size_t)-1 for sizes that loglin_fwd_chunked would reject.
+ */
+LOGLIN_API size_t loglin_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int C);
+
+/*
+ * Chunked forward O = (Q K^T (.) M) V over whole sequences.
+ *
+ * Section 3 of the page splits M into a block diagonal of T/C causal C x C
+ * blocks (every level finer than the chunk) plus one term per coarser level,
+ * each a decayed state passed between chunks; this entry point computes
+ * exactly O, in that chunked form, on the GPU.
+ *
+ *   q          [B, H, T, dk]  in_dtype
+ *   k          [B, H, T, dk]  in_dtype
+ *   v          [B, H, T, dv]  in_dtype
+ *   log_decay  [B, H, T]      fp32, a_t <= 0 (the gate is exp(a_t))
+ *   lambda     [B, H, T, L]   fp32, lambda_t^(l) >= 0, indexed by query t
+ *   out        [B, H, T, dv]  fp32, written (not accumulated)
+ *   C          chunk size, one of 16, 32, 64, 128; T need not be a multiple
+ *              of C (the last chunk is ragged)
+ *   dk, dv     each one of 16, 32, 64, 128
+ *   L          levels in lambda; must cover every level the sequence uses:
+ *              L >= bit_length(T-1) + 1 (L >= 1 for T = 1), and L <= 64
+ *   workspace  device buffer of at least loglin_fwd_workspace_bytes(...)
+ *              bytes, 256-byte aligned (may be NULL when that is 0); its
+ *              contents on entry are ignored and on return are unspecified
+ * B, H or T equal to 0 is a no-op.  T / C may be at most 65536 chunks.
+ * Numerics: in_dtype BF16 feeds bf16 matrix cores with fp32 accumulation;
+ * in_dtype F32 uses fp32 matrix cores throughout.
+ */
+LOGLIN_API loglin_status loglin_fwd_chunked(const void* q, const void* k, const void* v,
+                                 const float* log_decay, const float* lambda, float* out,
+                                 int B, int H, int T, int dk, int dv, int L, int C,
+                                 loglin_dtype in_dtype, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/*
+ * Profiling variant of loglin_fwd_chunked: the same arguments plus a bit mask
+ * of the kernels to enqueue, in their fixed order -- bit 0 chunk states,
+ * bit 1 Fenwick node scan over chunks, bit 2 output (intra-chunk block plus
+ * coarse levels).  Bits 0 and 1 do nothing when T <= C.  `out` is the
+ * mixer's output only after all three ran, in order, on the same workspace;
+ * running bit 2 alone again after that recomputes the same output.
+ * stage_mask = 7 is loglin_fwd_chunked.  Other bits: LOGLIN_EINVAL.
+ */
+LOGLIN_API loglin_status loglin_fwd_chunked_stages(const void* q, const void* k, const void* v,
+                                        const float* log_decay, const float* lambda, float* out,
+                                        int B, int H, int T, int dk, int dv, int L, int C,
+                                        loglin_dtype in_dtype, void* workspace,
+                                        size_t workspace_bytes, unsigned stage_mask,
+                                        void* stream);
+
+/*
+ * Decode state: for nseq sequences x H heads, Lmax level states of dk x dv
+ * fp32 (S = sum k v^T orientation) plus the next position of each sequence.
+ * Allocates device memory (hipMalloc) and zeroes it on `stream`; every
+ * sequence starts at position 0.  dk, dv in {16, 32, 64, 128};
+ * 1 <= Lmax <= 48.  *st is set only on success.
+ */
+LOGLIN_API loglin_status loglin_state_init(loglin_state** st, int nseq, int H, int dk, int dv, int Lmax,
+                                void* stream);
+
+/* Releases the state's device memory (after synchronising the device).  NULL is a no-op. */
+LOGLIN_API loglin_status loglin_state_free(loglin_state* st);
+
+/*
+ * Loads positions and level states.
+ *   pos_host  [nseq] host int64: next position of each sequence (the state
+ *             holds the buckets of tokens 0..pos-1); 0 <= pos <= 2^(Lmax-1)
+ *   levels    [nseq, H, Lmax, dk, dv] device fp32, or NULL for all zeros.
+ *             Slots that are not live for position pos-1 (slot 0 and slot
+ *             p+1 for each set bit p of pos-1 are live) are ignored.
+ * The level copy is enqueued on `stream` (`levels` must stay valid until it
+ * ran); the call returns after the small position copy has completed.
+ */
+LOGLIN_API loglin_status loglin_state_load(loglin_state* st, const int64_t* pos_host, const float* levels,
+                                void* stream);
+
+/*
+ * Exports positions (host, written before return) and the level states
+ * [nseq, H, Lmax, dk, dv] (device fp32, enqueued on `stream`), with every
+ * slot that is not live written as zero -- the states of the recurrence.
+ * Either pointer may be NULL to skip that part.
+ */
+LOGLIN_API loglin_status loglin_state_export(const loglin_state* st, int64_t* pos_host, float* levels,
+                                  void* stream);
+
+/*
+ * One Fenwick decode step for every (sequence, head), section 2 of the page:
+ * at position t with j = lssb(t) (trailing zero bits of t), levels 0..j are
+ * summed and promoted to level j+1, levels above decay by exp(a_t), v_t k_t^T
+ * enters level 0 (at t = 0 only that), then o_t = sum_l lambda^(l) q^T S^(l).
+ *   q, k   [nseq, H, dk] in_dtype;  v [nseq, H, dv] in_dtype
+ *   log_decay [nseq, H] fp32;  lambda [nseq, H, Lmax] fp32
+ *   out    [nseq, H, dv] fp32
+ * Returns LOGLIN_ECAPACITY (and does nothing) if some sequence's position is
+ * 2^(Lmax-1) or more.  Steps on one state must be ordered (same stream).
+ */
+LOGLIN_API loglin_status loglin_decode_step(loglin_state* st, const void* q, const void* k, const void* v,
+                                 const float* log_decay, const float* lambda, float* out,
+                                 loglin_dtype in_dtype, void* stream);
+
+/*
+ * Level map used by the kernels, for checking: out[t * T + s] = level(t, s)
+ * for s <= t and -1 for s > t.  out is [T, T] device int8; 1 <= T <= 16384.
+ */
+LOGLIN_API loglin_status loglin_debug_level_map(int T, int8_t* out, void* stream);
+
+/* Text of the calling thread's last error ("" if none). */
+LOGLIN_API const char* loglin_last_error(void);
+
+/* Name of a status code. */
+LOGLIN_API const char* loglin_status_string(loglin_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* LOGLIN_H */

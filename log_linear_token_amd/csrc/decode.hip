@@ -1,0 +1,195 @@
+// Fenwick decode step, state export and level map on gfx950.
+//
+// "Log-linear attention, and what a logarithm buys", section 2: the decode
+// recurrence is the Fenwick update.  At position t >= 1 with j = lssb(t), the
+// new token's outer product enters level 0, levels 0..j (the old token and
+// the buckets of the trailing one bits of t-1) are summed and promoted to
+// level j+1, and, composing with the Mamba-2 scalar gate (section 1 and 3),
+// every carried state is decayed by alpha_t = exp(a_t).  The output reads
+// o_t = sum_l lambda_t^(l) q_t^T S_t^(l) over the live levels.
+//
+// This kernel is bound by HBM traffic: per (sequence, head) it reads the
+// 1 + popcount(t-1) live states of d_k x d_v fp32 and writes the
+// 1 + popcount(t) live states of position t.  Slots that are not live are
+// neither read nor written (their contents are stale; the export zeroes them).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace loglin {
+
+namespace {
+
+constexpr int kThreads = 256;
+constexpr int kMaxPer = 16;  // float4 elements per thread for a 128 x 128 state
+
+template <typename E>
+__global__ __launch_bounds__(kThreads) void k_decode_step(DecodeParams p) {
+    __shared__ float qs[128], ks[128], vs[128];
+    __shared__ float4 red[kThreads];
+    const int sh = blockIdx.x;  // sequence * H + head
+    const int seq = sh / p.H;
+    const int tid = threadIdx.x;
+    const int64_t t = p.base_pos[seq] + p.step;
+    const int dk = p.dk, dv = p.dv;
+
+    const E* q = static_cast<const E*>(p.q) + (size_t)sh * dk;
+    const E* k = static_cast<const E*>(p.k) + (size_t)sh * dk;
+    const E* v = static_cast<const E*>(p.v) + (size_t)sh * dv;
+    if (tid < dk) {
+        qs[tid] = to_f32(q[tid]);
+        ks[tid] = to_f32(k[tid]);
+    }
+    if (tid < dv) vs[tid] = to_f32(v[tid]);
+    __syncthreads();
+
+    const float alpha = __expf(p.a[sh]);
+    const float* lam = p.lam + (size_t)sh * p.Lmax;
+    const size_t nst4 = (size_t)dk * dv / 4;
+    float4* S = reinterpret_cast<float4*>(p.states) + (size_t)sh * p.Lmax * nst4;
+    const int quads = dv / 4;
+    const int col = (tid % quads) * 4;  // the same for every element of this thread
+
+    // positions of this thread: e4 = tid + kThreads * u
+    int row[kMaxPer];
+#pragma unroll
+    for (int u = 0; u < kMaxPer; ++u) row[u] = (int)(((size_t)(tid + kThreads * u) * 4) / dv);
+    auto valid = [&](int u) { return (size_t)(tid + kThreads * u) < nst4; };
+
+    float4 part = make_float4(0.f, 0.f, 0.f, 0.f);
+    auto accum = [&](float w, float qr, const float4& x) {
+        const float f = w * qr;
+        part.x += f * x.x;
+        part.y += f * x.y;
+        part.z += f * x.z;
+        part.w += f * x.w;
+    };
+
+    if (t >= 1) {
+        const int j = lssb((uint64_t)t);
+        // merge levels 0..j into level j+1 (decayed)
+        float4 acc[kMaxPer];
+#pragma unroll
+        for (int u = 0; u < kMaxPer; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int l = 0; l <= j; ++l) {
+            const float4* src = S + (size_t)l * nst4;
+#pragma unroll
+            for (int u = 0; u < kMaxPer; ++u) {
+                if (valid(u)) {
+                    const float4 x = src[tid + kThreads * u];
+                    acc[u].x += x.x;
+                    acc[u].y += x.y;
+                    acc[u].z += x.z;
+                    acc[u].w += x.w;
+                }
+            }
+        }
+        float4* dst = S + (size_t)(j + 1) * nst4;
+        const float lj = lam[j + 1];
+#pragma unroll
+        for (int u = 0; u < kMaxPer; ++u) {
+            if (valid(u)) {
+                const float4 m = make_float4(alpha * acc[u].x, alpha * acc[u].y, alpha * acc[u].z,
+                                             alpha * acc[u].w);
+                dst[tid + kThreads * u] = m;
+                accum(lj, qs[row[u]], m);
+            }
+        }
+        // live levels above j+1: decay in place
+        for (uint64_t hb = (uint64_t)t >> (j + 1); hb; hb &= hb - 1) {
+            const int l = j + 2 + __builtin_ctzll(hb);
+            float4* s = S + (size_t)l * nst4;
+            const float ll = lam[l];
+            float4 x[kMaxPer];
+#pragma unroll
+            for (int u = 0; u < kMaxPer; ++u)
+                if (valid(u)) x[u] = s[tid + kThreads * u];
+#pragma unroll
+            for (int u = 0; u < kMaxPer; ++u) {
+                if (valid(u)) {
+                    const float4 y = make_float4(alpha * x[u].x, alpha * x[u].y, alpha * x[u].z,
+                                                 alpha * x[u].w);
+                    s[tid + kThreads * u] = y;
+                    accum(ll, qs[row[u]], y);
+                }
+            }
+        }
+    }
+    // level 0 holds the new token alone
+    const float l0 = lam[0];
+#pragma unroll
+    for (int u = 0; u < kMaxPer; ++u) {
+        if (valid(u)) {
+            const float kr = ks[row[u]];
+            const float4 y = make_float4(kr * vs[col], kr * vs[col + 1], kr * vs[col + 2],
+                                         kr * vs[col + 3]);
+            S[tid + kThreads * u] = y;
+            accum(l0, qs[row[u]], y);
+        }
+    }
+
+    red[tid] = part;
+    __syncthreads();
+    if (tid < quads) {
+        float4 o = make_float4(0.f, 0.f, 0.f, 0.f);
+        for (int r = tid; r < kThreads; r += quads) {
+            o.x += red[r].x;
+            o.y += red[r].y;
+            o.z += red[r].z;
+            o.w += red[r].w;
+        }
+        *reinterpret_cast<float4*>(p.out + (size_t)sh * dv + col) = o;
+    }
+}
+
+__global__ void k_state_export(DecodeParams p, float4* dst) {
+    const size_t nst4 = (size_t)p.dk * p.dv / 4;
+    const size_t total = (size_t)p.nseq * p.H * p.Lmax * nst4;
+    const float4* src = reinterpret_cast<const float4*>(p.states);
+    for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+         e += (size_t)gridDim.x * blockDim.x) {
+        const size_t slot = e / nst4;  // (seq * H + h) * Lmax + l
+        const int l = (int)(slot % p.Lmax);
+        const int seq = (int)(slot / ((size_t)p.Lmax * p.H));
+        const int64_t n = p.base_pos[seq] + p.step;  // tokens absorbed so far
+        bool live = false;
+        if (n >= 1) live = (l == 0) || (((uint64_t)(n - 1) >> (l - 1)) & 1);
+        dst[e] = live ? src[e] : make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+}
+
+__global__ void k_level_map(int T, int8_t* out) {
+    const size_t total = (size_t)T * T;
+    for (size_t e = (size_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+         e += (size_t)gridDim.x * blockDim.x) {
+        const int t = (int)(e / T), s = (int)(e % T);
+        out[e] = s > t ? (int8_t)-1 : (int8_t)fenwick_level((uint32_t)t, (uint32_t)s);
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode_step(const DecodeParams& p, bool bf16, hipStream_t stream) {
+    const unsigned nblk = (unsigned)p.nseq * p.H;
+    if (bf16)
+        hipLaunchKernelGGL(k_decode_step<bf16_t>, dim3(nblk), dim3(kThreads), 0, stream, p);
+    else
+        hipLaunchKernelGGL(k_decode_step<float>, dim3(nblk), dim3(kThreads), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_state_export(const DecodeParams& p, float* dst, hipStream_t stream) {
+    const size_t total = (size_t)p.nseq * p.H * p.Lmax * p.dk * p.dv / 4;
+    const unsigned nblk = (unsigned)((total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536);
+    hipLaunchKernelGGL(k_state_export, dim3(nblk), dim3(256), 0, stream, p,
+                       reinterpret_cast<float4*>(dst));
+    return hipGetLastError();
+}
+
+hipError_t launch_level_map(int T, int8_t* out, hipStream_t stream) {
+    const size_t total = (size_t)T * T;
+    const unsigned nblk = (unsigned)((total + 255) / 256 < 65536 ? (total + 255) / 256 : 65536);
+    hipLaunchKernelGGL(k_level_map, dim3(nblk), dim3(256), 0, stream, T, out);
+    return hipGetLastError();
+}
+
+}  // namespace loglin

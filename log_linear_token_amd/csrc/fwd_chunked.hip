@@ -1,0 +1,418 @@
+// Chunked forward of the log-linear token mixer on gfx950.
+//
+// "Log-linear attention, and what a logarithm buys", section 3: with chunk
+// size C the Fenwick mask splits into a block diagonal of causal C x C blocks
+// (every level up to log2 C lives inside a chunk) plus one term per coarser
+// level.  For a query in chunk i and a key in an earlier chunk j the level is
+// log2(C) + floor(log2(i XOR j)) + 1, so the keys of coarse level
+// log2(C) + p + 1 are exactly the 2^p chunks of the block that ends at chunk
+// ((i >> p) << p) - 1, present when bit p of i is set.  Writing G(e) for the
+// decayed sum of k v^T over such a block, taken at the end of its last chunk
+// e, the output of token t in chunk i is
+//
+//   o_t = sum_{s in chunk i, s <= t} lambda_t^(level) e^(A_t - A_s) (q_t.k_s) v_s
+//       + sum_{p : bit p of i} lambda_t^(log2 C + p + 1) e^(A_t - A_end(e_p)) q_t^T G(e_p).
+//
+// Three kernels:
+//   chunk_state   U_i = sum_{s in chunk i} e^(A_end(i) - A_s) v_s k_s^T   (MFMA)
+//   fenwick_scan  G(i) for every chunk i: the Fenwick recurrence of section 2
+//                 run over chunks -- U_i plus the decayed live nodes of levels
+//                 below lssb(i+1), i.e. the block of 2^lssb(i+1) chunks ending
+//                 at i -- computed in place over U (HBM-streaming).
+//   chunk_output  the intra-chunk block (S^T = K Q^T on MFMA, masked in
+//                 registers, then P V on MFMA) plus Q G(e_p) for each set bit
+//                 of i (MFMA), weighted per row, one write of the output.
+//
+// Workspace layout (per (batch*head) bh, chunk i):
+//   ust [BH][N][dv][dk] fp32   U_i transposed, then G(i) transposed
+//   tot [BH][N]         fp32   sum of a over the chunk
+//   cum [BH][N]         fp64   A at the end of each chunk (prefix of tot)
+#include <type_traits>
+
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace loglin {
+
+namespace {
+
+constexpr int kPadT = 4;  // elements of padding on transposed (token-major) LDS rows
+constexpr int kPadK = 8;  // elements of padding on natural (head-dim-major) LDS rows
+
+// Blocks are dispatched round-robin over the 8 XCDs of the chip.  Remap the
+// hardware block index so that consecutive logical indices (the chunks of one
+// head, which share Fenwick nodes) land on the same XCD and its L2.
+__device__ __forceinline__ int xcd_local_block(int b, int nblocks) {
+    if (nblocks % 8 != 0) return b;
+    return (b % 8) * (nblocks / 8) + b / 8;
+}
+
+template <typename E>
+__device__ __forceinline__ void load_vec16(const E* src, bool ok, E* dst) {
+    constexpr int V = 16 / sizeof(E);
+    if (ok) {
+        const uint4 x = *reinterpret_cast<const uint4*>(src);
+        *reinterpret_cast<uint4*>(dst) = x;
+    } else {
+#pragma unroll
+        for (int j = 0; j < V; ++j) dst[j] = E(0);
+    }
+}
+
+// Stage rows [t0, t0 + C) of a [T][D] tensor into LDS transposed: dst[d][s]
+// with row stride C + kPadT; rows past T are zero.
+template <typename E, int C>
+__device__ __forceinline__ void stage_transposed(const E* __restrict__ src, int D, int nvalid,
+                                                 E* dst, const float* scale) {
+    constexpr int V = 16 / sizeof(E);
+    const int vpr = D / V;
+    for (int idx = threadIdx.x; idx < C * vpr; idx += blockDim.x) {
+        const int s = idx / vpr;
+        const int d0 = (idx - s * vpr) * V;
+        E buf[V];
+        load_vec16<E>(src + (size_t)s * D + d0, s < nvalid, buf);
+        if (scale) {
+            const float f = scale[s];
+#pragma unroll
+            for (int j = 0; j < V; ++j) {
+                if constexpr (sizeof(E) == 2) {
+                    __bf16 b = (__bf16)(bf16_to_f32(buf[j]) * f);
+                    dst[(d0 + j) * (C + kPadT) + s] = __builtin_bit_cast(bf16_t, b);
+                } else {
+                    dst[(d0 + j) * (C + kPadT) + s] = buf[j] * f;
+                }
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < V; ++j) dst[(d0 + j) * (C + kPadT) + s] = buf[j];
+        }
+    }
+}
+
+// Stage rows [t0, t0 + C) of a [T][D] tensor into LDS as is: dst[s][d] with
+// row stride D + kPadK; rows past T are zero.
+template <typename E, int C>
+__device__ __forceinline__ void stage_natural(const E* __restrict__ src, int D, int nvalid,
+                                              E* dst) {
+    constexpr int V = 16 / sizeof(E);
+    const int vpr = D / V;
+    for (int idx = threadIdx.x; idx < C * vpr; idx += blockDim.x) {
+        const int s = idx / vpr;
+        const int d0 = (idx - s * vpr) * V;
+        load_vec16<E>(src + (size_t)s * D + d0, s < nvalid, dst + s * (D + kPadK) + d0);
+    }
+}
+
+// --------------------------------------------------------------------------
+// chunk_state: U_i^T = sum_s e^(A_end - A_s) v_s k_s^T  -> ust[bh][i] ([dv][dk])
+
+template <typename E, int C>
+__global__ __launch_bounds__(256) void k_chunk_state(FwdParams p) {
+    extern __shared__ __align__(16) char smem[];
+    const int blk = xcd_local_block(blockIdx.x, gridDim.x);
+    const int bh = blk / p.N;
+    const int i = blk - bh * p.N;
+    const int t0 = i * C;
+    const int nvalid = min(C, p.T - t0);
+    float* a_raw = reinterpret_cast<float*>(smem);
+    float* A = a_raw + C;
+    float* e = A + C;
+    E* KT = reinterpret_cast<E*>(e + C);
+    E* VT = KT + p.dk * (C + kPadT);
+    const size_t row0 = (size_t)bh * p.T + t0;
+
+    for (int s = threadIdx.x; s < C; s += blockDim.x) a_raw[s] = s < nvalid ? p.a[row0 + s] : 0.f;
+    __syncthreads();
+    if (threadIdx.x < kWave) wave_cumsum(a_raw, A, C);
+    __syncthreads();
+    const float Aend = A[C - 1];
+    for (int s = threadIdx.x; s < C; s += blockDim.x) e[s] = __expf(Aend - A[s]);
+    __syncthreads();
+    stage_transposed<E, C>(static_cast<const E*>(p.k) + row0 * p.dk, p.dk, nvalid, KT, nullptr);
+    stage_transposed<E, C>(static_cast<const E*>(p.v) + row0 * p.dv, p.dv, nvalid, VT, e);
+    if (threadIdx.x == 0) p.tot[(size_t)bh * p.N + i] = Aend;
+    __syncthreads();
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int nw = blockDim.x / kWave;
+    const int m = lane & 15, g = lane >> 4;
+    const int ntk = p.dk / 16;
+    const int ntiles = (p.dv / 16) * ntk;
+    float* dstU = p.ust + ((size_t)bh * p.N + i) * p.dv * p.dk;
+    for (int tile = wave; tile < ntiles; tile += nw) {
+        const int cv0 = (tile / ntk) * 16, ck0 = (tile % ntk) * 16;
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const E* va = VT + (cv0 + m) * (C + kPadT) + 4 * g;
+        const E* kb = KT + (ck0 + m) * (C + kPadT) + 4 * g;
+#pragma unroll
+        for (int S = 0; S < C / 16; ++S) {
+            if constexpr (sizeof(E) == 2) {
+                acc = mma(Frag<bf16_t, 16>::load(va + 16 * S), Frag<bf16_t, 16>::load(kb + 16 * S),
+                          acc);
+            } else {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc = mma(va[16 * S + j], kb[16 * S + j], acc);
+            }
+        }
+#pragma unroll
+        for (int r = 0; r < 4; ++r) dstU[(size_t)(cv0 + 4 * g + r) * p.dk + ck0 + m] = acc[r];
+    }
+}
+
+// --------------------------------------------------------------------------
+// fenwick_scan: one thread per (bh, 4 state elements), walking the chunks.
+
+constexpr int kScanLevels = 16;  // supports up to 2^16 chunks per sequence
+constexpr int kScanDepth = 8;    // loads kept in flight per thread
+
+__global__ __launch_bounds__(256) void k_fenwick_scan(FwdParams p) {
+    const int per4 = p.dv * p.dk / 4;
+    const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    const int bh = (int)(gid / per4);
+    const int e4 = (int)(gid - (long)bh * per4);
+    if (bh >= p.BH) return;
+    const int N = p.N;
+    float4* base = reinterpret_cast<float4*>(p.ust) + (size_t)bh * N * per4 + e4;
+    const float* tot = p.tot + (size_t)bh * N;
+    double* cum = p.cum + (size_t)bh * N;
+
+    float4 live[kScanLevels];
+    double lcum[kScanLevels];
+#pragma unroll
+    for (int q = 0; q < kScanLevels; ++q) {
+        live[q] = make_float4(0.f, 0.f, 0.f, 0.f);
+        lcum[q] = 0.0;
+    }
+    float4 ring[kScanDepth];
+#pragma unroll
+    for (int d = 0; d < kScanDepth; ++d)
+        ring[d] = d < N ? base[(size_t)d * per4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    double c = 0.0;
+    for (int i0 = 0; i0 < N; i0 += kScanDepth) {
+#pragma unroll
+        for (int d = 0; d < kScanDepth; ++d) {
+            const int i = i0 + d;
+            if (i < N) {
+                float4 acc = ring[d];
+                if (i + kScanDepth < N) ring[d] = base[(size_t)(i + kScanDepth) * per4];
+                c += (double)tot[i];
+                const int j = lssb((uint64_t)i + 1);
+#pragma unroll
+                for (int q = 0; q < kScanLevels; ++q) {
+                    if (q < j) {
+                        const float w = __expf((float)(c - lcum[q]));
+                        acc.x += w * live[q].x;
+                        acc.y += w * live[q].y;
+                        acc.z += w * live[q].z;
+                        acc.w += w * live[q].w;
+                    }
+                }
+#pragma unroll
+                for (int q = 0; q < kScanLevels; ++q) {
+                    if (q == j) {
+                        live[q] = acc;
+                        lcum[q] = c;
+                    }
+                }
+                if (i + 1 < N) base[(size_t)i * per4] = acc;
+                if (e4 == 0) cum[i] = c;
+            }
+        }
+    }
+}
+
+// --------------------------------------------------------------------------
+// chunk_output: intra-chunk block plus the coarse levels, one block per chunk,
+// one wave per 16 query rows.
+
+template <int LOGC>
+__device__ __forceinline__ float pick_level(const float (&lamr)[LOGC + 1], int lev) {
+    float r = lamr[0];
+#pragma unroll
+    for (int l = 1; l <= LOGC; ++l) r = lev == l ? lamr[l] : r;
+    return r;
+}
+
+template <typename E, int C, int DK>
+__global__ __launch_bounds__(C / 16 * 64) void k_chunk_output(FwdParams p) {
+    constexpr int NW = C / 16;
+    constexpr int LOGC = (C == 16) ? 4 : (C == 32) ? 5 : (C == 64) ? 6 : 7;
+    constexpr int KS = HeadStep<E, DK>::KS;
+    constexpr int NKS = DK / KS;
+    typedef Frag<E, KS> FR;
+    typedef typename FR::type frag_t;
+    constexpr int KPL = FR::kpl;
+
+    extern __shared__ __align__(16) char smem[];
+    const int blk = xcd_local_block(blockIdx.x, gridDim.x);
+    const int bh = blk / p.N;
+    const int i = blk - bh * p.N;
+    const int t0 = i * C;
+    const int nvalid = min(C, p.T - t0);
+    const int dv = p.dv;
+    float* a_raw = reinterpret_cast<float*>(smem);
+    float* A = a_raw + C;
+    E* Kn = reinterpret_cast<E*>(A + C);
+    E* VT = Kn + C * (DK + kPadK);
+    const size_t row0 = (size_t)bh * p.T + t0;
+
+    for (int s = threadIdx.x; s < C; s += blockDim.x) a_raw[s] = s < nvalid ? p.a[row0 + s] : 0.f;
+    stage_natural<E, C>(static_cast<const E*>(p.k) + row0 * DK, DK, nvalid, Kn);
+    stage_transposed<E, C>(static_cast<const E*>(p.v) + row0 * dv, dv, nvalid, VT, nullptr);
+    __syncthreads();
+    if (threadIdx.x < kWave) wave_cumsum(a_raw, A, C);
+    __syncthreads();
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int R = threadIdx.x / kWave;  // row block of this wave
+    const int m = lane & 15, g = lane >> 4;
+    const int r = 16 * R + m;           // query row within the chunk
+    const bool rvalid = r < nvalid;
+    const size_t trow = row0 + r;
+
+    // Q row r as the B operand of S^T = K Q^T (contraction over the head dim)
+    frag_t qf[NKS];
+    const E* qrow = static_cast<const E*>(p.q) + trow * DK;
+#pragma unroll
+    for (int ks = 0; ks < NKS; ++ks) {
+        if (rvalid) {
+            qf[ks] = FR::load(qrow + ks * KS + g * KPL);
+        } else {
+            qf[ks] = frag_t{};
+        }
+    }
+    // lambda of row r at the levels inside a chunk
+    float lamr[LOGC + 1];
+    const float* lrow = p.lam + trow * p.L;
+#pragma unroll
+    for (int l = 0; l <= LOGC; ++l) lamr[l] = (rvalid && l < p.L) ? lrow[l] : 0.f;
+    const float Ar = A[r];
+
+    // P^T tiles: the masked scores, kept as B operands of O^T = V^T P^T
+    typedef typename std::conditional<sizeof(E) == 2, bf16x4, f32x4>::type pfrag_t;
+    pfrag_t P[NW];
+#pragma unroll
+    for (int S = 0; S < NW; ++S) {
+        if (S <= R) {
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            const E* krow = Kn + (16 * S + m) * (DK + kPadK) + g * KPL;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) acc = mma(FR::load(krow + ks * KS), qf[ks], acc);
+            float w[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int s = 16 * S + 4 * g + q;
+                const float lam = pick_level<LOGC>(lamr, fenwick_level(r, s));
+                w[q] = s <= r ? acc[q] * lam * __expf(Ar - A[s]) : 0.f;
+            }
+            if constexpr (sizeof(E) == 2) {
+                P[S] = pack4(w[0], w[1], w[2], w[3]);
+            } else {
+                P[S] = f32x4{w[0], w[1], w[2], w[3]};
+            }
+        }
+    }
+
+    const double* cum = p.cum + (size_t)bh * p.N;
+    float* orow = p.out + trow * dv;
+    for (int cv0 = 0; cv0 < dv; cv0 += 16) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        const E* vrow = VT + (cv0 + m) * (C + kPadT) + 4 * g;
+#pragma unroll
+        for (int S = 0; S < NW; ++S) {
+            if (S <= R) {
+                if constexpr (sizeof(E) == 2) {
+                    acc = mma(Frag<bf16_t, 16>::load(vrow + 16 * S), P[S], acc);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) acc = mma(vrow[16 * S + j], P[S][j], acc);
+                }
+            }
+        }
+        // coarse levels: one Fenwick node per set bit of the chunk index
+        for (int pb = 0; (i >> pb) != 0; ++pb) {
+            if (!((i >> pb) & 1)) continue;
+            const int node = ((i >> pb) << pb) - 1;
+            const float dl = (float)(cum[i - 1] - cum[node]);
+            const int lev = LOGC + pb + 1;
+            const float w = rvalid ? lrow[lev] * __expf(Ar + dl) : 0.f;
+            const float* G = p.ust + ((size_t)bh * p.N + node) * dv * DK + (size_t)(cv0 + m) * DK +
+                             g * KPL;
+            f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) y = mma(FR::from_f32(G + ks * KS), qf[ks], y);
+            acc[0] += w * y[0];
+            acc[1] += w * y[1];
+            acc[2] += w * y[2];
+            acc[3] += w * y[3];
+        }
+        if (rvalid)
+            *reinterpret_cast<float4*>(orow + cv0 + 4 * g) = make_float4(acc[0], acc[1], acc[2],
+                                                                          acc[3]);
+    }
+}
+
+template <typename E, int C>
+size_t state_smem(int dk, int dv) {
+    return 3 * C * sizeof(float) + (size_t)(dk + dv) * (C + kPadT) * sizeof(E);
+}
+template <typename E, int C, int DK>
+size_t output_smem(int dv) {
+    return 2 * C * sizeof(float) + (size_t)C * (DK + kPadK) * sizeof(E) +
+           (size_t)dv * (C + kPadT) * sizeof(E);
+}
+
+template <typename E, int C, int DK>
+hipError_t launch_typed(const FwdParams& p, unsigned stages, hipStream_t stream) {
+    const int nblk = p.BH * p.N;
+    if (p.N > 1 && (stages & kStageChunkState)) {
+        const size_t sm1 = state_smem<E, C>(p.dk, p.dv);
+        hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_chunk_state<E, C>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm1);
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL((k_chunk_state<E, C>), dim3(nblk), dim3(256), sm1, stream, p);
+    }
+    if (p.N > 1 && (stages & kStageScan)) {
+        const long threads = (long)p.BH * (p.dv * p.dk / 4);
+        hipLaunchKernelGGL(k_fenwick_scan, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
+                           stream, p);
+    }
+    if (!(stages & kStageOutput)) return hipGetLastError();
+    const size_t sm3 = output_smem<E, C, DK>(p.dv);
+    hipError_t err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_chunk_output<E, C, DK>),
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)sm3);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((k_chunk_output<E, C, DK>), dim3(nblk), dim3(C / 16 * 64), sm3, stream, p);
+    return hipGetLastError();
+}
+
+template <typename E, int C>
+hipError_t launch_c(const FwdParams& p, unsigned st, hipStream_t s) {
+    switch (p.dk) {
+        case 16: return launch_typed<E, C, 16>(p, st, s);
+        case 32: return launch_typed<E, C, 32>(p, st, s);
+        case 64: return launch_typed<E, C, 64>(p, st, s);
+        case 128: return launch_typed<E, C, 128>(p, st, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename E>
+hipError_t launch_e(const FwdParams& p, unsigned st, hipStream_t s) {
+    switch (p.C) {
+        case 16: return launch_c<E, 16>(p, st, s);
+        case 32: return launch_c<E, 32>(p, st, s);
+        case 64: return launch_c<E, 64>(p, st, s);
+        case 128: return launch_c<E, 128>(p, st, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_fwd_chunked(const FwdParams& p, bool bf16, unsigned stages, hipStream_t stream) {
+    return bf16 ? launch_e<bf16_t>(p, stages, stream) : launch_e<float>(p, stages, stream);
+}
+
+}  // namespace loglin

@@ -1,0 +1,49 @@
+// Internal launch interface between the C ABI (loglin_api.cpp) and the HIP
+// kernels.  Not exported.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace loglin {
+
+struct FwdParams {
+    const void* q;       // [BH][T][dk]
+    const void* k;       // [BH][T][dk]
+    const void* v;       // [BH][T][dv]
+    const float* a;      // [BH][T]
+    const float* lam;    // [BH][T][L]
+    float* out;          // [BH][T][dv]
+    int BH, T, dk, dv, L, C, N;  // N = ceil(T / C)
+    float* ust;          // workspace [BH][N][dv][dk]
+    float* tot;          // workspace [BH][N]
+    double* cum;         // workspace [BH][N]
+};
+
+// workspace carving shared by the size query and the launch
+struct FwdWorkspace {
+    size_t ust_off, tot_off, cum_off, total;
+};
+FwdWorkspace fwd_workspace_layout(long BH, long N, int dk, int dv);
+
+enum : unsigned { kStageChunkState = 1u, kStageScan = 2u, kStageOutput = 4u, kStageAll = 7u };
+hipError_t launch_fwd_chunked(const FwdParams& p, bool bf16, unsigned stages, hipStream_t stream);
+
+struct DecodeParams {
+    float* states;            // [nseq][H][Lmax][dk][dv]
+    const int64_t* base_pos;  // [nseq]: position of the first step after the last load
+    int64_t step;             // steps taken since that load
+    const void* q;            // [nseq][H][dk]
+    const void* k;            // [nseq][H][dk]
+    const void* v;            // [nseq][H][dv]
+    const float* a;           // [nseq][H]
+    const float* lam;         // [nseq][H][Lmax]
+    float* out;               // [nseq][H][dv]
+    int nseq, H, dk, dv, Lmax;
+};
+
+hipError_t launch_decode_step(const DecodeParams& p, bool bf16, hipStream_t stream);
+// copy states to dst, zeroing every slot that is not live at the current position
+hipError_t launch_state_export(const DecodeParams& p, float* dst, hipStream_t stream);
+hipError_t launch_level_map(int T, int8_t* out, hipStream_t stream);
+
+}  // namespace loglin

@@ -1,0 +1,365 @@
+// C ABI of libloglin.so: argument checks on the host, workspace carving,
+// decode-state lifecycle, and the launches.  Declared in include/loglin.h.
+#include "loglin.h"
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "kernels.hpp"
+
+using namespace loglin;
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+loglin_status fail(loglin_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+loglin_status ok() {
+    g_err[0] = '\0';
+    return LOGLIN_OK;
+}
+
+loglin_status hip_fail(hipError_t e, const char* where) {
+    return fail(LOGLIN_EHIP, "%s: %s", where, hipGetErrorString(e));
+}
+
+bool supported_dim(int d) { return d == 16 || d == 32 || d == 64 || d == 128; }
+
+int bit_length(long x) {
+    int n = 0;
+    while (x > 0) {
+        ++n;
+        x >>= 1;
+    }
+    return n;
+}
+
+// levels a sequence of T tokens uses: level 0 and up to bit_length(T-1)
+int levels_needed(long T) { return T <= 1 ? 1 : bit_length(T - 1) + 1; }
+
+constexpr long kMaxChunks = 65536;
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+// Checks shared by the workspace query and the forward; on failure sets the
+// error text and returns the status.
+loglin_status check_fwd_sizes(int B, int H, int T, int dk, int dv, int C) {
+    if (B < 0 || H < 0 || T < 0)
+        return fail(LOGLIN_EINVAL, "B, H, T must be >= 0 (got %d, %d, %d)", B, H, T);
+    if (!supported_dim(C)) return fail(LOGLIN_EUNSUPPORTED, "chunk size C=%d not in {16,32,64,128}", C);
+    if (!supported_dim(dk) || !supported_dim(dv))
+        return fail(LOGLIN_EUNSUPPORTED, "head dims dk=%d dv=%d must be in {16,32,64,128}", dk, dv);
+    const long N = ((long)T + C - 1) / C;
+    if (N > kMaxChunks)
+        return fail(LOGLIN_EUNSUPPORTED, "T/C = %ld chunks exceeds %ld", N, kMaxChunks);
+    if ((long)B * H * N > 0x7fffffffL)
+        return fail(LOGLIN_EUNSUPPORTED, "B*H*ceil(T/C) = %ld blocks is too many", (long)B * H * N);
+    return LOGLIN_OK;
+}
+
+}  // namespace
+
+namespace loglin {
+FwdWorkspace fwd_workspace_layout(long BH, long N, int dk, int dv) {
+    FwdWorkspace w{};
+    if (N <= 1 || BH == 0) return w;
+    w.ust_off = 0;
+    w.tot_off = align_up(w.ust_off + (size_t)BH * N * dv * dk * sizeof(float));
+    w.cum_off = align_up(w.tot_off + (size_t)BH * N * sizeof(float));
+    w.total = align_up(w.cum_off + (size_t)BH * N * sizeof(double));
+    return w;
+}
+}  // namespace loglin
+
+extern "C" {
+
+const char* loglin_last_error(void) { return g_err; }
+
+const char* loglin_status_string(loglin_status s) {
+    switch (s) {
+        case LOGLIN_OK: return "LOGLIN_OK";
+        case LOGLIN_EINVAL: return "LOGLIN_EINVAL";
+        case LOGLIN_EUNSUPPORTED: return "LOGLIN_EUNSUPPORTED";
+        case LOGLIN_ENOMEM: return "LOGLIN_ENOMEM";
+        case LOGLIN_ECAPACITY: return "LOGLIN_ECAPACITY";
+        case LOGLIN_EHIP: return "LOGLIN_EHIP";
+    }
+    return "LOGLIN_<unknown>";
+}
+
+size_t loglin_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int C) {
+    if (check_fwd_sizes(B, H, T, dk, dv, C) != LOGLIN_OK) return (size_t)-1;
+    const long N = ((long)T + C - 1) / C;
+    return fwd_workspace_layout((long)B * H, N, dk, dv).total;
+}
+
+loglin_status loglin_fwd_chunked_stages(const void* q, const void* k, const void* v,
+                                        const float* log_decay, const float* lambda, float* out,
+                                        int B, int H, int T, int dk, int dv, int L, int C,
+                                        loglin_dtype in_dtype, void* workspace,
+                                        size_t workspace_bytes, unsigned stage_mask,
+                                        void* stream) {
+    if (stage_mask & ~kStageAll) return fail(LOGLIN_EINVAL, "stage mask 0x%x has unknown bits", stage_mask);
+    loglin_status s = check_fwd_sizes(B, H, T, dk, dv, C);
+    if (s != LOGLIN_OK) return s;
+    if (in_dtype != LOGLIN_F32 && in_dtype != LOGLIN_BF16)
+        return fail(LOGLIN_EINVAL, "in_dtype %d is neither LOGLIN_F32 nor LOGLIN_BF16", (int)in_dtype);
+    if ((long)B * H * T == 0) return ok();
+    if (L < levels_needed(T) || L > 64)
+        return fail(LOGLIN_EINVAL, "L=%d: T=%d needs %d levels (and L <= 64)", L, T, levels_needed(T));
+    if (!q || !k || !v || !log_decay || !lambda || !out)
+        return fail(LOGLIN_EINVAL, "null tensor pointer");
+    const long N = ((long)T + C - 1) / C;
+    const long BH = (long)B * H;
+    const FwdWorkspace w = fwd_workspace_layout(BH, N, dk, dv);
+    if (w.total > 0) {
+        if (!workspace || workspace_bytes < w.total)
+            return fail(LOGLIN_EINVAL, "workspace of %zu bytes needed, got %zu%s", w.total,
+                        workspace_bytes, workspace ? "" : " (NULL)");
+        if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
+            return fail(LOGLIN_EINVAL, "workspace must be %zu-byte aligned", kAlign);
+    }
+    const size_t esz = in_dtype == LOGLIN_BF16 ? 2 : 4;
+    if (reinterpret_cast<uintptr_t>(q) % 16 || reinterpret_cast<uintptr_t>(k) % 16 ||
+        reinterpret_cast<uintptr_t>(v) % 16 || reinterpret_cast<uintptr_t>(out) % 16)
+        return fail(LOGLIN_EINVAL, "q, k, v and out must be 16-byte aligned");
+    (void)esz;
+
+    FwdParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.a = log_decay;
+    p.lam = lambda;
+    p.out = out;
+    p.BH = (int)BH;
+    p.T = T;
+    p.dk = dk;
+    p.dv = dv;
+    p.L = L;
+    p.C = C;
+    p.N = (int)N;
+    if (w.total > 0) {
+        char* base = static_cast<char*>(workspace);
+        p.ust = reinterpret_cast<float*>(base + w.ust_off);
+        p.tot = reinterpret_cast<float*>(base + w.tot_off);
+        p.cum = reinterpret_cast<double*>(base + w.cum_off);
+    }
+    hipError_t e = launch_fwd_chunked(p, in_dtype == LOGLIN_BF16, stage_mask,
+                                      static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "loglin_fwd_chunked launch");
+    return ok();
+}
+
+loglin_status loglin_fwd_chunked(const void* q, const void* k, const void* v,
+                                 const float* log_decay, const float* lambda, float* out, int B,
+                                 int H, int T, int dk, int dv, int L, int C, loglin_dtype in_dtype,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+    return loglin_fwd_chunked_stages(q, k, v, log_decay, lambda, out, B, H, T, dk, dv, L, C,
+                                     in_dtype, workspace, workspace_bytes, kStageAll, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// decode state
+
+struct loglin_state {
+    int nseq, H, dk, dv, Lmax;
+    float* levels;               // device [nseq][H][Lmax][dk][dv]
+    int64_t* base_pos;           // device [nseq]
+    std::vector<int64_t> host_base;  // host mirror of base_pos
+    int64_t step;                // steps since the last load
+    int64_t max_base;
+    uint32_t magic;
+};
+
+namespace {
+constexpr uint32_t kMagic = 0x4c4f474cu;  // "LOGL"
+
+loglin_status check_state(const loglin_state* st) {
+    if (!st || st->magic != kMagic) return fail(LOGLIN_EINVAL, "invalid or freed state handle");
+    return LOGLIN_OK;
+}
+
+DecodeParams decode_params(const loglin_state* st) {
+    DecodeParams p{};
+    p.states = st->levels;
+    p.base_pos = st->base_pos;
+    p.step = st->step;
+    p.nseq = st->nseq;
+    p.H = st->H;
+    p.dk = st->dk;
+    p.dv = st->dv;
+    p.Lmax = st->Lmax;
+    return p;
+}
+
+bool alloc_fail_injected() {
+    const char* e = getenv("LOGLIN_TEST_FAIL_ALLOC");
+    return e && e[0] == '1';
+}
+}  // namespace
+
+extern "C" {
+
+loglin_status loglin_state_init(loglin_state** out, int nseq, int H, int dk, int dv, int Lmax,
+                                void* stream) {
+    if (!out) return fail(LOGLIN_EINVAL, "null output handle pointer");
+    if (nseq < 1 || H < 1) return fail(LOGLIN_EINVAL, "nseq=%d and H=%d must be >= 1", nseq, H);
+    if (!supported_dim(dk) || !supported_dim(dv))
+        return fail(LOGLIN_EUNSUPPORTED, "head dims dk=%d dv=%d must be in {16,32,64,128}", dk, dv);
+    if (Lmax < 1 || Lmax > 48) return fail(LOGLIN_EINVAL, "Lmax=%d must be in [1, 48]", Lmax);
+    if ((long)nseq * H > 0x7fffffffL) return fail(LOGLIN_EUNSUPPORTED, "nseq*H too large");
+    loglin_state* st = new (std::nothrow) loglin_state();
+    if (!st) return fail(LOGLIN_ENOMEM, "host allocation failed");
+    st->nseq = nseq;
+    st->H = H;
+    st->dk = dk;
+    st->dv = dv;
+    st->Lmax = Lmax;
+    st->step = 0;
+    st->max_base = 0;
+    st->host_base.assign(nseq, 0);
+    const size_t bytes = (size_t)nseq * H * Lmax * dk * dv * sizeof(float);
+    if (alloc_fail_injected()) {
+        delete st;
+        return fail(LOGLIN_ENOMEM, "device allocation of %zu bytes failed (injected)", bytes);
+    }
+    hipError_t e = hipMalloc(&st->levels, bytes);
+    if (e != hipSuccess) {
+        delete st;
+        return fail(LOGLIN_ENOMEM, "hipMalloc(%zu): %s", bytes, hipGetErrorString(e));
+    }
+    e = hipMalloc(&st->base_pos, (size_t)nseq * sizeof(int64_t));
+    if (e != hipSuccess) {
+        (void)hipFree(st->levels);
+        delete st;
+        return fail(LOGLIN_ENOMEM, "hipMalloc positions: %s", hipGetErrorString(e));
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    e = hipMemsetAsync(st->levels, 0, bytes, s);
+    if (e == hipSuccess) e = hipMemsetAsync(st->base_pos, 0, (size_t)nseq * sizeof(int64_t), s);
+    if (e != hipSuccess) {
+        (void)hipFree(st->levels);
+        (void)hipFree(st->base_pos);
+        delete st;
+        return hip_fail(e, "loglin_state_init");
+    }
+    st->magic = kMagic;
+    *out = st;
+    return ok();
+}
+
+loglin_status loglin_state_free(loglin_state* st) {
+    if (!st) return ok();
+    loglin_status s = check_state(st);
+    if (s != LOGLIN_OK) return s;
+    hipError_t e = hipDeviceSynchronize();
+    st->magic = 0;
+    hipError_t e1 = hipFree(st->levels);
+    hipError_t e2 = hipFree(st->base_pos);
+    delete st;
+    if (e != hipSuccess) return hip_fail(e, "loglin_state_free (synchronize)");
+    if (e1 != hipSuccess) return hip_fail(e1, "loglin_state_free");
+    if (e2 != hipSuccess) return hip_fail(e2, "loglin_state_free");
+    return ok();
+}
+
+loglin_status loglin_state_load(loglin_state* st, const int64_t* pos_host, const float* levels,
+                                void* stream) {
+    loglin_status s = check_state(st);
+    if (s != LOGLIN_OK) return s;
+    if (!pos_host) return fail(LOGLIN_EINVAL, "null positions");
+    const int64_t cap = (int64_t)1 << (st->Lmax - 1);
+    int64_t mx = 0;
+    for (int i = 0; i < st->nseq; ++i) {
+        if (pos_host[i] < 0) return fail(LOGLIN_EINVAL, "position %lld of sequence %d is negative",
+                                         (long long)pos_host[i], i);
+        if (pos_host[i] > cap)
+            return fail(LOGLIN_ECAPACITY, "position %lld of sequence %d needs more than %d levels",
+                        (long long)pos_host[i], i, st->Lmax);
+        mx = pos_host[i] > mx ? pos_host[i] : mx;
+    }
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    const size_t bytes = (size_t)st->nseq * st->H * st->Lmax * st->dk * st->dv * sizeof(float);
+    hipError_t e = levels ? hipMemcpyAsync(st->levels, levels, bytes, hipMemcpyDeviceToDevice, hs)
+                          : hipMemsetAsync(st->levels, 0, bytes, hs);
+    if (e != hipSuccess) return hip_fail(e, "loglin_state_load (levels)");
+    st->host_base.assign(pos_host, pos_host + st->nseq);
+    // the host vector must outlive the asynchronous copy: it does, as it is
+    // only replaced by the next load, which is ordered after this one only if
+    // we wait here for the small copy to finish.
+    e = hipMemcpyAsync(st->base_pos, st->host_base.data(), (size_t)st->nseq * sizeof(int64_t),
+                       hipMemcpyHostToDevice, hs);
+    if (e == hipSuccess) e = hipStreamSynchronize(hs);
+    if (e != hipSuccess) return hip_fail(e, "loglin_state_load (positions)");
+    st->step = 0;
+    st->max_base = mx;
+    return ok();
+}
+
+loglin_status loglin_state_export(const loglin_state* st, int64_t* pos_host, float* levels,
+                                  void* stream) {
+    loglin_status s = check_state(st);
+    if (s != LOGLIN_OK) return s;
+    if (pos_host)
+        for (int i = 0; i < st->nseq; ++i) pos_host[i] = st->host_base[i] + st->step;
+    if (levels) {
+        hipError_t e = launch_state_export(decode_params(st), levels, static_cast<hipStream_t>(stream));
+        if (e != hipSuccess) return hip_fail(e, "loglin_state_export");
+    }
+    return ok();
+}
+
+loglin_status loglin_decode_step(loglin_state* st, const void* q, const void* k, const void* v,
+                                 const float* log_decay, const float* lambda, float* out,
+                                 loglin_dtype in_dtype, void* stream) {
+    loglin_status s = check_state(st);
+    if (s != LOGLIN_OK) return s;
+    if (in_dtype != LOGLIN_F32 && in_dtype != LOGLIN_BF16)
+        return fail(LOGLIN_EINVAL, "in_dtype %d is neither LOGLIN_F32 nor LOGLIN_BF16", (int)in_dtype);
+    if (!q || !k || !v || !log_decay || !lambda || !out)
+        return fail(LOGLIN_EINVAL, "null tensor pointer");
+    if (reinterpret_cast<uintptr_t>(out) % 16)
+        return fail(LOGLIN_EINVAL, "out must be 16-byte aligned");
+    const int64_t t = st->max_base + st->step;  // largest position decoded by this step
+    if (t >= ((int64_t)1 << (st->Lmax - 1)))
+        return fail(LOGLIN_ECAPACITY, "position %lld needs more than %d levels", (long long)t,
+                    st->Lmax);
+    DecodeParams p = decode_params(st);
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.a = log_decay;
+    p.lam = lambda;
+    p.out = out;
+    hipError_t e = launch_decode_step(p, in_dtype == LOGLIN_BF16, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "loglin_decode_step launch");
+    st->step += 1;
+    return ok();
+}
+
+loglin_status loglin_debug_level_map(int T, int8_t* out, void* stream) {
+    if (T < 1 || T > 16384) return fail(LOGLIN_EINVAL, "T=%d must be in [1, 16384]", T);
+    if (!out) return fail(LOGLIN_EINVAL, "null output");
+    hipError_t e = launch_level_map(T, out, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "loglin_debug_level_map");
+    return ok();
+}
+
+}  // extern "C"

@@ -1,0 +1,240 @@
+"""Thin ctypes binding of libloglin.so (C ABI in include/loglin.h).
+
+The functions carry the names of the C entry points and only marshal
+arguments: they check that tensors are contiguous CUDA (HIP) tensors of the
+right dtype and shape, allocate outputs and workspace with torch when the
+caller passes none, and pass raw pointers plus torch's current stream.  All
+arithmetic runs in the library's HIP kernels.  If the library is missing the
+first call raises; there is no fallback.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from dataclasses import dataclass
+
+import torch
+
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libloglin.so")
+
+LOGLIN_OK, LOGLIN_EINVAL, LOGLIN_EUNSUPPORTED, LOGLIN_ENOMEM, LOGLIN_ECAPACITY, LOGLIN_EHIP = range(6)
+LOGLIN_F32, LOGLIN_BF16 = 0, 1
+
+_DTYPES = {torch.float32: LOGLIN_F32, torch.bfloat16: LOGLIN_BF16}
+
+
+class LoglinError(RuntimeError):
+    def __init__(self, status: int, message: str):
+        super().__init__(f"{_status_name(status)}: {message}")
+        self.status = status
+
+
+_lib = None
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(
+            f"{_LIB_PATH} is not built; run `python -m log_linear_token_amd.build` "
+            "(or __graft_entry__.build()) first")
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.loglin_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.loglin_fwd_workspace_bytes.restype = sz
+    lib.loglin_fwd_chunked.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, sz, vp]
+    lib.loglin_fwd_chunked.restype = i
+    lib.loglin_fwd_chunked_stages.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp,
+                                              sz, ctypes.c_uint, vp]
+    lib.loglin_fwd_chunked_stages.restype = i
+    lib.loglin_state_init.argtypes = [ctypes.POINTER(vp), i, i, i, i, i, vp]
+    lib.loglin_state_init.restype = i
+    lib.loglin_state_free.argtypes = [vp]
+    lib.loglin_state_free.restype = i
+    lib.loglin_state_load.argtypes = [vp, vp, vp, vp]
+    lib.loglin_state_load.restype = i
+    lib.loglin_state_export.argtypes = [vp, vp, vp, vp]
+    lib.loglin_state_export.restype = i
+    lib.loglin_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, vp]
+    lib.loglin_decode_step.restype = i
+    lib.loglin_debug_level_map.argtypes = [i, vp, vp]
+    lib.loglin_debug_level_map.restype = i
+    lib.loglin_last_error.argtypes = []
+    lib.loglin_last_error.restype = ctypes.c_char_p
+    lib.loglin_status_string.argtypes = [i]
+    lib.loglin_status_string.restype = ctypes.c_char_p
+    _lib = lib
+    return lib
+
+
+def _status_name(s: int) -> str:
+    try:
+        return _load().loglin_status_string(s).decode()
+    except Exception:  # library not loadable: still produce a message
+        return f"status {s}"
+
+
+def loglin_last_error() -> str:
+    return _load().loglin_last_error().decode()
+
+
+def _check(rc: int) -> None:
+    if rc != LOGLIN_OK:
+        raise LoglinError(rc, loglin_last_error())
+
+
+def _stream(t: torch.Tensor):
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def _dev(t: torch.Tensor, name: str, dtype=None, shape=None) -> int:
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must live on the GPU (got {t.device})")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if dtype is not None and t.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype} (got {t.dtype})")
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)} (got {tuple(t.shape)})")
+    return t.data_ptr()
+
+
+# ---------------------------------------------------------------- forward
+
+def loglin_fwd_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, C: int) -> int:
+    n = _load().loglin_fwd_workspace_bytes(B, H, T, dk, dv, C)
+    if n == ctypes.c_size_t(-1).value:
+        raise LoglinError(LOGLIN_EINVAL, loglin_last_error())
+    return n
+
+
+STAGE_CHUNK_STATE, STAGE_SCAN, STAGE_OUTPUT, STAGE_ALL = 1, 2, 4, 7
+
+
+def loglin_fwd_chunked(q, k, v, log_decay, lam, C: int, out=None, workspace=None):
+    """O = (Q K^T (.) M) V for the log-linear mask, chunked on the GPU.
+
+    q, k [B,H,T,dk] and v [B,H,T,dv] (float32 or bfloat16, same dtype);
+    log_decay [B,H,T] float32; lam [B,H,T,L] float32.  Returns out
+    [B,H,T,dv] float32.
+    """
+    return loglin_fwd_chunked_stages(q, k, v, log_decay, lam, C, STAGE_ALL, out, workspace)
+
+
+def loglin_fwd_chunked_stages(q, k, v, log_decay, lam, C: int, stage_mask: int, out=None,
+                              workspace=None):
+    """Profiling variant: enqueue only the kernels selected by stage_mask."""
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"q must be float32 or bfloat16 (got {q.dtype})")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    L = lam.shape[-1]
+    pq = _dev(q, "q", q.dtype)
+    pk = _dev(k, "k", q.dtype, (B, H, T, dk))
+    pv = _dev(v, "v", q.dtype, (B, H, T, dv))
+    pa = _dev(log_decay, "log_decay", torch.float32, (B, H, T))
+    pl = _dev(lam, "lam", torch.float32, (B, H, T, L))
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=torch.float32, device=q.device)
+    po = _dev(out, "out", torch.float32, (B, H, T, dv))
+    need = loglin_fwd_workspace_bytes(B, H, T, dk, dv, C)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    pw = _dev(workspace, "workspace") if workspace is not None else None
+    nws = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_load().loglin_fwd_chunked_stages(pq, pk, pv, pa, pl, po, B, H, T, dk, dv, L, C,
+                                             _DTYPES[q.dtype], pw, nws, stage_mask, _stream(q)))
+    return out
+
+
+# ---------------------------------------------------------------- decode
+
+@dataclass
+class DecodeState:
+    handle: ctypes.c_void_p
+    nseq: int
+    H: int
+    dk: int
+    dv: int
+    Lmax: int
+    device: torch.device
+
+    def __del__(self):
+        if self.handle and _lib is not None:
+            try:
+                _lib.loglin_state_free(self.handle)
+            except Exception:
+                pass
+            self.handle = None
+
+
+def loglin_state_init(nseq: int, H: int, dk: int, dv: int, Lmax: int, device=None) -> DecodeState:
+    device = torch.device(device or "cuda")
+    h = ctypes.c_void_p()
+    s = ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    _check(_load().loglin_state_init(ctypes.byref(h), nseq, H, dk, dv, Lmax, s))
+    return DecodeState(h, nseq, H, dk, dv, Lmax, device)
+
+
+def loglin_state_free(st: DecodeState) -> None:
+    if st.handle:
+        h, st.handle = st.handle, None
+        _check(_load().loglin_state_free(h))
+
+
+def loglin_state_load(st: DecodeState, pos, levels=None) -> None:
+    """pos: next position per sequence (host ints); levels: [nseq,H,Lmax,dk,dv] float32 or None."""
+    p = torch.as_tensor(pos, dtype=torch.int64).contiguous().cpu()
+    if tuple(p.shape) != (st.nseq,):
+        raise ValueError(f"pos must have shape ({st.nseq},)")
+    pl = None
+    if levels is not None:
+        pl = _dev(levels, "levels", torch.float32, (st.nseq, st.H, st.Lmax, st.dk, st.dv))
+    s = ctypes.c_void_p(torch.cuda.current_stream(st.device).cuda_stream)
+    _check(_load().loglin_state_load(st.handle, p.data_ptr(), pl, s))
+
+
+def loglin_state_export(st: DecodeState, levels: bool = True):
+    """Returns (pos int64 host tensor, levels [nseq,H,Lmax,dk,dv] float32 or None)."""
+    pos = torch.empty(st.nseq, dtype=torch.int64)
+    lv = None
+    if levels:
+        lv = torch.empty((st.nseq, st.H, st.Lmax, st.dk, st.dv), dtype=torch.float32,
+                         device=st.device)
+    s = ctypes.c_void_p(torch.cuda.current_stream(st.device).cuda_stream)
+    _check(_load().loglin_state_export(st.handle, pos.data_ptr(),
+                                       lv.data_ptr() if lv is not None else None, s))
+    return pos, lv
+
+
+def loglin_decode_step(st: DecodeState, q, k, v, log_decay, lam, out=None):
+    """One Fenwick step for every (sequence, head); returns out [nseq,H,dv] float32."""
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"q must be float32 or bfloat16 (got {q.dtype})")
+    pq = _dev(q, "q", q.dtype, (st.nseq, st.H, st.dk))
+    pk = _dev(k, "k", q.dtype, (st.nseq, st.H, st.dk))
+    pv = _dev(v, "v", q.dtype, (st.nseq, st.H, st.dv))
+    pa = _dev(log_decay, "log_decay", torch.float32, (st.nseq, st.H))
+    pl = _dev(lam, "lam", torch.float32, (st.nseq, st.H, st.Lmax))
+    if out is None:
+        out = torch.empty((st.nseq, st.H, st.dv), dtype=torch.float32, device=q.device)
+    po = _dev(out, "out", torch.float32, (st.nseq, st.H, st.dv))
+    _check(_load().loglin_decode_step(st.handle, pq, pk, pv, pa, pl, po, _DTYPES[q.dtype],
+                                      _stream(q)))
+    return out
+
+
+def loglin_debug_level_map(T: int, device=None):
+    device = torch.device(device or "cuda")
+    out = torch.empty((T, T), dtype=torch.int8, device=device)
+    s = ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+    _check(_load().loglin_debug_level_map(T, out.data_ptr(), s))
+    return out

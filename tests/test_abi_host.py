@@ -1,0 +1,148 @@
+"""C ABI checks that need no GPU: the library loads, exports every entry point
+the header declares, and rejects bad arguments on the host before any launch."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "loglin.h")
+LIB = os.path.join(ROOT, "log_linear_token_amd", "libloglin.so")
+
+EINVAL, EUNSUPPORTED, ENOMEM, ECAPACITY = 1, 2, 3, 4
+
+
+def _declared():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"LOGLIN_API\s+[\w\s\*]*?\b(loglin_\w+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(LIB):
+        pytest.fail(f"{LIB} missing: build it with python -m log_linear_token_amd.build")
+    lib = ctypes.CDLL(LIB)
+    vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
+    lib.loglin_fwd_workspace_bytes.argtypes = [i] * 6
+    lib.loglin_fwd_workspace_bytes.restype = sz
+    lib.loglin_fwd_chunked.argtypes = [vp] * 6 + [i] * 8 + [vp, sz, vp]
+    lib.loglin_fwd_chunked.restype = i
+    lib.loglin_state_init.argtypes = [ctypes.POINTER(vp), i, i, i, i, i, vp]
+    lib.loglin_state_free.argtypes = [vp]
+    lib.loglin_state_load.argtypes = [vp, vp, vp, vp]
+    lib.loglin_state_export.argtypes = [vp, vp, vp, vp]
+    lib.loglin_decode_step.argtypes = [vp] * 7 + [i, vp]
+    lib.loglin_debug_level_map.argtypes = [i, vp, vp]
+    lib.loglin_last_error.restype = ctypes.c_char_p
+    lib.loglin_status_string.restype = ctypes.c_char_p
+    return lib
+
+
+def test_header_declares_the_entry_points():
+    names = _declared()
+    for n in ["loglin_fwd_chunked", "loglin_fwd_workspace_bytes", "loglin_decode_step",
+              "loglin_state_init", "loglin_state_free", "loglin_state_load",
+              "loglin_state_export", "loglin_debug_level_map", "loglin_last_error"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(lib):
+    for n in _declared():
+        assert hasattr(lib, n), n
+
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def _fwd(lib, B=1, H=1, T=64, dk=16, dv=16, L=8, C=16, dtype=1, ws=None, nws=0, ptrs=None):
+    p = [FAKE] * 6 if ptrs is None else ptrs
+    return lib.loglin_fwd_chunked(*p, B, H, T, dk, dv, L, C, dtype, ws, nws, None)
+
+
+@pytest.mark.parametrize("C", [0, 8, 48, 256])
+def test_unsupported_chunk(lib, C):
+    assert _fwd(lib, C=C) == EUNSUPPORTED
+    assert b"chunk" in lib.loglin_last_error()
+
+
+@pytest.mark.parametrize("dk,dv", [(8, 16), (16, 24), (256, 64), (64, 0)])
+def test_unsupported_head_dims(lib, dk, dv):
+    assert _fwd(lib, dk=dk, dv=dv) == EUNSUPPORTED
+
+
+def test_too_few_levels(lib):
+    # T = 64 uses levels 0..6 -> L >= 7
+    assert _fwd(lib, T=64, L=6, C=64) == EINVAL
+    assert _fwd(lib, T=65, L=7, C=16, ws=None) == EINVAL  # 65 tokens need 8 levels
+    assert _fwd(lib, T=64, L=65, C=64) == EINVAL
+
+
+def test_null_pointer(lib):
+    assert _fwd(lib, C=64, ptrs=[FAKE, None, FAKE, FAKE, FAKE, FAKE]) == EINVAL
+
+
+def test_bad_dtype(lib):
+    assert _fwd(lib, dtype=7) == EINVAL
+
+
+def test_empty_is_noop(lib):
+    assert _fwd(lib, B=0, ptrs=[None] * 6) == 0
+    assert _fwd(lib, T=0, ptrs=[None] * 6) == 0
+    assert _fwd(lib, B=-1) == EINVAL
+
+
+def test_workspace_sizes(lib):
+    w = lib.loglin_fwd_workspace_bytes
+    assert w(1, 1, 64, 16, 16, 64) == 0           # one chunk: no inter-chunk state
+    assert w(1, 1, 64, 16, 16, 16) > 4 * 16 * 16 * 4
+    n = w(2, 3, 1000, 64, 32, 64)                   # 16 chunks, ragged
+    assert n >= 6 * 16 * 64 * 32 * 4 and n % 256 == 0
+    assert w(1, 1, 64, 16, 16, 12) == ctypes.c_size_t(-1).value
+
+
+def test_workspace_too_small(lib):
+    assert _fwd(lib, T=64, C=16, ws=None, nws=0) == EINVAL
+    assert b"workspace" in lib.loglin_last_error()
+    assert _fwd(lib, T=64, C=16, ws=FAKE * 256, nws=16) == EINVAL
+    assert _fwd(lib, T=64, C=16, ws=FAKE + 16, nws=1 << 20) == EINVAL  # misaligned
+
+
+def test_too_many_chunks(lib):
+    assert _fwd(lib, T=16 * 65536 + 16, C=16, L=30) == EUNSUPPORTED
+
+
+def test_state_init_validation(lib):
+    h = ctypes.c_void_p()
+    assert lib.loglin_state_init(None, 1, 1, 16, 16, 8, None) == EINVAL
+    assert lib.loglin_state_init(ctypes.byref(h), 0, 1, 16, 16, 8, None) == EINVAL
+    assert lib.loglin_state_init(ctypes.byref(h), 1, 1, 12, 16, 8, None) == EUNSUPPORTED
+    assert lib.loglin_state_init(ctypes.byref(h), 1, 1, 16, 16, 0, None) == EINVAL
+    assert lib.loglin_state_init(ctypes.byref(h), 1, 1, 16, 16, 49, None) == EINVAL
+    assert not h.value
+
+
+def test_state_init_allocation_failure_is_reported(lib, monkeypatch):
+    monkeypatch.setenv("LOGLIN_TEST_FAIL_ALLOC", "1")
+    h = ctypes.c_void_p()
+    assert lib.loglin_state_init(ctypes.byref(h), 2, 2, 16, 16, 8, None) == ENOMEM
+    assert not h.value
+    assert b"injected" in lib.loglin_last_error()
+
+
+def test_state_calls_reject_null_handle(lib):
+    assert lib.loglin_state_free(None) == 0
+    assert lib.loglin_state_load(None, FAKE, None, None) == EINVAL
+    assert lib.loglin_state_export(None, None, None, None) == EINVAL
+    assert lib.loglin_decode_step(None, *[FAKE] * 6, 1, None) == EINVAL
+
+
+def test_level_map_validation(lib):
+    assert lib.loglin_debug_level_map(0, FAKE, None) == EINVAL
+    assert lib.loglin_debug_level_map(16385, FAKE, None) == EINVAL
+    assert lib.loglin_debug_level_map(8, None, None) == EINVAL
+
+
+def test_status_strings(lib):
+    assert lib.loglin_status_string(0) == b"LOGLIN_OK"
+    assert lib.loglin_status_string(4) == b"LOGLIN_ECAPACITY"

@@ -1,0 +1,234 @@
+"""GPU parity of the chunked forward against the fp64 oracle.
+
+Page: "Log-linear attention, and what a logarithm buys" (sections 1-3).
+Every case prints a banner naming itself before touching the GPU.
+"""
+import numpy as np
+import pytest
+import torch
+
+from log_linear_token_amd import inputs as I
+from log_linear_token_amd import loglin as LL
+from oracle import reference as ref
+from tests.helpers import TOL_BF16, TOL_F32, banner, in_dtype, slice_rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(d, C=None):
+    cfg = d["cfg"]
+    dt = in_dtype(cfg.dtype)
+    q, k, v = to_dev(d["q"], dt), to_dev(d["k"], dt), to_dev(d["v"], dt)
+    a, lam = to_dev(d["a"]), to_dev(d["lam"])
+    out = LL.loglin_fwd_chunked(q, k, v, a, lam, C or cfg.C)
+    torch.cuda.synchronize()
+    return out.cpu().numpy()
+
+
+def _tol(cfg):
+    return TOL_BF16 if cfg.dtype == "bf16" else TOL_F32
+
+
+# ------------------------------------------------------------------ indexing
+
+@pytest.mark.parametrize("T", [1, 2, 7, 64, 1000, 4096])
+def test_level_map_bit_exact(T):
+    banner(f"level_map T={T}")
+    got = LL.loglin_debug_level_map(T).cpu().numpy()
+    assert np.array_equal(got, ref.level_map(T))
+
+
+# ------------------------------------------------------------------ small, full Form A
+
+SMALL = [
+    # (C, T, dk, dv, dtype)
+    (16, 64, 16, 16, "f32"),
+    (16, 100, 32, 16, "f32"),
+    (32, 257, 16, 64, "f32"),
+    (64, 200, 64, 32, "f32"),
+    (128, 300, 128, 128, "f32"),
+    (16, 64, 16, 16, "bf16"),
+    (16, 333, 16, 32, "bf16"),
+    (32, 512, 32, 32, "bf16"),
+    (64, 777, 128, 64, "bf16"),
+    (64, 1024, 64, 128, "bf16"),
+    (128, 1000, 128, 128, "bf16"),
+    (128, 129, 64, 16, "bf16"),
+    (32, 31, 64, 64, "bf16"),
+]
+
+
+@pytest.mark.parametrize("variant", ["base", "unit", "weak"])
+@pytest.mark.parametrize("C,T,dk,dv,dtype", SMALL)
+def test_small_shapes_vs_materialised_mask(C, T, dk, dv, dtype, variant):
+    banner(f"small C={C} T={T} dk={dk} dv={dv} {dtype} {variant}")
+    L = (T - 1).bit_length() + 1 + (1 if T % 3 == 0 else 0)
+    cfg = I.CONFIGS["fwd2k"].scaled(B=2, H=2, T=T, dk=dk, dv=dv, C=C, L=L, dtype=dtype,
+                                    qk="scaled")
+    d = I.make_fwd(cfg, variant, seed=1000 + T + C + dk)
+    got = _run(d)
+    want = ref.form_a(d["q"], d["k"], d["v"], d["a"], d["lam"])
+    err = slice_rel_err(got, want, 2)
+    assert err <= _tol(cfg), err
+
+
+@pytest.mark.parametrize("stage", ["intra_only", "inter_only"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_stage_isolation_unit_decay(stage, dtype):
+    """lambda zero on the coarse levels tests the block diagonal alone; zero on
+    the levels inside a chunk tests the inter-chunk levels alone."""
+    banner(f"stage isolation {stage} {dtype}")
+    C, T = 32, 1024
+    cfg = I.CONFIGS["fwd2k"].scaled(B=1, H=3, T=T, dk=64, dv=32, C=C, L=11, dtype=dtype,
+                                    qk="scaled")
+    d = I.make_fwd(cfg, "unit", seed=77)
+    c = 5  # log2 C
+    if stage == "intra_only":
+        d["lam"][..., c + 1:] = 0.0
+    else:
+        d["lam"][..., : c + 1] = 0.0
+    got = _run(d)
+    want = ref.form_a(d["q"], d["k"], d["v"], d["a"], d["lam"])
+    assert np.max(np.abs(want)) > 1.0
+    err = slice_rel_err(got, want, 2)
+    assert err <= _tol(cfg), err
+
+
+@pytest.mark.parametrize("level", [6, 7, 8, 9, 10])
+def test_one_hot_coarse_level(level):
+    """lambda one-hot on a single coarse level: exactly one Fenwick node per chunk."""
+    banner(f"one-hot level {level}")
+    cfg = I.CONFIGS["tiny"].scaled(B=1, H=2, T=1024, dk=32, dv=32, C=32, L=11)
+    d = I.make_fwd(cfg, "weak", seed=level)
+    d["lam"][:] = 0.0
+    d["lam"][..., level] = 1.0
+    got = _run(d)
+    want = ref.form_a(d["q"], d["k"], d["v"], d["a"], d["lam"])
+    err = slice_rel_err(got, want, 2)
+    assert err <= TOL_F32, err
+
+
+@pytest.mark.parametrize("dtype,T,C", [("f32", 2048, 16), ("bf16", 256, 16), ("bf16", 512, 32)])
+def test_exact_arithmetic_is_bit_exact(dtype, T, C):
+    """No decay, entries in {-1,0,1}, lambda in {0,1/2,1}: every intermediate is
+    exactly representable (bf16 node states stay below 256 in magnitude for
+    these T, C), so the GPU result equals the fp64 result bit for bit."""
+    banner(f"exact arithmetic {dtype} T={T} C={C}")
+    rng = np.random.default_rng(5)
+    B, H, dk, dv = 1, 2, 16, 16
+    L = (T - 1).bit_length() + 1
+    q = rng.integers(-1, 2, (B, H, T, dk)).astype(np.float32)
+    k = rng.integers(-1, 2, (B, H, T, dk)).astype(np.float32)
+    v = rng.integers(-1, 2, (B, H, T, dv)).astype(np.float32)
+    lam = (rng.integers(0, 3, (B, H, T, L)) / 2.0).astype(np.float32)
+    a = np.zeros((B, H, T), np.float32)
+    dt = torch.bfloat16 if dtype == "bf16" else torch.float32
+    out = LL.loglin_fwd_chunked(to_dev(q, dt), to_dev(k, dt), to_dev(v, dt), to_dev(a),
+                                to_dev(lam), C)
+    got = out.cpu().numpy().astype(np.float64)
+    want = ref.form_a(q, k, v, a, lam)
+    assert np.array_equal(got, want), np.max(np.abs(got - want))
+
+
+def test_deterministic():
+    banner("determinism fwd2k")
+    d = I.make_fwd(I.CONFIGS["fwd2k"], "unit")
+    a = _run(d)
+    b = _run(d)
+    assert np.array_equal(a, b)
+
+
+def test_single_token_and_single_chunk():
+    banner("T=1 and T<=C")
+    for T, C in [(1, 16), (16, 16), (5, 128)]:
+        cfg = I.CONFIGS["tiny"].scaled(T=T, C=C, L=max(1, (T - 1).bit_length() + 1))
+        d = I.make_fwd(cfg, "base", seed=T)
+        got = _run(d)
+        want = ref.form_a(d["q"], d["k"], d["v"], d["a"], d["lam"])
+        assert slice_rel_err(got, want, 2) <= TOL_F32
+
+
+def test_empty_sequence_is_noop():
+    q = torch.empty((1, 1, 0, 16), device="cuda")
+    a = torch.empty((1, 1, 0), device="cuda")
+    lam = torch.empty((1, 1, 0, 1), device="cuda")
+    out = LL.loglin_fwd_chunked(q, q, q, a, lam, 16)
+    assert out.shape == (1, 1, 0, 16)
+
+
+def test_rejects_too_few_levels_on_device():
+    cfg = I.CONFIGS["tiny"]
+    d = I.make_fwd(cfg)
+    with pytest.raises(LL.LoglinError) as ei:
+        LL.loglin_fwd_chunked(to_dev(d["q"]), to_dev(d["k"]), to_dev(d["v"]), to_dev(d["a"]),
+                              to_dev(d["lam"][..., :6]), 16)
+    assert ei.value.status == LL.LOGLIN_EINVAL
+
+
+# ------------------------------------------------------------------ the named workloads
+
+@pytest.mark.parametrize("variant", ["base", "unit", "weak"])
+def test_tiny_workload(variant):
+    banner(f"tiny {variant}")
+    d = I.make_fwd(I.CONFIGS["tiny"], variant)
+    got = _run(d)
+    want = ref.form_a(d["q"], d["k"], d["v"], d["a"], d["lam"])
+    np.testing.assert_allclose(ref.form_b(d["q"], d["k"], d["v"], d["a"], d["lam"]), want,
+                               rtol=1e-10, atol=1e-10)
+    assert slice_rel_err(got, want, 2) <= TOL_F32
+
+
+@pytest.mark.parametrize("variant", ["base", "unit", "weak"])
+def test_fwd2k_workload_all_rows(variant):
+    banner(f"fwd2k {variant}")
+    d = I.make_fwd(I.CONFIGS["fwd2k"], variant)
+    got = _run(d)
+    want = ref.form_b(d["q"], d["k"], d["v"], d["a"], d["lam"])
+    assert slice_rel_err(got, want, 2) <= TOL_BF16
+
+
+def _sample_rows(T, C, rng, n=48):
+    rows = {0, 1, T - 1}
+    p = 1
+    while p < T:
+        rows.update({p - 1, p})
+        p *= 2
+    for m in range(C, T, C * max(1, (T // C) // 16)):
+        rows.update({m - 1, m})
+    rows.update(int(x) for x in rng.integers(0, T, n))
+    return sorted(r for r in rows if 0 <= r < T)
+
+
+def _check_big(name, variant, full_slices, row_slices, prefix):
+    cfg = I.CONFIGS[name]
+    banner(f"{name} {variant} (full size)")
+    d = I.make_fwd(cfg, variant)
+    got = _run(d)
+    q, k, v, a, lam = d["q"], d["k"], d["v"], d["a"], d["lam"]
+    errs = []
+    # Form B over a prefix of some slices: every row of that prefix
+    for b, h in full_slices:
+        P = min(prefix, cfg.T)
+        want = ref.form_b(q[b, h, :P], k[b, h, :P], v[b, h, :P], a[b, h, :P], lam[b, h, :P])
+        errs.append(slice_rel_err(got[b, h, :P], want, 0))
+    # Form A on sampled rows of other slices, spanning the whole length
+    rng = np.random.default_rng(99)
+    for b, h in row_slices:
+        rows = _sample_rows(cfg.T, cfg.C, rng)
+        want = ref.form_a_rows(q[b, h], k[b, h], v[b, h], a[b, h], lam[b, h], rows)
+        errs.append(slice_rel_err(got[b, h, rows], want, 0))
+    err = max(errs)
+    print(f"  {name} {variant}: max slice rel err {err:.3e}", flush=True)
+    assert err <= TOL_BF16, errs
+
+
+@pytest.mark.parametrize("variant", ["base", "unit", "weak"])
+def test_fwd8k_workload(variant):
+    _check_big("fwd8k", variant, full_slices=[(0, 0), (3, 15)],
+               row_slices=[(1, 5), (2, 9)], prefix=8192)
+
+
+@pytest.mark.parametrize("variant", ["base", "unit", "weak"])
+def test_long64k_workload(variant):
+    _check_big("long64k", variant, full_slices=[(0, 3)], row_slices=[(0, 0), (0, 15)],
+               prefix=2048)
