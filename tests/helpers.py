@@ -36,5 +36,23 @@ def slice_rel_err(got, ref, lead: int) -> float:
     return float(np.max(num / den))
 
 
+def state_rel_err(got, ref) -> float:
+    """Error of level states [P, L, dk, dv]: per (pair, level) slice, the largest
+    absolute difference over max(largest |ref| in the slice, 1e-6 x the largest
+    |ref| over all levels of that pair).  The floor keeps levels that decay has
+    driven far below fp32 range relative to their siblings (the fp64 oracle
+    keeps 1e-80 where fp32 holds 0) from reading as a 100% error; such a level
+    contributes nothing measurable to any output."""
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape and got.ndim == 4, (got.shape, ref.shape)
+    P, L = ref.shape[:2]
+    r = np.abs(ref).reshape(P, L, -1).max(axis=2)
+    d = np.abs(got - ref).reshape(P, L, -1).max(axis=2)
+    floor = 1e-6 * r.max(axis=1, keepdims=True)
+    den = np.maximum(np.maximum(r, floor), 1e-300)
+    return float(np.max(d / den))
+
+
 def banner(msg: str) -> None:
     print(f"[gpu-case] {msg}", flush=True)

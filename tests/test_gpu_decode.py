@@ -10,7 +10,7 @@ import torch
 from log_linear_token_amd import inputs as I
 from log_linear_token_amd import loglin as LL
 from oracle import reference as ref
-from tests.helpers import TOL_BF16, TOL_F32, banner, slice_rel_err, to_dev
+from tests.helpers import TOL_BF16, TOL_F32, banner, slice_rel_err, state_rel_err, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -43,13 +43,17 @@ def _oracle(d, states_np, pairs, steps):
                       sel(d["lam"]))
 
 
-def _live_mask_ok(levels, pos, Lmax):
+def _live_mask_ok(levels, pos, Lmax, live_nonzero=True):
+    """Exported slots that are not live must be exactly zero; live slots must
+    hold data (checked unless decay may have flushed old levels to zero)."""
     for s, n in enumerate(pos):
         live = set(I.live_levels(int(n)))
         for lv in range(Lmax):
             nz = bool(np.any(levels[s, :, lv] != 0))
-            if nz != (lv in live):
-                return False, (s, int(n), lv)
+            if lv not in live and nz:
+                return False, (s, int(n), lv, "dead slot not zero")
+            if lv in live and live_nonzero and not nz:
+                return False, (s, int(n), lv, "live slot empty")
     return True, None
 
 
@@ -81,7 +85,7 @@ def test_true_prefill_then_decode(dk, dv):
     assert slice_rel_err(got, o_ref.transpose(1, 0, 2), 1) <= TOL_BF16
     assert np.array_equal(pos, pos_ref.reshape(cfg.nseq, cfg.H)[:, 0])
     lv_pairs = lv.reshape(-1, cfg.Lmax, dk, dv)
-    assert slice_rel_err(lv_pairs, st_ref, 2) <= TOL_BF16
+    assert state_rel_err(lv_pairs, st_ref) <= TOL_BF16
     ok, where = _live_mask_ok(lv, pos, cfg.Lmax)
     assert ok, where
 
@@ -120,7 +124,7 @@ def test_synthetic_prefill_reduced():
     o_ref, st_ref, _ = _oracle(d, d["states"], pairs, cfg.steps)
     got = out.reshape(cfg.steps, -1, cfg.dv).transpose(1, 0, 2)
     assert slice_rel_err(got, o_ref.transpose(1, 0, 2), 1) <= TOL_BF16
-    assert slice_rel_err(lv.reshape(-1, cfg.Lmax, cfg.dk, cfg.dv), st_ref, 2) <= TOL_BF16
+    assert state_rel_err(lv.reshape(-1, cfg.Lmax, cfg.dk, cfg.dv), st_ref) <= TOL_BF16
     ok, where = _live_mask_ok(lv, pos, cfg.Lmax)
     assert ok, where
 
@@ -140,11 +144,13 @@ def test_decode_workload_full_size(variant):
     got = np.stack([out[:, s, h] for s, h in pairs], axis=0)
     err_o = slice_rel_err(got, o_ref.transpose(1, 0, 2), 1)
     got_st = np.stack([lv[s, h] for s, h in pairs])
-    err_s = slice_rel_err(got_st, st_ref, 2)
+    err_s = state_rel_err(got_st, st_ref)
     print(f"  decode {variant}: out err {err_o:.3e} state err {err_s:.3e}", flush=True)
     assert err_o <= TOL_BF16 and err_s <= TOL_BF16
     assert np.array_equal(pos, d["pos"] + cfg.steps)
-    ok, where = _live_mask_ok(lv, pos, cfg.Lmax)
+    # with the workload's decay (about e^-180 over 256 steps) the oldest levels
+    # underflow fp32, so only the no-decay variant requires live slots to be nonzero
+    ok, where = _live_mask_ok(lv, pos, cfg.Lmax, live_nonzero=(variant == "unit"))
     assert ok, where
 
 
