@@ -142,6 +142,8 @@ def main() -> int:
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 1 GiB device-to-device copy (for scaling HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py runs on one GPU only: this build has no multi-GPU path "
@@ -151,6 +153,16 @@ def main() -> int:
         print("bench.py needs a GPU", file=sys.stderr)
         return 2
 
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n // 4, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_bytes_read": n, "copy_bytes_written": n, "launches": 3}))
+        return 0
+
     cfg = I.CONFIGS["fwd8k"]
     log(f"generating fwd8k inputs (B={cfg.B} H={cfg.H} T={cfg.T} dk={cfg.dk} dv={cfg.dv})")
     d = I.make_fwd(cfg, "base")
@@ -158,7 +170,7 @@ def main() -> int:
     q, k, v = (dev(d[n], torch.bfloat16) for n in ("q", "k", "v"))
     a, lam = dev(d["a"]), dev(d["lam"])
     out = torch.empty((cfg.B, cfg.H, cfg.T, cfg.dv), device="cuda")
-    ws = torch.empty(LL.loglin_fwd_workspace_bytes(cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv, cfg.C),
+    ws = torch.empty(LL.loglin_fwd_workspace_bytes(cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv, cfg.C, torch.bfloat16),
                      dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
 

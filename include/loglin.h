@@ -54,11 +54,37 @@ typedef enum { LOGLIN_F32 = 0, LOGLIN_BF16 = 1 } loglin_dtype;
 typedef struct loglin_state loglin_state; /* opaque, owned by the library */
 
 /*
- * Bytes of device workspace loglin_fwd_chunked needs for these sizes
- * (0 when T <= C: a single chunk needs no inter-chunk state).  Returns
- * (size_t)-1 for sizes that loglin_fwd_chunked would reject.
+ * Bytes of device workspace loglin_fwd_chunked needs for these sizes and
+ * input dtype (0 when no inter-chunk state is needed).  Returns (size_t)-1
+ * for arguments that loglin_fwd_chunked would reject.
  */
-LOGLIN_API size_t loglin_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int C);
+LOGLIN_API size_t loglin_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int C,
+                                             loglin_dtype in_dtype);
+
+/*
+ * How loglin_fwd_chunked evaluates these sizes (for profiling and sizing).
+ *  path 0, "chunked": three kernels over chunks of C tokens -- chunk states
+ *    (MFMA), a Fenwick scan over chunks (HBM), and a fused intra-chunk plus
+ *    coarse-level output kernel (MFMA).  Used for fp32 inputs.
+ *  path 1, "fused": bf16 inputs.  One block walks a segment of seg_tiles
+ *    64-token tiles in order with the Fenwick levels inside the segment held
+ *    in registers; a segment-state kernel and the Fenwick scan over segments
+ *    supply the coarse_levels levels above the segment.  The output does not
+ *    depend on the tiling: every level of the mask is evaluated exactly, only
+ *    the split between intra-tile blocks and carried states changes.
+ */
+typedef struct {
+    int path;            /* 0 chunked, 1 fused */
+    int tile;            /* tokens per intra block (C, or 64 on the fused path) */
+    int seg_tiles;       /* tiles walked in order by one block (1 on the chunked path) */
+    int nseg;            /* chunks (chunked) or segments (fused) per sequence */
+    int col_block;       /* output columns per block */
+    int coarse_levels;   /* levels carried between chunks / segments through the scan */
+    size_t workspace_bytes;
+} loglin_fwd_plan_t;
+
+LOGLIN_API loglin_status loglin_fwd_plan(int B, int H, int T, int dk, int dv, int C,
+                                         loglin_dtype in_dtype, loglin_fwd_plan_t* out);
 
 /*
  * Chunked forward O = (Q K^T (.) M) V over whole sequences.
@@ -83,8 +109,11 @@ LOGLIN_API size_t loglin_fwd_workspace_bytes(int B, int H, int T, int dk, int dv
  *              bytes, 256-byte aligned (may be NULL when that is 0); its
  *              contents on entry are ignored and on return are unspecified
  * B, H or T equal to 0 is a no-op.  T / C may be at most 65536 chunks.
- * Numerics: in_dtype BF16 feeds bf16 matrix cores with fp32 accumulation;
- * in_dtype F32 uses fp32 matrix cores throughout.
+ * Numerics: in_dtype BF16 feeds bf16 matrix cores with fp32 accumulation
+ * (scores, carried states and V are rounded to bf16 as MFMA operands);
+ * in_dtype F32 uses fp32 matrix cores throughout.  Which kernels run is
+ * reported by loglin_fwd_plan; the environment variable
+ * LOGLIN_FWD_PATH=chunked selects the chunked path for bf16 too.
  */
 LOGLIN_API loglin_status loglin_fwd_chunked(const void* q, const void* k, const void* v,
                                  const float* log_decay, const float* lambda, float* out,

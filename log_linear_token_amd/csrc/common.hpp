@@ -13,6 +13,12 @@ typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 constexpr int kWave = 64;
 
+// Broadcast lane 0's value to the whole wave as a wave-uniform (scalar) value.
+// The builtin works on 32-bit integers, so the float travels as its bits.
+__device__ __forceinline__ float wave_uniform(float x) {
+    return __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(x)));
+}
+
 __device__ __forceinline__ float bf16_to_f32(bf16_t x) {
     return __uint_as_float(static_cast<uint32_t>(x) << 16);
 }

@@ -172,10 +172,10 @@ __global__ __launch_bounds__(256) void k_fenwick_scan(FwdParams p) {
     const int bh = (int)(gid / per4);
     const int e4 = (int)(gid - (long)bh * per4);
     if (bh >= p.BH) return;
-    const int N = p.N;
-    float4* base = reinterpret_cast<float4*>(p.ust) + (size_t)bh * N * per4 + e4;
-    const float* tot = p.tot + (size_t)bh * N;
-    double* cum = p.cum + (size_t)bh * N;
+    const int n = p.nscan;  // nodes produced: 0 .. n-1
+    float4* base = reinterpret_cast<float4*>(p.ust) + (size_t)bh * p.N * per4 + e4;
+    const float* tot = p.tot + (size_t)bh * p.N;
+    double* cum = p.cum + (size_t)bh * p.N;
 
     float4 live[kScanLevels];
     double lcum[kScanLevels];
@@ -187,15 +187,15 @@ __global__ __launch_bounds__(256) void k_fenwick_scan(FwdParams p) {
     float4 ring[kScanDepth];
 #pragma unroll
     for (int d = 0; d < kScanDepth; ++d)
-        ring[d] = d < N ? base[(size_t)d * per4] : make_float4(0.f, 0.f, 0.f, 0.f);
+        ring[d] = d < n ? base[(size_t)d * per4] : make_float4(0.f, 0.f, 0.f, 0.f);
     double c = 0.0;
-    for (int i0 = 0; i0 < N; i0 += kScanDepth) {
+    for (int i0 = 0; i0 < n; i0 += kScanDepth) {
 #pragma unroll
         for (int d = 0; d < kScanDepth; ++d) {
             const int i = i0 + d;
-            if (i < N) {
+            if (i < n) {
                 float4 acc = ring[d];
-                if (i + kScanDepth < N) ring[d] = base[(size_t)(i + kScanDepth) * per4];
+                if (i + kScanDepth < n) ring[d] = base[(size_t)(i + kScanDepth) * per4];
                 c += (double)tot[i];
                 const int j = lssb((uint64_t)i + 1);
 #pragma unroll
@@ -215,7 +215,7 @@ __global__ __launch_bounds__(256) void k_fenwick_scan(FwdParams p) {
                         lcum[q] = c;
                     }
                 }
-                if (i + 1 < N) base[(size_t)i * per4] = acc;
+                base[(size_t)i * per4] = acc;
                 if (e4 == 0) cum[i] = c;
             }
         }
@@ -374,9 +374,8 @@ hipError_t launch_typed(const FwdParams& p, unsigned stages, hipStream_t stream)
         hipLaunchKernelGGL((k_chunk_state<E, C>), dim3(nblk), dim3(256), sm1, stream, p);
     }
     if (p.N > 1 && (stages & kStageScan)) {
-        const long threads = (long)p.BH * (p.dv * p.dk / 4);
-        hipLaunchKernelGGL(k_fenwick_scan, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0,
-                           stream, p);
+        hipError_t err = launch_fenwick_scan(p, stream);
+        if (err != hipSuccess) return err;
     }
     if (!(stages & kStageOutput)) return hipGetLastError();
     const size_t sm3 = output_smem<E, C, DK>(p.dv);
@@ -410,6 +409,14 @@ hipError_t launch_e(const FwdParams& p, unsigned st, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_fenwick_scan(const FwdParams& p, hipStream_t stream) {
+    if (p.nscan <= 0) return hipSuccess;
+    const long threads = (long)p.BH * (p.dv * p.dk / 4);
+    hipLaunchKernelGGL(k_fenwick_scan, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
+                       p);
+    return hipGetLastError();
+}
 
 hipError_t launch_fwd_chunked(const FwdParams& p, bool bf16, unsigned stages, hipStream_t stream) {
     return bf16 ? launch_e<bf16_t>(p, stages, stream) : launch_e<float>(p, stages, stream);

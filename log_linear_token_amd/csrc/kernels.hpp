@@ -6,6 +6,8 @@
 
 namespace loglin {
 
+typedef unsigned short bf16_t_storage;  // raw bf16 bits (same as bf16_t)
+
 struct FwdParams {
     const void* q;       // [BH][T][dk]
     const void* k;       // [BH][T][dk]
@@ -13,7 +15,8 @@ struct FwdParams {
     const float* a;      // [BH][T]
     const float* lam;    // [BH][T][L]
     float* out;          // [BH][T][dv]
-    int BH, T, dk, dv, L, C, N;  // N = ceil(T / C)
+    int BH, T, dk, dv, L, C, N;  // N = ceil(T / C): chunks per sequence (state stride)
+    int nscan;           // Fenwick nodes the scan produces per sequence (N - 1)
     float* ust;          // workspace [BH][N][dv][dk]
     float* tot;          // workspace [BH][N]
     double* cum;         // workspace [BH][N]
@@ -27,6 +30,32 @@ FwdWorkspace fwd_workspace_layout(long BH, long N, int dk, int dv);
 
 enum : unsigned { kStageChunkState = 1u, kStageScan = 2u, kStageOutput = 4u, kStageAll = 7u };
 hipError_t launch_fwd_chunked(const FwdParams& p, bool bf16, unsigned stages, hipStream_t stream);
+// the Fenwick node scan over chunk (or segment) states, in place
+hipError_t launch_fenwick_scan(const FwdParams& p, hipStream_t stream);
+
+// Fused tile-recurrent forward (bf16 inputs): 64-token tiles, segments of
+// 2^m tiles per block, Fenwick levels inside a segment held in registers.
+constexpr int kMaxLocal = 5;  // register-resident levels per block
+struct FusedParams {
+    const bf16_t_storage* q;
+    const bf16_t_storage* k;
+    const bf16_t_storage* v;
+    const float* a;
+    const float* lam;
+    float* out;
+    int BH, T, dk, dv, L, LU;  // LU: levels the sequence uses (staged per token)
+    int ntiles, m, nseg, ntop, dvw, ndvb;
+    float* useg;   // [BH][nseg][dv][dk] segment states, then Fenwick nodes over segments
+    float* stot;   // [BH][nseg]
+    double* scum;  // [BH][nseg]
+};
+struct FusedPlan {
+    int ok, m, nseg, ntop, dvw, ndvb, ntiles, lds_main, lds_seg;
+};
+// force_m >= 0 asks for segments of 2^force_m tiles (plan fails if that does not fit)
+FusedPlan plan_fused(int BH, int T, int dk, int dv, int lu, int force_m);
+hipError_t launch_fused_fwd(const FusedParams& p, const FwdParams& scan, unsigned stages,
+                            int lds_main, int lds_seg, hipStream_t stream);
 
 struct DecodeParams {
     float* states;            // [nseq][H][Lmax][dk][dv]

@@ -85,6 +85,53 @@ FwdWorkspace fwd_workspace_layout(long BH, long N, int dk, int dv) {
 }
 }  // namespace loglin
 
+namespace {
+
+enum Path { kPathChunked = 0, kPathFused = 1 };
+
+// LOGLIN_FWD_PATH=chunked forces the three-kernel chunked path for bf16
+// inputs as well (the fused path is the default where it applies).
+bool force_chunked() {
+    const char* e = getenv("LOGLIN_FWD_PATH");
+    return e && strcmp(e, "chunked") == 0;
+}
+
+// LOGLIN_FUSED_SEGMENT=<tiles> (a power of two, 1..32) fixes the fused path's
+// segment length; -1 when unset (the planner chooses).
+int forced_segment_log2() {
+    const char* e = getenv("LOGLIN_FUSED_SEGMENT");
+    if (!e || !*e) return -1;
+    const long n = strtol(e, nullptr, 10);
+    for (int m = 0; m <= 5; ++m)
+        if (n == (1L << m)) return m;
+    return -1;
+}
+
+struct Plan {
+    Path path;
+    FusedPlan fused;
+    FwdWorkspace ws;  // layout of the workspace (chunked: per chunk; fused: per segment)
+    long N;           // chunks (chunked) or segments (fused) per sequence
+};
+
+Plan make_plan(long BH, int T, int dk, int dv, int C, loglin_dtype dt) {
+    Plan pl{};
+    pl.path = kPathChunked;
+    pl.N = ((long)T + C - 1) / C;
+    if (dt == LOGLIN_BF16 && !force_chunked() && T > 0 && BH > 0) {
+        FusedPlan f = plan_fused((int)BH, T, dk, dv, levels_needed(T), forced_segment_log2());
+        if (f.ok) {
+            pl.path = kPathFused;
+            pl.fused = f;
+            pl.N = f.nseg;
+        }
+    }
+    pl.ws = fwd_workspace_layout(BH, pl.N, dk, dv);
+    return pl;
+}
+
+}  // namespace
+
 extern "C" {
 
 const char* loglin_last_error(void) { return g_err; }
@@ -101,10 +148,42 @@ const char* loglin_status_string(loglin_status s) {
     return "LOGLIN_<unknown>";
 }
 
-size_t loglin_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int C) {
+size_t loglin_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int C, loglin_dtype in_dtype) {
     if (check_fwd_sizes(B, H, T, dk, dv, C) != LOGLIN_OK) return (size_t)-1;
-    const long N = ((long)T + C - 1) / C;
-    return fwd_workspace_layout((long)B * H, N, dk, dv).total;
+    if (in_dtype != LOGLIN_F32 && in_dtype != LOGLIN_BF16) {
+        fail(LOGLIN_EINVAL, "in_dtype %d is neither LOGLIN_F32 nor LOGLIN_BF16", (int)in_dtype);
+        return (size_t)-1;
+    }
+    return make_plan((long)B * H, T, dk, dv, C, in_dtype).ws.total;
+}
+
+loglin_status loglin_fwd_plan(int B, int H, int T, int dk, int dv, int C, loglin_dtype in_dtype,
+                              loglin_fwd_plan_t* out) {
+    if (!out) return fail(LOGLIN_EINVAL, "null plan pointer");
+    loglin_status s = check_fwd_sizes(B, H, T, dk, dv, C);
+    if (s != LOGLIN_OK) return s;
+    if (in_dtype != LOGLIN_F32 && in_dtype != LOGLIN_BF16)
+        return fail(LOGLIN_EINVAL, "in_dtype %d is neither LOGLIN_F32 nor LOGLIN_BF16", (int)in_dtype);
+    const Plan pl = make_plan((long)B * H, T, dk, dv, C, in_dtype);
+    loglin_fwd_plan_t r{};
+    r.path = pl.path;
+    r.workspace_bytes = pl.ws.total;
+    if (pl.path == kPathFused) {
+        r.tile = 64;
+        r.seg_tiles = 1 << pl.fused.m;
+        r.nseg = pl.fused.nseg;
+        r.col_block = pl.fused.dvw;
+        r.coarse_levels = pl.fused.ntop;
+    } else {
+        r.tile = C;
+        r.seg_tiles = 1;
+        r.nseg = (int)pl.N;
+        r.col_block = dv;
+        r.coarse_levels = 0;
+        while ((1L << r.coarse_levels) < pl.N) ++r.coarse_levels;
+    }
+    *out = r;
+    return ok();
 }
 
 loglin_status loglin_fwd_chunked_stages(const void* q, const void* k, const void* v,
@@ -123,9 +202,9 @@ loglin_status loglin_fwd_chunked_stages(const void* q, const void* k, const void
         return fail(LOGLIN_EINVAL, "L=%d: T=%d needs %d levels (and L <= 64)", L, T, levels_needed(T));
     if (!q || !k || !v || !log_decay || !lambda || !out)
         return fail(LOGLIN_EINVAL, "null tensor pointer");
-    const long N = ((long)T + C - 1) / C;
     const long BH = (long)B * H;
-    const FwdWorkspace w = fwd_workspace_layout(BH, N, dk, dv);
+    const Plan pl = make_plan(BH, T, dk, dv, C, in_dtype);
+    const FwdWorkspace& w = pl.ws;
     if (w.total > 0) {
         if (!workspace || workspace_bytes < w.total)
             return fail(LOGLIN_EINVAL, "workspace of %zu bytes needed, got %zu%s", w.total,
@@ -133,12 +212,11 @@ loglin_status loglin_fwd_chunked_stages(const void* q, const void* k, const void
         if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
             return fail(LOGLIN_EINVAL, "workspace must be %zu-byte aligned", kAlign);
     }
-    const size_t esz = in_dtype == LOGLIN_BF16 ? 2 : 4;
     if (reinterpret_cast<uintptr_t>(q) % 16 || reinterpret_cast<uintptr_t>(k) % 16 ||
         reinterpret_cast<uintptr_t>(v) % 16 || reinterpret_cast<uintptr_t>(out) % 16)
         return fail(LOGLIN_EINVAL, "q, k, v and out must be 16-byte aligned");
-    (void)esz;
 
+    // the chunk (or segment) state buffers, shared by both paths' scan
     FwdParams p{};
     p.q = q;
     p.k = k;
@@ -152,15 +230,44 @@ loglin_status loglin_fwd_chunked_stages(const void* q, const void* k, const void
     p.dv = dv;
     p.L = L;
     p.C = C;
-    p.N = (int)N;
+    p.N = (int)pl.N;
+    p.nscan = (int)pl.N - 1;
     if (w.total > 0) {
         char* base = static_cast<char*>(workspace);
         p.ust = reinterpret_cast<float*>(base + w.ust_off);
         p.tot = reinterpret_cast<float*>(base + w.tot_off);
         p.cum = reinterpret_cast<double*>(base + w.cum_off);
     }
-    hipError_t e = launch_fwd_chunked(p, in_dtype == LOGLIN_BF16, stage_mask,
-                                      static_cast<hipStream_t>(stream));
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (pl.path == kPathFused) {
+        const FusedPlan& f = pl.fused;
+        FusedParams fp{};
+        fp.q = static_cast<const bf16_t_storage*>(q);
+        fp.k = static_cast<const bf16_t_storage*>(k);
+        fp.v = static_cast<const bf16_t_storage*>(v);
+        fp.a = log_decay;
+        fp.lam = lambda;
+        fp.out = out;
+        fp.BH = (int)BH;
+        fp.T = T;
+        fp.dk = dk;
+        fp.dv = dv;
+        fp.L = L;
+        fp.LU = levels_needed(T);
+        fp.ntiles = f.ntiles;
+        fp.m = f.m;
+        fp.nseg = f.nseg;
+        fp.ntop = f.ntop;
+        fp.dvw = f.dvw;
+        fp.ndvb = f.ndvb;
+        fp.useg = p.ust;
+        fp.stot = p.tot;
+        fp.scum = p.cum;
+        e = launch_fused_fwd(fp, p, stage_mask, f.lds_main, f.lds_seg, hs);
+    } else {
+        e = launch_fwd_chunked(p, in_dtype == LOGLIN_BF16, stage_mask, hs);
+    }
     if (e != hipSuccess) return hip_fail(e, "loglin_fwd_chunked launch");
     return ok();
 }

@@ -29,6 +29,17 @@ class LoglinError(RuntimeError):
         self.status = status
 
 
+class FwdPlan(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int), ("tile", ctypes.c_int), ("seg_tiles", ctypes.c_int),
+                ("nseg", ctypes.c_int), ("col_block", ctypes.c_int),
+                ("coarse_levels", ctypes.c_int), ("workspace_bytes", ctypes.c_size_t)]
+
+    def as_dict(self) -> dict:
+        d = {n: getattr(self, n) for n, _ in self._fields_}
+        d["path"] = {0: "chunked", 1: "fused"}.get(self.path, str(self.path))
+        return d
+
+
 _lib = None
 
 
@@ -46,13 +57,15 @@ def _load():
             "(or __graft_entry__.build()) first")
     lib = ctypes.CDLL(_LIB_PATH)
     vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
-    lib.loglin_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.loglin_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
     lib.loglin_fwd_workspace_bytes.restype = sz
     lib.loglin_fwd_chunked.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp, sz, vp]
     lib.loglin_fwd_chunked.restype = i
     lib.loglin_fwd_chunked_stages.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp,
                                               sz, ctypes.c_uint, vp]
     lib.loglin_fwd_chunked_stages.restype = i
+    lib.loglin_fwd_plan.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(FwdPlan)]
+    lib.loglin_fwd_plan.restype = i
     lib.loglin_state_init.argtypes = [ctypes.POINTER(vp), i, i, i, i, i, vp]
     lib.loglin_state_init.restype = i
     lib.loglin_state_free.argtypes = [vp]
@@ -109,11 +122,26 @@ def _dev(t: torch.Tensor, name: str, dtype=None, shape=None) -> int:
 
 # ---------------------------------------------------------------- forward
 
-def loglin_fwd_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, C: int) -> int:
-    n = _load().loglin_fwd_workspace_bytes(B, H, T, dk, dv, C)
+def _dt_code(dtype) -> int:
+    if isinstance(dtype, int):
+        return dtype
+    if dtype not in _DTYPES:
+        raise ValueError(f"dtype must be torch.float32 or torch.bfloat16 (got {dtype})")
+    return _DTYPES[dtype]
+
+
+def loglin_fwd_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, C: int,
+                               dtype=torch.bfloat16) -> int:
+    n = _load().loglin_fwd_workspace_bytes(B, H, T, dk, dv, C, _dt_code(dtype))
     if n == ctypes.c_size_t(-1).value:
         raise LoglinError(LOGLIN_EINVAL, loglin_last_error())
     return n
+
+
+def loglin_fwd_plan(B: int, H: int, T: int, dk: int, dv: int, C: int, dtype=torch.bfloat16) -> dict:
+    pl = FwdPlan()
+    _check(_load().loglin_fwd_plan(B, H, T, dk, dv, C, _dt_code(dtype), ctypes.byref(pl)))
+    return pl.as_dict()
 
 
 STAGE_CHUNK_STATE, STAGE_SCAN, STAGE_OUTPUT, STAGE_ALL = 1, 2, 4, 7
@@ -145,7 +173,7 @@ def loglin_fwd_chunked_stages(q, k, v, log_decay, lam, C: int, stage_mask: int, 
     if out is None:
         out = torch.empty((B, H, T, dv), dtype=torch.float32, device=q.device)
     po = _dev(out, "out", torch.float32, (B, H, T, dv))
-    need = loglin_fwd_workspace_bytes(B, H, T, dk, dv, C)
+    need = loglin_fwd_workspace_bytes(B, H, T, dk, dv, C, q.dtype)
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
     pw = _dev(workspace, "workspace") if workspace is not None else None

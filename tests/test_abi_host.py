@@ -24,10 +24,11 @@ def lib():
         pytest.fail(f"{LIB} missing: build it with python -m log_linear_token_amd.build")
     lib = ctypes.CDLL(LIB)
     vp, i, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t
-    lib.loglin_fwd_workspace_bytes.argtypes = [i] * 6
+    lib.loglin_fwd_workspace_bytes.argtypes = [i] * 7
     lib.loglin_fwd_workspace_bytes.restype = sz
     lib.loglin_fwd_chunked.argtypes = [vp] * 6 + [i] * 8 + [vp, sz, vp]
     lib.loglin_fwd_chunked.restype = i
+    lib.loglin_fwd_plan.argtypes = [i] * 7 + [vp]
     lib.loglin_state_init.argtypes = [ctypes.POINTER(vp), i, i, i, i, i, vp]
     lib.loglin_state_free.argtypes = [vp]
     lib.loglin_state_load.argtypes = [vp, vp, vp, vp]
@@ -93,19 +94,56 @@ def test_empty_is_noop(lib):
 
 
 def test_workspace_sizes(lib):
-    w = lib.loglin_fwd_workspace_bytes
+    w = lambda *a: lib.loglin_fwd_workspace_bytes(*a, 0)  # noqa: E731  (fp32: chunked path)
     assert w(1, 1, 64, 16, 16, 64) == 0           # one chunk: no inter-chunk state
     assert w(1, 1, 64, 16, 16, 16) > 4 * 16 * 16 * 4
     n = w(2, 3, 1000, 64, 32, 64)                   # 16 chunks, ragged
     assert n >= 6 * 16 * 64 * 32 * 4 and n % 256 == 0
     assert w(1, 1, 64, 16, 16, 12) == ctypes.c_size_t(-1).value
+    assert lib.loglin_fwd_workspace_bytes(1, 1, 64, 16, 16, 16, 5) == ctypes.c_size_t(-1).value
+    # bf16: fused path, one state per segment instead of one per chunk
+    nb = lib.loglin_fwd_workspace_bytes(4, 16, 8192, 128, 64, 64, 1)
+    nf = lib.loglin_fwd_workspace_bytes(4, 16, 8192, 128, 64, 64, 0)
+    assert 0 < nb < nf
+
+
+class Plan(ctypes.Structure):
+    _fields_ = [("path", ctypes.c_int), ("tile", ctypes.c_int), ("seg_tiles", ctypes.c_int),
+                ("nseg", ctypes.c_int), ("col_block", ctypes.c_int),
+                ("coarse_levels", ctypes.c_int), ("workspace_bytes", ctypes.c_size_t)]
+
+
+@pytest.mark.parametrize("B,H,T,dk,dv,C", [(4, 16, 8192, 128, 64, 64), (1, 16, 65536, 128, 128, 128),
+                                           (2, 8, 2048, 64, 64, 64), (1, 1, 64, 16, 16, 16),
+                                           (1, 1, 1, 16, 16, 16), (3, 5, 1000, 32, 16, 32)])
+def test_plan(lib, B, H, T, dk, dv, C):
+    pl = Plan()
+    assert lib.loglin_fwd_plan(B, H, T, dk, dv, C, 1, ctypes.byref(pl)) == 0
+    assert pl.path == 1 and pl.tile == 64
+    ntiles = -(-T // 64)
+    assert pl.nseg == -(-ntiles // pl.seg_tiles)
+    assert (1 << pl.coarse_levels) >= pl.nseg > (1 << pl.coarse_levels) // 2 or pl.nseg == 1
+    assert pl.col_block == min(dv, 64)
+    assert pl.workspace_bytes == lib.loglin_fwd_workspace_bytes(B, H, T, dk, dv, C, 1)
+    assert lib.loglin_fwd_plan(B, H, T, dk, dv, C, 0, ctypes.byref(pl)) == 0
+    assert pl.path == 0 and pl.tile == C and pl.nseg == -(-T // C)
+
+
+def test_plan_env_forces_chunked(lib, monkeypatch):
+    monkeypatch.setenv("LOGLIN_FWD_PATH", "chunked")
+    pl = Plan()
+    assert lib.loglin_fwd_plan(4, 16, 8192, 128, 64, 64, 1, ctypes.byref(pl)) == 0
+    assert pl.path == 0 and pl.nseg == 128
 
 
 def test_workspace_too_small(lib):
-    assert _fwd(lib, T=64, C=16, ws=None, nws=0) == EINVAL
+    # fp32 inputs take the chunked path: 4 chunks of 16 need chunk states
+    assert _fwd(lib, T=64, C=16, dtype=0, ws=None, nws=0) == EINVAL
     assert b"workspace" in lib.loglin_last_error()
-    assert _fwd(lib, T=64, C=16, ws=FAKE * 256, nws=16) == EINVAL
-    assert _fwd(lib, T=64, C=16, ws=FAKE + 16, nws=1 << 20) == EINVAL  # misaligned
+    assert _fwd(lib, T=64, C=16, dtype=0, ws=FAKE * 256, nws=16) == EINVAL
+    assert _fwd(lib, T=64, C=16, dtype=0, ws=FAKE + 16, nws=1 << 20) == EINVAL  # misaligned
+    # bf16: 1024 tokens make 16 tiles; with 16 heads the fused path uses segments
+    assert _fwd(lib, B=1, H=16, T=1024, dk=64, dv=64, L=11, C=64, dtype=1, ws=None) == EINVAL
 
 
 def test_too_many_chunks(lib):

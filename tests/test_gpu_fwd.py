@@ -72,6 +72,48 @@ def test_small_shapes_vs_materialised_mask(C, T, dk, dv, dtype, variant):
     assert err <= _tol(cfg), err
 
 
+FUSED = [
+    # (T, dk, dv, segment tiles): register-resident levels, scanned levels, both
+    (1000, 128, 64, 1), (1000, 128, 64, 4), (1000, 128, 64, 16), (2048, 128, 64, 32),
+    (4096, 128, 128, 8), (777, 64, 64, 2), (3000, 32, 16, 8), (513, 16, 32, 4),
+    (64, 128, 64, 1), (65, 64, 64, 2), (4096, 64, 32, 32),
+]
+
+
+@pytest.mark.parametrize("variant", ["unit", "weak", "base"])
+@pytest.mark.parametrize("T,dk,dv,seg", FUSED)
+def test_fused_segments_vs_materialised_mask(T, dk, dv, seg, variant, monkeypatch):
+    """bf16 fused path with a fixed segment length: levels inside a segment are
+    carried in registers, the ones above come from the segment scan."""
+    banner(f"fused T={T} dk={dk} dv={dv} seg={seg} {variant}")
+    monkeypatch.setenv("LOGLIN_FUSED_SEGMENT", str(seg))
+    L = (T - 1).bit_length() + 1
+    cfg = I.CONFIGS["fwd2k"].scaled(B=1, H=2, T=T, dk=dk, dv=dv, C=64, L=L, qk="scaled")
+    plan = LL.loglin_fwd_plan(1, 2, T, dk, dv, 64)
+    assert plan["path"] == "fused" and plan["seg_tiles"] == seg, plan
+    d = I.make_fwd(cfg, variant, seed=T + dk + seg)
+    got = _run(d)
+    want = ref.form_a(d["q"], d["k"], d["v"], d["a"], d["lam"])
+    err = slice_rel_err(got, want, 2)
+    assert err <= TOL_BF16, err
+
+
+@pytest.mark.parametrize("C,T,dk,dv", [(16, 333, 16, 32), (64, 777, 128, 64), (128, 1000, 128, 128),
+                                       (32, 31, 64, 64)])
+def test_chunked_path_bf16(C, T, dk, dv, monkeypatch):
+    """The three-kernel chunked path also serves bf16 inputs when selected."""
+    banner(f"chunked path bf16 C={C} T={T}")
+    monkeypatch.setenv("LOGLIN_FWD_PATH", "chunked")
+    assert LL.loglin_fwd_plan(2, 2, T, dk, dv, C)["path"] == "chunked"
+    L = (T - 1).bit_length() + 1
+    cfg = I.CONFIGS["fwd2k"].scaled(B=2, H=2, T=T, dk=dk, dv=dv, C=C, L=L, qk="scaled")
+    for variant in ("unit", "weak"):
+        d = I.make_fwd(cfg, variant, seed=T + C)
+        got = _run(d)
+        want = ref.form_a(d["q"], d["k"], d["v"], d["a"], d["lam"])
+        assert slice_rel_err(got, want, 2) <= TOL_BF16
+
+
 @pytest.mark.parametrize("stage", ["intra_only", "inter_only"])
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 def test_stage_isolation_unit_decay(stage, dtype):
