@@ -55,29 +55,60 @@ def timed(fn, reps: int, stream) -> float:
 
 # --------------------------------------------------------------------- byte and flop models
 
-def fwd_models(cfg) -> dict:
-    """Algorithmic bytes / flops per launch of each forward kernel (bf16 inputs)."""
-    B, H, T, dk, dv, C, L = cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv, cfg.C, cfg.L
+def _causal_blocks(c: int) -> int:
+    """16 x 16 blocks on or below the diagonal of a c x c causal tile."""
+    nb = c // 16
+    return nb * (nb + 1) // 2
+
+
+def fwd_models(cfg, plan) -> dict:
+    """Algorithmic bytes and flops per launch of each forward kernel.
+
+    Bytes count what each kernel must move at least once: its inputs read
+    once, its outputs written once, and every distinct carried state it reads
+    or writes once (fp32 d_k x d_v).  Flops count the MFMA work of the causal
+    16 x 16 blocks of each intra tile, the tile (or chunk) states, and one
+    d_k x d_v product per row per coarse level read.  bf16 inputs.
+    """
+    B, H, T, dk, dv, L = cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv, cfg.L
     BH = B * H
-    N = -(-T // C)
-    st = dk * dv * 4                      # one fp32 state
-    qk = BH * T * dk * 2
-    vv = BH * T * dv * 2
-    a = BH * T * 4
-    lam = BH * T * L * 4
-    o = BH * T * dv * 4
-    nodes = BH * (N - 1) * st             # distinct Fenwick nodes ever read
-    nw = C // 16
-    tiles = nw * (nw + 1) // 2            # causal 16 x 16 tiles per chunk
-    intra_flops = BH * N * tiles * 2 * 16 * 16 * (dk + dv)
+    lu = (T - 1).bit_length() + 1          # levels the sequence uses
+    st = dk * dv * 4
+    tok_in = 2 * (2 * dk + dv) + 4 + 4 * lu  # q, k, v bf16 + a + lambda per token-head
+    tok_out = 4 * dv
+    tile = plan["tile"]
+    ntiles = -(-T // tile)
+    nseg = plan["nseg"]
+    intra = _causal_blocks(tile) * 2 * 16 * 16 * (dk + dv)
+    if plan["path"] == "fused":
+        segt = plan["seg_tiles"]
+        tiles_pre = min(ntiles, (nseg - 1) * segt)   # tiles before the last segment
+        # per segment: tile states folded inside it, local levels read, top levels read
+        local_reads = 0
+        top_reads = 0
+        states = 0
+        for s in range(nseg):
+            n = min(segt, ntiles - s * segt)
+            local_reads += sum(bin(il).count("1") for il in range(n))
+            top_reads += n * bin(s).count("1")
+            states += n - 1
+        return {
+            "seg_state": {"bytes": BH * tiles_pre * tile * (2 * (dk + dv) + 4)
+                          + BH * (nseg - 1) * (st + 4),
+                          "flops": BH * tiles_pre * tile * 2 * dk * dv},
+            "fenwick_scan": {"bytes": BH * (nseg - 1) * (2 * st + 4 + 8), "flops": 0},
+            "fused_fwd": {"bytes": BH * T * (tok_in + tok_out) + BH * (nseg - 1) * (st + 8),
+                          "flops": BH * (ntiles * intra + (states + local_reads + top_reads)
+                                         * tile * 2 * dk * dv)},
+        }
+    N = ntiles
     pops = sum(bin(i).count("1") for i in range(N))
-    inter_flops = BH * pops * 2 * C * dk * dv
-    state_flops = BH * N * 2 * C * dk * dv
     return {
-        "chunk_state": {"bytes": qk + vv + a + BH * N * (st + 4), "flops": state_flops},
-        "fenwick_scan": {"bytes": BH * N * (st + 4) + nodes + BH * N * 8, "flops": 0},
-        "chunk_output": {"bytes": 2 * qk + vv + a + lam + nodes + BH * N * 8 + o,
-                         "flops": intra_flops + inter_flops},
+        "chunk_state": {"bytes": BH * T * (2 * (dk + dv) + 4) + BH * N * (st + 4),
+                        "flops": BH * N * tile * 2 * dk * dv},
+        "fenwick_scan": {"bytes": BH * (N - 1) * (2 * st + 4 + 8), "flops": 0},
+        "chunk_output": {"bytes": BH * T * (tok_in + tok_out) + BH * (N - 1) * (st + 8),
+                         "flops": BH * (N * intra + pops * tile * 2 * dk * dv)},
     }
 
 
@@ -189,10 +220,12 @@ def main() -> int:
     log(f"forward: {ms:.3f} ms/step ({value:.3e} tokens/s; wall {wall:.2f} s)")
 
     # per-kernel timing, each launched alone on the same stream
-    models = fwd_models(cfg)
+    plan = LL.loglin_fwd_plan(cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv, cfg.C, torch.bfloat16)
+    log(f"plan: {plan}")
+    models = fwd_models(cfg, plan)
+    names = list(models)  # kernel names in launch order
     kernels = {}
-    for name, mask in (("chunk_state", LL.STAGE_CHUNK_STATE), ("fenwick_scan", LL.STAGE_SCAN),
-                       ("chunk_output", LL.STAGE_OUTPUT)):
+    for name, mask in zip(names, (LL.STAGE_CHUNK_STATE, LL.STAGE_SCAN, LL.STAGE_OUTPUT)):
         fwd(mask)
         kms = timed(lambda: fwd(mask), max(5, args.steps), stream)
         m = models[name]
@@ -206,7 +239,9 @@ def main() -> int:
     km = kernels[dom]
     roof = {"kernel": dom, "bound": "hbm", "achieved": round(km["GB/s"], 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(km["GB/s"] / HBM_PEAK_GBS, 4),
-            "traffic": None}
+            "traffic": None,
+            "mfma": {"achieved": round(km["TFLOP/s"], 2), "peak": BF16_PEAK_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(km["TFLOP/s"] / BF16_PEAK_TFLOPS, 4)}}
 
     result = {
         "metric": "fwd tokens/s + MFMA util, log-linear mixer T=8192; decode steps/s",
@@ -218,7 +253,7 @@ def main() -> int:
         "roofline": roof,
         "kernels": {n: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
                         for kk, vv in m.items()} for n, m in kernels.items()},
-        "mfma_util_chunk_output": round(kernels["chunk_output"]["TFLOP/s"] / BF16_PEAK_TFLOPS, 4),
+        "plan": plan,
     }
     del q, k, v, a, lam, out, ws
     torch.cuda.empty_cache()
