@@ -1,27 +1,35 @@
 // Fused chunked forward of the log-linear token mixer for bf16 inputs (gfx950).
 //
 // The chunked form of "Log-linear attention, and what a logarithm buys"
-// (section 3) evaluated with the Fenwick states held in registers: one block
-// walks the 64-token tiles of a segment in order, and for every tile
-//   - the intra-tile block: S^T = K Q^T on MFMA, masked in registers with
-//     lambda_t^(level(t,s)) e^(A_t - A_s), stored to LDS as bf16 P, then
-//     O^T = V^T P^T on MFMA;
-//   - the coarse levels: for each set bit of the tile index a state G holding
-//     the decayed sum of k v^T over the matching block of earlier tiles,
-//     read with one MFMA per row block and weighted per row by
+// (section 3) evaluated with the Fenwick states held in registers.  The
+// sequence is cut into 64-token tiles and the tiles into segments of 2^m
+// tiles; one block walks the tiles of one segment in order and, per tile,
+//   - the intra-tile block: S^T = K Q^T on MFMA, weighted in registers by
+//     lambda_t^(level(t,s)) e^(A_t - A_s) for s <= t, stored to LDS as bf16 P,
+//     then O^T = V^T P^T on MFMA;
+//   - the levels above the tile: for each set bit of the tile index a state G
+//     holding the decayed sum of k v^T over the matching block of earlier
+//     tiles, read as G^T Q^T on MFMA and weighted per row by
 //     lambda_t^(level) e^(A_t - A_end(block));
-//   - the tile's own state U = K^T diag(e^(A_end - A_s)) V (MFMA), which the
-//     Fenwick update of section 2, run over tiles, folds together with the
-//     states of the levels below lssb(tile+1) into the next level.
-// Levels inside the segment (up to kMaxLocal) live in registers as fp32 MFMA
-// accumulators and never touch memory.  The levels above the segment are the
-// same for all of its tiles; they come from two small launches before the main
-// one: seg_state (the decayed state of every segment but the last) and the
-// Fenwick scan over segments (fenwick_scan in fwd_chunked.hip), and sit in LDS
-// as bf16 MFMA operands.
+//   - the tile's own state U = K^T diag(e^(A_end - A_s)) V (MFMA), folded by
+//     the Fenwick update of section 2, run over tiles, together with the
+//     levels below lssb(tile + 1) into the next level.
+// Levels inside the segment live in registers as fp32 MFMA accumulators.
+// The levels above the segment are the same for all of its tiles; a
+// segment-state kernel (k_seg_state) and the Fenwick scan over segments
+// (fenwick_scan in fwd_chunked.hip) provide them as bf16 MFMA operand
+// fragments, which the main kernel loads into registers once per block.
 //
-// One wave owns 16 columns of d_v and computes them for all 64 rows of a tile;
-// the waves of a block share the tile's Q, K, V^T, P and lambda through LDS.
+// Data movement: Q, K, V (and lambda, a where aligned) of the next tile are
+// copied global -> LDS by the LDS-DMA path (global_load_lds_dwordx4) while the
+// current tile is computed (two buffers, kept in distinct __shared__ arrays so
+// that the compiler's alias analysis does not serialise the copies).  Tiles
+// are stored row-major with an XOR swizzle of their 16-byte chunks; operands
+// that contract over tokens (V^T for P V, K^T and V for the tile state) are
+// read with the LDS transpose read (ds_read_b64_tr_b16), so no transposed
+// copy is ever written.
+//
+// One wave owns 16 columns of d_v and computes them for all 64 rows of a tile.
 #include <type_traits>
 
 #include "common.hpp"
@@ -33,49 +41,91 @@ static_assert(sizeof(bf16_t_storage) == sizeof(bf16_t), "bf16 storage");
 
 namespace {
 
-constexpr int TC = 64;          // tokens per tile
-constexpr int NRB = TC / 16;    // 16-row blocks per tile
+typedef __attribute__((address_space(3))) void lds_void_t;
+typedef __attribute__((address_space(1))) void glb_void_t;
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
+
+constexpr int TC = 64;        // tokens per tile
+constexpr int NRB = TC / 16;  // 16-row blocks per tile
 constexpr int LOGTC = 6;
-constexpr int PAD = 8;          // bf16 elements of padding per LDS row (16 bytes)
-constexpr int kTopMax = 16;     // coarse slots tracked (LDS use is checked on the host)
+constexpr int PPAD = 8;       // bf16 padding per row of the P tile
+constexpr int PROW = TC + PPAD;
 
-struct Lds {
-    int q, k, kt, vt, p, lam, araw, aloc, ev, top, total;
-};
+// ---------------------------------------------------------------------------
+// Swizzled LDS tiles: 64 rows of CPR 16-byte chunks; chunk c of row r is
+// stored at position c ^ swz(r).  The swizzles keep 16-byte reads of 16
+// consecutive rows, the paired 8-byte reads of the level products and the
+// transpose reads free of bank conflicts for CPR = 8 and 16.
 
-__host__ __device__ inline int round16(int x) { return (x + 15) & ~15; }
-
-// Byte offsets of the fused kernel's LDS regions (the host sizes the launch
-// with the same function).
-__host__ __device__ inline Lds fused_lds(int dk, int dvw, int lu, int ntop) {
-    Lds o;
-    int off = 0;
-    o.q = off;    off += round16(TC * (dk + PAD) * 2);
-    o.k = off;    off += round16(TC * (dk + PAD) * 2);
-    o.kt = off;   off += round16(dk * (TC + PAD) * 2);
-    o.vt = off;   off += round16(dvw * (TC + PAD) * 2);
-    o.p = off;    off += round16(TC * (TC + PAD) * 2);
-    o.lam = off;  off += round16(TC * lu * 4);
-    o.araw = off; off += round16(TC * 4);
-    o.aloc = off; off += round16(TC * 4);
-    o.ev = off;   off += round16(TC * 4);
-    o.top = off;  off += round16(ntop * dk * dvw * 2);
-    o.total = off;
-    return o;
+template <int CPR>
+__device__ __forceinline__ int swz(int r) {
+    if constexpr (CPR == 16) {
+        return (((r & 7) ^ ((r >> 1) & 4)) << 1) | ((r >> 3) & 1);
+    } else if constexpr (CPR == 8) {
+        const int u = (r >> 1) & 7;
+        return (u & 4) | ((u & 1) << 1) | ((u >> 1) & 1);
+    } else if constexpr (CPR == 4) {
+        return (((r >> 1) & 7) ^ ((r >> 3) & 1)) & 3;
+    } else {
+        return (r >> 3) & 1;
+    }
 }
 
-// LDS of the segment-state kernel: K^T, V^T, a, A, e.
-__host__ __device__ inline int segstate_lds(int dk, int dvw) {
-    return round16(dk * (TC + PAD) * 2) + round16(dvw * (TC + PAD) * 2) + 3 * round16(TC * 4);
+// element offset of (row, col) in a swizzled tile with D columns
+template <int D>
+__device__ __forceinline__ int toff(int r, int col) {
+    constexpr int CPR = D / 8;
+    return (r * CPR + ((col >> 3) ^ swz<CPR>(r))) * 8 + (col & 7);
 }
 
-__device__ __forceinline__ int xcd_block(int b, int nblocks) {
-    if (nblocks % 8 != 0) return b;
-    return (b % 8) * (nblocks / 8) + b / 8;
+template <int D>
+__device__ __forceinline__ bf16x8 ld8(const bf16_t* t, int r, int col) {  // col % 8 == 0
+    return *reinterpret_cast<const bf16x8*>(t + toff<D>(r, col));
+}
+template <int D>
+__device__ __forceinline__ bf16x4 ld4(const bf16_t* t, int r, int col) {  // col % 4 == 0
+    return *reinterpret_cast<const bf16x4*>(t + toff<D>(r, col));
 }
 
-__device__ __forceinline__ uint32_t pack2(bf16_t lo, bf16_t hi) {
-    return (uint32_t)lo | ((uint32_t)hi << 16);
+// Transpose read of a 16-wide column block: lane l of 16-lane group g gets
+// X[k0 + 8g + i][n0 + l % 16] for i < 8 (X row-major [token][column]).
+// Within a group, lane j supplies the row k + j/4 and columns n + 4 (j % 4);
+// the hardware returns column n + j of rows k..k+3.
+template <int D>
+__device__ __forceinline__ bf16x8 ld_tr8(const bf16_t* t, int k0, int n0) {
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, j = lane & 15;
+    const int r = k0 + 8 * g + (j >> 2);
+    const int c = n0 + 4 * (j & 3);
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4*)(t + toff<D>(r, c)));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4*)(t + toff<D>(r + 4, c)));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
+__device__ __forceinline__ void dma16(const void* g, void* lds) {
+    __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)lds, 16, 0, 0);
+}
+
+// Copies rows [0, 64) of a bf16 [rows][pitch] matrix, columns [col0, col0 + D),
+// into a swizzled LDS tile.  Rows at or past nvalid repeat row nvalid - 1
+// (finite values; they only meet masked or discarded entries).  Each wave
+// instruction fills 1 KB of consecutive LDS chunks; a lane picks the source
+// chunk that belongs at its position.
+template <int D, int NW>
+__device__ __forceinline__ void dma_tile(const bf16_t* __restrict__ src, size_t pitch, int col0,
+                                         int nvalid, bf16_t* lds, int wave) {
+    constexpr int CPR = D / 8;
+    constexpr int NI = TC * CPR / 64;
+    const int lane = threadIdx.x & 63;
+    for (int u = wave; u < NI; u += NW) {
+        const int pch = u * 64 + lane;
+        const int r = pch / CPR, pc = pch % CPR;
+        const int lc = pc ^ swz<CPR>(r);
+        const int rs = min(r, nvalid - 1);
+        dma16(src + (size_t)rs * pitch + col0 + lc * 8, lds + u * 512);
+    }
 }
 
 __device__ __forceinline__ bf16x8 cvt8(const f32x4& a, const f32x4& b) {
@@ -90,187 +140,35 @@ __device__ __forceinline__ bf16x4 cvt4(const f32x4& a) {
     return r;
 }
 
-// Head-dimension contraction step: 32 with the K=32 MFMA, 16 for d_k = 16.
+__device__ __forceinline__ int xcd_block(int b, int nblocks) {
+    if (nblocks % 8 != 0) return b;
+    return (b % 8) * (nblocks / 8) + b / 8;
+}
+
+// Head-dimension contraction: steps of 32 with the K=32 MFMA (16 for d_k = 16).
 template <int DK>
 struct HD {
     static constexpr int KS = DK >= 32 ? 32 : 16;
     static constexpr int NKS = DK / KS;
+    static constexpr int NDT = DK / 16;
     typedef typename std::conditional<(DK >= 32), bf16x8, bf16x4>::type frag;
-    static constexpr int KPL = DK >= 32 ? 8 : 4;
 };
 
-// ---------------------------------------------------------------------------
-// Tile staging: global -> registers (prefetch) -> LDS.
-
-template <int DK, int NW>
-struct TileRegs {
-    static constexpr int NT = NW * 64;
-    static constexpr int DVW = NW * 16;
-    static constexpr int QV = TC * DK / 8;                 // 16-byte vectors of Q
-    static constexpr int KP = (TC / 2) * (DK / 8);         // token pairs x 8 head dims of K
-    static constexpr int VP = (TC / 2) * (DVW / 8);        // token pairs x 8 columns of V
-    static constexpr int NQ = (QV + NT - 1) / NT;
-    static constexpr int NK = (KP + NT - 1) / NT;
-    static constexpr int NV = (VP + NT - 1) / NT;
-    static constexpr int LUMAX = 24;                        // levels staged per token (max)
-    static constexpr int NL = (TC * LUMAX + NT - 1) / NT;
-    uint4 q[NQ];
-    uint4 k[NK][2];
-    uint4 v[NV][2];
-    float a;
-    float lam[NL];
-};
-
-// Loads tile `i` (tokens i*TC ...) of sequence row0 into registers; rows past
-// T are zero.  withQ=false skips Q and lambda (segment-state kernel).
-template <int DK, int NW, bool withQ>
-__device__ __forceinline__ void load_tile(TileRegs<DK, NW>& R, const bf16_t* __restrict__ q,
-                                          const bf16_t* __restrict__ k,
-                                          const bf16_t* __restrict__ v, const float* __restrict__ a,
-                                          const float* __restrict__ lam, size_t row0, int t0, int T,
-                                          int dv, int cb, int L, int lu) {
-    typedef TileRegs<DK, NW> TR;
-    const int tid = threadIdx.x;
-    const int nvalid = min(TC, T - t0);
-    const uint4 z = make_uint4(0, 0, 0, 0);
-    const size_t r0 = row0 + t0;
-    if constexpr (withQ) {
-#pragma unroll
-        for (int u = 0; u < TR::NQ; ++u) {
-            const int x = tid + u * TR::NT;
-            if (x < TR::QV) {
-                const int s = x / (DK / 8), d0 = (x % (DK / 8)) * 8;
-                R.q[u] = s < nvalid ? *reinterpret_cast<const uint4*>(q + (r0 + s) * DK + d0) : z;
-            }
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < TR::NK; ++u) {
-        const int x = tid + u * TR::NT;
-        if (x < TR::KP) {
-            const int ps = x % (TC / 2), d0 = (x / (TC / 2)) * 8;
-            const int s = 2 * ps;
-            R.k[u][0] = s < nvalid ? *reinterpret_cast<const uint4*>(k + (r0 + s) * DK + d0) : z;
-            R.k[u][1] =
-                s + 1 < nvalid ? *reinterpret_cast<const uint4*>(k + (r0 + s + 1) * DK + d0) : z;
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < TR::NV; ++u) {
-        const int x = tid + u * TR::NT;
-        if (x < TR::VP) {
-            const int ps = x % (TC / 2), c = cb + (x / (TC / 2)) * 8;
-            const int s = 2 * ps;
-            R.v[u][0] = s < nvalid ? *reinterpret_cast<const uint4*>(v + (r0 + s) * dv + c) : z;
-            R.v[u][1] =
-                s + 1 < nvalid ? *reinterpret_cast<const uint4*>(v + (r0 + s + 1) * dv + c) : z;
-        }
-    }
-    if (tid < TC) R.a = tid < nvalid ? a[r0 + tid] : 0.f;
-    if constexpr (withQ) {
-#pragma unroll
-        for (int u = 0; u < TR::NL; ++u) {
-            const int x = tid + u * TR::NT;
-            if (x < TC * lu) {
-                const int s = x / lu, l = x - s * lu;
-                R.lam[u] = s < nvalid ? lam[(r0 + s) * L + l] : 0.f;
-            }
-        }
-    }
-}
-
-// Writes a loaded tile to LDS: Q and K as [token][d_k], K^T [d_k][token],
-// V^T [column][token], lambda [token][level], raw a.
-template <int DK, int NW, bool withQ>
-__device__ __forceinline__ void store_tile(const TileRegs<DK, NW>& R, bf16_t* Qs, bf16_t* Ks,
-                                           bf16_t* KTs, bf16_t* VTs, float* lam_s, float* araw,
-                                           int lu) {
-    typedef TileRegs<DK, NW> TR;
-    constexpr int QROW = DK + PAD, TROW = TC + PAD;
-    const int tid = threadIdx.x;
-    if constexpr (withQ) {
-#pragma unroll
-        for (int u = 0; u < TR::NQ; ++u) {
-            const int x = tid + u * TR::NT;
-            if (x < TR::QV) {
-                const int s = x / (DK / 8), d0 = (x % (DK / 8)) * 8;
-                *reinterpret_cast<uint4*>(Qs + s * QROW + d0) = R.q[u];
-            }
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < TR::NK; ++u) {
-        const int x = tid + u * TR::NT;
-        if (x < TR::KP) {
-            const int ps = x % (TC / 2), d0 = (x / (TC / 2)) * 8;
-            const int s = 2 * ps;
-            if constexpr (withQ) {
-                *reinterpret_cast<uint4*>(Ks + s * QROW + d0) = R.k[u][0];
-                *reinterpret_cast<uint4*>(Ks + (s + 1) * QROW + d0) = R.k[u][1];
-            }
-            const bf16_t* e0 = reinterpret_cast<const bf16_t*>(&R.k[u][0]);
-            const bf16_t* e1 = reinterpret_cast<const bf16_t*>(&R.k[u][1]);
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                *reinterpret_cast<uint32_t*>(KTs + (d0 + j) * TROW + s) = pack2(e0[j], e1[j]);
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < TR::NV; ++u) {
-        const int x = tid + u * TR::NT;
-        if (x < TR::VP) {
-            const int ps = x % (TC / 2), c0 = (x / (TC / 2)) * 8;
-            const int s = 2 * ps;
-            const bf16_t* e0 = reinterpret_cast<const bf16_t*>(&R.v[u][0]);
-            const bf16_t* e1 = reinterpret_cast<const bf16_t*>(&R.v[u][1]);
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-                *reinterpret_cast<uint32_t*>(VTs + (c0 + j) * TROW + s) = pack2(e0[j], e1[j]);
-        }
-    }
-    if (tid < TC) araw[tid] = R.a;
-    if constexpr (withQ) {
-#pragma unroll
-        for (int u = 0; u < TR::NL; ++u) {
-            const int x = tid + u * TR::NT;
-            if (x < TC * lu) lam_s[x] = R.lam[u];
-        }
-    }
-}
-
-// Wave 0: local inclusive cumsum of a and e_s = exp(A_end - A_s).
-__device__ __forceinline__ void tile_decay(const float* araw, float* aloc, float* ev) {
-    wave_cumsum(araw, aloc, TC);
-    __builtin_amdgcn_wave_barrier();
+// Tile-local decay of one wave: lane s gets A_s (inclusive cumsum of a over
+// the tile); the wave's private LDS rows receive A and e_s = exp(A_end - A_s).
+// Returns the tile total A_end, uniform over the wave.
+__device__ __forceinline__ float tile_decay(const float* a_tile, float* Aw, float* Ew) {
     const int lane = threadIdx.x & 63;
-    const float end = __shfl(aloc[TC - 1], 0);  // all lanes read the same slot
-    ev[lane] = __expf(end - aloc[lane]);
-}
-
-// U (d_k x 16 columns of this wave) of the staged tile: U = K^T diag(e) V.
-// Accumulates into u (C-layout: lane holds U[16 kt + 4 g + i][c0 + m16]).
-template <int DK>
-__device__ __forceinline__ void tile_state(f32x4 (&u)[DK / 16], const bf16_t* KTs,
-                                           const bf16_t* VTs, const float* ev, int wave) {
-    constexpr int TROW = TC + PAD;
-    const int lane = threadIdx.x & 63, m16 = lane & 15, g = lane >> 4;
+    float x = a_tile[lane];
 #pragma unroll
-    for (int ss = 0; ss < TC / 32; ++ss) {
-        const int s0 = 32 * ss + 8 * g;
-        const bf16x8 vr = *reinterpret_cast<const bf16x8*>(VTs + (wave * 16 + m16) * TROW + s0);
-        const float4 e0 = *reinterpret_cast<const float4*>(ev + s0);
-        const float4 e1 = *reinterpret_cast<const float4*>(ev + s0 + 4);
-        bf16x8 b;
-        b[0] = (__bf16)((float)vr[0] * e0.x); b[1] = (__bf16)((float)vr[1] * e0.y);
-        b[2] = (__bf16)((float)vr[2] * e0.z); b[3] = (__bf16)((float)vr[3] * e0.w);
-        b[4] = (__bf16)((float)vr[4] * e1.x); b[5] = (__bf16)((float)vr[5] * e1.y);
-        b[6] = (__bf16)((float)vr[6] * e1.z); b[7] = (__bf16)((float)vr[7] * e1.w);
-#pragma unroll
-        for (int kt = 0; kt < DK / 16; ++kt) {
-            const bf16x8 ka = *reinterpret_cast<const bf16x8*>(KTs + (16 * kt + m16) * TROW + s0);
-            u[kt] = mma(ka, b, u[kt]);
-        }
+    for (int off = 1; off < 64; off <<= 1) {
+        const float y = __shfl_up(x, off, 64);
+        if (lane >= off) x += y;
     }
+    const float end = wave_uniform(__shfl(x, 63, 64));
+    Aw[lane] = x;
+    Ew[lane] = __expf(end - x);
+    return end;
 }
 
 template <int N>
@@ -281,67 +179,92 @@ __device__ __forceinline__ float pick(const float (&x)[N], int idx) {
     return r;
 }
 
-// Scores of row block RB against key blocks 0..RB, masked, to LDS as bf16.
+// Masked, weighted scores of row block RB against key blocks 0..RB, to the P
+// tile as bf16.  The block past the diagonal that the K=32 product pairs with
+// an even RB is written as zeros.
 template <int DK, int RB>
 __device__ __forceinline__ void tile_scores(const bf16_t* Qs, const bf16_t* Ks, bf16_t* Ps,
-                                            const float* aloc, const float* lam_s, int lu) {
-    constexpr int QROW = DK + PAD, TROW = TC + PAD;
+                                            const float* Aw, const float* lam_s, int L) {
     typedef HD<DK> H;
     const int lane = threadIdx.x & 63, m16 = lane & 15, g = lane >> 4;
-    const int r = 16 * RB + m16;
-    typename H::frag qb[H::NKS];
-#pragma unroll
-    for (int ks = 0; ks < H::NKS; ++ks)
-        qb[ks] = *reinterpret_cast<const typename H::frag*>(Qs + r * QROW + ks * H::KS +
-                                                             g * H::KPL);
+    const int t = 16 * RB + m16;
     f32x4 acc[RB + 1];
 #pragma unroll
     for (int sb = 0; sb <= RB; ++sb) acc[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < H::NKS; ++ks) {
+        typename H::frag qb;
+        if constexpr (DK >= 32) qb = ld8<DK>(Qs, t, ks * 32 + 8 * g);
+        else qb = ld4<DK>(Qs, t, 4 * g);
 #pragma unroll
         for (int sb = 0; sb <= RB; ++sb) {
-            const typename H::frag ka = *reinterpret_cast<const typename H::frag*>(
-                Ks + (16 * sb + m16) * QROW + ks * H::KS + g * H::KPL);
-            acc[sb] = mma(ka, qb[ks], acc[sb]);
+            typename H::frag ka;
+            if constexpr (DK >= 32) ka = ld8<DK>(Ks, 16 * sb + m16, ks * 32 + 8 * g);
+            else ka = ld4<DK>(Ks, 16 * sb + m16, 4 * g);
+            acc[sb] = mma(ka, qb, acc[sb]);
         }
     }
-    float lamr[LOGTC + 1];
-#pragma unroll
-    for (int l = 0; l <= LOGTC; ++l) lamr[l] = l < lu ? lam_s[r * lu + l] : 0.f;
-    const float Ar = aloc[r];
+    const float* lam_t = lam_s + t * L;  // levels inside a tile are < L (see the host checks)
+    const float At = Aw[t];
 #pragma unroll
     for (int sb = 0; sb <= RB; ++sb) {
+        const float4 As = *reinterpret_cast<const float4*>(Aw + 16 * sb + 4 * g);
+        const float Asv[4] = {As.x, As.y, As.z, As.w};
         float w[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int s = 16 * sb + 4 * g + i;
-            w[i] = s <= r ? acc[sb][i] * pick(lamr, fenwick_level(r, s)) * __expf(Ar - aloc[s])
-                          : 0.f;
+            w[i] = s <= t ? acc[sb][i] * lam_t[fenwick_level(t, s)] * __expf(At - Asv[i]) : 0.f;
         }
-        *reinterpret_cast<bf16x4*>(Ps + r * TROW + 16 * sb + 4 * g) = pack4(w[0], w[1], w[2], w[3]);
+        *reinterpret_cast<bf16x4*>(Ps + t * PROW + 16 * sb + 4 * g) = pack4(w[0], w[1], w[2], w[3]);
     }
-    if constexpr ((RB & 1) == 0 && RB + 1 < NRB) {
-        // the K=32 product below pairs key blocks; the block past the diagonal is zero
-        *reinterpret_cast<bf16x4*>(Ps + r * TROW + 16 * (RB + 1) + 4 * g) = bf16x4{};
-    }
+    if constexpr ((RB & 1) == 0 && RB + 1 < NRB)
+        *reinterpret_cast<bf16x4*>(Ps + t * PROW + 16 * (RB + 1) + 4 * g) = bf16x4{};
 }
 
 template <int DK, int NW>
 __device__ __forceinline__ void scores_for_wave(int wave, const bf16_t* Qs, const bf16_t* Ks,
-                                                bf16_t* Ps, const float* aloc,
-                                                const float* lam_s, int lu) {
+                                                bf16_t* Ps, const float* Aw, const float* lam_s,
+                                                int L) {
 #pragma unroll
     for (int rb0 = 0; rb0 < NRB; rb0 += NW) {
-        const int rb = rb0 + wave;
-        switch (rb) {
-            case 0: tile_scores<DK, 0>(Qs, Ks, Ps, aloc, lam_s, lu); break;
-            case 1: tile_scores<DK, 1>(Qs, Ks, Ps, aloc, lam_s, lu); break;
-            case 2: tile_scores<DK, 2>(Qs, Ks, Ps, aloc, lam_s, lu); break;
-            case 3: tile_scores<DK, 3>(Qs, Ks, Ps, aloc, lam_s, lu); break;
+        switch (rb0 + wave) {
+            case 0: tile_scores<DK, 0>(Qs, Ks, Ps, Aw, lam_s, L); break;
+            case 1: tile_scores<DK, 1>(Qs, Ks, Ps, Aw, lam_s, L); break;
+            case 2: tile_scores<DK, 2>(Qs, Ks, Ps, Aw, lam_s, L); break;
+            case 3: tile_scores<DK, 3>(Qs, Ks, Ps, Aw, lam_s, L); break;
             default: break;
         }
     }
+}
+
+// U (d_k x this wave's 16 columns) of the staged tile, U = K^T diag(e) V:
+// u[kt] (C layout) holds U[16 kt + 4g + i][column m16].  vf[sp] are the V
+// fragments (lane: V[32 sp + 8g + i][column]) shared with the P V product.
+template <int DK, int DVW>
+__device__ __forceinline__ void tile_state(f32x4 (&u)[DK / 16], const bf16_t* Ks,
+                                           const bf16x8 (&vf)[2], const float* Ew) {
+    const int lane = threadIdx.x & 63, g = lane >> 4;
+#pragma unroll
+    for (int sp = 0; sp < 2; ++sp) {
+        const float4 e0 = *reinterpret_cast<const float4*>(Ew + 32 * sp + 8 * g);
+        const float4 e1 = *reinterpret_cast<const float4*>(Ew + 32 * sp + 8 * g + 4);
+        const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
+        bf16x8 b;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) b[i] = (__bf16)((float)vf[sp][i] * ev[i]);
+#pragma unroll
+        for (int kt = 0; kt < DK / 16; ++kt) u[kt] = mma(ld_tr8<DK>(Ks, 32 * sp, 16 * kt), b, u[kt]);
+    }
+}
+
+// Fragment of the bf16 copy of a Fenwick node written by the scan:
+// [node][column block of 16][contraction step][lane][8 or 4 bf16].
+template <int DK>
+__device__ __forceinline__ size_t frag_index(size_t node_global, int ncb, int cblk, int ks) {
+    constexpr int NKS = HD<DK>::NKS;
+    constexpr int PER = DK >= 32 ? 8 : 4;
+    return (((node_global * ncb + cblk) * NKS + ks) * 64 + (threadIdx.x & 63)) * PER;
 }
 
 }  // namespace
@@ -352,16 +275,16 @@ __device__ __forceinline__ void scores_for_wave(int wave, const bf16_t* Qs, cons
 
 template <int DK, int NW>
 __global__ __launch_bounds__(NW * 64) void k_seg_state(FusedParams p) {
-    typedef TileRegs<DK, NW> TR;
     constexpr int DVW = NW * 16;
     constexpr int NDT = DK / 16;
-    extern __shared__ __align__(16) char smem[];
-    bf16_t* KTs = reinterpret_cast<bf16_t*>(smem);
-    bf16_t* VTs = reinterpret_cast<bf16_t*>(smem + round16(DK * (TC + PAD) * 2));
-    float* araw = reinterpret_cast<float*>(smem + round16(DK * (TC + PAD) * 2) +
-                                           round16(DVW * (TC + PAD) * 2));
-    float* aloc = araw + round16(TC * 4) / 4;
-    float* ev = aloc + round16(TC * 4) / 4;
+    __shared__ __align__(16) bf16_t sK0[TC * DK];
+    __shared__ __align__(16) bf16_t sK1[TC * DK];
+    __shared__ __align__(16) bf16_t sV0[TC * DVW];
+    __shared__ __align__(16) bf16_t sV1[TC * DVW];
+    __shared__ __align__(16) float sa0[TC];
+    __shared__ __align__(16) float sa1[TC];
+    __shared__ __align__(16) float sAw[NW][TC];
+    __shared__ __align__(16) float sEw[NW][TC];
 
     const int nsegs = p.nseg - 1;
     int blk = xcd_block(blockIdx.x, gridDim.x);
@@ -370,34 +293,49 @@ __global__ __launch_bounds__(NW * 64) void k_seg_state(FusedParams p) {
     const int seg = blk % nsegs;
     const int bh = blk / nsegs;
     const int cb = dvb * DVW;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, m16 = lane & 15, g = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, m16 = lane & 15, g = lane >> 4;
     const size_t row0 = (size_t)bh * p.T;
-    const int tile0 = seg << p.m, ntl = 1 << p.m;
+    const int tile0 = seg << p.m, ntl = 1 << p.m;  // every tile of a non-last segment is full
+
+    auto issue = [&](int il, bf16_t* Kd, bf16_t* Vd, float* ad) __attribute__((always_inline)) {
+        const size_t r = row0 + (size_t)(tile0 + il) * TC;
+        dma_tile<DK, NW>(p.k + r * DK, DK, 0, TC, Kd, wave);
+        dma_tile<DVW, NW>(p.v + r * p.dv, p.dv, cb, TC, Vd, wave);
+        if (p.a_dma) {
+            if (wave == 0 && lane < TC / 4) dma16(p.a + r + 4 * lane, ad);
+        } else if (wave == 0) {
+            ad[lane] = p.a[r + lane];
+        }
+    };
 
     f32x4 u[NDT];
 #pragma unroll
     for (int kt = 0; kt < NDT; ++kt) u[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float total = 0.f;
-    TR R;
-    load_tile<DK, NW, false>(R, nullptr, p.k, p.v, p.a, nullptr, row0, tile0 * TC, p.T, p.dv, cb,
-                             p.L, p.LU);
-    for (int il = 0; il < ntl; ++il) {
+
+    auto body = [&](int il, const bf16_t* Kc, const bf16_t* Vc, const float* ac, bf16_t* Kn,
+                    bf16_t* Vn, float* an) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        store_tile<DK, NW, false>(R, nullptr, nullptr, KTs, VTs, nullptr, araw, p.LU);
-        __syncthreads();
-        if (il + 1 < ntl)
-            load_tile<DK, NW, false>(R, nullptr, p.k, p.v, p.a, nullptr, row0,
-                                     (tile0 + il + 1) * TC, p.T, p.dv, cb, p.L, p.LU);
-        if (wave == 0) tile_decay(araw, aloc, ev);
-        __syncthreads();
-        const float tot = wave_uniform(aloc[TC - 1]);
+        if (il + 1 < ntl) issue(il + 1, Kn, Vn, an);
+        const float tot = tile_decay(ac, sAw[wave], sEw[wave]);
         const float f = __expf(tot);
 #pragma unroll
         for (int kt = 0; kt < NDT; ++kt) {
             u[kt][0] *= f; u[kt][1] *= f; u[kt][2] *= f; u[kt][3] *= f;
         }
-        tile_state<DK>(u, KTs, VTs, ev, wave);
+        bf16x8 vf[2];
+        vf[0] = ld_tr8<DVW>(Vc, 0, 16 * wave);
+        vf[1] = ld_tr8<DVW>(Vc, 32, 16 * wave);
+        tile_state<DK, DVW>(u, Kc, vf, sEw[wave]);
         total += tot;
+    };
+
+    issue(0, sK0, sV0, sa0);
+    for (int il = 0; il < ntl; il += 2) {
+        body(il, sK0, sV0, sa0, sK1, sV1, sa1);
+        if (il + 1 < ntl) body(il + 1, sK1, sV1, sa1, sK0, sV0, sa0);
     }
     float* dst = p.useg + ((size_t)bh * p.nseg + seg) * p.dv * DK;
     const int c = cb + wave * 16 + m16;
@@ -410,26 +348,27 @@ __global__ __launch_bounds__(NW * 64) void k_seg_state(FusedParams p) {
 
 // ---------------------------------------------------------------------------
 // Main fused kernel: one block per (bh, segment, column block).
+//   MLOC    register-resident levels inside a segment (segments of <= 2^MLOC tiles)
+//   TOPMAX  levels above the segment held as bf16 fragments
 
-template <int DK, int NW>
-__global__ __launch_bounds__(NW * 64) void k_fused_fwd(FusedParams p) {
-    typedef TileRegs<DK, NW> TR;
+template <int DK, int NW, int MLOC, int TOPMAX>
+__global__ __launch_bounds__(NW * 64, 1) void k_fused_fwd(FusedParams p) {
     typedef HD<DK> H;
     constexpr int DVW = NW * 16;
-    constexpr int NDT = DK / 16;
-    constexpr int QROW = DK + PAD, TROW = TC + PAD;
-    extern __shared__ __align__(16) char smem[];
-    const Lds lo = fused_lds(DK, DVW, p.LU, p.ntop);
-    bf16_t* Qs = reinterpret_cast<bf16_t*>(smem + lo.q);
-    bf16_t* Ks = reinterpret_cast<bf16_t*>(smem + lo.k);
-    bf16_t* KTs = reinterpret_cast<bf16_t*>(smem + lo.kt);
-    bf16_t* VTs = reinterpret_cast<bf16_t*>(smem + lo.vt);
-    bf16_t* Ps = reinterpret_cast<bf16_t*>(smem + lo.p);
-    float* lam_s = reinterpret_cast<float*>(smem + lo.lam);
-    float* araw = reinterpret_cast<float*>(smem + lo.araw);
-    float* aloc = reinterpret_cast<float*>(smem + lo.aloc);
-    float* ev = reinterpret_cast<float*>(smem + lo.ev);
-    typename H::frag* top = reinterpret_cast<typename H::frag*>(smem + lo.top);
+    constexpr int NDT = H::NDT, NKS = H::NKS;
+    __shared__ __align__(16) bf16_t sQ0[TC * DK];
+    __shared__ __align__(16) bf16_t sQ1[TC * DK];
+    __shared__ __align__(16) bf16_t sK0[TC * DK];
+    __shared__ __align__(16) bf16_t sK1[TC * DK];
+    __shared__ __align__(16) bf16_t sV0[TC * DVW];
+    __shared__ __align__(16) bf16_t sV1[TC * DVW];
+    __shared__ __align__(16) float sL0[TC * kFusedMaxL];
+    __shared__ __align__(16) float sL1[TC * kFusedMaxL];
+    __shared__ __align__(16) float sa0[TC];
+    __shared__ __align__(16) float sa1[TC];
+    __shared__ __align__(16) bf16_t sP[TC * PROW];
+    __shared__ __align__(16) float sAw[NW][TC];
+    __shared__ __align__(16) float sEw[NW][TC];
 
     int blk = xcd_block(blockIdx.x, gridDim.x);
     const int dvb = blk % p.ndvb;
@@ -437,150 +376,174 @@ __global__ __launch_bounds__(NW * 64) void k_fused_fwd(FusedParams p) {
     const int seg = blk % p.nseg;
     const int bh = blk / p.nseg;
     const int cb = dvb * DVW;
-    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, m16 = lane & 15, g = lane >> 4;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, m16 = lane & 15, g = lane >> 4;
+    const int tid = threadIdx.x;
     const int c0 = cb + wave * 16;  // first column of this wave
     const size_t row0 = (size_t)bh * p.T;
     const int tile0 = seg << p.m;
     const int ntl = min(1 << p.m, p.ntiles - tile0);
-    const int lu = p.LU;
+    const int L = p.L;         // lambda row length in global memory
+    const int LP = p.lpitch;   // lambda row length in LDS
 
-    // coarse levels of this segment: Fenwick nodes over segments, bf16 in LDS
-    float logd_top[kTopMax];
+    // levels above the segment: Fenwick nodes over segments, bf16 fragments
+    typename H::frag top[TOPMAX][NKS];
+    float logd_top[TOPMAX];
 #pragma unroll
-    for (int q = 0; q < kTopMax; ++q) {
+    for (int q = 0; q < TOPMAX; ++q) {
         logd_top[q] = 0.f;
         if (q < p.ntop && ((seg >> q) & 1)) {
             const int node = ((seg >> q) << q) - 1;
             const double* cum = p.scum + (size_t)bh * p.nseg;
             logd_top[q] = (float)(cum[seg - 1] - cum[node]);
-            const float* G = p.useg + ((size_t)bh * p.nseg + node) * p.dv * DK +
-                             (size_t)(c0 + m16) * DK;
+            const size_t ng = (size_t)bh * p.nseg + node;
 #pragma unroll
-            for (int ks = 0; ks < H::NKS; ++ks) {
-                typename H::frag f;
-                if constexpr (DK >= 32) {
-                    const float4 x = *reinterpret_cast<const float4*>(G + 32 * ks + 4 * g);
-                    const float4 y = *reinterpret_cast<const float4*>(G + 32 * ks + 16 + 4 * g);
-                    f = cvt8(f32x4{x.x, x.y, x.z, x.w}, f32x4{y.x, y.y, y.z, y.w});
-                } else {
-                    const float4 x = *reinterpret_cast<const float4*>(G + 4 * g);
-                    f = cvt4(f32x4{x.x, x.y, x.z, x.w});
-                }
-                top[((q * NW + wave) * H::NKS + ks) * 64 + lane] = f;
-            }
+            for (int ks = 0; ks < NKS; ++ks)
+                top[q][ks] = *reinterpret_cast<const typename H::frag*>(
+                    p.gfrag + frag_index<DK>(ng, p.dv / 16, c0 / 16, ks));
+        } else {
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) top[q][ks] = typename H::frag{};
         }
     }
 
-    // levels inside the segment: fp32 states in registers
-    f32x4 G[kMaxLocal][NDT];
-    float logd_loc[kMaxLocal];
+    // lambda and a of a tile: LDS-DMA when the rows are 16-byte aligned and
+    // whole, plain loads (staged through registers) otherwise
+    constexpr int NLR = (TC * kFusedMaxL + NW * 64 - 1) / (NW * 64);
+    float lam_r[NLR];
+    float a_r = 0.f;
+    auto issue = [&](int il, bf16_t* Qd, bf16_t* Kd, bf16_t* Vd, float* Ld, float* ad)
+        __attribute__((always_inline)) -> bool {
+        const int t0 = (tile0 + il) * TC;
+        const int nvalid = min(TC, p.T - t0);
+        const size_t r = row0 + t0;
+        dma_tile<DK, NW>(p.q + r * DK, DK, 0, nvalid, Qd, wave);
+        dma_tile<DK, NW>(p.k + r * DK, DK, 0, nvalid, Kd, wave);
+        dma_tile<DVW, NW>(p.v + r * p.dv, p.dv, cb, nvalid, Vd, wave);
+        const bool whole = nvalid == TC;
+        if (whole && p.lam_dma) {
+            const int nch = 16 * L;  // 64 rows x L floats
+            for (int u = wave; u * 64 < nch; u += NW)
+                if (u * 64 + lane < nch) dma16(p.lam + r * L + 4 * (u * 64 + lane), Ld + u * 256);
+        } else {
 #pragma unroll
-    for (int s = 0; s < kMaxLocal; ++s) logd_loc[s] = 0.f;
+            for (int k = 0; k < NLR; ++k) {
+                const int x = tid + k * NW * 64;
+                const int row = x / LP, l = x - row * LP;
+                lam_r[k] = x < nvalid * LP ? p.lam[(r + row) * L + l] : 0.f;
+            }
+        }
+        if (whole && p.a_dma) {
+            if (wave == 0 && lane < TC / 4) dma16(p.a + r + 4 * lane, ad);
+        } else if (tid < TC) {
+            a_r = tid < nvalid ? p.a[r + tid] : 0.f;
+        }
+        return whole;
+    };
+    // completes the plain-load part of issue() (called before the next barrier)
+    auto finish = [&](int il, bool whole, float* Ld, float* ad) __attribute__((always_inline)) {
+        if (!(whole && p.lam_dma)) {
+#pragma unroll
+            for (int k = 0; k < NLR; ++k) {
+                const int x = tid + k * NW * 64;
+                if (x < TC * LP) Ld[x] = lam_r[k];
+            }
+        }
+        if (!(whole && p.a_dma) && tid < TC) ad[tid] = a_r;
+    };
 
-    TR R;
-    load_tile<DK, NW, true>(R, p.q, p.k, p.v, p.a, p.lam, row0, tile0 * TC, p.T, p.dv, cb, p.L,
-                            lu);
-    for (int il = 0; il < ntl; ++il) {
+    f32x4 G[MLOC][NDT];
+    float logd_loc[MLOC];
+#pragma unroll
+    for (int s = 0; s < MLOC; ++s) {
+        logd_loc[s] = 0.f;
+#pragma unroll
+        for (int kt = 0; kt < NDT; ++kt) G[s][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+    auto body = [&](int il, const bf16_t* Qc, const bf16_t* Kc, const bf16_t* Vc,
+                    const float* Lc, const float* ac, bf16_t* Qn, bf16_t* Kn, bf16_t* Vn,
+                    float* Ln, float* an) __attribute__((always_inline)) {
+        // tile il is in LDS and every wave is done with tile il - 1
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        bool next_whole = true;
+        if (il + 1 < ntl) next_whole = issue(il + 1, Qn, Kn, Vn, Ln, an);
         const int i = tile0 + il;
         const int nvalid = min(TC, p.T - i * TC);
+        const float tot = tile_decay(ac, sAw[wave], sEw[wave]);
+        scores_for_wave<DK, NW>(wave, Qc, Kc, sP, sAw[wave], Lc, LP);
         __syncthreads();
-        store_tile<DK, NW, true>(R, Qs, Ks, KTs, VTs, lam_s, araw, lu);
-        __syncthreads();
-        if (il + 1 < ntl)
-            load_tile<DK, NW, true>(R, p.q, p.k, p.v, p.a, p.lam, row0, (i + 1) * TC, p.T, p.dv,
-                                    cb, p.L, lu);
-        if (wave == 0) tile_decay(araw, aloc, ev);
-        __syncthreads();
-        scores_for_wave<DK, NW>(wave, Qs, Ks, Ps, aloc, lam_s, lu);
-        __syncthreads();
-        const float tot = wave_uniform(aloc[TC - 1]);  // wave-uniform
 
         // ---- outputs of this wave's 16 columns, all rows of the tile
+        bf16x8 vf[2];
+        vf[0] = ld_tr8<DVW>(Vc, 0, 16 * wave);
+        vf[1] = ld_tr8<DVW>(Vc, 32, 16 * wave);
         f32x4 o[NRB];
-        typename H::frag qp[NRB][H::NKS];
-        float Ar[NRB];
+        float At[NRB];
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
             o[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            const int r = 16 * rb + m16;
-            Ar[rb] = aloc[r];
-#pragma unroll
-            for (int ks = 0; ks < H::NKS; ++ks) {
-                if constexpr (DK >= 32) {
-                    // head-dim order of the register states: 4g..4g+3, 16+4g..16+4g+3
-                    const bf16x4 x = *reinterpret_cast<const bf16x4*>(Qs + r * QROW + 32 * ks + 4 * g);
-                    const bf16x4 y =
-                        *reinterpret_cast<const bf16x4*>(Qs + r * QROW + 32 * ks + 16 + 4 * g);
-                    qp[rb][ks] = bf16x8{x[0], x[1], x[2], x[3], y[0], y[1], y[2], y[3]};
-                } else {
-                    qp[rb][ks] = *reinterpret_cast<const bf16x4*>(Qs + r * QROW + 4 * g);
-                }
-            }
+            At[rb] = sAw[wave][16 * rb + m16];
         }
-        // intra-tile block: O^T = V^T P^T over pairs of 16-token key blocks
 #pragma unroll
         for (int sp = 0; sp < NRB / 2; ++sp) {
-            const bf16x8 va =
-                *reinterpret_cast<const bf16x8*>(VTs + (wave * 16 + m16) * TROW + 32 * sp + 8 * g);
 #pragma unroll
             for (int rb = 2 * sp; rb < NRB; ++rb) {
-                const int r = 16 * rb + m16;
-                const bf16x8 pb = *reinterpret_cast<const bf16x8*>(Ps + r * TROW + 32 * sp + 8 * g);
-                o[rb] = mma(va, pb, o[rb]);
+                const bf16x8 pb =
+                    *reinterpret_cast<const bf16x8*>(sP + (16 * rb + m16) * PROW + 32 * sp + 8 * g);
+                o[rb] = mma(vf[sp], pb, o[rb]);
             }
         }
+        // Q fragment in the head-dim order of the register states:
+        // 4g..4g+3 and 16+4g..16+4g+3 of each 32-wide step
+        auto qfrag = [&](int rb, int ks) __attribute__((always_inline)) {
+            typename H::frag r;
+            if constexpr (DK >= 32) {
+                const bf16x4 x = ld4<DK>(Qc, 16 * rb + m16, 32 * ks + 4 * g);
+                const bf16x4 y = ld4<DK>(Qc, 16 * rb + m16, 32 * ks + 16 + 4 * g);
+                r = __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
+            } else {
+                r = ld4<DK>(Qc, 16 * rb + m16, 4 * g);
+            }
+            return r;
+        };
+        auto add_level = [&](const typename H::frag (&ga)[NKS], int lev, float logd)
+            __attribute__((always_inline)) {
+            f32x4 y[NRB];
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb) y[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks)
+#pragma unroll
+                for (int rb = 0; rb < NRB; ++rb) y[rb] = mma(ga[ks], qfrag(rb, ks), y[rb]);
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb) {
+                const float w = Lc[(16 * rb + m16) * LP + lev] * __expf(At[rb] + logd);
+                o[rb][0] += w * y[rb][0];
+                o[rb][1] += w * y[rb][1];
+                o[rb][2] += w * y[rb][2];
+                o[rb][3] += w * y[rb][3];
+            }
+        };
         // levels inside the segment
 #pragma unroll
-        for (int s = 0; s < kMaxLocal; ++s) {
+        for (int s = 0; s < MLOC; ++s) {
             if (s < p.m && ((il >> s) & 1)) {
-                typename H::frag ga[H::NKS];
+                typename H::frag ga[NKS];
 #pragma unroll
-                for (int ks = 0; ks < H::NKS; ++ks) {
+                for (int ks = 0; ks < NKS; ++ks) {
                     if constexpr (DK >= 32) ga[ks] = cvt8(G[s][2 * ks], G[s][2 * ks + 1]);
                     else ga[ks] = cvt4(G[s][ks]);
                 }
-                f32x4 y[NRB];
-#pragma unroll
-                for (int rb = 0; rb < NRB; ++rb) y[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < H::NKS; ++ks)
-#pragma unroll
-                    for (int rb = 0; rb < NRB; ++rb) y[rb] = mma(ga[ks], qp[rb][ks], y[rb]);
-                const int lev = LOGTC + s + 1;
-#pragma unroll
-                for (int rb = 0; rb < NRB; ++rb) {
-                    const float w = lam_s[(16 * rb + m16) * lu + lev] * __expf(Ar[rb] + logd_loc[s]);
-                    o[rb][0] += w * y[rb][0];
-                    o[rb][1] += w * y[rb][1];
-                    o[rb][2] += w * y[rb][2];
-                    o[rb][3] += w * y[rb][3];
-                }
+                add_level(ga, LOGTC + s + 1, logd_loc[s]);
             }
         }
         // levels above the segment
 #pragma unroll
-        for (int q = 0; q < kTopMax; ++q) {
-            if (q < p.ntop && ((seg >> q) & 1)) {
-                f32x4 y[NRB];
-#pragma unroll
-                for (int rb = 0; rb < NRB; ++rb) y[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < H::NKS; ++ks) {
-                    const typename H::frag ga = top[((q * NW + wave) * H::NKS + ks) * 64 + lane];
-#pragma unroll
-                    for (int rb = 0; rb < NRB; ++rb) y[rb] = mma(ga, qp[rb][ks], y[rb]);
-                }
-                const int lev = LOGTC + p.m + q + 1;
-#pragma unroll
-                for (int rb = 0; rb < NRB; ++rb) {
-                    const float w = lam_s[(16 * rb + m16) * lu + lev] * __expf(Ar[rb] + logd_top[q]);
-                    o[rb][0] += w * y[rb][0];
-                    o[rb][1] += w * y[rb][1];
-                    o[rb][2] += w * y[rb][2];
-                    o[rb][3] += w * y[rb][3];
-                }
-            }
-        }
+        for (int q = 0; q < TOPMAX; ++q)
+            if (q < p.ntop && ((seg >> q) & 1)) add_level(top[q], LOGTC + p.m + q + 1, logd_top[q]);
+
         float* orow = p.out + (row0 + (size_t)i * TC) * p.dv + c0 + 4 * g;
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
@@ -591,15 +554,15 @@ __global__ __launch_bounds__(NW * 64) void k_fused_fwd(FusedParams p) {
         }
 
         // ---- Fenwick update over tiles: fold the tile's state and the slots
-        // below lssb(il+1) into slot lssb(il+1)
+        // below lssb(il + 1) into slot lssb(il + 1)
         if (il + 1 < ntl) {
             f32x4 u[NDT];
 #pragma unroll
             for (int kt = 0; kt < NDT; ++kt) u[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            tile_state<DK>(u, KTs, VTs, ev, wave);
+            tile_state<DK, DVW>(u, Kc, vf, sEw[wave]);
             const int j = lssb((uint64_t)il + 1);
 #pragma unroll
-            for (int s = 0; s < kMaxLocal; ++s) {
+            for (int s = 0; s < MLOC; ++s) {
                 if (s < j) {
                     const float w = __expf(logd_loc[s] + tot);
 #pragma unroll
@@ -612,7 +575,7 @@ __global__ __launch_bounds__(NW * 64) void k_fused_fwd(FusedParams p) {
                 }
             }
 #pragma unroll
-            for (int s = 0; s < kMaxLocal; ++s) {
+            for (int s = 0; s < MLOC; ++s) {
                 if (s == j) {
 #pragma unroll
                     for (int kt = 0; kt < NDT; ++kt) G[s][kt] = u[kt];
@@ -621,92 +584,131 @@ __global__ __launch_bounds__(NW * 64) void k_fused_fwd(FusedParams p) {
                     logd_loc[s] += tot;
                 }
             }
+            finish(il + 1, next_whole, Ln, an);
         }
 #pragma unroll
-        for (int q = 0; q < kTopMax; ++q) logd_top[q] += tot;
+        for (int q = 0; q < TOPMAX; ++q) logd_top[q] += tot;
+    };
+
+    {
+        const bool w0 = issue(0, sQ0, sK0, sV0, sL0, sa0);
+        finish(0, w0, sL0, sa0);
+    }
+    for (int il = 0; il < ntl; il += 2) {
+        body(il, sQ0, sK0, sV0, sL0, sa0, sQ1, sK1, sV1, sL1, sa1);
+        if (il + 1 < ntl) body(il + 1, sQ1, sK1, sV1, sL1, sa1, sQ0, sK0, sV0, sL0, sa0);
     }
 }
 
 // ---------------------------------------------------------------------------
 // host side
 
+namespace {
+
+// Register budgets of the main kernel: (levels inside a segment, levels above it).
+struct Combo {
+    int mloc, topmax;
+};
+constexpr Combo kCombos[] = {{2, 4}, {3, 4}, {5, 2}, {5, 7}};
+constexpr int kNumCombos = sizeof(kCombos) / sizeof(kCombos[0]);
+
+int bit_len(long x) {
+    int n = 0;
+    while (x > 0) {
+        ++n;
+        x >>= 1;
+    }
+    return n;
+}
+
+}  // namespace
+
 FusedPlan plan_fused(int BH, int T, int dk, int dv, int lu, int force_m) {
     FusedPlan pl{};
-    if (lu > TileRegs<16, 4>::LUMAX) return pl;  // too many levels to stage per token
-    const int nw = dv >= 64 ? 4 : dv / 16;
-    pl.dvw = nw * 16;
-    pl.ndvb = dv / pl.dvw;
+    if (lu > kFusedMaxL) return pl;  // lambda levels staged per token
+    const int dvw = dv >= 64 ? 64 : dv;
+    pl.dvw = dvw;
+    pl.ndvb = dv / dvw;
     pl.ntiles = (T + TC - 1) / TC;
-    const long per_seg_blocks = (long)BH * pl.ndvb;
-    const int lds_cap = 160 * 1024;
-    // Largest segment (fewest extra reads of K and V by the segment-state
-    // pass) that still gives every CU a block; if no size does, the smallest
-    // segment whose coarse levels still fit in LDS.
-    int best = -1, smallest_fit = -1;
-    for (int m = kMaxLocal; m >= 0; --m) {
-        const int nseg = (pl.ntiles + (1 << m) - 1) >> m;
-        int ntop = 0;
-        while ((1 << ntop) < nseg) ++ntop;  // bit_length(nseg - 1)
-        if (ntop > kTopMax || fused_lds(dk, pl.dvw, lu, ntop).total > lds_cap) break;
-        smallest_fit = m;
-        if (per_seg_blocks * nseg >= 256) {
+    const long pairs = (long)BH * pl.ndvb;
+    const long slots = 256;  // one resident block per CU (register budget)
+    // Cost: the serial tiles a CU walks, rounds of resident blocks x tiles per
+    // block.
+    int best = -1, best_combo = -1;
+    long best_cost = 0;
+    for (int m = 0; m <= 5; ++m) {
+        if (force_m >= 0 && m != force_m) continue;
+        const long nseg = (pl.ntiles + (1L << m) - 1) >> m;
+        const int ntop = bit_len(nseg - 1);
+        int combo = -1;
+        for (int c = 0; c < kNumCombos; ++c)
+            if (m <= kCombos[c].mloc && ntop <= kCombos[c].topmax) {
+                combo = c;
+                break;
+            }
+        if (combo < 0) continue;
+        const long blocks = pairs * nseg;
+        const long rounds = (blocks + slots - 1) / slots;
+        const long cost = rounds * (1L << m);
+        // equal cost: the smaller register budget, then the longer segment
+        if (best < 0 || cost < best_cost || (cost == best_cost && combo <= best_combo)) {
             best = m;
-            break;
+            best_cost = cost;
+            best_combo = combo;
         }
-    }
-    if (best < 0) best = smallest_fit;
-    if (force_m >= 0) {  // a requested segment size, if its coarse levels fit
-        const int nseg = (pl.ntiles + (1 << force_m) - 1) >> force_m;
-        int ntop = 0;
-        while ((1 << ntop) < nseg) ++ntop;
-        best = (force_m <= kMaxLocal && ntop <= kTopMax &&
-                fused_lds(dk, pl.dvw, lu, ntop).total <= lds_cap) ? force_m : -1;
     }
     if (best < 0) return pl;
     pl.m = best;
-    pl.nseg = (pl.ntiles + (1 << best) - 1) >> best;
-    pl.ntop = 0;
-    while ((1 << pl.ntop) < pl.nseg) ++pl.ntop;
-    pl.lds_main = fused_lds(dk, pl.dvw, lu, pl.ntop).total;
-    pl.lds_seg = segstate_lds(dk, pl.dvw);
+    pl.nseg = (int)((pl.ntiles + (1L << best) - 1) >> best);
+    pl.ntop = bit_len(pl.nseg - 1);
+    pl.combo = best_combo;
     pl.ok = 1;
     return pl;
 }
 
 namespace {
 
+template <int DK, int NW, int MLOC, int TOPMAX>
+hipError_t launch_main(const FusedParams& p, hipStream_t stream) {
+    const unsigned nblk = (unsigned)p.BH * p.nseg * p.ndvb;
+    hipLaunchKernelGGL((k_fused_fwd<DK, NW, MLOC, TOPMAX>), dim3(nblk), dim3(NW * 64), 0, stream,
+                       p);
+    return hipGetLastError();
+}
+
 template <int DK, int NW>
 hipError_t launch_fused_t(const FusedParams& p, const FwdParams& scan, unsigned stages,
-                          hipStream_t stream, int lds_main, int lds_seg) {
+                          hipStream_t stream) {
     hipError_t err;
     if (p.nseg > 1 && (stages & kStageChunkState)) {
-        err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_seg_state<DK, NW>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, lds_seg);
-        if (err != hipSuccess) return err;
         const unsigned nblk = (unsigned)p.BH * (p.nseg - 1) * p.ndvb;
-        hipLaunchKernelGGL((k_seg_state<DK, NW>), dim3(nblk), dim3(NW * 64), lds_seg, stream, p);
+        hipLaunchKernelGGL((k_seg_state<DK, NW>), dim3(nblk), dim3(NW * 64), 0, stream, p);
+        err = hipGetLastError();
+        if (err != hipSuccess) return err;
     }
     if (p.nseg > 1 && (stages & kStageScan)) {
         err = launch_fenwick_scan(scan, stream);
         if (err != hipSuccess) return err;
     }
     if (stages & kStageOutput) {
-        err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_fused_fwd<DK, NW>),
-                                  hipFuncAttributeMaxDynamicSharedMemorySize, lds_main);
-        if (err != hipSuccess) return err;
-        const unsigned nblk = (unsigned)p.BH * p.nseg * p.ndvb;
-        hipLaunchKernelGGL((k_fused_fwd<DK, NW>), dim3(nblk), dim3(NW * 64), lds_main, stream, p);
+        switch (p.combo) {
+            case 0: return launch_main<DK, NW, kCombos[0].mloc, kCombos[0].topmax>(p, stream);
+            case 1: return launch_main<DK, NW, kCombos[1].mloc, kCombos[1].topmax>(p, stream);
+            case 2: return launch_main<DK, NW, kCombos[2].mloc, kCombos[2].topmax>(p, stream);
+            case 3: return launch_main<DK, NW, kCombos[3].mloc, kCombos[3].topmax>(p, stream);
+        }
+        return hipErrorInvalidValue;
     }
-    return hipGetLastError();
+    return hipSuccess;
 }
 
 template <int DK>
 hipError_t launch_fused_dk(const FusedParams& p, const FwdParams& scan, unsigned stages,
-                           hipStream_t s, int lm, int ls) {
+                           hipStream_t s) {
     switch (p.dvw) {
-        case 16: return launch_fused_t<DK, 1>(p, scan, stages, s, lm, ls);
-        case 32: return launch_fused_t<DK, 2>(p, scan, stages, s, lm, ls);
-        case 64: return launch_fused_t<DK, 4>(p, scan, stages, s, lm, ls);
+        case 16: return launch_fused_t<DK, 1>(p, scan, stages, s);
+        case 32: return launch_fused_t<DK, 2>(p, scan, stages, s);
+        case 64: return launch_fused_t<DK, 4>(p, scan, stages, s);
     }
     return hipErrorInvalidValue;
 }
@@ -714,12 +716,12 @@ hipError_t launch_fused_dk(const FusedParams& p, const FwdParams& scan, unsigned
 }  // namespace
 
 hipError_t launch_fused_fwd(const FusedParams& p, const FwdParams& scan, unsigned stages,
-                            int lds_main, int lds_seg, hipStream_t stream) {
+                            hipStream_t stream) {
     switch (p.dk) {
-        case 16: return launch_fused_dk<16>(p, scan, stages, stream, lds_main, lds_seg);
-        case 32: return launch_fused_dk<32>(p, scan, stages, stream, lds_main, lds_seg);
-        case 64: return launch_fused_dk<64>(p, scan, stages, stream, lds_main, lds_seg);
-        case 128: return launch_fused_dk<128>(p, scan, stages, stream, lds_main, lds_seg);
+        case 16: return launch_fused_dk<16>(p, scan, stages, stream);
+        case 32: return launch_fused_dk<32>(p, scan, stages, stream);
+        case 64: return launch_fused_dk<64>(p, scan, stages, stream);
+        case 128: return launch_fused_dk<128>(p, scan, stages, stream);
     }
     return hipErrorInvalidValue;
 }

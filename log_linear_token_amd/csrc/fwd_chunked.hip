@@ -177,6 +177,26 @@ __global__ __launch_bounds__(256) void k_fenwick_scan(FwdParams p) {
     const float* tot = p.tot + (size_t)bh * p.N;
     double* cum = p.cum + (size_t)bh * p.N;
 
+    // bf16 copy of each node in the operand order of the fused kernel's level
+    // products: [node][column block of 16][32-wide step][lane][8], lane 16g + m
+    // holding rows 4g..4g+3 (first half) and 16+4g..16+4g+3 (second half) of
+    // the step for column m; for d_k = 16 one step of 4 rows per lane.
+    bf16_t* frag = nullptr;
+    size_t fstride = 0;
+    if (p.gfrag) {
+        const int e = 4 * e4;
+        const int col = e / p.dk, d0 = e % p.dk;
+        const int cblk = col >> 4, m = col & 15;
+        size_t off;
+        if (p.dk >= 32) {
+            const int j = d0 >> 5, w32 = d0 & 31, half = w32 >> 4, g = (w32 & 15) >> 2;
+            off = (((size_t)cblk * (p.dk / 32) + j) * 64 + 16 * g + m) * 8 + 4 * half;
+        } else {
+            off = ((size_t)cblk * 64 + 16 * (d0 >> 2) + m) * 4;
+        }
+        fstride = (size_t)p.dv * p.dk;
+        frag = reinterpret_cast<bf16_t*>(p.gfrag) + (size_t)bh * p.N * fstride + off;
+    }
     float4 live[kScanLevels];
     double lcum[kScanLevels];
 #pragma unroll
@@ -216,6 +236,12 @@ __global__ __launch_bounds__(256) void k_fenwick_scan(FwdParams p) {
                     }
                 }
                 base[(size_t)i * per4] = acc;
+                if (frag) {
+                    bf16x4 h;
+                    h[0] = (__bf16)acc.x; h[1] = (__bf16)acc.y; h[2] = (__bf16)acc.z;
+                    h[3] = (__bf16)acc.w;
+                    *reinterpret_cast<bf16x4*>(frag + (size_t)i * fstride) = h;
+                }
                 if (e4 == 0) cum[i] = c;
             }
         }

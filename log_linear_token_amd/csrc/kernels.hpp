@@ -20,13 +20,14 @@ struct FwdParams {
     float* ust;          // workspace [BH][N][dv][dk]
     float* tot;          // workspace [BH][N]
     double* cum;         // workspace [BH][N]
+    bf16_t_storage* gfrag;  // optional bf16 copy of the nodes in MFMA fragment order
 };
 
 // workspace carving shared by the size query and the launch
 struct FwdWorkspace {
-    size_t ust_off, tot_off, cum_off, total;
+    size_t ust_off, tot_off, cum_off, frag_off, total;
 };
-FwdWorkspace fwd_workspace_layout(long BH, long N, int dk, int dv);
+FwdWorkspace fwd_workspace_layout(long BH, long N, int dk, int dv, bool frags);
 
 enum : unsigned { kStageChunkState = 1u, kStageScan = 2u, kStageOutput = 4u, kStageAll = 7u };
 hipError_t launch_fwd_chunked(const FwdParams& p, bool bf16, unsigned stages, hipStream_t stream);
@@ -35,7 +36,7 @@ hipError_t launch_fenwick_scan(const FwdParams& p, hipStream_t stream);
 
 // Fused tile-recurrent forward (bf16 inputs): 64-token tiles, segments of
 // 2^m tiles per block, Fenwick levels inside a segment held in registers.
-constexpr int kMaxLocal = 5;  // register-resident levels per block
+constexpr int kFusedMaxL = 24;  // lambda levels staged per token (whole rows)
 struct FusedParams {
     const bf16_t_storage* q;
     const bf16_t_storage* k;
@@ -43,19 +44,22 @@ struct FusedParams {
     const float* a;
     const float* lam;
     float* out;
-    int BH, T, dk, dv, L, LU;  // LU: levels the sequence uses (staged per token)
-    int ntiles, m, nseg, ntop, dvw, ndvb;
-    float* useg;   // [BH][nseg][dv][dk] segment states, then Fenwick nodes over segments
-    float* stot;   // [BH][nseg]
-    double* scum;  // [BH][nseg]
+    int BH, T, dk, dv, L, LU;       // LU: levels the sequence uses
+    int lpitch;                     // row pitch of lambda in LDS (L, or LU if L is too long)
+    int ntiles, m, nseg, ntop, dvw, ndvb, combo;
+    int lam_dma, a_dma;             // lambda / a rows of a whole tile are 16-byte aligned
+    float* useg;                    // [BH][nseg][dv][dk] segment states, then Fenwick nodes
+    float* stot;                    // [BH][nseg]
+    double* scum;                   // [BH][nseg]
+    const bf16_t_storage* gfrag;    // bf16 MFMA fragments of the nodes (written by the scan)
 };
 struct FusedPlan {
-    int ok, m, nseg, ntop, dvw, ndvb, ntiles, lds_main, lds_seg;
+    int ok, m, nseg, ntop, dvw, ndvb, ntiles, combo;
 };
 // force_m >= 0 asks for segments of 2^force_m tiles (plan fails if that does not fit)
 FusedPlan plan_fused(int BH, int T, int dk, int dv, int lu, int force_m);
 hipError_t launch_fused_fwd(const FusedParams& p, const FwdParams& scan, unsigned stages,
-                            int lds_main, int lds_seg, hipStream_t stream);
+                            hipStream_t stream);
 
 struct DecodeParams {
     float* states;            // [nseq][H][Lmax][dk][dv]

@@ -74,13 +74,14 @@ loglin_status check_fwd_sizes(int B, int H, int T, int dk, int dv, int C) {
 }  // namespace
 
 namespace loglin {
-FwdWorkspace fwd_workspace_layout(long BH, long N, int dk, int dv) {
+FwdWorkspace fwd_workspace_layout(long BH, long N, int dk, int dv, bool frags) {
     FwdWorkspace w{};
     if (N <= 1 || BH == 0) return w;
     w.ust_off = 0;
     w.tot_off = align_up(w.ust_off + (size_t)BH * N * dv * dk * sizeof(float));
     w.cum_off = align_up(w.tot_off + (size_t)BH * N * sizeof(float));
-    w.total = align_up(w.cum_off + (size_t)BH * N * sizeof(double));
+    w.frag_off = align_up(w.cum_off + (size_t)BH * N * sizeof(double));
+    w.total = frags ? align_up(w.frag_off + (size_t)BH * N * dv * dk * 2) : w.frag_off;
     return w;
 }
 }  // namespace loglin
@@ -126,7 +127,7 @@ Plan make_plan(long BH, int T, int dk, int dv, int C, loglin_dtype dt) {
             pl.N = f.nseg;
         }
     }
-    pl.ws = fwd_workspace_layout(BH, pl.N, dk, dv);
+    pl.ws = fwd_workspace_layout(BH, pl.N, dk, dv, pl.path == kPathFused);
     return pl;
 }
 
@@ -264,7 +265,19 @@ loglin_status loglin_fwd_chunked_stages(const void* q, const void* k, const void
         fp.useg = p.ust;
         fp.stot = p.tot;
         fp.scum = p.cum;
-        e = launch_fused_fwd(fp, p, stage_mask, f.lds_main, f.lds_seg, hs);
+        fp.combo = f.combo;
+        // lambda rows are copied whole when they fit the kernel's staging area
+        // and every tile's rows start on a 16-byte boundary; otherwise the
+        // levels in use are loaded element by element
+        fp.lpitch = L <= kFusedMaxL ? L : fp.LU;
+        fp.lam_dma = L <= kFusedMaxL && ((long)T * L) % 4 == 0 &&
+                     reinterpret_cast<uintptr_t>(lambda) % 16 == 0;
+        fp.a_dma = T % 4 == 0 && reinterpret_cast<uintptr_t>(log_decay) % 16 == 0;
+        if (w.total > 0) {
+            p.gfrag = reinterpret_cast<bf16_t_storage*>(static_cast<char*>(workspace) + w.frag_off);
+            fp.gfrag = p.gfrag;
+        }
+        e = launch_fused_fwd(fp, p, stage_mask, hs);
     } else {
         e = launch_fwd_chunked(p, in_dtype == LOGLIN_BF16, stage_mask, hs);
     }
