@@ -45,6 +45,10 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
+#ifndef LOGLIN_FUSED_NH
+#define LOGLIN_FUSED_NH 1
+#endif
+
 constexpr int TC = 64;        // tokens per tile
 constexpr int NRB = TC / 16;  // 16-row blocks per tile
 constexpr int LOGTC = 6;
@@ -104,8 +108,32 @@ __device__ __forceinline__ bf16x8 ld_tr8(const bf16_t* t, int k0, int n0) {
     return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
 }
 
+// 16 bytes per lane from global memory into LDS at lds + 16 * lane (lds is
+// uniform over the wave).  Written as inline assembly so that the compiler
+// does not track these loads: it would otherwise wait for them before the
+// first read of any LDS buffer.  Completion is awaited explicitly with
+// s_waitcnt vmcnt(0) before the barrier that publishes a tile.
 __device__ __forceinline__ void dma16(const void* g, void* lds) {
-    __builtin_amdgcn_global_load_lds((glb_void_t*)g, (lds_void_t*)lds, 16, 0, 0);
+    // the low 32 bits of a generic pointer into LDS are the LDS address
+    const uint32_t l = (uint32_t)(uintptr_t)lds;
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, off"
+        :
+        : "s"(__builtin_amdgcn_readfirstlane(l)), "v"(g)
+        : "memory", "m0");
+}
+// 4 bytes per lane into LDS at lds + 4 * lane (any 4-byte alignment)
+__device__ __forceinline__ void dma4(const void* g, void* lds) {
+    const uint32_t l = (uint32_t)(uintptr_t)lds;
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dword %1, off"
+        :
+        : "s"(__builtin_amdgcn_readfirstlane(l)), "v"(g)
+        : "memory", "m0");
 }
 
 // Copies rows [0, 64) of a bf16 [rows][pitch] matrix, columns [col0, col0 + D),
@@ -157,92 +185,83 @@ struct HD {
 // Tile-local decay of one wave: lane s gets A_s (inclusive cumsum of a over
 // the tile); the wave's private LDS rows receive A and e_s = exp(A_end - A_s).
 // Returns the tile total A_end, uniform over the wave.
+// DPP controls (GFX9): row_shr:n shifts within rows of 16 lanes; row_bcast
+// 15 / 31 broadcast lane 15 of each row (31 of each half) to the next rows.
+template <int CTRL, int ROWMASK>
+__device__ __forceinline__ float dpp_or_zero(float x) {
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, ROWMASK, 0xf, false));
+}
+
+// Inclusive prefix sum over the 64 lanes of a wave (Hillis-Steele within rows
+// of 16 lanes, then the row totals carried across rows).
+__device__ __forceinline__ float wave_inclusive_sum(float x) {
+    x += dpp_or_zero<0x111, 0xf>(x);  // row_shr:1
+    x += dpp_or_zero<0x112, 0xf>(x);  // row_shr:2
+    x += dpp_or_zero<0x114, 0xf>(x);  // row_shr:4
+    x += dpp_or_zero<0x118, 0xf>(x);  // row_shr:8
+    x += dpp_or_zero<0x142, 0xa>(x);  // row_bcast:15 into rows 1 and 3
+    x += dpp_or_zero<0x143, 0xc>(x);  // row_bcast:31 into rows 2 and 3
+    return x;
+}
+
 __device__ __forceinline__ float tile_decay(const float* a_tile, float* Aw, float* Ew) {
     const int lane = threadIdx.x & 63;
-    float x = a_tile[lane];
-#pragma unroll
-    for (int off = 1; off < 64; off <<= 1) {
-        const float y = __shfl_up(x, off, 64);
-        if (lane >= off) x += y;
-    }
-    const float end = wave_uniform(__shfl(x, 63, 64));
+    const float x = wave_inclusive_sum(a_tile[lane]);
+    const float end = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
     Aw[lane] = x;
     Ew[lane] = __expf(end - x);
     return end;
 }
 
-template <int N>
-__device__ __forceinline__ float pick(const float (&x)[N], int idx) {
-    float r = x[0];
-#pragma unroll
-    for (int l = 1; l < N; ++l) r = idx == l ? x[l] : r;
-    return r;
-}
-
-// Masked, weighted scores of row block RB against key blocks 0..RB, to the P
-// tile as bf16.  The block past the diagonal that the K=32 product pairs with
-// an even RB is written as zeros.
-template <int DK, int RB>
-__device__ __forceinline__ void tile_scores(const bf16_t* Qs, const bf16_t* Ks, bf16_t* Ps,
-                                            const float* Aw, const float* lam_s, int L) {
+// One 16 x 16 block of masked, weighted scores (rows 16 rb.., keys 16 sb..) to
+// the P tile as bf16.  The diagonal block of an even row block also writes the
+// block past the diagonal, which the K=32 P V product pairs with it, as zeros.
+template <int DK>
+__device__ __forceinline__ void score_block(int rb, int sb, const bf16_t* Qs, const bf16_t* Ks,
+                                            bf16_t* Ps, const float* Aw, const float* lam_s,
+                                            int L) {
     typedef HD<DK> H;
     const int lane = threadIdx.x & 63, m16 = lane & 15, g = lane >> 4;
-    const int t = 16 * RB + m16;
-    f32x4 acc[RB + 1];
-#pragma unroll
-    for (int sb = 0; sb <= RB; ++sb) acc[sb] = f32x4{0.f, 0.f, 0.f, 0.f};
+    const int t = 16 * rb + m16;
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < H::NKS; ++ks) {
-        typename H::frag qb;
-        if constexpr (DK >= 32) qb = ld8<DK>(Qs, t, ks * 32 + 8 * g);
-        else qb = ld4<DK>(Qs, t, 4 * g);
-#pragma unroll
-        for (int sb = 0; sb <= RB; ++sb) {
-            typename H::frag ka;
-            if constexpr (DK >= 32) ka = ld8<DK>(Ks, 16 * sb + m16, ks * 32 + 8 * g);
-            else ka = ld4<DK>(Ks, 16 * sb + m16, 4 * g);
-            acc[sb] = mma(ka, qb, acc[sb]);
-        }
+        if constexpr (DK >= 32)
+            acc = mma(ld8<DK>(Ks, 16 * sb + m16, ks * 32 + 8 * g), ld8<DK>(Qs, t, ks * 32 + 8 * g), acc);
+        else
+            acc = mma(ld4<DK>(Ks, 16 * sb + m16, 4 * g), ld4<DK>(Qs, t, 4 * g), acc);
     }
     const float* lam_t = lam_s + t * L;  // levels inside a tile are < L (see the host checks)
     const float At = Aw[t];
+    const float4 As = *reinterpret_cast<const float4*>(Aw + 16 * sb + 4 * g);
+    const float Asv[4] = {As.x, As.y, As.z, As.w};
+    float w[4];
 #pragma unroll
-    for (int sb = 0; sb <= RB; ++sb) {
-        const float4 As = *reinterpret_cast<const float4*>(Aw + 16 * sb + 4 * g);
-        const float Asv[4] = {As.x, As.y, As.z, As.w};
-        float w[4];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int s = 16 * sb + 4 * g + i;
-            w[i] = s <= t ? acc[sb][i] * lam_t[fenwick_level(t, s)] * __expf(At - Asv[i]) : 0.f;
-        }
-        *reinterpret_cast<bf16x4*>(Ps + t * PROW + 16 * sb + 4 * g) = pack4(w[0], w[1], w[2], w[3]);
+    for (int i = 0; i < 4; ++i) {
+        const int s = 16 * sb + 4 * g + i;
+        w[i] = s <= t ? acc[i] * lam_t[fenwick_level(t, s)] * __expf(At - Asv[i]) : 0.f;
     }
-    if constexpr ((RB & 1) == 0 && RB + 1 < NRB)
-        *reinterpret_cast<bf16x4*>(Ps + t * PROW + 16 * (RB + 1) + 4 * g) = bf16x4{};
+    *reinterpret_cast<bf16x4*>(Ps + t * PROW + 16 * sb + 4 * g) = pack4(w[0], w[1], w[2], w[3]);
+    if (sb == rb && (rb & 1) == 0)
+        *reinterpret_cast<bf16x4*>(Ps + t * PROW + 16 * (rb + 1) + 4 * g) = bf16x4{};
 }
 
-template <int DK, int NW>
+// The ten causal 16 x 16 score blocks of a tile, dealt round-robin to the waves.
+template <int DK, int NWT>
 __device__ __forceinline__ void scores_for_wave(int wave, const bf16_t* Qs, const bf16_t* Ks,
                                                 bf16_t* Ps, const float* Aw, const float* lam_s,
                                                 int L) {
-#pragma unroll
-    for (int rb0 = 0; rb0 < NRB; rb0 += NW) {
-        switch (rb0 + wave) {
-            case 0: tile_scores<DK, 0>(Qs, Ks, Ps, Aw, lam_s, L); break;
-            case 1: tile_scores<DK, 1>(Qs, Ks, Ps, Aw, lam_s, L); break;
-            case 2: tile_scores<DK, 2>(Qs, Ks, Ps, Aw, lam_s, L); break;
-            case 3: tile_scores<DK, 3>(Qs, Ks, Ps, Aw, lam_s, L); break;
-            default: break;
-        }
+    for (int tau = wave; tau < NRB * (NRB + 1) / 2; tau += NWT) {
+        const int rb = tau < 1 ? 0 : tau < 3 ? 1 : tau < 6 ? 2 : 3;
+        score_block<DK>(rb, tau - rb * (rb + 1) / 2, Qs, Ks, Ps, Aw, lam_s, L);
     }
 }
 
-// U (d_k x this wave's 16 columns) of the staged tile, U = K^T diag(e) V:
-// u[kt] (C layout) holds U[16 kt + 4g + i][column m16].  vf[sp] are the V
-// fragments (lane: V[32 sp + 8g + i][column]) shared with the P V product.
-template <int DK, int DVW>
-__device__ __forceinline__ void tile_state(f32x4 (&u)[DK / 16], const bf16_t* Ks,
+// Rows [16 kt0, 16 (kt0 + NT)) of U = K^T diag(e) V for this wave's 16 columns:
+// u[kt] (C layout) holds U[16 (kt0 + kt) + 4g + i][column m16].  vf[sp] are the
+// V fragments (lane: V[32 sp + 8g + i][column]) shared with the P V product.
+template <int DK, int NT>
+__device__ __forceinline__ void tile_state(f32x4 (&u)[NT], int kt0, const bf16_t* Ks,
                                            const bf16x8 (&vf)[2], const float* Ew) {
     const int lane = threadIdx.x & 63, g = lane >> 4;
 #pragma unroll
@@ -254,7 +273,8 @@ __device__ __forceinline__ void tile_state(f32x4 (&u)[DK / 16], const bf16_t* Ks
 #pragma unroll
         for (int i = 0; i < 8; ++i) b[i] = (__bf16)((float)vf[sp][i] * ev[i]);
 #pragma unroll
-        for (int kt = 0; kt < DK / 16; ++kt) u[kt] = mma(ld_tr8<DK>(Ks, 32 * sp, 16 * kt), b, u[kt]);
+        for (int kt = 0; kt < NT; ++kt)
+            u[kt] = mma(ld_tr8<DK>(Ks, 32 * sp, 16 * (kt0 + kt)), b, u[kt]);
     }
 }
 
@@ -305,7 +325,7 @@ __global__ __launch_bounds__(NW * 64) void k_seg_state(FusedParams p) {
         if (p.a_dma) {
             if (wave == 0 && lane < TC / 4) dma16(p.a + r + 4 * lane, ad);
         } else if (wave == 0) {
-            ad[lane] = p.a[r + lane];
+            dma4(p.a + r + lane, ad);
         }
     };
 
@@ -328,7 +348,7 @@ __global__ __launch_bounds__(NW * 64) void k_seg_state(FusedParams p) {
         bf16x8 vf[2];
         vf[0] = ld_tr8<DVW>(Vc, 0, 16 * wave);
         vf[1] = ld_tr8<DVW>(Vc, 32, 16 * wave);
-        tile_state<DK, DVW>(u, Kc, vf, sEw[wave]);
+        tile_state<DK, NDT>(u, 0, Kc, vf, sEw[wave]);
         total += tot;
     };
 
@@ -348,14 +368,22 @@ __global__ __launch_bounds__(NW * 64) void k_seg_state(FusedParams p) {
 
 // ---------------------------------------------------------------------------
 // Main fused kernel: one block per (bh, segment, column block).
+//   NW      waves per 16-column slab set (the block covers 16 NW columns)
+//   NH      waves per column slab; each holds 1/NH of the head dimension of
+//           every state and contracts only over that part, the partial level
+//           products of the NH waves of a slab being summed through LDS
 //   MLOC    register-resident levels inside a segment (segments of <= 2^MLOC tiles)
 //   TOPMAX  levels above the segment held as bf16 fragments
 
-template <int DK, int NW, int MLOC, int TOPMAX>
-__global__ __launch_bounds__(NW * 64, 1) void k_fused_fwd(FusedParams p) {
+template <int DK, int NW, int NH, int MLOC, int TOPMAX>
+__global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
     typedef HD<DK> H;
+    constexpr int NWT = NW * NH;            // waves per block
     constexpr int DVW = NW * 16;
-    constexpr int NDT = H::NDT, NKS = H::NKS;
+    constexpr int NKSH = H::NKS / NH;       // contraction steps of this wave's head-dim part
+    constexpr int NDTH = H::NDT / NH;       // 16-row state blocks of this wave's part
+    constexpr int RBH = NRB / NH;           // row blocks whose output this wave writes
+    static_assert(NKSH >= 1 && NDTH >= 1, "head dimension too small for the split");
     __shared__ __align__(16) bf16_t sQ0[TC * DK];
     __shared__ __align__(16) bf16_t sQ1[TC * DK];
     __shared__ __align__(16) bf16_t sK0[TC * DK];
@@ -367,8 +395,9 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_fwd(FusedParams p) {
     __shared__ __align__(16) float sa0[TC];
     __shared__ __align__(16) float sa1[TC];
     __shared__ __align__(16) bf16_t sP[TC * PROW];
-    __shared__ __align__(16) float sAw[NW][TC];
-    __shared__ __align__(16) float sEw[NW][TC];
+    __shared__ __align__(16) float sAw[NWT][TC];
+    __shared__ __align__(16) float sEw[NWT][TC];
+    __shared__ __align__(16) f32x4 sX[(NH > 1 ? NW * NRB : 1) * 64];  // partial outputs
 
     int blk = xcd_block(blockIdx.x, gridDim.x);
     const int dvb = blk % p.ndvb;
@@ -377,9 +406,11 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_fwd(FusedParams p) {
     const int bh = blk / p.nseg;
     const int cb = dvb * DVW;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int cs = wave % NW, hh = wave / NW;  // column slab, head-dim part
     const int lane = threadIdx.x & 63, m16 = lane & 15, g = lane >> 4;
     const int tid = threadIdx.x;
-    const int c0 = cb + wave * 16;  // first column of this wave
+    const int c0 = cb + cs * 16;  // first column of this wave
+    const int ks0 = hh * NKSH, kt0 = hh * NDTH;
     const size_t row0 = (size_t)bh * p.T;
     const int tile0 = seg << p.m;
     const int ntl = min(1 << p.m, p.ntiles - tile0);
@@ -387,7 +418,7 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_fwd(FusedParams p) {
     const int LP = p.lpitch;   // lambda row length in LDS
 
     // levels above the segment: Fenwick nodes over segments, bf16 fragments
-    typename H::frag top[TOPMAX][NKS];
+    typename H::frag top[TOPMAX][NKSH];
     float logd_top[TOPMAX];
 #pragma unroll
     for (int q = 0; q < TOPMAX; ++q) {
@@ -398,67 +429,61 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_fwd(FusedParams p) {
             logd_top[q] = (float)(cum[seg - 1] - cum[node]);
             const size_t ng = (size_t)bh * p.nseg + node;
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
+            for (int ks = 0; ks < NKSH; ++ks)
                 top[q][ks] = *reinterpret_cast<const typename H::frag*>(
-                    p.gfrag + frag_index<DK>(ng, p.dv / 16, c0 / 16, ks));
+                    p.gfrag + frag_index<DK>(ng, p.dv / 16, c0 / 16, ks0 + ks));
         } else {
 #pragma unroll
-            for (int ks = 0; ks < NKS; ++ks) top[q][ks] = typename H::frag{};
+            for (int ks = 0; ks < NKSH; ++ks) top[q][ks] = typename H::frag{};
         }
     }
 
-    // lambda and a of a tile: LDS-DMA when the rows are 16-byte aligned and
-    // whole, plain loads (staged through registers) otherwise
-    constexpr int NLR = (TC * kFusedMaxL + NW * 64 - 1) / (NW * 64);
-    float lam_r[NLR];
-    float a_r = 0.f;
+    // Every tile input goes global -> LDS through the DMA path: 16-byte
+    // copies where rows are whole and aligned, 4-byte copies of lambda and a
+    // otherwise (entries past the sequence are stored as zeros).
     auto issue = [&](int il, bf16_t* Qd, bf16_t* Kd, bf16_t* Vd, float* Ld, float* ad)
-        __attribute__((always_inline)) -> bool {
+        __attribute__((always_inline)) {
         const int t0 = (tile0 + il) * TC;
         const int nvalid = min(TC, p.T - t0);
         const size_t r = row0 + t0;
-        dma_tile<DK, NW>(p.q + r * DK, DK, 0, nvalid, Qd, wave);
-        dma_tile<DK, NW>(p.k + r * DK, DK, 0, nvalid, Kd, wave);
-        dma_tile<DVW, NW>(p.v + r * p.dv, p.dv, cb, nvalid, Vd, wave);
+        dma_tile<DK, NWT>(p.q + r * DK, DK, 0, nvalid, Qd, wave);
+        dma_tile<DK, NWT>(p.k + r * DK, DK, 0, nvalid, Kd, wave);
+        dma_tile<DVW, NWT>(p.v + r * p.dv, p.dv, cb, nvalid, Vd, wave);
         const bool whole = nvalid == TC;
         if (whole && p.lam_dma) {
             const int nch = 16 * L;  // 64 rows x L floats
-            for (int u = wave; u * 64 < nch; u += NW)
+            for (int u = wave; u * 64 < nch; u += NWT)
                 if (u * 64 + lane < nch) dma16(p.lam + r * L + 4 * (u * 64 + lane), Ld + u * 256);
         } else {
-#pragma unroll
-            for (int k = 0; k < NLR; ++k) {
-                const int x = tid + k * NW * 64;
-                const int row = x / LP, l = x - row * LP;
-                lam_r[k] = x < nvalid * LP ? p.lam[(r + row) * L + l] : 0.f;
+            const int nel = nvalid * LP;
+            for (int u = wave; u * 64 < TC * LP; u += NWT) {
+                const int x = u * 64 + lane;
+                if (x < nel) {
+                    const int row = x / LP, l = x - row * LP;
+                    dma4(p.lam + (r + row) * L + l, Ld + u * 64);
+                } else if (x < TC * LP) {
+                    Ld[x] = 0.f;
+                }
             }
         }
-        if (whole && p.a_dma) {
-            if (wave == 0 && lane < TC / 4) dma16(p.a + r + 4 * lane, ad);
-        } else if (tid < TC) {
-            a_r = tid < nvalid ? p.a[r + tid] : 0.f;
-        }
-        return whole;
-    };
-    // completes the plain-load part of issue() (called before the next barrier)
-    auto finish = [&](int il, bool whole, float* Ld, float* ad) __attribute__((always_inline)) {
-        if (!(whole && p.lam_dma)) {
-#pragma unroll
-            for (int k = 0; k < NLR; ++k) {
-                const int x = tid + k * NW * 64;
-                if (x < TC * LP) Ld[x] = lam_r[k];
+        if (wave == 0) {
+            if (whole && p.a_dma) {
+                if (lane < TC / 4) dma16(p.a + r + 4 * lane, ad);
+            } else if (lane < nvalid) {
+                dma4(p.a + r + lane, ad);
+            } else {
+                ad[lane] = 0.f;
             }
         }
-        if (!(whole && p.a_dma) && tid < TC) ad[tid] = a_r;
     };
 
-    f32x4 G[MLOC][NDT];
+    f32x4 G[MLOC][NDTH];
     float logd_loc[MLOC];
 #pragma unroll
     for (int s = 0; s < MLOC; ++s) {
         logd_loc[s] = 0.f;
 #pragma unroll
-        for (int kt = 0; kt < NDT; ++kt) G[s][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int kt = 0; kt < NDTH; ++kt) G[s][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
     auto body = [&](int il, const bf16_t* Qc, const bf16_t* Kc, const bf16_t* Vc,
@@ -467,32 +492,30 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_fwd(FusedParams p) {
         // tile il is in LDS and every wave is done with tile il - 1
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        bool next_whole = true;
-        if (il + 1 < ntl) next_whole = issue(il + 1, Qn, Kn, Vn, Ln, an);
+        if (il + 1 < ntl) issue(il + 1, Qn, Kn, Vn, Ln, an);
         const int i = tile0 + il;
         const int nvalid = min(TC, p.T - i * TC);
         const float tot = tile_decay(ac, sAw[wave], sEw[wave]);
-        scores_for_wave<DK, NW>(wave, Qc, Kc, sP, sAw[wave], Lc, LP);
+        scores_for_wave<DK, NWT>(wave, Qc, Kc, sP, sAw[wave], Lc, LP);
         __syncthreads();
 
-        // ---- outputs of this wave's 16 columns, all rows of the tile
+        // ---- outputs of this wave's 16 columns: intra-tile P V for the row
+        // blocks it writes, level products (its head-dim part) for all rows
         bf16x8 vf[2];
-        vf[0] = ld_tr8<DVW>(Vc, 0, 16 * wave);
-        vf[1] = ld_tr8<DVW>(Vc, 32, 16 * wave);
+        vf[0] = ld_tr8<DVW>(Vc, 0, 16 * cs);
+        vf[1] = ld_tr8<DVW>(Vc, 32, 16 * cs);
         f32x4 o[NRB];
-        float At[NRB];
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) o[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
-            o[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            At[rb] = sAw[wave][16 * rb + m16];
-        }
+            if (rb / RBH == hh) {
 #pragma unroll
-        for (int sp = 0; sp < NRB / 2; ++sp) {
-#pragma unroll
-            for (int rb = 2 * sp; rb < NRB; ++rb) {
-                const bf16x8 pb =
-                    *reinterpret_cast<const bf16x8*>(sP + (16 * rb + m16) * PROW + 32 * sp + 8 * g);
-                o[rb] = mma(vf[sp], pb, o[rb]);
+                for (int sp = 0; sp <= rb / 2; ++sp) {
+                    const bf16x8 pb = *reinterpret_cast<const bf16x8*>(sP + (16 * rb + m16) * PROW +
+                                                                       32 * sp + 8 * g);
+                    o[rb] = mma(vf[sp], pb, o[rb]);
+                }
             }
         }
         // Q fragment in the head-dim order of the register states:
@@ -508,31 +531,32 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_fwd(FusedParams p) {
             }
             return r;
         };
-        auto add_level = [&](const typename H::frag (&ga)[NKS], int lev, float logd)
+        // one row block at a time keeps few operands live
+        auto add_level = [&](const typename H::frag (&ga)[NKSH], int lev, float logd)
             __attribute__((always_inline)) {
-            f32x4 y[NRB];
-#pragma unroll
-            for (int rb = 0; rb < NRB; ++rb) y[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < NKS; ++ks)
-#pragma unroll
-                for (int rb = 0; rb < NRB; ++rb) y[rb] = mma(ga[ks], qfrag(rb, ks), y[rb]);
+            // re-read the Q fragments for every level rather than keeping them
+            // live across levels (registers are the scarce resource here)
+            asm volatile("" ::: "memory");
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb) {
-                const float w = Lc[(16 * rb + m16) * LP + lev] * __expf(At[rb] + logd);
-                o[rb][0] += w * y[rb][0];
-                o[rb][1] += w * y[rb][1];
-                o[rb][2] += w * y[rb][2];
-                o[rb][3] += w * y[rb][3];
+                f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < NKSH; ++ks) y = mma(ga[ks], qfrag(rb, ks0 + ks), y);
+                const float w = Lc[(16 * rb + m16) * LP + lev] *
+                                __expf(sAw[wave][16 * rb + m16] + logd);
+                o[rb][0] += w * y[0];
+                o[rb][1] += w * y[1];
+                o[rb][2] += w * y[2];
+                o[rb][3] += w * y[3];
             }
         };
         // levels inside the segment
 #pragma unroll
         for (int s = 0; s < MLOC; ++s) {
             if (s < p.m && ((il >> s) & 1)) {
-                typename H::frag ga[NKS];
+                typename H::frag ga[NKSH];
 #pragma unroll
-                for (int ks = 0; ks < NKS; ++ks) {
+                for (int ks = 0; ks < NKSH; ++ks) {
                     if constexpr (DK >= 32) ga[ks] = cvt8(G[s][2 * ks], G[s][2 * ks + 1]);
                     else ga[ks] = cvt4(G[s][ks]);
                 }
@@ -544,11 +568,25 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_fwd(FusedParams p) {
         for (int q = 0; q < TOPMAX; ++q)
             if (q < p.ntop && ((seg >> q) & 1)) add_level(top[q], LOGTC + p.m + q + 1, logd_top[q]);
 
+        // sum the head-dim parts: each wave hands over the rows it does not write
+        if constexpr (NH > 1) {
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb)
+                if (rb / RBH != hh) sX[(cs * NRB + rb) * 64 + lane] = o[rb];
+            __syncthreads();
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb) {
+                if (rb / RBH == hh) {
+                    const f32x4 x = sX[(cs * NRB + rb) * 64 + lane];
+                    o[rb][0] += x[0]; o[rb][1] += x[1]; o[rb][2] += x[2]; o[rb][3] += x[3];
+                }
+            }
+        }
         float* orow = p.out + (row0 + (size_t)i * TC) * p.dv + c0 + 4 * g;
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
             const int r = 16 * rb + m16;
-            if (r < nvalid)
+            if (rb / RBH == hh && r < nvalid)
                 *reinterpret_cast<float4*>(orow + (size_t)r * p.dv) =
                     make_float4(o[rb][0], o[rb][1], o[rb][2], o[rb][3]);
         }
@@ -556,17 +594,17 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_fwd(FusedParams p) {
         // ---- Fenwick update over tiles: fold the tile's state and the slots
         // below lssb(il + 1) into slot lssb(il + 1)
         if (il + 1 < ntl) {
-            f32x4 u[NDT];
+            f32x4 u[NDTH];
 #pragma unroll
-            for (int kt = 0; kt < NDT; ++kt) u[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            tile_state<DK, DVW>(u, Kc, vf, sEw[wave]);
+            for (int kt = 0; kt < NDTH; ++kt) u[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+            tile_state<DK, NDTH>(u, kt0, Kc, vf, sEw[wave]);
             const int j = lssb((uint64_t)il + 1);
 #pragma unroll
             for (int s = 0; s < MLOC; ++s) {
                 if (s < j) {
                     const float w = __expf(logd_loc[s] + tot);
 #pragma unroll
-                    for (int kt = 0; kt < NDT; ++kt) {
+                    for (int kt = 0; kt < NDTH; ++kt) {
                         u[kt][0] += w * G[s][kt][0];
                         u[kt][1] += w * G[s][kt][1];
                         u[kt][2] += w * G[s][kt][2];
@@ -578,22 +616,18 @@ __global__ __launch_bounds__(NW * 64, 1) void k_fused_fwd(FusedParams p) {
             for (int s = 0; s < MLOC; ++s) {
                 if (s == j) {
 #pragma unroll
-                    for (int kt = 0; kt < NDT; ++kt) G[s][kt] = u[kt];
+                    for (int kt = 0; kt < NDTH; ++kt) G[s][kt] = u[kt];
                     logd_loc[s] = 0.f;
                 } else {
                     logd_loc[s] += tot;
                 }
             }
-            finish(il + 1, next_whole, Ln, an);
         }
 #pragma unroll
         for (int q = 0; q < TOPMAX; ++q) logd_top[q] += tot;
     };
 
-    {
-        const bool w0 = issue(0, sQ0, sK0, sV0, sL0, sa0);
-        finish(0, w0, sL0, sa0);
-    }
+    issue(0, sQ0, sK0, sV0, sL0, sa0);
     for (int il = 0; il < ntl; il += 2) {
         body(il, sQ0, sK0, sV0, sL0, sa0, sQ1, sK1, sV1, sL1, sa1);
         if (il + 1 < ntl) body(il + 1, sQ1, sK1, sV1, sL1, sa1, sQ0, sK0, sV0, sL0, sa0);
@@ -670,9 +704,10 @@ namespace {
 
 template <int DK, int NW, int MLOC, int TOPMAX>
 hipError_t launch_main(const FusedParams& p, hipStream_t stream) {
+    constexpr int NH = LOGLIN_FUSED_NH;  // waves sharing a column slab (head-dim split)
     const unsigned nblk = (unsigned)p.BH * p.nseg * p.ndvb;
-    hipLaunchKernelGGL((k_fused_fwd<DK, NW, MLOC, TOPMAX>), dim3(nblk), dim3(NW * 64), 0, stream,
-                       p);
+    hipLaunchKernelGGL((k_fused_fwd<DK, NW, NH, MLOC, TOPMAX>), dim3(nblk), dim3(NW * NH * 64), 0,
+                       stream, p);
     return hipGetLastError();
 }
 
