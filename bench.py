@@ -17,6 +17,7 @@ stderr.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -34,6 +35,26 @@ from log_linear_token_amd import loglin as LL  # noqa: E402
 
 HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0    # dense bf16 MFMA, TFLOP/s
+
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd8k_decode_hbm_traffic.txt")
+
+
+def measured_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed counter summary, or
+    None when there is none or the kernel's source has changed since."""
+    try:
+        with open(TRAFFIC_FILE) as f:
+            for ln in f:
+                parts = ln.split()
+                if len(parts) == 5 and parts[0] == "traffic" and parts[1] == kernel:
+                    with open(os.path.join(ROOT, parts[3]), "rb") as src:
+                        if hashlib.sha256(src.read()).hexdigest()[:16] != parts[4]:
+                            return None
+                    return float(parts[2])
+    except OSError:
+        return None
+    return None
 
 
 def log(msg: str) -> None:
@@ -239,7 +260,7 @@ def main() -> int:
     km = kernels[dom]
     roof = {"kernel": dom, "bound": "hbm", "achieved": round(km["GB/s"], 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(km["GB/s"] / HBM_PEAK_GBS, 4),
-            "traffic": None,
+            "traffic": measured_traffic(dom),
             "mfma": {"achieved": round(km["TFLOP/s"], 2), "peak": BF16_PEAK_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(km["TFLOP/s"] / BF16_PEAK_TFLOPS, 4)}}
 
@@ -304,7 +325,8 @@ def bench_decode(steps: int) -> dict:
                                        "dk": cfg.dk, "dv": cfg.dv, "Lmax": cfg.Lmax},
             "roofline": {"kernel": "decode_step", "bound": "hbm", "achieved": round(gbs, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(gbs / HBM_PEAK_GBS, 4), "traffic": None,
+                         "frac": round(gbs / HBM_PEAK_GBS, 4),
+                         "traffic": measured_traffic("decode_step"),
                          "alg_bytes_per_step": byts}}
 
 
