@@ -113,11 +113,14 @@ def fwd_models(cfg, plan) -> dict:
             local_reads += sum(bin(il).count("1") for il in range(n))
             top_reads += n * bin(s).count("1")
             states += n - 1
+        nsub = plan["state_split"]
         return {
             "seg_state": {"bytes": BH * tiles_pre * tile * (2 * (dk + dv) + 4)
-                          + BH * (nseg - 1) * (st + 4),
+                          + BH * (nseg - 1) * nsub * (st + 4),
                           "flops": BH * tiles_pre * tile * 2 * dk * dv},
-            "fenwick_scan": {"bytes": BH * (nseg - 1) * (2 * st + 4 + 8), "flops": 0},
+            # reads the sub-range states, writes each node in fp32 and bf16
+            "fenwick_scan": {"bytes": BH * (nseg - 1) * (nsub * (st + 4) + st + st // 2 + 8),
+                             "flops": 0},
             "fused_fwd": {"bytes": BH * T * (tok_in + tok_out) + BH * (nseg - 1) * (st + 8),
                           "flops": BH * (ntiles * intra + (states + local_reads + top_reads)
                                          * tile * 2 * dk * dv)},

@@ -80,6 +80,8 @@ typedef struct {
     int nseg;            /* chunks (chunked) or segments (fused) per sequence */
     int col_block;       /* output columns per block */
     int coarse_levels;   /* levels carried between chunks / segments through the scan */
+    int state_split;     /* fused path: each segment state is summed from this many
+                            sub-range states (1 on the chunked path) */
     size_t workspace_bytes;
 } loglin_fwd_plan_t;
 

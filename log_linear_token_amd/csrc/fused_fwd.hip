@@ -14,7 +14,9 @@
 //   - the tile's own state U = K^T diag(e^(A_end - A_s)) V (MFMA), folded by
 //     the Fenwick update of section 2, run over tiles, together with the
 //     levels below lssb(tile + 1) into the next level.
-// Levels inside the segment live in registers as fp32 MFMA accumulators.
+// Levels inside the segment live in registers as bf16 MFMA operands; the
+// Fenwick merge that builds a level sums in fp32 (tile state, decayed lower
+// levels) and rounds the result once.
 // The levels above the segment are the same for all of its tiles; a
 // segment-state kernel (k_seg_state) and the Fenwick scan over segments
 // (fenwick_scan in fwd_chunked.hip) provide them as bf16 MFMA operand
@@ -29,7 +31,9 @@
 // read with the LDS transpose read (ds_read_b64_tr_b16), so no transposed
 // copy is ever written.
 //
-// One wave owns 16 columns of d_v and computes them for all 64 rows of a tile.
+// Two waves own 16 columns of d_v (for d_k >= 64; one wave otherwise): each
+// holds half of the head dimension of every level state, contracts over it,
+// and the halves of the level products are summed through LDS.
 #include <type_traits>
 
 #include "common.hpp"
@@ -45,9 +49,6 @@ typedef __attribute__((address_space(3))) void lds_void_t;
 typedef __attribute__((address_space(1))) void glb_void_t;
 typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4;
 
-#ifndef LOGLIN_FUSED_NH
-#define LOGLIN_FUSED_NH 1
-#endif
 
 constexpr int TC = 64;        // tokens per tile
 constexpr int NRB = TC / 16;  // 16-row blocks per tile
@@ -307,16 +308,20 @@ __global__ __launch_bounds__(NW * 64) void k_seg_state(FusedParams p) {
     __shared__ __align__(16) float sEw[NW][TC];
 
     const int nsegs = p.nseg - 1;
+    const int nsub = 1 << (p.m - p.msub);
     int blk = xcd_block(blockIdx.x, gridDim.x);
     const int dvb = blk % p.ndvb;
     blk /= p.ndvb;
+    const int sub = blk % nsub;
+    blk /= nsub;
     const int seg = blk % nsegs;
     const int bh = blk / nsegs;
     const int cb = dvb * DVW;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, m16 = lane & 15, g = lane >> 4;
     const size_t row0 = (size_t)bh * p.T;
-    const int tile0 = seg << p.m, ntl = 1 << p.m;  // every tile of a non-last segment is full
+    // every tile of a non-last segment is whole
+    const int tile0 = (seg << p.m) + (sub << p.msub), ntl = 1 << p.msub;
 
     auto issue = [&](int il, bf16_t* Kd, bf16_t* Vd, float* ad) __attribute__((always_inline)) {
         const size_t r = row0 + (size_t)(tile0 + il) * TC;
@@ -357,13 +362,16 @@ __global__ __launch_bounds__(NW * 64) void k_seg_state(FusedParams p) {
         body(il, sK0, sV0, sa0, sK1, sV1, sa1);
         if (il + 1 < ntl) body(il + 1, sK1, sV1, sa1, sK0, sV0, sa0);
     }
-    float* dst = p.useg + ((size_t)bh * p.nseg + seg) * p.dv * DK;
+    // the whole segment's state, or one of its sub-range states (the scan
+    // decays and sums those in order)
+    const size_t slot = ((size_t)bh * p.nseg + seg) * nsub + sub;
+    float* dst = (nsub == 1 ? p.useg : p.upart) + slot * p.dv * DK;
     const int c = cb + wave * 16 + m16;
 #pragma unroll
     for (int kt = 0; kt < NDT; ++kt)
         *reinterpret_cast<float4*>(dst + (size_t)c * DK + 16 * kt + 4 * g) =
             make_float4(u[kt][0], u[kt][1], u[kt][2], u[kt][3]);
-    if (threadIdx.x == 0 && dvb == 0) p.stot[(size_t)bh * p.nseg + seg] = total;
+    if (threadIdx.x == 0 && dvb == 0) (nsub == 1 ? p.stot : p.tpart)[slot] = total;
 }
 
 // ---------------------------------------------------------------------------
@@ -477,13 +485,13 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
         }
     };
 
-    f32x4 G[MLOC][NDTH];
+    bf16x4 G[MLOC][NDTH];
     float logd_loc[MLOC];
 #pragma unroll
     for (int s = 0; s < MLOC; ++s) {
         logd_loc[s] = 0.f;
 #pragma unroll
-        for (int kt = 0; kt < NDTH; ++kt) G[s][kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+        for (int kt = 0; kt < NDTH; ++kt) G[s][kt] = bf16x4{};
     }
 
     auto body = [&](int il, const bf16_t* Qc, const bf16_t* Kc, const bf16_t* Vc,
@@ -557,8 +565,8 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
                 typename H::frag ga[NKSH];
 #pragma unroll
                 for (int ks = 0; ks < NKSH; ++ks) {
-                    if constexpr (DK >= 32) ga[ks] = cvt8(G[s][2 * ks], G[s][2 * ks + 1]);
-                    else ga[ks] = cvt4(G[s][ks]);
+                    if constexpr (DK >= 32) ga[ks] = __builtin_shufflevector(G[s][2 * ks], G[s][2 * ks + 1], 0, 1, 2, 3, 4, 5, 6, 7);
+                    else ga[ks] = G[s][ks];
                 }
                 add_level(ga, LOGTC + s + 1, logd_loc[s]);
             }
@@ -605,10 +613,10 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
                     const float w = __expf(logd_loc[s] + tot);
 #pragma unroll
                     for (int kt = 0; kt < NDTH; ++kt) {
-                        u[kt][0] += w * G[s][kt][0];
-                        u[kt][1] += w * G[s][kt][1];
-                        u[kt][2] += w * G[s][kt][2];
-                        u[kt][3] += w * G[s][kt][3];
+                        u[kt][0] += w * (float)G[s][kt][0];
+                        u[kt][1] += w * (float)G[s][kt][1];
+                        u[kt][2] += w * (float)G[s][kt][2];
+                        u[kt][3] += w * (float)G[s][kt][3];
                     }
                 }
             }
@@ -616,7 +624,7 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
             for (int s = 0; s < MLOC; ++s) {
                 if (s == j) {
 #pragma unroll
-                    for (int kt = 0; kt < NDTH; ++kt) G[s][kt] = u[kt];
+                    for (int kt = 0; kt < NDTH; ++kt) G[s][kt] = cvt4(u[kt]);
                     logd_loc[s] = 0.f;
                 } else {
                     logd_loc[s] += tot;
@@ -643,7 +651,7 @@ namespace {
 struct Combo {
     int mloc, topmax;
 };
-constexpr Combo kCombos[] = {{2, 4}, {3, 4}, {5, 2}, {5, 7}};
+constexpr Combo kCombos[] = {{2, 4}, {3, 4}, {5, 2}, {5, 5}, {3, 7}};
 constexpr int kNumCombos = sizeof(kCombos) / sizeof(kCombos[0]);
 
 int bit_len(long x) {
@@ -683,9 +691,10 @@ FusedPlan plan_fused(int BH, int T, int dk, int dv, int lu, int force_m) {
         if (combo < 0) continue;
         const long blocks = pairs * nseg;
         const long rounds = (blocks + slots - 1) / slots;
-        const long cost = rounds * (1L << m);
-        // equal cost: the smaller register budget, then the longer segment
-        if (best < 0 || cost < best_cost || (cost == best_cost && combo <= best_combo)) {
+        // the two largest budgets spill a few registers at d_k = 128: last resort
+        const long cost = rounds * (1L << m) + (combo >= 3 ? 1000000L : 0L);
+        // equal cost: the longer segment (fewer segment states and nodes)
+        if (best < 0 || cost <= best_cost) {
             best = m;
             best_cost = cost;
             best_combo = combo;
@@ -696,6 +705,11 @@ FusedPlan plan_fused(int BH, int T, int dk, int dv, int lu, int force_m) {
     pl.nseg = (int)((pl.ntiles + (1L << best) - 1) >> best);
     pl.ntop = bit_len(pl.nseg - 1);
     pl.combo = best_combo;
+    // segment states in up to 8 sub-ranges, enough blocks for two per CU
+    pl.msub = best;
+    while (pl.msub > 0 && best - pl.msub < 3 &&
+           pairs * (pl.nseg - 1) * (1L << (best - pl.msub)) < 512)
+        --pl.msub;
     pl.ok = 1;
     return pl;
 }
@@ -704,7 +718,7 @@ namespace {
 
 template <int DK, int NW, int MLOC, int TOPMAX>
 hipError_t launch_main(const FusedParams& p, hipStream_t stream) {
-    constexpr int NH = LOGLIN_FUSED_NH;  // waves sharing a column slab (head-dim split)
+    constexpr int NH = DK >= 64 ? 2 : 1;  // two waves share a column slab, each half of d_k
     const unsigned nblk = (unsigned)p.BH * p.nseg * p.ndvb;
     hipLaunchKernelGGL((k_fused_fwd<DK, NW, NH, MLOC, TOPMAX>), dim3(nblk), dim3(NW * NH * 64), 0,
                        stream, p);
@@ -716,7 +730,7 @@ hipError_t launch_fused_t(const FusedParams& p, const FwdParams& scan, unsigned 
                           hipStream_t stream) {
     hipError_t err;
     if (p.nseg > 1 && (stages & kStageChunkState)) {
-        const unsigned nblk = (unsigned)p.BH * (p.nseg - 1) * p.ndvb;
+        const unsigned nblk = (unsigned)p.BH * (p.nseg - 1) * (1u << (p.m - p.msub)) * p.ndvb;
         hipLaunchKernelGGL((k_seg_state<DK, NW>), dim3(nblk), dim3(NW * 64), 0, stream, p);
         err = hipGetLastError();
         if (err != hipSuccess) return err;
@@ -731,6 +745,7 @@ hipError_t launch_fused_t(const FusedParams& p, const FwdParams& scan, unsigned 
             case 1: return launch_main<DK, NW, kCombos[1].mloc, kCombos[1].topmax>(p, stream);
             case 2: return launch_main<DK, NW, kCombos[2].mloc, kCombos[2].topmax>(p, stream);
             case 3: return launch_main<DK, NW, kCombos[3].mloc, kCombos[3].topmax>(p, stream);
+            case 4: return launch_main<DK, NW, kCombos[4].mloc, kCombos[4].topmax>(p, stream);
         }
         return hipErrorInvalidValue;
     }

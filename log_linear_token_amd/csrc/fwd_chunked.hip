@@ -166,7 +166,49 @@ __global__ __launch_bounds__(256) void k_chunk_state(FwdParams p) {
 constexpr int kScanLevels = 16;  // supports up to 2^16 chunks per sequence
 constexpr int kScanDepth = 8;    // loads kept in flight per thread
 
+// The state entering the scan for chunk (segment) i: U_i itself, or, when the
+// states were computed in NSUB sub-ranges, the sub-range states decayed to the
+// end of the segment and summed in order.
+template <int NSUB>
+struct ScanLoad {
+    float4 part[NSUB];
+    __device__ void issue(const FwdParams& p, int bh, int e4, int per4, int i) {
+        if constexpr (NSUB == 1) {
+            part[0] = reinterpret_cast<const float4*>(p.ust)[((size_t)bh * p.N + i) * per4 + e4];
+        } else {
+            const float4* src = reinterpret_cast<const float4*>(p.upart) +
+                                (((size_t)bh * p.N + i) * NSUB) * per4 + e4;
+#pragma unroll
+            for (int s = 0; s < NSUB; ++s) part[s] = src[(size_t)s * per4];
+        }
+    }
+    // returns the combined state; *total receives the segment's decay total
+    __device__ float4 combine(const FwdParams& p, int bh, int i, float* total) const {
+        if constexpr (NSUB == 1) {
+            *total = p.tot[(size_t)bh * p.N + i];
+            return part[0];
+        } else {
+            const float* tp = p.tpart + ((size_t)bh * p.N + i) * NSUB;
+            float4 acc = part[NSUB - 1];
+            float after = tp[NSUB - 1];  // decay of the sub-ranges after s
+#pragma unroll
+            for (int s = NSUB - 2; s >= 0; --s) {
+                const float w = __expf(after);
+                acc.x += w * part[s].x;
+                acc.y += w * part[s].y;
+                acc.z += w * part[s].z;
+                acc.w += w * part[s].w;
+                after += tp[s];
+            }
+            *total = after;
+            return acc;
+        }
+    }
+};
+
+template <int NSUB>
 __global__ __launch_bounds__(256) void k_fenwick_scan(FwdParams p) {
+    constexpr int DEPTH = NSUB >= 8 ? 1 : kScanDepth / NSUB;  // segments kept in flight
     const int per4 = p.dv * p.dk / 4;
     const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
     const int bh = (int)(gid / per4);
@@ -174,7 +216,6 @@ __global__ __launch_bounds__(256) void k_fenwick_scan(FwdParams p) {
     if (bh >= p.BH) return;
     const int n = p.nscan;  // nodes produced: 0 .. n-1
     float4* base = reinterpret_cast<float4*>(p.ust) + (size_t)bh * p.N * per4 + e4;
-    const float* tot = p.tot + (size_t)bh * p.N;
     double* cum = p.cum + (size_t)bh * p.N;
 
     // bf16 copy of each node in the operand order of the fused kernel's level
@@ -204,19 +245,20 @@ __global__ __launch_bounds__(256) void k_fenwick_scan(FwdParams p) {
         live[q] = make_float4(0.f, 0.f, 0.f, 0.f);
         lcum[q] = 0.0;
     }
-    float4 ring[kScanDepth];
+    ScanLoad<NSUB> ring[DEPTH];
 #pragma unroll
-    for (int d = 0; d < kScanDepth; ++d)
-        ring[d] = d < n ? base[(size_t)d * per4] : make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int d = 0; d < DEPTH; ++d)
+        if (d < n) ring[d].issue(p, bh, e4, per4, d);
     double c = 0.0;
-    for (int i0 = 0; i0 < n; i0 += kScanDepth) {
+    for (int i0 = 0; i0 < n; i0 += DEPTH) {
 #pragma unroll
-        for (int d = 0; d < kScanDepth; ++d) {
+        for (int d = 0; d < DEPTH; ++d) {
             const int i = i0 + d;
             if (i < n) {
-                float4 acc = ring[d];
-                if (i + kScanDepth < n) ring[d] = base[(size_t)(i + kScanDepth) * per4];
-                c += (double)tot[i];
+                float total;
+                float4 acc = ring[d].combine(p, bh, i, &total);
+                if (i + DEPTH < n) ring[d].issue(p, bh, e4, per4, i + DEPTH);
+                c += (double)total;
                 const int j = lssb((uint64_t)i + 1);
 #pragma unroll
                 for (int q = 0; q < kScanLevels; ++q) {
@@ -439,8 +481,14 @@ hipError_t launch_e(const FwdParams& p, unsigned st, hipStream_t s) {
 hipError_t launch_fenwick_scan(const FwdParams& p, hipStream_t stream) {
     if (p.nscan <= 0) return hipSuccess;
     const long threads = (long)p.BH * (p.dv * p.dk / 4);
-    hipLaunchKernelGGL(k_fenwick_scan, dim3((unsigned)((threads + 255) / 256)), dim3(256), 0, stream,
-                       p);
+    const dim3 grid((unsigned)((threads + 255) / 256));
+    switch (p.upart ? p.nsub : 1) {
+        case 1: hipLaunchKernelGGL(k_fenwick_scan<1>, grid, dim3(256), 0, stream, p); break;
+        case 2: hipLaunchKernelGGL(k_fenwick_scan<2>, grid, dim3(256), 0, stream, p); break;
+        case 4: hipLaunchKernelGGL(k_fenwick_scan<4>, grid, dim3(256), 0, stream, p); break;
+        case 8: hipLaunchKernelGGL(k_fenwick_scan<8>, grid, dim3(256), 0, stream, p); break;
+        default: return hipErrorInvalidValue;
+    }
     return hipGetLastError();
 }
 

@@ -21,13 +21,17 @@ struct FwdParams {
     float* tot;          // workspace [BH][N]
     double* cum;         // workspace [BH][N]
     bf16_t_storage* gfrag;  // optional bf16 copy of the nodes in MFMA fragment order
+    const float* upart;  // optional [BH][N][nsub][dv][dk] states of sub-ranges (then tpart)
+    const float* tpart;  // [BH][N][nsub] decay totals of the sub-ranges
+    int nsub;            // sub-ranges per chunk (1, 2, 4 or 8) when upart is set
 };
 
 // workspace carving shared by the size query and the launch
 struct FwdWorkspace {
-    size_t ust_off, tot_off, cum_off, frag_off, total;
+    size_t ust_off, tot_off, cum_off, frag_off, upart_off, tpart_off, total;
 };
-FwdWorkspace fwd_workspace_layout(long BH, long N, int dk, int dv, bool frags);
+// frags: bf16 node copies (fused path); nsub > 1: sub-range states per chunk
+FwdWorkspace fwd_workspace_layout(long BH, long N, int dk, int dv, bool frags, int nsub);
 
 enum : unsigned { kStageChunkState = 1u, kStageScan = 2u, kStageOutput = 4u, kStageAll = 7u };
 hipError_t launch_fwd_chunked(const FwdParams& p, bool bf16, unsigned stages, hipStream_t stream);
@@ -48,13 +52,16 @@ struct FusedParams {
     int lpitch;                     // row pitch of lambda in LDS (L, or LU if L is too long)
     int ntiles, m, nseg, ntop, dvw, ndvb, combo;
     int lam_dma, a_dma;             // lambda / a rows of a whole tile are 16-byte aligned
-    float* useg;                    // [BH][nseg][dv][dk] segment states, then Fenwick nodes
+    float* useg;                    // [BH][nseg][dv][dk] Fenwick nodes over segments
+    float* upart;                   // [BH][nseg][nsub][dv][dk] states of segment sub-ranges
+    float* tpart;                   // [BH][nseg][nsub] their decay totals
+    int msub;                       // sub-ranges of 2^msub tiles (nsub = 2^(m - msub))
     float* stot;                    // [BH][nseg]
     double* scum;                   // [BH][nseg]
     const bf16_t_storage* gfrag;    // bf16 MFMA fragments of the nodes (written by the scan)
 };
 struct FusedPlan {
-    int ok, m, nseg, ntop, dvw, ndvb, ntiles, combo;
+    int ok, m, nseg, ntop, dvw, ndvb, ntiles, combo, msub;
 };
 // force_m >= 0 asks for segments of 2^force_m tiles (plan fails if that does not fit)
 FusedPlan plan_fused(int BH, int T, int dk, int dv, int lu, int force_m);

@@ -74,14 +74,17 @@ loglin_status check_fwd_sizes(int B, int H, int T, int dk, int dv, int C) {
 }  // namespace
 
 namespace loglin {
-FwdWorkspace fwd_workspace_layout(long BH, long N, int dk, int dv, bool frags) {
+FwdWorkspace fwd_workspace_layout(long BH, long N, int dk, int dv, bool frags, int nsub) {
     FwdWorkspace w{};
     if (N <= 1 || BH == 0) return w;
     w.ust_off = 0;
     w.tot_off = align_up(w.ust_off + (size_t)BH * N * dv * dk * sizeof(float));
     w.cum_off = align_up(w.tot_off + (size_t)BH * N * sizeof(float));
     w.frag_off = align_up(w.cum_off + (size_t)BH * N * sizeof(double));
-    w.total = frags ? align_up(w.frag_off + (size_t)BH * N * dv * dk * 2) : w.frag_off;
+    w.upart_off = frags ? align_up(w.frag_off + (size_t)BH * N * dv * dk * 2) : w.frag_off;
+    w.tpart_off = nsub > 1 ? align_up(w.upart_off + (size_t)BH * N * nsub * dv * dk * sizeof(float))
+                           : w.upart_off;
+    w.total = nsub > 1 ? align_up(w.tpart_off + (size_t)BH * N * nsub * sizeof(float)) : w.tpart_off;
     return w;
 }
 }  // namespace loglin
@@ -127,7 +130,8 @@ Plan make_plan(long BH, int T, int dk, int dv, int C, loglin_dtype dt) {
             pl.N = f.nseg;
         }
     }
-    pl.ws = fwd_workspace_layout(BH, pl.N, dk, dv, pl.path == kPathFused);
+    const int nsub = pl.path == kPathFused ? 1 << (pl.fused.m - pl.fused.msub) : 1;
+    pl.ws = fwd_workspace_layout(BH, pl.N, dk, dv, pl.path == kPathFused, nsub);
     return pl;
 }
 
@@ -175,11 +179,13 @@ loglin_status loglin_fwd_plan(int B, int H, int T, int dk, int dv, int C, loglin
         r.nseg = pl.fused.nseg;
         r.col_block = pl.fused.dvw;
         r.coarse_levels = pl.fused.ntop;
+        r.state_split = 1 << (pl.fused.m - pl.fused.msub);
     } else {
         r.tile = C;
         r.seg_tiles = 1;
         r.nseg = (int)pl.N;
         r.col_block = dv;
+        r.state_split = 1;
         r.coarse_levels = 0;
         while ((1L << r.coarse_levels) < pl.N) ++r.coarse_levels;
     }
@@ -273,9 +279,18 @@ loglin_status loglin_fwd_chunked_stages(const void* q, const void* k, const void
         fp.lam_dma = L <= kFusedMaxL && ((long)T * L) % 4 == 0 &&
                      reinterpret_cast<uintptr_t>(lambda) % 16 == 0;
         fp.a_dma = T % 4 == 0 && reinterpret_cast<uintptr_t>(log_decay) % 16 == 0;
+        fp.msub = f.msub;
         if (w.total > 0) {
-            p.gfrag = reinterpret_cast<bf16_t_storage*>(static_cast<char*>(workspace) + w.frag_off);
+            char* base = static_cast<char*>(workspace);
+            p.gfrag = reinterpret_cast<bf16_t_storage*>(base + w.frag_off);
             fp.gfrag = p.gfrag;
+            if (f.m > f.msub) {  // segment states come in sub-ranges
+                fp.upart = reinterpret_cast<float*>(base + w.upart_off);
+                fp.tpart = reinterpret_cast<float*>(base + w.tpart_off);
+                p.upart = fp.upart;
+                p.tpart = fp.tpart;
+                p.nsub = 1 << (f.m - f.msub);
+            }
         }
         e = launch_fused_fwd(fp, p, stage_mask, hs);
     } else {

@@ -32,7 +32,8 @@ class LoglinError(RuntimeError):
 class FwdPlan(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int), ("tile", ctypes.c_int), ("seg_tiles", ctypes.c_int),
                 ("nseg", ctypes.c_int), ("col_block", ctypes.c_int),
-                ("coarse_levels", ctypes.c_int), ("workspace_bytes", ctypes.c_size_t)]
+                ("coarse_levels", ctypes.c_int), ("state_split", ctypes.c_int),
+                ("workspace_bytes", ctypes.c_size_t)]
 
     def as_dict(self) -> dict:
         d = {n: getattr(self, n) for n, _ in self._fields_}

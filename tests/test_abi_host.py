@@ -110,7 +110,8 @@ def test_workspace_sizes(lib):
 class Plan(ctypes.Structure):
     _fields_ = [("path", ctypes.c_int), ("tile", ctypes.c_int), ("seg_tiles", ctypes.c_int),
                 ("nseg", ctypes.c_int), ("col_block", ctypes.c_int),
-                ("coarse_levels", ctypes.c_int), ("workspace_bytes", ctypes.c_size_t)]
+                ("coarse_levels", ctypes.c_int), ("state_split", ctypes.c_int),
+                ("workspace_bytes", ctypes.c_size_t)]
 
 
 @pytest.mark.parametrize("B,H,T,dk,dv,C", [(4, 16, 8192, 128, 64, 64), (1, 16, 65536, 128, 128, 128),
