@@ -114,6 +114,24 @@ __device__ __forceinline__ bf16x8 ld_tr8(const bf16_t* t, int k0, int n0) {
 // does not track these loads: it would otherwise wait for them before the
 // first read of any LDS buffer.  Completion is awaited explicitly with
 // s_waitcnt vmcnt(0) before the barrier that publishes a tile.
+// Transpose read with free column quads: lane l of group g gets
+// X[k0 + 8g + i][cbase + 8 (m / 4) + m % 4] for i < 8, m = l % 16, i.e. the
+// MFMA row m of the result covers columns cbase + 8q .. cbase + 8q + 3 for
+// q = m / 4.  Two such reads with cbase and cbase + 4 give C-layout rows
+// 4g..4g+3 that together hold 8 consecutive columns per lane group.
+template <int D>
+__device__ __forceinline__ bf16x8 ld_tr8_q(const bf16_t* t, int k0, int cbase) {
+    const int lane = threadIdx.x & 63;
+    const int g = lane >> 4, j = lane & 15;
+    const int r = k0 + 8 * g + (j >> 2);
+    const int c = cbase + 8 * (j & 3);
+    const bf16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4*)(t + toff<D>(r, c)));
+    const bf16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4bf16(
+        (lds_bf16x4*)(t + toff<D>(r + 4, c)));
+    return __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+}
+
 __device__ __forceinline__ void dma16(const void* g, void* lds) {
     // the low 32 bits of a generic pointer into LDS are the LDS address
     const uint32_t l = (uint32_t)(uintptr_t)lds;
@@ -258,11 +276,15 @@ __device__ __forceinline__ void scores_for_wave(int wave, const bf16_t* Qs, cons
     }
 }
 
-// Rows [16 kt0, 16 (kt0 + NT)) of U = K^T diag(e) V for this wave's 16 columns:
-// u[kt] (C layout) holds U[16 (kt0 + kt) + 4g + i][column m16].  vf[sp] are the
-// V fragments (lane: V[32 sp + 8g + i][column]) shared with the P V product.
+// U = K^T diag(e) V over the staged tile, for this wave's 16 columns and the
+// NT / 2 contraction steps of 32 head-dim rows starting at step ks0 (d_k >= 32):
+// u[2 j] holds rows 32 (ks0 + j) + 8g + i and u[2 j + 1] rows 32 (ks0 + j) +
+// 8g + 4 + i (C layout, lane group g), so that the pair is the A operand of
+// a level product over those 32 rows with natural 8-wide lane groups.
+// For d_k = 16 (NT = 1): u[0] holds rows 4g + i.  vf[sp] are the V fragments
+// (lane: V[32 sp + 8g + i][column]) shared with the P V product.
 template <int DK, int NT>
-__device__ __forceinline__ void tile_state(f32x4 (&u)[NT], int kt0, const bf16_t* Ks,
+__device__ __forceinline__ void tile_state(f32x4 (&u)[NT], int ks0, const bf16_t* Ks,
                                            const bf16x8 (&vf)[2], const float* Ew) {
     const int lane = threadIdx.x & 63, g = lane >> 4;
 #pragma unroll
@@ -273,9 +295,15 @@ __device__ __forceinline__ void tile_state(f32x4 (&u)[NT], int kt0, const bf16_t
         bf16x8 b;
 #pragma unroll
         for (int i = 0; i < 8; ++i) b[i] = (__bf16)((float)vf[sp][i] * ev[i]);
+        if constexpr (DK >= 32) {
 #pragma unroll
-        for (int kt = 0; kt < NT; ++kt)
-            u[kt] = mma(ld_tr8<DK>(Ks, 32 * sp, 16 * (kt0 + kt)), b, u[kt]);
+            for (int j = 0; j < NT / 2; ++j) {
+                u[2 * j] = mma(ld_tr8_q<DK>(Ks, 32 * sp, 32 * (ks0 + j)), b, u[2 * j]);
+                u[2 * j + 1] = mma(ld_tr8_q<DK>(Ks, 32 * sp, 32 * (ks0 + j) + 4), b, u[2 * j + 1]);
+            }
+        } else {
+            u[0] = mma(ld_tr8<DK>(Ks, 32 * sp, 0), b, u[0]);
+        }
     }
 }
 
@@ -368,9 +396,12 @@ __global__ __launch_bounds__(NW * 64) void k_seg_state(FusedParams p) {
     float* dst = (nsub == 1 ? p.useg : p.upart) + slot * p.dv * DK;
     const int c = cb + wave * 16 + m16;
 #pragma unroll
-    for (int kt = 0; kt < NDT; ++kt)
-        *reinterpret_cast<float4*>(dst + (size_t)c * DK + 16 * kt + 4 * g) =
+    for (int kt = 0; kt < NDT; ++kt) {
+        // row of u[kt] (see tile_state): 32 (kt / 2) + 8g + 4 (kt % 2), or 4g for d_k = 16
+        const int row = DK >= 32 ? 32 * (kt / 2) + 8 * g + 4 * (kt % 2) : 4 * g;
+        *reinterpret_cast<float4*>(dst + (size_t)c * DK + row) =
             make_float4(u[kt][0], u[kt][1], u[kt][2], u[kt][3]);
+    }
     if (threadIdx.x == 0 && dvb == 0) (nsub == 1 ? p.stot : p.tpart)[slot] = total;
 }
 
@@ -418,7 +449,7 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
     const int lane = threadIdx.x & 63, m16 = lane & 15, g = lane >> 4;
     const int tid = threadIdx.x;
     const int c0 = cb + cs * 16;  // first column of this wave
-    const int ks0 = hh * NKSH, kt0 = hh * NDTH;
+    const int ks0 = hh * NKSH;
     const size_t row0 = (size_t)bh * p.T;
     const int tile0 = seg << p.m;
     const int ntl = min(1 << p.m, p.ntiles - tile0);
@@ -526,17 +557,12 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
                 }
             }
         }
-        // Q fragment in the head-dim order of the register states:
-        // 4g..4g+3 and 16+4g..16+4g+3 of each 32-wide step
+        // Q fragment of a level product: 8 consecutive head-dim rows per lane
+        // group, the order in which tile_state lays out the register states
         auto qfrag = [&](int rb, int ks) __attribute__((always_inline)) {
             typename H::frag r;
-            if constexpr (DK >= 32) {
-                const bf16x4 x = ld4<DK>(Qc, 16 * rb + m16, 32 * ks + 4 * g);
-                const bf16x4 y = ld4<DK>(Qc, 16 * rb + m16, 32 * ks + 16 + 4 * g);
-                r = __builtin_shufflevector(x, y, 0, 1, 2, 3, 4, 5, 6, 7);
-            } else {
-                r = ld4<DK>(Qc, 16 * rb + m16, 4 * g);
-            }
+            if constexpr (DK >= 32) r = ld8<DK>(Qc, 16 * rb + m16, 32 * ks + 8 * g);
+            else r = ld4<DK>(Qc, 16 * rb + m16, 4 * g);
             return r;
         };
         // one row block at a time keeps few operands live
@@ -605,7 +631,7 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
             f32x4 u[NDTH];
 #pragma unroll
             for (int kt = 0; kt < NDTH; ++kt) u[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            tile_state<DK, NDTH>(u, kt0, Kc, vf, sEw[wave]);
+            tile_state<DK, NDTH>(u, ks0, Kc, vf, sEw[wave]);
             const int j = lssb((uint64_t)il + 1);
 #pragma unroll
             for (int s = 0; s < MLOC; ++s) {
@@ -691,8 +717,7 @@ FusedPlan plan_fused(int BH, int T, int dk, int dv, int lu, int force_m) {
         if (combo < 0) continue;
         const long blocks = pairs * nseg;
         const long rounds = (blocks + slots - 1) / slots;
-        // the two largest budgets spill a few registers at d_k = 128: last resort
-        const long cost = rounds * (1L << m) + (combo >= 3 ? 1000000L : 0L);
+        const long cost = rounds * (1L << m);
         // equal cost: the longer segment (fewer segment states and nodes)
         if (best < 0 || cost <= best_cost) {
             best = m;

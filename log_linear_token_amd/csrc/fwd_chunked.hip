@@ -220,8 +220,8 @@ __global__ __launch_bounds__(256) void k_fenwick_scan(FwdParams p) {
 
     // bf16 copy of each node in the operand order of the fused kernel's level
     // products: [node][column block of 16][32-wide step][lane][8], lane 16g + m
-    // holding rows 4g..4g+3 (first half) and 16+4g..16+4g+3 (second half) of
-    // the step for column m; for d_k = 16 one step of 4 rows per lane.
+    // holding rows 8g..8g+7 of the step for column m; for d_k = 16 one step of
+    // 4 rows (4g..4g+3) per lane.
     bf16_t* frag = nullptr;
     size_t fstride = 0;
     if (p.gfrag) {
@@ -230,7 +230,7 @@ __global__ __launch_bounds__(256) void k_fenwick_scan(FwdParams p) {
         const int cblk = col >> 4, m = col & 15;
         size_t off;
         if (p.dk >= 32) {
-            const int j = d0 >> 5, w32 = d0 & 31, half = w32 >> 4, g = (w32 & 15) >> 2;
+            const int j = d0 >> 5, w32 = d0 & 31, g = w32 >> 3, half = (w32 >> 2) & 1;
             off = (((size_t)cblk * (p.dk / 32) + j) * 64 + 16 * g + m) * 8 + 4 * half;
         } else {
             off = ((size_t)cblk * 64 + 16 * (d0 >> 2) + m) * 4;
