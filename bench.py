@@ -138,16 +138,16 @@ def fwd_models(cfg, plan) -> dict:
 
 def decode_bytes(pos0: np.ndarray, H: int, dk: int, dv: int, Lmax: int, steps: int) -> float:
     """Average algorithmic bytes per decode step: each (sequence, head) reads the
-    1 + popcount(t-1) live states of position t-1 and writes the 1 + popcount(t)
-    of position t (fp32 d_k x d_v each), plus q, k, v (bf16), a, lambda, out."""
+    1 + popcount(t-1) live states of position t-1 (which the output needs) and
+    writes the two it changes, the merged level and level 0 (fp32 d_k x d_v
+    each), plus q, k, v (bf16), a, lambda, the level scales and out."""
     st = dk * dv * 4
-    small = (2 * dk + dv) * 2 + 4 + Lmax * 4 + dv * 4
+    small = (2 * dk + dv) * 2 + 4 + Lmax * 4 + 2 * Lmax * 4 + dv * 4
     tot = 0.0
     for s in range(steps):
         t = pos0 + s
-        pc = np.array([bin(int(x)).count("1") for x in t])
         pcm = np.array([bin(int(x) - 1).count("1") if x >= 1 else -1 for x in t])
-        tot += float(np.sum((1 + pcm) + (1 + pc))) * st * H + len(t) * H * small
+        tot += float(np.sum((1 + pcm) + 2)) * st * H + len(t) * H * small
     return tot / steps
 
 

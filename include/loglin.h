@@ -141,7 +141,10 @@ LOGLIN_API loglin_status loglin_fwd_chunked_stages(const void* q, const void* k,
 
 /*
  * Decode state: for nseq sequences x H heads, Lmax level states of dk x dv
- * fp32 (S = sum k v^T orientation) plus the next position of each sequence.
+ * (S = sum k v^T orientation) plus the next position of each sequence.  Each
+ * level is held as an fp32 matrix and a scalar log-scale (the state is the
+ * matrix times exp(scale)), so a step rewrites only the level it merges into
+ * and level 0; loglin_state_export returns the states themselves.
  * Allocates device memory (hipMalloc) and zeroes it on `stream`; every
  * sequence starts at position 0.  dk, dv in {16, 32, 64, 128};
  * 1 <= Lmax <= 48.  *st is set only on success.

@@ -4,14 +4,16 @@
 // recurrence is the Fenwick update.  At position t >= 1 with j = lssb(t), the
 // new token's outer product enters level 0, levels 0..j (the old token and
 // the buckets of the trailing one bits of t-1) are summed and promoted to
-// level j+1, and, composing with the Mamba-2 scalar gate (section 1 and 3),
+// level j+1, and, composing with the Mamba-2 scalar gate (sections 1 and 3),
 // every carried state is decayed by alpha_t = exp(a_t).  The output reads
 // o_t = sum_l lambda_t^(l) q_t^T S_t^(l) over the live levels.
 //
-// This kernel is bound by HBM traffic: per (sequence, head) it reads the
-// 1 + popcount(t-1) live states of d_k x d_v fp32 and writes the
-// 1 + popcount(t) live states of position t.  Slots that are not live are
-// neither read nor written (their contents are stale; the export zeroes them).
+// Storage: each level keeps an fp32 d_k x d_v matrix X and a log-scale sigma,
+// the state being S = exp(sigma) X.  Decaying a level only adds a_t to its
+// sigma, so a step writes two matrices (the merged level j+1 and level 0)
+// and reads the 1 + popcount(t-1) live ones, which the output needs anyway.
+// Slots that are not live are neither read nor written (their contents are
+// stale; the export zeroes them and applies the scales).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -25,6 +27,7 @@ constexpr int kMaxPer = 16;  // float4 elements per thread for a 128 x 128 state
 template <typename E>
 __global__ __launch_bounds__(kThreads) void k_decode_step(DecodeParams p) {
     __shared__ float qs[128], ks[128], vs[128];
+    __shared__ float sig_s[64];
     __shared__ float4 red[kThreads];
     const int sh = blockIdx.x;  // sequence * H + head
     const int seq = sh / p.H;
@@ -35,17 +38,20 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(DecodeParams p) {
     const E* q = static_cast<const E*>(p.q) + (size_t)sh * dk;
     const E* k = static_cast<const E*>(p.k) + (size_t)sh * dk;
     const E* v = static_cast<const E*>(p.v) + (size_t)sh * dv;
+    float* sig = p.sigma + (size_t)sh * p.Lmax;
     if (tid < dk) {
         qs[tid] = to_f32(q[tid]);
         ks[tid] = to_f32(k[tid]);
     }
     if (tid < dv) vs[tid] = to_f32(v[tid]);
+    if (tid < p.Lmax) sig_s[tid] = sig[tid];
     __syncthreads();
 
-    const float alpha = __expf(p.a[sh]);
+    const float a = p.a[sh];
+    const float alpha = __expf(a);
     const float* lam = p.lam + (size_t)sh * p.Lmax;
     const size_t nst4 = (size_t)dk * dv / 4;
-    float4* S = reinterpret_cast<float4*>(p.states) + (size_t)sh * p.Lmax * nst4;
+    float4* X = reinterpret_cast<float4*>(p.states) + (size_t)sh * p.Lmax * nst4;
     const int quads = dv / 4;
     const int col = (tid % quads) * 4;  // the same for every element of this thread
 
@@ -64,54 +70,51 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(DecodeParams p) {
         part.w += f * x.w;
     };
 
+    int j = -1;
     if (t >= 1) {
-        const int j = lssb((uint64_t)t);
-        // merge levels 0..j into level j+1 (decayed)
+        j = lssb((uint64_t)t);
+        // merge levels 0..j (decayed by their scales) into level j+1
         float4 acc[kMaxPer];
 #pragma unroll
         for (int u = 0; u < kMaxPer; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
         for (int l = 0; l <= j; ++l) {
-            const float4* src = S + (size_t)l * nst4;
+            const float w = alpha * __expf(sig_s[l]);
+            const float4* src = X + (size_t)l * nst4;
+            float4 x[kMaxPer];
+#pragma unroll
+            for (int u = 0; u < kMaxPer; ++u)
+                if (valid(u)) x[u] = src[tid + kThreads * u];
 #pragma unroll
             for (int u = 0; u < kMaxPer; ++u) {
                 if (valid(u)) {
-                    const float4 x = src[tid + kThreads * u];
-                    acc[u].x += x.x;
-                    acc[u].y += x.y;
-                    acc[u].z += x.z;
-                    acc[u].w += x.w;
+                    acc[u].x += w * x[u].x;
+                    acc[u].y += w * x[u].y;
+                    acc[u].z += w * x[u].z;
+                    acc[u].w += w * x[u].w;
                 }
             }
         }
-        float4* dst = S + (size_t)(j + 1) * nst4;
+        float4* dst = X + (size_t)(j + 1) * nst4;
         const float lj = lam[j + 1];
 #pragma unroll
         for (int u = 0; u < kMaxPer; ++u) {
             if (valid(u)) {
-                const float4 m = make_float4(alpha * acc[u].x, alpha * acc[u].y, alpha * acc[u].z,
-                                             alpha * acc[u].w);
-                dst[tid + kThreads * u] = m;
-                accum(lj, qs[row[u]], m);
+                dst[tid + kThreads * u] = acc[u];
+                accum(lj, qs[row[u]], acc[u]);
             }
         }
-        // live levels above j+1: decay in place
+        // live levels above j+1: decay through the scale, read for the output
         for (uint64_t hb = (uint64_t)t >> (j + 1); hb; hb &= hb - 1) {
             const int l = j + 2 + __builtin_ctzll(hb);
-            float4* s = S + (size_t)l * nst4;
-            const float ll = lam[l];
+            const float w = lam[l] * __expf(sig_s[l] + a);
+            const float4* s = X + (size_t)l * nst4;
             float4 x[kMaxPer];
 #pragma unroll
             for (int u = 0; u < kMaxPer; ++u)
                 if (valid(u)) x[u] = s[tid + kThreads * u];
 #pragma unroll
-            for (int u = 0; u < kMaxPer; ++u) {
-                if (valid(u)) {
-                    const float4 y = make_float4(alpha * x[u].x, alpha * x[u].y, alpha * x[u].z,
-                                                 alpha * x[u].w);
-                    s[tid + kThreads * u] = y;
-                    accum(ll, qs[row[u]], y);
-                }
-            }
+            for (int u = 0; u < kMaxPer; ++u)
+                if (valid(u)) accum(w, qs[row[u]], x[u]);
         }
     }
     // level 0 holds the new token alone
@@ -122,7 +125,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(DecodeParams p) {
             const float kr = ks[row[u]];
             const float4 y = make_float4(kr * vs[col], kr * vs[col + 1], kr * vs[col + 2],
                                          kr * vs[col + 3]);
-            S[tid + kThreads * u] = y;
+            X[tid + kThreads * u] = y;
             accum(l0, qs[row[u]], y);
         }
     }
@@ -139,6 +142,13 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(DecodeParams p) {
         }
         *reinterpret_cast<float4*>(p.out + (size_t)sh * dv + col) = o;
     }
+    // new scales: 0 for the rewritten levels, + a for the carried ones
+    if (tid < p.Lmax) {
+        float s = sig_s[tid];
+        if (tid == 0 || tid == j + 1) s = 0.f;
+        else if (t >= 1 && tid > j + 1 && (((uint64_t)t >> (tid - 1)) & 1)) s += a;
+        sig[tid] = s;
+    }
 }
 
 __global__ void k_state_export(DecodeParams p, float4* dst) {
@@ -153,7 +163,13 @@ __global__ void k_state_export(DecodeParams p, float4* dst) {
         const int64_t n = p.base_pos[seq] + p.step;  // tokens absorbed so far
         bool live = false;
         if (n >= 1) live = (l == 0) || (((uint64_t)(n - 1) >> (l - 1)) & 1);
-        dst[e] = live ? src[e] : make_float4(0.f, 0.f, 0.f, 0.f);
+        float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
+        if (live) {
+            const float w = __expf(p.sigma[slot]);
+            x = src[e];
+            x.x *= w; x.y *= w; x.z *= w; x.w *= w;
+        }
+        dst[e] = x;
     }
 }
 

@@ -69,7 +69,8 @@ hipError_t launch_fused_fwd(const FusedParams& p, const FwdParams& scan, unsigne
                             hipStream_t stream);
 
 struct DecodeParams {
-    float* states;            // [nseq][H][Lmax][dk][dv]
+    float* states;            // [nseq][H][Lmax][dk][dv] matrices X (state = exp(sigma) X)
+    float* sigma;             // [nseq][H][Lmax] per-level log-scales
     const int64_t* base_pos;  // [nseq]: position of the first step after the last load
     int64_t step;             // steps taken since that load
     const void* q;            // [nseq][H][dk]

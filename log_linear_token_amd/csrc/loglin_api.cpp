@@ -315,7 +315,8 @@ loglin_status loglin_fwd_chunked(const void* q, const void* k, const void* v,
 
 struct loglin_state {
     int nseq, H, dk, dv, Lmax;
-    float* levels;               // device [nseq][H][Lmax][dk][dv]
+    float* levels;               // device [nseq][H][Lmax][dk][dv] matrices X
+    float* sigma;                // device [nseq][H][Lmax] log-scales (state = exp(sigma) X)
     int64_t* base_pos;           // device [nseq]
     std::vector<int64_t> host_base;  // host mirror of base_pos
     int64_t step;                // steps since the last load
@@ -334,6 +335,7 @@ loglin_status check_state(const loglin_state* st) {
 DecodeParams decode_params(const loglin_state* st) {
     DecodeParams p{};
     p.states = st->levels;
+    p.sigma = st->sigma;
     p.base_pos = st->base_pos;
     p.step = st->step;
     p.nseq = st->nseq;
@@ -386,12 +388,22 @@ loglin_status loglin_state_init(loglin_state** out, int nseq, int H, int dk, int
         delete st;
         return fail(LOGLIN_ENOMEM, "hipMalloc positions: %s", hipGetErrorString(e));
     }
-    hipStream_t s = static_cast<hipStream_t>(stream);
-    e = hipMemsetAsync(st->levels, 0, bytes, s);
-    if (e == hipSuccess) e = hipMemsetAsync(st->base_pos, 0, (size_t)nseq * sizeof(int64_t), s);
+    const size_t sbytes = (size_t)nseq * H * Lmax * sizeof(float);
+    e = hipMalloc(&st->sigma, sbytes);
     if (e != hipSuccess) {
         (void)hipFree(st->levels);
         (void)hipFree(st->base_pos);
+        delete st;
+        return fail(LOGLIN_ENOMEM, "hipMalloc level scales: %s", hipGetErrorString(e));
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    e = hipMemsetAsync(st->levels, 0, bytes, s);
+    if (e == hipSuccess) e = hipMemsetAsync(st->base_pos, 0, (size_t)nseq * sizeof(int64_t), s);
+    if (e == hipSuccess) e = hipMemsetAsync(st->sigma, 0, sbytes, s);
+    if (e != hipSuccess) {
+        (void)hipFree(st->levels);
+        (void)hipFree(st->base_pos);
+        (void)hipFree(st->sigma);
         delete st;
         return hip_fail(e, "loglin_state_init");
     }
@@ -408,6 +420,8 @@ loglin_status loglin_state_free(loglin_state* st) {
     st->magic = 0;
     hipError_t e1 = hipFree(st->levels);
     hipError_t e2 = hipFree(st->base_pos);
+    hipError_t e3 = hipFree(st->sigma);
+    if (e2 == hipSuccess) e2 = e3;
     delete st;
     if (e != hipSuccess) return hip_fail(e, "loglin_state_free (synchronize)");
     if (e1 != hipSuccess) return hip_fail(e1, "loglin_state_free");
@@ -434,6 +448,8 @@ loglin_status loglin_state_load(loglin_state* st, const int64_t* pos_host, const
     const size_t bytes = (size_t)st->nseq * st->H * st->Lmax * st->dk * st->dv * sizeof(float);
     hipError_t e = levels ? hipMemcpyAsync(st->levels, levels, bytes, hipMemcpyDeviceToDevice, hs)
                           : hipMemsetAsync(st->levels, 0, bytes, hs);
+    if (e == hipSuccess)
+        e = hipMemsetAsync(st->sigma, 0, (size_t)st->nseq * st->H * st->Lmax * sizeof(float), hs);
     if (e != hipSuccess) return hip_fail(e, "loglin_state_load (levels)");
     st->host_base.assign(pos_host, pos_host + st->nseq);
     // the host vector must outlive the asynchronous copy: it does, as it is
