@@ -525,6 +525,27 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
         for (int kt = 0; kt < NDTH; ++kt) G[s][kt] = bf16x4{};
     }
 
+    // Output of the previous tile, rows this wave writes, waiting for the
+    // other head-dim half (d_k split only).  The halves meet in sX: each wave
+    // leaves the rows it does not write there at the end of a tile and picks
+    // up its own after the next tile's first barrier, so the exchange costs
+    // no barrier of its own.
+    f32x4 oprev[RBH];
+    int prev_tile = -1, prev_valid = 0;
+    auto finish_prev = [&]() __attribute__((always_inline)) {
+        float* orow = p.out + (row0 + (size_t)prev_tile * TC) * p.dv + c0 + 4 * g;
+#pragma unroll
+        for (int r = 0; r < RBH; ++r) {
+            const int rb = hh * RBH + r;
+            const f32x4 x = sX[(cs * NRB + rb) * 64 + lane];
+            const int row = 16 * rb + m16;
+            if (row < prev_valid)
+                *reinterpret_cast<float4*>(orow + (size_t)row * p.dv) =
+                    make_float4(oprev[r][0] + x[0], oprev[r][1] + x[1], oprev[r][2] + x[2],
+                                oprev[r][3] + x[3]);
+        }
+    };
+
     auto body = [&](int il, const bf16_t* Qc, const bf16_t* Kc, const bf16_t* Vc,
                     const float* Lc, const float* ac, bf16_t* Qn, bf16_t* Kn, bf16_t* Vn,
                     float* Ln, float* an) __attribute__((always_inline)) {
@@ -532,31 +553,21 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (il + 1 < ntl) issue(il + 1, Qn, Kn, Vn, Ln, an);
+        if constexpr (NH > 1) {
+            if (prev_tile >= 0) finish_prev();
+        }
         const int i = tile0 + il;
         const int nvalid = min(TC, p.T - i * TC);
         const float tot = tile_decay(ac, sAw[wave], sEw[wave]);
         scores_for_wave<DK, NWT>(wave, Qc, Kc, sP, sAw[wave], Lc, LP);
-        __syncthreads();
 
-        // ---- outputs of this wave's 16 columns: intra-tile P V for the row
-        // blocks it writes, level products (its head-dim part) for all rows
-        bf16x8 vf[2];
-        vf[0] = ld_tr8<DVW>(Vc, 0, 16 * cs);
-        vf[1] = ld_tr8<DVW>(Vc, 32, 16 * cs);
-        f32x4 o[NRB];
+        // ---- level products (this wave's head-dim part, all rows), before the
+        // barrier that publishes P: they do not need it.  The weight of level
+        // l for row t is lambda_t^(l) e^(A_t) e^(logd_l); the per-level part
+        // is applied here, e^(A_t) once per row block at the end.
+        f32x4 lv[NRB];
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) o[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-            if (rb / RBH == hh) {
-#pragma unroll
-                for (int sp = 0; sp <= rb / 2; ++sp) {
-                    const bf16x8 pb = *reinterpret_cast<const bf16x8*>(sP + (16 * rb + m16) * PROW +
-                                                                       32 * sp + 8 * g);
-                    o[rb] = mma(vf[sp], pb, o[rb]);
-                }
-            }
-        }
+        for (int rb = 0; rb < NRB; ++rb) lv[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
         // Q fragment of a level product: 8 consecutive head-dim rows per lane
         // group, the order in which tile_state lays out the register states
         auto qfrag = [&](int rb, int ks) __attribute__((always_inline)) {
@@ -571,17 +582,17 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
             // re-read the Q fragments for every level rather than keeping them
             // live across levels (registers are the scarce resource here)
             asm volatile("" ::: "memory");
+            const float d = __expf(logd);
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb) {
                 f32x4 y = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int ks = 0; ks < NKSH; ++ks) y = mma(ga[ks], qfrag(rb, ks0 + ks), y);
-                const float w = Lc[(16 * rb + m16) * LP + lev] *
-                                __expf(sAw[wave][16 * rb + m16] + logd);
-                o[rb][0] += w * y[0];
-                o[rb][1] += w * y[1];
-                o[rb][2] += w * y[2];
-                o[rb][3] += w * y[3];
+                const float w = Lc[(16 * rb + m16) * LP + lev] * d;
+                lv[rb][0] += w * y[0];
+                lv[rb][1] += w * y[1];
+                lv[rb][2] += w * y[2];
+                lv[rb][3] += w * y[3];
             }
         };
         // levels inside the segment
@@ -601,28 +612,50 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
 #pragma unroll
         for (int q = 0; q < TOPMAX; ++q)
             if (q < p.ntop && ((seg >> q) & 1)) add_level(top[q], LOGTC + p.m + q + 1, logd_top[q]);
+        __syncthreads();
 
-        // sum the head-dim parts: each wave hands over the rows it does not write
-        if constexpr (NH > 1) {
+        // ---- intra-tile P V for the row blocks this wave writes
+        bf16x8 vf[2];
+        vf[0] = ld_tr8<DVW>(Vc, 0, 16 * cs);
+        vf[1] = ld_tr8<DVW>(Vc, 32, 16 * cs);
+        f32x4 o[NRB];
 #pragma unroll
-            for (int rb = 0; rb < NRB; ++rb)
-                if (rb / RBH != hh) sX[(cs * NRB + rb) * 64 + lane] = o[rb];
-            __syncthreads();
+        for (int rb = 0; rb < NRB; ++rb) {
+            const float eA = __expf(sAw[wave][16 * rb + m16]);
+            o[rb] = f32x4{eA * lv[rb][0], eA * lv[rb][1], eA * lv[rb][2], eA * lv[rb][3]};
+        }
 #pragma unroll
-            for (int rb = 0; rb < NRB; ++rb) {
-                if (rb / RBH == hh) {
-                    const f32x4 x = sX[(cs * NRB + rb) * 64 + lane];
-                    o[rb][0] += x[0]; o[rb][1] += x[1]; o[rb][2] += x[2]; o[rb][3] += x[3];
+        for (int rb = 0; rb < NRB; ++rb) {
+            if (rb / RBH == hh) {
+#pragma unroll
+                for (int sp = 0; sp <= rb / 2; ++sp) {
+                    const bf16x8 pb = *reinterpret_cast<const bf16x8*>(sP + (16 * rb + m16) * PROW +
+                                                                       32 * sp + 8 * g);
+                    o[rb] = mma(vf[sp], pb, o[rb]);
                 }
             }
         }
-        float* orow = p.out + (row0 + (size_t)i * TC) * p.dv + c0 + 4 * g;
+
+        if constexpr (NH > 1) {
+            // hand over the rows the other half writes; keep ours until the
+            // next tile (or the end) picks up the other half's part
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-            const int r = 16 * rb + m16;
-            if (rb / RBH == hh && r < nvalid)
-                *reinterpret_cast<float4*>(orow + (size_t)r * p.dv) =
-                    make_float4(o[rb][0], o[rb][1], o[rb][2], o[rb][3]);
+            for (int rb = 0; rb < NRB; ++rb)
+                if (rb / RBH != hh) sX[(cs * NRB + rb) * 64 + lane] = o[rb];
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb)
+                if (rb / RBH == hh) oprev[rb % RBH] = o[rb];  // static indices only
+            prev_tile = i;
+            prev_valid = nvalid;
+        } else {
+            float* orow = p.out + (row0 + (size_t)i * TC) * p.dv + c0 + 4 * g;
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb) {
+                const int r = 16 * rb + m16;
+                if (r < nvalid)
+                    *reinterpret_cast<float4*>(orow + (size_t)r * p.dv) =
+                        make_float4(o[rb][0], o[rb][1], o[rb][2], o[rb][3]);
+            }
         }
 
         // ---- Fenwick update over tiles: fold the tile's state and the slots
@@ -665,6 +698,10 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
     for (int il = 0; il < ntl; il += 2) {
         body(il, sQ0, sK0, sV0, sL0, sa0, sQ1, sK1, sV1, sL1, sa1);
         if (il + 1 < ntl) body(il + 1, sQ1, sK1, sV1, sL1, sa1, sQ0, sK0, sV0, sL0, sa0);
+    }
+    if constexpr (NH > 1) {
+        __syncthreads();
+        finish_prev();
     }
 }
 
