@@ -155,6 +155,65 @@ __device__ __forceinline__ void dma4(const void* g, void* lds) {
         : "memory", "m0");
 }
 
+// The same copy from a uniform base address plus a per-lane 32-bit byte offset
+// (the scalar-base form of the instruction: no 64-bit address arithmetic per
+// lane).
+__device__ __forceinline__ void dma16o(const void* base, uint32_t off, void* lds) {
+    const uint32_t l = (uint32_t)(uintptr_t)lds;
+    const uint64_t b = (uint64_t)(uintptr_t)base;
+    const uint64_t bu = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
+                        (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
+    asm volatile(
+        "s_mov_b32 m0, %0\n\t"
+        "s_nop 0\n\t"
+        "global_load_lds_dwordx4 %1, %2"
+        :
+        : "s"(__builtin_amdgcn_readfirstlane(l)), "v"(off), "s"(bu)
+        : "memory", "m0");
+}
+
+// Copy plan of a whole 64-row tile with D bf16 columns: the tile is NI
+// wave-instructions of 1 KB (RPI rows each); a wave issues those with index
+// w + NWI k.  The swizzle repeats every 16 rows, so when the stride NWI
+// covers whole repeats the lane offsets of a wave's instructions differ by a
+// uniform amount, added to the scalar base, and one offset register serves
+// them all; otherwise every instruction keeps its own offset.
+template <int D, int NWI>
+struct TileCopy {
+    static constexpr int CPR = D / 8;                   // 16-byte chunks per row
+    static constexpr int NI = TC * CPR / 64;            // wave-instructions per tile
+    static constexpr int RPI = TC / NI;                 // rows per instruction
+    static constexpr int UP = CPR / 4 > 1 ? CPR / 4 : 1;  // instructions per swizzle repeat
+    static constexpr bool ONE = NWI % UP == 0;
+    static constexpr int PER = (NI + NWI - 1) / NWI;
+    static constexpr int NOFF = ONE ? 1 : PER;
+    uint32_t off[NOFF];                                 // byte offsets from the tile's first row
+    uint32_t step;                                      // bytes between a wave's instructions (ONE)
+
+    // pitch: row length of the matrix in elements; col0: first column copied
+    __device__ __forceinline__ void init(int pitch, int col0, int w) {
+        const int lane = threadIdx.x & 63;
+#pragma unroll
+        for (int k = 0; k < NOFF; ++k) {
+            const int pch = (w + NWI * k) * 64 + lane;
+            const int r = pch / CPR, pc = pch % CPR;
+            off[k] = (uint32_t)(r * pitch + col0 + (pc ^ swz<CPR>(r)) * 8) * 2u;
+        }
+        step = (uint32_t)(NWI * RPI * pitch) * 2u;
+    }
+    __device__ __forceinline__ void issue(const bf16_t* tile, bf16_t* lds, int w) const {
+        const char* base = reinterpret_cast<const char*>(tile);
+#pragma unroll
+        for (int k = 0; k < PER; ++k) {
+            const int u = w + NWI * k;
+            if (NI % NWI == 0 || u < NI) {
+                if constexpr (ONE) dma16o(base + (size_t)k * step, off[0], lds + u * 512);
+                else dma16o(base, off[k], lds + u * 512);
+            }
+        }
+    }
+};
+
 // Copies rows [0, 64) of a bf16 [rows][pitch] matrix, columns [col0, col0 + D),
 // into a swizzled LDS tile.  Rows at or past nvalid repeat row nvalid - 1
 // (finite values; they only meet masked or discarded entries).  Each wave
@@ -255,24 +314,46 @@ __device__ __forceinline__ void score_block(int rb, int sb, const bf16_t* Qs, co
     const float4 As = *reinterpret_cast<const float4*>(Aw + 16 * sb + 4 * g);
     const float Asv[4] = {As.x, As.y, As.z, As.w};
     float w[4];
+    if (sb < rb) {
+        // every key of an earlier 16-block differs from t first in bit
+        // 4 + floor(log2(rb ^ sb)): one level for the whole block
+        const float lam = lam_t[5 + (31 - __builtin_clz(rb ^ sb))];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int s = 16 * sb + 4 * g + i;
-        w[i] = s <= t ? acc[i] * lam_t[fenwick_level(t, s)] * __expf(At - Asv[i]) : 0.f;
+        for (int i = 0; i < 4; ++i) w[i] = acc[i] * lam * __expf(At - Asv[i]);
+    } else {
+        // diagonal block: per-key level, causal mask by selection (the
+        // masked entries' values are discarded whatever they are)
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int s = 16 * sb + 4 * g + i;
+            const float x = acc[i] * lam_t[fenwick_level(t, s)] * __expf(At - Asv[i]);
+            w[i] = s <= t ? x : 0.f;
+        }
     }
     *reinterpret_cast<bf16x4*>(Ps + t * PROW + 16 * sb + 4 * g) = pack4(w[0], w[1], w[2], w[3]);
     if (sb == rb && (rb & 1) == 0)
         *reinterpret_cast<bf16x4*>(Ps + t * PROW + 16 * (rb + 1) + 4 * g) = bf16x4{};
 }
 
-// The ten causal 16 x 16 score blocks of a tile, dealt round-robin to the waves.
+// The ten causal 16 x 16 score blocks of a tile.  With eight waves, waves
+// 0 and 1 take three blocks, waves 2 and 3 two and waves 4-7 none (those make
+// the tile copies and the output stores); otherwise they are dealt
+// round-robin.
 template <int DK, int NWT>
 __device__ __forceinline__ void scores_for_wave(int wave, const bf16_t* Qs, const bf16_t* Ks,
                                                 bf16_t* Ps, const float* Aw, const float* lam_s,
                                                 int L) {
-    for (int tau = wave; tau < NRB * (NRB + 1) / 2; tau += NWT) {
+    auto block = [&](int tau) __attribute__((always_inline)) {
         const int rb = tau < 1 ? 0 : tau < 3 ? 1 : tau < 6 ? 2 : 3;
         score_block<DK>(rb, tau - rb * (rb + 1) / 2, Qs, Ks, Ps, Aw, lam_s, L);
+    };
+    if constexpr (NWT == 8) {
+        // one loop (a single call site): waves 0-3 take tau = w, w + 4 and
+        // waves 0 and 1 also w + 8
+        const int t1 = wave < 2 ? wave + 12 : wave < 4 ? wave + 8 : 0;
+        for (int tau = wave; tau < t1; tau += 4) block(tau);
+    } else {
+        for (int tau = wave; tau < NRB * (NRB + 1) / 2; tau += NWT) block(tau);
     }
 }
 
@@ -351,12 +432,16 @@ __global__ __launch_bounds__(NW * 64) void k_seg_state(FusedParams p) {
     // every tile of a non-last segment is whole
     const int tile0 = (seg << p.m) + (sub << p.msub), ntl = 1 << p.msub;
 
+    TileCopy<DK, NW> ck;
+    TileCopy<DVW, NW> cv;
+    ck.init(DK, 0, wave);
+    cv.init(p.dv, cb, wave);
     auto issue = [&](int il, bf16_t* Kd, bf16_t* Vd, float* ad) __attribute__((always_inline)) {
         const size_t r = row0 + (size_t)(tile0 + il) * TC;
-        dma_tile<DK, NW>(p.k + r * DK, DK, 0, TC, Kd, wave);
-        dma_tile<DVW, NW>(p.v + r * p.dv, p.dv, cb, TC, Vd, wave);
+        ck.issue(p.k + r * DK, Kd, wave);
+        cv.issue(p.v + r * p.dv, Vd, wave);
         if (p.a_dma) {
-            if (wave == 0 && lane < TC / 4) dma16(p.a + r + 4 * lane, ad);
+            if (wave == 0 && lane < TC / 4) dma16o(p.a + r, 16u * lane, ad);
         } else if (wave == 0) {
             dma4(p.a + r + lane, ad);
         }
@@ -421,7 +506,7 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
     constexpr int DVW = NW * 16;
     constexpr int NKSH = H::NKS / NH;       // contraction steps of this wave's head-dim part
     constexpr int NDTH = H::NDT / NH;       // 16-row state blocks of this wave's part
-    constexpr int RBH = NRB / NH;           // row blocks whose output this wave writes
+
     static_assert(NKSH >= 1 && NDTH >= 1, "head dimension too small for the split");
     __shared__ __align__(16) bf16_t sQ0[TC * DK];
     __shared__ __align__(16) bf16_t sQ1[TC * DK];
@@ -436,7 +521,7 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
     __shared__ __align__(16) bf16_t sP[TC * PROW];
     __shared__ __align__(16) float sAw[NWT][TC];
     __shared__ __align__(16) float sEw[NWT][TC];
-    __shared__ __align__(16) f32x4 sX[(NH > 1 ? NW * NRB : 1) * 64];  // partial outputs
+    __shared__ __align__(16) f32x4 sX[(NH > 1 ? NH * NW * NRB : 1) * 64];  // partial outputs
 
     int blk = xcd_block(blockIdx.x, gridDim.x);
     const int dvb = blk % p.ndvb;
@@ -477,6 +562,18 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
         }
     }
 
+    // Issuing waves make the copies of the next tile and, with the d_k split,
+    // sum and store the previous tile's output, both after their scores: the
+    // upper head-dim half with eight waves (they hold fewer score blocks),
+    // every wave otherwise.
+    constexpr int NIW = NWT == 8 ? 4 : NWT;
+    const bool issuer = wave >= NWT - NIW;
+    const int iw = issuer ? wave - (NWT - NIW) : 0;
+    TileCopy<DK, NIW> cqk;  // Q and K tiles share the layout
+    TileCopy<DVW, NIW> cv;
+    cqk.init(DK, 0, iw);
+    cv.init(p.dv, cb, iw);
+
     // Every tile input goes global -> LDS through the DMA path: 16-byte
     // copies where rows are whole and aligned, 4-byte copies of lambda and a
     // otherwise (entries past the sequence are stored as zeros).
@@ -485,17 +582,25 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
         const int t0 = (tile0 + il) * TC;
         const int nvalid = min(TC, p.T - t0);
         const size_t r = row0 + t0;
-        dma_tile<DK, NWT>(p.q + r * DK, DK, 0, nvalid, Qd, wave);
-        dma_tile<DK, NWT>(p.k + r * DK, DK, 0, nvalid, Kd, wave);
-        dma_tile<DVW, NWT>(p.v + r * p.dv, p.dv, cb, nvalid, Vd, wave);
         const bool whole = nvalid == TC;
+        if (whole) {
+            cqk.issue(p.q + r * DK, Qd, iw);
+            cqk.issue(p.k + r * DK, Kd, iw);
+            cv.issue(p.v + r * p.dv, Vd, iw);
+        } else {
+            dma_tile<DK, NIW>(p.q + r * DK, DK, 0, nvalid, Qd, iw);
+            dma_tile<DK, NIW>(p.k + r * DK, DK, 0, nvalid, Kd, iw);
+            dma_tile<DVW, NIW>(p.v + r * p.dv, p.dv, cb, nvalid, Vd, iw);
+        }
+        // lambda from the last issuing wave down (those hold fewer Q/K/V jobs)
+        const int lw = NIW - 1 - iw;
         if (whole && p.lam_dma) {
             const int nch = 16 * L;  // 64 rows x L floats
-            for (int u = wave; u * 64 < nch; u += NWT)
-                if (u * 64 + lane < nch) dma16(p.lam + r * L + 4 * (u * 64 + lane), Ld + u * 256);
+            for (int u = lw; u * 64 < nch; u += NIW)
+                if (u * 64 + lane < nch) dma16o(p.lam + r * L, 16u * (u * 64 + lane), Ld + u * 256);
         } else {
             const int nel = nvalid * LP;
-            for (int u = wave; u * 64 < TC * LP; u += NWT) {
+            for (int u = lw; u * 64 < TC * LP; u += NIW) {
                 const int x = u * 64 + lane;
                 if (x < nel) {
                     const int row = x / LP, l = x - row * LP;
@@ -505,9 +610,9 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
                 }
             }
         }
-        if (wave == 0) {
+        if (iw == 0) {
             if (whole && p.a_dma) {
-                if (lane < TC / 4) dma16(p.a + r + 4 * lane, ad);
+                if (lane < TC / 4) dma16o(p.a + r, 16u * lane, ad);
             } else if (lane < nvalid) {
                 dma4(p.a + r + lane, ad);
             } else {
@@ -525,26 +630,40 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
         for (int kt = 0; kt < NDTH; ++kt) G[s][kt] = bf16x4{};
     }
 
-    // Output of the previous tile, rows this wave writes, waiting for the
-    // other head-dim half (d_k split only).  The halves meet in sX: each wave
-    // leaves the rows it does not write there at the end of a tile and picks
-    // up its own after the next tile's first barrier, so the exchange costs
-    // no barrier of its own.
-    f32x4 oprev[RBH];
+    // Output of the previous tile (d_k split only): after the P V product
+    // each wave leaves its partial rows (its half of the level products, and
+    // the intra-tile part for the row blocks it owns) in sX; after the next
+    // tile's first barrier the issuing waves of the last head-dim part sum
+    // the NH partials of their column slab and store the rows, so the
+    // exchange costs no barrier of its own.
     int prev_tile = -1, prev_valid = 0;
+    // The finisher of slab cs takes the row blocks rb = cs (mod NW) across
+    // all DVW columns, so that each store covers whole rows (DVW * 4 bytes
+    // of a row per LPR lanes) instead of 64-byte pieces of 16 rows.
     auto finish_prev = [&]() __attribute__((always_inline)) {
-        float* orow = p.out + (row0 + (size_t)prev_tile * TC) * p.dv + c0 + 4 * g;
+        constexpr int LPR = NW * 4;     // lanes per row (16 bytes each)
+        constexpr int RPI = 64 / LPR;   // rows per store
+        const int c = (lane % LPR) * 4;  // column within the block
+        const int m0 = lane / LPR;       // row within the store
+        for (int rb = cs; rb < NRB; rb += NW) {
+            // the C-layout lane holding (row m0 + RPI k, column c) of slab c / 16
+            const f32x4* xs = sX + ((c / 16) * NRB + rb) * 64 + ((c % 16) / 4) * 16 + m0;
+            float* op = p.out + (row0 + (size_t)prev_tile * TC + 16 * rb + m0) * p.dv + cb + c;
 #pragma unroll
-        for (int r = 0; r < RBH; ++r) {
-            const int rb = hh * RBH + r;
-            const f32x4 x = sX[(cs * NRB + rb) * 64 + lane];
-            const int row = 16 * rb + m16;
-            if (row < prev_valid)
-                *reinterpret_cast<float4*>(orow + (size_t)row * p.dv) =
-                    make_float4(oprev[r][0] + x[0], oprev[r][1] + x[1], oprev[r][2] + x[2],
-                                oprev[r][3] + x[3]);
+            for (int k = 0; k < 16 / RPI; ++k) {
+                f32x4 x = xs[k * RPI];
+#pragma unroll
+                for (int h = 1; h < NH; ++h) {
+                    const f32x4 y = xs[k * RPI + h * NW * NRB * 64];
+                    x[0] += y[0]; x[1] += y[1]; x[2] += y[2]; x[3] += y[3];
+                }
+                if (16 * rb + k * RPI + m0 < prev_valid)
+                    *reinterpret_cast<float4*>(op + (size_t)(k * RPI) * p.dv) =
+                        make_float4(x[0], x[1], x[2], x[3]);
+            }
         }
     };
+    const bool finisher = NH > 1 && hh == NH - 1;
 
     auto body = [&](int il, const bf16_t* Qc, const bf16_t* Kc, const bf16_t* Vc,
                     const float* Lc, const float* ac, bf16_t* Qn, bf16_t* Kn, bf16_t* Vn,
@@ -552,14 +671,19 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
         // tile il is in LDS and every wave is done with tile il - 1
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
-        if (il + 1 < ntl) issue(il + 1, Qn, Kn, Vn, Ln, an);
         if constexpr (NH > 1) {
-            if (prev_tile >= 0) finish_prev();
+            if (finisher && !issuer && prev_tile >= 0) finish_prev();
         }
         const int i = tile0 + il;
         const int nvalid = min(TC, p.T - i * TC);
         const float tot = tile_decay(ac, sAw[wave], sEw[wave]);
         scores_for_wave<DK, NWT>(wave, Qc, Kc, sP, sAw[wave], Lc, LP);
+        if (issuer) {
+            if constexpr (NH > 1) {
+                if (finisher && prev_tile >= 0) finish_prev();
+            }
+            if (il + 1 < ntl) issue(il + 1, Qn, Kn, Vn, Ln, an);
+        }
 
         // ---- level products (this wave's head-dim part, all rows), before the
         // barrier that publishes P: they do not need it.  The weight of level
@@ -568,31 +692,38 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
         f32x4 lv[NRB];
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) lv[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        // Q fragment of a level product: 8 consecutive head-dim rows per lane
-        // group, the order in which tile_state lays out the register states
-        auto qfrag = [&](int rb, int ks) __attribute__((always_inline)) {
-            typename H::frag r;
-            if constexpr (DK >= 32) r = ld8<DK>(Qc, 16 * rb + m16, 32 * ks + 8 * g);
-            else r = ld4<DK>(Qc, 16 * rb + m16, 4 * g);
-            return r;
-        };
-        // one row block at a time keeps few operands live
+        // Q fragments of the level products (this wave's head-dim part, all
+        // row blocks): 8 consecutive head-dim rows per lane group, the order in
+        // which tile_state lays out the register states.  Read once per tile.
+        typename H::frag qf[NRB][NKSH];
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) {
+#pragma unroll
+            for (int ks = 0; ks < NKSH; ++ks) {
+                if constexpr (DK >= 32) qf[rb][ks] = ld8<DK>(Qc, 16 * rb + m16, 32 * (ks0 + ks) + 8 * g);
+                else qf[rb][ks] = ld4<DK>(Qc, 16 * rb + m16, 4 * g);
+            }
+        }
         auto add_level = [&](const typename H::frag (&ga)[NKSH], int lev, float logd)
             __attribute__((always_inline)) {
-            // re-read the Q fragments for every level rather than keeping them
-            // live across levels (registers are the scarce resource here)
-            asm volatile("" ::: "memory");
             const float d = __expf(logd);
+            float w[NRB];
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb) w[rb] = Lc[(16 * rb + m16) * LP + lev];
+            f32x4 y[NRB];
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb) {
-                f32x4 y = {0.f, 0.f, 0.f, 0.f};
+                y[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < NKSH; ++ks) y = mma(ga[ks], qfrag(rb, ks0 + ks), y);
-                const float w = Lc[(16 * rb + m16) * LP + lev] * d;
-                lv[rb][0] += w * y[0];
-                lv[rb][1] += w * y[1];
-                lv[rb][2] += w * y[2];
-                lv[rb][3] += w * y[3];
+                for (int ks = 0; ks < NKSH; ++ks) y[rb] = mma(ga[ks], qf[rb][ks], y[rb]);
+            }
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb) {
+                const float wr = w[rb] * d;
+                lv[rb][0] += wr * y[rb][0];
+                lv[rb][1] += wr * y[rb][1];
+                lv[rb][2] += wr * y[rb][2];
+                lv[rb][3] += wr * y[rb][3];
             }
         };
         // levels inside the segment
@@ -626,7 +757,10 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
         }
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
-            if (rb / RBH == hh) {
+            // the row blocks whose intra-tile part this wave adds: with the
+            // d_k split the first half takes 0 and 3, the second 1 and 2
+            // (equal P V work)
+            if (NH == 1 || ((rb == 0 || rb == 3) ? 0 : 1) == hh) {
 #pragma unroll
                 for (int sp = 0; sp <= rb / 2; ++sp) {
                     const bf16x8 pb = *reinterpret_cast<const bf16x8*>(sP + (16 * rb + m16) * PROW +
@@ -637,14 +771,8 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
         }
 
         if constexpr (NH > 1) {
-            // hand over the rows the other half writes; keep ours until the
-            // next tile (or the end) picks up the other half's part
 #pragma unroll
-            for (int rb = 0; rb < NRB; ++rb)
-                if (rb / RBH != hh) sX[(cs * NRB + rb) * 64 + lane] = o[rb];
-#pragma unroll
-            for (int rb = 0; rb < NRB; ++rb)
-                if (rb / RBH == hh) oprev[rb % RBH] = o[rb];  // static indices only
+            for (int rb = 0; rb < NRB; ++rb) sX[((hh * NW + cs) * NRB + rb) * 64 + lane] = o[rb];
             prev_tile = i;
             prev_valid = nvalid;
         } else {
@@ -694,14 +822,14 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
         for (int q = 0; q < TOPMAX; ++q) logd_top[q] += tot;
     };
 
-    issue(0, sQ0, sK0, sV0, sL0, sa0);
+    if (issuer) issue(0, sQ0, sK0, sV0, sL0, sa0);
     for (int il = 0; il < ntl; il += 2) {
         body(il, sQ0, sK0, sV0, sL0, sa0, sQ1, sK1, sV1, sL1, sa1);
         if (il + 1 < ntl) body(il + 1, sQ1, sK1, sV1, sL1, sa1, sQ0, sK0, sV0, sL0, sa0);
     }
     if constexpr (NH > 1) {
         __syncthreads();
-        finish_prev();
+        if (finisher) finish_prev();
     }
 }
 
