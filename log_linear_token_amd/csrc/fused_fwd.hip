@@ -301,34 +301,43 @@ __device__ __forceinline__ void score_block(int rb, int sb, const bf16_t* Qs, co
     typedef HD<DK> H;
     const int lane = threadIdx.x & 63, m16 = lane & 15, g = lane >> 4;
     const int t = 16 * rb + m16;
-    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+    // every LDS read of the block is issued before the first product, so
+    // their latencies overlap instead of adding up
+    typename H::frag kf[H::NKS], qf[H::NKS];
 #pragma unroll
     for (int ks = 0; ks < H::NKS; ++ks) {
-        if constexpr (DK >= 32)
-            acc = mma(ld8<DK>(Ks, 16 * sb + m16, ks * 32 + 8 * g), ld8<DK>(Qs, t, ks * 32 + 8 * g), acc);
-        else
-            acc = mma(ld4<DK>(Ks, 16 * sb + m16, 4 * g), ld4<DK>(Qs, t, 4 * g), acc);
+        if constexpr (DK >= 32) {
+            kf[ks] = ld8<DK>(Ks, 16 * sb + m16, ks * 32 + 8 * g);
+            qf[ks] = ld8<DK>(Qs, t, ks * 32 + 8 * g);
+        } else {
+            kf[ks] = ld4<DK>(Ks, 16 * sb + m16, 4 * g);
+            qf[ks] = ld4<DK>(Qs, t, 4 * g);
+        }
     }
     const float* lam_t = lam_s + t * L;  // levels inside a tile are < L (see the host checks)
     const float At = Aw[t];
     const float4 As = *reinterpret_cast<const float4*>(Aw + 16 * sb + 4 * g);
-    const float Asv[4] = {As.x, As.y, As.z, As.w};
-    float w[4];
+    float lam[4];
     if (sb < rb) {
         // every key of an earlier 16-block differs from t first in bit
         // 4 + floor(log2(rb ^ sb)): one level for the whole block
-        const float lam = lam_t[5 + (31 - __builtin_clz(rb ^ sb))];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) w[i] = acc[i] * lam * __expf(At - Asv[i]);
+        lam[0] = lam[1] = lam[2] = lam[3] = lam_t[5 + (31 - __builtin_clz(rb ^ sb))];
     } else {
-        // diagonal block: per-key level, causal mask by selection (the
-        // masked entries' values are discarded whatever they are)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int s = 16 * sb + 4 * g + i;
-            const float x = acc[i] * lam_t[fenwick_level(t, s)] * __expf(At - Asv[i]);
-            w[i] = s <= t ? x : 0.f;
-        }
+        for (int i = 0; i < 4; ++i) lam[i] = lam_t[fenwick_level(t, 16 * sb + 4 * g + i)];
+    }
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < H::NKS; ++ks) acc = mma(kf[ks], qf[ks], acc);
+    const float Asv[4] = {As.x, As.y, As.z, As.w};
+    float w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        // diagonal block: causal mask by selection (the masked entries'
+        // values are discarded whatever they are)
+        const float x = acc[i] * lam[i] * __expf(At - Asv[i]);
+        w[i] = (sb < rb || 16 * sb + 4 * g + i <= t) ? x : 0.f;
     }
     *reinterpret_cast<bf16x4*>(Ps + t * PROW + 16 * sb + 4 * g) = pack4(w[0], w[1], w[2], w[3]);
     if (sb == rb && (rb & 1) == 0)
@@ -364,26 +373,50 @@ __device__ __forceinline__ void scores_for_wave(int wave, const bf16_t* Qs, cons
 // a level product over those 32 rows with natural 8-wide lane groups.
 // For d_k = 16 (NT = 1): u[0] holds rows 4g + i.  vf[sp] are the V fragments
 // (lane: V[32 sp + 8g + i][column]) shared with the P V product.
-template <int DK, int NT>
+// Operand reads are issued ahead of the products: for both 32-token halves
+// at once when BOTH (more registers, more overlap), else one half at a time.
+template <int DK, int NT, bool BOTH>
 __device__ __forceinline__ void tile_state(f32x4 (&u)[NT], int ks0, const bf16_t* Ks,
                                            const bf16x8 (&vf)[2], const float* Ew) {
     const int lane = threadIdx.x & 63, g = lane >> 4;
-#pragma unroll
-    for (int sp = 0; sp < 2; ++sp) {
-        const float4 e0 = *reinterpret_cast<const float4*>(Ew + 32 * sp + 8 * g);
-        const float4 e1 = *reinterpret_cast<const float4*>(Ew + 32 * sp + 8 * g + 4);
-        const float ev[8] = {e0.x, e0.y, e0.z, e0.w, e1.x, e1.y, e1.z, e1.w};
-        bf16x8 b;
-#pragma unroll
-        for (int i = 0; i < 8; ++i) b[i] = (__bf16)((float)vf[sp][i] * ev[i]);
+    constexpr int NR = DK >= 32 ? NT : 1;  // K fragments per 32-token half
+    constexpr int NB = BOTH ? 2 : 1;       // halves whose reads are in flight together
+    float4 e[NB][2];
+    bf16x8 kq[NB][NR];
+    auto load = [&](int sp, int slot) __attribute__((always_inline)) {
+        e[slot][0] = *reinterpret_cast<const float4*>(Ew + 32 * sp + 8 * g);
+        e[slot][1] = *reinterpret_cast<const float4*>(Ew + 32 * sp + 8 * g + 4);
         if constexpr (DK >= 32) {
 #pragma unroll
             for (int j = 0; j < NT / 2; ++j) {
-                u[2 * j] = mma(ld_tr8_q<DK>(Ks, 32 * sp, 32 * (ks0 + j)), b, u[2 * j]);
-                u[2 * j + 1] = mma(ld_tr8_q<DK>(Ks, 32 * sp, 32 * (ks0 + j) + 4), b, u[2 * j + 1]);
+                kq[slot][2 * j] = ld_tr8_q<DK>(Ks, 32 * sp, 32 * (ks0 + j));
+                kq[slot][2 * j + 1] = ld_tr8_q<DK>(Ks, 32 * sp, 32 * (ks0 + j) + 4);
             }
         } else {
-            u[0] = mma(ld_tr8<DK>(Ks, 32 * sp, 0), b, u[0]);
+            kq[slot][0] = ld_tr8<DK>(Ks, 32 * sp, 0);
+        }
+    };
+    auto product = [&](int sp, int slot) __attribute__((always_inline)) {
+        const float ev[8] = {e[slot][0].x, e[slot][0].y, e[slot][0].z, e[slot][0].w,
+                             e[slot][1].x, e[slot][1].y, e[slot][1].z, e[slot][1].w};
+        bf16x8 b;
+#pragma unroll
+        for (int i = 0; i < 8; ++i) b[i] = (__bf16)((float)vf[sp][i] * ev[i]);
+#pragma unroll
+        for (int j = 0; j < NR; ++j) u[j] = mma(kq[slot][j], b, u[j]);
+    };
+    if constexpr (BOTH) {
+        load(0, 0);
+        load(1, 1);
+        __builtin_amdgcn_sched_barrier(0);
+        product(0, 0);
+        product(1, 1);
+    } else {
+#pragma unroll
+        for (int sp = 0; sp < 2; ++sp) {
+            load(sp, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            product(sp, 0);
         }
     }
 }
@@ -466,7 +499,7 @@ __global__ __launch_bounds__(NW * 64) void k_seg_state(FusedParams p) {
         bf16x8 vf[2];
         vf[0] = ld_tr8<DVW>(Vc, 0, 16 * wave);
         vf[1] = ld_tr8<DVW>(Vc, 32, 16 * wave);
-        tile_state<DK, NDT>(u, 0, Kc, vf, sEw[wave]);
+        tile_state<DK, NDT, false>(u, 0, Kc, vf, sEw[wave]);
         total += tot;
     };
 
@@ -563,44 +596,54 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
     }
 
     // Issuing waves make the copies of the next tile and, with the d_k split,
-    // sum and store the previous tile's output, both after their scores: the
-    // upper head-dim half with eight waves (they hold fewer score blocks),
-    // every wave otherwise.
-    constexpr int NIW = NWT == 8 ? 4 : NWT;
+    // sum and store the previous tile's output, both after their scores.
+    // With eight waves, waves 4-7 (no score blocks) store the output and copy
+    // Q and K, and waves 2 and 3 (two score blocks) copy V, lambda and a;
+    // otherwise every wave does its share of everything.
+    constexpr int NIW = NWT == 8 ? 4 : NWT;      // Q/K copies and stores
     const bool issuer = wave >= NWT - NIW;
     const int iw = issuer ? wave - (NWT - NIW) : 0;
+    constexpr int NIW1 = NWT == 8 ? 2 : NIW;     // V, lambda and a copies
+    constexpr int P1W0 = NWT == 8 ? 2 : NWT - NIW;
+    const bool issuer1 = wave >= P1W0 && wave < P1W0 + NIW1;
+    const int i1 = issuer1 ? wave - P1W0 : 0;
     TileCopy<DK, NIW> cqk;  // Q and K tiles share the layout
-    TileCopy<DVW, NIW> cv;
+    TileCopy<DVW, NIW1> cv;
     cqk.init(DK, 0, iw);
-    cv.init(p.dv, cb, iw);
+    cv.init(p.dv, cb, i1);
 
     // Every tile input goes global -> LDS through the DMA path: 16-byte
     // copies where rows are whole and aligned, 4-byte copies of lambda and a
     // otherwise (entries past the sequence are stored as zeros).
-    auto issue = [&](int il, bf16_t* Qd, bf16_t* Kd, bf16_t* Vd, float* Ld, float* ad)
+    // part 0: Q and K (issuing waves iw); part 1: V, lambda and a (issuing
+    // waves i1)
+    auto issue = [&](int il, int part, bf16_t* Qd, bf16_t* Kd, bf16_t* Vd, float* Ld, float* ad)
         __attribute__((always_inline)) {
         const int t0 = (tile0 + il) * TC;
         const int nvalid = min(TC, p.T - t0);
         const size_t r = row0 + t0;
         const bool whole = nvalid == TC;
-        if (whole) {
-            cqk.issue(p.q + r * DK, Qd, iw);
-            cqk.issue(p.k + r * DK, Kd, iw);
-            cv.issue(p.v + r * p.dv, Vd, iw);
-        } else {
-            dma_tile<DK, NIW>(p.q + r * DK, DK, 0, nvalid, Qd, iw);
-            dma_tile<DK, NIW>(p.k + r * DK, DK, 0, nvalid, Kd, iw);
-            dma_tile<DVW, NIW>(p.v + r * p.dv, p.dv, cb, nvalid, Vd, iw);
+        if (part == 0) {
+            if (whole) {
+                cqk.issue(p.q + r * DK, Qd, iw);
+                cqk.issue(p.k + r * DK, Kd, iw);
+            } else {
+                dma_tile<DK, NIW>(p.q + r * DK, DK, 0, nvalid, Qd, iw);
+                dma_tile<DK, NIW>(p.k + r * DK, DK, 0, nvalid, Kd, iw);
+            }
+            return;
         }
+        if (whole) cv.issue(p.v + r * p.dv, Vd, i1);
+        else dma_tile<DVW, NIW1>(p.v + r * p.dv, p.dv, cb, nvalid, Vd, i1);
         // lambda from the last issuing wave down (those hold fewer Q/K/V jobs)
-        const int lw = NIW - 1 - iw;
+        const int lw = NIW1 - 1 - i1;
         if (whole && p.lam_dma) {
             const int nch = 16 * L;  // 64 rows x L floats
-            for (int u = lw; u * 64 < nch; u += NIW)
+            for (int u = lw; u * 64 < nch; u += NIW1)
                 if (u * 64 + lane < nch) dma16o(p.lam + r * L, 16u * (u * 64 + lane), Ld + u * 256);
         } else {
             const int nel = nvalid * LP;
-            for (int u = lw; u * 64 < TC * LP; u += NIW) {
+            for (int u = lw; u * 64 < TC * LP; u += NIW1) {
                 const int x = u * 64 + lane;
                 if (x < nel) {
                     const int row = x / LP, l = x - row * LP;
@@ -610,7 +653,7 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
                 }
             }
         }
-        if (iw == 0) {
+        if (i1 == 0) {
             if (whole && p.a_dma) {
                 if (lane < TC / 4) dma16o(p.a + r, 16u * lane, ad);
             } else if (lane < nvalid) {
@@ -682,8 +725,9 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
             if constexpr (NH > 1) {
                 if (finisher && prev_tile >= 0) finish_prev();
             }
-            if (il + 1 < ntl) issue(il + 1, Qn, Kn, Vn, Ln, an);
+            if (il + 1 < ntl) issue(il + 1, 0, Qn, Kn, Vn, Ln, an);
         }
+        if (issuer1 && il + 1 < ntl) issue(il + 1, 1, Qn, Kn, Vn, Ln, an);
 
         // ---- level products (this wave's head-dim part, all rows), before the
         // barrier that publishes P: they do not need it.  The weight of level
@@ -749,25 +793,30 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
         bf16x8 vf[2];
         vf[0] = ld_tr8<DVW>(Vc, 0, 16 * cs);
         vf[1] = ld_tr8<DVW>(Vc, 32, 16 * cs);
+        float eA[NRB];
+#pragma unroll
+        for (int rb = 0; rb < NRB; ++rb) eA[rb] = sAw[wave][16 * rb + m16];
         f32x4 o[NRB];
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
-            const float eA = __expf(sAw[wave][16 * rb + m16]);
-            o[rb] = f32x4{eA * lv[rb][0], eA * lv[rb][1], eA * lv[rb][2], eA * lv[rb][3]};
+            const float e = __expf(eA[rb]);
+            o[rb] = f32x4{e * lv[rb][0], e * lv[rb][1], e * lv[rb][2], e * lv[rb][3]};
         }
+        // the intra-tile part: all row blocks in the first head-dim half (the
+        // second half, slower to issue after the barrier, adds none); row
+        // block rb pairs with the first rb / 2 + 1 32-key halves of P
+        if (hh == 0) {
+            bf16x8 pf[NRB][2];
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
-            // the row blocks whose intra-tile part this wave adds: with the
-            // d_k split the first half takes 0 and 3, the second 1 and 2
-            // (equal P V work)
-            if (NH == 1 || ((rb == 0 || rb == 3) ? 0 : 1) == hh) {
+            for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-                for (int sp = 0; sp <= rb / 2; ++sp) {
-                    const bf16x8 pb = *reinterpret_cast<const bf16x8*>(sP + (16 * rb + m16) * PROW +
-                                                                       32 * sp + 8 * g);
-                    o[rb] = mma(vf[sp], pb, o[rb]);
-                }
-            }
+                for (int sp = 0; sp <= rb / 2; ++sp)
+                    pf[rb][sp] = *reinterpret_cast<const bf16x8*>(sP + (16 * rb + m16) * PROW + 32 * sp + 8 * g);
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb)
+#pragma unroll
+                for (int sp = 0; sp <= rb / 2; ++sp) o[rb] = mma(vf[sp], pf[rb][sp], o[rb]);
         }
 
         if constexpr (NH > 1) {
@@ -792,7 +841,7 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
             f32x4 u[NDTH];
 #pragma unroll
             for (int kt = 0; kt < NDTH; ++kt) u[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            tile_state<DK, NDTH>(u, ks0, Kc, vf, sEw[wave]);
+            tile_state<DK, NDTH, true>(u, ks0, Kc, vf, sEw[wave]);
             const int j = lssb((uint64_t)il + 1);
 #pragma unroll
             for (int s = 0; s < MLOC; ++s) {
@@ -822,7 +871,8 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
         for (int q = 0; q < TOPMAX; ++q) logd_top[q] += tot;
     };
 
-    if (issuer) issue(0, sQ0, sK0, sV0, sL0, sa0);
+    if (issuer) issue(0, 0, sQ0, sK0, sV0, sL0, sa0);
+    if (issuer1) issue(0, 1, sQ0, sK0, sV0, sL0, sa0);
     for (int il = 0; il < ntl; il += 2) {
         body(il, sQ0, sK0, sV0, sL0, sa0, sQ1, sK1, sV1, sL1, sa1);
         if (il + 1 < ntl) body(il + 1, sQ1, sK1, sV1, sL1, sa1, sQ0, sK0, sV0, sL0, sa0);
