@@ -552,9 +552,20 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
     __shared__ __align__(16) float sa0[TC];
     __shared__ __align__(16) float sa1[TC];
     __shared__ __align__(16) bf16_t sP[TC * PROW];
-    __shared__ __align__(16) float sAw[NWT][TC];
-    __shared__ __align__(16) float sEw[NWT][TC];
+    // tile decay (A_s and e^(A_end - A_s)), one copy per tile buffer, computed
+    // by the wave that copies a, as soon as its copy has landed
+    __shared__ __align__(16) float sAw0[TC];
+    __shared__ __align__(16) float sAw1[TC];
+    __shared__ __align__(16) float sEw0[TC];
+    __shared__ __align__(16) float sEw1[TC];
     __shared__ __align__(16) f32x4 sX[(NH > 1 ? NH * NW * NRB : 1) * 64];  // partial outputs
+    // sX slots hold the 64 lanes of a C-layout fragment; lane l of slab cs is
+    // stored at l ^ ((l / 16 + 4 (cs & 1)) & 7), so that the whole-row reads
+    // of the finishers (eight lanes over two slabs and four lane groups per
+    // LDS cycle) fall in distinct banks
+    auto xswz = [](int l, int slab) __attribute__((always_inline)) {
+        return l ^ (((l >> 4) + 4 * (slab & 1)) & 7);
+    };
 
     int blk = xcd_block(blockIdx.x, gridDim.x);
     const int dvb = blk % p.ndvb;
@@ -607,6 +618,7 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
     constexpr int P1W0 = NWT == 8 ? 2 : NWT - NIW;
     const bool issuer1 = wave >= P1W0 && wave < P1W0 + NIW1;
     const int i1 = issuer1 ? wave - P1W0 : 0;
+    const bool dwave = wave == P1W0;  // copies a; computes each tile's decay
     TileCopy<DK, NIW> cqk;  // Q and K tiles share the layout
     TileCopy<DVW, NIW1> cv;
     cqk.init(DK, 0, iw);
@@ -689,15 +701,16 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
         const int c = (lane % LPR) * 4;  // column within the block
         const int m0 = lane / LPR;       // row within the store
         for (int rb = cs; rb < NRB; rb += NW) {
-            // the C-layout lane holding (row m0 + RPI k, column c) of slab c / 16
-            const f32x4* xs = sX + ((c / 16) * NRB + rb) * 64 + ((c % 16) / 4) * 16 + m0;
+            const f32x4* xs = sX + ((c / 16) * NRB + rb) * 64;
             float* op = p.out + (row0 + (size_t)prev_tile * TC + 16 * rb + m0) * p.dv + cb + c;
 #pragma unroll
             for (int k = 0; k < 16 / RPI; ++k) {
-                f32x4 x = xs[k * RPI];
+                // the C-layout lane holding (row m0 + RPI k, column c) of slab c / 16
+                const int at = xswz(((c % 16) / 4) * 16 + m0 + k * RPI, c / 16);
+                f32x4 x = xs[at];
 #pragma unroll
                 for (int h = 1; h < NH; ++h) {
-                    const f32x4 y = xs[k * RPI + h * NW * NRB * 64];
+                    const f32x4 y = xs[at + h * NW * NRB * 64];
                     x[0] += y[0]; x[1] += y[1]; x[2] += y[2]; x[3] += y[3];
                 }
                 if (16 * rb + k * RPI + m0 < prev_valid)
@@ -709,8 +722,9 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
     const bool finisher = NH > 1 && hh == NH - 1;
 
     auto body = [&](int il, const bf16_t* Qc, const bf16_t* Kc, const bf16_t* Vc,
-                    const float* Lc, const float* ac, bf16_t* Qn, bf16_t* Kn, bf16_t* Vn,
-                    float* Ln, float* an) __attribute__((always_inline)) {
+                    const float* Lc, const float* Awc, const float* Ewc, bf16_t* Qn, bf16_t* Kn,
+                    bf16_t* Vn, float* Ln, float* an, float* Awn, float* Ewn)
+        __attribute__((always_inline)) {
         // tile il is in LDS and every wave is done with tile il - 1
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
@@ -719,8 +733,8 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
         }
         const int i = tile0 + il;
         const int nvalid = min(TC, p.T - i * TC);
-        const float tot = tile_decay(ac, sAw[wave], sEw[wave]);
-        scores_for_wave<DK, NWT>(wave, Qc, Kc, sP, sAw[wave], Lc, LP);
+        const float tot = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(Awc[TC - 1])));
+        scores_for_wave<DK, NWT>(wave, Qc, Kc, sP, Awc, Lc, LP);
         if (issuer) {
             if constexpr (NH > 1) {
                 if (finisher && prev_tile >= 0) finish_prev();
@@ -795,7 +809,7 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
         vf[1] = ld_tr8<DVW>(Vc, 32, 16 * cs);
         float eA[NRB];
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) eA[rb] = sAw[wave][16 * rb + m16];
+        for (int rb = 0; rb < NRB; ++rb) eA[rb] = Awc[16 * rb + m16];
         f32x4 o[NRB];
 #pragma unroll
         for (int rb = 0; rb < NRB; ++rb) {
@@ -821,7 +835,7 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
 
         if constexpr (NH > 1) {
 #pragma unroll
-            for (int rb = 0; rb < NRB; ++rb) sX[((hh * NW + cs) * NRB + rb) * 64 + lane] = o[rb];
+            for (int rb = 0; rb < NRB; ++rb) sX[((hh * NW + cs) * NRB + rb) * 64 + xswz(lane, cs)] = o[rb];
             prev_tile = i;
             prev_valid = nvalid;
         } else {
@@ -841,7 +855,7 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
             f32x4 u[NDTH];
 #pragma unroll
             for (int kt = 0; kt < NDTH; ++kt) u[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
-            tile_state<DK, NDTH, true>(u, ks0, Kc, vf, sEw[wave]);
+            tile_state<DK, NDTH, true>(u, ks0, Kc, vf, Ewc);
             const int j = lssb((uint64_t)il + 1);
 #pragma unroll
             for (int s = 0; s < MLOC; ++s) {
@@ -869,13 +883,23 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
         }
 #pragma unroll
         for (int q = 0; q < TOPMAX; ++q) logd_top[q] += tot;
+        // the next tile's decay, from its a (this wave's own copy)
+        if (dwave && il + 1 < ntl) {
+            __builtin_amdgcn_s_waitcnt(0);
+            tile_decay(an, Awn, Ewn);
+        }
     };
 
     if (issuer) issue(0, 0, sQ0, sK0, sV0, sL0, sa0);
     if (issuer1) issue(0, 1, sQ0, sK0, sV0, sL0, sa0);
+    if (dwave) {
+        __builtin_amdgcn_s_waitcnt(0);
+        tile_decay(sa0, sAw0, sEw0);
+    }
     for (int il = 0; il < ntl; il += 2) {
-        body(il, sQ0, sK0, sV0, sL0, sa0, sQ1, sK1, sV1, sL1, sa1);
-        if (il + 1 < ntl) body(il + 1, sQ1, sK1, sV1, sL1, sa1, sQ0, sK0, sV0, sL0, sa0);
+        body(il, sQ0, sK0, sV0, sL0, sAw0, sEw0, sQ1, sK1, sV1, sL1, sa1, sAw1, sEw1);
+        if (il + 1 < ntl)
+            body(il + 1, sQ1, sK1, sV1, sL1, sAw1, sEw1, sQ0, sK0, sV0, sL0, sa0, sAw0, sEw0);
     }
     if constexpr (NH > 1) {
         __syncthreads();
