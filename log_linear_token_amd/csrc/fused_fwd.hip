@@ -446,8 +446,12 @@ __global__ __launch_bounds__(NW * 64) void k_seg_state(FusedParams p) {
     __shared__ __align__(16) bf16_t sV1[TC * DVW];
     __shared__ __align__(16) float sa0[TC];
     __shared__ __align__(16) float sa1[TC];
-    __shared__ __align__(16) float sAw[NW][TC];
-    __shared__ __align__(16) float sEw[NW][TC];
+    // tile decay, one copy per tile buffer, computed by wave 0 (which copies
+    // a) as soon as its copy has landed
+    __shared__ __align__(16) float sAw0[TC];
+    __shared__ __align__(16) float sAw1[TC];
+    __shared__ __align__(16) float sEw0[TC];
+    __shared__ __align__(16) float sEw1[TC];
 
     const int nsegs = p.nseg - 1;
     const int nsub = 1 << (p.m - p.msub);
@@ -485,12 +489,13 @@ __global__ __launch_bounds__(NW * 64) void k_seg_state(FusedParams p) {
     for (int kt = 0; kt < NDT; ++kt) u[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
     float total = 0.f;
 
-    auto body = [&](int il, const bf16_t* Kc, const bf16_t* Vc, const float* ac, bf16_t* Kn,
-                    bf16_t* Vn, float* an) __attribute__((always_inline)) {
+    auto body = [&](int il, const bf16_t* Kc, const bf16_t* Vc, const float* Awc, const float* Ewc,
+                    bf16_t* Kn, bf16_t* Vn, float* an, float* Awn, float* Ewn)
+        __attribute__((always_inline)) {
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
         if (il + 1 < ntl) issue(il + 1, Kn, Vn, an);
-        const float tot = tile_decay(ac, sAw[wave], sEw[wave]);
+        const float tot = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(Awc[TC - 1])));
         const float f = __expf(tot);
 #pragma unroll
         for (int kt = 0; kt < NDT; ++kt) {
@@ -499,14 +504,22 @@ __global__ __launch_bounds__(NW * 64) void k_seg_state(FusedParams p) {
         bf16x8 vf[2];
         vf[0] = ld_tr8<DVW>(Vc, 0, 16 * wave);
         vf[1] = ld_tr8<DVW>(Vc, 32, 16 * wave);
-        tile_state<DK, NDT, false>(u, 0, Kc, vf, sEw[wave]);
+        tile_state<DK, NDT, false>(u, 0, Kc, vf, Ewc);
         total += tot;
+        if (wave == 0 && il + 1 < ntl) {
+            __builtin_amdgcn_s_waitcnt(0);
+            tile_decay(an, Awn, Ewn);
+        }
     };
 
     issue(0, sK0, sV0, sa0);
+    if (wave == 0) {
+        __builtin_amdgcn_s_waitcnt(0);
+        tile_decay(sa0, sAw0, sEw0);
+    }
     for (int il = 0; il < ntl; il += 2) {
-        body(il, sK0, sV0, sa0, sK1, sV1, sa1);
-        if (il + 1 < ntl) body(il + 1, sK1, sV1, sa1, sK0, sV0, sa0);
+        body(il, sK0, sV0, sAw0, sEw0, sK1, sV1, sa1, sAw1, sEw1);
+        if (il + 1 < ntl) body(il + 1, sK1, sV1, sAw1, sEw1, sK0, sV0, sa0, sAw0, sEw0);
     }
     // the whole segment's state, or one of its sub-range states (the scan
     // decays and sums those in order)
@@ -930,7 +943,7 @@ int bit_len(long x) {
 
 }  // namespace
 
-FusedPlan plan_fused(int BH, int T, int dk, int dv, int lu, int force_m) {
+FusedPlan plan_fused(int BH, int T, int dk, int dv, int lu, int force_m, int force_split) {
     FusedPlan pl{};
     if (lu > kFusedMaxL) return pl;  // lambda levels staged per token
     const int dvw = dv >= 64 ? 64 : dv;
@@ -969,11 +982,13 @@ FusedPlan plan_fused(int BH, int T, int dk, int dv, int lu, int force_m) {
     pl.nseg = (int)((pl.ntiles + (1L << best) - 1) >> best);
     pl.ntop = bit_len(pl.nseg - 1);
     pl.combo = best_combo;
-    // segment states in up to 8 sub-ranges, enough blocks for two per CU
+    // segment states in up to 8 sub-ranges: the fewest that give every CU a
+    // block (more sub-ranges add partial states to write and combine)
     pl.msub = best;
     while (pl.msub > 0 && best - pl.msub < 3 &&
-           pairs * (pl.nseg - 1) * (1L << (best - pl.msub)) < 512)
+           pairs * (pl.nseg - 1) * (1L << (best - pl.msub)) < 256)
         --pl.msub;
+    if (force_split >= 0) pl.msub = best > force_split ? best - force_split : 0;
     pl.ok = 1;
     return pl;
 }

@@ -64,7 +64,7 @@ struct FusedPlan {
     int ok, m, nseg, ntop, dvw, ndvb, ntiles, combo, msub;
 };
 // force_m >= 0 asks for segments of 2^force_m tiles (plan fails if that does not fit)
-FusedPlan plan_fused(int BH, int T, int dk, int dv, int lu, int force_m);
+FusedPlan plan_fused(int BH, int T, int dk, int dv, int lu, int force_m, int force_split);
 hipError_t launch_fused_fwd(const FusedParams& p, const FwdParams& scan, unsigned stages,
                             hipStream_t stream);
 

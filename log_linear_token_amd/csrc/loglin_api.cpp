@@ -111,6 +111,17 @@ int forced_segment_log2() {
     return -1;
 }
 
+// LOGLIN_FUSED_SPLIT=<n> (a power of two, 1..8) fixes the number of sub-ranges
+// the segment states are built in; -1 when unset (the planner chooses).
+int forced_split_log2() {
+    const char* e = getenv("LOGLIN_FUSED_SPLIT");
+    if (!e || !*e) return -1;
+    const long n = strtol(e, nullptr, 10);
+    for (int k = 0; k <= 3; ++k)
+        if (n == (1L << k)) return k;
+    return -1;
+}
+
 struct Plan {
     Path path;
     FusedPlan fused;
@@ -123,7 +134,7 @@ Plan make_plan(long BH, int T, int dk, int dv, int C, loglin_dtype dt) {
     pl.path = kPathChunked;
     pl.N = ((long)T + C - 1) / C;
     if (dt == LOGLIN_BF16 && !force_chunked() && T > 0 && BH > 0) {
-        FusedPlan f = plan_fused((int)BH, T, dk, dv, levels_needed(T), forced_segment_log2());
+        FusedPlan f = plan_fused((int)BH, T, dk, dv, levels_needed(T), forced_segment_log2(), forced_split_log2());
         if (f.ok) {
             pl.path = kPathFused;
             pl.fused = f;

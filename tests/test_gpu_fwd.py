@@ -98,6 +98,31 @@ def test_fused_segments_vs_materialised_mask(T, dk, dv, seg, variant, monkeypatc
     assert err <= TOL_BF16, err
 
 
+@pytest.mark.parametrize("split", [1, 2, 4, 8])
+def test_fused_segment_state_sub_ranges(split, monkeypatch):
+    """Segment states built in 1, 2, 4 or 8 sub-ranges that the segment scan
+    decays and sums in order: the output must not depend on the split."""
+    banner(f"fused sub-ranges split={split}")
+    monkeypatch.setenv("LOGLIN_FUSED_SEGMENT", "32")
+    monkeypatch.setenv("LOGLIN_FUSED_SPLIT", str(split))
+    T, dk, dv = 8192 + 100, 128, 64
+    L = (T - 1).bit_length() + 1
+    cfg = I.CONFIGS["fwd2k"].scaled(B=1, H=2, T=T, dk=dk, dv=dv, C=64, L=L, qk="scaled")
+    plan = LL.loglin_fwd_plan(1, 2, T, dk, dv, 64)
+    assert plan["path"] == "fused" and plan["seg_tiles"] == 32 and plan["state_split"] == split, plan
+    d = I.make_fwd(cfg, "weak", seed=split)
+    got = _run(d)
+    # rows of the last segment read every scanned level; compare them and a
+    # spread of earlier rows with the materialised mask, row by row
+    rows = np.concatenate([np.arange(0, T, 997), np.arange(T - 300, T)])
+    errs = []
+    for h in range(2):
+        want = ref.form_a_rows(d["q"][0, h], d["k"][0, h], d["v"][0, h], d["a"][0, h],
+                               d["lam"][0, h], rows)
+        errs.append(slice_rel_err(got[0, h, rows], want, 0))
+    assert max(errs) <= TOL_BF16, errs
+
+
 @pytest.mark.parametrize("C,T,dk,dv", [(16, 333, 16, 32), (64, 777, 128, 64), (128, 1000, 128, 128),
                                        (32, 31, 64, 64)])
 def test_chunked_path_bf16(C, T, dk, dv, monkeypatch):
