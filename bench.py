@@ -137,17 +137,22 @@ def fwd_models(cfg, plan) -> dict:
 
 
 def decode_bytes(pos0: np.ndarray, H: int, dk: int, dv: int, Lmax: int, steps: int) -> float:
-    """Average algorithmic bytes per decode step: each (sequence, head) reads the
-    1 + popcount(t-1) live states of position t-1 (which the output needs) and
-    writes the two it changes, the merged level and level 0 (fp32 d_k x d_v
-    each), plus q, k, v (bf16), a, lambda, the level scales and out."""
+    """Average algorithmic bytes per decode step (steps counted from a load).
+
+    At position t >= 1 each (sequence, head) reads the popcount(t-1) live
+    levels above 0 (fp32 d_k x d_v each; the output needs them) and writes the
+    merged level j+1.  Level 0 is the previous token's k and v (two vectors)
+    except on the first step after a load, when it is the loaded matrix and is
+    read as such.  Plus q, k, v (bf16), a, lambda, the level scales (read and
+    written), the level-0 vectors (read and written) and out."""
     st = dk * dv * 4
-    small = (2 * dk + dv) * 2 + 4 + Lmax * 4 + 2 * Lmax * 4 + dv * 4
+    small = (2 * dk + dv) * 2 + 4 + Lmax * 4 + 2 * Lmax * 4 + 2 * (dk + dv) * 4 + dv * 4
     tot = 0.0
     for s in range(steps):
         t = pos0 + s
-        pcm = np.array([bin(int(x) - 1).count("1") if x >= 1 else -1 for x in t])
-        tot += float(np.sum((1 + pcm) + 2)) * st * H + len(t) * H * small
+        live = np.array([bin(int(x) - 1).count("1") + (1 if s == 0 else 0) if x >= 1 else 0 for x in t])
+        merged = (t >= 1).astype(np.int64)
+        tot += float(np.sum(live + merged)) * st * H + len(t) * H * small
     return tot / steps
 
 

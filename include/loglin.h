@@ -143,8 +143,10 @@ LOGLIN_API loglin_status loglin_fwd_chunked_stages(const void* q, const void* k,
  * Decode state: for nseq sequences x H heads, Lmax level states of dk x dv
  * (S = sum k v^T orientation) plus the next position of each sequence.  Each
  * level is held as an fp32 matrix and a scalar log-scale (the state is the
- * matrix times exp(scale)), so a step rewrites only the level it merges into
- * and level 0; loglin_state_export returns the states themselves.
+ * matrix times exp(scale)), and level 0, which only ever holds the newest
+ * token's k v^T, as the vectors k and v once a step has run; a step then
+ * rewrites only the level it merges into.  loglin_state_export returns the
+ * states themselves (dk x dv matrices).
  * Allocates device memory (hipMalloc) and zeroes it on `stream`; every
  * sequence starts at position 0.  dk, dv in {16, 32, 64, 128};
  * 1 <= Lmax <= 48.  *st is set only on success.

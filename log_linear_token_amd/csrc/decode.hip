@@ -10,10 +10,12 @@
 //
 // Storage: each level keeps an fp32 d_k x d_v matrix X and a log-scale sigma,
 // the state being S = exp(sigma) X.  Decaying a level only adds a_t to its
-// sigma, so a step writes two matrices (the merged level j+1 and level 0)
-// and reads the 1 + popcount(t-1) live ones, which the output needs anyway.
-// Slots that are not live are neither read nor written (their contents are
-// stale; the export zeroes them and applies the scales).
+// sigma.  Level 0 only ever holds the newest token's k v^T, so after the first
+// step it is kept as the two vectors k and v (raw0) and expanded where it is
+// used.  A step then writes one matrix (the merged level j+1) and reads the
+// popcount(t-1) live levels above 0, which the output needs anyway.  Slots that
+// are not live are neither read nor written (their contents are stale; the
+// export zeroes them, applies the scales and expands level 0).
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -27,6 +29,7 @@ constexpr int kMaxPer = 16;  // float4 elements per thread for a 128 x 128 state
 template <typename E>
 __global__ __launch_bounds__(kThreads) void k_decode_step(DecodeParams p) {
     __shared__ float qs[128], ks[128], vs[128];
+    __shared__ float k0[128], v0[128];  // the previous token: level 0 when raw0
     __shared__ float sig_s[64];
     __shared__ float4 red[kThreads];
     const int sh = blockIdx.x;  // sequence * H + head
@@ -45,7 +48,15 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(DecodeParams p) {
     }
     if (tid < dv) vs[tid] = to_f32(v[tid]);
     if (tid < p.Lmax) sig_s[tid] = sig[tid];
+    float* raw = p.raw + (size_t)sh * (dk + dv);
+    if (p.raw0) {
+        if (tid < dk) k0[tid] = raw[tid];
+        if (tid < dv) v0[tid] = raw[dk + tid];
+    }
     __syncthreads();
+    // this token becomes level 0 (every thread has read the previous one)
+    if (tid < dk) raw[tid] = ks[tid];
+    if (tid < dv) raw[dk + tid] = vs[tid];
 
     const float a = p.a[sh];
     const float alpha = __expf(a);
@@ -55,10 +66,10 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(DecodeParams p) {
     const int quads = dv / 4;
     const int col = (tid % quads) * 4;  // the same for every element of this thread
 
-    // positions of this thread: e4 = tid + kThreads * u
-    int row[kMaxPer];
-#pragma unroll
-    for (int u = 0; u < kMaxPer; ++u) row[u] = (int)(((size_t)(tid + kThreads * u) * 4) / dv);
+    // positions of this thread: e4 = tid + kThreads * u, in row r0 + u * rstep
+    // (4 kThreads is a multiple of every supported dv)
+    const int r0 = tid * 4 / dv, rstep = kThreads * 4 / dv;
+    auto row = [&](int u) { return r0 + u * rstep; };
     auto valid = [&](int u) { return (size_t)(tid + kThreads * u) < nst4; };
 
     float4 part = make_float4(0.f, 0.f, 0.f, 0.f);
@@ -77,7 +88,23 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(DecodeParams p) {
         float4 acc[kMaxPer];
 #pragma unroll
         for (int u = 0; u < kMaxPer; ++u) acc[u] = make_float4(0.f, 0.f, 0.f, 0.f);
-        for (int l = 0; l <= j; ++l) {
+        int lfirst = 0;
+        if (p.raw0) {  // level 0 = k0 v0^T
+            const float w = alpha * __expf(sig_s[0]);
+            const float4 vv = make_float4(w * v0[col], w * v0[col + 1], w * v0[col + 2], w * v0[col + 3]);
+#pragma unroll
+            for (int u = 0; u < kMaxPer; ++u) {
+                if (valid(u)) {
+                    const float kr = k0[row(u)];
+                    acc[u].x += kr * vv.x;
+                    acc[u].y += kr * vv.y;
+                    acc[u].z += kr * vv.z;
+                    acc[u].w += kr * vv.w;
+                }
+            }
+            lfirst = 1;
+        }
+        for (int l = lfirst; l <= j; ++l) {
             const float w = alpha * __expf(sig_s[l]);
             const float4* src = X + (size_t)l * nst4;
             float4 x[kMaxPer];
@@ -100,7 +127,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(DecodeParams p) {
         for (int u = 0; u < kMaxPer; ++u) {
             if (valid(u)) {
                 dst[tid + kThreads * u] = acc[u];
-                accum(lj, qs[row[u]], acc[u]);
+                accum(lj, qs[row(u)], acc[u]);
             }
         }
         // live levels above j+1: decay through the scale, read for the output
@@ -114,19 +141,18 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(DecodeParams p) {
                 if (valid(u)) x[u] = s[tid + kThreads * u];
 #pragma unroll
             for (int u = 0; u < kMaxPer; ++u)
-                if (valid(u)) accum(w, qs[row[u]], x[u]);
+                if (valid(u)) accum(w, qs[row(u)], x[u]);
         }
     }
-    // level 0 holds the new token alone
+    // level 0 holds the new token alone (kept as k, v above)
     const float l0 = lam[0];
 #pragma unroll
     for (int u = 0; u < kMaxPer; ++u) {
         if (valid(u)) {
-            const float kr = ks[row[u]];
+            const float kr = ks[row(u)];
             const float4 y = make_float4(kr * vs[col], kr * vs[col + 1], kr * vs[col + 2],
                                          kr * vs[col + 3]);
-            X[tid + kThreads * u] = y;
-            accum(l0, qs[row[u]], y);
+            accum(l0, qs[row(u)], y);
         }
     }
 
@@ -166,7 +192,16 @@ __global__ void k_state_export(DecodeParams p, float4* dst) {
         float4 x = make_float4(0.f, 0.f, 0.f, 0.f);
         if (live) {
             const float w = __expf(p.sigma[slot]);
-            x = src[e];
+            if (l == 0 && p.raw0) {  // k v^T of the newest token
+                const size_t idx = (e % nst4) * 4;
+                const int r = (int)(idx / p.dv), c = (int)(idx % p.dv);
+                const float* raw = p.raw + (slot / p.Lmax) * (p.dk + p.dv);
+                const float kr = raw[r];
+                x = make_float4(kr * raw[p.dk + c], kr * raw[p.dk + c + 1], kr * raw[p.dk + c + 2],
+                                kr * raw[p.dk + c + 3]);
+            } else {
+                x = src[e];
+            }
             x.x *= w; x.y *= w; x.z *= w; x.w *= w;
         }
         dst[e] = x;

@@ -71,6 +71,8 @@ hipError_t launch_fused_fwd(const FusedParams& p, const FwdParams& scan, unsigne
 struct DecodeParams {
     float* states;            // [nseq][H][Lmax][dk][dv] matrices X (state = exp(sigma) X)
     float* sigma;             // [nseq][H][Lmax] per-level log-scales
+    float* raw;               // [nseq][H][dk + dv]: k and v of the newest token (level 0)
+    int raw0;                 // level 0 is raw's k v^T (else the matrix in states)
     const int64_t* base_pos;  // [nseq]: position of the first step after the last load
     int64_t step;             // steps taken since that load
     const void* q;            // [nseq][H][dk]

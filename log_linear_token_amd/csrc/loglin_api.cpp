@@ -328,6 +328,7 @@ struct loglin_state {
     int nseq, H, dk, dv, Lmax;
     float* levels;               // device [nseq][H][Lmax][dk][dv] matrices X
     float* sigma;                // device [nseq][H][Lmax] log-scales (state = exp(sigma) X)
+    float* raw;                  // device [nseq][H][dk + dv]: level 0 as k, v once a step ran
     int64_t* base_pos;           // device [nseq]
     std::vector<int64_t> host_base;  // host mirror of base_pos
     int64_t step;                // steps since the last load
@@ -347,6 +348,8 @@ DecodeParams decode_params(const loglin_state* st) {
     DecodeParams p{};
     p.states = st->levels;
     p.sigma = st->sigma;
+    p.raw = st->raw;
+    p.raw0 = st->step > 0;  // every step rewrites level 0 of every (sequence, head)
     p.base_pos = st->base_pos;
     p.step = st->step;
     p.nseq = st->nseq;
@@ -407,6 +410,14 @@ loglin_status loglin_state_init(loglin_state** out, int nseq, int H, int dk, int
         delete st;
         return fail(LOGLIN_ENOMEM, "hipMalloc level scales: %s", hipGetErrorString(e));
     }
+    e = hipMalloc(&st->raw, (size_t)nseq * H * (dk + dv) * sizeof(float));
+    if (e != hipSuccess) {
+        (void)hipFree(st->levels);
+        (void)hipFree(st->base_pos);
+        (void)hipFree(st->sigma);
+        delete st;
+        return fail(LOGLIN_ENOMEM, "hipMalloc level 0 vectors: %s", hipGetErrorString(e));
+    }
     hipStream_t s = static_cast<hipStream_t>(stream);
     e = hipMemsetAsync(st->levels, 0, bytes, s);
     if (e == hipSuccess) e = hipMemsetAsync(st->base_pos, 0, (size_t)nseq * sizeof(int64_t), s);
@@ -415,6 +426,7 @@ loglin_status loglin_state_init(loglin_state** out, int nseq, int H, int dk, int
         (void)hipFree(st->levels);
         (void)hipFree(st->base_pos);
         (void)hipFree(st->sigma);
+        (void)hipFree(st->raw);
         delete st;
         return hip_fail(e, "loglin_state_init");
     }
@@ -432,7 +444,9 @@ loglin_status loglin_state_free(loglin_state* st) {
     hipError_t e1 = hipFree(st->levels);
     hipError_t e2 = hipFree(st->base_pos);
     hipError_t e3 = hipFree(st->sigma);
+    hipError_t e4 = hipFree(st->raw);
     if (e2 == hipSuccess) e2 = e3;
+    if (e2 == hipSuccess) e2 = e4;
     delete st;
     if (e != hipSuccess) return hip_fail(e, "loglin_state_free (synchronize)");
     if (e1 != hipSuccess) return hip_fail(e1, "loglin_state_free");
