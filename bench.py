@@ -173,11 +173,18 @@ def cpu_baseline(cfg, d) -> dict:
     dt = time.perf_counter() - t0
     # a token of the workload is one position of one sequence across all H heads
     toks = nslices * cfg.T / cfg.H
+    # one core, on two slices
+    n1 = 2
+    t0 = time.perf_counter()
+    ref.form_b(q[:n1], k[:n1], v[:n1], a[:n1], lam[:n1], nthreads=1)
+    dt1 = time.perf_counter() - t0
     return {"value": toks / dt, "unit": "tokens/s", "cores": min(threads, nslices),
             "kind": "oracle",
             "sample": f"fp64 Fenwick recurrence over {nslices} of the {cfg.B * cfg.H} "
                       f"(batch, head) slices of fwd8k, all {cfg.T} positions each "
                       f"({dt:.1f} s wall); tokens counted as slices*T/H",
+            "value_1core": n1 * cfg.T / cfg.H / dt1,
+            "sample_1core": f"the same recurrence on {n1} slices with one thread ({dt1:.1f} s wall)",
             "cpu_model": _cpu_model()}
 
 
@@ -202,6 +209,8 @@ def main() -> int:
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-other", action="store_true",
+                    help="skip the 2K and 64K forward workloads")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 1 GiB device-to-device copy (for scaling HBM counters)")
     args = ap.parse_args()
@@ -279,8 +288,7 @@ def main() -> int:
     roof = {"kernel": dom, "bound": "hbm", "achieved": round(km["GB/s"], 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(km["GB/s"] / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(dom),
-            "mfma": {"achieved": round(km["TFLOP/s"], 2), "peak": BF16_PEAK_TFLOPS,
-                     "unit": "TFLOP/s", "frac": round(km["TFLOP/s"] / BF16_PEAK_TFLOPS, 4)}}
+            "mfma": mfma_entry(km)}
 
     result = {
         "metric": "fwd tokens/s + MFMA util, log-linear mixer T=8192; decode steps/s",
@@ -297,12 +305,70 @@ def main() -> int:
     del q, k, v, a, lam, out, ws
     torch.cuda.empty_cache()
 
+    if not args.no_other:
+        result["other_workloads"] = [bench_fwd_other(n, args.steps, args.warmup)
+                                     for n in ("fwd2k", "long64k")]
     if not args.no_decode:
         result["decode"] = bench_decode(args.decode_steps)
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, d)
     print(json.dumps(result), flush=True)
     return 0
+
+
+def mfma_entry(km: dict) -> dict:
+    """MFMA side of a forward kernel: achieved bf16 TFLOP/s against the dense
+    peak and against what HBM allows at the kernel's arithmetic intensity."""
+    ai = km["alg_flops"] / km["alg_bytes"]
+    attainable = min(BF16_PEAK_TFLOPS, ai * HBM_PEAK_GBS / 1e3)
+    return {"achieved": round(km["TFLOP/s"], 2), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(km["TFLOP/s"] / BF16_PEAK_TFLOPS, 4),
+            "flop_per_byte": round(ai, 1), "attainable": round(attainable, 1),
+            "frac_of_attainable": round(km["TFLOP/s"] / attainable, 4)}
+
+
+def bench_fwd_other(name: str, steps: int, warmup: int) -> dict:
+    """Forward throughput of another workload at 1 GPU: the whole path per
+    step, and the output kernel alone against the HBM and MFMA rooflines."""
+    cfg = I.CONFIGS[name]
+    log(f"{name}: generating inputs (B={cfg.B} H={cfg.H} T={cfg.T} dk={cfg.dk} dv={cfg.dv})")
+    d = I.make_fwd(cfg, "base")
+    dev = lambda x, dt=torch.float32: torch.from_numpy(x).to("cuda").to(dt).contiguous()  # noqa
+    q, k, v = (dev(d[n], torch.bfloat16) for n in ("q", "k", "v"))
+    a, lam = dev(d["a"]), dev(d["lam"])
+    del d
+    out = torch.empty((cfg.B, cfg.H, cfg.T, cfg.dv), device="cuda")
+    ws = torch.empty(max(1, LL.loglin_fwd_workspace_bytes(cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv, cfg.C,
+                                                          torch.bfloat16)),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+
+    def fwd(mask=LL.STAGE_ALL):
+        LL.loglin_fwd_chunked_stages(q, k, v, a, lam, cfg.C, mask, out=out, workspace=ws)
+
+    for _ in range(warmup):
+        fwd()
+    ms = timed(fwd, steps, stream)
+    plan = LL.loglin_fwd_plan(cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv, cfg.C, torch.bfloat16)
+    models = fwd_models(cfg, plan)
+    name_out = list(models)[-1]
+    fwd(LL.STAGE_OUTPUT)
+    kms = timed(lambda: fwd(LL.STAGE_OUTPUT), steps, stream)
+    m = models[name_out]
+    km = {"ms": kms, "GB/s": m["bytes"] / (kms / 1e3) / 1e9, "TFLOP/s": m["flops"] / (kms / 1e3) / 1e12,
+          "alg_bytes": m["bytes"], "alg_flops": m["flops"]}
+    tps = cfg.B * cfg.T / (ms / 1e3)
+    log(f"{name}: {ms:.3f} ms/step, {tps:.3e} tokens/s; {name_out} {kms:.3f} ms, "
+        f"{km['GB/s']:.0f} GB/s")
+    del q, k, v, a, lam, out, ws
+    torch.cuda.empty_cache()
+    return {"workload": name, "tokens_per_s": tps, "ms_per_step": ms,
+            "config": {"B": cfg.B, "H": cfg.H, "T": cfg.T, "dk": cfg.dk, "dv": cfg.dv, "C": cfg.C,
+                       "L": cfg.L},
+            "plan": plan,
+            "roofline": {"kernel": name_out, "bound": "hbm", "achieved": round(km["GB/s"], 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                         "frac": round(km["GB/s"] / HBM_PEAK_GBS, 4), "mfma": mfma_entry(km)}}
 
 
 def bench_decode(steps: int) -> dict:
