@@ -24,6 +24,16 @@ namespace loglin {
 namespace {
 
 constexpr int kThreads = 256;
+
+// level matrices are streamed once per step: non-temporal 16-byte accesses
+__device__ __forceinline__ float4 ld_stream(const float4* p) {
+    const f32x4 x = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(p));
+    return make_float4(x[0], x[1], x[2], x[3]);
+}
+__device__ __forceinline__ void st_stream(float4* p, const float4& v) {
+    const f32x4 x = {v.x, v.y, v.z, v.w};
+    __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(p));
+}
 constexpr int kMaxPer = 16;  // float4 elements per thread for a 128 x 128 state
 
 template <typename E>
@@ -110,7 +120,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(DecodeParams p) {
             float4 x[kMaxPer];
 #pragma unroll
             for (int u = 0; u < kMaxPer; ++u)
-                if (valid(u)) x[u] = src[tid + kThreads * u];
+                if (valid(u)) x[u] = ld_stream(src + tid + kThreads * u);
 #pragma unroll
             for (int u = 0; u < kMaxPer; ++u) {
                 if (valid(u)) {
@@ -126,7 +136,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(DecodeParams p) {
 #pragma unroll
         for (int u = 0; u < kMaxPer; ++u) {
             if (valid(u)) {
-                dst[tid + kThreads * u] = acc[u];
+                st_stream(dst + tid + kThreads * u, acc[u]);
                 accum(lj, qs[row(u)], acc[u]);
             }
         }
@@ -138,7 +148,7 @@ __global__ __launch_bounds__(kThreads) void k_decode_step(DecodeParams p) {
             float4 x[kMaxPer];
 #pragma unroll
             for (int u = 0; u < kMaxPer; ++u)
-                if (valid(u)) x[u] = s[tid + kThreads * u];
+                if (valid(u)) x[u] = ld_stream(s + tid + kThreads * u);
 #pragma unroll
             for (int u = 0; u < kMaxPer; ++u)
                 if (valid(u)) accum(w, qs[row(u)], x[u]);
