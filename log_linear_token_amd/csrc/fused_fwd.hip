@@ -726,9 +726,8 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
                     const f32x4 y = xs[at + h * NW * NRB * 64];
                     x[0] += y[0]; x[1] += y[1]; x[2] += y[2]; x[3] += y[3];
                 }
-                if (16 * rb + k * RPI + m0 < prev_valid)
-                    *reinterpret_cast<float4*>(op + (size_t)(k * RPI) * p.dv) =
-                        make_float4(x[0], x[1], x[2], x[3]);
+                if (16 * rb + k * RPI + m0 < prev_valid)  // written once: non-temporal
+                    __builtin_nontemporal_store(x, reinterpret_cast<f32x4*>(op + (size_t)(k * RPI) * p.dv));
             }
         }
     };
@@ -856,9 +855,8 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb) {
                 const int r = 16 * rb + m16;
-                if (r < nvalid)
-                    *reinterpret_cast<float4*>(orow + (size_t)r * p.dv) =
-                        make_float4(o[rb][0], o[rb][1], o[rb][2], o[rb][3]);
+                if (r < nvalid)  // written once: non-temporal
+                    __builtin_nontemporal_store(o[rb], reinterpret_cast<f32x4*>(orow + (size_t)r * p.dv));
             }
         }
 
