@@ -57,6 +57,28 @@ def measured_traffic(kernel: str):
     return None
 
 
+NSETS = 3  # input/output copies the timed steps rotate through
+
+
+def rotating_forward(cfg, q, k, v, a, lam, ws):
+    """A forward over NSETS copies of the inputs and outputs, the next copy
+    on every call: each step reads inputs that the previous steps did not
+    touch, so none of them is served from the 256 MB last-level cache (every
+    copy of the 8K workload's inputs is 335 MB)."""
+    sets = [(q, k, v, a, lam, torch.empty((cfg.B, cfg.H, cfg.T, cfg.dv), device="cuda"))]
+    for _ in range(NSETS - 1):
+        sets.append(tuple(x.clone() for x in (q, k, v, a, lam)) +
+                    (torch.empty((cfg.B, cfg.H, cfg.T, cfg.dv), device="cuda"),))
+    state = {"i": 0}
+
+    def fwd(mask=LL.STAGE_ALL):
+        qq, kk, vv, aa, ll, oo = sets[state["i"] % NSETS]
+        state["i"] += 1
+        LL.loglin_fwd_chunked_stages(qq, kk, vv, aa, ll, cfg.C, mask, out=oo, workspace=ws)
+
+    return fwd, sets
+
+
 def log(msg: str) -> None:
     print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
@@ -204,8 +226,11 @@ def _cpu_model() -> str:
 def main() -> int:
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    # the GPU needs some tens of milliseconds of work to reach its steady clock:
+    # the default warm-up covers that (200 forward steps of the 8K workload
+    # take about 35 ms)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
@@ -238,13 +263,10 @@ def main() -> int:
     dev = lambda x, dt=torch.float32: torch.from_numpy(x).to("cuda").to(dt).contiguous()  # noqa
     q, k, v = (dev(d[n], torch.bfloat16) for n in ("q", "k", "v"))
     a, lam = dev(d["a"]), dev(d["lam"])
-    out = torch.empty((cfg.B, cfg.H, cfg.T, cfg.dv), device="cuda")
     ws = torch.empty(LL.loglin_fwd_workspace_bytes(cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv, cfg.C, torch.bfloat16),
                      dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
-
-    def fwd(mask=LL.STAGE_ALL):
-        LL.loglin_fwd_chunked_stages(q, k, v, a, lam, cfg.C, mask, out=out, workspace=ws)
+    fwd, sets = rotating_forward(cfg, q, k, v, a, lam, ws)
 
     for _ in range(args.warmup):
         fwd()
@@ -302,7 +324,7 @@ def main() -> int:
                         for kk, vv in m.items()} for n, m in kernels.items()},
         "plan": plan,
     }
-    del q, k, v, a, lam, out, ws
+    del q, k, v, a, lam, ws, sets, fwd
     torch.cuda.empty_cache()
 
     if not args.no_other:
@@ -337,14 +359,11 @@ def bench_fwd_other(name: str, steps: int, warmup: int) -> dict:
     q, k, v = (dev(d[n], torch.bfloat16) for n in ("q", "k", "v"))
     a, lam = dev(d["a"]), dev(d["lam"])
     del d
-    out = torch.empty((cfg.B, cfg.H, cfg.T, cfg.dv), device="cuda")
     ws = torch.empty(max(1, LL.loglin_fwd_workspace_bytes(cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv, cfg.C,
                                                           torch.bfloat16)),
                      dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
-
-    def fwd(mask=LL.STAGE_ALL):
-        LL.loglin_fwd_chunked_stages(q, k, v, a, lam, cfg.C, mask, out=out, workspace=ws)
+    fwd, sets = rotating_forward(cfg, q, k, v, a, lam, ws)
 
     for _ in range(warmup):
         fwd()
@@ -360,7 +379,7 @@ def bench_fwd_other(name: str, steps: int, warmup: int) -> dict:
     tps = cfg.B * cfg.T / (ms / 1e3)
     log(f"{name}: {ms:.3f} ms/step, {tps:.3e} tokens/s; {name_out} {kms:.3f} ms, "
         f"{km['GB/s']:.0f} GB/s")
-    del q, k, v, a, lam, out, ws
+    del q, k, v, a, lam, ws, sets, fwd
     torch.cuda.empty_cache()
     return {"workload": name, "tokens_per_s": tps, "ms_per_step": ms,
             "config": {"B": cfg.B, "H": cfg.H, "T": cfg.T, "dk": cfg.dk, "dv": cfg.dv, "C": cfg.C,
@@ -386,12 +405,17 @@ def bench_decode(steps: int) -> dict:
         live[s, I.live_levels(int(n))] = True
     levels *= torch.from_numpy(live).to("cuda")[:, None, :, None, None]
     st = LL.loglin_state_init(cfg.nseq, cfg.H, cfg.dk, cfg.dv, cfg.Lmax)
-    LL.loglin_state_load(st, pos, levels)
-    del levels
     q, k, v = (torch.from_numpy(d[n]).to("cuda").to(torch.bfloat16) for n in ("q", "k", "v"))
     a, lam = torch.from_numpy(d["a"]).to("cuda"), torch.from_numpy(d["lam"]).to("cuda")
     out = torch.empty((cfg.nseq, cfg.H, cfg.dv), device="cuda")
     stream = torch.cuda.current_stream()
+    # warm-up: the same steps from the same loaded state, which is then
+    # loaded again for the timed steps
+    LL.loglin_state_load(st, pos, levels)
+    for s in range(min(steps, 64)):
+        LL.loglin_decode_step(st, q[s], k[s], v[s], a[s], lam[s], out=out)
+    LL.loglin_state_load(st, pos, levels)
+    del levels
     it = iter(range(steps))
 
     def step():
