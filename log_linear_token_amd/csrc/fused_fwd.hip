@@ -157,19 +157,30 @@ __device__ __forceinline__ void dma4(const void* g, void* lds) {
 
 // The same copy from a uniform base address plus a per-lane 32-bit byte offset
 // (the scalar-base form of the instruction: no 64-bit address arithmetic per
-// lane).
+// lane).  NT marks the data as read for the last time (non-temporal).
+template <bool NT = false>
 __device__ __forceinline__ void dma16o(const void* base, uint32_t off, void* lds) {
     const uint32_t l = (uint32_t)(uintptr_t)lds;
     const uint64_t b = (uint64_t)(uintptr_t)base;
     const uint64_t bu = ((uint64_t)__builtin_amdgcn_readfirstlane((uint32_t)(b >> 32)) << 32) |
                         (uint32_t)__builtin_amdgcn_readfirstlane((uint32_t)b);
-    asm volatile(
-        "s_mov_b32 m0, %0\n\t"
-        "s_nop 0\n\t"
-        "global_load_lds_dwordx4 %1, %2"
-        :
-        : "s"(__builtin_amdgcn_readfirstlane(l)), "v"(off), "s"(bu)
-        : "memory", "m0");
+    if constexpr (NT) {
+        asm volatile(
+            "s_mov_b32 m0, %0\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %1, %2 nt"
+            :
+            : "s"(__builtin_amdgcn_readfirstlane(l)), "v"(off), "s"(bu)
+            : "memory", "m0");
+    } else {
+        asm volatile(
+            "s_mov_b32 m0, %0\n\t"
+            "s_nop 0\n\t"
+            "global_load_lds_dwordx4 %1, %2"
+            :
+            : "s"(__builtin_amdgcn_readfirstlane(l)), "v"(off), "s"(bu)
+            : "memory", "m0");
+    }
 }
 
 // Copy plan of a whole 64-row tile with D bf16 columns: the tile is NI
@@ -201,14 +212,15 @@ struct TileCopy {
         }
         step = (uint32_t)(NWI * RPI * pitch) * 2u;
     }
+    template <bool NT = false>
     __device__ __forceinline__ void issue(const bf16_t* tile, bf16_t* lds, int w) const {
         const char* base = reinterpret_cast<const char*>(tile);
 #pragma unroll
         for (int k = 0; k < PER; ++k) {
             const int u = w + NWI * k;
             if (NI % NWI == 0 || u < NI) {
-                if constexpr (ONE) dma16o(base + (size_t)k * step, off[0], lds + u * 512);
-                else dma16o(base, off[k], lds + u * 512);
+                if constexpr (ONE) dma16o<NT>(base + (size_t)k * step, off[0], lds + u * 512);
+                else dma16o<NT>(base, off[k], lds + u * 512);
             }
         }
     }
@@ -650,22 +662,23 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
         const bool whole = nvalid == TC;
         if (part == 0) {
             if (whole) {
-                cqk.issue(p.q + r * DK, Qd, iw);
-                cqk.issue(p.k + r * DK, Kd, iw);
+                // the forward's last read of q, k, v, lambda and a
+                cqk.template issue<true>(p.q + r * DK, Qd, iw);
+                cqk.template issue<true>(p.k + r * DK, Kd, iw);
             } else {
                 dma_tile<DK, NIW>(p.q + r * DK, DK, 0, nvalid, Qd, iw);
                 dma_tile<DK, NIW>(p.k + r * DK, DK, 0, nvalid, Kd, iw);
             }
             return;
         }
-        if (whole) cv.issue(p.v + r * p.dv, Vd, i1);
+        if (whole) cv.template issue<true>(p.v + r * p.dv, Vd, i1);
         else dma_tile<DVW, NIW1>(p.v + r * p.dv, p.dv, cb, nvalid, Vd, i1);
         // lambda from the last issuing wave down (those hold fewer Q/K/V jobs)
         const int lw = NIW1 - 1 - i1;
         if (whole && p.lam_dma) {
             const int nch = 16 * L;  // 64 rows x L floats
             for (int u = lw; u * 64 < nch; u += NIW1)
-                if (u * 64 + lane < nch) dma16o(p.lam + r * L, 16u * (u * 64 + lane), Ld + u * 256);
+                if (u * 64 + lane < nch) dma16o<true>(p.lam + r * L, 16u * (u * 64 + lane), Ld + u * 256);
         } else {
             const int nel = nvalid * LP;
             for (int u = lw; u * 64 < TC * LP; u += NIW1) {
@@ -680,7 +693,7 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
         }
         if (i1 == 0) {
             if (whole && p.a_dma) {
-                if (lane < TC / 4) dma16o(p.a + r, 16u * lane, ad);
+                if (lane < TC / 4) dma16o<true>(p.a + r, 16u * lane, ad);
             } else if (lane < nvalid) {
                 dma4(p.a + r + lane, ad);
             } else {
