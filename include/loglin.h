@@ -195,6 +195,34 @@ LOGLIN_API loglin_status loglin_decode_step(loglin_state* st, const void* q, con
                                  loglin_dtype in_dtype, void* stream);
 
 /*
+ * Prefill -> decode hand-over ("Log-linear attention, and what a logarithm
+ * buys", section 2, with the scalar gate of sections 1 and 3): the Fenwick
+ * level states after the T tokens 0..T-1 of each (batch, head) sequence, i.e.
+ * the state a decode step at position T reads.  Level 0 holds the last
+ * token's k v^T; level p+1, for each set bit p of T-1, the bucket of 2^p
+ * tokens the greedy (oldest, largest first) decomposition of the prefix
+ * assigns that bit; every token decayed to position T-1:
+ *     S^(l) = sum over s in bucket l of exp(A_{T-1} - A_s) k_s v_s^T.
+ * The result loads into a decode state with loglin_state_load(pos = T).
+ *
+ *   k          [B, H, T, dk]  in_dtype
+ *   v          [B, H, T, dv]  in_dtype
+ *   log_decay  [B, H, T]      fp32
+ *   states     [B, H, Lmax, dk, dv] fp32, written; slots that are not live
+ *              are zero.  16-byte aligned.
+ *   Lmax       1..48 and at least bit_length(T-1) + 1 (else LOGLIN_ECAPACITY)
+ *   workspace  device buffer of at least loglin_prefill_workspace_bytes(...)
+ *              bytes, 256-byte aligned (NULL allowed when that is 0)
+ * T = 0 writes zero states; B or H = 0 is a no-op.  Accumulates in fp32 for
+ * either input type.  Asynchronous on `stream`.
+ */
+LOGLIN_API size_t loglin_prefill_workspace_bytes(int B, int H, int T, int dk, int dv, int Lmax);
+LOGLIN_API loglin_status loglin_prefill_states(const void* k, const void* v, const float* log_decay,
+                                               float* states, int B, int H, int T, int dk, int dv,
+                                               int Lmax, loglin_dtype in_dtype, void* workspace,
+                                               size_t workspace_bytes, void* stream);
+
+/*
  * Level map used by the kernels, for checking: out[t * T + s] = level(t, s)
  * for s <= t and -1 for s > t.  out is [T, T] device int8; 1 <= T <= 16384.
  */

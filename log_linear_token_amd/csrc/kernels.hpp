@@ -85,6 +85,19 @@ struct DecodeParams {
 };
 
 hipError_t launch_decode_step(const DecodeParams& p, bool bf16, hipStream_t stream);
+
+// Fenwick level states after the T tokens of a prefill (the state a decode
+// step at position T reads)
+struct PrefillParams {
+    const void* k;            // [BH][T][dk]
+    const void* v;            // [BH][T][dv]
+    const float* a;           // [BH][T]
+    float* states;            // [BH][Lmax][dk][dv]
+    float* ws;                // [BH][njobs][dk][dv] partial sums
+    int BH, T, dk, dv, Lmax, njobs;
+};
+int prefill_jobs(int T);      // jobs the prefix of T tokens is cut into
+hipError_t launch_prefill_states(const PrefillParams& p, bool bf16, hipStream_t stream);
 // copy states to dst, zeroing every slot that is not live at the current position
 hipError_t launch_state_export(const DecodeParams& p, float* dst, hipStream_t stream);
 hipError_t launch_level_map(int T, int8_t* out, hipStream_t stream);

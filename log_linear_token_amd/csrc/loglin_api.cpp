@@ -530,6 +530,71 @@ loglin_status loglin_decode_step(loglin_state* st, const void* q, const void* k,
     return ok();
 }
 
+// ---------------------------------------------------------------------------
+// prefill -> decode hand-over
+
+namespace {
+loglin_status check_prefill(int B, int H, int T, int dk, int dv, int Lmax) {
+    if (B < 0 || H < 0 || T < 0)
+        return fail(LOGLIN_EINVAL, "B, H, T must be >= 0 (got %d, %d, %d)", B, H, T);
+    if (!supported_dim(dk) || !supported_dim(dv))
+        return fail(LOGLIN_EUNSUPPORTED, "head dims dk=%d dv=%d must be in {16,32,64,128}", dk, dv);
+    if (Lmax < 1 || Lmax > 48) return fail(LOGLIN_EINVAL, "Lmax=%d must be in [1, 48]", Lmax);
+    if (T > 0 && levels_needed(T) > Lmax)
+        return fail(LOGLIN_ECAPACITY, "T=%d needs %d levels, Lmax=%d", T, levels_needed(T), Lmax);
+    if ((long)T > ((long)1 << 30)) return fail(LOGLIN_EUNSUPPORTED, "T=%d too long", T);
+    return LOGLIN_OK;
+}
+size_t prefill_ws_bytes(long BH, int T, int dk, int dv) {
+    return align_up((size_t)BH * prefill_jobs(T) * dk * dv * sizeof(float));
+}
+}  // namespace
+
+size_t loglin_prefill_workspace_bytes(int B, int H, int T, int dk, int dv, int Lmax) {
+    if (check_prefill(B, H, T, dk, dv, Lmax) != LOGLIN_OK) return (size_t)-1;
+    return prefill_ws_bytes((long)B * H, T, dk, dv);
+}
+
+loglin_status loglin_prefill_states(const void* k, const void* v, const float* log_decay,
+                                    float* states, int B, int H, int T, int dk, int dv, int Lmax,
+                                    loglin_dtype in_dtype, void* workspace, size_t workspace_bytes,
+                                    void* stream) {
+    loglin_status s = check_prefill(B, H, T, dk, dv, Lmax);
+    if (s != LOGLIN_OK) return s;
+    if (in_dtype != LOGLIN_F32 && in_dtype != LOGLIN_BF16)
+        return fail(LOGLIN_EINVAL, "in_dtype %d is neither LOGLIN_F32 nor LOGLIN_BF16", (int)in_dtype);
+    const long BH = (long)B * H;
+    if (BH == 0) return ok();
+    if (!states) return fail(LOGLIN_EINVAL, "null states pointer");
+    if (T > 0 && (!k || !v || !log_decay)) return fail(LOGLIN_EINVAL, "null tensor pointer");
+    if (reinterpret_cast<uintptr_t>(states) % 16)
+        return fail(LOGLIN_EINVAL, "states must be 16-byte aligned");
+    const size_t need = prefill_ws_bytes(BH, T, dk, dv);
+    if (need > 0) {
+        if (!workspace || workspace_bytes < need)
+            return fail(LOGLIN_EINVAL, "workspace of %zu bytes needed, got %zu%s", need,
+                        workspace_bytes, workspace ? "" : " (NULL)");
+        if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
+            return fail(LOGLIN_EINVAL, "workspace must be %zu-byte aligned", kAlign);
+    }
+    if ((long)BH * Lmax > 0x7fffffffL / 64) return fail(LOGLIN_EUNSUPPORTED, "B*H*Lmax too large");
+    PrefillParams p{};
+    p.k = k;
+    p.v = v;
+    p.a = log_decay;
+    p.states = states;
+    p.ws = static_cast<float*>(workspace);
+    p.BH = (int)BH;
+    p.T = T;
+    p.dk = dk;
+    p.dv = dv;
+    p.Lmax = Lmax;
+    p.njobs = prefill_jobs(T);
+    hipError_t e = launch_prefill_states(p, in_dtype == LOGLIN_BF16, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "loglin_prefill_states launch");
+    return ok();
+}
+
 loglin_status loglin_debug_level_map(int T, int8_t* out, void* stream) {
     if (T < 1 || T > 16384) return fail(LOGLIN_EINVAL, "T=%d must be in [1, 16384]", T);
     if (!out) return fail(LOGLIN_EINVAL, "null output");

@@ -1,0 +1,216 @@
+// Fenwick level states after a prefill, for continuing with decode steps.
+//
+// "Log-linear attention, and what a logarithm buys", section 2: after the T
+// tokens 0..T-1 the state a decode step at position T reads is, for level 0,
+// the last token's k v^T, and for each set bit p of T - 1 the bucket of 2^p
+// tokens that the greedy (oldest, largest first) decomposition of the prefix
+// gives that bit, at level p + 1.  With the scalar gate (sections 1 and 3)
+// every token is decayed to position T - 1:
+//     S^(l) = sum over s in bucket l of exp(A_{T-1} - A_s) k_s v_s^T.
+// Token s of the prefix lies in the bucket of level floor(log2((T-1) xor s)) + 1.
+//
+// The prefix is cut into jobs: whole 1024-token pieces of the buckets of 1024
+// tokens or more (every such bucket is a whole number of aligned pieces), one
+// job per smaller bucket, and one for level 0.  k_prefill_part computes each
+// job's decayed sum (fp32, any input type) into the workspace; k_prefill_sum
+// adds the jobs of each level into the state layout the decode state loads
+// ([B, H, Lmax, dk, dv], slots that are not live zero).
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace loglin {
+
+namespace {
+
+constexpr int kThr = 256;
+constexpr int kTile = 64;
+constexpr int kJobTokens = 1024;
+
+struct Job {
+    int level, s0, s1;
+};
+
+// job j of the prefix of T tokens (n = T - 1 >= 0); njobs = n / 1024 +
+// popcount(n % 1024) + 1
+__device__ __forceinline__ Job prefill_job(int n, int j) {
+    const int nfull = n / kJobTokens;
+    if (j < nfull) {
+        const int s0 = j * kJobTokens;
+        return Job{32 - __clz(n ^ s0), s0, s0 + kJobTokens};
+    }
+    int jj = j - nfull;
+    const int low = n % kJobTokens;
+    for (int p = 9; p >= 0; --p) {
+        if ((low >> p) & 1) {
+            if (jj == 0) {
+                const int s0 = (n >> (p + 1)) << (p + 1);
+                return Job{p + 1, s0, s0 + (1 << p)};
+            }
+            --jj;
+        }
+    }
+    return Job{0, n, n + 1};
+}
+
+template <typename E>
+__global__ __launch_bounds__(kThr) void k_prefill_part(PrefillParams p) {
+    __shared__ float sk[kTile][129];  // K tile, fp32 (odd pitch: rows on distinct banks)
+    __shared__ float4 sv[kTile][16];  // V tile, this block's columns (<= 64)
+    __shared__ float se[kTile];       // per-token weights exp(A_{T-1} - A_s)
+    __shared__ float sa[kTile];
+    __shared__ float sred[kThr / 64];
+    __shared__ float carry_s;
+
+    const int dk = p.dk, dv = p.dv;
+    const int dvw = dv < 64 ? dv : 64;
+    const int ncb = dv / dvw;
+    int blk = blockIdx.x;
+    const int cb = blk % ncb;
+    blk /= ncb;
+    const int job = blk % p.njobs;
+    const int bh = blk / p.njobs;
+    const int tid = threadIdx.x;
+    const int n = p.T - 1;
+    const Job jb = prefill_job(n, job);
+
+    const float* a = p.a + (size_t)bh * p.T;
+    const E* k = static_cast<const E*>(p.k) + (size_t)bh * p.T * dk;
+    const E* v = static_cast<const E*>(p.v) + (size_t)bh * p.T * dv + cb * dvw;
+
+    // decay from the end of the job to position T - 1: sum of a over (s1 - 1, T - 1]
+    float part = 0.f;
+    for (int r = jb.s1 + tid; r < p.T; r += kThr) part += a[r];
+    for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o);
+    if ((tid & 63) == 0) sred[tid >> 6] = part;
+    __syncthreads();
+    if (tid == 0) {
+        float c = 0.f;
+        for (int w = 0; w < kThr / 64; ++w) c += sred[w];
+        carry_s = c;
+    }
+
+    // output ownership: 4 consecutive columns and rows rg + nrg * i
+    const int q4 = dvw / 4;          // column quads of the block
+    const int cq = tid % q4;
+    const int rg = tid / q4;
+    const int nrg = kThr / q4;       // row groups
+    const int nrow = (dk + nrg - 1) / nrg;
+    float4 acc[8];                   // nrow <= 8 (dk <= 128, dvw >= 16 -> nrg <= 64)
+#pragma unroll
+    for (int i = 0; i < 8; ++i) acc[i] = make_float4(0.f, 0.f, 0.f, 0.f);
+
+    const int tfirst = jb.s0 / kTile, tlast = (jb.s1 - 1) / kTile;
+    for (int tb = tlast; tb >= tfirst; --tb) {
+        const int base = tb * kTile;
+        __syncthreads();  // previous tile consumed; carry_s written
+        if (tid < kTile) {
+            const int s = base + tid;
+            sa[tid] = (s >= jb.s0 && s < jb.s1) ? a[s] : 0.f;
+        }
+        for (int x = tid; x < kTile * dk; x += kThr) {
+            const int s = x / dk, c = x % dk;
+            const int g = base + s;
+            sk[s][c] = g < p.T ? to_f32(k[(size_t)g * dk + c]) : 0.f;
+        }
+        for (int x = tid; x < kTile * q4; x += kThr) {
+            const int s = x / q4, c4 = x % q4;
+            const int g = base + s;
+            float4 y = make_float4(0.f, 0.f, 0.f, 0.f);
+            if (g < p.T) {
+                const E* vr = v + (size_t)g * dv + 4 * c4;
+                y = make_float4(to_f32(vr[0]), to_f32(vr[1]), to_f32(vr[2]), to_f32(vr[3]));
+            }
+            sv[s][c4] = y;
+        }
+        __syncthreads();
+        if (tid < kTile) {
+            // tokens after s inside this tile and the job, then everything after it
+            float suf = 0.f;
+            for (int r = tid + 1; r < kTile; ++r) suf += sa[r];
+            const int s = base + tid;
+            se[tid] = (s >= jb.s0 && s < jb.s1) ? __expf(suf + carry_s) : 0.f;
+        }
+        __syncthreads();
+        if (tid == 0) {
+            float t = 0.f;
+            for (int r = 0; r < kTile; ++r) t += sa[r];
+            carry_s += t;
+        }
+        for (int s = 0; s < kTile; ++s) {
+            const float e = se[s];
+            if (e == 0.f) continue;  // uniform: outside the job
+            const float4 vv = sv[s][cq];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                if (i < nrow) {
+                    const int r = rg + nrg * i;
+                    if (r < dk) {
+                        const float w = e * sk[s][r];
+                        acc[i].x += w * vv.x;
+                        acc[i].y += w * vv.y;
+                        acc[i].z += w * vv.z;
+                        acc[i].w += w * vv.w;
+                    }
+                }
+            }
+        }
+    }
+    // partial [bh][job][dk][dv]
+    float* dst = p.ws + ((size_t)bh * p.njobs + job) * dk * dv + cb * dvw + 4 * cq;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int r = rg + nrg * i;
+        if (i < nrow && r < dk) *reinterpret_cast<float4*>(dst + (size_t)r * dv) = acc[i];
+    }
+}
+
+__global__ __launch_bounds__(kThr) void k_prefill_sum(PrefillParams p) {
+    // block: (bh, level, element chunk of kThr float4)
+    const size_t n4 = (size_t)p.dk * p.dv / 4;
+    const int nchunk = (int)((n4 + kThr - 1) / kThr);
+    int blk = blockIdx.x;
+    const int chunk = blk % nchunk;
+    blk /= nchunk;
+    const int level = blk % p.Lmax;
+    const int bh = blk / p.Lmax;
+    const size_t e = (size_t)chunk * kThr + threadIdx.x;
+    if (e >= n4) return;
+    const int n = p.T - 1;
+    float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
+    if (n >= 0) {
+        const float4* ws = reinterpret_cast<const float4*>(p.ws) + (size_t)bh * p.njobs * n4;
+        for (int j = 0; j < p.njobs; ++j) {
+            if (prefill_job(n, j).level != level) continue;  // uniform over the block
+            const float4 x = ws[(size_t)j * n4 + e];
+            s.x += x.x; s.y += x.y; s.z += x.z; s.w += x.w;
+        }
+    }
+    reinterpret_cast<float4*>(p.states)[((size_t)bh * p.Lmax + level) * n4 + e] = s;
+}
+
+}  // namespace
+
+int prefill_jobs(int T) {
+    if (T <= 0) return 0;
+    const int n = T - 1;
+    return n / kJobTokens + __builtin_popcount((unsigned)(n % kJobTokens)) + 1;
+}
+
+hipError_t launch_prefill_states(const PrefillParams& p, bool bf16, hipStream_t stream) {
+    const int dvw = p.dv < 64 ? p.dv : 64;
+    if (p.njobs > 0) {
+        const unsigned nb = (unsigned)((long)p.BH * p.njobs * (p.dv / dvw));
+        if (bf16)
+            hipLaunchKernelGGL(k_prefill_part<bf16_t>, dim3(nb), dim3(kThr), 0, stream, p);
+        else
+            hipLaunchKernelGGL(k_prefill_part<float>, dim3(nb), dim3(kThr), 0, stream, p);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    const size_t n4 = (size_t)p.dk * p.dv / 4;
+    const unsigned nchunk = (unsigned)((n4 + kThr - 1) / kThr);
+    hipLaunchKernelGGL(k_prefill_sum, dim3((unsigned)p.BH * p.Lmax * nchunk), dim3(kThr), 0, stream, p);
+    return hipGetLastError();
+}
+
+}  // namespace loglin

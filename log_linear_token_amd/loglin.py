@@ -77,6 +77,10 @@ def _load():
     lib.loglin_state_export.restype = i
     lib.loglin_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, vp]
     lib.loglin_decode_step.restype = i
+    lib.loglin_prefill_workspace_bytes.argtypes = [i, i, i, i, i, i]
+    lib.loglin_prefill_workspace_bytes.restype = sz
+    lib.loglin_prefill_states.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, vp, sz, vp]
+    lib.loglin_prefill_states.restype = i
     lib.loglin_debug_level_map.argtypes = [i, vp, vp]
     lib.loglin_debug_level_map.restype = i
     lib.loglin_last_error.argtypes = []
@@ -181,6 +185,39 @@ def loglin_fwd_chunked_stages(q, k, v, log_decay, lam, C: int, stage_mask: int, 
     nws = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_load().loglin_fwd_chunked_stages(pq, pk, pv, pa, pl, po, B, H, T, dk, dv, L, C,
                                              _DTYPES[q.dtype], pw, nws, stage_mask, _stream(q)))
+    return out
+
+
+# ---------------------------------------------------------------- prefill -> decode
+
+def loglin_prefill_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, Lmax: int) -> int:
+    n = _load().loglin_prefill_workspace_bytes(B, H, T, dk, dv, Lmax)
+    if n == ctypes.c_size_t(-1).value:
+        raise LoglinError(LOGLIN_EINVAL, loglin_last_error())
+    return n
+
+
+def loglin_prefill_states(k, v, log_decay, Lmax: int, out=None, workspace=None):
+    """Fenwick level states after the T tokens of each sequence, in the layout
+    loglin_state_load takes: k [B,H,T,dk], v [B,H,T,dv] (float32 or
+    bfloat16), log_decay [B,H,T] float32.  Returns [B,H,Lmax,dk,dv] float32."""
+    if k.dtype not in _DTYPES:
+        raise ValueError(f"k must be float32 or bfloat16 (got {k.dtype})")
+    B, H, T, dk = k.shape
+    dv = v.shape[-1]
+    pk = _dev(k, "k", k.dtype)
+    pv = _dev(v, "v", k.dtype, (B, H, T, dv))
+    pa = _dev(log_decay, "log_decay", torch.float32, (B, H, T))
+    if out is None:
+        out = torch.empty((B, H, Lmax, dk, dv), dtype=torch.float32, device=k.device)
+    po = _dev(out, "out", torch.float32, (B, H, Lmax, dk, dv))
+    need = loglin_prefill_workspace_bytes(B, H, T, dk, dv, Lmax)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=k.device)
+    pw = _dev(workspace, "workspace") if workspace is not None else None
+    nws = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_load().loglin_prefill_states(pk, pv, pa, po, B, H, T, dk, dv, Lmax, _DTYPES[k.dtype],
+                                         pw, nws, _stream(k)))
     return out
 
 

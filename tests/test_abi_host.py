@@ -35,6 +35,9 @@ def lib():
     lib.loglin_state_export.argtypes = [vp, vp, vp, vp]
     lib.loglin_decode_step.argtypes = [vp] * 7 + [i, vp]
     lib.loglin_debug_level_map.argtypes = [i, vp, vp]
+    lib.loglin_prefill_workspace_bytes.argtypes = [i] * 6
+    lib.loglin_prefill_workspace_bytes.restype = sz
+    lib.loglin_prefill_states.argtypes = [vp] * 4 + [i] * 7 + [vp, sz, vp]
     lib.loglin_last_error.restype = ctypes.c_char_p
     lib.loglin_status_string.restype = ctypes.c_char_p
     return lib
@@ -44,7 +47,8 @@ def test_header_declares_the_entry_points():
     names = _declared()
     for n in ["loglin_fwd_chunked", "loglin_fwd_workspace_bytes", "loglin_decode_step",
               "loglin_state_init", "loglin_state_free", "loglin_state_load",
-              "loglin_state_export", "loglin_debug_level_map", "loglin_last_error"]:
+              "loglin_state_export", "loglin_debug_level_map", "loglin_last_error",
+              "loglin_prefill_states", "loglin_prefill_workspace_bytes"]:
         assert n in names
 
 
@@ -185,3 +189,44 @@ def test_level_map_validation(lib):
 def test_status_strings(lib):
     assert lib.loglin_status_string(0) == b"LOGLIN_OK"
     assert lib.loglin_status_string(4) == b"LOGLIN_ECAPACITY"
+
+
+# ---------------------------------------------------------------- prefill -> decode
+
+def _prefill_jobs(T):
+    """Pieces of the prefix: whole 1024-token pieces of the large buckets, one
+    per smaller bucket (set bits of (T-1) mod 1024), one for level 0."""
+    if T <= 0:
+        return 0
+    n = T - 1
+    return n // 1024 + bin(n % 1024).count("1") + 1
+
+
+@pytest.mark.parametrize("B,H,T,dk,dv,Lmax", [(1, 1, 1, 16, 16, 1), (2, 3, 64, 64, 32, 8),
+                                              (4, 16, 8192, 128, 64, 15), (1, 16, 65536, 128, 128, 18),
+                                              (1, 1, 0, 16, 16, 4)])
+def test_prefill_workspace_bytes(lib, B, H, T, dk, dv, Lmax):
+    want = B * H * _prefill_jobs(T) * dk * dv * 4
+    want = (want + 255) // 256 * 256
+    assert lib.loglin_prefill_workspace_bytes(B, H, T, dk, dv, Lmax) == want
+
+
+def _prefill(lib, B=1, H=1, T=64, dk=16, dv=16, Lmax=8, dtype=1, ws=FAKE, nws=1 << 30, ptrs=None):
+    p = [FAKE] * 4 if ptrs is None else ptrs
+    return lib.loglin_prefill_states(*p, B, H, T, dk, dv, Lmax, dtype, ws, nws, None)
+
+
+def test_prefill_validation(lib):
+    # T = 1000 needs bit_length(999) + 1 = 11 levels
+    assert _prefill(lib, T=1000, Lmax=10) == ECAPACITY
+    assert lib.loglin_prefill_workspace_bytes(1, 1, 1000, 16, 16, 10) == ctypes.c_size_t(-1).value
+    assert _prefill(lib, dk=48) == EUNSUPPORTED
+    assert _prefill(lib, Lmax=0) == EINVAL
+    assert _prefill(lib, Lmax=49) == EINVAL
+    assert _prefill(lib, dtype=7) == EINVAL
+    assert _prefill(lib, ptrs=[FAKE, FAKE, FAKE, None]) == EINVAL
+    assert _prefill(lib, ptrs=[None, FAKE, FAKE, FAKE]) == EINVAL
+    assert _prefill(lib, ptrs=[FAKE, FAKE, FAKE, FAKE + 4]) == EINVAL  # states misaligned
+    assert _prefill(lib, nws=16) == EINVAL                             # workspace too small
+    assert _prefill(lib, ws=FAKE + 64) == EINVAL                       # workspace misaligned
+    assert _prefill(lib, B=0) == 0                                      # no-op
