@@ -324,6 +324,7 @@ def main() -> int:
                         for kk, vv in m.items()} for n, m in kernels.items()},
         "plan": plan,
     }
+    result["prefill_states"] = bench_prefill(cfg, sets, stream, args.steps)
     del q, k, v, a, lam, ws, sets, fwd
     torch.cuda.empty_cache()
 
@@ -388,6 +389,33 @@ def bench_fwd_other(name: str, steps: int, warmup: int) -> dict:
             "roofline": {"kernel": name_out, "bound": "hbm", "achieved": round(km["GB/s"], 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(km["GB/s"] / HBM_PEAK_GBS, 4), "mfma": mfma_entry(km)}}
+
+
+def bench_prefill(cfg, sets, stream, steps: int) -> dict:
+    """The prefill -> decode hand-over on the 8K workload: the Fenwick level
+    states after all T tokens.  Algorithmic bytes: k, v (bf16) and a read
+    once, the live level states written once."""
+    B, H, T, dk, dv = cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv
+    Lmax = (T - 1).bit_length() + 1
+    out = torch.empty((B, H, Lmax, dk, dv), device="cuda")
+    ws = torch.empty(max(1, LL.loglin_prefill_workspace_bytes(B, H, T, dk, dv, Lmax)),
+                     dtype=torch.uint8, device="cuda")
+    state = {"i": 0}
+
+    def run():
+        _, kk, vv, aa, _, _ = sets[state["i"] % len(sets)]
+        state["i"] += 1
+        LL.loglin_prefill_states(kk, vv, aa, Lmax, out=out, workspace=ws)
+
+    for _ in range(5):
+        run()
+    ms = timed(run, max(5, steps // 4), stream)
+    live = 1 + bin(T - 1).count("1")
+    byts = B * H * (T * (2 * dk + 2 * dv + 4) + live * dk * dv * 4)
+    gbs = byts / (ms / 1e3) / 1e9
+    log(f"prefill states: {ms:.3f} ms, {gbs:.0f} GB/s")
+    return {"ms": ms, "alg_bytes": byts, "GB/s": round(gbs, 1),
+            "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
 
 
 def bench_decode(steps: int) -> dict:

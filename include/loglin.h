@@ -209,12 +209,14 @@ LOGLIN_API loglin_status loglin_decode_step(loglin_state* st, const void* q, con
  *   v          [B, H, T, dv]  in_dtype
  *   log_decay  [B, H, T]      fp32
  *   states     [B, H, Lmax, dk, dv] fp32, written; slots that are not live
- *              are zero.  16-byte aligned.
+ *              are zero.  k, v and states 16-byte aligned.
  *   Lmax       1..48 and at least bit_length(T-1) + 1 (else LOGLIN_ECAPACITY)
  *   workspace  device buffer of at least loglin_prefill_workspace_bytes(...)
  *              bytes, 256-byte aligned (NULL allowed when that is 0)
- * T = 0 writes zero states; B or H = 0 is a no-op.  Accumulates in fp32 for
- * either input type.  Asynchronous on `stream`.
+ * T = 0 writes zero states; B or H = 0 is a no-op.  Accumulates in fp32:
+ * bf16 inputs on the matrix cores (k v^T products of bf16 operands, the
+ * per-token decay rounded to bf16 with v), fp32 inputs with fp32 vector FMAs.
+ * Asynchronous on `stream`.
  */
 LOGLIN_API size_t loglin_prefill_workspace_bytes(int B, int H, int T, int dk, int dv, int Lmax);
 LOGLIN_API loglin_status loglin_prefill_states(const void* k, const void* v, const float* log_decay,

@@ -97,6 +97,38 @@ struct PrefillParams {
     int BH, T, dk, dv, Lmax, njobs;
 };
 int prefill_jobs(int T);      // jobs the prefix of T tokens is cut into
+
+// Job j of the prefix of T tokens (n = T - 1 >= 0): the prefix is cut into
+// whole 1024-token pieces of the buckets of 1024 tokens or more (each such
+// bucket is a whole number of aligned pieces), one job per smaller bucket
+// (the set bits of n mod 1024, largest first) and a last one for level 0 (the
+// token n itself).  Token s < n lies in the bucket of level
+// floor(log2(n xor s)) + 1.
+constexpr int kPrefillJobTokens = 1024;
+struct PrefillJob {
+    int level, s0, s1;  // tokens [s0, s1) of level `level`
+};
+__device__ __forceinline__ PrefillJob prefill_job(int n, int j) {
+    const int nfull = n / kPrefillJobTokens;
+    if (j < nfull) {
+        const int s0 = j * kPrefillJobTokens;
+        return PrefillJob{32 - __clz(n ^ s0), s0, s0 + kPrefillJobTokens};
+    }
+    int jj = j - nfull;
+    const int low = n % kPrefillJobTokens;
+    for (int p = 9; p >= 0; --p) {
+        if ((low >> p) & 1) {
+            if (jj == 0) {
+                const int s0 = (n >> (p + 1)) << (p + 1);
+                return PrefillJob{p + 1, s0, s0 + (1 << p)};
+            }
+            --jj;
+        }
+    }
+    return PrefillJob{0, n, n + 1};
+}
+// bf16 inputs: each job's decayed sum on the matrix cores (fused_fwd.hip)
+hipError_t launch_prefill_jobs_bf16(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_prefill_states(const PrefillParams& p, bool bf16, hipStream_t stream);
 // copy states to dst, zeroing every slot that is not live at the current position
 hipError_t launch_state_export(const DecodeParams& p, float* dst, hipStream_t stream);

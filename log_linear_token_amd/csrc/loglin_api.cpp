@@ -567,8 +567,9 @@ loglin_status loglin_prefill_states(const void* k, const void* v, const float* l
     if (BH == 0) return ok();
     if (!states) return fail(LOGLIN_EINVAL, "null states pointer");
     if (T > 0 && (!k || !v || !log_decay)) return fail(LOGLIN_EINVAL, "null tensor pointer");
-    if (reinterpret_cast<uintptr_t>(states) % 16)
-        return fail(LOGLIN_EINVAL, "states must be 16-byte aligned");
+    if (reinterpret_cast<uintptr_t>(states) % 16 || reinterpret_cast<uintptr_t>(k) % 16 ||
+        reinterpret_cast<uintptr_t>(v) % 16)
+        return fail(LOGLIN_EINVAL, "k, v and states must be 16-byte aligned");
     const size_t need = prefill_ws_bytes(BH, T, dk, dv);
     if (need > 0) {
         if (!workspace || workspace_bytes < need)

@@ -11,8 +11,10 @@
 //
 // The prefix is cut into jobs: whole 1024-token pieces of the buckets of 1024
 // tokens or more (every such bucket is a whole number of aligned pieces), one
-// job per smaller bucket, and one for level 0.  k_prefill_part computes each
-// job's decayed sum (fp32, any input type) into the workspace; k_prefill_sum
+// job per smaller bucket, and one for level 0.  Each job's decayed sum goes to
+// the workspace: for bf16 inputs on the matrix cores (k_prefill_job in
+// fused_fwd.hip, which shares the forward's tile machinery), for fp32 inputs
+// by k_prefill_part below (fp32 vector FMAs); k_prefill_sum
 // adds the jobs of each level into the state layout the decode state loads
 // ([B, H, Lmax, dk, dv], slots that are not live zero).
 #include "common.hpp"
@@ -24,33 +26,6 @@ namespace {
 
 constexpr int kThr = 256;
 constexpr int kTile = 64;
-constexpr int kJobTokens = 1024;
-
-struct Job {
-    int level, s0, s1;
-};
-
-// job j of the prefix of T tokens (n = T - 1 >= 0); njobs = n / 1024 +
-// popcount(n % 1024) + 1
-__device__ __forceinline__ Job prefill_job(int n, int j) {
-    const int nfull = n / kJobTokens;
-    if (j < nfull) {
-        const int s0 = j * kJobTokens;
-        return Job{32 - __clz(n ^ s0), s0, s0 + kJobTokens};
-    }
-    int jj = j - nfull;
-    const int low = n % kJobTokens;
-    for (int p = 9; p >= 0; --p) {
-        if ((low >> p) & 1) {
-            if (jj == 0) {
-                const int s0 = (n >> (p + 1)) << (p + 1);
-                return Job{p + 1, s0, s0 + (1 << p)};
-            }
-            --jj;
-        }
-    }
-    return Job{0, n, n + 1};
-}
 
 template <typename E>
 __global__ __launch_bounds__(kThr) void k_prefill_part(PrefillParams p) {
@@ -71,7 +46,7 @@ __global__ __launch_bounds__(kThr) void k_prefill_part(PrefillParams p) {
     const int bh = blk / p.njobs;
     const int tid = threadIdx.x;
     const int n = p.T - 1;
-    const Job jb = prefill_job(n, job);
+    const PrefillJob jb = prefill_job(n, job);
 
     const float* a = p.a + (size_t)bh * p.T;
     const E* k = static_cast<const E*>(p.k) + (size_t)bh * p.T * dk;
@@ -193,18 +168,20 @@ __global__ __launch_bounds__(kThr) void k_prefill_sum(PrefillParams p) {
 int prefill_jobs(int T) {
     if (T <= 0) return 0;
     const int n = T - 1;
-    return n / kJobTokens + __builtin_popcount((unsigned)(n % kJobTokens)) + 1;
+    return n / kPrefillJobTokens + __builtin_popcount((unsigned)(n % kPrefillJobTokens)) + 1;
 }
 
 hipError_t launch_prefill_states(const PrefillParams& p, bool bf16, hipStream_t stream) {
     const int dvw = p.dv < 64 ? p.dv : 64;
     if (p.njobs > 0) {
-        const unsigned nb = (unsigned)((long)p.BH * p.njobs * (p.dv / dvw));
-        if (bf16)
-            hipLaunchKernelGGL(k_prefill_part<bf16_t>, dim3(nb), dim3(kThr), 0, stream, p);
-        else
+        hipError_t e;
+        if (bf16) {
+            e = launch_prefill_jobs_bf16(p, stream);
+        } else {
+            const unsigned nb = (unsigned)((long)p.BH * p.njobs * (p.dv / dvw));
             hipLaunchKernelGGL(k_prefill_part<float>, dim3(nb), dim3(kThr), 0, stream, p);
-        hipError_t e = hipGetLastError();
+            e = hipGetLastError();
+        }
         if (e != hipSuccess) return e;
     }
     const size_t n4 = (size_t)p.dk * p.dv / 4;
