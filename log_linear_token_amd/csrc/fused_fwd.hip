@@ -552,8 +552,9 @@ __global__ __launch_bounds__(NW * 64) void k_seg_state(FusedParams p) {
 // Prefill states (bf16 inputs): one block per (bh, job, column block) sums
 // exp(A_{s1-1} - A_s) k_s v_s^T over the job's tokens [s0, s1) tile by tile
 // (the forward's tile state, with the tokens outside the job masked), decays
-// the sum to position T - 1 and writes it, [d_k][d_v], to the job's slot of
-// the workspace.  The jobs are described with PrefillJob (kernels.hpp).
+// the sum to position T - 1 and writes it, [d_k][d_v], to the state of its
+// level (a level of one job) or to the job's slot of the workspace.  The jobs
+// are described with PrefillJob (kernels.hpp).
 
 // Tile decay restricted to the tokens [lo, hi) of the tile: the others get
 // a = 0 (no decay) and e = 0 (no contribution).
@@ -645,7 +646,10 @@ __global__ __launch_bounds__(NW * 64) void k_prefill_job(PrefillParams p) {
 #pragma unroll
     for (int w = 0; w < NW; ++w) carry += sred[w];
     const float fin = __expf(carry);
-    float* dst = p.ws + ((size_t)bh * p.njobs + job) * DK * p.dv + cb + wave * 16 + m16;
+    float* dst = (prefill_single(jb.level)
+                      ? p.states + ((size_t)bh * p.Lmax + jb.level) * DK * p.dv
+                      : p.ws + ((size_t)bh * p.njobs + job) * DK * p.dv) +
+                 cb + wave * 16 + m16;
 #pragma unroll
     for (int kt = 0; kt < NDT; ++kt) {
         // row of u[kt] (see tile_state): 32 (kt / 2) + 8g + 4 (kt % 2), or 4g for d_k = 16

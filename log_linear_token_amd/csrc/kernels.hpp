@@ -127,6 +127,11 @@ __device__ __forceinline__ PrefillJob prefill_job(int n, int j) {
     }
     return PrefillJob{0, n, n + 1};
 }
+// A level whose bucket is at most one job long is written by its job
+// directly; the pieces of longer buckets go to the workspace and are summed.
+__device__ __forceinline__ bool prefill_single(int level) {
+    return level == 0 || (1 << (level - 1)) <= kPrefillJobTokens;
+}
 // bf16 inputs: each job's decayed sum on the matrix cores (fused_fwd.hip)
 hipError_t launch_prefill_jobs_bf16(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_prefill_states(const PrefillParams& p, bool bf16, hipStream_t stream);

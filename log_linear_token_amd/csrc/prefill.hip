@@ -14,9 +14,10 @@
 // job per smaller bucket, and one for level 0.  Each job's decayed sum goes to
 // the workspace: for bf16 inputs on the matrix cores (k_prefill_job in
 // fused_fwd.hip, which shares the forward's tile machinery), for fp32 inputs
-// by k_prefill_part below (fp32 vector FMAs); k_prefill_sum
-// adds the jobs of each level into the state layout the decode state loads
-// ([B, H, Lmax, dk, dv], slots that are not live zero).
+// by k_prefill_part below (fp32 vector FMAs).  A level of one job is written
+// to the state layout the decode state loads ([B, H, Lmax, dk, dv]) by its job;
+// k_prefill_sum adds the pieces of the longer buckets and zeroes the slots
+// that are not live.
 #include "common.hpp"
 #include "kernels.hpp"
 
@@ -130,8 +131,10 @@ __global__ __launch_bounds__(kThr) void k_prefill_part(PrefillParams p) {
             }
         }
     }
-    // partial [bh][job][dk][dv]
-    float* dst = p.ws + ((size_t)bh * p.njobs + job) * dk * dv + cb * dvw + 4 * cq;
+    // the level's state, or the partial [bh][job][dk][dv]
+    float* dst = (prefill_single(jb.level) ? p.states + ((size_t)bh * p.Lmax + jb.level) * dk * dv
+                                           : p.ws + ((size_t)bh * p.njobs + job) * dk * dv) +
+                 cb * dvw + 4 * cq;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
         const int r = rg + nrg * i;
@@ -151,11 +154,16 @@ __global__ __launch_bounds__(kThr) void k_prefill_sum(PrefillParams p) {
     const size_t e = (size_t)chunk * kThr + threadIdx.x;
     if (e >= n4) return;
     const int n = p.T - 1;
+    const bool live = n >= 0 && (level == 0 || ((n >> (level - 1)) & 1));
+    if (live && prefill_single(level)) return;  // written by its job
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
-    if (n >= 0) {
+    if (live) {
+        // the pieces of a long bucket are consecutive jobs from the first
+        // piece: floor(s0 / 1024) of the bucket's first token
         const float4* ws = reinterpret_cast<const float4*>(p.ws) + (size_t)bh * p.njobs * n4;
-        for (int j = 0; j < p.njobs; ++j) {
-            if (prefill_job(n, j).level != level) continue;  // uniform over the block
+        const int first = ((n >> level) << level) / kPrefillJobTokens;
+        const int count = (1 << (level - 1)) / kPrefillJobTokens;
+        for (int j = first; j < first + count; ++j) {
             const float4 x = ws[(size_t)j * n4 + e];
             s.x += x.x; s.y += x.y; s.z += x.z; s.w += x.w;
         }
