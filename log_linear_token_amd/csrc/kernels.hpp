@@ -132,7 +132,7 @@ __device__ __forceinline__ PrefillJob prefill_job(int n, int j) {
 __device__ __forceinline__ bool prefill_single(int level) {
     return level == 0 || (1 << (level - 1)) <= kPrefillJobTokens;
 }
-// bf16 inputs: each job's decayed sum on the matrix cores (fused_fwd.hip)
+// bf16 inputs: each job's decayed sum on the matrix cores
 hipError_t launch_prefill_jobs_bf16(const PrefillParams& p, hipStream_t stream);
 hipError_t launch_prefill_states(const PrefillParams& p, bool bf16, hipStream_t stream);
 // copy states to dst, zeroing every slot that is not live at the current position

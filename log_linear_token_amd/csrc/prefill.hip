@@ -11,15 +11,14 @@
 //
 // The prefix is cut into jobs: whole 1024-token pieces of the buckets of 1024
 // tokens or more (every such bucket is a whole number of aligned pieces), one
-// job per smaller bucket, and one for level 0.  Each job's decayed sum goes to
-// the workspace: for bf16 inputs on the matrix cores (k_prefill_job in
-// fused_fwd.hip, which shares the forward's tile machinery), for fp32 inputs
-// by k_prefill_part below (fp32 vector FMAs).  A level of one job is written
+// job per smaller bucket, and one for level 0.  Each job's decayed sum is
+// computed for bf16 inputs on the matrix cores (k_prefill_job, with the
+// forward's tile machinery), for fp32 inputs with fp32 vector FMAs
+// (k_prefill_part).  A level of one job is written
 // to the state layout the decode state loads ([B, H, Lmax, dk, dv]) by its job;
 // k_prefill_sum adds the pieces of the longer buckets and zeroes the slots
 // that are not live.
-#include "common.hpp"
-#include "kernels.hpp"
+#include "tile_ops.hpp"
 
 namespace loglin {
 
@@ -27,6 +26,116 @@ namespace {
 
 constexpr int kThr = 256;
 constexpr int kTile = 64;
+
+// Prefill states (bf16 inputs): one block per (bh, job, column block) sums
+// exp(A_{s1-1} - A_s) k_s v_s^T over the job's tokens [s0, s1) tile by tile
+// (the forward's tile state, with the tokens outside the job masked), decays
+// the sum to position T - 1 and writes it, [d_k][d_v], to the state of its
+// level (a level of one job) or to the job's slot of the workspace.  The jobs
+// are described with PrefillJob (kernels.hpp).
+
+// Tile decay restricted to the tokens [lo, hi) of the tile: the others get
+// a = 0 (no decay) and e = 0 (no contribution).
+__device__ __forceinline__ float tile_decay_masked(const float* a_tile, int lo, int hi, float* Aw,
+                                                   float* Ew) {
+    const int lane = threadIdx.x & 63;
+    const bool in = lane >= lo && lane < hi;
+    const float x = wave_inclusive_sum(in ? a_tile[lane] : 0.f);
+    const float end = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+    Aw[lane] = x;
+    Ew[lane] = in ? __expf(end - x) : 0.f;
+    return end;
+}
+
+template <int DK, int NW>
+__global__ __launch_bounds__(NW * 64) void k_prefill_job(PrefillParams p) {
+    constexpr int DVW = NW * 16;
+    constexpr int NDT = DK / 16;
+    __shared__ __align__(16) bf16_t sK0[TC * DK];
+    __shared__ __align__(16) bf16_t sK1[TC * DK];
+    __shared__ __align__(16) bf16_t sV0[TC * DVW];
+    __shared__ __align__(16) bf16_t sV1[TC * DVW];
+    __shared__ __align__(16) float sa0[TC];
+    __shared__ __align__(16) float sa1[TC];
+    __shared__ __align__(16) float sAw[NW][TC];
+    __shared__ __align__(16) float sEw[NW][TC];
+    __shared__ float sred[NW];
+
+    const int ncb = p.dv / DVW;
+    int blk = blockIdx.x;
+    const int cb = (blk % ncb) * DVW;
+    blk /= ncb;
+    const int job = blk % p.njobs;
+    const int bh = blk / p.njobs;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, m16 = lane & 15, g = lane >> 4;
+    const PrefillJob jb = prefill_job(p.T - 1, job);
+    const size_t row0 = (size_t)bh * p.T;
+    const bf16_t* kg = reinterpret_cast<const bf16_t*>(p.k);
+    const bf16_t* vg = reinterpret_cast<const bf16_t*>(p.v);
+
+    // decay from the end of the job to position T - 1 (read after a barrier)
+    float part = 0.f;
+    for (int r = jb.s1 + (int)threadIdx.x; r < p.T; r += NW * 64) part += p.a[row0 + r];
+    for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o);
+    if (lane == 0) sred[wave] = part;
+
+    const int t0 = jb.s0 / TC, t1 = (jb.s1 - 1) / TC;  // the job's tiles
+    auto issue = [&](int tile, bf16_t* Kd, bf16_t* Vd, float* ad) __attribute__((always_inline)) {
+        const int base = tile * TC;
+        const int nvalid = min(TC, p.T - base);
+        const size_t r = row0 + base;
+        dma_tile<DK, NW>(kg + r * DK, DK, 0, nvalid, Kd, wave);
+        dma_tile<DVW, NW>(vg + r * p.dv, p.dv, cb, nvalid, Vd, wave);
+        if (wave == 0) {
+            if (lane < nvalid) dma4(p.a + r + lane, ad);
+            else ad[lane] = 0.f;
+        }
+    };
+
+    f32x4 u[NDT];
+#pragma unroll
+    for (int kt = 0; kt < NDT; ++kt) u[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    auto body = [&](int tile, const bf16_t* Kc, const bf16_t* Vc, const float* ac, bf16_t* Kn,
+                    bf16_t* Vn, float* an) __attribute__((always_inline)) {
+        __builtin_amdgcn_s_waitcnt(0);
+        __syncthreads();
+        if (tile + 1 <= t1) issue(tile + 1, Kn, Vn, an);
+        const int base = tile * TC;
+        const float tot = tile_decay_masked(ac, jb.s0 - base, jb.s1 - base, sAw[wave], sEw[wave]);
+        const float f = __expf(tot);
+#pragma unroll
+        for (int kt = 0; kt < NDT; ++kt) {
+            u[kt][0] *= f; u[kt][1] *= f; u[kt][2] *= f; u[kt][3] *= f;
+        }
+        bf16x8 vf[2];
+        vf[0] = ld_tr8<DVW>(Vc, 0, 16 * wave);
+        vf[1] = ld_tr8<DVW>(Vc, 32, 16 * wave);
+        tile_state<DK, NDT, false>(u, 0, Kc, vf, sEw[wave]);
+    };
+
+    issue(t0, sK0, sV0, sa0);
+    for (int tile = t0; tile <= t1; tile += 2) {
+        body(tile, sK0, sV0, sa0, sK1, sV1, sa1);
+        if (tile + 1 <= t1) body(tile + 1, sK1, sV1, sa1, sK0, sV0, sa0);
+    }
+    float carry = 0.f;
+#pragma unroll
+    for (int w = 0; w < NW; ++w) carry += sred[w];
+    const float fin = __expf(carry);
+    float* dst = (prefill_single(jb.level)
+                      ? p.states + ((size_t)bh * p.Lmax + jb.level) * DK * p.dv
+                      : p.ws + ((size_t)bh * p.njobs + job) * DK * p.dv) +
+                 cb + wave * 16 + m16;
+#pragma unroll
+    for (int kt = 0; kt < NDT; ++kt) {
+        // row of u[kt] (see tile_state): 32 (kt / 2) + 8g + 4 (kt % 2), or 4g for d_k = 16
+        const int row = DK >= 32 ? 32 * (kt / 2) + 8 * g + 4 * (kt % 2) : 4 * g;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) dst[(size_t)(row + i) * p.dv] = fin * u[kt][i];
+    }
+}
 
 template <typename E>
 __global__ __launch_bounds__(kThr) void k_prefill_part(PrefillParams p) {
@@ -177,6 +286,31 @@ int prefill_jobs(int T) {
     if (T <= 0) return 0;
     const int n = T - 1;
     return n / kPrefillJobTokens + __builtin_popcount((unsigned)(n % kPrefillJobTokens)) + 1;
+}
+
+namespace {
+template <int DK>
+hipError_t launch_prefill_dk(const PrefillParams& p, hipStream_t stream) {
+    const int dvw = p.dv >= 64 ? 64 : p.dv;
+    const unsigned nb = (unsigned)((long)p.BH * p.njobs * (p.dv / dvw));
+    switch (dvw) {
+        case 16: hipLaunchKernelGGL((k_prefill_job<DK, 1>), dim3(nb), dim3(64), 0, stream, p); break;
+        case 32: hipLaunchKernelGGL((k_prefill_job<DK, 2>), dim3(nb), dim3(128), 0, stream, p); break;
+        case 64: hipLaunchKernelGGL((k_prefill_job<DK, 4>), dim3(nb), dim3(256), 0, stream, p); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+}  // namespace
+
+hipError_t launch_prefill_jobs_bf16(const PrefillParams& p, hipStream_t stream) {
+    switch (p.dk) {
+        case 16: return launch_prefill_dk<16>(p, stream);
+        case 32: return launch_prefill_dk<32>(p, stream);
+        case 64: return launch_prefill_dk<64>(p, stream);
+        case 128: return launch_prefill_dk<128>(p, stream);
+    }
+    return hipErrorInvalidValue;
 }
 
 hipError_t launch_prefill_states(const PrefillParams& p, bool bf16, hipStream_t stream) {
