@@ -40,17 +40,25 @@ BF16_PEAK_TFLOPS = 2500.0    # dense bf16 MFMA, TFLOP/s
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd8k_decode_hbm_traffic.txt")
 
 
+def sources_hash(files: str) -> str:
+    """sha256[:16] of the concatenated contents of comma-separated source files."""
+    h = hashlib.sha256()
+    for f in files.split(","):
+        with open(os.path.join(ROOT, f), "rb") as src:
+            h.update(src.read())
+    return h.hexdigest()[:16]
+
+
 def measured_traffic(kernel: str):
     """HBM bytes per launch of `kernel` from the committed counter summary, or
-    None when there is none or the kernel's source has changed since."""
+    None when there is none or the kernel's sources have changed since."""
     try:
         with open(TRAFFIC_FILE) as f:
             for ln in f:
                 parts = ln.split()
                 if len(parts) == 5 and parts[0] == "traffic" and parts[1] == kernel:
-                    with open(os.path.join(ROOT, parts[3]), "rb") as src:
-                        if hashlib.sha256(src.read()).hexdigest()[:16] != parts[4]:
-                            return None
+                    if sources_hash(parts[3]) != parts[4]:
+                        return None
                     return float(parts[2])
     except OSError:
         return None
