@@ -17,6 +17,8 @@ Two independent forms of the same output are provided:
   greedily (not from a closed-form bit formula).
 * Form B -- the token-by-token Fenwick recurrence of section 2, in C
   (loglin_oracle.c), which also serves decode.
+* The backward pass -- the gradients of Form A by the chain rule
+  (form_a_grads), pinned by finite differences of Form A.
 
 Readings of points the page leaves open (positions 0-indexed, oldest tokens in
 the largest bucket, lambda indexed by the query, the decay convention) are
@@ -175,6 +177,72 @@ def form_a_rows(q, k, v, a, lam, rows) -> np.ndarray:
         scores = np.asarray(k[: t + 1], dtype=np.float64) @ np.asarray(q[t], dtype=np.float64)
         out[n] = (scores * w) @ np.asarray(v[: t + 1], dtype=np.float64)
     return out
+
+
+# --------------------------------------------------------------------------
+# Gradients of Form A (the backward pass)
+
+def _running_sum_grad(W):
+    """dA_t = sum_s W[t, s] - sum_t' W[t', t] for W = dP (.) P."""
+    return W.sum(axis=1) - W.sum(axis=0)
+
+
+def _suffix_sum(x):
+    """y_j = sum_{t >= j} x_t."""
+    return np.cumsum(x[::-1])[::-1]
+
+
+def form_a_grads(q, k, v, a, lam, dout):
+    """Gradients of sum(O * dout) for O = form_a(q, k, v, a, lam), in fp64.
+
+    "Log-linear attention, and what a logarithm buys", section 3 trains the
+    mixer forward and backward, and section 6 notes that the gradients of the
+    lambda terms have to be derived by hand.  This is the chain rule through
+    section 1's masked form O = P V with P = (Q K^T) (.) M and
+    M[t, s] = lambda_t^(level(t, s)) exp(A_t - A_s), s <= t, A the running
+    sum of a:
+
+      dP = dO V^T                 (cotangent of P, kept below the diagonal)
+      dV = P^T dO
+      dQ = (dP (.) M) K,          dK = (dP (.) M)^T Q
+      dlambda_t^(l) = sum over the keys s of level l of dP[t, s] (q_t . k_s) exp(A_t - A_s)
+      dA_t = sum_s W[t, s] - sum_t' W[t', t],   W = dP (.) P
+             (A_t enters row t of M with a plus sign and column t with a minus)
+      da_j = sum_{t >= j} dA_t    (a_j is in A_t for every t >= j)
+
+    Shapes as in form_a, dout like the output.  Returns (dq, dk, dv, da, dlam).
+    """
+    q, k, v, a, lam, dout = map(_f64, (q, k, v, a, lam, dout))
+    lead = q.shape[:-2]
+    T, dk = q.shape[-2:]
+    dv = v.shape[-1]
+    L = lam.shape[-1]
+    lev = level_map(T).astype(np.int64)
+    tri = lev >= 0
+    if T > 0 and lev.max() >= L:
+        raise ValueError(f"lambda has {L} levels; T={T} needs {lev.max() + 1}")
+    qf, kf, vf = q.reshape(-1, T, dk), k.reshape(-1, T, dk), v.reshape(-1, T, dv)
+    af, lf, gf = a.reshape(-1, T), lam.reshape(-1, T, L), dout.reshape(-1, T, dv)
+    n = qf.shape[0]
+    dq, dkk, dvv = np.zeros_like(qf), np.zeros_like(kf), np.zeros_like(vf)
+    da, dlam = np.zeros_like(af), np.zeros_like(lf)
+    rows = np.arange(T)[:, None]
+    for i in range(n):
+        A = np.cumsum(af[i])
+        decay = np.where(tri, np.exp(np.where(tri, A[:, None] - A[None, :], 0.0)), 0.0)
+        M = decay * np.where(tri, lf[i][rows, np.maximum(lev, 0)], 0.0)
+        S = qf[i] @ kf[i].T
+        P = S * M
+        dP = np.where(tri, gf[i] @ vf[i].T, 0.0)
+        dvv[i] = P.T @ gf[i]
+        dq[i] = (dP * M) @ kf[i]
+        dkk[i] = (dP * M).T @ qf[i]
+        G = dP * S * decay  # derivative of the loss in the weight lambda_t^(level)
+        for l in range(L):
+            dlam[i][:, l] = np.sum(np.where(lev == l, G, 0.0), axis=1)
+        da[i] = _suffix_sum(_running_sum_grad(dP * P))
+    return (dq.reshape(*lead, T, dk), dkk.reshape(*lead, T, dk), dvv.reshape(*lead, T, dv),
+            da.reshape(*lead, T), dlam.reshape(*lead, T, L))
 
 
 # --------------------------------------------------------------------------
