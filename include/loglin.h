@@ -140,6 +140,48 @@ LOGLIN_API loglin_status loglin_fwd_chunked_stages(const void* q, const void* k,
                                         void* stream);
 
 /*
+ * Bytes of device workspace loglin_bwd_chunked needs for these sizes, or
+ * (size_t)-1 (with the error text set) for sizes it would reject.
+ */
+LOGLIN_API size_t loglin_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int C,
+                                             loglin_dtype in_dtype);
+
+/*
+ * Backward pass of loglin_fwd_chunked: the gradients of sum(O (.) dO) with
+ * respect to every input.  Section 3 of "Log-linear attention, and what a
+ * logarithm buys" trains the mixer forward and backward with the same chunk
+ * split; section 6 notes that the lambda gradients must be derived by hand.
+ * With P = Q K^T (.) M and dP = dO V^T:
+ *   dq = (dP (.) M) K,  dk = (dP (.) M)^T Q,  dv = P^T dO,
+ *   dlambda_t^(l) = sum over the keys s of level l of dP[t,s] (q_t.k_s) e^(A_t - A_s),
+ *   dlog_decay_j = sum_{t >= j} (q_t.dq_t - k_t.dk_t).
+ *
+ *   q, k, v, log_decay, lambda, B, H, T, dk, dv, L, C, in_dtype
+ *              as for loglin_fwd_chunked (same layouts and limits)
+ *   dout       [B, H, T, dv]  in_dtype: the gradient of the output
+ *   dq, dk_out [B, H, T, dk]  fp32, written
+ *   dv_out     [B, H, T, dv]  fp32, written
+ *   dlog_decay [B, H, T]      fp32, written
+ *   dlambda    [B, H, T, L]   fp32, written (zero at levels a row does not use)
+ *   workspace  device buffer of at least loglin_bwd_workspace_bytes(...)
+ *              bytes, 256-byte aligned; contents on entry ignored, on
+ *              return unspecified
+ * q, k, v, dout, dq, dk_out and dv_out must be 16-byte aligned.  B, H or T
+ * equal to 0 is a no-op.  Errors as for loglin_fwd_chunked; nothing is
+ * launched when an argument is rejected.  Numerics: bf16 in_dtype feeds
+ * bf16 matrix cores (16-deep steps) with fp32 accumulation, the carried
+ * states and the masked score tiles rounded to bf16 as operands; the decay
+ * gradient's suffix sums run in fp64.
+ */
+LOGLIN_API loglin_status loglin_bwd_chunked(const void* q, const void* k, const void* v,
+                                 const float* log_decay, const float* lambda, const void* dout,
+                                 float* dq, float* dk_out, float* dv_out, float* dlog_decay,
+                                 float* dlambda, int B, int H, int T, int dk, int dv, int L,
+                                 int C, loglin_dtype in_dtype, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/*
+ * Decode state:/*
  * Decode state: for nseq sequences x H heads, Lmax level states of dk x dv
  * (S = sum k v^T orientation) plus the next position of each sequence.  Each
  * level is held as an fp32 matrix and a scalar log-scale (the state is the

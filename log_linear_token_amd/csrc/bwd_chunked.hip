@@ -1,0 +1,643 @@
+// Backward pass of the chunked log-linear token mixer on gfx950.
+//
+// "Log-linear attention, and what a logarithm buys", section 3 trains the
+// mixer with chunked matrix products forward and backward, and section 6
+// notes that the gradients of the lambda terms are derived by hand.  For the
+// loss sum(O (.) dO) with O = (Q K^T (.) M) V and
+// M[t, s] = lambda_t^(level(t, s)) e^(A_t - A_s):
+//
+//   dQ = (dP (.) M) K                     dP = dO V^T
+//   dK = (dP (.) M)^T Q,  dV = (Q K^T (.) M)^T dO
+//   dlambda_t^(l) = sum over the keys s of level l of dP[t, s] (q_t . k_s) e^(A_t - A_s)
+//   da_j = sum_{t >= j} (q_t . dq_t - k_t . dk_t)
+//
+// (the last line: A_t enters row t of M with a plus sign and column t with a
+// minus, and a_j is part of every A_t with t >= j).  The chunk split is the
+// forward's: inside a chunk the C x C block is materialised; the coarse
+// levels go through states.
+//
+//   dq / dlambda  for query chunk i, one Fenwick node per set bit p of i,
+//                 built by the forward's chunk-state and scan kernels over k
+//                 and v swapped (G'(e) = sum e^(A_end(e) - A_s) k_s v_s^T):
+//                   dq_t += lambda_t^(l) e^(A_t - A_end(e)) G'(e) dO_t
+//                   dlambda_t^(l) = e^(A_t - A_end(e)) q_t^T G'(e) dO_t
+//   rstate        the keys of chunk i reach the queries of the block of 2^p
+//                 chunks starting at j = ((i >> p) | 1) << p at level
+//                 log2 C + p + 1, for each clear bit p of i.  Every chunk
+//                 j >= 1 starts exactly one such block (p = lssb(j)), whose
+//                 state is
+//                   R(j) = sum_{t in block} lambda_t^(log2 C + p + 1) e^(A_t - A_(jC-1)) q_t dO_t^T
+//   dk / dv       dk_s += e^(A_(jC-1) - A_s) R(j) v_s,  dv_s += e^(A_(jC-1) - A_s) R(j)^T k_s
+//                 plus the chunk's own block
+//   da            the suffix sums of q_t . dq_t - k_t . dk_t
+//
+// Workspace (per (batch*head) bh): the forward's node buffers for G', R and
+// R^T ([N][dk][dv] and [N][dv][dk] fp32, R at the index j of the block's
+// first chunk), and the two dot products per token.
+#include <type_traits>
+
+#include "chunk_stage.hpp"
+#include "common.hpp"
+#include "kernels.hpp"
+
+namespace loglin {
+
+namespace {
+
+// Contraction steps of the backward's matrix-core products: bf16 K = 16
+// (4 values a lane, the operand layout of the P hand-off), fp32 K = 4.
+template <typename E>
+struct BStep {
+    static constexpr int KS = 16;
+};
+template <>
+struct BStep<float> {
+    static constexpr int KS = 4;
+};
+
+template <int C>
+struct LogC {
+    static constexpr int v = C == 16 ? 4 : C == 32 ? 5 : C == 64 ? 6 : 7;
+};
+
+// A operand rows x0 .. x0 + 15 of a staged chunk, contraction step ks over
+// the head dim: bf16 reads the natural copy (D + kPadK per row), fp32 the
+// transposed one (one element a lane).
+template <typename E, int C>
+__device__ __forceinline__ typename Frag<E, BStep<E>::KS>::type rows_op(const E* nat, const E* tr,
+                                                                        int D, int x0, int ks,
+                                                                        int m, int g) {
+    if constexpr (sizeof(E) == 2) {
+        return Frag<E, 16>::load(nat + (x0 + m) * (D + kPadK) + ks * 16 + 4 * g);
+    } else {
+        return tr[(ks * 4 + g) * (C + kPadT) + x0 + m];
+    }
+}
+
+// B operand of the lane's own token row (row n = lane % 16), step ks
+template <typename E>
+__device__ __forceinline__ typename Frag<E, BStep<E>::KS>::type own_op(const E* row, bool ok, int ks,
+                                                                       int g) {
+    typedef typename Frag<E, BStep<E>::KS>::type frag_t;
+    if (!ok) return frag_t{};
+    if constexpr (sizeof(E) == 2) {
+        return Frag<E, 16>::load(row + ks * 16 + 4 * g);
+    } else {
+        return row[ks * 4 + g];
+    }
+}
+
+// the C-layout tile (4 values of column m) as the B operand of the next product
+template <typename E>
+struct Hand {
+    typedef typename std::conditional<sizeof(E) == 2, bf16x4, f32x4>::type type;
+    __device__ static type pack(float a, float b, float c, float d) {
+        if constexpr (sizeof(E) == 2) {
+            return pack4(a, b, c, d);
+        } else {
+            return f32x4{a, b, c, d};
+        }
+    }
+};
+
+// acc += X^T-rows (x0 + m, the transposed copy) times a handed-off tile of
+// 16 tokens starting at 16 S
+template <typename E, int C>
+__device__ __forceinline__ f32x4 mma_hand(const E* tr, int x0, int S, typename Hand<E>::type h,
+                                          f32x4 acc, int m, int g) {
+    const E* row = tr + (x0 + m) * (C + kPadT) + 16 * S + 4 * g;
+    if constexpr (sizeof(E) == 2) {
+        return mma(Frag<bf16_t, 16>::load(row), h, acc);
+    } else {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc = mma(row[j], h[j], acc);
+        return acc;
+    }
+}
+
+__device__ __forceinline__ float sum_groups(float x) {  // over the 4 lanes of one column
+    x += __shfl_xor(x, 16, kWave);
+    x += __shfl_xor(x, 32, kWave);
+    return x;
+}
+
+__device__ __forceinline__ float load_f32(const float* p) { return *p; }
+__device__ __forceinline__ float load_f32(const bf16_t* p) { return bf16_to_f32(*p); }
+
+// --------------------------------------------------------------------------
+// dq and dlambda: one block per chunk, one wave per 16 query rows
+
+template <typename E, int C, int DM>
+__global__ __launch_bounds__(C / 16 * 64) void k_bwd_dq(BwdParams p) {
+    constexpr int NW = C / 16;
+    constexpr int LOGC = LogC<C>::v;
+    constexpr int KS = BStep<E>::KS;
+    constexpr int MAXK = DM / KS;
+    constexpr int NB = DM / 16;
+    typedef Frag<E, KS> FR;
+    typedef typename FR::type frag_t;
+    constexpr int KPL = FR::kpl;
+    constexpr bool NAT = sizeof(E) == 2;
+
+    extern __shared__ __align__(16) char smem[];
+    const int blk = xcd_local_block(blockIdx.x, gridDim.x);
+    const int bh = blk / p.N;
+    const int i = blk - bh * p.N;
+    const int t0 = i * C;
+    const int nvalid = min(C, p.T - t0);
+    const int dk = p.dk, dv = p.dv;
+    const int nkk = dk / KS, nkv = dv / KS;
+    float* a_raw = reinterpret_cast<float*>(smem);
+    float* A = a_raw + C;
+    E* KT = reinterpret_cast<E*>(A + C);       // [dk][C + kPadT]
+    E* X1 = KT + dk * (C + kPadT);             // bf16: K natural; fp32: V transposed
+    E* X2 = X1 + (NAT ? C * (dk + kPadK) : 0); // bf16: V natural
+    const E* Kn = X1;
+    const E* Vn = X2;
+    const E* VT = X1;
+    const size_t row0 = (size_t)bh * p.T + t0;
+
+    for (int s = threadIdx.x; s < C; s += blockDim.x) a_raw[s] = s < nvalid ? p.a[row0 + s] : 0.f;
+    const E* kg = static_cast<const E*>(p.k) + row0 * dk;
+    const E* vg = static_cast<const E*>(p.v) + row0 * dv;
+    stage_transposed<E, C>(kg, dk, nvalid, KT, nullptr);
+    if constexpr (NAT) {
+        stage_natural<E, C>(kg, dk, nvalid, X1);
+        stage_natural<E, C>(vg, dv, nvalid, X2);
+    } else {
+        stage_transposed<E, C>(vg, dv, nvalid, X1, nullptr);
+    }
+    __syncthreads();
+    if (threadIdx.x < kWave) wave_cumsum(a_raw, A, C);
+    __syncthreads();
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int R = threadIdx.x / kWave;
+    const int m = lane & 15, g = lane >> 4;
+    const int r = 16 * R + m;
+    const bool rvalid = r < nvalid;
+    const size_t trow = row0 + r;
+    const E* qrow = static_cast<const E*>(p.q) + trow * dk;
+    const E* orow = static_cast<const E*>(p.dout) + trow * dv;
+
+    frag_t df[MAXK], qf[MAXK];
+#pragma unroll
+    for (int ks = 0; ks < MAXK; ++ks) {
+        df[ks] = ks < nkv ? own_op<E>(orow, rvalid, ks, g) : frag_t{};
+        qf[ks] = ks < nkk ? own_op<E>(qrow, rvalid, ks, g) : frag_t{};
+    }
+    const float* lrow = p.lam + trow * p.L;
+    float lamr[LOGC + 1];
+#pragma unroll
+    for (int l = 0; l <= LOGC; ++l) lamr[l] = (rvalid && l < p.L) ? lrow[l] : 0.f;
+    const float Ar = A[r];
+
+    // the chunk's own block: dS = dO V^T and Q K^T for the keys s <= r
+    typename Hand<E>::type Z[NW];
+    float dl[LOGC + 1];
+#pragma unroll
+    for (int l = 0; l <= LOGC; ++l) dl[l] = 0.f;
+#pragma unroll
+    for (int S = 0; S < NW; ++S) {
+        if (S <= R) {
+            f32x4 ds = {0.f, 0.f, 0.f, 0.f}, sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < MAXK; ++ks)
+                if (ks < nkv) ds = mma(rows_op<E, C>(Vn, VT, dv, 16 * S, ks, m, g), df[ks], ds);
+#pragma unroll
+            for (int ks = 0; ks < MAXK; ++ks)
+                if (ks < nkk) sc = mma(rows_op<E, C>(Kn, KT, dk, 16 * S, ks, m, g), qf[ks], sc);
+            float w[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int s = 16 * S + 4 * g + q;
+                const int lev = fenwick_level(r, s);
+                const float dec = s <= r ? __expf(Ar - A[s]) : 0.f;
+                w[q] = ds[q] * pick_level<LOGC>(lamr, lev) * dec;
+                const float gq = ds[q] * sc[q] * dec;
+#pragma unroll
+                for (int l = 0; l <= LOGC; ++l) dl[l] += lev == l ? gq : 0.f;
+            }
+            Z[S] = Hand<E>::pack(w[0], w[1], w[2], w[3]);
+        }
+    }
+
+    // dq^T column blocks: K^T Z^T, then one term per coarse level
+    f32x4 acc[NB];
+    float qv[NB][4];
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
+        acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+        if (16 * cb < dk) {
+#pragma unroll
+            for (int S = 0; S < NW; ++S)
+                if (S <= R) acc[cb] = mma_hand<E, C>(KT, 16 * cb, S, Z[S], acc[cb], m, g);
+        }
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            qv[cb][j] = (rvalid && 16 * cb < dk) ? load_f32(qrow + 16 * cb + 4 * g + j) : 0.f;
+    }
+    const double* cum = p.cum + (size_t)bh * p.N;
+    float* glrow = p.glam + trow * p.L;
+    for (int pb = 0; (i >> pb) != 0; ++pb) {
+        if (!((i >> pb) & 1)) continue;
+        const int node = ((i >> pb) << pb) - 1;
+        const int lev = LOGC + pb + 1;
+        const float e = rvalid ? __expf(Ar + (float)(cum[i - 1] - cum[node])) : 0.f;
+        const float lw = rvalid ? lrow[lev] * e : 0.f;
+        const float* G = p.gnode + ((size_t)bh * p.N + node) * dk * dv;
+        float dot = 0.f;
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb) {
+            if (16 * cb < dk) {
+                f32x4 y = {0.f, 0.f, 0.f, 0.f};
+                const float* grow = G + (size_t)(16 * cb + m) * dv + g * KPL;
+#pragma unroll
+                for (int ks = 0; ks < MAXK; ++ks)
+                    if (ks < nkv) y = mma(FR::from_f32(grow + ks * KS), df[ks], y);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    acc[cb][j] += lw * y[j];
+                    dot += qv[cb][j] * y[j];
+                }
+            }
+        }
+        dot = sum_groups(dot) * e;
+        if (rvalid && g == 0) glrow[lev] = dot;
+    }
+
+    float da1 = 0.f;
+    float* dqrow = p.gq + trow * dk;
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
+        if (16 * cb < dk) {
+#pragma unroll
+            for (int j = 0; j < 4; ++j) da1 += acc[cb][j] * qv[cb][j];
+            if (rvalid)
+                *reinterpret_cast<float4*>(dqrow + 16 * cb + 4 * g) =
+                    make_float4(acc[cb][0], acc[cb][1], acc[cb][2], acc[cb][3]);
+        }
+    }
+    da1 = sum_groups(da1);
+#pragma unroll
+    for (int l = 0; l <= LOGC; ++l) dl[l] = sum_groups(dl[l]);
+    if (rvalid && g == 0) {
+        p.dA1[trow] = da1;
+#pragma unroll
+        for (int l = 0; l <= LOGC; ++l)
+            if (l < p.L) glrow[l] = dl[l];
+        for (int l = LOGC + 1; l < p.L; ++l) {
+            const int pb = l - LOGC - 1;
+            if (pb >= 31 || !((i >> pb) & 1)) glrow[l] = 0.f;  // a level this row does not reach
+        }
+    }
+}
+
+// --------------------------------------------------------------------------
+// R(j): the lambda-weighted state of the block of chunks that starts at
+// chunk j, for the keys of its left sibling.  Blocks are taken largest first.
+
+template <typename E, int C>
+__global__ __launch_bounds__(256) void k_bwd_rstate(BwdParams p) {
+    constexpr int LOGC = LogC<C>::v;
+    constexpr int MAXT = 16;  // tiles of 16 x 16 per wave: (128 / 16)^2 / 4 waves
+    extern __shared__ __align__(16) char smem[];
+    int x = blockIdx.x, lev = -1, j = 0, bh = 0;
+    for (int pp = p.nlev - 1; pp >= 0; --pp) {
+        const int first = 1 << pp;
+        if (first >= p.N) continue;
+        const int cnt = (p.N - 1 - first) / (2 << pp) + 1;
+        if (x < cnt * p.BH) {
+            bh = x % p.BH;
+            j = (x / p.BH) * (2 << pp) + first;
+            lev = pp;
+            break;
+        }
+        x -= cnt * p.BH;
+    }
+    if (lev < 0) return;
+    const int jend = min(j + (1 << lev), p.N);
+    const int lidx = LOGC + lev + 1;
+    const int dk = p.dk, dv = p.dv;
+    float* a_raw = reinterpret_cast<float*>(smem);
+    float* Al = a_raw + C;
+    float* e = Al + C;
+    E* QT = reinterpret_cast<E*>(e + C);   // [dk][C + kPadT], scaled rows
+    E* OT = QT + dk * (C + kPadT);         // [dv][C + kPadT]
+    const double* cum = p.cum + (size_t)bh * p.N;
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int wave = threadIdx.x / kWave;
+    const int nw = blockDim.x / kWave;
+    const int m = lane & 15, g = lane >> 4;
+    const int ncv = dv / 16;
+    const int ntiles = (dk / 16) * ncv;
+    f32x4 acc[MAXT];
+#pragma unroll
+    for (int u = 0; u < MAXT; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+    for (int c = j; c < jend; ++c) {
+        const int t0 = c * C;
+        const int nvalid = min(C, p.T - t0);
+        const size_t row0 = (size_t)bh * p.T + t0;
+        __syncthreads();  // the previous chunk's operands are consumed
+        for (int s = threadIdx.x; s < C; s += blockDim.x) a_raw[s] = s < nvalid ? p.a[row0 + s] : 0.f;
+        __syncthreads();
+        if (threadIdx.x < kWave) wave_cumsum(a_raw, Al, C);
+        __syncthreads();
+        const float base = (float)(cum[c - 1] - cum[j - 1]);
+        for (int s = threadIdx.x; s < C; s += blockDim.x)
+            e[s] = s < nvalid ? p.lam[(row0 + s) * p.L + lidx] * __expf(base + Al[s]) : 0.f;
+        __syncthreads();
+        stage_transposed<E, C>(static_cast<const E*>(p.q) + row0 * dk, dk, nvalid, QT, e);
+        stage_transposed<E, C>(static_cast<const E*>(p.dout) + row0 * dv, dv, nvalid, OT, nullptr);
+        __syncthreads();
+#pragma unroll
+        for (int u = 0; u < MAXT; ++u) {
+            const int tile = wave + u * nw;
+            if (tile < ntiles) {
+                const int d0 = (tile / ncv) * 16, c0 = (tile % ncv) * 16;
+                const E* qa = QT + (d0 + m) * (C + kPadT) + 4 * g;
+                const E* ob = OT + (c0 + m) * (C + kPadT) + 4 * g;
+#pragma unroll
+                for (int S = 0; S < C / 16; ++S) {
+                    if constexpr (sizeof(E) == 2) {
+                        acc[u] = mma(Frag<bf16_t, 16>::load(qa + 16 * S), Frag<bf16_t, 16>::load(ob + 16 * S),
+                                     acc[u]);
+                    } else {
+#pragma unroll
+                        for (int jj = 0; jj < 4; ++jj) acc[u] = mma(qa[16 * S + jj], ob[16 * S + jj], acc[u]);
+                    }
+                }
+            }
+        }
+    }
+    float* Rd = p.rst + ((size_t)bh * p.N + j) * dk * dv;
+    float* RTd = p.rstT + ((size_t)bh * p.N + j) * dv * dk;
+#pragma unroll
+    for (int u = 0; u < MAXT; ++u) {
+        const int tile = wave + u * nw;
+        if (tile < ntiles) {
+            const int d0 = (tile / ncv) * 16, c0 = (tile % ncv) * 16;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) Rd[(size_t)(d0 + 4 * g + q) * dv + c0 + m] = acc[u][q];
+            *reinterpret_cast<float4*>(RTd + (size_t)(c0 + m) * dk + d0 + 4 * g) =
+                make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
+        }
+    }
+}
+
+// --------------------------------------------------------------------------
+// dk and dv: one block per chunk, one wave per 16 key rows
+
+template <typename E, int C, int DM>
+__global__ __launch_bounds__(C / 16 * 64) void k_bwd_dkv(BwdParams p) {
+    constexpr int NW = C / 16;
+    constexpr int LOGC = LogC<C>::v;
+    constexpr int KS = BStep<E>::KS;
+    constexpr int MAXK = DM / KS;
+    constexpr int NB = DM / 16;
+    typedef Frag<E, KS> FR;
+    typedef typename FR::type frag_t;
+    constexpr int KPL = FR::kpl;
+    constexpr bool NAT = sizeof(E) == 2;
+
+    extern __shared__ __align__(16) char smem[];
+    const int blk = xcd_local_block(blockIdx.x, gridDim.x);
+    const int bh = blk / p.N;
+    const int i = blk - bh * p.N;
+    const int t0 = i * C;
+    const int nvalid = min(C, p.T - t0);
+    const int dk = p.dk, dv = p.dv;
+    const int nkk = dk / KS, nkv = dv / KS;
+    float* a_raw = reinterpret_cast<float*>(smem);
+    float* A = a_raw + C;
+    float* lamc = A + C;                          // [C][LOGC + 1]
+    E* QT = reinterpret_cast<E*>(lamc + C * (LOGC + 1));  // [dk][C + kPadT]
+    E* OT = QT + dk * (C + kPadT);                // [dv][C + kPadT]
+    E* Qn = OT + dv * (C + kPadT);                // bf16: [C][dk + kPadK]
+    E* On = Qn + (NAT ? C * (dk + kPadK) : 0);    // bf16: [C][dv + kPadK]
+    const size_t row0 = (size_t)bh * p.T + t0;
+
+    for (int s = threadIdx.x; s < C; s += blockDim.x) a_raw[s] = s < nvalid ? p.a[row0 + s] : 0.f;
+    for (int x = threadIdx.x; x < C * (LOGC + 1); x += blockDim.x) {
+        const int t = x / (LOGC + 1), l = x - t * (LOGC + 1);
+        lamc[x] = (t < nvalid && l < p.L) ? p.lam[(row0 + t) * p.L + l] : 0.f;
+    }
+    const E* qg = static_cast<const E*>(p.q) + row0 * dk;
+    const E* og = static_cast<const E*>(p.dout) + row0 * dv;
+    stage_transposed<E, C>(qg, dk, nvalid, QT, nullptr);
+    stage_transposed<E, C>(og, dv, nvalid, OT, nullptr);
+    if constexpr (NAT) {
+        stage_natural<E, C>(qg, dk, nvalid, Qn);
+        stage_natural<E, C>(og, dv, nvalid, On);
+    }
+    __syncthreads();
+    if (threadIdx.x < kWave) wave_cumsum(a_raw, A, C);
+    __syncthreads();
+
+    const int lane = threadIdx.x & (kWave - 1);
+    const int R = threadIdx.x / kWave;
+    const int m = lane & 15, g = lane >> 4;
+    const int s = 16 * R + m;  // key row within the chunk
+    const bool svalid = s < nvalid;
+    const size_t srow = row0 + s;
+    const E* krow = static_cast<const E*>(p.k) + srow * dk;
+    const E* vrow = static_cast<const E*>(p.v) + srow * dv;
+    frag_t vf[MAXK], kf[MAXK];
+#pragma unroll
+    for (int ks = 0; ks < MAXK; ++ks) {
+        vf[ks] = ks < nkv ? own_op<E>(vrow, svalid, ks, g) : frag_t{};
+        kf[ks] = ks < nkk ? own_op<E>(krow, svalid, ks, g) : frag_t{};
+    }
+    const float As = A[s];
+
+    const double* cum = p.cum + (size_t)bh * p.N;
+    const double ci = i > 0 ? cum[i - 1] : 0.0;
+    float da2 = 0.f;
+
+    // Two passes, dk then dv, so that only one set of handed-off tiles and
+    // accumulators is live at a time.  dk^T[d][s] = sum_t Q^T[d][t] Z[t][s]
+    // with Z = dP (.) M (dP from dO and v_s); dv^T[c][s] = sum_t dO^T[c][t] P[t][s]
+    // with P = (Q K^T) (.) M (from q and k_s); then the coarse levels through R(j).
+    auto pass = [&](auto kpass) __attribute__((always_inline)) {
+        constexpr bool GK = decltype(kpass)::value;
+        const int dout_dim = GK ? dk : dv;       // columns of the gradient
+        const int nkc = GK ? nkv : nkk;          // contraction steps of the tile products
+        const E* tn = GK ? On : Qn;              // rows t of the tile products
+        const E* tt = GK ? OT : QT;
+        const E* ht = GK ? QT : OT;              // transposed rows of the hand-off product
+        const frag_t* own = GK ? vf : kf;
+        typename Hand<E>::type H[NW];
+#pragma unroll
+        for (int S = 0; S < NW; ++S) {
+            if (S >= R) {
+                f32x4 x = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < MAXK; ++ks)
+                    if (ks < nkc) x = mma(rows_op<E, C>(tn, tt, GK ? dv : dk, 16 * S, ks, m, g), own[ks], x);
+                float z[4];
+#pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                    const int t = 16 * S + 4 * g + q;
+                    const float dec = t >= s ? __expf(A[t] - As) : 0.f;
+                    z[q] = x[q] * lamc[t * (LOGC + 1) + fenwick_level(t, s)] * dec;
+                }
+                H[S] = Hand<E>::pack(z[0], z[1], z[2], z[3]);
+            }
+        }
+        f32x4 acc[NB];
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb) {
+            acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+            if (16 * cb < dout_dim) {
+#pragma unroll
+                for (int S = 0; S < NW; ++S)
+                    if (S >= R) acc[cb] = mma_hand<E, C>(ht, 16 * cb, S, H[S], acc[cb], m, g);
+            }
+        }
+        // later blocks that see this chunk at a coarse level
+        for (int pb = 0; (1 << pb) < p.N; ++pb) {
+            if ((i >> pb) & 1) continue;
+            const int j = ((i >> pb) | 1) << pb;
+            if (j >= p.N) continue;
+            const float w = svalid ? __expf((float)(cum[j - 1] - ci) - As) : 0.f;
+            const float* Rs = GK ? p.rst + ((size_t)bh * p.N + j) * dk * dv
+                                 : p.rstT + ((size_t)bh * p.N + j) * dv * dk;
+            const int rpitch = GK ? dv : dk;
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb) {
+                if (16 * cb < dout_dim) {
+                    f32x4 y = {0.f, 0.f, 0.f, 0.f};
+                    const float* rr = Rs + (size_t)(16 * cb + m) * rpitch + g * KPL;
+#pragma unroll
+                    for (int ks = 0; ks < MAXK; ++ks)
+                        if (ks < nkc) y = mma(FR::from_f32(rr + ks * KS), own[ks], y);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acc[cb][q] += w * y[q];
+                }
+            }
+        }
+        float* grow = (GK ? p.gk : p.gv) + srow * dout_dim;
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb) {
+            if (16 * cb < dout_dim) {
+                if constexpr (GK) {
+#pragma unroll
+                    for (int q = 0; q < 4; ++q)
+                        da2 += acc[cb][q] * (svalid ? load_f32(krow + 16 * cb + 4 * g + q) : 0.f);
+                }
+                if (svalid)
+                    *reinterpret_cast<float4*>(grow + 16 * cb + 4 * g) =
+                        make_float4(acc[cb][0], acc[cb][1], acc[cb][2], acc[cb][3]);
+            }
+        }
+    };
+    pass(std::integral_constant<bool, true>{});
+    pass(std::integral_constant<bool, false>{});
+    da2 = sum_groups(da2);
+    if (svalid && g == 0) p.dA2[srow] = da2;
+}
+
+// --------------------------------------------------------------------------
+// da_j = sum_{t >= j} (dA1_t - dA2_t): one block per (batch, head), each
+// thread a contiguous run of tokens, fp64 sums.
+
+__global__ __launch_bounds__(256) void k_bwd_da(BwdParams p) {
+    __shared__ double part[256];
+    const int bh = blockIdx.x;
+    const int tid = threadIdx.x;
+    const int per = (p.T + 255) / 256;
+    const int tb = min(p.T, tid * per), te = min(p.T, tb + per);
+    const size_t base = (size_t)bh * p.T;
+    double sum = 0.0;
+    for (int t = tb; t < te; ++t) sum += (double)p.dA1[base + t] - (double)p.dA2[base + t];
+    part[tid] = sum;
+    __syncthreads();
+    // inclusive suffix scan over the threads (Hillis-Steele)
+    for (int off = 1; off < 256; off <<= 1) {
+        const double y = tid + off < 256 ? part[tid + off] : 0.0;
+        __syncthreads();
+        part[tid] += y;
+        __syncthreads();
+    }
+    double run = part[tid] - sum;  // the threads after this one
+    for (int t = te - 1; t >= tb; --t) {
+        run += (double)p.dA1[base + t] - (double)p.dA2[base + t];
+        p.ga[base + t] = (float)run;
+    }
+}
+
+template <typename E, int C>
+size_t dq_smem(int dk, int dv) {
+    const size_t nat = sizeof(E) == 2 ? (size_t)C * (dk + kPadK) + (size_t)C * (dv + kPadK)
+                                      : (size_t)dv * (C + kPadT);
+    return 2 * C * sizeof(float) + ((size_t)dk * (C + kPadT) + nat) * sizeof(E);
+}
+template <typename E, int C>
+size_t dkv_smem(int dk, int dv) {
+    const size_t nat = sizeof(E) == 2 ? (size_t)C * (dk + kPadK) + (size_t)C * (dv + kPadK) : 0;
+    return (2 * C + (size_t)C * (LogC<C>::v + 1)) * sizeof(float) +
+           ((size_t)(dk + dv) * (C + kPadT) + nat) * sizeof(E);
+}
+template <typename E, int C>
+size_t rstate_smem(int dk, int dv) {
+    return 3 * C * sizeof(float) + (size_t)(dk + dv) * (C + kPadT) * sizeof(E);
+}
+
+template <typename K>
+hipError_t set_smem(K kernel, size_t bytes) {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+}
+
+template <typename E, int C, int DM>
+hipError_t launch_bwd_typed(const BwdParams& p, hipStream_t stream) {
+    const int nblk = p.BH * p.N;
+    const size_t s1 = dq_smem<E, C>(p.dk, p.dv);
+    hipError_t err = set_smem(&k_bwd_dq<E, C, DM>, s1);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((k_bwd_dq<E, C, DM>), dim3(nblk), dim3(C / 16 * 64), s1, stream, p);
+    if (p.N > 1) {
+        const size_t s2 = rstate_smem<E, C>(p.dk, p.dv);
+        err = set_smem(&k_bwd_rstate<E, C>, s2);
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL((k_bwd_rstate<E, C>), dim3(p.BH * (p.N - 1)), dim3(256), s2, stream, p);
+    }
+    const size_t s3 = dkv_smem<E, C>(p.dk, p.dv);
+    err = set_smem(&k_bwd_dkv<E, C, DM>, s3);
+    if (err != hipSuccess) return err;
+    hipLaunchKernelGGL((k_bwd_dkv<E, C, DM>), dim3(nblk), dim3(C / 16 * 64), s3, stream, p);
+    hipLaunchKernelGGL(k_bwd_da, dim3(p.BH), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+template <typename E, int C>
+hipError_t launch_bwd_c(const BwdParams& p, hipStream_t s) {
+    switch (p.dk > p.dv ? p.dk : p.dv) {
+        case 16: return launch_bwd_typed<E, C, 16>(p, s);
+        case 32: return launch_bwd_typed<E, C, 32>(p, s);
+        case 64: return launch_bwd_typed<E, C, 64>(p, s);
+        case 128: return launch_bwd_typed<E, C, 128>(p, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+template <typename E>
+hipError_t launch_bwd_e(const BwdParams& p, hipStream_t s) {
+    switch (p.C) {
+        case 16: return launch_bwd_c<E, 16>(p, s);
+        case 32: return launch_bwd_c<E, 32>(p, s);
+        case 64: return launch_bwd_c<E, 64>(p, s);
+        case 128: return launch_bwd_c<E, 128>(p, s);
+    }
+    return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_bwd_chunked(const BwdParams& p, bool bf16, hipStream_t stream) {
+    return bf16 ? launch_bwd_e<bf16_t>(p, stream) : launch_bwd_e<float>(p, stream);
+}
+
+}  // namespace loglin

@@ -86,6 +86,29 @@ struct DecodeParams {
 
 hipError_t launch_decode_step(const DecodeParams& p, bool bf16, hipStream_t stream);
 
+// Backward pass of the chunked forward: gradients of sum(O (.) dO)
+struct BwdParams {
+    const void* q;            // [BH][T][dk]
+    const void* k;            // [BH][T][dk]
+    const void* v;            // [BH][T][dv]
+    const void* dout;         // [BH][T][dv]
+    const float* a;           // [BH][T]
+    const float* lam;         // [BH][T][L]
+    float* gq;                // [BH][T][dk]
+    float* gk;                // [BH][T][dk]
+    float* gv;                // [BH][T][dv]
+    float* ga;                // [BH][T]
+    float* glam;              // [BH][T][L]
+    int BH, T, dk, dv, L, C, N, nlev;  // nlev = bit_length(N - 1)
+    const float* gnode;       // [BH][N][dk][dv] Fenwick nodes of sum k v^T over chunks
+    const double* cum;        // [BH][N] A at the end of each chunk
+    float* rst;               // [BH][N][dk][dv] block states R(j)
+    float* rstT;              // [BH][N][dv][dk] the same, transposed
+    float* dA1;               // [BH][T] q_t . dq_t
+    float* dA2;               // [BH][T] k_t . dk_t
+};
+hipError_t launch_bwd_chunked(const BwdParams& p, bool bf16, hipStream_t stream);
+
 // Fenwick level states after the T tokens of a prefill (the state a decode
 // step at position T reads)
 struct PrefillParams {

@@ -322,6 +322,136 @@ loglin_status loglin_fwd_chunked(const void* q, const void* k, const void* v,
 }  // extern "C"
 
 // ---------------------------------------------------------------------------
+// backward pass
+
+namespace {
+
+// workspace of the backward: the Fenwick nodes of k v^T over chunks (the
+// forward's chunk-state and scan buffers), the block states R and R^T, and
+// the two per-token dot products that make up the decay gradient
+struct BwdWorkspace {
+    FwdWorkspace nodes;
+    size_t rst_off, rstT_off, da1_off, da2_off, total;
+};
+
+BwdWorkspace bwd_layout(long BH, int T, int dk, int dv, int C) {
+    BwdWorkspace w{};
+    const long N = ((long)T + C - 1) / C;
+    w.nodes = fwd_workspace_layout(BH, N, dk, dv, false, 1);
+    const size_t st = N > 1 ? (size_t)BH * N * dk * dv * sizeof(float) : 0;
+    size_t off = w.nodes.total;
+    w.rst_off = off;
+    off = align_up(off + st);
+    w.rstT_off = off;
+    off = align_up(off + st);
+    w.da1_off = off;
+    off = align_up(off + (size_t)BH * T * sizeof(float));
+    w.da2_off = off;
+    off = align_up(off + (size_t)BH * T * sizeof(float));
+    w.total = BH * T > 0 ? off : 0;
+    return w;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t loglin_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int C, loglin_dtype in_dtype) {
+    if (check_fwd_sizes(B, H, T, dk, dv, C) != LOGLIN_OK) return (size_t)-1;
+    if (in_dtype != LOGLIN_F32 && in_dtype != LOGLIN_BF16) {
+        fail(LOGLIN_EINVAL, "in_dtype %d is neither LOGLIN_F32 nor LOGLIN_BF16", (int)in_dtype);
+        return (size_t)-1;
+    }
+    return bwd_layout((long)B * H, T, dk, dv, C).total;
+}
+
+loglin_status loglin_bwd_chunked(const void* q, const void* k, const void* v, const float* log_decay,
+                                 const float* lambda, const void* dout, float* dq, float* dk_out,
+                                 float* dv_out, float* dlog_decay, float* dlambda, int B, int H,
+                                 int T, int dk, int dv, int L, int C, loglin_dtype in_dtype,
+                                 void* workspace, size_t workspace_bytes, void* stream) {
+    loglin_status s = check_fwd_sizes(B, H, T, dk, dv, C);
+    if (s != LOGLIN_OK) return s;
+    if (in_dtype != LOGLIN_F32 && in_dtype != LOGLIN_BF16)
+        return fail(LOGLIN_EINVAL, "in_dtype %d is neither LOGLIN_F32 nor LOGLIN_BF16", (int)in_dtype);
+    if ((long)B * H * T == 0) return ok();
+    if (L < levels_needed(T) || L > 64)
+        return fail(LOGLIN_EINVAL, "L=%d: T=%d needs %d levels (and L <= 64)", L, T, levels_needed(T));
+    if (!q || !k || !v || !log_decay || !lambda || !dout || !dq || !dk_out || !dv_out || !dlog_decay ||
+        !dlambda)
+        return fail(LOGLIN_EINVAL, "null tensor pointer");
+    const uintptr_t al = reinterpret_cast<uintptr_t>(q) | reinterpret_cast<uintptr_t>(k) |
+                         reinterpret_cast<uintptr_t>(v) | reinterpret_cast<uintptr_t>(dout) |
+                         reinterpret_cast<uintptr_t>(dq) | reinterpret_cast<uintptr_t>(dk_out) |
+                         reinterpret_cast<uintptr_t>(dv_out);
+    if (al % 16) return fail(LOGLIN_EINVAL, "q, k, v, dout, dq, dk and dv must be 16-byte aligned");
+    const long BH = (long)B * H;
+    const BwdWorkspace w = bwd_layout(BH, T, dk, dv, C);
+    if (!workspace || workspace_bytes < w.total)
+        return fail(LOGLIN_EINVAL, "workspace of %zu bytes needed, got %zu%s", w.total, workspace_bytes,
+                    workspace ? "" : " (NULL)");
+    if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
+        return fail(LOGLIN_EINVAL, "workspace must be %zu-byte aligned", kAlign);
+    char* base = static_cast<char*>(workspace);
+    const int N = (int)(((long)T + C - 1) / C);
+    hipStream_t hs = static_cast<hipStream_t>(stream);
+
+    BwdParams bp{};
+    bp.q = q;
+    bp.k = k;
+    bp.v = v;
+    bp.dout = dout;
+    bp.a = log_decay;
+    bp.lam = lambda;
+    bp.gq = dq;
+    bp.gk = dk_out;
+    bp.gv = dv_out;
+    bp.ga = dlog_decay;
+    bp.glam = dlambda;
+    bp.BH = (int)BH;
+    bp.T = T;
+    bp.dk = dk;
+    bp.dv = dv;
+    bp.L = L;
+    bp.C = C;
+    bp.N = N;
+    bp.nlev = bit_length(N - 1);
+    bp.dA1 = reinterpret_cast<float*>(base + w.da1_off);
+    bp.dA2 = reinterpret_cast<float*>(base + w.da2_off);
+    if (N > 1) {
+        // the forward's chunk states and node scan over k and v swapped: the
+        // nodes come out as sum k v^T, [dk][dv]
+        FwdParams fp{};
+        fp.k = v;
+        fp.v = k;
+        fp.a = log_decay;
+        fp.lam = lambda;
+        fp.BH = (int)BH;
+        fp.T = T;
+        fp.dk = dv;
+        fp.dv = dk;
+        fp.L = L;
+        fp.C = C;
+        fp.N = N;
+        fp.nscan = N - 1;
+        fp.ust = reinterpret_cast<float*>(base + w.nodes.ust_off);
+        fp.tot = reinterpret_cast<float*>(base + w.nodes.tot_off);
+        fp.cum = reinterpret_cast<double*>(base + w.nodes.cum_off);
+        hipError_t e = launch_fwd_chunked(fp, in_dtype == LOGLIN_BF16, kStageChunkState | kStageScan, hs);
+        if (e != hipSuccess) return hip_fail(e, "loglin_bwd_chunked node launch");
+        bp.gnode = fp.ust;
+        bp.cum = fp.cum;
+        bp.rst = reinterpret_cast<float*>(base + w.rst_off);
+        bp.rstT = reinterpret_cast<float*>(base + w.rstT_off);
+    }
+    hipError_t e = launch_bwd_chunked(bp, in_dtype == LOGLIN_BF16, hs);
+    if (e != hipSuccess) return hip_fail(e, "loglin_bwd_chunked launch");
+    return ok();
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
 // decode state
 
 struct loglin_state {

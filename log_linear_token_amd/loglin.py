@@ -77,6 +77,10 @@ def _load():
     lib.loglin_state_export.restype = i
     lib.loglin_decode_step.argtypes = [vp, vp, vp, vp, vp, vp, vp, i, vp]
     lib.loglin_decode_step.restype = i
+    lib.loglin_bwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.loglin_bwd_workspace_bytes.restype = sz
+    lib.loglin_bwd_chunked.argtypes = [vp] * 11 + [i] * 8 + [vp, sz, vp]
+    lib.loglin_bwd_chunked.restype = i
     lib.loglin_prefill_workspace_bytes.argtypes = [i, i, i, i, i, i]
     lib.loglin_prefill_workspace_bytes.restype = sz
     lib.loglin_prefill_states.argtypes = [vp, vp, vp, vp, i, i, i, i, i, i, i, vp, sz, vp]
@@ -186,6 +190,48 @@ def loglin_fwd_chunked_stages(q, k, v, log_decay, lam, C: int, stage_mask: int, 
     _check(_load().loglin_fwd_chunked_stages(pq, pk, pv, pa, pl, po, B, H, T, dk, dv, L, C,
                                              _DTYPES[q.dtype], pw, nws, stage_mask, _stream(q)))
     return out
+
+
+# ---------------------------------------------------------------- backward
+
+def loglin_bwd_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, C: int,
+                               dtype=torch.bfloat16) -> int:
+    n = _load().loglin_bwd_workspace_bytes(B, H, T, dk, dv, C, _dt_code(dtype))
+    if n == ctypes.c_size_t(-1).value:
+        raise LoglinError(LOGLIN_EINVAL, loglin_last_error())
+    return n
+
+
+def loglin_bwd_chunked(q, k, v, log_decay, lam, dout, C: int, grads=None, workspace=None):
+    """Gradients of sum(O * dout) for O = loglin_fwd_chunked(q, k, v, log_decay, lam, C).
+
+    dout [B,H,T,dv] in the dtype of q.  Returns (dq, dk, dv, dlog_decay,
+    dlam), all float32, shaped like q, k, v, log_decay and lam; `grads`
+    may pass those five tensors in to be written.
+    """
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"q must be float32 or bfloat16 (got {q.dtype})")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    L = lam.shape[-1]
+    ptrs = [_dev(q, "q", q.dtype), _dev(k, "k", q.dtype, (B, H, T, dk)),
+            _dev(v, "v", q.dtype, (B, H, T, dv)),
+            _dev(log_decay, "log_decay", torch.float32, (B, H, T)),
+            _dev(lam, "lam", torch.float32, (B, H, T, L)),
+            _dev(dout, "dout", q.dtype, (B, H, T, dv))]
+    shapes = [(B, H, T, dk), (B, H, T, dk), (B, H, T, dv), (B, H, T), (B, H, T, L)]
+    names = ["dq", "dk", "dv", "dlog_decay", "dlam"]
+    if grads is None:
+        grads = tuple(torch.empty(sh, dtype=torch.float32, device=q.device) for sh in shapes)
+    ptrs += [_dev(g, n, torch.float32, sh) for g, n, sh in zip(grads, names, shapes)]
+    need = loglin_bwd_workspace_bytes(B, H, T, dk, dv, C, q.dtype)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    pw = _dev(workspace, "workspace") if workspace is not None else None
+    nws = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_load().loglin_bwd_chunked(*ptrs, B, H, T, dk, dv, L, C, _DTYPES[q.dtype], pw, nws,
+                                      _stream(q)))
+    return tuple(grads)
 
 
 # ---------------------------------------------------------------- prefill -> decode

@@ -38,6 +38,9 @@ def lib():
     lib.loglin_prefill_workspace_bytes.argtypes = [i] * 6
     lib.loglin_prefill_workspace_bytes.restype = sz
     lib.loglin_prefill_states.argtypes = [vp] * 4 + [i] * 7 + [vp, sz, vp]
+    lib.loglin_bwd_workspace_bytes.argtypes = [i] * 7
+    lib.loglin_bwd_workspace_bytes.restype = sz
+    lib.loglin_bwd_chunked.argtypes = [vp] * 11 + [i] * 8 + [vp, sz, vp]
     lib.loglin_last_error.restype = ctypes.c_char_p
     lib.loglin_status_string.restype = ctypes.c_char_p
     return lib
@@ -48,7 +51,8 @@ def test_header_declares_the_entry_points():
     for n in ["loglin_fwd_chunked", "loglin_fwd_workspace_bytes", "loglin_decode_step",
               "loglin_state_init", "loglin_state_free", "loglin_state_load",
               "loglin_state_export", "loglin_debug_level_map", "loglin_last_error",
-              "loglin_prefill_states", "loglin_prefill_workspace_bytes"]:
+              "loglin_prefill_states", "loglin_prefill_workspace_bytes",
+              "loglin_bwd_chunked", "loglin_bwd_workspace_bytes"]:
         assert n in names
 
 
@@ -230,3 +234,50 @@ def test_prefill_validation(lib):
     assert _prefill(lib, nws=16) == EINVAL                             # workspace too small
     assert _prefill(lib, ws=FAKE + 64) == EINVAL                       # workspace misaligned
     assert _prefill(lib, B=0) == 0                                      # no-op
+
+
+# ---- backward pass: workspace sizes and argument checks (nothing launched)
+
+def _align(x):
+    return (x + 255) // 256 * 256
+
+
+@pytest.mark.parametrize("B,H,T,dk,dv,C", [(1, 1, 1, 16, 16, 16), (1, 2, 37, 16, 32, 16),
+                                           (4, 16, 8192, 128, 64, 64), (1, 16, 65536, 128, 128, 128)])
+def test_bwd_workspace_bytes(lib, B, H, T, dk, dv, C):
+    BH, N = B * H, (T + C - 1) // C
+    want = 0
+    if N > 1:  # nodes, chunk totals, fp64 chunk ends, then R and R^T
+        want = _align(_align(_align(BH * N * dk * dv * 4) + BH * N * 4) + BH * N * 8)
+        want = _align(_align(want + BH * N * dk * dv * 4) + BH * N * dk * dv * 4)
+    want = _align(_align(want + BH * T * 4) + BH * T * 4)
+    assert lib.loglin_bwd_workspace_bytes(B, H, T, dk, dv, C, 1) == want
+    assert lib.loglin_bwd_workspace_bytes(B, H, T, dk, dv, C, 0) == want
+
+
+def _bwd(lib, B=1, H=1, T=64, dk=16, dv=16, L=8, C=16, dtype=1, ws=FAKE * 256, nws=1 << 30,
+         ptrs=None):
+    p = [FAKE] * 11 if ptrs is None else ptrs
+    return lib.loglin_bwd_chunked(*p, B, H, T, dk, dv, L, C, dtype, ws, nws, None)
+
+
+def test_bwd_validation(lib):
+    assert lib.loglin_bwd_workspace_bytes(1, 1, 64, 48, 16, 16, 1) == ctypes.c_size_t(-1).value
+    assert lib.loglin_bwd_workspace_bytes(1, 1, 64, 16, 16, 16, 9) == ctypes.c_size_t(-1).value
+    assert _bwd(lib, C=8) == EUNSUPPORTED
+    assert _bwd(lib, dv=24) == EUNSUPPORTED
+    assert _bwd(lib, T=1000, L=10) == EINVAL          # needs 11 levels
+    assert _bwd(lib, L=65) == EINVAL
+    assert _bwd(lib, dtype=3) == EINVAL
+    for k in range(11):
+        p = [FAKE] * 11
+        p[k] = None
+        assert _bwd(lib, ptrs=p) == EINVAL, k
+    p = [FAKE] * 11
+    p[5] = FAKE + 8                                     # dout misaligned
+    assert _bwd(lib, ptrs=p) == EINVAL
+    assert _bwd(lib, nws=16) == EINVAL                  # workspace too small
+    assert b"workspace" in lib.loglin_last_error()
+    assert _bwd(lib, ws=None) == EINVAL
+    assert _bwd(lib, ws=FAKE * 256 + 64) == EINVAL      # workspace misaligned
+    assert _bwd(lib, B=0) == 0 and _bwd(lib, T=0, ws=None, nws=0) == 0

@@ -1,0 +1,96 @@
+"""GPU parity of the backward pass against the fp64 oracle's gradients.
+
+Page: "Log-linear attention, and what a logarithm buys", section 3 (the mixer
+is trained through the same chunked form, forward and backward) and section 6
+(the lambda gradients are derived by hand).  Every gradient -- dq, dk, dv,
+the decay gradient and dlambda -- is compared element by element with
+oracle.reference.form_a_grads on the same seeded inputs, over single chunks,
+ragged tails, every chunk size and head-dim mix, and several coarse levels.
+"""
+import numpy as np
+import pytest
+import torch
+
+from log_linear_token_amd import loglin as LL
+from oracle import reference as ref
+from tests.helpers import TOL_BF16, TOL_F32, banner, slice_rel_err, to_dev
+
+pytestmark = pytest.mark.gpu
+
+NAMES = ["dq", "dk", "dv", "dlog_decay", "dlam"]
+
+
+def _inputs(B, H, T, dk, dv, L, seed, mu=-1.0):
+    rng = np.random.default_rng(seed)
+    q = rng.standard_normal((B, H, T, dk)) / np.sqrt(dk)
+    k = rng.standard_normal((B, H, T, dk)) / np.sqrt(dk)
+    v = rng.standard_normal((B, H, T, dv))
+    g = rng.standard_normal((B, H, T, dv))
+    a = (-np.logaddexp(0, rng.normal(mu, 0.5, (B, H, T)))).astype(np.float32).astype(np.float64)
+    lam = rng.random((B, H, T, L)).astype(np.float32).astype(np.float64)
+    return q, k, v, a, lam, g
+
+
+def _round(x, dtype):
+    return to_dev(x, dtype).float().cpu().numpy().astype(np.float64)
+
+
+def _check(B, H, T, dk, dv, C, dtype, L=None, seed=0, mu=-1.0):
+    L = L or max(1, (T - 1).bit_length() + 1)
+    q, k, v, a, lam, g = _inputs(B, H, T, dk, dv, L, seed, mu)
+    dev = [to_dev(x, dtype) for x in (q, k, v)]
+    got = LL.loglin_bwd_chunked(*dev, to_dev(a), to_dev(lam), to_dev(g, dtype), C)
+    got = [x.cpu().numpy() for x in got]
+    want = ref.form_a_grads(*(_round(x, dtype) for x in (q, k, v)), a, lam, _round(g, dtype))
+    tol = TOL_F32 if dtype == torch.float32 else TOL_BF16
+    errs = {}
+    for n, x, y in zip(NAMES, got, want):
+        errs[n] = slice_rel_err(x, y, 2)
+    print("  " + " ".join(f"{n} {e:.2e}" for n, e in errs.items()), flush=True)
+    for n, e in errs.items():
+        assert e <= tol, (n, e)
+    return got
+
+
+CASES = [
+    # B, H, T, dk, dv, C, dtype: one token, one ragged chunk, exact chunks,
+    # many coarse levels, every chunk size, mixed head dims
+    (1, 2, 1, 16, 16, 16, torch.float32),
+    (1, 2, 37, 16, 32, 16, torch.float32),
+    (1, 1, 64, 32, 16, 16, torch.float32),
+    (2, 1, 200, 64, 64, 32, torch.float32),
+    (1, 2, 300, 32, 64, 64, torch.float32),
+    (1, 1, 513, 128, 128, 128, torch.float32),
+    (1, 2, 130, 16, 16, 16, torch.bfloat16),
+    (2, 2, 1000, 64, 64, 64, torch.bfloat16),
+    (1, 2, 777, 128, 64, 64, torch.bfloat16),
+    (1, 1, 1100, 64, 128, 32, torch.bfloat16),
+    (1, 1, 2048, 128, 128, 128, torch.bfloat16),
+]
+
+
+@pytest.mark.parametrize("B,H,T,dk,dv,C,dtype", CASES)
+def test_bwd_vs_oracle(B, H, T, dk, dv, C, dtype):
+    banner(f"bwd B={B} H={H} T={T} dk={dk} dv={dv} C={C} {dtype}")
+    _check(B, H, T, dk, dv, C, dtype, seed=T + dk + C)
+
+
+def test_bwd_extra_levels_get_zero():
+    """lambda with more levels than the sequence uses: those get no gradient."""
+    banner("bwd extra levels")
+    got = _check(1, 1, 100, 16, 16, 16, torch.float32, L=12, seed=5)
+    assert not np.any(got[4][..., 8:])
+
+
+def test_bwd_long_memory_head_shape():
+    """The long-memory decay and head shape of the 8K-token workload, one head."""
+    banner("bwd T=4096 dk=128 dv=64 C=64 bf16 long memory")
+    _check(1, 1, 4096, 128, 64, 64, torch.bfloat16, seed=9, mu=-2.0)
+
+
+def test_bwd_empty_is_noop():
+    banner("bwd T=0")
+    z = torch.empty((1, 1, 0, 16), device="cuda")
+    out = LL.loglin_bwd_chunked(z, z, z, torch.empty((1, 1, 0), device="cuda"),
+                                torch.empty((1, 1, 0, 4), device="cuda"), z, 16)
+    assert all(x.numel() == 0 for x in out)
