@@ -242,6 +242,7 @@ def main() -> int:
     ap.add_argument("--decode-steps", type=int, default=256)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-backward", action="store_true")
     ap.add_argument("--no-other", action="store_true",
                     help="skip the 2K and 64K forward workloads")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -333,6 +334,8 @@ def main() -> int:
         "plan": plan,
     }
     result["prefill_states"] = bench_prefill(cfg, sets, stream, args.steps)
+    if not args.no_backward:
+        result["backward"] = bench_backward(cfg, sets, stream, max(5, args.steps // 4))
     del q, k, v, a, lam, ws, sets, fwd
     torch.cuda.empty_cache()
 
@@ -424,6 +427,63 @@ def bench_prefill(cfg, sets, stream, steps: int) -> dict:
     log(f"prefill states: {ms:.3f} ms, {gbs:.0f} GB/s")
     return {"ms": ms, "alg_bytes": byts, "GB/s": round(gbs, 1),
             "frac_hbm": round(gbs / HBM_PEAK_GBS, 4)}
+
+
+def bwd_model(cfg) -> dict:
+    """Algorithmic bytes and flops of one backward pass.
+
+    Bytes: q, k, v and dO read once (input dtype), a and the lu levels of
+    lambda read once, dq, dk, dv, da and the lu levels of dlambda written
+    once (fp32); the carried states (the swapped chunk states and their nodes,
+    the R states) are not counted: a pass that kept them on chip would not
+    move them.  Flops: per chunk the five C x C products of the causal block
+    (scores, dP, and the dq, dk, dv contractions), full tiles, plus per chunk
+    the swapped chunk state and one state product per coarse level a chunk
+    reads (dq) or feeds (dk, dv, R)."""
+    B, H, T, dk, dv, C = cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv, cfg.C
+    lu = (T - 1).bit_length() + 1
+    per_tok = 2 * (2 * dk + 2 * dv) + 4 + 4 * lu + 4 * (2 * dk + dv) + 4 + 4 * lu
+    byts = B * H * T * per_tok
+    N = T // C
+    coarse = sum(bin(i).count("1") for i in range(N))  # node reads of dq, and R feeds of dk/dv
+    intra = N * 2 * C * C * (3 * dk + 2 * dv)  # Q K^T, dO V^T, dq, dk (over dk); dv (over dv)
+    states = N * 2 * C * dk * dv * 2 + coarse * 2 * C * dk * dv * 4  # G', R; dq, dk, dv reads
+    return {"bytes": byts, "flops": B * H * (intra + states)}
+
+
+def bench_backward(cfg, sets, stream, steps: int) -> dict:
+    """The backward pass on the 8K workload: dq, dk, dv, the decay and lambda
+    gradients, rotating through the forward's input copies."""
+    B, H, T, dk, dv = cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv
+    ws = torch.empty(LL.loglin_bwd_workspace_bytes(B, H, T, dk, dv, cfg.C, torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+    gen = torch.Generator(device="cuda")
+    gen.manual_seed(cfg.seed + 1)
+    douts = [torch.randn((B, H, T, dv), device="cuda", generator=gen).to(torch.bfloat16)
+             for _ in sets]
+    grads = [torch.empty((B, H, T, dk), device="cuda"), torch.empty((B, H, T, dk), device="cuda"),
+             torch.empty((B, H, T, dv), device="cuda"), torch.empty((B, H, T), device="cuda"),
+             torch.empty((B, H, T, cfg.L), device="cuda")]
+    state = {"i": 0}
+
+    def run():
+        j = state["i"] % len(sets)
+        qq, kk, vv, aa, ll, _ = sets[j]
+        state["i"] += 1
+        LL.loglin_bwd_chunked(qq, kk, vv, aa, ll, douts[j], cfg.C, grads=grads, workspace=ws)
+
+    for _ in range(10):
+        run()
+    ms = timed(run, steps, stream)
+    m = bwd_model(cfg)
+    gbs = m["bytes"] / (ms / 1e3) / 1e9
+    tfl = m["flops"] / (ms / 1e3) / 1e12
+    tps = B * T / (ms / 1e3)
+    log(f"backward: {ms:.3f} ms, {tps:.3e} tokens/s, {gbs:.0f} GB/s, {tfl:.0f} TFLOP/s")
+    del ws, douts, grads
+    return {"ms": ms, "tokens_per_s": tps, "alg_bytes": m["bytes"], "alg_flops": m["flops"],
+            "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+            "TFLOP/s": round(tfl, 1), "frac_mfma": round(tfl / BF16_PEAK_TFLOPS, 4)}
 
 
 def bench_decode(steps: int) -> dict:

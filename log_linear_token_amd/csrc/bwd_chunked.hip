@@ -34,6 +34,7 @@
 // Workspace (per (batch*head) bh): the forward's node buffers for G', R and
 // R^T ([N][dk][dv] and [N][dv][dk] fp32, R at the index j of the block's
 // first chunk), and the two dot products per token.
+#include <algorithm>
 #include <type_traits>
 
 #include "chunk_stage.hpp"
@@ -55,6 +56,9 @@ struct BStep<float> {
     static constexpr int KS = 4;
 };
 
+// Coarse levels a chunk can have: bit_length(N - 1) for N < 2^31 chunks.
+constexpr int kMaxLev = 32;
+
 template <int C>
 struct LogC {
     static constexpr int v = C == 16 ? 4 : C == 32 ? 5 : C == 64 ? 6 : 7;
@@ -74,17 +78,20 @@ __device__ __forceinline__ typename Frag<E, BStep<E>::KS>::type rows_op(const E*
     }
 }
 
-// B operand of the lane's own token row (row n = lane % 16), step ks
+// B operand of the lane's own token row (row n = lane % 16), step ks; zero
+// unless ok.  `row` must be readable either way: the load is unconditional,
+// so that a run of these loads has no branch between them.
 template <typename E>
 __device__ __forceinline__ typename Frag<E, BStep<E>::KS>::type own_op(const E* row, bool ok, int ks,
                                                                        int g) {
     typedef typename Frag<E, BStep<E>::KS>::type frag_t;
-    if (!ok) return frag_t{};
+    frag_t x;
     if constexpr (sizeof(E) == 2) {
-        return Frag<E, 16>::load(row + ks * 16 + 4 * g);
+        x = Frag<E, 16>::load(row + ks * 16 + 4 * g);
     } else {
-        return row[ks * 4 + g];
+        x = row[ks * 4 + g];
     }
+    return ok ? x : frag_t{};
 }
 
 // the C-layout tile (4 values of column m) as the B operand of the next product
@@ -128,12 +135,14 @@ __device__ __forceinline__ float load_f32(const bf16_t* p) { return bf16_to_f32(
 // dq and dlambda: one block per chunk, one wave per 16 query rows
 
 template <typename E, int C, int DM>
-__global__ __launch_bounds__(C / 16 * 64) void k_bwd_dq(BwdParams p) {
+__global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_dq(BwdParams p) {
     constexpr int NW = C / 16;
+    constexpr int NT = NW * kWave;
     constexpr int LOGC = LogC<C>::v;
     constexpr int KS = BStep<E>::KS;
     constexpr int MAXK = DM / KS;
     constexpr int NB = DM / 16;
+    constexpr int NLC = C * kMaxLev / NT;  // coarse lambda values staged per thread
     typedef Frag<E, KS> FR;
     typedef typename FR::type frag_t;
     constexpr int KPL = FR::kpl;
@@ -145,31 +154,20 @@ __global__ __launch_bounds__(C / 16 * 64) void k_bwd_dq(BwdParams p) {
     const int i = blk - bh * p.N;
     const int t0 = i * C;
     const int nvalid = min(C, p.T - t0);
-    const int dk = p.dk, dv = p.dv;
+    const int dk = p.dk, dv = p.dv, L = p.L, nlev = p.nlev;
     const int nkk = dk / KS, nkv = dv / KS;
     float* a_raw = reinterpret_cast<float*>(smem);
     float* A = a_raw + C;
-    E* KT = reinterpret_cast<E*>(A + C);       // [dk][C + kPadT]
+    float* dlog = A + C;                       // [kMaxLev] A(end of chunk i-1) - A(node) per set bit
+    float* lamco = dlog + kMaxLev;             // [C][nlev] lambda of the coarse levels
+    E* KT = reinterpret_cast<E*>(lamco + C * nlev);  // [dk][C + kPadT]
     E* X1 = KT + dk * (C + kPadT);             // bf16: K natural; fp32: V transposed
     E* X2 = X1 + (NAT ? C * (dk + kPadK) : 0); // bf16: V natural
+    E* Gs = X2 + (NAT ? C * (dv + kPadK) : 0); // bf16: one carried state, p.st_elems elements
     const E* Kn = X1;
     const E* Vn = X2;
     const E* VT = X1;
     const size_t row0 = (size_t)bh * p.T + t0;
-
-    for (int s = threadIdx.x; s < C; s += blockDim.x) a_raw[s] = s < nvalid ? p.a[row0 + s] : 0.f;
-    const E* kg = static_cast<const E*>(p.k) + row0 * dk;
-    const E* vg = static_cast<const E*>(p.v) + row0 * dv;
-    stage_transposed<E, C>(kg, dk, nvalid, KT, nullptr);
-    if constexpr (NAT) {
-        stage_natural<E, C>(kg, dk, nvalid, X1);
-        stage_natural<E, C>(vg, dv, nvalid, X2);
-    } else {
-        stage_transposed<E, C>(vg, dv, nvalid, X1, nullptr);
-    }
-    __syncthreads();
-    if (threadIdx.x < kWave) wave_cumsum(a_raw, A, C);
-    __syncthreads();
 
     const int lane = threadIdx.x & (kWave - 1);
     const int R = threadIdx.x / kWave;
@@ -177,19 +175,67 @@ __global__ __launch_bounds__(C / 16 * 64) void k_bwd_dq(BwdParams p) {
     const int r = 16 * R + m;
     const bool rvalid = r < nvalid;
     const size_t trow = row0 + r;
-    const E* qrow = static_cast<const E*>(p.q) + trow * dk;
-    const E* orow = static_cast<const E*>(p.dout) + trow * dv;
+    const size_t lrow0 = row0 + (rvalid ? r : 0);  // the row the loads read (row t0 past T)
 
+    // Every global load of the prologue is issued before the first LDS
+    // write, without branches, so that they are all in flight together:
+    // the lane's own dO and q fragments and lambda, the chunk's a, K and V,
+    // and the scalars of the coarse levels.
+    const E* qrow = static_cast<const E*>(p.q) + lrow0 * dk;
+    const E* orow = static_cast<const E*>(p.dout) + lrow0 * dv;
     frag_t df[MAXK], qf[MAXK];
 #pragma unroll
     for (int ks = 0; ks < MAXK; ++ks) {
         df[ks] = ks < nkv ? own_op<E>(orow, rvalid, ks, g) : frag_t{};
         qf[ks] = ks < nkk ? own_op<E>(qrow, rvalid, ks, g) : frag_t{};
     }
-    const float* lrow = p.lam + trow * p.L;
+    const float* lrow = p.lam + lrow0 * L;
     float lamr[LOGC + 1];
 #pragma unroll
-    for (int l = 0; l <= LOGC; ++l) lamr[l] = (rvalid && l < p.L) ? lrow[l] : 0.f;
+    for (int l = 0; l <= LOGC; ++l) {
+        const float x = lrow[min(l, L - 1)];
+        lamr[l] = (rvalid && l < L) ? x : 0.f;
+    }
+    const float av = p.a[row0 + min((int)threadIdx.x, nvalid - 1)];
+    float lco[NLC];
+#pragma unroll
+    for (int u = 0; u < NLC; ++u) {
+        const int idx = threadIdx.x + u * NT;
+        const int rr = nlev > 0 ? idx / nlev : 0, pb = idx - rr * nlev;
+        const size_t row = row0 + min(rr, nvalid - 1);
+        lco[u] = p.lam[row * L + min(LOGC + 1 + pb, L - 1)];
+    }
+    float dl0 = 0.f;
+    if (threadIdx.x < nlev) {  // at most one load per thread
+        const int pb = threadIdx.x;
+        const bool set = (i >> pb) & 1;
+        const int node = set ? ((i >> pb) << pb) - 1 : 0;
+        const double* cum = p.cum + (size_t)bh * p.N;
+        const double ce = cum[set ? i - 1 : 0];  // set implies i >= 1
+        dl0 = set ? (float)(ce - cum[node]) : 0.f;
+    }
+    const E* kg = static_cast<const E*>(p.k) + row0 * dk;
+    const E* vg = static_cast<const E*>(p.v) + row0 * dv;
+    ChunkRows<E, C, DM, NT> kr, vr;
+    kr.load(kg, dk, nvalid);
+    vr.load(vg, dv, nvalid);
+
+    if (threadIdx.x < C) a_raw[threadIdx.x] = (int)threadIdx.x < nvalid ? av : 0.f;
+    if (threadIdx.x < nlev) dlog[threadIdx.x] = dl0;
+#pragma unroll
+    for (int u = 0; u < NLC; ++u) {
+        const int idx = threadIdx.x + u * NT;
+        if (idx < C * nlev) lamco[idx] = lco[u];
+    }
+    kr.store(dk, NAT ? X1 : nullptr, KT, nullptr);
+    if constexpr (NAT) {
+        vr.store(dv, X2, nullptr, nullptr);
+    } else {
+        vr.store(dv, nullptr, X1, nullptr);
+    }
+    __syncthreads();
+    if (threadIdx.x < kWave) wave_cumsum(a_raw, A, C);
+    __syncthreads();
     const float Ar = A[r];
 
     // the chunk's own block: dS = dO V^T and Q K^T for the keys s <= r
@@ -222,9 +268,24 @@ __global__ __launch_bounds__(C / 16 * 64) void k_bwd_dq(BwdParams p) {
         }
     }
 
+    // q in the C layout of the dq tiles (column 16 cb + 4 g + j of row r):
+    // for bf16 exactly the elements of the lane's own q fragments
+    float qv[NB][4];
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if constexpr (NAT) {
+                qv[cb][j] = 16 * cb < dk ? (float)qf[cb][j] : 0.f;
+            } else {
+                const float x = qrow[16 * cb < dk ? 16 * cb + 4 * g + j : 0];
+                qv[cb][j] = (rvalid && 16 * cb < dk) ? x : 0.f;
+            }
+        }
+    }
+
     // dq^T column blocks: K^T Z^T, then one term per coarse level
     f32x4 acc[NB];
-    float qv[NB][4];
 #pragma unroll
     for (int cb = 0; cb < NB; ++cb) {
         acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -233,32 +294,55 @@ __global__ __launch_bounds__(C / 16 * 64) void k_bwd_dq(BwdParams p) {
             for (int S = 0; S < NW; ++S)
                 if (S <= R) acc[cb] = mma_hand<E, C>(KT, 16 * cb, S, Z[S], acc[cb], m, g);
         }
-#pragma unroll
-        for (int j = 0; j < 4; ++j)
-            qv[cb][j] = (rvalid && 16 * cb < dk) ? load_f32(qrow + 16 * cb + 4 * g + j) : 0.f;
     }
-    const double* cum = p.cum + (size_t)bh * p.N;
-    float* glrow = p.glam + trow * p.L;
+    float* glrow = p.glam + trow * L;
     for (int pb = 0; (i >> pb) != 0; ++pb) {
         if (!((i >> pb) & 1)) continue;
         const int node = ((i >> pb) << pb) - 1;
         const int lev = LOGC + pb + 1;
-        const float e = rvalid ? __expf(Ar + (float)(cum[i - 1] - cum[node])) : 0.f;
-        const float lw = rvalid ? lrow[lev] * e : 0.f;
+        const float e = rvalid ? __expf(Ar + dlog[pb]) : 0.f;
+        const float lw = e * lamco[r * nlev + pb];
         const float* G = p.gnode + ((size_t)bh * p.N + node) * dk * dv;
         float dot = 0.f;
+        if constexpr (NAT) {
+            // the node goes through LDS as bf16, staged once for all waves,
+            // in rounds of srows of its dk rows
+            const int pitch = dv + kPadK;
+            const int srows = min(dk, (p.st_elems / pitch) & ~15);
+            for (int r0 = 0; r0 < dk; r0 += srows) {
+                __syncthreads();  // the previous round's reads are done
+                stage_state_bf16<NT>(G, dv, r0, min(srows, dk - r0), Gs);
+                __syncthreads();
 #pragma unroll
-        for (int cb = 0; cb < NB; ++cb) {
-            if (16 * cb < dk) {
-                f32x4 y = {0.f, 0.f, 0.f, 0.f};
-                const float* grow = G + (size_t)(16 * cb + m) * dv + g * KPL;
+                for (int cb = 0; cb < NB; ++cb) {
+                    if (16 * cb < dk && 16 * cb >= r0 && 16 * cb < r0 + srows) {
+                        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+                        const E* grow = Gs + (16 * cb - r0 + m) * pitch + 4 * g;
 #pragma unroll
-                for (int ks = 0; ks < MAXK; ++ks)
-                    if (ks < nkv) y = mma(FR::from_f32(grow + ks * KS), df[ks], y);
+                        for (int ks = 0; ks < MAXK; ++ks)
+                            if (ks < nkv) y = mma(Frag<bf16_t, 16>::load(grow + ks * 16), df[ks], y);
 #pragma unroll
-                for (int j = 0; j < 4; ++j) {
-                    acc[cb][j] += lw * y[j];
-                    dot += qv[cb][j] * y[j];
+                        for (int j = 0; j < 4; ++j) {
+                            acc[cb][j] += lw * y[j];
+                            dot += qv[cb][j] * y[j];
+                        }
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb) {
+                if (16 * cb < dk) {
+                    f32x4 y = {0.f, 0.f, 0.f, 0.f};
+                    const float* grow = G + (size_t)(16 * cb + m) * dv + g * KPL;
+#pragma unroll
+                    for (int ks = 0; ks < MAXK; ++ks)
+                        if (ks < nkv) y = mma(FR::from_f32(grow + ks * KS), df[ks], y);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        acc[cb][j] += lw * y[j];
+                        dot += qv[cb][j] * y[j];
+                    }
                 }
             }
         }
@@ -285,8 +369,8 @@ __global__ __launch_bounds__(C / 16 * 64) void k_bwd_dq(BwdParams p) {
         p.dA1[trow] = da1;
 #pragma unroll
         for (int l = 0; l <= LOGC; ++l)
-            if (l < p.L) glrow[l] = dl[l];
-        for (int l = LOGC + 1; l < p.L; ++l) {
+            if (l < L) glrow[l] = dl[l];
+        for (int l = LOGC + 1; l < L; ++l) {
             const int pb = l - LOGC - 1;
             if (pb >= 31 || !((i >> pb) & 1)) glrow[l] = 0.f;  // a level this row does not reach
         }
@@ -296,9 +380,10 @@ __global__ __launch_bounds__(C / 16 * 64) void k_bwd_dq(BwdParams p) {
 // --------------------------------------------------------------------------
 // R(j): the lambda-weighted state of the block of chunks that starts at
 // chunk j, for the keys of its left sibling.  Blocks are taken largest first.
+// The loads of chunk c + 1 are issued before the products of chunk c.
 
-template <typename E, int C>
-__global__ __launch_bounds__(256) void k_bwd_rstate(BwdParams p) {
+template <typename E, int C, int DM>
+__global__ __launch_bounds__(256, 2) void k_bwd_rstate(BwdParams p) {
     constexpr int LOGC = LogC<C>::v;
     constexpr int MAXT = 16;  // tiles of 16 x 16 per wave: (128 / 16)^2 / 4 waves
     extern __shared__ __align__(16) char smem[];
@@ -319,15 +404,17 @@ __global__ __launch_bounds__(256) void k_bwd_rstate(BwdParams p) {
     const int jend = min(j + (1 << lev), p.N);
     const int lidx = LOGC + lev + 1;
     const int dk = p.dk, dv = p.dv;
+    const int tid = threadIdx.x;
     float* a_raw = reinterpret_cast<float*>(smem);
     float* Al = a_raw + C;
     float* e = Al + C;
     E* QT = reinterpret_cast<E*>(e + C);   // [dk][C + kPadT], scaled rows
     E* OT = QT + dk * (C + kPadT);         // [dv][C + kPadT]
     const double* cum = p.cum + (size_t)bh * p.N;
+    const double cj = cum[j - 1];
 
-    const int lane = threadIdx.x & (kWave - 1);
-    const int wave = threadIdx.x / kWave;
+    const int lane = tid & (kWave - 1);
+    const int wave = tid / kWave;
     const int nw = blockDim.x / kWave;
     const int m = lane & 15, g = lane >> 4;
     const int ncv = dv / 16;
@@ -336,22 +423,35 @@ __global__ __launch_bounds__(256) void k_bwd_rstate(BwdParams p) {
 #pragma unroll
     for (int u = 0; u < MAXT; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 
+    // a chunk's loads, all branch-free: a and lambda of the token of this
+    // thread (rows past T read the chunk's first row), A at the end of the
+    // previous chunk, and the chunk's q and dO rows
+    ChunkRows<E, C, DM, 256> qr, orr;
+    float av, lv, base;
+    auto load = [&](int c) __attribute__((always_inline)) {
+        const int nvalid = min(C, p.T - c * C);
+        const size_t row0 = (size_t)bh * p.T + (size_t)c * C;
+        const size_t rr = row0 + min(tid % C, nvalid - 1);
+        av = p.a[rr];
+        lv = p.lam[rr * p.L + lidx];
+        base = (float)(cum[c - 1] - cj);
+        qr.load(static_cast<const E*>(p.q) + row0 * dk, dk, nvalid);
+        orr.load(static_cast<const E*>(p.dout) + row0 * dv, dv, nvalid);
+    };
+    load(j);
     for (int c = j; c < jend; ++c) {
-        const int t0 = c * C;
-        const int nvalid = min(C, p.T - t0);
-        const size_t row0 = (size_t)bh * p.T + t0;
+        const int nvalid = min(C, p.T - c * C);
         __syncthreads();  // the previous chunk's operands are consumed
-        for (int s = threadIdx.x; s < C; s += blockDim.x) a_raw[s] = s < nvalid ? p.a[row0 + s] : 0.f;
+        if (tid < C) a_raw[tid] = tid < nvalid ? av : 0.f;
         __syncthreads();
-        if (threadIdx.x < kWave) wave_cumsum(a_raw, Al, C);
+        if (tid < kWave) wave_cumsum(a_raw, Al, C);
         __syncthreads();
-        const float base = (float)(cum[c - 1] - cum[j - 1]);
-        for (int s = threadIdx.x; s < C; s += blockDim.x)
-            e[s] = s < nvalid ? p.lam[(row0 + s) * p.L + lidx] * __expf(base + Al[s]) : 0.f;
+        if (tid < C) e[tid] = tid < nvalid ? lv * __expf(base + Al[tid]) : 0.f;
         __syncthreads();
-        stage_transposed<E, C>(static_cast<const E*>(p.q) + row0 * dk, dk, nvalid, QT, e);
-        stage_transposed<E, C>(static_cast<const E*>(p.dout) + row0 * dv, dv, nvalid, OT, nullptr);
+        qr.store(dk, nullptr, QT, e);
+        orr.store(dv, nullptr, OT, nullptr);
         __syncthreads();
+        if (c + 1 < jend) load(c + 1);
 #pragma unroll
         for (int u = 0; u < MAXT; ++u) {
             const int tile = wave + u * nw;
@@ -391,7 +491,7 @@ __global__ __launch_bounds__(256) void k_bwd_rstate(BwdParams p) {
 // dk and dv: one block per chunk, one wave per 16 key rows
 
 template <typename E, int C, int DM>
-__global__ __launch_bounds__(C / 16 * 64) void k_bwd_dkv(BwdParams p) {
+__global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_dkv(BwdParams p) {
     constexpr int NW = C / 16;
     constexpr int LOGC = LogC<C>::v;
     constexpr int KS = BStep<E>::KS;
@@ -408,33 +508,20 @@ __global__ __launch_bounds__(C / 16 * 64) void k_bwd_dkv(BwdParams p) {
     const int i = blk - bh * p.N;
     const int t0 = i * C;
     const int nvalid = min(C, p.T - t0);
-    const int dk = p.dk, dv = p.dv;
+    const int dk = p.dk, dv = p.dv, L = p.L, nlev = p.nlev;
     const int nkk = dk / KS, nkv = dv / KS;
+    constexpr int NT = NW * kWave;
+    constexpr int NLM = (C * (LOGC + 1) + NT - 1) / NT;  // intra-chunk lambda values per thread
     float* a_raw = reinterpret_cast<float*>(smem);
     float* A = a_raw + C;
-    float* lamc = A + C;                          // [C][LOGC + 1]
+    float* wlog = A + C;                          // [kMaxLev] A(end of block j - 1) - A(end of chunk i - 1)
+    float* lamc = wlog + kMaxLev;                 // [C][LOGC + 1]
     E* QT = reinterpret_cast<E*>(lamc + C * (LOGC + 1));  // [dk][C + kPadT]
     E* OT = QT + dk * (C + kPadT);                // [dv][C + kPadT]
     E* Qn = OT + dv * (C + kPadT);                // bf16: [C][dk + kPadK]
     E* On = Qn + (NAT ? C * (dk + kPadK) : 0);    // bf16: [C][dv + kPadK]
+    E* Ss = On + (NAT ? C * (dv + kPadK) : 0);    // bf16: one carried state, p.st_elems elements
     const size_t row0 = (size_t)bh * p.T + t0;
-
-    for (int s = threadIdx.x; s < C; s += blockDim.x) a_raw[s] = s < nvalid ? p.a[row0 + s] : 0.f;
-    for (int x = threadIdx.x; x < C * (LOGC + 1); x += blockDim.x) {
-        const int t = x / (LOGC + 1), l = x - t * (LOGC + 1);
-        lamc[x] = (t < nvalid && l < p.L) ? p.lam[(row0 + t) * p.L + l] : 0.f;
-    }
-    const E* qg = static_cast<const E*>(p.q) + row0 * dk;
-    const E* og = static_cast<const E*>(p.dout) + row0 * dv;
-    stage_transposed<E, C>(qg, dk, nvalid, QT, nullptr);
-    stage_transposed<E, C>(og, dv, nvalid, OT, nullptr);
-    if constexpr (NAT) {
-        stage_natural<E, C>(qg, dk, nvalid, Qn);
-        stage_natural<E, C>(og, dv, nvalid, On);
-    }
-    __syncthreads();
-    if (threadIdx.x < kWave) wave_cumsum(a_raw, A, C);
-    __syncthreads();
 
     const int lane = threadIdx.x & (kWave - 1);
     const int R = threadIdx.x / kWave;
@@ -442,18 +529,59 @@ __global__ __launch_bounds__(C / 16 * 64) void k_bwd_dkv(BwdParams p) {
     const int s = 16 * R + m;  // key row within the chunk
     const bool svalid = s < nvalid;
     const size_t srow = row0 + s;
-    const E* krow = static_cast<const E*>(p.k) + srow * dk;
-    const E* vrow = static_cast<const E*>(p.v) + srow * dv;
+    const size_t lrow0 = row0 + (svalid ? s : 0);  // the row the loads read (row t0 past T)
+
+    // Every global load of the prologue is issued before the first LDS
+    // write, without branches: the lane's own k and v fragments, the chunk's
+    // a, lambda (intra-chunk levels), Q and dO, and the decays of the coarse
+    // levels.
+    const E* krow = static_cast<const E*>(p.k) + lrow0 * dk;
+    const E* vrow = static_cast<const E*>(p.v) + lrow0 * dv;
     frag_t vf[MAXK], kf[MAXK];
 #pragma unroll
     for (int ks = 0; ks < MAXK; ++ks) {
         vf[ks] = ks < nkv ? own_op<E>(vrow, svalid, ks, g) : frag_t{};
         kf[ks] = ks < nkk ? own_op<E>(krow, svalid, ks, g) : frag_t{};
     }
+    const float av = p.a[row0 + min((int)threadIdx.x, nvalid - 1)];
+    float lm[NLM];
+#pragma unroll
+    for (int u = 0; u < NLM; ++u) {
+        const int x = threadIdx.x + u * NT;
+        const int t = x / (LOGC + 1), l = x - t * (LOGC + 1);
+        const float y = p.lam[(row0 + min(t, nvalid - 1)) * L + min(l, L - 1)];
+        lm[u] = (t < nvalid && l < L) ? y : 0.f;
+    }
+    float wl = 0.f;
+    if (threadIdx.x < nlev) {  // at most two loads per thread
+        const int pb = threadIdx.x;
+        const int j = ((i >> pb) | 1) << pb;
+        const bool use = !((i >> pb) & 1) && j < p.N;
+        const double* cum = p.cum + (size_t)bh * p.N;
+        const double cj = cum[use ? j - 1 : 0];
+        const double ci = cum[i > 0 ? i - 1 : 0];
+        wl = use ? (float)(cj - (i > 0 ? ci : 0.0)) : 0.f;
+    }
+    const E* qg = static_cast<const E*>(p.q) + row0 * dk;
+    const E* og = static_cast<const E*>(p.dout) + row0 * dv;
+    ChunkRows<E, C, DM, NT> qr, orr;
+    qr.load(qg, dk, nvalid);
+    orr.load(og, dv, nvalid);
+
+    if (threadIdx.x < C) a_raw[threadIdx.x] = (int)threadIdx.x < nvalid ? av : 0.f;
+    if (threadIdx.x < nlev) wlog[threadIdx.x] = wl;
+#pragma unroll
+    for (int u = 0; u < NLM; ++u) {
+        const int x = threadIdx.x + u * NT;
+        if (x < C * (LOGC + 1)) lamc[x] = lm[u];
+    }
+    qr.store(dk, NAT ? Qn : nullptr, QT, nullptr);
+    orr.store(dv, NAT ? On : nullptr, OT, nullptr);
+    __syncthreads();
+    if (threadIdx.x < kWave) wave_cumsum(a_raw, A, C);
+    __syncthreads();
     const float As = A[s];
 
-    const double* cum = p.cum + (size_t)bh * p.N;
-    const double ci = i > 0 ? cum[i - 1] : 0.0;
     float da2 = 0.f;
 
     // Two passes, dk then dv, so that only one set of handed-off tiles and
@@ -501,20 +629,44 @@ __global__ __launch_bounds__(C / 16 * 64) void k_bwd_dkv(BwdParams p) {
             if ((i >> pb) & 1) continue;
             const int j = ((i >> pb) | 1) << pb;
             if (j >= p.N) continue;
-            const float w = svalid ? __expf((float)(cum[j - 1] - ci) - As) : 0.f;
+            const float w = svalid ? __expf(wlog[pb] - As) : 0.f;
             const float* Rs = GK ? p.rst + ((size_t)bh * p.N + j) * dk * dv
                                  : p.rstT + ((size_t)bh * p.N + j) * dv * dk;
             const int rpitch = GK ? dv : dk;
+            if constexpr (NAT) {
+                // the state goes through LDS as bf16, staged once for all
+                // waves, in rounds of srows of its rows
+                const int pitch = rpitch + kPadK;
+                const int srows = min(dout_dim, (p.st_elems / pitch) & ~15);
+                for (int r0 = 0; r0 < dout_dim; r0 += srows) {
+                    __syncthreads();  // the previous round's reads are done
+                    stage_state_bf16<NT>(Rs, rpitch, r0, min(srows, dout_dim - r0), Ss);
+                    __syncthreads();
 #pragma unroll
-            for (int cb = 0; cb < NB; ++cb) {
-                if (16 * cb < dout_dim) {
-                    f32x4 y = {0.f, 0.f, 0.f, 0.f};
-                    const float* rr = Rs + (size_t)(16 * cb + m) * rpitch + g * KPL;
+                    for (int cb = 0; cb < NB; ++cb) {
+                        if (16 * cb < dout_dim && 16 * cb >= r0 && 16 * cb < r0 + srows) {
+                            f32x4 y = {0.f, 0.f, 0.f, 0.f};
+                            const E* rr = Ss + (16 * cb - r0 + m) * pitch + 4 * g;
 #pragma unroll
-                    for (int ks = 0; ks < MAXK; ++ks)
-                        if (ks < nkc) y = mma(FR::from_f32(rr + ks * KS), own[ks], y);
+                            for (int ks = 0; ks < MAXK; ++ks)
+                                if (ks < nkc) y = mma(Frag<bf16_t, 16>::load(rr + ks * 16), own[ks], y);
 #pragma unroll
-                    for (int q = 0; q < 4; ++q) acc[cb][q] += w * y[q];
+                            for (int q = 0; q < 4; ++q) acc[cb][q] += w * y[q];
+                        }
+                    }
+                }
+            } else {
+#pragma unroll
+                for (int cb = 0; cb < NB; ++cb) {
+                    if (16 * cb < dout_dim) {
+                        f32x4 y = {0.f, 0.f, 0.f, 0.f};
+                        const float* rr = Rs + (size_t)(16 * cb + m) * rpitch + g * KPL;
+#pragma unroll
+                        for (int ks = 0; ks < MAXK; ++ks)
+                            if (ks < nkc) y = mma(FR::from_f32(rr + ks * KS), own[ks], y);
+#pragma unroll
+                        for (int q = 0; q < 4; ++q) acc[cb][q] += w * y[q];
+                    }
                 }
             }
         }
@@ -523,9 +675,19 @@ __global__ __launch_bounds__(C / 16 * 64) void k_bwd_dkv(BwdParams p) {
         for (int cb = 0; cb < NB; ++cb) {
             if (16 * cb < dout_dim) {
                 if constexpr (GK) {
+                    // k in the C layout of the dk tiles: for bf16 exactly the
+                    // elements of the lane's own k fragments
 #pragma unroll
-                    for (int q = 0; q < 4; ++q)
-                        da2 += acc[cb][q] * (svalid ? load_f32(krow + 16 * cb + 4 * g + q) : 0.f);
+                    for (int q = 0; q < 4; ++q) {
+                        float kq;
+                        if constexpr (NAT) {
+                            kq = (float)kf[cb][q];
+                        } else {
+                            const float x = krow[16 * cb + 4 * g + q];
+                            kq = svalid ? x : 0.f;
+                        }
+                        da2 += acc[cb][q] * kq;
+                    }
                 }
                 if (svalid)
                     *reinterpret_cast<float4*>(grow + 16 * cb + 4 * g) =
@@ -569,20 +731,37 @@ __global__ __launch_bounds__(256) void k_bwd_da(BwdParams p) {
 }
 
 template <typename E, int C>
-size_t dq_smem(int dk, int dv) {
+size_t dq_smem(int dk, int dv, int nlev) {
     const size_t nat = sizeof(E) == 2 ? (size_t)C * (dk + kPadK) + (size_t)C * (dv + kPadK)
                                       : (size_t)dv * (C + kPadT);
-    return 2 * C * sizeof(float) + ((size_t)dk * (C + kPadT) + nat) * sizeof(E);
+    return (2 * C + kMaxLev + (size_t)C * nlev) * sizeof(float) +
+           ((size_t)dk * (C + kPadT) + nat) * sizeof(E);
 }
 template <typename E, int C>
 size_t dkv_smem(int dk, int dv) {
     const size_t nat = sizeof(E) == 2 ? (size_t)C * (dk + kPadK) + (size_t)C * (dv + kPadK) : 0;
-    return (2 * C + (size_t)C * (LogC<C>::v + 1)) * sizeof(float) +
+    return (2 * C + kMaxLev + (size_t)C * (LogC<C>::v + 1)) * sizeof(float) +
            ((size_t)(dk + dv) * (C + kPadT) + nat) * sizeof(E);
 }
 template <typename E, int C>
 size_t rstate_smem(int dk, int dv) {
     return 3 * C * sizeof(float) + (size_t)(dk + dv) * (C + kPadT) * sizeof(E);
+}
+
+constexpr size_t kLdsMax = 160 * 1024;  // bytes of LDS one block may use on gfx950
+
+// bf16 elements of the state-staging buffer behind `base` bytes of other LDS:
+// the whole state when it fits, else as many 16-row rounds as fit.  0 for
+// fp32 inputs (the fp32 path reads states from global memory) and -1 when
+// not even one round of 16 rows fits.
+template <typename E>
+long state_elems(size_t base, int dk, int dv) {
+    if (sizeof(E) != 2) return 0;
+    const long need = std::max((long)dk * (dv + kPadK), (long)dv * (dk + kPadK));
+    const long avail = base < kLdsMax ? (long)((kLdsMax - base) / 2) : 0;
+    const long minimum = 16L * (std::max(dk, dv) + kPadK);
+    const long got = std::min(need, avail);
+    return got >= minimum ? got : -1;
 }
 
 template <typename K>
@@ -594,20 +773,28 @@ hipError_t set_smem(K kernel, size_t bytes) {
 template <typename E, int C, int DM>
 hipError_t launch_bwd_typed(const BwdParams& p, hipStream_t stream) {
     const int nblk = p.BH * p.N;
-    const size_t s1 = dq_smem<E, C>(p.dk, p.dv);
+    BwdParams p1 = p, p3 = p;
+    size_t s1 = dq_smem<E, C>(p.dk, p.dv, p.nlev);
+    const long e1 = state_elems<E>(s1, p.dk, p.dv);
+    size_t s3 = dkv_smem<E, C>(p.dk, p.dv);
+    const long e3 = state_elems<E>(s3, p.dk, p.dv);
+    if (e1 < 0 || e3 < 0) return hipErrorInvalidValue;
+    p1.st_elems = (int)e1;
+    p3.st_elems = (int)e3;
+    s1 += (size_t)e1 * sizeof(E);
+    s3 += (size_t)e3 * sizeof(E);
     hipError_t err = set_smem(&k_bwd_dq<E, C, DM>, s1);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((k_bwd_dq<E, C, DM>), dim3(nblk), dim3(C / 16 * 64), s1, stream, p);
+    hipLaunchKernelGGL((k_bwd_dq<E, C, DM>), dim3(nblk), dim3(C / 16 * 64), s1, stream, p1);
     if (p.N > 1) {
         const size_t s2 = rstate_smem<E, C>(p.dk, p.dv);
-        err = set_smem(&k_bwd_rstate<E, C>, s2);
+        err = set_smem(&k_bwd_rstate<E, C, DM>, s2);
         if (err != hipSuccess) return err;
-        hipLaunchKernelGGL((k_bwd_rstate<E, C>), dim3(p.BH * (p.N - 1)), dim3(256), s2, stream, p);
+        hipLaunchKernelGGL((k_bwd_rstate<E, C, DM>), dim3(p.BH * (p.N - 1)), dim3(256), s2, stream, p);
     }
-    const size_t s3 = dkv_smem<E, C>(p.dk, p.dv);
     err = set_smem(&k_bwd_dkv<E, C, DM>, s3);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((k_bwd_dkv<E, C, DM>), dim3(nblk), dim3(C / 16 * 64), s3, stream, p);
+    hipLaunchKernelGGL((k_bwd_dkv<E, C, DM>), dim3(nblk), dim3(C / 16 * 64), s3, stream, p3);
     hipLaunchKernelGGL(k_bwd_da, dim3(p.BH), dim3(256), 0, stream, p);
     return hipGetLastError();
 }

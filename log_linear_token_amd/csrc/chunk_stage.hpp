@@ -77,6 +77,98 @@ __device__ __forceinline__ void stage_natural(const E* __restrict__ src, int D, 
     }
 }
 
+// Rows [t0, t0 + C) of a [T][D] tensor (D <= DM, a power of two) staged
+// into LDS in two halves: chunk_load issues every 16-byte load of the
+// thread (at most NV = C DM / (8 NT) for bf16) into registers, without
+// branches (rows past T read row t0 and are zeroed by a select), so that all
+// of them are in flight at once; chunk_store writes them as a natural copy
+// nat[s][d] (row stride D + kPadK) and/or a transposed copy tr[d][s] (row
+// stride C + kPadT, each token optionally multiplied by scale[s] from LDS);
+// either pointer may be null.
+template <typename E, int C, int DM, int NT>
+struct ChunkRows {
+    static constexpr int V = 16 / sizeof(E);
+    static constexpr int NV = (C * DM / V + NT - 1) / NT;
+    uint4 buf[NV];
+
+    __device__ __forceinline__ void load(const E* __restrict__ src, int D, int nvalid) {
+        const int sh = __builtin_ctz(D / V);
+        const int total = C << sh;
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int idx = threadIdx.x + u * NT;
+            const int s = idx >> sh;
+            const bool ok = idx < total && s < nvalid;
+            const int off = ok ? s * D + (idx - (s << sh)) * V : 0;
+            const uint4 x = *reinterpret_cast<const uint4*>(src + off);
+            buf[u] = ok ? x : make_uint4(0u, 0u, 0u, 0u);
+        }
+    }
+
+    __device__ __forceinline__ void store(int D, E* nat, E* tr, const float* scale) const {
+        const int sh = __builtin_ctz(D / V);
+        const int total = C << sh;
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int idx = threadIdx.x + u * NT;
+            if (idx < total) {
+                const int s = idx >> sh;
+                const int d0 = (idx - (s << sh)) * V;
+                if (nat) *reinterpret_cast<uint4*>(nat + s * (D + kPadK) + d0) = buf[u];
+                if (tr) {
+                    E e[V];
+                    __builtin_memcpy(e, &buf[u], 16);
+                    const float f = scale ? scale[s] : 1.f;
+#pragma unroll
+                    for (int j = 0; j < V; ++j) {
+                        if (scale) {
+                            if constexpr (sizeof(E) == 2) {
+                                __bf16 b = (__bf16)(bf16_to_f32(e[j]) * f);
+                                tr[(d0 + j) * (C + kPadT) + s] = __builtin_bit_cast(bf16_t, b);
+                            } else {
+                                tr[(d0 + j) * (C + kPadT) + s] = e[j] * f;
+                            }
+                        } else {
+                            tr[(d0 + j) * (C + kPadT) + s] = e[j];
+                        }
+                    }
+                }
+            }
+        }
+    }
+};
+
+// Stage rows [r0, r0 + nr) of a row-major fp32 matrix with `cols` columns (a
+// power of two >= 4) into LDS as bf16, dst[r - r0][c] with row stride
+// cols + kPadK.  NT threads; each round's loads (8 per thread) are all in
+// flight before its LDS writes.
+template <int NT>
+__device__ __forceinline__ void stage_state_bf16(const float* __restrict__ g, int cols, int r0, int nr,
+                                                 bf16_t* dst) {
+    constexpr int R = 8;
+    const int sh = __builtin_ctz(cols / 4);
+    const int mask = (1 << sh) - 1;
+    const int total = nr << sh;  // float4 vectors
+    const float4* src = reinterpret_cast<const float4*>(g + (size_t)r0 * cols);
+    for (int base = 0; base < total; base += R * NT) {
+        float4 buf[R];
+#pragma unroll
+        for (int u = 0; u < R; ++u) {  // no branch: out-of-range lanes read vector 0
+            const int idx = base + threadIdx.x + u * NT;
+            buf[u] = src[idx < total ? idx : 0];
+        }
+#pragma unroll
+        for (int u = 0; u < R; ++u) {
+            const int idx = base + threadIdx.x + u * NT;
+            if (idx < total) {
+                const int r = idx >> sh, c = (idx & mask) << 2;
+                *reinterpret_cast<bf16x4*>(dst + r * (cols + kPadK) + c) =
+                    pack4(buf[u].x, buf[u].y, buf[u].z, buf[u].w);
+            }
+        }
+    }
+}
+
 template <int LOGC>
 __device__ __forceinline__ float pick_level(const float (&lamr)[LOGC + 1], int lev) {
     float r = lamr[0];

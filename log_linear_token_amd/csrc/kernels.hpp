@@ -106,6 +106,7 @@ struct BwdParams {
     float* rstT;              // [BH][N][dv][dk] the same, transposed
     float* dA1;               // [BH][T] q_t . dq_t
     float* dA2;               // [BH][T] k_t . dk_t
+    int st_elems;             // bf16 elements of the LDS buffer that stages one carried state
 };
 hipError_t launch_bwd_chunked(const BwdParams& p, bool bf16, hipStream_t stream);
 
