@@ -134,7 +134,7 @@ __device__ __forceinline__ float load_f32(const bf16_t* p) { return bf16_to_f32(
 // --------------------------------------------------------------------------
 // dq and dlambda: one block per chunk, one wave per 16 query rows
 
-template <typename E, int C, int DM>
+template <typename E, int C, int DM, int FDK, int FDV>
 __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_dq(BwdParams p) {
     constexpr int NW = C / 16;
     constexpr int NT = NW * kWave;
@@ -154,7 +154,8 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_dq(BwdParams p) {
     const int i = blk - bh * p.N;
     const int t0 = i * C;
     const int nvalid = min(C, p.T - t0);
-    const int dk = p.dk, dv = p.dv, L = p.L, nlev = p.nlev;
+    const int dk = FDK ? FDK : p.dk, dv = FDV ? FDV : p.dv;  // FDK, FDV: head dims fixed at compile time
+    const int L = p.L, nlev = p.nlev;
     const int nkk = dk / KS, nkv = dv / KS;
     float* a_raw = reinterpret_cast<float*>(smem);
     float* A = a_raw + C;
@@ -238,36 +239,6 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_dq(BwdParams p) {
     __syncthreads();
     const float Ar = A[r];
 
-    // the chunk's own block: dS = dO V^T and Q K^T for the keys s <= r
-    typename Hand<E>::type Z[NW];
-    float dl[LOGC + 1];
-#pragma unroll
-    for (int l = 0; l <= LOGC; ++l) dl[l] = 0.f;
-#pragma unroll
-    for (int S = 0; S < NW; ++S) {
-        if (S <= R) {
-            f32x4 ds = {0.f, 0.f, 0.f, 0.f}, sc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int ks = 0; ks < MAXK; ++ks)
-                if (ks < nkv) ds = mma(rows_op<E, C>(Vn, VT, dv, 16 * S, ks, m, g), df[ks], ds);
-#pragma unroll
-            for (int ks = 0; ks < MAXK; ++ks)
-                if (ks < nkk) sc = mma(rows_op<E, C>(Kn, KT, dk, 16 * S, ks, m, g), qf[ks], sc);
-            float w[4];
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int s = 16 * S + 4 * g + q;
-                const int lev = fenwick_level(r, s);
-                const float dec = s <= r ? __expf(Ar - A[s]) : 0.f;
-                w[q] = ds[q] * pick_level<LOGC>(lamr, lev) * dec;
-                const float gq = ds[q] * sc[q] * dec;
-#pragma unroll
-                for (int l = 0; l <= LOGC; ++l) dl[l] += lev == l ? gq : 0.f;
-            }
-            Z[S] = Hand<E>::pack(w[0], w[1], w[2], w[3]);
-        }
-    }
-
     // q in the C layout of the dq tiles (column 16 cb + 4 g + j of row r):
     // for bf16 exactly the elements of the lane's own q fragments
     float qv[NB][4];
@@ -284,17 +255,43 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_dq(BwdParams p) {
         }
     }
 
-    // dq^T column blocks: K^T Z^T, then one term per coarse level
+    // The chunk's own block, one tile of 16 keys S <= R at a time: dS = dO V^T
+    // and Q K^T, weighted into Z = dS (.) M and handed straight to the dq
+    // product K^T Z^T.  A runtime loop, so that the accumulators are updated
+    // in place rather than merged across branches.
+    float dl[LOGC + 1];
+#pragma unroll
+    for (int l = 0; l <= LOGC; ++l) dl[l] = 0.f;
     f32x4 acc[NB];
 #pragma unroll
-    for (int cb = 0; cb < NB; ++cb) {
-        acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-        if (16 * cb < dk) {
+    for (int cb = 0; cb < NB; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+    for (int S = 0; S <= R; ++S) {
+        f32x4 ds = {0.f, 0.f, 0.f, 0.f}, sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int S = 0; S < NW; ++S)
-                if (S <= R) acc[cb] = mma_hand<E, C>(KT, 16 * cb, S, Z[S], acc[cb], m, g);
+        for (int ks = 0; ks < MAXK; ++ks)
+            if (ks < nkv) ds = mma(rows_op<E, C>(Vn, VT, dv, 16 * S, ks, m, g), df[ks], ds);
+#pragma unroll
+        for (int ks = 0; ks < MAXK; ++ks)
+            if (ks < nkk) sc = mma(rows_op<E, C>(Kn, KT, dk, 16 * S, ks, m, g), qf[ks], sc);
+        float w[4];
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+            const int s = 16 * S + 4 * g + q;
+            const int lev = fenwick_level(r, s);
+            const float dec = s <= r ? __expf(Ar - A[s]) : 0.f;
+            w[q] = ds[q] * pick_level<LOGC>(lamr, lev) * dec;
+            const float gq = ds[q] * sc[q] * dec;
+#pragma unroll
+            for (int l = 0; l <= LOGC; ++l) dl[l] += lev == l ? gq : 0.f;
         }
+        const typename Hand<E>::type Zs = Hand<E>::pack(w[0], w[1], w[2], w[3]);
+#pragma unroll
+        for (int cb = 0; cb < NB; ++cb)
+            if (16 * cb < dk) acc[cb] = mma_hand<E, C>(KT, 16 * cb, S, Zs, acc[cb], m, g);
     }
+
+    // one term per coarse level
     float* glrow = p.glam + trow * L;
     for (int pb = 0; (i >> pb) != 0; ++pb) {
         if (!((i >> pb) & 1)) continue;
@@ -490,7 +487,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_rstate(BwdParams p) {
 // --------------------------------------------------------------------------
 // dk and dv: one block per chunk, one wave per 16 key rows
 
-template <typename E, int C, int DM>
+template <typename E, int C, int DM, int FDK, int FDV>
 __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_dkv(BwdParams p) {
     constexpr int NW = C / 16;
     constexpr int LOGC = LogC<C>::v;
@@ -508,7 +505,8 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_dkv(BwdParams p) {
     const int i = blk - bh * p.N;
     const int t0 = i * C;
     const int nvalid = min(C, p.T - t0);
-    const int dk = p.dk, dv = p.dv, L = p.L, nlev = p.nlev;
+    const int dk = FDK ? FDK : p.dk, dv = FDV ? FDV : p.dv;  // FDK, FDV: head dims fixed at compile time
+    const int L = p.L, nlev = p.nlev;
     const int nkk = dk / KS, nkv = dv / KS;
     constexpr int NT = NW * kWave;
     constexpr int NLM = (C * (LOGC + 1) + NT - 1) / NT;  // intra-chunk lambda values per thread
@@ -596,33 +594,28 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_dkv(BwdParams p) {
         const E* tt = GK ? OT : QT;
         const E* ht = GK ? QT : OT;              // transposed rows of the hand-off product
         const frag_t* own = GK ? vf : kf;
-        typename Hand<E>::type H[NW];
-#pragma unroll
-        for (int S = 0; S < NW; ++S) {
-            if (S >= R) {
-                f32x4 x = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int ks = 0; ks < MAXK; ++ks)
-                    if (ks < nkc) x = mma(rows_op<E, C>(tn, tt, GK ? dv : dk, 16 * S, ks, m, g), own[ks], x);
-                float z[4];
-#pragma unroll
-                for (int q = 0; q < 4; ++q) {
-                    const int t = 16 * S + 4 * g + q;
-                    const float dec = t >= s ? __expf(A[t] - As) : 0.f;
-                    z[q] = x[q] * lamc[t * (LOGC + 1) + fenwick_level(t, s)] * dec;
-                }
-                H[S] = Hand<E>::pack(z[0], z[1], z[2], z[3]);
-            }
-        }
+        // one tile of 16 rows t, S >= R, at a time, handed straight to the
+        // gradient product (a runtime loop: accumulators updated in place)
         f32x4 acc[NB];
 #pragma unroll
-        for (int cb = 0; cb < NB; ++cb) {
-            acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
-            if (16 * cb < dout_dim) {
+        for (int cb = 0; cb < NB; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll 1
+        for (int S = R; S < NW; ++S) {
+            f32x4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int S = 0; S < NW; ++S)
-                    if (S >= R) acc[cb] = mma_hand<E, C>(ht, 16 * cb, S, H[S], acc[cb], m, g);
+            for (int ks = 0; ks < MAXK; ++ks)
+                if (ks < nkc) x = mma(rows_op<E, C>(tn, tt, GK ? dv : dk, 16 * S, ks, m, g), own[ks], x);
+            float z[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int t = 16 * S + 4 * g + q;
+                const float dec = t >= s ? __expf(A[t] - As) : 0.f;
+                z[q] = x[q] * lamc[t * (LOGC + 1) + fenwick_level(t, s)] * dec;
             }
+            const typename Hand<E>::type Hs = Hand<E>::pack(z[0], z[1], z[2], z[3]);
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb)
+                if (16 * cb < dout_dim) acc[cb] = mma_hand<E, C>(ht, 16 * cb, S, Hs, acc[cb], m, g);
         }
         // later blocks that see this chunk at a coarse level
         for (int pb = 0; (1 << pb) < p.N; ++pb) {
@@ -770,7 +763,8 @@ hipError_t set_smem(K kernel, size_t bytes) {
                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
 }
 
-template <typename E, int C, int DM>
+// FDK, FDV: the head dims when fixed at compile time (0: read from p)
+template <typename E, int C, int DM, int FDK = 0, int FDV = 0>
 hipError_t launch_bwd_typed(const BwdParams& p, hipStream_t stream) {
     const int nblk = p.BH * p.N;
     BwdParams p1 = p, p3 = p;
@@ -783,24 +777,33 @@ hipError_t launch_bwd_typed(const BwdParams& p, hipStream_t stream) {
     p3.st_elems = (int)e3;
     s1 += (size_t)e1 * sizeof(E);
     s3 += (size_t)e3 * sizeof(E);
-    hipError_t err = set_smem(&k_bwd_dq<E, C, DM>, s1);
+    hipError_t err = set_smem(&k_bwd_dq<E, C, DM, FDK, FDV>, s1);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((k_bwd_dq<E, C, DM>), dim3(nblk), dim3(C / 16 * 64), s1, stream, p1);
+    hipLaunchKernelGGL((k_bwd_dq<E, C, DM, FDK, FDV>), dim3(nblk), dim3(C / 16 * 64), s1, stream, p1);
     if (p.N > 1) {
         const size_t s2 = rstate_smem<E, C>(p.dk, p.dv);
         err = set_smem(&k_bwd_rstate<E, C, DM>, s2);
         if (err != hipSuccess) return err;
         hipLaunchKernelGGL((k_bwd_rstate<E, C, DM>), dim3(p.BH * (p.N - 1)), dim3(256), s2, stream, p);
     }
-    err = set_smem(&k_bwd_dkv<E, C, DM>, s3);
+    err = set_smem(&k_bwd_dkv<E, C, DM, FDK, FDV>, s3);
     if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((k_bwd_dkv<E, C, DM>), dim3(nblk), dim3(C / 16 * 64), s3, stream, p3);
+    hipLaunchKernelGGL((k_bwd_dkv<E, C, DM, FDK, FDV>), dim3(nblk), dim3(C / 16 * 64), s3, stream, p3);
     hipLaunchKernelGGL(k_bwd_da, dim3(p.BH), dim3(256), 0, stream, p);
     return hipGetLastError();
 }
 
 template <typename E, int C>
 hipError_t launch_bwd_c(const BwdParams& p, hipStream_t s) {
+    // bf16 head-dim pairs of the measured workloads get kernels with the
+    // dims fixed at compile time (every head-dim branch folded away)
+    if constexpr (sizeof(E) == 2 && C == 64) {
+        if (p.dk == 128 && p.dv == 64) return launch_bwd_typed<E, C, 128, 128, 64>(p, s);
+        if (p.dk == 64 && p.dv == 64) return launch_bwd_typed<E, C, 64, 64, 64>(p, s);
+    }
+    if constexpr (sizeof(E) == 2 && C == 128) {
+        if (p.dk == 128 && p.dv == 128) return launch_bwd_typed<E, C, 128, 128, 128>(p, s);
+    }
     switch (p.dk > p.dv ? p.dk : p.dv) {
         case 16: return launch_bwd_typed<E, C, 16>(p, s);
         case 32: return launch_bwd_typed<E, C, 32>(p, s);
