@@ -59,20 +59,25 @@ struct BStep<float> {
 // Coarse levels a chunk can have: bit_length(N - 1) for N < 2^31 chunks.
 constexpr int kMaxLev = 32;
 
+// Padding (elements) of the bf16 natural copies and staged states: rows of
+// 64 or 128 elements plus 16 put the four rows of one transpose read, and
+// the four lane groups of a wave, on disjoint LDS banks.
+constexpr int kPadB = 16;
+
 template <int C>
 struct LogC {
     static constexpr int v = C == 16 ? 4 : C == 32 ? 5 : C == 64 ? 6 : 7;
 };
 
 // A operand rows x0 .. x0 + 15 of a staged chunk, contraction step ks over
-// the head dim: bf16 reads the natural copy (D + kPadK per row), fp32 the
+// the head dim: bf16 reads the natural copy (D + kPadB per row), fp32 the
 // transposed one (one element a lane).
 template <typename E, int C>
 __device__ __forceinline__ typename Frag<E, BStep<E>::KS>::type rows_op(const E* nat, const E* tr,
                                                                         int D, int x0, int ks,
                                                                         int m, int g) {
     if constexpr (sizeof(E) == 2) {
-        return Frag<E, 16>::load(nat + (x0 + m) * (D + kPadK) + ks * 16 + 4 * g);
+        return Frag<E, 16>::load(nat + (x0 + m) * (D + kPadB) + ks * 16 + 4 * g);
     } else {
         return tr[(ks * 4 + g) * (C + kPadT) + x0 + m];
     }
@@ -122,10 +127,109 @@ __device__ __forceinline__ f32x4 mma_hand(const E* tr, int x0, int S, typename H
     }
 }
 
+typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
+
+// A operand of rows c0 .. c0 + 15 of X^T, contraction rows k0 .. k0 + 15 of X,
+// for a row-major bf16 LDS matrix X (row stride pitch elements, 8-byte aligned
+// rows): lane (m, g) gets X[k0 + 4g + i][c0 + m], i < 4.  One LDS transpose
+// read: in each group of 16 lanes, lane j names row k0 + 4g + j / 4 and
+// columns c0 + 4 (j % 4) .. + 3, and receives column c0 + j of the four rows.
+__device__ __forceinline__ bf16x4 tr_op(const bf16_t* X, int pitch, int k0, int c0, int m, int g) {
+    const bf16_t* a = X + (k0 + 4 * g + (m >> 2)) * pitch + c0 + 4 * (m & 3);
+    return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)a);
+}
+
+// acc += (the chunk's [C][D] matrix X)^T rows x0 .. x0 + 15 times a handed-off
+// tile of 16 tokens starting at 16 S: bf16 reads the natural copy
+// ([C][D + kPadB]) through transpose reads, fp32 the transposed copy.
+template <typename E, int C>
+__device__ __forceinline__ f32x4 hand_mma(const E* X, int D, int x0, int S, typename Hand<E>::type h,
+                                          f32x4 acc, int m, int g) {
+    if constexpr (sizeof(E) == 2) {
+        return mma(tr_op(X, D + kPadB, 16 * S, x0, m, g), h, acc);
+    } else {
+        return mma_hand<E, C>(X, x0, S, h, acc, m, g);
+    }
+}
+
 __device__ __forceinline__ float sum_groups(float x) {  // over the 4 lanes of one column
     x += __shfl_xor(x, 16, kWave);
     x += __shfl_xor(x, 32, kWave);
     return x;
+}
+
+// One carried state ([rows][cols] fp32 in global memory, rows * cols =
+// 4 NS NT) on its way to LDS as bf16: load() issues the thread's NS float4
+// loads into registers, where they stay in flight while the previous state
+// is being used; store() writes them with row stride cols + kPadB.
+template <int NS, int NT>
+struct StateRegs {
+    f32x4 buf[NS];  // a clang vector type, so that the array stays in registers
+    __device__ __forceinline__ void load(const float* __restrict__ g) {
+#pragma unroll
+        for (int u = 0; u < NS; ++u) buf[u] = reinterpret_cast<const f32x4*>(g)[threadIdx.x + u * NT];
+    }
+    __device__ __forceinline__ void store(int cols, bf16_t* dst) const {
+        const int sh = __builtin_ctz(cols / 4);
+        const int mask = (1 << sh) - 1;
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+            const int idx = threadIdx.x + u * NT;
+            const int r = idx >> sh, c = (idx & mask) << 2;
+            *reinterpret_cast<bf16x4*>(dst + r * (cols + kPadB) + c) =
+                pack4(buf[u].x, buf[u].y, buf[u].z, buf[u].w);
+        }
+    }
+};
+
+// The same for a bf16 state ([rows][cols] bf16, rows * cols = 8 NS NT):
+// 16-byte copies, no conversion.
+typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
+
+template <int NS, int NT>
+struct StateRegs16 {
+    u32x4 buf[NS];  // a clang vector type, so that the array stays in registers
+    __device__ __forceinline__ void load(const bf16_t* __restrict__ g) {
+#pragma unroll
+        for (int u = 0; u < NS; ++u) buf[u] = reinterpret_cast<const u32x4*>(g)[threadIdx.x + u * NT];
+    }
+    __device__ __forceinline__ void store(int cols, bf16_t* dst) const {
+        const int sh = __builtin_ctz(cols / 8);
+        const int mask = (1 << sh) - 1;
+#pragma unroll
+        for (int u = 0; u < NS; ++u) {
+            const int idx = threadIdx.x + u * NT;
+            const int r = idx >> sh, c = (idx & mask) << 3;
+            *reinterpret_cast<u32x4*>(dst + r * (cols + kPadB) + c) = buf[u];
+        }
+    }
+};
+
+// Rows [r0, r0 + nr) of a row-major bf16 matrix with `cols` columns (a power
+// of two >= 8) into LDS, row stride cols + kPadB; NT threads, each round's
+// loads (8 per thread) in flight before its LDS writes.
+template <int NT>
+__device__ __forceinline__ void stage_rows16(const bf16_t* __restrict__ g, int cols, int r0, int nr,
+                                             bf16_t* dst) {
+    constexpr int RD = 8;
+    const int sh = __builtin_ctz(cols / 8);
+    const int mask = (1 << sh) - 1;
+    const int total = nr << sh;  // 16-byte vectors
+    const uint4* src = reinterpret_cast<const uint4*>(g + (size_t)r0 * cols);
+    for (int base = 0; base < total; base += RD * NT) {
+        uint4 buf[RD];
+#pragma unroll
+        for (int u = 0; u < RD; ++u) {  // no branch: out-of-range lanes read vector 0
+            const int idx = base + threadIdx.x + u * NT;
+            buf[u] = src[idx < total ? idx : 0];
+        }
+#pragma unroll
+        for (int u = 0; u < RD; ++u) {
+            const int idx = base + threadIdx.x + u * NT;
+            if (idx < total)
+                *reinterpret_cast<uint4*>(dst + (idx >> sh) * (cols + kPadB) + ((idx & mask) << 3)) = buf[u];
+        }
+    }
 }
 
 __device__ __forceinline__ float load_f32(const float* p) { return *p; }
@@ -135,7 +239,7 @@ __device__ __forceinline__ float load_f32(const bf16_t* p) { return bf16_to_f32(
 // dq and dlambda: one block per chunk, one wave per 16 query rows
 
 template <typename E, int C, int DM, int FDK, int FDV>
-__global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_dq(BwdParams p) {
+__global__ __launch_bounds__(C / 16 * 64, C == 128 ? 2 : 3) void k_bwd_dq(BwdParams p) {
     constexpr int NW = C / 16;
     constexpr int NT = NW * kWave;
     constexpr int LOGC = LogC<C>::v;
@@ -161,13 +265,11 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_dq(BwdParams p) {
     float* A = a_raw + C;
     float* dlog = A + C;                       // [kMaxLev] A(end of chunk i-1) - A(node) per set bit
     float* lamco = dlog + kMaxLev;             // [C][nlev] lambda of the coarse levels
-    E* KT = reinterpret_cast<E*>(lamco + C * nlev);  // [dk][C + kPadT]
-    E* X1 = KT + dk * (C + kPadT);             // bf16: K natural; fp32: V transposed
-    E* X2 = X1 + (NAT ? C * (dk + kPadK) : 0); // bf16: V natural
-    E* Gs = X2 + (NAT ? C * (dv + kPadK) : 0); // bf16: one carried state, p.st_elems elements
-    const E* Kn = X1;
-    const E* Vn = X2;
-    const E* VT = X1;
+    // the chunk's K and V: bf16 natural ([C][d + kPadB]), fp32 transposed
+    // ([d][C + kPadT]); then (bf16) one carried state, p.st_elems elements
+    E* Kc = reinterpret_cast<E*>(lamco + C * nlev);
+    E* Vc = Kc + (NAT ? C * (dk + kPadB) : dk * (C + kPadT));
+    E* Gs = Vc + (NAT ? C * (dv + kPadB) : dv * (C + kPadT));
     const size_t row0 = (size_t)bh * p.T + t0;
 
     const int lane = threadIdx.x & (kWave - 1);
@@ -217,7 +319,7 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_dq(BwdParams p) {
     }
     const E* kg = static_cast<const E*>(p.k) + row0 * dk;
     const E* vg = static_cast<const E*>(p.v) + row0 * dv;
-    ChunkRows<E, C, DM, NT> kr, vr;
+    ChunkRows<E, C, DM, NT, kPadB> kr, vr;
     kr.load(kg, dk, nvalid);
     vr.load(vg, dv, nvalid);
 
@@ -228,12 +330,8 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_dq(BwdParams p) {
         const int idx = threadIdx.x + u * NT;
         if (idx < C * nlev) lamco[idx] = lco[u];
     }
-    kr.store(dk, NAT ? X1 : nullptr, KT, nullptr);
-    if constexpr (NAT) {
-        vr.store(dv, X2, nullptr, nullptr);
-    } else {
-        vr.store(dv, nullptr, X1, nullptr);
-    }
+    kr.store(dk, NAT ? Kc : nullptr, NAT ? nullptr : Kc, nullptr);
+    vr.store(dv, NAT ? Vc : nullptr, NAT ? nullptr : Vc, nullptr);
     __syncthreads();
     if (threadIdx.x < kWave) wave_cumsum(a_raw, A, C);
     __syncthreads();
@@ -270,10 +368,10 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_dq(BwdParams p) {
         f32x4 ds = {0.f, 0.f, 0.f, 0.f}, sc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
         for (int ks = 0; ks < MAXK; ++ks)
-            if (ks < nkv) ds = mma(rows_op<E, C>(Vn, VT, dv, 16 * S, ks, m, g), df[ks], ds);
+            if (ks < nkv) ds = mma(rows_op<E, C>(Vc, Vc, dv, 16 * S, ks, m, g), df[ks], ds);
 #pragma unroll
         for (int ks = 0; ks < MAXK; ++ks)
-            if (ks < nkk) sc = mma(rows_op<E, C>(Kn, KT, dk, 16 * S, ks, m, g), qf[ks], sc);
+            if (ks < nkk) sc = mma(rows_op<E, C>(Kc, Kc, dk, 16 * S, ks, m, g), qf[ks], sc);
         float w[4];
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
@@ -288,27 +386,59 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_dq(BwdParams p) {
         const typename Hand<E>::type Zs = Hand<E>::pack(w[0], w[1], w[2], w[3]);
 #pragma unroll
         for (int cb = 0; cb < NB; ++cb)
-            if (16 * cb < dk) acc[cb] = mma_hand<E, C>(KT, 16 * cb, S, Zs, acc[cb], m, g);
+            if (16 * cb < dk) acc[cb] = hand_mma<E, C>(Kc, dk, 16 * cb, S, Zs, acc[cb], m, g);
     }
 
-    // one term per coarse level
+    // one term per coarse level: the set bits of i, lowest first.  With the
+    // head dims fixed at compile time (PF) the whole node is staged at once
+    // and the next node's loads are issued before the current one is used;
+    // otherwise the node is staged in rounds of srows of its dk rows.
+    constexpr bool PF = NAT && FDK > 0 && FDV > 0;
+    constexpr int NS = PF ? FDK * FDV / (4 * NT) : 1;
     float* glrow = p.glam + trow * L;
-    for (int pb = 0; (i >> pb) != 0; ++pb) {
-        if (!((i >> pb) & 1)) continue;
-        const int node = ((i >> pb) << pb) - 1;
+    auto node_of = [&](int pb) __attribute__((always_inline)) {
+        return p.gnode + ((size_t)bh * p.N + ((i >> pb) << pb) - 1) * dk * dv;
+    };
+    StateRegs<NS, NT> st;
+    unsigned bits = (unsigned)i;
+    if constexpr (PF) {
+        if (bits) st.load(node_of(__builtin_ctz(bits)));
+    }
+    while (bits) {
+        const int pb = __builtin_ctz(bits);
+        bits &= bits - 1;
         const int lev = LOGC + pb + 1;
         const float e = rvalid ? __expf(Ar + dlog[pb]) : 0.f;
         const float lw = e * lamco[r * nlev + pb];
-        const float* G = p.gnode + ((size_t)bh * p.N + node) * dk * dv;
+        const float* G = node_of(pb);
         float dot = 0.f;
-        if constexpr (NAT) {
-            // the node goes through LDS as bf16, staged once for all waves,
-            // in rounds of srows of its dk rows
-            const int pitch = dv + kPadK;
+        if constexpr (PF) {
+            const int pitch = dv + kPadB;
+            __syncthreads();  // the previous node's reads are done
+            st.store(dv, Gs);
+            __syncthreads();
+            if (bits) st.load(node_of(__builtin_ctz(bits)));
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb) {
+                if (16 * cb < dk) {
+                    f32x4 y = {0.f, 0.f, 0.f, 0.f};
+                    const E* grow = Gs + (16 * cb + m) * pitch + 4 * g;
+#pragma unroll
+                    for (int ks = 0; ks < MAXK; ++ks)
+                        if (ks < nkv) y = mma(Frag<bf16_t, 16>::load(grow + ks * 16), df[ks], y);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        acc[cb][j] += lw * y[j];
+                        dot += qv[cb][j] * y[j];
+                    }
+                }
+            }
+        } else if constexpr (NAT) {
+            const int pitch = dv + kPadB;
             const int srows = min(dk, (p.st_elems / pitch) & ~15);
             for (int r0 = 0; r0 < dk; r0 += srows) {
                 __syncthreads();  // the previous round's reads are done
-                stage_state_bf16<NT>(G, dv, r0, min(srows, dk - r0), Gs);
+                stage_state_bf16<NT, kPadB>(G, dv, r0, min(srows, dk - r0), Gs);
                 __syncthreads();
 #pragma unroll
                 for (int cb = 0; cb < NB; ++cb) {
@@ -469,17 +599,33 @@ __global__ __launch_bounds__(256, 2) void k_bwd_rstate(BwdParams p) {
             }
         }
     }
-    float* Rd = p.rst + ((size_t)bh * p.N + j) * dk * dv;
-    float* RTd = p.rstT + ((size_t)bh * p.N + j) * dv * dk;
+    if constexpr (sizeof(E) == 2) {
+        // bf16 inputs: R alone, in bf16 ([dk][dv]), the one operand form the
+        // dk / dv kernel stages (it reads R^T through transpose reads)
+        bf16_t* Rd = p.rst16 + ((size_t)bh * p.N + j) * dk * dv;
 #pragma unroll
-    for (int u = 0; u < MAXT; ++u) {
-        const int tile = wave + u * nw;
-        if (tile < ntiles) {
-            const int d0 = (tile / ncv) * 16, c0 = (tile % ncv) * 16;
+        for (int u = 0; u < MAXT; ++u) {
+            const int tile = wave + u * nw;
+            if (tile < ntiles) {
+                const int d0 = (tile / ncv) * 16, c0 = (tile % ncv) * 16;
 #pragma unroll
-            for (int q = 0; q < 4; ++q) Rd[(size_t)(d0 + 4 * g + q) * dv + c0 + m] = acc[u][q];
-            *reinterpret_cast<float4*>(RTd + (size_t)(c0 + m) * dk + d0 + 4 * g) =
-                make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
+                for (int q = 0; q < 4; ++q)
+                    Rd[(size_t)(d0 + 4 * g + q) * dv + c0 + m] = __builtin_bit_cast(bf16_t, (__bf16)acc[u][q]);
+            }
+        }
+    } else {
+        float* Rd = p.rst + ((size_t)bh * p.N + j) * dk * dv;
+        float* RTd = p.rstT + ((size_t)bh * p.N + j) * dv * dk;
+#pragma unroll
+        for (int u = 0; u < MAXT; ++u) {
+            const int tile = wave + u * nw;
+            if (tile < ntiles) {
+                const int d0 = (tile / ncv) * 16, c0 = (tile % ncv) * 16;
+#pragma unroll
+                for (int q = 0; q < 4; ++q) Rd[(size_t)(d0 + 4 * g + q) * dv + c0 + m] = acc[u][q];
+                *reinterpret_cast<float4*>(RTd + (size_t)(c0 + m) * dk + d0 + 4 * g) =
+                    make_float4(acc[u][0], acc[u][1], acc[u][2], acc[u][3]);
+            }
         }
     }
 }
@@ -488,7 +634,7 @@ __global__ __launch_bounds__(256, 2) void k_bwd_rstate(BwdParams p) {
 // dk and dv: one block per chunk, one wave per 16 key rows
 
 template <typename E, int C, int DM, int FDK, int FDV>
-__global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_dkv(BwdParams p) {
+__global__ __launch_bounds__(C / 16 * 64, C == 128 ? 2 : 3) void k_bwd_dkv(BwdParams p) {
     constexpr int NW = C / 16;
     constexpr int LOGC = LogC<C>::v;
     constexpr int KS = BStep<E>::KS;
@@ -514,11 +660,11 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_dkv(BwdParams p) {
     float* A = a_raw + C;
     float* wlog = A + C;                          // [kMaxLev] A(end of block j - 1) - A(end of chunk i - 1)
     float* lamc = wlog + kMaxLev;                 // [C][LOGC + 1]
-    E* QT = reinterpret_cast<E*>(lamc + C * (LOGC + 1));  // [dk][C + kPadT]
-    E* OT = QT + dk * (C + kPadT);                // [dv][C + kPadT]
-    E* Qn = OT + dv * (C + kPadT);                // bf16: [C][dk + kPadK]
-    E* On = Qn + (NAT ? C * (dk + kPadK) : 0);    // bf16: [C][dv + kPadK]
-    E* Ss = On + (NAT ? C * (dv + kPadK) : 0);    // bf16: one carried state, p.st_elems elements
+    // the chunk's Q and dO: bf16 natural ([C][d + kPadB]), fp32 transposed
+    // ([d][C + kPadT]); then (bf16) one carried state, p.st_elems elements
+    E* Qc = reinterpret_cast<E*>(lamc + C * (LOGC + 1));
+    E* Oc = Qc + (NAT ? C * (dk + kPadB) : dk * (C + kPadT));
+    E* Ss = Oc + (NAT ? C * (dv + kPadB) : dv * (C + kPadT));
     const size_t row0 = (size_t)bh * p.T + t0;
 
     const int lane = threadIdx.x & (kWave - 1);
@@ -562,7 +708,7 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_dkv(BwdParams p) {
     }
     const E* qg = static_cast<const E*>(p.q) + row0 * dk;
     const E* og = static_cast<const E*>(p.dout) + row0 * dv;
-    ChunkRows<E, C, DM, NT> qr, orr;
+    ChunkRows<E, C, DM, NT, kPadB> qr, orr;
     qr.load(qg, dk, nvalid);
     orr.load(og, dv, nvalid);
 
@@ -573,30 +719,26 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_dkv(BwdParams p) {
         const int x = threadIdx.x + u * NT;
         if (x < C * (LOGC + 1)) lamc[x] = lm[u];
     }
-    qr.store(dk, NAT ? Qn : nullptr, QT, nullptr);
-    orr.store(dv, NAT ? On : nullptr, OT, nullptr);
+    qr.store(dk, NAT ? Qc : nullptr, NAT ? nullptr : Qc, nullptr);
+    orr.store(dv, NAT ? Oc : nullptr, NAT ? nullptr : Oc, nullptr);
     __syncthreads();
     if (threadIdx.x < kWave) wave_cumsum(a_raw, A, C);
     __syncthreads();
     const float As = A[s];
 
-    float da2 = 0.f;
-
-    // Two passes, dk then dv, so that only one set of handed-off tiles and
-    // accumulators is live at a time.  dk^T[d][s] = sum_t Q^T[d][t] Z[t][s]
-    // with Z = dP (.) M (dP from dO and v_s); dv^T[c][s] = sum_t dO^T[c][t] P[t][s]
-    // with P = (Q K^T) (.) M (from q and k_s); then the coarse levels through R(j).
-    auto pass = [&](auto kpass) __attribute__((always_inline)) {
+    // The chunk's own block, transposed: dk^T[d][s] = sum_t Q^T[d][t] Z[t][s]
+    // with Z = dP (.) M (dP from dO and v_s), dv^T[c][s] = sum_t dO^T[c][t] P[t][s]
+    // with P = (Q K^T) (.) M (from q and k_s).  One tile of 16 rows t, S >= R,
+    // at a time, handed straight to the gradient product (a runtime loop:
+    // accumulators updated in place).
+    auto tiles = [&](auto kpass, f32x4 (&acc)[NB]) __attribute__((always_inline)) {
         constexpr bool GK = decltype(kpass)::value;
         const int dout_dim = GK ? dk : dv;       // columns of the gradient
         const int nkc = GK ? nkv : nkk;          // contraction steps of the tile products
-        const E* tn = GK ? On : Qn;              // rows t of the tile products
-        const E* tt = GK ? OT : QT;
-        const E* ht = GK ? QT : OT;              // transposed rows of the hand-off product
+        const E* tn = GK ? Oc : Qc;              // rows t of the tile products
+        const E* ht = GK ? Qc : Oc;              // the hand-off product's matrix
+        const int hd = GK ? dk : dv;
         const frag_t* own = GK ? vf : kf;
-        // one tile of 16 rows t, S >= R, at a time, handed straight to the
-        // gradient product (a runtime loop: accumulators updated in place)
-        f32x4 acc[NB];
 #pragma unroll
         for (int cb = 0; cb < NB; ++cb) acc[cb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll 1
@@ -604,7 +746,7 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_dkv(BwdParams p) {
             f32x4 x = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int ks = 0; ks < MAXK; ++ks)
-                if (ks < nkc) x = mma(rows_op<E, C>(tn, tt, GK ? dv : dk, 16 * S, ks, m, g), own[ks], x);
+                if (ks < nkc) x = mma(rows_op<E, C>(tn, tn, GK ? dv : dk, 16 * S, ks, m, g), own[ks], x);
             float z[4];
 #pragma unroll
             for (int q = 0; q < 4; ++q) {
@@ -615,81 +757,146 @@ __global__ __launch_bounds__(C / 16 * 64, 2) void k_bwd_dkv(BwdParams p) {
             const typename Hand<E>::type Hs = Hand<E>::pack(z[0], z[1], z[2], z[3]);
 #pragma unroll
             for (int cb = 0; cb < NB; ++cb)
-                if (16 * cb < dout_dim) acc[cb] = mma_hand<E, C>(ht, 16 * cb, S, Hs, acc[cb], m, g);
-        }
-        // later blocks that see this chunk at a coarse level
-        for (int pb = 0; (1 << pb) < p.N; ++pb) {
-            if ((i >> pb) & 1) continue;
-            const int j = ((i >> pb) | 1) << pb;
-            if (j >= p.N) continue;
-            const float w = svalid ? __expf(wlog[pb] - As) : 0.f;
-            const float* Rs = GK ? p.rst + ((size_t)bh * p.N + j) * dk * dv
-                                 : p.rstT + ((size_t)bh * p.N + j) * dv * dk;
-            const int rpitch = GK ? dv : dk;
-            if constexpr (NAT) {
-                // the state goes through LDS as bf16, staged once for all
-                // waves, in rounds of srows of its rows
-                const int pitch = rpitch + kPadK;
-                const int srows = min(dout_dim, (p.st_elems / pitch) & ~15);
-                for (int r0 = 0; r0 < dout_dim; r0 += srows) {
-                    __syncthreads();  // the previous round's reads are done
-                    stage_state_bf16<NT>(Rs, rpitch, r0, min(srows, dout_dim - r0), Ss);
-                    __syncthreads();
-#pragma unroll
-                    for (int cb = 0; cb < NB; ++cb) {
-                        if (16 * cb < dout_dim && 16 * cb >= r0 && 16 * cb < r0 + srows) {
-                            f32x4 y = {0.f, 0.f, 0.f, 0.f};
-                            const E* rr = Ss + (16 * cb - r0 + m) * pitch + 4 * g;
-#pragma unroll
-                            for (int ks = 0; ks < MAXK; ++ks)
-                                if (ks < nkc) y = mma(Frag<bf16_t, 16>::load(rr + ks * 16), own[ks], y);
-#pragma unroll
-                            for (int q = 0; q < 4; ++q) acc[cb][q] += w * y[q];
-                        }
-                    }
-                }
-            } else {
-#pragma unroll
-                for (int cb = 0; cb < NB; ++cb) {
-                    if (16 * cb < dout_dim) {
-                        f32x4 y = {0.f, 0.f, 0.f, 0.f};
-                        const float* rr = Rs + (size_t)(16 * cb + m) * rpitch + g * KPL;
-#pragma unroll
-                        for (int ks = 0; ks < MAXK; ++ks)
-                            if (ks < nkc) y = mma(FR::from_f32(rr + ks * KS), own[ks], y);
-#pragma unroll
-                        for (int q = 0; q < 4; ++q) acc[cb][q] += w * y[q];
-                    }
-                }
-            }
-        }
-        float* grow = (GK ? p.gk : p.gv) + srow * dout_dim;
-#pragma unroll
-        for (int cb = 0; cb < NB; ++cb) {
-            if (16 * cb < dout_dim) {
-                if constexpr (GK) {
-                    // k in the C layout of the dk tiles: for bf16 exactly the
-                    // elements of the lane's own k fragments
-#pragma unroll
-                    for (int q = 0; q < 4; ++q) {
-                        float kq;
-                        if constexpr (NAT) {
-                            kq = (float)kf[cb][q];
-                        } else {
-                            const float x = krow[16 * cb + 4 * g + q];
-                            kq = svalid ? x : 0.f;
-                        }
-                        da2 += acc[cb][q] * kq;
-                    }
-                }
-                if (svalid)
-                    *reinterpret_cast<float4*>(grow + 16 * cb + 4 * g) =
-                        make_float4(acc[cb][0], acc[cb][1], acc[cb][2], acc[cb][3]);
-            }
+                if (16 * cb < dout_dim) acc[cb] = hand_mma<E, C>(ht, hd, 16 * cb, S, Hs, acc[cb], m, g);
         }
     };
-    pass(std::integral_constant<bool, true>{});
-    pass(std::integral_constant<bool, false>{});
+    f32x4 acck[NB], accv[NB];
+    tiles(std::integral_constant<bool, true>{}, acck);
+    tiles(std::integral_constant<bool, false>{}, accv);
+
+    // Later blocks that see this chunk at a coarse level: the clear bits pb
+    // of i whose block j = ((i >> pb) | 1) << pb exists, lowest first; each
+    // adds w_s R(j) v_s to dk_s and w_s R(j)^T k_s to dv_s.
+    unsigned todo = 0;
+    for (int pb = 0; pb < nlev; ++pb)
+        if (!((i >> pb) & 1) && ((((i >> pb) | 1) << pb) < p.N)) todo |= 1u << pb;
+    auto block_of = [&](int pb) __attribute__((always_inline)) {
+        return (size_t)bh * p.N + (((i >> pb) | 1) << pb);
+    };
+    if constexpr (NAT) {
+        // R(j) is bf16 [dk][dv]: staged once per level for both products; the
+        // dk rows read it as is (contraction over dv), the dv rows through
+        // transpose reads (contraction over dk).  With the head dims fixed at
+        // compile time (PF) it is staged whole and the next state's loads are
+        // issued before the current one is used; otherwise in rounds of
+        // srows of its dk rows.
+        constexpr bool PF = FDK > 0 && FDV > 0;
+        const int pitch = dv + kPadB;
+        auto use = [&](float w, int r0, int nr) __attribute__((always_inline)) {
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb) {
+                if (16 * cb < dk && 16 * cb >= r0 && 16 * cb < r0 + nr) {
+                    f32x4 y = {0.f, 0.f, 0.f, 0.f};
+                    const E* rr = Ss + (16 * cb - r0 + m) * pitch + 4 * g;
+#pragma unroll
+                    for (int ks = 0; ks < MAXK; ++ks)
+                        if (ks < nkv) y = mma(Frag<bf16_t, 16>::load(rr + ks * 16), vf[ks], y);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acck[cb][q] += w * y[q];
+                }
+            }
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb) {
+                if (16 * cb < dv) {
+                    f32x4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int ks = 0; ks < MAXK; ++ks)
+                        if (ks < nkk && 16 * ks >= r0 && 16 * ks < r0 + nr)
+                            y = mma(tr_op(Ss, pitch, 16 * ks - r0, 16 * cb, m, g), kf[ks], y);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) accv[cb][q] += w * y[q];
+                }
+            }
+        };
+        if constexpr (PF) {
+            constexpr int NS = FDK * FDV / (8 * NT);
+            StateRegs16<NS, NT> st;
+            if (todo) st.load(p.rst16 + block_of(__builtin_ctz(todo)) * dk * dv);
+            while (todo) {
+                const int pb = __builtin_ctz(todo);
+                todo &= todo - 1;
+                const float w = svalid ? __expf(wlog[pb] - As) : 0.f;
+                __syncthreads();  // the previous state's reads are done
+                st.store(dv, Ss);
+                __syncthreads();
+                if (todo) st.load(p.rst16 + block_of(__builtin_ctz(todo)) * dk * dv);
+                use(w, 0, dk);
+            }
+        } else {
+            const int srows = min(dk, (p.st_elems / pitch) & ~15);
+            while (todo) {
+                const int pb = __builtin_ctz(todo);
+                todo &= todo - 1;
+                const float w = svalid ? __expf(wlog[pb] - As) : 0.f;
+                const bf16_t* Rg = p.rst16 + block_of(pb) * dk * dv;
+                for (int r0 = 0; r0 < dk; r0 += srows) {
+                    const int nr = min(srows, dk - r0);
+                    __syncthreads();  // the previous round's reads are done
+                    stage_rows16<NT>(Rg, dv, r0, nr, Ss);
+                    __syncthreads();
+                    use(w, r0, nr);
+                }
+            }
+        }
+    } else {
+        // fp32 inputs: R and R^T read from global memory
+        while (todo) {
+            const int pb = __builtin_ctz(todo);
+            todo &= todo - 1;
+            const float w = svalid ? __expf(wlog[pb] - As) : 0.f;
+            const float* Rk = p.rst + block_of(pb) * dk * dv;
+            const float* Rv = p.rstT + block_of(pb) * dv * dk;
+#pragma unroll
+            for (int cb = 0; cb < NB; ++cb) {
+                if (16 * cb < dk) {
+                    f32x4 y = {0.f, 0.f, 0.f, 0.f};
+                    const float* rr = Rk + (size_t)(16 * cb + m) * dv + g * KPL;
+#pragma unroll
+                    for (int ks = 0; ks < MAXK; ++ks)
+                        if (ks < nkv) y = mma(FR::from_f32(rr + ks * KS), vf[ks], y);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) acck[cb][q] += w * y[q];
+                }
+                if (16 * cb < dv) {
+                    f32x4 y = {0.f, 0.f, 0.f, 0.f};
+                    const float* rr = Rv + (size_t)(16 * cb + m) * dk + g * KPL;
+#pragma unroll
+                    for (int ks = 0; ks < MAXK; ++ks)
+                        if (ks < nkk) y = mma(FR::from_f32(rr + ks * KS), kf[ks], y);
+#pragma unroll
+                    for (int q = 0; q < 4; ++q) accv[cb][q] += w * y[q];
+                }
+            }
+        }
+    }
+
+    // outputs, and k_s . dk_s for the decay gradient (k in the C layout of
+    // the dk tiles: for bf16 exactly the elements of the lane's own k fragments)
+    float da2 = 0.f;
+    float* gkrow = p.gk + srow * dk;
+    float* gvrow = p.gv + srow * dv;
+#pragma unroll
+    for (int cb = 0; cb < NB; ++cb) {
+        if (16 * cb < dk) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                float kq;
+                if constexpr (NAT) {
+                    kq = (float)kf[cb][q];
+                } else {
+                    const float x = krow[16 * cb + 4 * g + q];
+                    kq = svalid ? x : 0.f;
+                }
+                da2 += acck[cb][q] * kq;
+            }
+            if (svalid)
+                *reinterpret_cast<float4*>(gkrow + 16 * cb + 4 * g) =
+                    make_float4(acck[cb][0], acck[cb][1], acck[cb][2], acck[cb][3]);
+        }
+        if (16 * cb < dv && svalid)
+            *reinterpret_cast<float4*>(gvrow + 16 * cb + 4 * g) =
+                make_float4(accv[cb][0], accv[cb][1], accv[cb][2], accv[cb][3]);
+    }
     da2 = sum_groups(da2);
     if (svalid && g == 0) p.dA2[srow] = da2;
 }
@@ -723,18 +930,20 @@ __global__ __launch_bounds__(256) void k_bwd_da(BwdParams p) {
     }
 }
 
+// LDS of the chunk's two staged matrices (head dims dk and dv)
+template <typename E, int C>
+size_t chunk_pair_elems(int dk, int dv) {
+    return sizeof(E) == 2 ? (size_t)C * (dk + kPadB) + (size_t)C * (dv + kPadB)
+                          : (size_t)(dk + dv) * (C + kPadT);
+}
 template <typename E, int C>
 size_t dq_smem(int dk, int dv, int nlev) {
-    const size_t nat = sizeof(E) == 2 ? (size_t)C * (dk + kPadK) + (size_t)C * (dv + kPadK)
-                                      : (size_t)dv * (C + kPadT);
-    return (2 * C + kMaxLev + (size_t)C * nlev) * sizeof(float) +
-           ((size_t)dk * (C + kPadT) + nat) * sizeof(E);
+    return (2 * C + kMaxLev + (size_t)C * nlev) * sizeof(float) + chunk_pair_elems<E, C>(dk, dv) * sizeof(E);
 }
 template <typename E, int C>
 size_t dkv_smem(int dk, int dv) {
-    const size_t nat = sizeof(E) == 2 ? (size_t)C * (dk + kPadK) + (size_t)C * (dv + kPadK) : 0;
     return (2 * C + kMaxLev + (size_t)C * (LogC<C>::v + 1)) * sizeof(float) +
-           ((size_t)(dk + dv) * (C + kPadT) + nat) * sizeof(E);
+           chunk_pair_elems<E, C>(dk, dv) * sizeof(E);
 }
 template <typename E, int C>
 size_t rstate_smem(int dk, int dv) {
@@ -750,9 +959,9 @@ constexpr size_t kLdsMax = 160 * 1024;  // bytes of LDS one block may use on gfx
 template <typename E>
 long state_elems(size_t base, int dk, int dv) {
     if (sizeof(E) != 2) return 0;
-    const long need = std::max((long)dk * (dv + kPadK), (long)dv * (dk + kPadK));
+    const long need = (long)dk * (dv + kPadB);  // every staged state is [dk][dv]
     const long avail = base < kLdsMax ? (long)((kLdsMax - base) / 2) : 0;
-    const long minimum = 16L * (std::max(dk, dv) + kPadK);
+    const long minimum = 16L * (dv + kPadB);
     const long got = std::min(need, avail);
     return got >= minimum ? got : -1;
 }
@@ -777,18 +986,35 @@ hipError_t launch_bwd_typed(const BwdParams& p, hipStream_t stream) {
     p3.st_elems = (int)e3;
     s1 += (size_t)e1 * sizeof(E);
     s3 += (size_t)e3 * sizeof(E);
-    hipError_t err = set_smem(&k_bwd_dq<E, C, DM, FDK, FDV>, s1);
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((k_bwd_dq<E, C, DM, FDK, FDV>), dim3(nblk), dim3(C / 16 * 64), s1, stream, p1);
+    // the compile-time head-dim kernels stage every carried state whole:
+    // where it does not fit the LDS, the generic kernel runs instead
+    const long whole = (long)p.dk * (p.dv + kPadB);
+    const bool f1 = FDK > 0 && e1 >= whole, f3 = FDK > 0 && e3 >= whole;
+    hipError_t err;
+    if (f1) {
+        err = set_smem(&k_bwd_dq<E, C, DM, FDK, FDV>, s1);
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL((k_bwd_dq<E, C, DM, FDK, FDV>), dim3(nblk), dim3(C / 16 * 64), s1, stream, p1);
+    } else {
+        err = set_smem(&k_bwd_dq<E, C, DM, 0, 0>, s1);
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL((k_bwd_dq<E, C, DM, 0, 0>), dim3(nblk), dim3(C / 16 * 64), s1, stream, p1);
+    }
     if (p.N > 1) {
         const size_t s2 = rstate_smem<E, C>(p.dk, p.dv);
         err = set_smem(&k_bwd_rstate<E, C, DM>, s2);
         if (err != hipSuccess) return err;
         hipLaunchKernelGGL((k_bwd_rstate<E, C, DM>), dim3(p.BH * (p.N - 1)), dim3(256), s2, stream, p);
     }
-    err = set_smem(&k_bwd_dkv<E, C, DM, FDK, FDV>, s3);
-    if (err != hipSuccess) return err;
-    hipLaunchKernelGGL((k_bwd_dkv<E, C, DM, FDK, FDV>), dim3(nblk), dim3(C / 16 * 64), s3, stream, p3);
+    if (f3) {
+        err = set_smem(&k_bwd_dkv<E, C, DM, FDK, FDV>, s3);
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL((k_bwd_dkv<E, C, DM, FDK, FDV>), dim3(nblk), dim3(C / 16 * 64), s3, stream, p3);
+    } else {
+        err = set_smem(&k_bwd_dkv<E, C, DM, 0, 0>, s3);
+        if (err != hipSuccess) return err;
+        hipLaunchKernelGGL((k_bwd_dkv<E, C, DM, 0, 0>), dim3(nblk), dim3(C / 16 * 64), s3, stream, p3);
+    }
     hipLaunchKernelGGL(k_bwd_da, dim3(p.BH), dim3(256), 0, stream, p);
     return hipGetLastError();
 }

@@ -82,14 +82,29 @@ __device__ __forceinline__ void stage_natural(const E* __restrict__ src, int D, 
 // thread (at most NV = C DM / (8 NT) for bf16) into registers, without
 // branches (rows past T read row t0 and are zeroed by a select), so that all
 // of them are in flight at once; chunk_store writes them as a natural copy
-// nat[s][d] (row stride D + kPadK) and/or a transposed copy tr[d][s] (row
+// nat[s][d] (row stride D + PADN) and/or a transposed copy tr[d][s] (row
 // stride C + kPadT, each token optionally multiplied by scale[s] from LDS);
 // either pointer may be null.
-template <typename E, int C, int DM, int NT>
+template <typename E, int C, int DM, int NT, int PADN = kPadK>
 struct ChunkRows {
     static constexpr int V = 16 / sizeof(E);
     static constexpr int NV = (C * DM / V + NT - 1) / NT;
     uint4 buf[NV];
+
+    // Vector idx of the thread -> token s and first element d0.  With at
+    // least 4 vectors per row, each 64 consecutive vectors (one wave
+    // instruction) cover 16 tokens x 4 vectors, so that the 2-byte writes of
+    // the transposed copy fall into 32 distinct banks; otherwise row-major.
+    __device__ __forceinline__ static void where(int idx, int sh, int& s, int& d0) {
+        if (sh >= 2) {
+            const int l = idx & 63, w = idx >> 6;
+            s = 16 * (w % (C / 16)) + (l & 15);
+            d0 = (4 * (w / (C / 16)) + (l >> 4)) * V;
+        } else {
+            s = idx >> sh;
+            d0 = (idx - (s << sh)) * V;
+        }
+    }
 
     __device__ __forceinline__ void load(const E* __restrict__ src, int D, int nvalid) {
         const int sh = __builtin_ctz(D / V);
@@ -97,9 +112,10 @@ struct ChunkRows {
 #pragma unroll
         for (int u = 0; u < NV; ++u) {
             const int idx = threadIdx.x + u * NT;
-            const int s = idx >> sh;
+            int s, d0;
+            where(idx, sh, s, d0);
             const bool ok = idx < total && s < nvalid;
-            const int off = ok ? s * D + (idx - (s << sh)) * V : 0;
+            const int off = ok ? s * D + d0 : 0;
             const uint4 x = *reinterpret_cast<const uint4*>(src + off);
             buf[u] = ok ? x : make_uint4(0u, 0u, 0u, 0u);
         }
@@ -112,9 +128,9 @@ struct ChunkRows {
         for (int u = 0; u < NV; ++u) {
             const int idx = threadIdx.x + u * NT;
             if (idx < total) {
-                const int s = idx >> sh;
-                const int d0 = (idx - (s << sh)) * V;
-                if (nat) *reinterpret_cast<uint4*>(nat + s * (D + kPadK) + d0) = buf[u];
+                int s, d0;
+                where(idx, sh, s, d0);
+                if (nat) *reinterpret_cast<uint4*>(nat + s * (D + PADN) + d0) = buf[u];
                 if (tr) {
                     E e[V];
                     __builtin_memcpy(e, &buf[u], 16);
@@ -140,9 +156,9 @@ struct ChunkRows {
 
 // Stage rows [r0, r0 + nr) of a row-major fp32 matrix with `cols` columns (a
 // power of two >= 4) into LDS as bf16, dst[r - r0][c] with row stride
-// cols + kPadK.  NT threads; each round's loads (8 per thread) are all in
+// cols + PADN.  NT threads; each round's loads (8 per thread) are all in
 // flight before its LDS writes.
-template <int NT>
+template <int NT, int PADN = kPadK>
 __device__ __forceinline__ void stage_state_bf16(const float* __restrict__ g, int cols, int r0, int nr,
                                                  bf16_t* dst) {
     constexpr int R = 8;
@@ -162,7 +178,7 @@ __device__ __forceinline__ void stage_state_bf16(const float* __restrict__ g, in
             const int idx = base + threadIdx.x + u * NT;
             if (idx < total) {
                 const int r = idx >> sh, c = (idx & mask) << 2;
-                *reinterpret_cast<bf16x4*>(dst + r * (cols + kPadK) + c) =
+                *reinterpret_cast<bf16x4*>(dst + r * (cols + PADN) + c) =
                     pack4(buf[u].x, buf[u].y, buf[u].z, buf[u].w);
             }
         }

@@ -103,7 +103,8 @@ struct BwdParams {
     const float* gnode;       // [BH][N][dk][dv] Fenwick nodes of sum k v^T over chunks
     const double* cum;        // [BH][N] A at the end of each chunk
     float* rst;               // [BH][N][dk][dv] block states R(j)
-    float* rstT;              // [BH][N][dv][dk] the same, transposed
+    float* rstT;              // [BH][N][dv][dk] the same, transposed (fp32 inputs)
+    bf16_t_storage* rst16;    // [BH][N][dk][dv] R(j) in bf16 (bf16 inputs; in place of rst)
     float* dA1;               // [BH][T] q_t . dq_t
     float* dA2;               // [BH][T] k_t . dk_t
     int st_elems;             // bf16 elements of the LDS buffer that stages one carried state

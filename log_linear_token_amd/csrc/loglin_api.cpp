@@ -443,6 +443,7 @@ loglin_status loglin_bwd_chunked(const void* q, const void* k, const void* v, co
         bp.cum = fp.cum;
         bp.rst = reinterpret_cast<float*>(base + w.rst_off);
         bp.rstT = reinterpret_cast<float*>(base + w.rstT_off);
+        bp.rst16 = reinterpret_cast<bf16_t_storage*>(base + w.rst_off);
     }
     hipError_t e = launch_bwd_chunked(bp, in_dtype == LOGLIN_BF16, hs);
     if (e != hipSuccess) return hip_fail(e, "loglin_bwd_chunked launch");
