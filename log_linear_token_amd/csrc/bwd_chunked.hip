@@ -509,10 +509,15 @@ __global__ __launch_bounds__(C / 16 * 64, C == 128 ? 2 : 3) void k_bwd_dq(BwdPar
 // chunk j, for the keys of its left sibling.  Blocks are taken largest first.
 // The loads of chunk c + 1 are issued before the products of chunk c.
 
-template <typename E, int C, int DM>
+template <typename E, int C, int DM, int FDK, int FDV>
 __global__ __launch_bounds__(256, 2) void k_bwd_rstate(BwdParams p) {
     constexpr int LOGC = LogC<C>::v;
-    constexpr int MAXT = 16;  // tiles of 16 x 16 per wave: (128 / 16)^2 / 4 waves
+    // head dims fixed at compile time (FDK, FDV > 0) size the registers to
+    // them, which leaves room for two chunks in flight (DEPTH 2)
+    constexpr int QD = FDK ? FDK : DM, OD = FDV ? FDV : DM;
+    constexpr int MAXT = ((QD / 16) * (OD / 16) + 3) / 4;  // tiles of 16 x 16 per wave, 4 waves
+    constexpr int NVIN = (C * QD + C * OD) * (int)sizeof(E) / 16 / 256;  // 16-byte loads per thread and chunk
+    constexpr int DEPTH = (FDK && FDV && NVIN <= 8) ? 2 : 1;
     extern __shared__ __align__(16) char smem[];
     int x = blockIdx.x, lev = -1, j = 0, bh = 0;
     for (int pp = p.nlev - 1; pp >= 0; --pp) {
@@ -530,13 +535,14 @@ __global__ __launch_bounds__(256, 2) void k_bwd_rstate(BwdParams p) {
     if (lev < 0) return;
     const int jend = min(j + (1 << lev), p.N);
     const int lidx = LOGC + lev + 1;
-    const int dk = p.dk, dv = p.dv;
+    const int dk = FDK ? FDK : p.dk, dv = FDV ? FDV : p.dv;
     const int tid = threadIdx.x;
-    float* a_raw = reinterpret_cast<float*>(smem);
-    float* Al = a_raw + C;
-    float* e = Al + C;
-    E* QT = reinterpret_cast<E*>(e + C);   // [dk][C + kPadT], scaled rows
-    E* OT = QT + dk * (C + kPadT);         // [dv][C + kPadT]
+    // two copies of the chunk's scaled Q^T and dO^T where the LDS allows
+    // (p.rs_nbuf == 2): chunk c is written into copy c & 1 while the products
+    // of chunk c - 1 may still read the other, so that one barrier per chunk
+    // suffices; with one copy a second barrier guards the overwrite
+    const int csz = (dk + dv) * (C + kPadT);
+    E* buf0 = reinterpret_cast<E*>(smem);
     const double* cum = p.cum + (size_t)bh * p.N;
     const double cj = cum[j - 1];
 
@@ -550,35 +556,52 @@ __global__ __launch_bounds__(256, 2) void k_bwd_rstate(BwdParams p) {
 #pragma unroll
     for (int u = 0; u < MAXT; ++u) acc[u] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-    // a chunk's loads, all branch-free: a and lambda of the token of this
-    // thread (rows past T read the chunk's first row), A at the end of the
-    // previous chunk, and the chunk's q and dO rows
-    ChunkRows<E, C, DM, 256> qr, orr;
-    float av, lv, base;
-    auto load = [&](int c) __attribute__((always_inline)) {
+    // A chunk's loads, all branch-free: every wave reads a and lambda of the
+    // whole chunk (lane l: tokens 2l and 2l + 1; rows past T read the chunk's
+    // first row), A at the end of the previous chunk, and the chunk's q and
+    // dO rows.  Two chunks are in flight ahead of the one being used.
+    struct Loaded {
+        ChunkRows<E, C, QD, 256> qr;
+        ChunkRows<E, C, OD, 256> orr;
+        float a0, a1, l0, l1, base;
+    };
+    Loaded ld0, ld1;
+    auto load = [&](Loaded& L, int c) __attribute__((always_inline)) {
         const int nvalid = min(C, p.T - c * C);
         const size_t row0 = (size_t)bh * p.T + (size_t)c * C;
-        const size_t rr = row0 + min(tid % C, nvalid - 1);
-        av = p.a[rr];
-        lv = p.lam[rr * p.L + lidx];
-        base = (float)(cum[c - 1] - cj);
-        qr.load(static_cast<const E*>(p.q) + row0 * dk, dk, nvalid);
-        orr.load(static_cast<const E*>(p.dout) + row0 * dv, dv, nvalid);
+        const size_t r0 = row0 + min(2 * lane, nvalid - 1), r1 = row0 + min(2 * lane + 1, nvalid - 1);
+        L.a0 = p.a[r0];
+        L.a1 = p.a[r1];
+        L.l0 = p.lam[r0 * p.L + lidx];
+        L.l1 = p.lam[r1 * p.L + lidx];
+        L.base = (float)(cum[c - 1] - cj);
+        L.qr.load(static_cast<const E*>(p.q) + row0 * dk, dk, nvalid);
+        L.orr.load(static_cast<const E*>(p.dout) + row0 * dv, dv, nvalid);
     };
-    load(j);
-    for (int c = j; c < jend; ++c) {
+    auto step = [&](Loaded& L, int c) __attribute__((always_inline)) {
         const int nvalid = min(C, p.T - c * C);
-        __syncthreads();  // the previous chunk's operands are consumed
-        if (tid < C) a_raw[tid] = tid < nvalid ? av : 0.f;
-        __syncthreads();
-        if (tid < kWave) wave_cumsum(a_raw, Al, C);
-        __syncthreads();
-        if (tid < C) e[tid] = tid < nvalid ? lv * __expf(base + Al[tid]) : 0.f;
-        __syncthreads();
-        qr.store(dk, nullptr, QT, e);
-        orr.store(dv, nullptr, OT, nullptr);
-        __syncthreads();
-        if (c + 1 < jend) load(c + 1);
+        if (p.rs_nbuf == 1 && c > j) __syncthreads();  // the products of chunk c - 1 are done
+        E* QT = buf0 + (p.rs_nbuf == 2 ? (c & 1) * csz : 0);  // [dk][C + kPadT], scaled rows
+        E* OT = QT + dk * (C + kPadT);  // [dv][C + kPadT]
+        // chunk-local inclusive sum of a in registers (each wave the whole
+        // chunk), then e_t = lambda_t exp(A_t - A(end of block j - 1))
+        const bool ok0 = 2 * lane < nvalid, ok1 = 2 * lane + 1 < nvalid;
+        const float x0 = ok0 ? L.a0 : 0.f, x1 = ok1 ? L.a1 : 0.f;
+        float incl = x0 + x1;
+#pragma unroll
+        for (int off = 1; off < kWave; off <<= 1) {
+            const float y = __shfl_up(incl, off, kWave);
+            if (lane >= off) incl += y;
+        }
+        const float e0 = ok0 ? L.l0 * __expf(L.base + incl - x1) : 0.f;
+        const float e1 = ok1 ? L.l1 * __expf(L.base + incl) : 0.f;
+        L.qr.store_tr_scaled(dk, QT, [&](int s) __attribute__((always_inline)) {
+            const float y0 = __shfl(e0, s >> 1, kWave), y1 = __shfl(e1, s >> 1, kWave);
+            return (s & 1) ? y1 : y0;
+        });
+        L.orr.store(dv, nullptr, OT, nullptr);
+        __syncthreads();  // chunk c staged; every wave is past the products of chunk c - 1
+        if (c + DEPTH < jend) load(L, c + DEPTH);
 #pragma unroll
         for (int u = 0; u < MAXT; ++u) {
             const int tile = wave + u * nw;
@@ -598,6 +621,16 @@ __global__ __launch_bounds__(256, 2) void k_bwd_rstate(BwdParams p) {
                 }
             }
         }
+    };
+    load(ld0, j);
+    if constexpr (DEPTH == 2) {
+        if (j + 1 < jend) load(ld1, j + 1);
+        for (int c = j; c < jend; c += 2) {
+            step(ld0, c);
+            if (c + 1 < jend) step(ld1, c + 1);
+        }
+    } else {
+        for (int c = j; c < jend; ++c) step(ld0, c);
     }
     if constexpr (sizeof(E) == 2) {
         // bf16 inputs: R alone, in bf16 ([dk][dv]), the one operand form the
@@ -946,8 +979,8 @@ size_t dkv_smem(int dk, int dv) {
            chunk_pair_elems<E, C>(dk, dv) * sizeof(E);
 }
 template <typename E, int C>
-size_t rstate_smem(int dk, int dv) {
-    return 3 * C * sizeof(float) + (size_t)(dk + dv) * (C + kPadT) * sizeof(E);
+size_t rstate_smem(int dk, int dv, int nbuf) {
+    return nbuf * (size_t)(dk + dv) * (C + kPadT) * sizeof(E);
 }
 
 constexpr size_t kLdsMax = 160 * 1024;  // bytes of LDS one block may use on gfx950
@@ -1001,10 +1034,13 @@ hipError_t launch_bwd_typed(const BwdParams& p, hipStream_t stream) {
         hipLaunchKernelGGL((k_bwd_dq<E, C, DM, 0, 0>), dim3(nblk), dim3(C / 16 * 64), s1, stream, p1);
     }
     if (p.N > 1) {
-        const size_t s2 = rstate_smem<E, C>(p.dk, p.dv);
-        err = set_smem(&k_bwd_rstate<E, C, DM>, s2);
+        BwdParams p2 = p;
+        p2.rs_nbuf = rstate_smem<E, C>(p.dk, p.dv, 2) <= kLdsMax ? 2 : 1;
+        const size_t s2 = rstate_smem<E, C>(p.dk, p.dv, p2.rs_nbuf);
+        err = set_smem(&k_bwd_rstate<E, C, DM, FDK, FDV>, s2);
         if (err != hipSuccess) return err;
-        hipLaunchKernelGGL((k_bwd_rstate<E, C, DM>), dim3(p.BH * (p.N - 1)), dim3(256), s2, stream, p);
+        hipLaunchKernelGGL((k_bwd_rstate<E, C, DM, FDK, FDV>), dim3(p.BH * (p.N - 1)), dim3(256), s2, stream,
+                           p2);
     }
     if (f3) {
         err = set_smem(&k_bwd_dkv<E, C, DM, FDK, FDV>, s3);

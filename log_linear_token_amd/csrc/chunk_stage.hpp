@@ -121,6 +121,35 @@ struct ChunkRows {
         }
     }
 
+    // The transposed copy only, token s scaled by scale_of(s); scale_of is
+    // called by every lane for every vector (it may exchange values between
+    // lanes), with s clamped to the chunk.
+    template <typename F>
+    __device__ __forceinline__ void store_tr_scaled(int D, E* tr, F scale_of) const {
+        const int sh = __builtin_ctz(D / V);
+        const int total = C << sh;
+#pragma unroll
+        for (int u = 0; u < NV; ++u) {
+            const int idx = threadIdx.x + u * NT;
+            int s, d0;
+            where(idx, sh, s, d0);
+            const float f = scale_of(idx < total ? s : 0);
+            if (idx < total) {
+                E e[V];
+                __builtin_memcpy(e, &buf[u], 16);
+#pragma unroll
+                for (int j = 0; j < V; ++j) {
+                    if constexpr (sizeof(E) == 2) {
+                        __bf16 b = (__bf16)(bf16_to_f32(e[j]) * f);
+                        tr[(d0 + j) * (C + kPadT) + s] = __builtin_bit_cast(bf16_t, b);
+                    } else {
+                        tr[(d0 + j) * (C + kPadT) + s] = e[j] * f;
+                    }
+                }
+            }
+        }
+    }
+
     __device__ __forceinline__ void store(int D, E* nat, E* tr, const float* scale) const {
         const int sh = __builtin_ctz(D / V);
         const int total = C << sh;

@@ -108,6 +108,7 @@ struct BwdParams {
     float* dA1;               // [BH][T] q_t . dq_t
     float* dA2;               // [BH][T] k_t . dk_t
     int st_elems;             // bf16 elements of the LDS buffer that stages one carried state
+    int rs_nbuf;              // copies of the staged chunk the R(j) kernel keeps (1 or 2)
 };
 hipError_t launch_bwd_chunked(const BwdParams& p, bool bf16, hipStream_t stream);
 
