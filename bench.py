@@ -37,7 +37,7 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0    # dense bf16 MFMA, TFLOP/s
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd8k_decode_hbm_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd8k_bwd8k_decode_hbm_traffic.txt")
 
 
 def sources_hash(files: str) -> str:
@@ -483,7 +483,8 @@ def bench_backward(cfg, sets, stream, steps: int) -> dict:
     del ws, douts, grads
     return {"ms": ms, "tokens_per_s": tps, "alg_bytes": m["bytes"], "alg_flops": m["flops"],
             "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
-            "TFLOP/s": round(tfl, 1), "frac_mfma": round(tfl / BF16_PEAK_TFLOPS, 4)}
+            "TFLOP/s": round(tfl, 1), "frac_mfma": round(tfl / BF16_PEAK_TFLOPS, 4),
+            "traffic": measured_traffic("backward")}
 
 
 def bench_decode(steps: int) -> dict:
