@@ -394,15 +394,15 @@ __global__ __launch_bounds__(C / 16 * 64, C == 128 ? 2 : 3) void k_bwd_dq(BwdPar
     // and the next node's loads are issued before the current one is used;
     // otherwise the node is staged in rounds of srows of its dk rows.
     constexpr bool PF = NAT && FDK > 0 && FDV > 0;
-    constexpr int NS = PF ? FDK * FDV / (4 * NT) : 1;
+    constexpr int NS = PF ? FDK * FDV / (8 * NT) : 1;
     float* glrow = p.glam + trow * L;
-    auto node_of = [&](int pb) __attribute__((always_inline)) {
-        return p.gnode + ((size_t)bh * p.N + ((i >> pb) << pb) - 1) * dk * dv;
+    auto node_idx = [&](int pb) __attribute__((always_inline)) {
+        return ((size_t)bh * p.N + ((i >> pb) << pb) - 1) * dk * dv;
     };
-    StateRegs<NS, NT> st;
+    StateRegs16<NS, NT> st;
     unsigned bits = (unsigned)i;
     if constexpr (PF) {
-        if (bits) st.load(node_of(__builtin_ctz(bits)));
+        if (bits) st.load(p.gnode16 + node_idx(__builtin_ctz(bits)));
     }
     while (bits) {
         const int pb = __builtin_ctz(bits);
@@ -410,14 +410,13 @@ __global__ __launch_bounds__(C / 16 * 64, C == 128 ? 2 : 3) void k_bwd_dq(BwdPar
         const int lev = LOGC + pb + 1;
         const float e = rvalid ? __expf(Ar + dlog[pb]) : 0.f;
         const float lw = e * lamco[r * nlev + pb];
-        const float* G = node_of(pb);
         float dot = 0.f;
         if constexpr (PF) {
             const int pitch = dv + kPadB;
             __syncthreads();  // the previous node's reads are done
             st.store(dv, Gs);
             __syncthreads();
-            if (bits) st.load(node_of(__builtin_ctz(bits)));
+            if (bits) st.load(p.gnode16 + node_idx(__builtin_ctz(bits)));
 #pragma unroll
             for (int cb = 0; cb < NB; ++cb) {
                 if (16 * cb < dk) {
@@ -438,7 +437,7 @@ __global__ __launch_bounds__(C / 16 * 64, C == 128 ? 2 : 3) void k_bwd_dq(BwdPar
             const int srows = min(dk, (p.st_elems / pitch) & ~15);
             for (int r0 = 0; r0 < dk; r0 += srows) {
                 __syncthreads();  // the previous round's reads are done
-                stage_state_bf16<NT, kPadB>(G, dv, r0, min(srows, dk - r0), Gs);
+                stage_rows16<NT>(p.gnode16 + node_idx(pb), dv, r0, min(srows, dk - r0), Gs);
                 __syncthreads();
 #pragma unroll
                 for (int cb = 0; cb < NB; ++cb) {
@@ -461,7 +460,7 @@ __global__ __launch_bounds__(C / 16 * 64, C == 128 ? 2 : 3) void k_bwd_dq(BwdPar
             for (int cb = 0; cb < NB; ++cb) {
                 if (16 * cb < dk) {
                     f32x4 y = {0.f, 0.f, 0.f, 0.f};
-                    const float* grow = G + (size_t)(16 * cb + m) * dv + g * KPL;
+                    const float* grow = p.gnode + node_idx(pb) + (size_t)(16 * cb + m) * dv + g * KPL;
 #pragma unroll
                     for (int ks = 0; ks < MAXK; ++ks)
                         if (ks < nkv) y = mma(FR::from_f32(grow + ks * KS), df[ks], y);

@@ -211,7 +211,13 @@ __global__ __launch_bounds__(256) void k_fenwick_scan(FwdParams p) {
                         lcum[q] = c;
                     }
                 }
-                base[(size_t)i * per4] = acc;
+                if (!p.nodes16_only) base[(size_t)i * per4] = acc;
+                if (p.gnode16) {
+                    bf16x4 h;
+                    h[0] = (__bf16)acc.x; h[1] = (__bf16)acc.y; h[2] = (__bf16)acc.z;
+                    h[3] = (__bf16)acc.w;
+                    *reinterpret_cast<bf16x4*>(p.gnode16 + ((size_t)bh * p.N + i) * per4 * 4 + 4 * e4) = h;
+                }
                 if (frag) {
                     bf16x4 h;
                     h[0] = (__bf16)acc.x; h[1] = (__bf16)acc.y; h[2] = (__bf16)acc.z;

@@ -21,6 +21,8 @@ struct FwdParams {
     float* tot;          // workspace [BH][N]
     double* cum;         // workspace [BH][N]
     bf16_t_storage* gfrag;  // optional bf16 copy of the nodes in MFMA fragment order
+    bf16_t_storage* gnode16;  // optional bf16 copy of the nodes in the order of ust
+    bool nodes16_only;        // with gnode16: the fp32 nodes are not written back to ust
     const float* upart;  // optional [BH][N][nsub][dv][dk] states of sub-ranges (then tpart)
     const float* tpart;  // [BH][N][nsub] decay totals of the sub-ranges
     int nsub;            // sub-ranges per chunk (1, 2, 4 or 8) when upart is set
@@ -101,6 +103,7 @@ struct BwdParams {
     float* glam;              // [BH][T][L]
     int BH, T, dk, dv, L, C, N, nlev;  // nlev = bit_length(N - 1)
     const float* gnode;       // [BH][N][dk][dv] Fenwick nodes of sum k v^T over chunks
+    const bf16_t_storage* gnode16;  // the same in bf16 (bf16 inputs; gnode is then not written)
     const double* cum;        // [BH][N] A at the end of each chunk
     float* rst;               // [BH][N][dk][dv] block states R(j)
     float* rstT;              // [BH][N][dv][dk] the same, transposed (fp32 inputs)

@@ -437,9 +437,16 @@ loglin_status loglin_bwd_chunked(const void* q, const void* k, const void* v, co
         fp.ust = reinterpret_cast<float*>(base + w.nodes.ust_off);
         fp.tot = reinterpret_cast<float*>(base + w.nodes.tot_off);
         fp.cum = reinterpret_cast<double*>(base + w.nodes.cum_off);
+        if (in_dtype == LOGLIN_BF16) {
+            // bf16 inputs: the nodes only as bf16 (the operand form the dq
+            // kernel stages), in the region the fp32 R^T would use
+            fp.gnode16 = reinterpret_cast<bf16_t_storage*>(base + w.rstT_off);
+            fp.nodes16_only = true;
+        }
         hipError_t e = launch_fwd_chunked(fp, in_dtype == LOGLIN_BF16, kStageChunkState | kStageScan, hs);
         if (e != hipSuccess) return hip_fail(e, "loglin_bwd_chunked node launch");
         bp.gnode = fp.ust;
+        bp.gnode16 = fp.gnode16;
         bp.cum = fp.cum;
         bp.rst = reinterpret_cast<float*>(base + w.rst_off);
         bp.rstT = reinterpret_cast<float*>(base + w.rstT_off);
