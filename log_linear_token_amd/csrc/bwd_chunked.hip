@@ -59,10 +59,13 @@ struct BStep<float> {
 // Coarse levels a chunk can have: bit_length(N - 1) for N < 2^31 chunks.
 constexpr int kMaxLev = 32;
 
-// Padding (elements) of the bf16 natural copies and staged states: rows of
-// 64 or 128 elements plus 16 put the four rows of one transpose read, and
-// the four lane groups of a wave, on disjoint LDS banks.
+// Layout of the bf16 natural copies and staged states in LDS: rows padded by
+// 16 elements (64 or 128 + 16: consecutive rows start 8 banks apart), and
+// within each 16 rows, rows 8..15 store column c at c ^ 8.  Then the 8-byte
+// operand reads of 16 rows x 2 lane groups and the transpose reads of
+// 8 rows x 4 column quads each cover 64 distinct banks.
 constexpr int kPadB = 16;
+__device__ __forceinline__ int swz8(int row, int col) { return col ^ (row & 8); }
 
 template <int C>
 struct LogC {
@@ -77,7 +80,7 @@ __device__ __forceinline__ typename Frag<E, BStep<E>::KS>::type rows_op(const E*
                                                                         int D, int x0, int ks,
                                                                         int m, int g) {
     if constexpr (sizeof(E) == 2) {
-        return Frag<E, 16>::load(nat + (x0 + m) * (D + kPadB) + ks * 16 + 4 * g);
+        return Frag<E, 16>::load(nat + (x0 + m) * (D + kPadB) + swz8(m, ks * 16 + 4 * g));  // x0 % 16 == 0
     } else {
         return tr[(ks * 4 + g) * (C + kPadT) + x0 + m];
     }
@@ -135,7 +138,8 @@ typedef __attribute__((address_space(3))) bf16x4 lds_bf16x4_t;
 // read: in each group of 16 lanes, lane j names row k0 + 4g + j / 4 and
 // columns c0 + 4 (j % 4) .. + 3, and receives column c0 + j of the four rows.
 __device__ __forceinline__ bf16x4 tr_op(const bf16_t* X, int pitch, int k0, int c0, int m, int g) {
-    const bf16_t* a = X + (k0 + 4 * g + (m >> 2)) * pitch + c0 + 4 * (m & 3);
+    const int r = k0 + 4 * g + (m >> 2);  // k0 % 16 == 0: the swizzle of X applies
+    const bf16_t* a = X + r * pitch + swz8(r, c0 + 4 * (m & 3));
     return __builtin_amdgcn_ds_read_tr16_b64_v4bf16((lds_bf16x4_t*)a);
 }
 
@@ -158,32 +162,11 @@ __device__ __forceinline__ float sum_groups(float x) {  // over the 4 lanes of o
     return x;
 }
 
-// One carried state ([rows][cols] fp32 in global memory, rows * cols =
-// 4 NS NT) on its way to LDS as bf16: load() issues the thread's NS float4
-// loads into registers, where they stay in flight while the previous state
-// is being used; store() writes them with row stride cols + kPadB.
-template <int NS, int NT>
-struct StateRegs {
-    f32x4 buf[NS];  // a clang vector type, so that the array stays in registers
-    __device__ __forceinline__ void load(const float* __restrict__ g) {
-#pragma unroll
-        for (int u = 0; u < NS; ++u) buf[u] = reinterpret_cast<const f32x4*>(g)[threadIdx.x + u * NT];
-    }
-    __device__ __forceinline__ void store(int cols, bf16_t* dst) const {
-        const int sh = __builtin_ctz(cols / 4);
-        const int mask = (1 << sh) - 1;
-#pragma unroll
-        for (int u = 0; u < NS; ++u) {
-            const int idx = threadIdx.x + u * NT;
-            const int r = idx >> sh, c = (idx & mask) << 2;
-            *reinterpret_cast<bf16x4*>(dst + r * (cols + kPadB) + c) =
-                pack4(buf[u].x, buf[u].y, buf[u].z, buf[u].w);
-        }
-    }
-};
-
-// The same for a bf16 state ([rows][cols] bf16, rows * cols = 8 NS NT):
-// 16-byte copies, no conversion.
+// One carried state ([rows][cols] bf16 in global memory, rows * cols =
+// 8 NS NT) on its way to LDS: load() issues the thread's NS 16-byte loads
+// into registers, where they stay in flight while the previous state is
+// being used; store() writes them in the swizzled layout (row stride
+// cols + kPadB).
 typedef __attribute__((ext_vector_type(4))) unsigned int u32x4;
 
 template <int NS, int NT>
@@ -200,7 +183,7 @@ struct StateRegs16 {
         for (int u = 0; u < NS; ++u) {
             const int idx = threadIdx.x + u * NT;
             const int r = idx >> sh, c = (idx & mask) << 3;
-            *reinterpret_cast<u32x4*>(dst + r * (cols + kPadB) + c) = buf[u];
+            *reinterpret_cast<u32x4*>(dst + r * (cols + kPadB) + swz8(r, c)) = buf[u];
         }
     }
 };
@@ -227,7 +210,8 @@ __device__ __forceinline__ void stage_rows16(const bf16_t* __restrict__ g, int c
         for (int u = 0; u < RD; ++u) {
             const int idx = base + threadIdx.x + u * NT;
             if (idx < total)
-                *reinterpret_cast<uint4*>(dst + (idx >> sh) * (cols + kPadB) + ((idx & mask) << 3)) = buf[u];
+                *reinterpret_cast<uint4*>(dst + (idx >> sh) * (cols + kPadB) +
+                                          swz8(idx >> sh, (idx & mask) << 3)) = buf[u];
         }
     }
 }
@@ -319,7 +303,7 @@ __global__ __launch_bounds__(C / 16 * 64, C == 128 ? 2 : 3) void k_bwd_dq(BwdPar
     }
     const E* kg = static_cast<const E*>(p.k) + row0 * dk;
     const E* vg = static_cast<const E*>(p.v) + row0 * dv;
-    ChunkRows<E, C, DM, NT, kPadB> kr, vr;
+    ChunkRows<E, C, DM, NT, kPadB, true> kr, vr;
     kr.load(kg, dk, nvalid);
     vr.load(vg, dv, nvalid);
 
@@ -421,10 +405,10 @@ __global__ __launch_bounds__(C / 16 * 64, C == 128 ? 2 : 3) void k_bwd_dq(BwdPar
             for (int cb = 0; cb < NB; ++cb) {
                 if (16 * cb < dk) {
                     f32x4 y = {0.f, 0.f, 0.f, 0.f};
-                    const E* grow = Gs + (16 * cb + m) * pitch + 4 * g;
+                    const E* grow = Gs + (16 * cb + m) * pitch;
 #pragma unroll
                     for (int ks = 0; ks < MAXK; ++ks)
-                        if (ks < nkv) y = mma(Frag<bf16_t, 16>::load(grow + ks * 16), df[ks], y);
+                        if (ks < nkv) y = mma(Frag<bf16_t, 16>::load(grow + swz8(m, ks * 16 + 4 * g)), df[ks], y);
 #pragma unroll
                     for (int j = 0; j < 4; ++j) {
                         acc[cb][j] += lw * y[j];
@@ -443,10 +427,11 @@ __global__ __launch_bounds__(C / 16 * 64, C == 128 ? 2 : 3) void k_bwd_dq(BwdPar
                 for (int cb = 0; cb < NB; ++cb) {
                     if (16 * cb < dk && 16 * cb >= r0 && 16 * cb < r0 + srows) {
                         f32x4 y = {0.f, 0.f, 0.f, 0.f};
-                        const E* grow = Gs + (16 * cb - r0 + m) * pitch + 4 * g;
+                        const E* grow = Gs + (16 * cb - r0 + m) * pitch;  // r0 % 16 == 0
 #pragma unroll
                         for (int ks = 0; ks < MAXK; ++ks)
-                            if (ks < nkv) y = mma(Frag<bf16_t, 16>::load(grow + ks * 16), df[ks], y);
+                            if (ks < nkv)
+                                y = mma(Frag<bf16_t, 16>::load(grow + swz8(m, ks * 16 + 4 * g)), df[ks], y);
 #pragma unroll
                         for (int j = 0; j < 4; ++j) {
                             acc[cb][j] += lw * y[j];
@@ -740,7 +725,7 @@ __global__ __launch_bounds__(C / 16 * 64, C == 128 ? 2 : 3) void k_bwd_dkv(BwdPa
     }
     const E* qg = static_cast<const E*>(p.q) + row0 * dk;
     const E* og = static_cast<const E*>(p.dout) + row0 * dv;
-    ChunkRows<E, C, DM, NT, kPadB> qr, orr;
+    ChunkRows<E, C, DM, NT, kPadB, true> qr, orr;
     qr.load(qg, dk, nvalid);
     orr.load(og, dv, nvalid);
 
@@ -819,10 +804,10 @@ __global__ __launch_bounds__(C / 16 * 64, C == 128 ? 2 : 3) void k_bwd_dkv(BwdPa
             for (int cb = 0; cb < NB; ++cb) {
                 if (16 * cb < dk && 16 * cb >= r0 && 16 * cb < r0 + nr) {
                     f32x4 y = {0.f, 0.f, 0.f, 0.f};
-                    const E* rr = Ss + (16 * cb - r0 + m) * pitch + 4 * g;
+                    const E* rr = Ss + (16 * cb - r0 + m) * pitch;  // r0 % 16 == 0
 #pragma unroll
                     for (int ks = 0; ks < MAXK; ++ks)
-                        if (ks < nkv) y = mma(Frag<bf16_t, 16>::load(rr + ks * 16), vf[ks], y);
+                        if (ks < nkv) y = mma(Frag<bf16_t, 16>::load(rr + swz8(m, ks * 16 + 4 * g)), vf[ks], y);
 #pragma unroll
                     for (int q = 0; q < 4; ++q) acck[cb][q] += w * y[q];
                 }

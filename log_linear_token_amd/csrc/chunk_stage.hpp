@@ -85,7 +85,10 @@ __device__ __forceinline__ void stage_natural(const E* __restrict__ src, int D, 
 // nat[s][d] (row stride D + PADN) and/or a transposed copy tr[d][s] (row
 // stride C + kPadT, each token optionally multiplied by scale[s] from LDS);
 // either pointer may be null.
-template <typename E, int C, int DM, int NT, int PADN = kPadK>
+// SWZ: the natural copy's column c of row s is stored at c ^ (s & 8) (see
+// the backward kernels, whose direct and transpose reads this keeps free of
+// bank conflicts).
+template <typename E, int C, int DM, int NT, int PADN = kPadK, bool SWZ = false>
 struct ChunkRows {
     static constexpr int V = 16 / sizeof(E);
     static constexpr int NV = (C * DM / V + NT - 1) / NT;
@@ -159,7 +162,7 @@ struct ChunkRows {
             if (idx < total) {
                 int s, d0;
                 where(idx, sh, s, d0);
-                if (nat) *reinterpret_cast<uint4*>(nat + s * (D + PADN) + d0) = buf[u];
+                if (nat) *reinterpret_cast<uint4*>(nat + s * (D + PADN) + (SWZ ? d0 ^ (s & 8) : d0)) = buf[u];
                 if (tr) {
                     E e[V];
                     __builtin_memcpy(e, &buf[u], 16);
@@ -182,37 +185,6 @@ struct ChunkRows {
         }
     }
 };
-
-// Stage rows [r0, r0 + nr) of a row-major fp32 matrix with `cols` columns (a
-// power of two >= 4) into LDS as bf16, dst[r - r0][c] with row stride
-// cols + PADN.  NT threads; each round's loads (8 per thread) are all in
-// flight before its LDS writes.
-template <int NT, int PADN = kPadK>
-__device__ __forceinline__ void stage_state_bf16(const float* __restrict__ g, int cols, int r0, int nr,
-                                                 bf16_t* dst) {
-    constexpr int R = 8;
-    const int sh = __builtin_ctz(cols / 4);
-    const int mask = (1 << sh) - 1;
-    const int total = nr << sh;  // float4 vectors
-    const float4* src = reinterpret_cast<const float4*>(g + (size_t)r0 * cols);
-    for (int base = 0; base < total; base += R * NT) {
-        float4 buf[R];
-#pragma unroll
-        for (int u = 0; u < R; ++u) {  // no branch: out-of-range lanes read vector 0
-            const int idx = base + threadIdx.x + u * NT;
-            buf[u] = src[idx < total ? idx : 0];
-        }
-#pragma unroll
-        for (int u = 0; u < R; ++u) {
-            const int idx = base + threadIdx.x + u * NT;
-            if (idx < total) {
-                const int r = idx >> sh, c = (idx & mask) << 2;
-                *reinterpret_cast<bf16x4*>(dst + r * (cols + PADN) + c) =
-                    pack4(buf[u].x, buf[u].y, buf[u].z, buf[u].w);
-            }
-        }
-    }
-}
 
 template <int LOGC>
 __device__ __forceinline__ float pick_level(const float (&lamr)[LOGC + 1], int lev) {
