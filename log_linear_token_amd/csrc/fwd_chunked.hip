@@ -48,22 +48,37 @@ __global__ __launch_bounds__(256) void k_chunk_state(FwdParams p) {
     const int i = blk - bh * p.N;
     const int t0 = i * C;
     const int nvalid = min(C, p.T - t0);
-    float* a_raw = reinterpret_cast<float*>(smem);
-    float* A = a_raw + C;
-    float* e = A + C;
-    E* KT = reinterpret_cast<E*>(e + C);
+    E* KT = reinterpret_cast<E*>(smem);
     E* VT = KT + p.dk * (C + kPadT);
     const size_t row0 = (size_t)bh * p.T + t0;
+    const int lane0 = threadIdx.x & (kWave - 1);
 
-    for (int s = threadIdx.x; s < C; s += blockDim.x) a_raw[s] = s < nvalid ? p.a[row0 + s] : 0.f;
-    __syncthreads();
-    if (threadIdx.x < kWave) wave_cumsum(a_raw, A, C);
-    __syncthreads();
-    const float Aend = A[C - 1];
-    for (int s = threadIdx.x; s < C; s += blockDim.x) e[s] = __expf(Aend - A[s]);
-    __syncthreads();
-    stage_transposed<E, C>(static_cast<const E*>(p.k) + row0 * p.dk, p.dk, nvalid, KT, nullptr);
-    stage_transposed<E, C>(static_cast<const E*>(p.v) + row0 * p.dv, p.dv, nvalid, VT, e);
+    // Every load first, without branches (rows past T read the chunk's first
+    // row and are zeroed): a of tokens 2l and 2l + 1 in lane l of every wave,
+    // and the chunk's k and v rows.
+    const float a0 = p.a[row0 + min(2 * lane0, nvalid - 1)];
+    const float a1 = p.a[row0 + min(2 * lane0 + 1, nvalid - 1)];
+    ChunkRows<E, C, 128, 256> kr, vr;
+    kr.load(static_cast<const E*>(p.k) + row0 * p.dk, p.dk, nvalid);
+    vr.load(static_cast<const E*>(p.v) + row0 * p.dv, p.dv, nvalid);
+    // chunk-local inclusive sum of a in registers (each wave the whole
+    // chunk); the chunk total is lane 63's sum
+    const bool ok0 = 2 * lane0 < nvalid, ok1 = 2 * lane0 + 1 < nvalid;
+    const float x0 = ok0 ? a0 : 0.f, x1 = ok1 ? a1 : 0.f;
+    float incl = x0 + x1;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        const float y = __shfl_up(incl, off, kWave);
+        if (lane0 >= off) incl += y;
+    }
+    const float Aend = __shfl(incl, kWave - 1, kWave);
+    const float e0 = ok0 ? __expf(Aend - (incl - x1)) : 0.f;
+    const float e1 = ok1 ? __expf(Aend - incl) : 0.f;
+    kr.store(p.dk, nullptr, KT, nullptr);
+    vr.store_tr_scaled(p.dv, VT, [&](int s) __attribute__((always_inline)) {
+        const float y0 = __shfl(e0, s >> 1, kWave), y1 = __shfl(e1, s >> 1, kWave);
+        return (s & 1) ? y1 : y0;
+    });
     if (threadIdx.x == 0) p.tot[(size_t)bh * p.N + i] = Aend;
     __syncthreads();
 
@@ -355,7 +370,7 @@ __global__ __launch_bounds__(C / 16 * 64) void k_chunk_output(FwdParams p) {
 
 template <typename E, int C>
 size_t state_smem(int dk, int dv) {
-    return 3 * C * sizeof(float) + (size_t)(dk + dv) * (C + kPadT) * sizeof(E);
+    return (size_t)(dk + dv) * (C + kPadT) * sizeof(E);
 }
 template <typename E, int C, int DK>
 size_t output_smem(int dv) {
