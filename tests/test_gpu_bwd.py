@@ -94,3 +94,29 @@ def test_bwd_empty_is_noop():
     out = LL.loglin_bwd_chunked(z, z, z, torch.empty((1, 1, 0), device="cuda"),
                                 torch.empty((1, 1, 0, 4), device="cuda"), z, 16)
     assert all(x.numel() == 0 for x in out)
+
+
+def test_bwd_full_8k_workload_weak_decay():
+    """The 8K-token workload at full size (B=4, H=16, T=8192, d_k=128, d_v=64,
+    C=64, L=15), launched as the benchmark launches it, with the weak decay
+    (a = -softplus(N(-8, 0.5))) so that every coarse level carries weight:
+    the last (batch, head) slice against the oracle's gradients in full."""
+    from log_linear_token_amd import inputs as I
+
+    cfg = I.CONFIGS["fwd8k"]
+    banner(f"bwd full fwd8k weak B={cfg.B} H={cfg.H} T={cfg.T} dk={cfg.dk} dv={cfg.dv} C={cfg.C}")
+    d = I.make_fwd(cfg, "weak")
+    g = np.random.default_rng(cfg.seed + 5).standard_normal((cfg.B, cfg.H, cfg.T, cfg.dv)).astype(np.float32)
+    dt = torch.bfloat16
+    gd = to_dev(g, dt)
+    got = LL.loglin_bwd_chunked(to_dev(d["q"], dt), to_dev(d["k"], dt), to_dev(d["v"], dt),
+                                to_dev(d["a"]), to_dev(d["lam"]), gd, cfg.C)
+    torch.cuda.synchronize()
+    b, h = cfg.B - 1, cfg.H - 1
+    got = [x[b, h].cpu().numpy() for x in got]
+    g_r = gd[b, h].float().cpu().numpy().astype(np.float64)
+    want = ref.form_a_grads(d["q"][b, h], d["k"][b, h], d["v"][b, h], d["a"][b, h], d["lam"][b, h], g_r)
+    errs = {n: slice_rel_err(x[None], y[None], 1) for n, x, y in zip(NAMES, got, want)}
+    print("  " + " ".join(f"{n} {e:.2e}" for n, e in errs.items()), flush=True)
+    for n, e in errs.items():
+        assert e <= TOL_BF16, (n, e)
