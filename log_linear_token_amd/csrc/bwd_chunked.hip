@@ -919,31 +919,47 @@ __global__ __launch_bounds__(C / 16 * 64, C == 128 ? 2 : 3) void k_bwd_dkv(BwdPa
 }
 
 // --------------------------------------------------------------------------
-// da_j = sum_{t >= j} (dA1_t - dA2_t): one block per (batch, head), each
-// thread a contiguous run of tokens, fp64 sums.
+// da_j = sum_{t >= j} (dA1_t - dA2_t): one block per (batch, head), walking
+// the sequence from its end in tiles of 2048 tokens (8 consecutive tokens a
+// thread, so that loads and stores are contiguous over the block); fp64
+// sums, the sum of the later tiles carried from tile to tile.
 
 __global__ __launch_bounds__(256) void k_bwd_da(BwdParams p) {
-    __shared__ double part[256];
-    const int bh = blockIdx.x;
+    constexpr int PT = 8, NT = 256, TILE = PT * NT;
+    __shared__ double part[NT];
     const int tid = threadIdx.x;
-    const int per = (p.T + 255) / 256;
-    const int tb = min(p.T, tid * per), te = min(p.T, tb + per);
-    const size_t base = (size_t)bh * p.T;
-    double sum = 0.0;
-    for (int t = tb; t < te; ++t) sum += (double)p.dA1[base + t] - (double)p.dA2[base + t];
-    part[tid] = sum;
-    __syncthreads();
-    // inclusive suffix scan over the threads (Hillis-Steele)
-    for (int off = 1; off < 256; off <<= 1) {
-        const double y = tid + off < 256 ? part[tid + off] : 0.0;
+    const size_t base = (size_t)blockIdx.x * p.T;
+    double carry = 0.0;  // the tokens after the current tile
+    for (int t1 = p.T; t1 > 0; t1 -= TILE) {
+        const int t0 = max(0, t1 - TILE);
+        double x[PT];
+        double sum = 0.0;
+#pragma unroll
+        for (int j = 0; j < PT; ++j) {  // no branch: past t1 reads token t0 and is zeroed
+            const int t = t0 + tid * PT + j;
+            const int tc = t < t1 ? t : t0;
+            const double y = (double)p.dA1[base + tc] - (double)p.dA2[base + tc];
+            x[j] = t < t1 ? y : 0.0;
+            sum += x[j];
+        }
+        part[tid] = sum;
         __syncthreads();
-        part[tid] += y;
-        __syncthreads();
-    }
-    double run = part[tid] - sum;  // the threads after this one
-    for (int t = te - 1; t >= tb; --t) {
-        run += (double)p.dA1[base + t] - (double)p.dA2[base + t];
-        p.ga[base + t] = (float)run;
+        // inclusive suffix scan over the threads (Hillis-Steele)
+        for (int off = 1; off < NT; off <<= 1) {
+            const double y = tid + off < NT ? part[tid + off] : 0.0;
+            __syncthreads();
+            part[tid] += y;
+            __syncthreads();
+        }
+        double run = carry + part[tid] - sum;  // the threads after this one, and the later tiles
+#pragma unroll
+        for (int j = PT - 1; j >= 0; --j) {
+            const int t = t0 + tid * PT + j;
+            run += x[j];
+            if (t < t1) p.ga[base + t] = (float)run;
+        }
+        carry += part[0];
+        __syncthreads();  // part[] is rewritten by the next tile
     }
 }
 
