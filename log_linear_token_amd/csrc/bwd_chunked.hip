@@ -306,6 +306,17 @@ __global__ __launch_bounds__(C / 16 * 64, C == 128 ? 2 : 3) void k_bwd_dq(BwdPar
     ChunkRows<E, C, DM, NT, kPadB, true> kr, vr;
     kr.load(kg, dk, nvalid);
     vr.load(vg, dv, nvalid);
+    // the first coarse node (lowest set bit of i) as well: its loads stay in
+    // flight through the staging and the chunk's own block
+    constexpr bool PF = NAT && FDK > 0 && FDV > 0;
+    constexpr int NS = PF ? FDK * FDV / (8 * NT) : 1;
+    auto node_idx = [&](int pb) __attribute__((always_inline)) {
+        return ((size_t)bh * p.N + ((i >> pb) << pb) - 1) * dk * dv;
+    };
+    StateRegs16<NS, NT> st;
+    if constexpr (PF) {
+        if (i) st.load(p.gnode16 + node_idx(__builtin_ctz((unsigned)i)));
+    }
 
     if (threadIdx.x < C) a_raw[threadIdx.x] = (int)threadIdx.x < nvalid ? av : 0.f;
     if (threadIdx.x < nlev) dlog[threadIdx.x] = dl0;
@@ -377,17 +388,8 @@ __global__ __launch_bounds__(C / 16 * 64, C == 128 ? 2 : 3) void k_bwd_dq(BwdPar
     // head dims fixed at compile time (PF) the whole node is staged at once
     // and the next node's loads are issued before the current one is used;
     // otherwise the node is staged in rounds of srows of its dk rows.
-    constexpr bool PF = NAT && FDK > 0 && FDV > 0;
-    constexpr int NS = PF ? FDK * FDV / (8 * NT) : 1;
     float* glrow = p.glam + trow * L;
-    auto node_idx = [&](int pb) __attribute__((always_inline)) {
-        return ((size_t)bh * p.N + ((i >> pb) << pb) - 1) * dk * dv;
-    };
-    StateRegs16<NS, NT> st;
     unsigned bits = (unsigned)i;
-    if constexpr (PF) {
-        if (bits) st.load(p.gnode16 + node_idx(__builtin_ctz(bits)));
-    }
     while (bits) {
         const int pb = __builtin_ctz(bits);
         bits &= bits - 1;
@@ -728,6 +730,20 @@ __global__ __launch_bounds__(C / 16 * 64, C == 128 ? 2 : 3) void k_bwd_dkv(BwdPa
     ChunkRows<E, C, DM, NT, kPadB, true> qr, orr;
     qr.load(qg, dk, nvalid);
     orr.load(og, dv, nvalid);
+    // the coarse levels this chunk feeds (clear bits pb of i whose block
+    // j = ((i >> pb) | 1) << pb exists), and the first one's state, whose
+    // loads stay in flight through the staging and the chunk's own block
+    unsigned todo = 0;
+    for (int pb = 0; pb < nlev; ++pb)
+        if (!((i >> pb) & 1) && ((((i >> pb) | 1) << pb) < p.N)) todo |= 1u << pb;
+    auto block_of = [&](int pb) __attribute__((always_inline)) {
+        return (size_t)bh * p.N + (((i >> pb) | 1) << pb);
+    };
+    constexpr int NSR = (NAT && FDK > 0 && FDV > 0) ? FDK * FDV / (8 * NT) : 1;
+    StateRegs16<NSR, NT> str;
+    if constexpr (NAT && FDK > 0 && FDV > 0) {
+        if (todo) str.load(p.rst16 + block_of(__builtin_ctz(todo)) * dk * dv);
+    }
 
     if (threadIdx.x < C) a_raw[threadIdx.x] = (int)threadIdx.x < nvalid ? av : 0.f;
     if (threadIdx.x < nlev) wlog[threadIdx.x] = wl;
@@ -784,12 +800,6 @@ __global__ __launch_bounds__(C / 16 * 64, C == 128 ? 2 : 3) void k_bwd_dkv(BwdPa
     // Later blocks that see this chunk at a coarse level: the clear bits pb
     // of i whose block j = ((i >> pb) | 1) << pb exists, lowest first; each
     // adds w_s R(j) v_s to dk_s and w_s R(j)^T k_s to dv_s.
-    unsigned todo = 0;
-    for (int pb = 0; pb < nlev; ++pb)
-        if (!((i >> pb) & 1) && ((((i >> pb) | 1) << pb) < p.N)) todo |= 1u << pb;
-    auto block_of = [&](int pb) __attribute__((always_inline)) {
-        return (size_t)bh * p.N + (((i >> pb) | 1) << pb);
-    };
     if constexpr (NAT) {
         // R(j) is bf16 [dk][dv]: staged once per level for both products; the
         // dk rows read it as is (contraction over dv), the dv rows through
@@ -826,9 +836,7 @@ __global__ __launch_bounds__(C / 16 * 64, C == 128 ? 2 : 3) void k_bwd_dkv(BwdPa
             }
         };
         if constexpr (PF) {
-            constexpr int NS = FDK * FDV / (8 * NT);
-            StateRegs16<NS, NT> st;
-            if (todo) st.load(p.rst16 + block_of(__builtin_ctz(todo)) * dk * dv);
+            StateRegs16<NSR, NT>& st = str;
             while (todo) {
                 const int pb = __builtin_ctz(todo);
                 todo &= todo - 1;
