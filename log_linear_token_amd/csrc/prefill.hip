@@ -75,8 +75,21 @@ __global__ __launch_bounds__(NW * 64) void k_prefill_job(PrefillParams p) {
     const bf16_t* vg = reinterpret_cast<const bf16_t*>(p.v);
 
     // decay from the end of the job to position T - 1 (read after a barrier)
+    // (eight independent partial sums, so that eight loads are in flight)
     float part = 0.f;
-    for (int r = jb.s1 + (int)threadIdx.x; r < p.T; r += NW * 64) part += p.a[row0 + r];
+    {
+        constexpr int NT = NW * 64;
+        const int n = p.T - jb.s1;
+        const float* ap = p.a + row0 + jb.s1;
+        float ps[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+        int r = threadIdx.x;
+        for (; r + 7 * NT < n; r += 8 * NT) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) ps[j] += ap[r + j * NT];
+        }
+        for (; r < n; r += NT) ps[0] += ap[r];
+        part = ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
+    }
     for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o);
     if (lane == 0) sred[wave] = part;
 
