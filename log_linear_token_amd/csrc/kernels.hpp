@@ -128,12 +128,13 @@ struct PrefillParams {
 int prefill_jobs(int T);      // jobs the prefix of T tokens is cut into
 
 // Job j of the prefix of T tokens (n = T - 1 >= 0): the prefix is cut into
-// whole 1024-token pieces of the buckets of 1024 tokens or more (each such
-// bucket is a whole number of aligned pieces), one job per smaller bucket
-// (the set bits of n mod 1024, largest first) and a last one for level 0 (the
-// token n itself).  Token s < n lies in the bucket of level
-// floor(log2(n xor s)) + 1.
-constexpr int kPrefillJobTokens = 1024;
+// whole pieces of kPrefillJobTokens (512) tokens of the buckets of at least
+// that many tokens (each such bucket is a whole number of aligned pieces),
+// one job per smaller bucket (the set bits of n mod 512, largest first) and
+// a last one for level 0 (the token n itself).  Token s < n lies in the
+// bucket of level floor(log2(n xor s)) + 1.
+constexpr int kPrefillJobLog = 9;
+constexpr int kPrefillJobTokens = 1 << kPrefillJobLog;
 struct PrefillJob {
     int level, s0, s1;  // tokens [s0, s1) of level `level`
 };
@@ -145,7 +146,7 @@ __device__ __forceinline__ PrefillJob prefill_job(int n, int j) {
     }
     int jj = j - nfull;
     const int low = n % kPrefillJobTokens;
-    for (int p = 9; p >= 0; --p) {
+    for (int p = kPrefillJobLog - 1; p >= 0; --p) {
         if ((low >> p) & 1) {
             if (jj == 0) {
                 const int s0 = (n >> (p + 1)) << (p + 1);

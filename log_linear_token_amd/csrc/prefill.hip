@@ -9,7 +9,7 @@
 //     S^(l) = sum over s in bucket l of exp(A_{T-1} - A_s) k_s v_s^T.
 // Token s of the prefix lies in the bucket of level floor(log2((T-1) xor s)) + 1.
 //
-// The prefix is cut into jobs: whole 1024-token pieces of the buckets of 1024
+// The prefix is cut into jobs: whole 512-token pieces of the buckets of 512
 // tokens or more (every such bucket is a whole number of aligned pieces), one
 // job per smaller bucket, and one for level 0.  Each job's decayed sum is
 // computed for bf16 inputs on the matrix cores (k_prefill_job, with the
@@ -281,7 +281,7 @@ __global__ __launch_bounds__(kThr) void k_prefill_sum(PrefillParams p) {
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
     if (live) {
         // the pieces of a long bucket are consecutive jobs from the first
-        // piece: floor(s0 / 1024) of the bucket's first token
+        // piece: floor(s0 / kPrefillJobTokens) of the bucket's first token
         const float4* ws = reinterpret_cast<const float4*>(p.ws) + (size_t)bh * p.njobs * n4;
         const int first = ((n >> level) << level) / kPrefillJobTokens;
         const int count = (1 << (level - 1)) / kPrefillJobTokens;

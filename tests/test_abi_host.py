@@ -198,12 +198,12 @@ def test_status_strings(lib):
 # ---------------------------------------------------------------- prefill -> decode
 
 def _prefill_jobs(T):
-    """Pieces of the prefix: whole 1024-token pieces of the large buckets, one
-    per smaller bucket (set bits of (T-1) mod 1024), one for level 0."""
+    """Pieces of the prefix: whole 512-token pieces of the large buckets, one
+    per smaller bucket (set bits of (T-1) mod 512), one for level 0."""
     if T <= 0:
         return 0
     n = T - 1
-    return n // 1024 + bin(n % 1024).count("1") + 1
+    return n // 512 + bin(n % 512).count("1") + 1
 
 
 @pytest.mark.parametrize("B,H,T,dk,dv,Lmax", [(1, 1, 1, 16, 16, 1), (2, 3, 64, 64, 32, 8),

@@ -37,10 +37,12 @@ def _round(x, dtype):
 
 CASES = [
     # B, H, T, dk, dv, dtype: empty prefix aside, every ragged and power-of-two
-    # corner of the bucket decomposition, pieces of 1024 tokens and the tail
+    # corner of the bucket decomposition, whole 512-token pieces and the tail
     (1, 2, 1, 16, 16, torch.float32), (1, 2, 2, 16, 32, torch.float32),
     (1, 2, 63, 32, 16, torch.float32), (1, 2, 64, 16, 16, torch.float32),
-    (1, 2, 65, 64, 64, torch.float32), (2, 2, 1000, 64, 64, torch.bfloat16),
+    (1, 2, 65, 64, 64, torch.float32), (1, 2, 512, 64, 64, torch.bfloat16),
+    (1, 2, 513, 128, 64, torch.bfloat16), (1, 2, 514, 32, 32, torch.float32),
+    (2, 2, 1000, 64, 64, torch.bfloat16),
     (1, 2, 1024, 32, 32, torch.bfloat16), (1, 2, 1025, 128, 64, torch.bfloat16),
     (1, 1, 3000, 128, 128, torch.bfloat16), (1, 2, 5000, 16, 32, torch.float32),
 ]
