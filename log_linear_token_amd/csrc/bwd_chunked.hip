@@ -216,8 +216,6 @@ __device__ __forceinline__ void stage_rows16(const bf16_t* __restrict__ g, int c
     }
 }
 
-__device__ __forceinline__ float load_f32(const float* p) { return *p; }
-__device__ __forceinline__ float load_f32(const bf16_t* p) { return bf16_to_f32(*p); }
 
 // --------------------------------------------------------------------------
 // dq and dlambda: one block per chunk, one wave per 16 query rows
