@@ -66,6 +66,11 @@ CASES = [
     (1, 2, 777, 128, 64, 64, torch.bfloat16),
     (1, 1, 1100, 64, 128, 32, torch.bfloat16),
     (1, 1, 2048, 128, 128, 128, torch.bfloat16),
+    # the node scan in two levels (bf16, a multiple of 16 chunks, at least
+    # 32): two groups with a ragged last chunk, three groups, 16-token chunks
+    (1, 2, 2047, 64, 64, 64, torch.bfloat16),
+    (1, 1, 3072, 128, 64, 64, torch.bfloat16),
+    (1, 1, 1024, 32, 32, 16, torch.bfloat16),
 ]
 
 
