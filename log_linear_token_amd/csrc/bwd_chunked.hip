@@ -31,9 +31,12 @@
 //                 plus the chunk's own block
 //   da            the suffix sums of q_t . dq_t - k_t . dk_t
 //
-// Workspace (per (batch*head) bh): the forward's node buffers for G', R and
-// R^T ([N][dk][dv] and [N][dv][dk] fp32, R at the index j of the block's
-// first chunk), and the two dot products per token.
+// Workspace (per (batch*head) bh): the forward's chunk-state and node
+// buffers; R at the index j of its block's first chunk ([N][dk][dv]); the two
+// dot products per token.  fp32 inputs keep G' and R in fp32 and R^T
+// ([N][dv][dk]) beside R.  bf16 inputs keep G' ([N][dk][dv], in the R^T
+// region) and R in bf16 only: the operand form the dq and dk/dv kernels stage
+// (R^T is then read from R through LDS transpose reads).
 #include <algorithm>
 #include <type_traits>
 
