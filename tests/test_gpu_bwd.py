@@ -61,6 +61,8 @@ CASES = [
     (2, 1, 200, 64, 64, 32, torch.float32),
     (1, 2, 300, 32, 64, 64, torch.float32),
     (1, 1, 513, 128, 128, 128, torch.float32),
+    (1, 2, 1, 64, 64, 64, torch.bfloat16),
+    (1, 2, 40, 128, 64, 64, torch.bfloat16),
     (1, 2, 130, 16, 16, 16, torch.bfloat16),
     (2, 2, 1000, 64, 64, 64, torch.bfloat16),
     (1, 2, 777, 128, 64, 64, torch.bfloat16),
