@@ -121,23 +121,29 @@ constexpr int kScanDepth = 8;    // loads kept in flight per thread
 template <int NSUB>
 struct ScanLoad {
     float4 part[NSUB];
+    float tp[NSUB];  // decay totals of the segment (NSUB == 1) or of its sub-ranges,
+                     // loaded with the states rather than when they are combined
     __device__ void issue(const FwdParams& p, int bh, int e4, int per4, int i) {
         if constexpr (NSUB == 1) {
             part[0] = reinterpret_cast<const float4*>(p.ust)[((size_t)bh * p.N + i) * per4 + e4];
+            tp[0] = p.tot[(size_t)bh * p.N + i];
         } else {
             const float4* src = reinterpret_cast<const float4*>(p.upart) +
                                 (((size_t)bh * p.N + i) * NSUB) * per4 + e4;
+            const float* t = p.tpart + ((size_t)bh * p.N + i) * NSUB;
 #pragma unroll
-            for (int s = 0; s < NSUB; ++s) part[s] = src[(size_t)s * per4];
+            for (int s = 0; s < NSUB; ++s) {
+                part[s] = src[(size_t)s * per4];
+                tp[s] = t[s];
+            }
         }
     }
     // returns the combined state; *total receives the segment's decay total
     __device__ float4 combine(const FwdParams& p, int bh, int i, float* total) const {
         if constexpr (NSUB == 1) {
-            *total = p.tot[(size_t)bh * p.N + i];
+            *total = tp[0];
             return part[0];
         } else {
-            const float* tp = p.tpart + ((size_t)bh * p.N + i) * NSUB;
             float4 acc = part[NSUB - 1];
             float after = tp[NSUB - 1];  // decay of the sub-ranges after s
 #pragma unroll
