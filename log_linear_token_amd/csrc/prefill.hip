@@ -285,7 +285,18 @@ __global__ __launch_bounds__(kThr) void k_prefill_sum(PrefillParams p) {
         const float4* ws = reinterpret_cast<const float4*>(p.ws) + (size_t)bh * p.njobs * n4;
         const int first = ((n >> level) << level) / kPrefillJobTokens;
         const int count = (1 << (level - 1)) / kPrefillJobTokens;
-        for (int j = first; j < first + count; ++j) {
+        // four pieces' loads in flight at a time (the sum order is kept)
+        int j = first;
+        for (; j + 4 <= first + count; j += 4) {
+            float4 x[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) x[u] = ws[(size_t)(j + u) * n4 + e];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                s.x += x[u].x; s.y += x[u].y; s.z += x[u].z; s.w += x[u].w;
+            }
+        }
+        for (; j < first + count; ++j) {
             const float4 x = ws[(size_t)j * n4 + e];
             s.x += x.x; s.y += x.y; s.z += x.z; s.w += x.w;
         }
