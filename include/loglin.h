@@ -181,9 +181,11 @@ LOGLIN_API loglin_status loglin_bwd_chunked(const void* q, const void* k, const 
                                  size_t workspace_bytes, void* stream);
 
 /*
- * Decode state:/*
- * Decode state: for nseq sequences x H heads, Lmax level states of dk x dv
- * (S = sum k v^T orientation) plus the next position of each sequence.  Each
+ * Decode state ("Log-linear attention, and what a logarithm buys", section 2:
+ * every Fenwick bucket of the prefix keeps its own recurrent state, and the
+ * live set holds at most ceil(log2 t + 1) + 1 of them): for nseq sequences x
+ * H heads, Lmax level states of dk x dv (S = sum k v^T orientation) plus the
+ * next position of each sequence.  Each
  * level is held as an fp32 matrix and a scalar log-scale (the state is the
  * matrix times exp(scale)), and level 0, which only ever holds the newest
  * token's k v^T, as the vectors k and v once a step has run; a step then
@@ -196,11 +198,15 @@ LOGLIN_API loglin_status loglin_bwd_chunked(const void* q, const void* k, const 
 LOGLIN_API loglin_status loglin_state_init(loglin_state** st, int nseq, int H, int dk, int dv, int Lmax,
                                 void* stream);
 
-/* Releases the state's device memory (after synchronising the device).  NULL is a no-op. */
+/*
+ * Releases the state's device memory (after synchronising the device).  NULL
+ * is a no-op.  The state is the section-2 level set described above.
+ */
 LOGLIN_API loglin_status loglin_state_free(loglin_state* st);
 
 /*
- * Loads positions and level states.
+ * Loads positions and level states (a checkpoint of the section-2 level set,
+ * or the output of loglin_prefill_states).
  *   pos_host  [nseq] host int64: next position of each sequence (the state
  *             holds the buckets of tokens 0..pos-1); 0 <= pos <= 2^(Lmax-1)
  *   levels    [nseq, H, Lmax, dk, dv] device fp32, or NULL for all zeros.
@@ -215,8 +221,9 @@ LOGLIN_API loglin_status loglin_state_load(loglin_state* st, const int64_t* pos_
 /*
  * Exports positions (host, written before return) and the level states
  * [nseq, H, Lmax, dk, dv] (device fp32, enqueued on `stream`), with every
- * slot that is not live written as zero -- the states of the recurrence.
- * Either pointer may be NULL to skip that part.
+ * slot that is not live written as zero -- the states S_t^(l) of the
+ * section-2 recurrence after tokens 0..pos-1 (slot 0 and slot p+1 for each
+ * set bit p of pos-1 are live).  Either pointer may be NULL to skip that part.
  */
 LOGLIN_API loglin_status loglin_state_export(const loglin_state* st, int64_t* pos_host, float* levels,
                                   void* stream);
@@ -268,7 +275,10 @@ LOGLIN_API loglin_status loglin_prefill_states(const void* k, const void* v, con
 
 /*
  * Level map used by the kernels, for checking: out[t * T + s] = level(t, s)
- * for s <= t and -1 for s > t.  out is [T, T] device int8; 1 <= T <= 16384.
+ * for s <= t and -1 for s > t, where level(t, s) is the Fenwick bucket of
+ * key s in the prefix of query t ("Log-linear attention, and what a logarithm
+ * buys", section 2: 0 for s = t, else one more than the highest bit in which
+ * s and t differ).  out is [T, T] device int8; 1 <= T <= 16384.
  */
 LOGLIN_API loglin_status loglin_debug_level_map(int T, int8_t* out, void* stream);
 

@@ -159,8 +159,10 @@ __device__ __forceinline__ PrefillJob prefill_job(int n, int j) {
 }
 // A level whose bucket is at most one job long is written by its job
 // directly; the pieces of longer buckets go to the workspace and are summed.
+// (2^(level-1) <= 2^kPrefillJobLog, written without a shift so that every
+// level index up to the state's 48 slots is defined)
 __device__ __forceinline__ bool prefill_single(int level) {
-    return level == 0 || (1 << (level - 1)) <= kPrefillJobTokens;
+    return level <= kPrefillJobLog + 1;
 }
 // bf16 inputs: each job's decayed sum on the matrix cores
 hipError_t launch_prefill_jobs_bf16(const PrefillParams& p, hipStream_t stream);

@@ -276,7 +276,9 @@ __global__ __launch_bounds__(kThr) void k_prefill_sum(PrefillParams p) {
     const size_t e = (size_t)chunk * kThr + threadIdx.x;
     if (e >= n4) return;
     const int n = p.T - 1;
-    const bool live = n >= 0 && (level == 0 || ((n >> (level - 1)) & 1));
+    // n < 2^30, so no slot above level 31 is live (and the shift below
+    // stays within the 32-bit word)
+    const bool live = n >= 0 && (level == 0 || (level <= 31 && ((n >> (level - 1)) & 1)));
     if (live && prefill_single(level)) return;  // written by its job
     float4 s = make_float4(0.f, 0.f, 0.f, 0.f);
     if (live) {

@@ -147,28 +147,19 @@ def make_fwd(cfg: FwdConfig, variant: str = "base", seed: int | None = None) -> 
     }
 
 
-def live_levels(n: int) -> list[int]:
-    """Level slots that hold a bucket once tokens 0..n-1 have been absorbed.
-
-    This is bookkeeping for the synthetic prefill only (which slots to fill
-    with random states): slot 0 plus slot p+1 for every set bit p of n-1.
-    """
-    if n <= 0:
-        return []
-    m = n - 1
-    return [0] + [p + 1 for p in range(m.bit_length()) if (m >> p) & 1]
-
-
 def make_decode(cfg: DecodeConfig, variant: str = "base", seed: int | None = None,
-                fill: bool = True) -> dict:
+                fill: bool = True, live_slots=None) -> dict:
     """Draw a synthetic pre-filled decode state and the per-step inputs.
 
-    Every sequence gets a random prefill length n in [1, max_prefill]; the
-    level slots live after n tokens are filled with N(0, 1/dk) fp32 values,
-    the others are zero.  Per step: q, k, v [steps, nseq, H, d] (bf16 values,
-    N(0,1)/sqrt(dk)), a [steps, nseq, H], lam [steps, nseq, H, Lmax].
-    With fill=False the states are returned as None (callers that only need
-    the per-step inputs, or fill the device state themselves).
+    Every sequence gets a random prefill length n in [1, max_prefill].  With
+    fill=True the level slots are filled with N(0, 1/dk) fp32 values: only
+    the slots live_slots(n) lists (the others zero) when the caller passes
+    that function, every slot otherwise.  This module does not know which
+    slots a position uses; the state loader ignores the others.  Per step:
+    q, k, v [steps, nseq, H, d] (bf16 values, N(0,1)/sqrt(dk)),
+    a [steps, nseq, H], lam [steps, nseq, H, Lmax].  With fill=False the
+    states are returned as None (callers that only need the per-step inputs,
+    or fill the device state themselves).
     """
     rng = np.random.default_rng(cfg.seed if seed is None else seed)
     pos = rng.integers(1, cfg.max_prefill + 1, size=cfg.nseq).astype(np.int64)
@@ -178,7 +169,8 @@ def make_decode(cfg: DecodeConfig, variant: str = "base", seed: int | None = Non
         states = np.zeros(sshape, dtype=np.float32)
         sd = np.float32(1.0 / math.sqrt(cfg.dk))
         for s in range(cfg.nseq):
-            for lv in live_levels(int(pos[s])):
+            slots = range(cfg.Lmax) if live_slots is None else live_slots(int(pos[s]))
+            for lv in slots:
                 states[s, :, lv] = sd * rng.standard_normal((cfg.H, cfg.dk, cfg.dv),
                                                             dtype=np.float32)
     st = (cfg.steps, cfg.nseq, cfg.H)

@@ -107,6 +107,18 @@ def fenwick_buckets(t: int):
     return out
 
 
+def live_slots(n: int) -> list[int]:
+    """Level slots that hold a bucket once tokens 0..n-1 have been absorbed.
+
+    They are the levels of the buckets that query n-1 sees (section 2: the
+    newest token at level 0 and the greedy buckets of the older ones), read
+    off the greedy enumeration above.  Empty for n = 0.
+    """
+    if n <= 0:
+        return []
+    return sorted(lev for lev, _, _ in fenwick_buckets(n - 1))
+
+
 def level_row(t: int, length: int | None = None) -> np.ndarray:
     """int8 row: level of key s for query t (s <= t), -1 for s > t."""
     n = t + 1 if length is None else length

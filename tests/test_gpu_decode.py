@@ -47,7 +47,7 @@ def _live_mask_ok(levels, pos, Lmax, live_nonzero=True):
     """Exported slots that are not live must be exactly zero; live slots must
     hold data (checked unless decay may have flushed old levels to zero)."""
     for s, n in enumerate(pos):
-        live = set(I.live_levels(int(n)))
+        live = set(ref.live_slots(int(n)))
         for lv in range(Lmax):
             nz = bool(np.any(levels[s, :, lv] != 0))
             if lv not in live and nz:
@@ -118,7 +118,7 @@ def test_decode_from_empty_matches_materialised_mask():
 def test_synthetic_prefill_reduced():
     banner("decode synthetic prefill, reduced batch")
     cfg = I.CONFIGS["decode"].scaled(nseq=8, H=4, steps=64)
-    d = I.make_decode(cfg, "base", seed=11)
+    d = I.make_decode(cfg, "base", seed=11, live_slots=ref.live_slots)
     out, pos, lv = _decode_gpu(d, d["states"])
     pairs = [(s, h) for s in range(cfg.nseq) for h in range(cfg.H)]
     o_ref, st_ref, _ = _oracle(d, d["states"], pairs, cfg.steps)
@@ -135,7 +135,7 @@ def test_decode_workload_full_size(variant):
     the oracle follows 24 sampled (sequence, head) pairs through every step."""
     cfg = I.CONFIGS["decode"]
     banner(f"decode full size {variant}")
-    d = I.make_decode(cfg, variant)
+    d = I.make_decode(cfg, variant, live_slots=ref.live_slots)
     out, pos, lv = _decode_gpu(d, d["states"])
     rng = np.random.default_rng(4)
     pairs = sorted({(int(s), int(h)) for s, h in zip(rng.integers(0, cfg.nseq, 24),

@@ -299,3 +299,47 @@ def test_fwd8k_workload(variant):
 def test_long64k_workload(variant):
     _check_big("long64k", variant, full_slices=[(0, 3)], row_slices=[(0, 0), (0, 15)],
                prefix=2048)
+
+
+def _one_hot_level_rows(T, level, rng, n=40):
+    """Rows that read bucket `level` (bit level-1 of t set), the first and
+    last such rows of the sequence, and some rows that do not read it."""
+    reads = lambda t: (t >> (level - 1)) & 1  # noqa: E731
+    first = 1 << (level - 1)
+    rows = {first, min(T - 1, first + 63), T - 1}
+    rows.update(int(x) for x in rng.integers(0, T, n))
+    rows.update(t for t in (first - 1, T - 2) if t >= 0)
+    return sorted(r for r in rows if 0 <= r < T and (reads(r) or r % 5 == 0))
+
+
+# carried levels of the measured bf16 path: 64-token tiles, segments of 32
+# tiles, so levels 7..11 are held in registers inside a segment and levels
+# 12 and up come from the scan over segments
+CARRIED = [("fwd8k", lv) for lv in range(7, 14)] + [("long64k", lv) for lv in range(7, 17)]
+
+
+@pytest.mark.parametrize("name,level", CARRIED)
+def test_fused_one_hot_carried_level(name, level, monkeypatch):
+    """bf16 fused path at the measured shapes and segment length, lambda
+    one-hot on one carried level, weak decay: each register level and each
+    scanned level is checked on its own against the materialised mask."""
+    base = I.CONFIGS[name]
+    banner(f"fused one-hot level {level} at {name} shape")
+    monkeypatch.setenv("LOGLIN_FUSED_SEGMENT", "32")
+    cfg = base.scaled(B=1, H=2)
+    plan = LL.loglin_fwd_plan(cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv, cfg.C)
+    assert plan["path"] == "fused" and plan["seg_tiles"] == 32, plan
+    d = I.make_fwd(cfg, "weak", seed=level + cfg.T)
+    d["lam"][:] = 0.0
+    d["lam"][..., level] = 1.0
+    got = _run(d)
+    rng = np.random.default_rng(level)
+    rows = _one_hot_level_rows(cfg.T, level, rng)
+    errs = []
+    for h in range(cfg.H):
+        want = ref.form_a_rows(d["q"][0, h], d["k"][0, h], d["v"][0, h], d["a"][0, h],
+                               d["lam"][0, h], rows)
+        assert np.max(np.abs(want)) > 0.1
+        errs.append(slice_rel_err(got[0, h, rows], want, 0))
+    print(f"  one-hot level {level} ({name}): max rel err {max(errs):.3e}", flush=True)
+    assert max(errs) <= TOL_BF16, errs

@@ -62,7 +62,7 @@ def test_prefill_states_vs_recurrence(B, H, T, dk, dv, dtype, weak):
     print(f"  max state rel err {err:.2e}", flush=True)
     assert err <= tol, err
     # slots that are not live after T tokens are exactly zero
-    live = set(I.live_levels(T))
+    live = set(ref.live_slots(T))
     for lv in range(L):
         if lv not in live:
             assert not np.any(got[:, :, lv]), lv
@@ -103,4 +103,27 @@ def test_decode_continues_a_prefill(T, dk, dv, dtype):
     err = slice_rel_err(got, want, 2)
     tol = TOL_F32 if dtype == torch.float32 else TOL_BF16
     print(f"  max output rel err {err:.2e}", flush=True)
+    assert err <= tol, err
+
+
+@pytest.mark.parametrize("T,dtype", [(1000, torch.bfloat16), (5000, torch.float32),
+                                     (2049, torch.bfloat16)])
+def test_prefill_with_many_slots_zeroes_dead_ones(T, dtype):
+    """Lmax = 40 (slots far above the levels T uses, where a level index past
+    31 must not be taken for a live bucket) with the output buffer filled
+    with NaN first: live slots match the recurrence, every other slot is
+    exactly zero."""
+    banner(f"prefill Lmax=40 T={T} {dtype}")
+    B, H, dk, dv, Lmax = 1, 2, 32, 32, 40
+    q, k, v, a, lam = _inputs(B, H, T, dk, dv, Lmax, seed=T + 40, weak=True)
+    out = torch.full((B, H, Lmax, dk, dv), float("nan"), device="cuda")
+    got = LL.loglin_prefill_states(to_dev(k, dtype), to_dev(v, dtype), to_dev(a), Lmax,
+                                   out=out).cpu().numpy()
+    _, want = ref.form_b(q, _round(k, dtype), _round(v, dtype), a, lam, return_states=True)
+    live = set(ref.live_slots(T))
+    for lv in range(Lmax):
+        if lv not in live:
+            assert np.all(got[:, :, lv] == 0), lv
+    err = state_rel_err(got.reshape(B * H, Lmax, dk, dv), want.reshape(B * H, Lmax, dk, dv))
+    tol = TOL_F32 if dtype == torch.float32 else TOL_BF16
     assert err <= tol, err

@@ -20,9 +20,20 @@ def test_state_rel_err_floor():
     ref[0, 1] = 1e-80          # decayed far below fp32 range
     got = ref.copy()
     got[0, 1] = 0.0            # fp32 flushes it
-    assert state_rel_err(got, ref) < 1e-70
+    assert state_rel_err(got, ref) < 1e-40
     got[0, 0, 0, 0] = 1.5
     assert abs(state_rel_err(got, ref) - 0.5) < 1e-12
     got = ref.copy()
     got[0, 2, 1, 1] = 1e-3     # a dead level that should be zero
     assert state_rel_err(got, ref) >= 1e3
+
+
+def test_state_rel_err_floor_is_near_fp32_range():
+    """A level 1e-12 of its pair's largest is held to the full tolerance: a
+    20% error there must not pass as it did under a 1e-6 floor."""
+    ref = np.zeros((1, 2, 2, 2))
+    ref[0, 0] = 1.0
+    ref[0, 1] = 1e-12
+    got = ref.copy()
+    got[0, 1] *= 1.2
+    assert abs(state_rel_err(got, ref) - 0.2) < 1e-9

@@ -278,6 +278,9 @@ def test_live_levels_of_states():
         nz = [lv for lv in range(L) if np.any(st[lv] != 0)]
         want = [0] + [p + 1 for p in range((T - 1).bit_length()) if ((T - 1) >> p) & 1]
         assert nz == want, (T, nz, want)
+        # the live-slot list the parity tests use, read off the greedy buckets
+        assert ref.live_slots(T) == nz, (T, ref.live_slots(T), nz)
+    assert ref.live_slots(0) == []
 
 
 def test_capacity_error():
