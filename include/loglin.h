@@ -140,6 +140,33 @@ LOGLIN_API loglin_status loglin_fwd_chunked_stages(const void* q, const void* k,
                                         void* stream);
 
 /*
+ * Allocation-free forward, for callers that cannot allocate device memory:
+ * code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  It is loglin_fwd_chunked (same arguments, layouts, limits and
+ * numerics; the same kernels, so the same output bit for bit) with the
+ * workspace taken from a static device array inside the library instead of
+ * an argument.  The caller still passes every input and the output.
+ *  - The array holds LOGLIN_NOALLOC_SCRATCH_BYTES (64 MiB).  Sizes whose
+ *    workspace (loglin_fwd_workspace_bytes) is larger are rejected with
+ *    LOGLIN_EUNSUPPORTED before anything is enqueued.  The bf16 workloads
+ *    B=2,H=8,T=2048,d=64 (14 MB), B=4,H=16,T=8192,dk=128,dv=64 (28 MB) and
+ *    B=1,H=16,T=65536,d=128 (48 MB) fit.
+ *  - Each GPU the library runs on holds its own copy of the array until the
+ *    process ends.  The first call on a device looks up that copy's address
+ *    (with the device current); no call allocates or frees device memory.
+ *  - Every call on one GPU shares that GPU's array: calls that may overlap on
+ *    one GPU (two streams, or two threads without ordering between their
+ *    calls) race on it and may return wrong outputs.  Order such calls, e.g.
+ *    on one stream.  The array needs no clearing between calls.
+ */
+#define LOGLIN_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+LOGLIN_API loglin_status loglin_fwd_chunked_noalloc(const void* q, const void* k, const void* v,
+                                                    const float* log_decay, const float* lambda,
+                                                    float* out, int B, int H, int T, int dk,
+                                                    int dv, int L, int C, loglin_dtype in_dtype,
+                                                    void* stream);
+
+/*
  * Bytes of device workspace loglin_bwd_chunked needs for these sizes, or
  * (size_t)-1 (with the error text set) for sizes it would reject.
  */

@@ -74,6 +74,15 @@ loglin_status check_fwd_sizes(int B, int H, int T, int dk, int dv, int C) {
 }  // namespace
 
 namespace loglin {
+// the C ABI's error reporting for entry points defined in other sources
+loglin_status api_fail(loglin_status s, const char* fmt, ...) {
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(g_err, sizeof(g_err), fmt, ap);
+    va_end(ap);
+    return s;
+}
+
 FwdWorkspace fwd_workspace_layout(long BH, long N, int dk, int dv, bool frags, int nsub) {
     FwdWorkspace w{};
     if (N <= 1 || BH == 0) return w;

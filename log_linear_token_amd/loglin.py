@@ -65,6 +65,8 @@ def _load():
     lib.loglin_fwd_chunked_stages.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp,
                                               sz, ctypes.c_uint, vp]
     lib.loglin_fwd_chunked_stages.restype = i
+    lib.loglin_fwd_chunked_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp]
+    lib.loglin_fwd_chunked_noalloc.restype = i
     lib.loglin_fwd_plan.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(FwdPlan)]
     lib.loglin_fwd_plan.restype = i
     lib.loglin_state_init.argtypes = [ctypes.POINTER(vp), i, i, i, i, i, vp]
@@ -189,6 +191,32 @@ def loglin_fwd_chunked_stages(q, k, v, log_decay, lam, C: int, stage_mask: int, 
     nws = workspace.numel() * workspace.element_size() if workspace is not None else 0
     _check(_load().loglin_fwd_chunked_stages(pq, pk, pv, pa, pl, po, B, H, T, dk, dv, L, C,
                                              _DTYPES[q.dtype], pw, nws, stage_mask, _stream(q)))
+    return out
+
+
+NOALLOC_SCRATCH_BYTES = 64 << 20  # LOGLIN_NOALLOC_SCRATCH_BYTES
+
+
+def loglin_fwd_chunked_noalloc(q, k, v, log_decay, lam, C: int, out=None):
+    """loglin_fwd_chunked without a workspace argument: the library takes it
+    from its own static device array (no device allocation in the call).
+    `out` must be passed by callers that cannot allocate; when it is None it
+    is allocated here, outside the library call."""
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"q must be float32 or bfloat16 (got {q.dtype})")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    L = lam.shape[-1]
+    pq = _dev(q, "q", q.dtype)
+    pk = _dev(k, "k", q.dtype, (B, H, T, dk))
+    pv = _dev(v, "v", q.dtype, (B, H, T, dv))
+    pa = _dev(log_decay, "log_decay", torch.float32, (B, H, T))
+    pl = _dev(lam, "lam", torch.float32, (B, H, T, L))
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=torch.float32, device=q.device)
+    po = _dev(out, "out", torch.float32, (B, H, T, dv))
+    _check(_load().loglin_fwd_chunked_noalloc(pq, pk, pv, pa, pl, po, B, H, T, dk, dv, L, C,
+                                              _DTYPES[q.dtype], _stream(q)))
     return out
 
 

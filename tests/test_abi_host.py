@@ -281,3 +281,17 @@ def test_bwd_validation(lib):
     assert _bwd(lib, ws=None) == EINVAL
     assert _bwd(lib, ws=FAKE * 256 + 64) == EINVAL      # workspace misaligned
     assert _bwd(lib, B=0) == 0 and _bwd(lib, T=0, ws=None, nws=0) == 0
+
+
+def test_noalloc_rejects_on_the_host(lib):
+    """The allocation-free forward reports sizes its array cannot hold, and
+    whatever the forward itself rejects, before touching a device."""
+    f = lib.loglin_fwd_chunked_noalloc
+    f.argtypes = [ctypes.c_void_p] * 6 + [ctypes.c_int] * 8 + [ctypes.c_void_p]
+    f.restype = ctypes.c_int
+    # fp32 inputs at B=4, H=16, T=8192: a 256 MiB workspace
+    assert f(*([FAKE] * 6), 4, 16, 8192, 128, 64, 15, 64, 0, None) == EUNSUPPORTED
+    assert b"workspace" in lib.loglin_last_error()
+    assert f(*([FAKE] * 6), 1, 1, 64, 16, 16, 8, 48, 1, None) == EUNSUPPORTED  # chunk size
+    assert f(*([FAKE] * 6), 1, 1, 64, 16, 16, 3, 16, 1, None) == EINVAL        # levels
+    assert f(*([FAKE] * 6), 1, 1, 64, 16, 16, 8, 16, 7, None) == EINVAL        # dtype
