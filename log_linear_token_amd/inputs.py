@@ -14,6 +14,9 @@ mixer is measured on):
   fwd8k     B=4  H=16 T=8192  dk=128 dv=64    bf16 C=64  L=15  (long-memory decay)
   decode    128 sequences, H=32, dk=dv=128, fp32 states, Lmax=17, 256 steps
   long64k   B=1  H=16 T=65536 dk=dv=128       bf16 C=128 L=18
+  gdn8k     the fwd8k shape, log-linear Gated DeltaNet (beta added, q, k L2-normalised)
+  gdn2k     the fwd2k shape, log-linear Gated DeltaNet
+  gdn_decode the decode shape, log-linear Gated DeltaNet (beta per step)
 """
 from __future__ import annotations
 
@@ -82,6 +85,12 @@ CONFIGS = {
     "decode": DecodeConfig("decode", 4, 128, 32, 128, 128, 17, 256, 32768, "bf16"),
     "long64k": FwdConfig("long64k", 5, 1, 16, 65536, 128, 128, 128, 18, "bf16", "scaled", -3.0,
                          0.5, "uniform"),
+    # log-linear Gated DeltaNet (make_gdn adds beta): the 8K and 2K shapes
+    "gdn8k": FwdConfig("gdn8k", 6, 4, 16, 8192, 128, 64, 64, 15, "bf16", "l2", -2.0, 0.5,
+                       "softplus"),
+    "gdn2k": FwdConfig("gdn2k", 7, 2, 8, 2048, 64, 64, 64, 13, "bf16", "l2", 0.0, 1.0,
+                       "uniform"),
+    "gdn_decode": DecodeConfig("gdn_decode", 8, 128, 32, 128, 128, 17, 256, 32768, "bf16"),
 }
 
 
@@ -106,6 +115,22 @@ def _store(x: np.ndarray, dtype: str) -> np.ndarray:
     return round_bf16(x) if dtype == "bf16" else x
 
 
+def _sigmoid(x: np.ndarray) -> np.ndarray:
+    return (1.0 / (1.0 + np.exp(-x.astype(np.float64)))).astype(np.float32)
+
+
+def make_gdn(cfg: FwdConfig, variant: str = "base", seed: int | None = None) -> dict:
+    """Inputs of a log-linear Gated DeltaNet forward: make_fwd's q, k, v, a, lam
+    (q, k unit L2 norm over dk whatever cfg.qk says, as the delta rule needs
+    ||k|| <= 1 for beta <= 1 to keep its transition contractive) plus the
+    writing strength beta [B,H,T] = sigmoid(N(0,1)), drawn after the rest
+    from the same generator."""
+    rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    d = _draw_fwd(replace(cfg, qk="l2"), variant, rng)
+    d["beta"] = _sigmoid(rng.standard_normal((cfg.B, cfg.H, cfg.T), dtype=np.float32))
+    return d
+
+
 def make_fwd(cfg: FwdConfig, variant: str = "base", seed: int | None = None) -> dict:
     """Draw q, k, v, a, lam for one forward workload.
 
@@ -115,6 +140,10 @@ def make_fwd(cfg: FwdConfig, variant: str = "base", seed: int | None = None) -> 
     lam [B,H,T,L] plus the config.
     """
     rng = np.random.default_rng(cfg.seed if seed is None else seed)
+    return _draw_fwd(cfg, variant, rng)
+
+
+def _draw_fwd(cfg: FwdConfig, variant: str, rng: np.random.Generator) -> dict:
     shp = (cfg.B, cfg.H, cfg.T)
     q = rng.standard_normal(shp + (cfg.dk,), dtype=np.float32)
     k = rng.standard_normal(shp + (cfg.dk,), dtype=np.float32)
@@ -185,9 +214,13 @@ def make_decode(cfg: DecodeConfig, variant: str = "base", seed: int | None = Non
     else:
         raise ValueError(f"unknown variant {variant!r}")
     lam = rng.random(st + (cfg.Lmax,), dtype=np.float32)
+    # writing strength of the Gated DeltaNet step (drawn last; unused by the
+    # scalar-gated mixer)
+    beta = _sigmoid(rng.standard_normal(st, dtype=np.float32))
     return {
         "cfg": cfg,
         "pos": pos,
+        "beta": beta,
         "states": states,
         "q": _store(q, cfg.dtype),
         "k": _store(k, cfg.dtype),

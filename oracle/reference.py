@@ -19,6 +19,13 @@ Two independent forms of the same output are provided:
   (loglin_oracle.c), which also serves decode.
 * The backward pass -- the gradients of Form A by the chain rule
   (form_a_grads), pinned by finite differences of Form A.
+* The log-linear Gated DeltaNet -- section 1 says Gated DeltaNet differs from
+  Mamba-2 in how it structures A (the query-key interaction), not the mask M,
+  and section 3 lifts such a layer by composing its temporal mask with the
+  level mask.  gdn_form_a writes that out with the masked (parallel) form of
+  the gated delta rule of the Gated DeltaNet paper (the page's source 3);
+  gdn_form_b (C) runs the Fenwick recurrence with the gated delta-rule
+  transition on every bucket state.
 
 Readings of points the page leaves open (positions 0-indexed, oldest tokens in
 the largest bucket, lambda indexed by the query, the decay convention) are
@@ -65,6 +72,14 @@ def _load():
         _lib.llo_decode.argtypes = [dp, ip, dp, dp, dp, dp, dp, dp, ctypes.c_long, ctypes.c_int,
                                     ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int]
         _lib.llo_decode.restype = ctypes.c_int
+        _lib.llo_gdn_fwd_recurrent.argtypes = [dp, dp, dp, dp, dp, dp, dp, dp, ctypes.c_long,
+                                               ctypes.c_long, ctypes.c_int, ctypes.c_int,
+                                               ctypes.c_int, ctypes.c_int]
+        _lib.llo_gdn_fwd_recurrent.restype = ctypes.c_int
+        _lib.llo_gdn_decode.argtypes = [dp, ip, dp, dp, dp, dp, dp, dp, dp, ctypes.c_long,
+                                        ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                                        ctypes.c_int]
+        _lib.llo_gdn_decode.restype = ctypes.c_int
     return _lib
 
 
@@ -304,4 +319,95 @@ def decode(states, pos, q, k, v, a, lam, nthreads: int | None = None):
                             nthreads or default_threads())
     if rc != LLO_OK:
         raise RuntimeError(f"oracle decode failed with code {rc}")
+    return out, st, ps
+
+
+# --------------------------------------------------------------------------
+# Log-linear Gated DeltaNet
+
+def gdn_form_a(q, k, v, a, beta, lam) -> np.ndarray:
+    """Log-linear Gated DeltaNet with the mask written out, per slice (fp64).
+
+    The gated delta rule (the Gated DeltaNet paper, the page's source 3) is
+    S_t = exp(a_t) (I - beta_t k_t k_t^T) S_{t-1} + beta_t k_t v_t^T with
+    o_t = S_t^T q_t.  Its masked form P = A (.) M^S, O = P V has the
+    1-semiseparable decay mask M^S[t, s] = exp(A_t - A_s) of Mamba-2 and the
+    query-key interaction
+        A = (Q K^T (.) L) (I + diag(beta) (K K^T (.) (L - I)))^-1 diag(beta),
+    L the lower triangle with the diagonal; the decay factors out of the
+    inverse because it is a diagonal similarity (section 1: Gated DeltaNet
+    changes A, not M).  Section 3 lifts it by the elementwise product with the
+    level mask: P = A (.) M^S (.) M^H, M^H[t, s] = lambda_t^(level(t, s)).
+
+    q, k [..., T, dk]; v [..., T, dv]; a, beta [..., T]; lam [..., T, L].
+    Allocates T x T per slice (meant for T up to a few thousand).
+    """
+    from scipy.linalg import solve_triangular
+
+    q, k, v, a, beta, lam = map(_f64, (q, k, v, a, beta, lam))
+    lead = q.shape[:-2]
+    T, dk = q.shape[-2:]
+    dv = v.shape[-1]
+    L = lam.shape[-1]
+    lev = level_map(T).astype(np.int64)
+    tri = lev >= 0                      # s <= t
+    strict = np.tril(np.ones((T, T), dtype=bool), -1)
+    if T > 0 and lev.max() >= L:
+        raise ValueError(f"lambda has {L} levels; T={T} needs {lev.max() + 1}")
+    qf, kf, vf = q.reshape(-1, T, dk), k.reshape(-1, T, dk), v.reshape(-1, T, dv)
+    af, bf, lf = a.reshape(-1, T), beta.reshape(-1, T), lam.reshape(-1, T, L)
+    out = np.zeros((qf.shape[0], T, dv))
+    rows = np.arange(T)[:, None]
+    for i in range(qf.shape[0]):
+        A = np.cumsum(af[i])
+        # unit lower-triangular system of the delta rule, solved for diag(beta)
+        system = np.eye(T) + bf[i][:, None] * np.where(strict, kf[i] @ kf[i].T, 0.0)
+        inv_beta = solve_triangular(system, np.diag(bf[i]), lower=True, unit_diagonal=True)
+        interaction = np.where(tri, qf[i] @ kf[i].T, 0.0) @ inv_beta
+        decay = np.where(tri, np.exp(np.where(tri, A[:, None] - A[None, :], 0.0)), 0.0)
+        lvl = np.where(tri, lf[i][rows, np.maximum(lev, 0)], 0.0)
+        out[i] = (interaction * decay * lvl) @ vf[i]
+    return out.reshape(*lead, T, dv)
+
+
+def gdn_form_b(q, k, v, a, beta, lam, nthreads: int | None = None, return_states: bool = False):
+    """Log-linear Gated DeltaNet by the token-by-token Fenwick recurrence (C,
+    fp64): every carried or merged bucket state goes through
+    exp(a_t) (I - beta_t k_t k_t^T) at each step and beta_t k_t v_t^T enters
+    level 0.  Shapes as in gdn_form_a; with return_states also the level
+    states after the last token, [..., L, dk, dv]."""
+    q, k, v, a, beta, lam = map(_f64, (q, k, v, a, beta, lam))
+    lead = q.shape[:-2]
+    T, dk = q.shape[-2:]
+    dv = v.shape[-1]
+    L = lam.shape[-1]
+    BH = int(np.prod(lead)) if lead else 1
+    out = np.zeros((BH, T, dv))
+    st = np.zeros((BH, L, dk, dv)) if return_states else None
+    rc = _load().llo_gdn_fwd_recurrent(_ptr(q), _ptr(k), _ptr(v), _ptr(a), _ptr(beta), _ptr(lam),
+                                       _ptr(out), _ptr(st) if st is not None else None, BH, T,
+                                       dk, dv, L, nthreads or default_threads())
+    if rc != LLO_OK:
+        raise RuntimeError(f"oracle Gated DeltaNet recurrence failed with code {rc}")
+    out = out.reshape(*lead, T, dv)
+    if return_states:
+        return out, st.reshape(*lead, L, dk, dv)
+    return out
+
+
+def gdn_decode(states, pos, q, k, v, a, beta, lam, nthreads: int | None = None):
+    """Continue P (sequence, head) pairs of the log-linear Gated DeltaNet by
+    `steps` tokens; as decode() with beta [steps, P]."""
+    st = _f64(states).copy()
+    ps = np.ascontiguousarray(np.asarray(pos, dtype=np.int64)).copy()
+    q, k, v, a, beta, lam = map(_f64, (q, k, v, a, beta, lam))
+    steps, P, dk = q.shape
+    dv = v.shape[-1]
+    L = st.shape[1]
+    out = np.zeros((steps, P, dv))
+    rc = _load().llo_gdn_decode(_ptr(st), _ptr(ps, ctypes.c_int64), _ptr(q), _ptr(k), _ptr(v),
+                                _ptr(a), _ptr(beta), _ptr(lam), _ptr(out), P, steps, dk, dv, L,
+                                nthreads or default_threads())
+    if rc != LLO_OK:
+        raise RuntimeError(f"oracle Gated DeltaNet decode failed with code {rc}")
     return out, st, ps
