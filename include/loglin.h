@@ -167,6 +167,55 @@ LOGLIN_API loglin_status loglin_fwd_chunked_noalloc(const void* q, const void* k
                                                     void* stream);
 
 /*
+ * Log-linear Gated DeltaNet, chunked forward.  "Log-linear attention, and
+ * what a logarithm buys": Gated DeltaNet changes the query-key interaction,
+ * not the mask (section 1), and the log-linear lift composes its temporal mask
+ * with the Fenwick level mask (section 3).  With the gated delta rule of the
+ * Gated DeltaNet paper (the page's source 3), every bucket state takes the
+ * transition G_t = exp(a_t) (I - beta_t k_t k_t^T) and token t writes
+ * beta_t k_t v_t^T into level 0, so
+ *   o_t = sum_{s <= t} lambda_t^(level(t,s)) beta_s (q_t^T G_t ... G_{s+1} k_s) v_s,
+ * i.e. O = (A (.) M^S (.) M^H) V with
+ * A = (Q K^T (.) L)(I + diag(beta)(K K^T (.) (L - I)))^-1 diag(beta).
+ *
+ *   q, k, v, log_decay, lambda, out, B, H, T, L, in_dtype
+ *              as for loglin_fwd_chunked (same layouts)
+ *   beta       [B, H, T] fp32, the writing strength, 0 <= beta_t <= 1
+ *              (documented, not checked)
+ *   dk         64 or 128;  dv  16, 32 or 64 (else LOGLIN_EUNSUPPORTED)
+ *   C          validated as for loglin_fwd_chunked; the kernels always work
+ *              on 64-token chunks (the result does not depend on the split)
+ *   workspace  at least loglin_gdn_fwd_workspace_bytes(...) bytes, 256-byte
+ *              aligned (NULL allowed when that is 0); contents on entry
+ *              ignored, on return unspecified
+ * Numerics: fp32 matrix cores throughout (bf16 inputs are widened exactly);
+ * the delta rule's triangular system is inverted per chunk in fp32.  Keys of
+ * unit norm keep the transition contractive; other keys are computed as
+ * written.  B, H or T equal to 0 is a no-op.
+ */
+LOGLIN_API size_t loglin_gdn_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int C,
+                                                 loglin_dtype in_dtype);
+LOGLIN_API loglin_status loglin_gdn_fwd_chunked(const void* q, const void* k, const void* v,
+                                                const float* log_decay, const float* beta,
+                                                const float* lambda, float* out, int B, int H,
+                                                int T, int dk, int dv, int L, int C,
+                                                loglin_dtype in_dtype, void* workspace,
+                                                size_t workspace_bytes, void* stream);
+/*
+ * Profiling variant: bit 0 the per-chunk kernel (the chunk's own output, its
+ * read-out queries, transition and state), bit 1 the walk over chunk levels
+ * (adds the coarse levels to `out`).  `out` is the mixer's output only after
+ * both ran in order on the same workspace.  Other bits: LOGLIN_EINVAL.
+ */
+LOGLIN_API loglin_status loglin_gdn_fwd_chunked_stages(const void* q, const void* k, const void* v,
+                                                       const float* log_decay, const float* beta,
+                                                       const float* lambda, float* out, int B,
+                                                       int H, int T, int dk, int dv, int L, int C,
+                                                       loglin_dtype in_dtype, void* workspace,
+                                                       size_t workspace_bytes, unsigned stage_mask,
+                                                       void* stream);
+
+/*
  * Bytes of device workspace loglin_bwd_chunked needs for these sizes, or
  * (size_t)-1 (with the error text set) for sizes it would reject.
  */
@@ -269,6 +318,25 @@ LOGLIN_API loglin_status loglin_state_export(const loglin_state* st, int64_t* po
 LOGLIN_API loglin_status loglin_decode_step(loglin_state* st, const void* q, const void* k, const void* v,
                                  const float* log_decay, const float* lambda, float* out,
                                  loglin_dtype in_dtype, void* stream);
+
+/*
+ * One decode step of the log-linear Gated DeltaNet for every (sequence, head)
+ * on a state from loglin_state_init (section 2's Fenwick update with the gated
+ * delta-rule transition of loglin_gdn_fwd_chunked): at position t with
+ * j = lssb(t), levels 0..j are summed, taken through
+ * G_t = exp(a_t)(I - beta_t k_t k_t^T) and promoted to level j+1; every live
+ * level above is taken through G_t; beta_t k_t v_t^T enters level 0 (at t = 0
+ * only that); o_t = sum_l lambda^(l) q^T S^(l).
+ *   q, k, v, log_decay, lambda, out, in_dtype  as for loglin_decode_step
+ *   beta   [nseq, H] fp32
+ * A state must be stepped by one mixer only (this call or
+ * loglin_decode_step); export and load work the same for both.
+ * LOGLIN_ECAPACITY as for loglin_decode_step.
+ */
+LOGLIN_API loglin_status loglin_gdn_decode_step(loglin_state* st, const void* q, const void* k,
+                                                const void* v, const float* log_decay,
+                                                const float* beta, const float* lambda, float* out,
+                                                loglin_dtype in_dtype, void* stream);
 
 /*
  * Prefill -> decode hand-over ("Log-linear attention, and what a logarithm

@@ -87,6 +87,32 @@ struct DecodeParams {
 };
 
 hipError_t launch_decode_step(const DecodeParams& p, bool bf16, hipStream_t stream);
+// one step of the log-linear Gated DeltaNet (beta [nseq][H]) on the same state
+hipError_t launch_gdn_decode_step(const DecodeParams& p, const float* beta, bool bf16,
+                                  hipStream_t stream);
+
+// Chunked forward of the log-linear Gated DeltaNet (csrc/gdn_fwd.hip)
+constexpr int kGdnChunk = 64;                 // tokens per chunk
+constexpr size_t kGdnLdsMax = 160 * 1024;     // LDS one block may use on gfx950
+struct GdnParams {
+    const void* q;       // [BH][T][dk]
+    const void* k;       // [BH][T][dk]
+    const void* v;       // [BH][T][dv]
+    const float* a;      // [BH][T]
+    const float* beta;   // [BH][T]
+    const float* lam;    // [BH][T][L]
+    float* out;          // [BH][T][dv]
+    int BH, T, dk, dv, L;
+    int N;               // chunks per sequence
+    int nlev;            // chunk levels the walk holds: bit_length(N - 1)
+    float* fmat;         // [BH][N][dk*dk] chunk transitions (MFMA operand order)
+    float* qp;           // [BH][N][64*dk] read-out queries (MFMA operand order)
+    float* ust;          // [BH][N][dk][dv] each chunk's own state at its end
+};
+// LDS bytes of the level walk for head dim dk holding nlev levels
+size_t gdn_levels_smem(int dk, int nlev);
+// stages: bit 0 the per-chunk kernel, bit 1 the level walk
+hipError_t launch_gdn_fwd(const GdnParams& p, bool bf16, unsigned stages, hipStream_t stream);
 
 // Backward pass of the chunked forward: gradients of sum(O (.) dO)
 struct BwdParams {

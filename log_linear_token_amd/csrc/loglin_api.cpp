@@ -331,6 +331,117 @@ loglin_status loglin_fwd_chunked(const void* q, const void* k, const void* v,
 }  // extern "C"
 
 // ---------------------------------------------------------------------------
+// log-linear Gated DeltaNet: chunked forward
+
+namespace {
+
+struct GdnWorkspace {
+    size_t f_off, q_off, u_off, total;
+};
+
+GdnWorkspace gdn_layout(long BH, int T, int dk, int dv) {
+    GdnWorkspace w{};
+    const long N = ((long)T + kGdnChunk - 1) / kGdnChunk;
+    if (BH == 0 || N <= 1) return w;
+    w.f_off = 0;
+    w.q_off = align_up(w.f_off + (size_t)BH * N * dk * dk * sizeof(float));
+    w.u_off = align_up(w.q_off + (size_t)BH * N * kGdnChunk * dk * sizeof(float));
+    w.total = align_up(w.u_off + (size_t)BH * N * dk * dv * sizeof(float));
+    return w;
+}
+
+loglin_status check_gdn_sizes(int B, int H, int T, int dk, int dv, int C) {
+    loglin_status s = check_fwd_sizes(B, H, T, dk, dv, C);
+    if (s != LOGLIN_OK) return s;
+    if (dk != 64 && dk != 128)
+        return fail(LOGLIN_EUNSUPPORTED, "Gated DeltaNet forward: dk=%d must be 64 or 128", dk);
+    if (dv != 16 && dv != 32 && dv != 64)
+        return fail(LOGLIN_EUNSUPPORTED, "Gated DeltaNet forward: dv=%d must be 16, 32 or 64", dv);
+    const long N = ((long)T + kGdnChunk - 1) / kGdnChunk;
+    const int nlev = bit_length(N - 1);
+    if (gdn_levels_smem(dk, nlev) > kGdnLdsMax)
+        return fail(LOGLIN_EUNSUPPORTED, "Gated DeltaNet forward: T=%d needs %d chunk levels, "
+                    "more than one block holds", T, nlev);
+    return LOGLIN_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t loglin_gdn_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int C,
+                                      loglin_dtype in_dtype) {
+    if (check_gdn_sizes(B, H, T, dk, dv, C) != LOGLIN_OK) return (size_t)-1;
+    if (in_dtype != LOGLIN_F32 && in_dtype != LOGLIN_BF16) {
+        fail(LOGLIN_EINVAL, "in_dtype %d is neither LOGLIN_F32 nor LOGLIN_BF16", (int)in_dtype);
+        return (size_t)-1;
+    }
+    return gdn_layout((long)B * H, T, dk, dv).total;
+}
+
+loglin_status loglin_gdn_fwd_chunked_stages(const void* q, const void* k, const void* v,
+                                            const float* log_decay, const float* beta,
+                                            const float* lambda, float* out, int B, int H, int T,
+                                            int dk, int dv, int L, int C, loglin_dtype in_dtype,
+                                            void* workspace, size_t workspace_bytes,
+                                            unsigned stage_mask, void* stream) {
+    if (stage_mask & ~3u) return fail(LOGLIN_EINVAL, "stage mask 0x%x has unknown bits", stage_mask);
+    loglin_status s = check_gdn_sizes(B, H, T, dk, dv, C);
+    if (s != LOGLIN_OK) return s;
+    if (in_dtype != LOGLIN_F32 && in_dtype != LOGLIN_BF16)
+        return fail(LOGLIN_EINVAL, "in_dtype %d is neither LOGLIN_F32 nor LOGLIN_BF16", (int)in_dtype);
+    if ((long)B * H * T == 0) return ok();
+    if (L < levels_needed(T) || L > 64)
+        return fail(LOGLIN_EINVAL, "L=%d: T=%d needs %d levels (and L <= 64)", L, T, levels_needed(T));
+    if (!q || !k || !v || !log_decay || !beta || !lambda || !out)
+        return fail(LOGLIN_EINVAL, "null tensor pointer");
+    const long BH = (long)B * H;
+    const GdnWorkspace w = gdn_layout(BH, T, dk, dv);
+    if (w.total > 0) {
+        if (!workspace || workspace_bytes < w.total)
+            return fail(LOGLIN_EINVAL, "workspace of %zu bytes needed, got %zu%s", w.total,
+                        workspace_bytes, workspace ? "" : " (NULL)");
+        if (reinterpret_cast<uintptr_t>(workspace) % kAlign != 0)
+            return fail(LOGLIN_EINVAL, "workspace must be %zu-byte aligned", kAlign);
+    }
+    GdnParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.a = log_decay;
+    p.beta = beta;
+    p.lam = lambda;
+    p.out = out;
+    p.BH = (int)BH;
+    p.T = T;
+    p.dk = dk;
+    p.dv = dv;
+    p.L = L;
+    p.N = (int)(((long)T + kGdnChunk - 1) / kGdnChunk);
+    p.nlev = bit_length(p.N - 1);
+    if (w.total > 0) {
+        char* base = static_cast<char*>(workspace);
+        p.fmat = reinterpret_cast<float*>(base + w.f_off);
+        p.qp = reinterpret_cast<float*>(base + w.q_off);
+        p.ust = reinterpret_cast<float*>(base + w.u_off);
+    }
+    hipError_t e = launch_gdn_fwd(p, in_dtype == LOGLIN_BF16, stage_mask, static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "loglin_gdn_fwd_chunked launch");
+    return ok();
+}
+
+loglin_status loglin_gdn_fwd_chunked(const void* q, const void* k, const void* v,
+                                     const float* log_decay, const float* beta, const float* lambda,
+                                     float* out, int B, int H, int T, int dk, int dv, int L, int C,
+                                     loglin_dtype in_dtype, void* workspace, size_t workspace_bytes,
+                                     void* stream) {
+    return loglin_gdn_fwd_chunked_stages(q, k, v, log_decay, beta, lambda, out, B, H, T, dk, dv, L,
+                                         C, in_dtype, workspace, workspace_bytes, 3u, stream);
+}
+
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
 // backward pass
 
 namespace {
@@ -673,6 +784,35 @@ loglin_status loglin_decode_step(loglin_state* st, const void* q, const void* k,
     p.out = out;
     hipError_t e = launch_decode_step(p, in_dtype == LOGLIN_BF16, static_cast<hipStream_t>(stream));
     if (e != hipSuccess) return hip_fail(e, "loglin_decode_step launch");
+    st->step += 1;
+    return ok();
+}
+
+loglin_status loglin_gdn_decode_step(loglin_state* st, const void* q, const void* k, const void* v,
+                                     const float* log_decay, const float* beta, const float* lambda,
+                                     float* out, loglin_dtype in_dtype, void* stream) {
+    loglin_status s = check_state(st);
+    if (s != LOGLIN_OK) return s;
+    if (in_dtype != LOGLIN_F32 && in_dtype != LOGLIN_BF16)
+        return fail(LOGLIN_EINVAL, "in_dtype %d is neither LOGLIN_F32 nor LOGLIN_BF16", (int)in_dtype);
+    if (!q || !k || !v || !log_decay || !beta || !lambda || !out)
+        return fail(LOGLIN_EINVAL, "null tensor pointer");
+    if (reinterpret_cast<uintptr_t>(out) % 16)
+        return fail(LOGLIN_EINVAL, "out must be 16-byte aligned");
+    const int64_t t = st->max_base + st->step;
+    if (t >= ((int64_t)1 << (st->Lmax - 1)))
+        return fail(LOGLIN_ECAPACITY, "position %lld needs more than %d levels", (long long)t,
+                    st->Lmax);
+    DecodeParams p = decode_params(st);
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.a = log_decay;
+    p.lam = lambda;
+    p.out = out;
+    hipError_t e = launch_gdn_decode_step(p, beta, in_dtype == LOGLIN_BF16,
+                                          static_cast<hipStream_t>(stream));
+    if (e != hipSuccess) return hip_fail(e, "loglin_gdn_decode_step launch");
     st->step += 1;
     return ok();
 }

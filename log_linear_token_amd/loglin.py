@@ -67,6 +67,12 @@ def _load():
     lib.loglin_fwd_chunked_stages.restype = i
     lib.loglin_fwd_chunked_noalloc.argtypes = [vp, vp, vp, vp, vp, vp, i, i, i, i, i, i, i, i, vp]
     lib.loglin_fwd_chunked_noalloc.restype = i
+    lib.loglin_gdn_fwd_workspace_bytes.argtypes = [i, i, i, i, i, i, i]
+    lib.loglin_gdn_fwd_workspace_bytes.restype = sz
+    lib.loglin_gdn_fwd_chunked_stages.argtypes = [vp] * 7 + [i] * 8 + [vp, sz, ctypes.c_uint, vp]
+    lib.loglin_gdn_fwd_chunked_stages.restype = i
+    lib.loglin_gdn_decode_step.argtypes = [vp] * 8 + [i, vp]
+    lib.loglin_gdn_decode_step.restype = i
     lib.loglin_fwd_plan.argtypes = [i, i, i, i, i, i, i, ctypes.POINTER(FwdPlan)]
     lib.loglin_fwd_plan.restype = i
     lib.loglin_state_init.argtypes = [ctypes.POINTER(vp), i, i, i, i, i, vp]
@@ -220,6 +226,48 @@ def loglin_fwd_chunked_noalloc(q, k, v, log_decay, lam, C: int, out=None):
     return out
 
 
+# ---------------------------------------------------------------- Gated DeltaNet
+
+def loglin_gdn_fwd_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, C: int,
+                                   dtype=torch.bfloat16) -> int:
+    n = _load().loglin_gdn_fwd_workspace_bytes(B, H, T, dk, dv, C, _dt_code(dtype))
+    if n == ctypes.c_size_t(-1).value:
+        raise LoglinError(LOGLIN_EUNSUPPORTED, loglin_last_error())
+    return n
+
+
+GDN_STAGE_CHUNK, GDN_STAGE_LEVELS, GDN_STAGE_ALL = 1, 2, 3
+
+
+def loglin_gdn_fwd_chunked(q, k, v, log_decay, beta, lam, C: int, out=None, workspace=None,
+                           stage_mask: int = GDN_STAGE_ALL):
+    """Log-linear Gated DeltaNet forward: q, k [B,H,T,dk], v [B,H,T,dv] (float32
+    or bfloat16), log_decay and beta [B,H,T] float32, lam [B,H,T,L] float32.
+    Returns out [B,H,T,dv] float32."""
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"q must be float32 or bfloat16 (got {q.dtype})")
+    B, H, T, dk = q.shape
+    dv = v.shape[-1]
+    L = lam.shape[-1]
+    pq = _dev(q, "q", q.dtype)
+    pk = _dev(k, "k", q.dtype, (B, H, T, dk))
+    pv = _dev(v, "v", q.dtype, (B, H, T, dv))
+    pa = _dev(log_decay, "log_decay", torch.float32, (B, H, T))
+    pb = _dev(beta, "beta", torch.float32, (B, H, T))
+    pl = _dev(lam, "lam", torch.float32, (B, H, T, L))
+    if out is None:
+        out = torch.empty((B, H, T, dv), dtype=torch.float32, device=q.device)
+    po = _dev(out, "out", torch.float32, (B, H, T, dv))
+    need = loglin_gdn_fwd_workspace_bytes(B, H, T, dk, dv, C, q.dtype)
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    pw = _dev(workspace, "workspace") if workspace is not None else None
+    nws = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    _check(_load().loglin_gdn_fwd_chunked_stages(pq, pk, pv, pa, pb, pl, po, B, H, T, dk, dv, L, C,
+                                                 _DTYPES[q.dtype], pw, nws, stage_mask, _stream(q)))
+    return out
+
+
 # ---------------------------------------------------------------- backward
 
 def loglin_bwd_workspace_bytes(B: int, H: int, T: int, dk: int, dv: int, C: int,
@@ -369,6 +417,25 @@ def loglin_decode_step(st: DecodeState, q, k, v, log_decay, lam, out=None):
     po = _dev(out, "out", torch.float32, (st.nseq, st.H, st.dv))
     _check(_load().loglin_decode_step(st.handle, pq, pk, pv, pa, pl, po, _DTYPES[q.dtype],
                                       _stream(q)))
+    return out
+
+
+def loglin_gdn_decode_step(st: DecodeState, q, k, v, log_decay, beta, lam, out=None):
+    """One log-linear Gated DeltaNet decode step: q, k [nseq,H,dk], v [nseq,H,dv],
+    log_decay and beta [nseq,H], lam [nseq,H,Lmax].  Returns out [nseq,H,dv]."""
+    if q.dtype not in _DTYPES:
+        raise ValueError(f"q must be float32 or bfloat16 (got {q.dtype})")
+    pq = _dev(q, "q", q.dtype, (st.nseq, st.H, st.dk))
+    pk = _dev(k, "k", q.dtype, (st.nseq, st.H, st.dk))
+    pv = _dev(v, "v", q.dtype, (st.nseq, st.H, st.dv))
+    pa = _dev(log_decay, "log_decay", torch.float32, (st.nseq, st.H))
+    pb = _dev(beta, "beta", torch.float32, (st.nseq, st.H))
+    pl = _dev(lam, "lam", torch.float32, (st.nseq, st.H, st.Lmax))
+    if out is None:
+        out = torch.empty((st.nseq, st.H, st.dv), dtype=torch.float32, device=q.device)
+    po = _dev(out, "out", torch.float32, (st.nseq, st.H, st.dv))
+    _check(_load().loglin_gdn_decode_step(st.handle, pq, pk, pv, pa, pb, pl, po, _DTYPES[q.dtype],
+                                          _stream(q)))
     return out
 
 
