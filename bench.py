@@ -243,6 +243,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-gdn", action="store_true",
+                    help="skip the log-linear Gated DeltaNet forward and decode")
     ap.add_argument("--no-other", action="store_true",
                     help="skip the 2K and 64K forward workloads")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -344,6 +346,9 @@ def main() -> int:
                                      for n in ("fwd2k", "long64k")]
     if not args.no_decode:
         result["decode"] = bench_decode(args.decode_steps)
+    if not args.no_gdn:
+        result["gated_deltanet"] = {"forward": bench_gdn_fwd(args.steps, args.warmup),
+                                    "decode": bench_gdn_decode(args.decode_steps)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, d)
     print(json.dumps(result), flush=True)
@@ -530,6 +535,162 @@ def bench_decode(steps: int) -> dict:
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
                          "frac": round(gbs / HBM_PEAK_GBS, 4),
                          "traffic": measured_traffic("decode_step"),
+                         "alg_bytes_per_step": byts}}
+
+
+# --------------------------------------------------------------------- Gated DeltaNet
+
+FP32_PEAK_TFLOPS = 157.3     # dense fp32 MFMA, TFLOP/s
+
+
+def gdn_models(cfg) -> dict:
+    """Algorithmic bytes and flops per launch of the two Gated DeltaNet kernels
+    (64-token chunks, bf16 inputs).
+
+    Chunk kernel: reads q, k, v, a, beta and the 7 intra-chunk levels of
+    lambda once; writes the chunk's output and, for every chunk but the last
+    of a sequence, its read-out queries q' (64 x dk), transition F (dk x dk)
+    and state U (dk x dv) in fp32.  Flops: the products of full 16 x 16
+    tiles it computes -- Q K^T and K K^T on the 10 lower tiles, the block
+    inverse, W, U0, the chunk block Y Tb, P V, q', F and U.
+    Level walk: reads q', F, U and the coarse lambda of every chunk once and
+    the output once, writes the output once (the level states stay in LDS).
+    Flops: per chunk one read-out per live level (64 x dk x dv) and one
+    transition per level carried (dk x dk x dv).
+    """
+    B, H, T, dk, dv, L = cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv, cfg.L
+    BH = B * H
+    N = -(-T // 64)
+    nst = N - 1                      # chunks whose q', F and U are written
+    tile = 16 * 16 * 2
+    # a 16 x 16 output tile contracted over K costs tile * K flops; the lower
+    # tiles of a 64-token chunk contract over 16 (ti + 1) tokens, 10 * 16 in all
+    intra = (2 * 10 * tile * dk          # Q K^T and K K^T, lower tiles
+             + 12 * 16 * tile            # the off-diagonal blocks of the inverse
+             + 10 * 16 * tile * dk // 16 * 2  # W and q' (W: Tb Kd; q': Y W)
+             + 10 * 16 * tile * dv // 16 * 2  # U0 = Tb V and P V
+             + 20 * 16 * tile)           # Y Tb on the lower tiles
+    states = 64 * 2 * dk * dk + 64 * 2 * dk * dv
+    chunk_bytes = BH * T * (2 * (2 * dk + dv) + 8 + 4 * min(L, 7) + 4 * dv) \
+        + BH * nst * 4 * (64 * dk + dk * dk + dk * dv)
+    walk_reads = sum(bin(i).count("1") for i in range(N))
+    walk_trans = sum(1 + bin(i >> ((i + 1) & -(i + 1)).bit_length()).count("1")
+                     for i in range(N - 1))
+    lu = (T - 1).bit_length() + 1
+    walk_bytes = BH * nst * 4 * (64 * dk + dk * dk + dk * dv) + BH * T * (4 * max(0, lu - 7) + 8 * dv)
+    return {
+        "gdn_chunk": {"bytes": chunk_bytes, "flops": BH * (N * intra + nst * states)},
+        "gdn_levels": {"bytes": walk_bytes,
+                       "flops": BH * (walk_reads * 64 * 2 * dk * dv + walk_trans * 2 * dk * dk * dv)},
+    }
+
+
+def bench_gdn_fwd(steps: int, warmup: int) -> dict:
+    """Log-linear Gated DeltaNet forward on the gdn8k workload (the fwd8k
+    shape with a writing strength beta): the whole step, then each kernel
+    alone, against the fp32 MFMA and HBM rooflines."""
+    cfg = I.CONFIGS["gdn8k"]
+    log(f"gdn8k: generating inputs (B={cfg.B} H={cfg.H} T={cfg.T} dk={cfg.dk} dv={cfg.dv})")
+    d = I.make_gdn(cfg, "base")
+    dev = lambda x, dt=torch.float32: torch.from_numpy(x).to("cuda").to(dt).contiguous()  # noqa
+    base = tuple(dev(d[n], torch.bfloat16) for n in ("q", "k", "v")) + \
+        tuple(dev(d[n]) for n in ("a", "beta", "lam"))
+    del d
+    sets = [base + (torch.empty((cfg.B, cfg.H, cfg.T, cfg.dv), device="cuda"),)]
+    for _ in range(NSETS - 1):
+        sets.append(tuple(x.clone() for x in base) +
+                    (torch.empty((cfg.B, cfg.H, cfg.T, cfg.dv), device="cuda"),))
+    ws = torch.empty(LL.loglin_gdn_fwd_workspace_bytes(cfg.B, cfg.H, cfg.T, cfg.dk, cfg.dv, cfg.C,
+                                                       torch.bfloat16),
+                     dtype=torch.uint8, device="cuda")
+    stream = torch.cuda.current_stream()
+    state = {"i": 0}
+
+    def fwd(mask=LL.GDN_STAGE_ALL):
+        q, k, v, a, b, lam, out = sets[state["i"] % NSETS]
+        state["i"] += 1
+        LL.loglin_gdn_fwd_chunked(q, k, v, a, b, lam, cfg.C, out=out, workspace=ws, stage_mask=mask)
+
+    for _ in range(warmup):
+        fwd()
+    ms = timed(fwd, steps, stream)
+    tps = cfg.B * cfg.T / (ms / 1e3)
+    models = gdn_models(cfg)
+    kernels = {}
+    for name, mask in (("gdn_chunk", LL.GDN_STAGE_CHUNK), ("gdn_levels", LL.GDN_STAGE_LEVELS)):
+        fwd(mask)
+        kms = timed(lambda: fwd(mask), max(5, steps), stream)
+        m = models[name]
+        tfl = m["flops"] / (kms / 1e3) / 1e12
+        gbs = m["bytes"] / (kms / 1e3) / 1e9
+        kernels[name] = {"ms": round(kms, 4), "TFLOP/s": round(tfl, 1),
+                         "frac_fp32_mfma": round(tfl / FP32_PEAK_TFLOPS, 4),
+                         "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
+                         "alg_bytes": m["bytes"], "alg_flops": m["flops"]}
+        log(f"  {name}: {kms:.3f} ms, {tfl:.1f} TFLOP/s fp32, {gbs:.0f} GB/s")
+    log(f"gdn8k forward: {ms:.3f} ms/step, {tps:.3e} tokens/s")
+    del sets, ws, base
+    torch.cuda.empty_cache()
+    return {"workload": "gdn8k", "tokens_per_s": tps, "ms_per_step": ms,
+            "config": {"B": cfg.B, "H": cfg.H, "T": cfg.T, "dk": cfg.dk, "dv": cfg.dv, "L": cfg.L},
+            "kernels": kernels}
+
+
+def gdn_decode_bytes(pos0: np.ndarray, H: int, dk: int, dv: int, Lmax: int, steps: int) -> float:
+    """Average algorithmic bytes per Gated DeltaNet decode step: at position
+    t >= 1 the popcount(t-1) live levels above 0 are read and the popcount(t)
+    levels above 0 after the step are written (the merged one and every
+    carried one: the rank-one part of the transition changes each matrix);
+    on the first step after a load level 0 is a loaded matrix and is read.
+    Plus q, k, v (bf16), a, beta, lambda, the scales, the level-0 vectors
+    and out."""
+    st = dk * dv * 4
+    small = (2 * dk + dv) * 2 + 8 + Lmax * 4 + 2 * Lmax * 4 + 2 * (dk + dv) * 4 + dv * 4
+    tot = 0.0
+    for s in range(steps):
+        t = pos0 + s
+        rd = np.array([bin(int(x) - 1).count("1") + (1 if s == 0 else 0) if x >= 1 else 0 for x in t])
+        wr = np.array([bin(int(x)).count("1") if x >= 1 else 0 for x in t])
+        tot += float(np.sum(rd + wr)) * st * H + len(t) * H * small
+    return tot / steps
+
+
+def bench_gdn_decode(steps: int) -> dict:
+    cfg = I.CONFIGS["gdn_decode"]
+    log(f"gdn decode: {cfg.nseq} sequences x {cfg.H} heads, Lmax={cfg.Lmax}, {steps} steps")
+    d = I.make_decode(cfg.scaled(steps=steps), "base", fill=False)
+    pos = d["pos"]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(cfg.seed)
+    levels = torch.randn((cfg.nseq, cfg.H, cfg.Lmax, cfg.dk, cfg.dv), device="cuda",
+                         generator=g) * (1.0 / np.sqrt(cfg.dk))
+    st = LL.loglin_state_init(cfg.nseq, cfg.H, cfg.dk, cfg.dv, cfg.Lmax)
+    q, k, v = (torch.from_numpy(d[n]).to("cuda").to(torch.bfloat16) for n in ("q", "k", "v"))
+    a, beta, lam = (torch.from_numpy(d[n]).to("cuda") for n in ("a", "beta", "lam"))
+    out = torch.empty((cfg.nseq, cfg.H, cfg.dv), device="cuda")
+    stream = torch.cuda.current_stream()
+    LL.loglin_state_load(st, pos, levels)
+    for s in range(min(steps, 64)):
+        LL.loglin_gdn_decode_step(st, q[s], k[s], v[s], a[s], beta[s], lam[s], out=out)
+    LL.loglin_state_load(st, pos, levels)
+    del levels
+    it = iter(range(steps))
+
+    def step():
+        s = next(it)
+        LL.loglin_gdn_decode_step(st, q[s], k[s], v[s], a[s], beta[s], lam[s], out=out)
+
+    ms = timed(step, steps, stream)
+    LL.loglin_state_free(st)
+    sps = 1e3 / ms
+    byts = gdn_decode_bytes(pos, cfg.H, cfg.dk, cfg.dv, cfg.Lmax, steps)
+    gbs = byts / (ms / 1e3) / 1e9
+    log(f"gdn decode: {ms:.3f} ms/step, {sps:.1f} steps/s, {gbs:.0f} GB/s")
+    return {"steps_per_s": sps, "tokens_per_s": sps * cfg.nseq, "ms_per_step": ms, "steps": steps,
+            "config": {"workload": "gdn_decode", "nseq": cfg.nseq, "H": cfg.H, "dk": cfg.dk,
+                       "dv": cfg.dv, "Lmax": cfg.Lmax},
+            "roofline": {"kernel": "gdn_decode_step", "bound": "hbm", "achieved": round(gbs, 1),
+                         "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
                          "alg_bytes_per_step": byts}}
 
 
