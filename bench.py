@@ -169,21 +169,43 @@ def fwd_models(cfg, plan) -> dict:
 def decode_bytes(pos0: np.ndarray, H: int, dk: int, dv: int, Lmax: int, steps: int) -> float:
     """Average algorithmic bytes per decode step (steps counted from a load).
 
-    At position t >= 1 each (sequence, head) reads the popcount(t-1) live
-    levels above 0 (fp32 d_k x d_v each; the output needs them) and writes the
-    merged level j+1.  Level 0 is the previous token's k and v (two vectors)
-    except on the first step after a load, when it is the loaded matrix and is
-    read as such.  Plus q, k, v (bf16), a, lambda, the level scales (read and
-    written), the level-0 vectors (read and written) and out."""
+    The step keeps levels 0..6 of position t as the raw k, v rows (fp32, plus
+    the running decay sum) of t's 64-token window and levels >= 7 as fp32
+    d_k x d_v matrices.  Inside a window (t mod 64 = m > 0) it reads the m
+    earlier rows and the live matrix levels (set bits >= 6 of t) and writes
+    one row.  At a window boundary (m = 0) it reads the finished window's 64
+    rows and the matrix levels 7..j below the merge, writes the merged level
+    j+1, and reads the live levels above.  Until the first boundary after a
+    load the loaded levels 0..6 are matrices and the step works on matrices
+    only: it reads the popcount(t-1) live levels above 0 (and the loaded
+    level 0 on the first step) and writes the merged level.  Plus q, k, v
+    (bf16), a, lambda, the level scales (read and written), the level-0
+    vectors and out."""
     st = dk * dv * 4
+    row = (dk + dv) * 4 + 4
     small = (2 * dk + dv) * 2 + 4 + Lmax * 4 + 2 * Lmax * 4 + 2 * (dk + dv) * 4 + dv * 4
+    pc = lambda x: bin(x).count("1")  # noqa: E731
     tot = 0.0
-    for s in range(steps):
-        t = pos0 + s
-        live = np.array([bin(int(x) - 1).count("1") + (1 if s == 0 else 0) if x >= 1 else 0 for x in t])
-        merged = (t >= 1).astype(np.int64)
-        tot += float(np.sum(live + merged)) * st * H + len(t) * H * small
-    return tot / steps
+    for p0 in (int(x) for x in pos0):
+        for s in range(steps):
+            t = p0 + s
+            if t >= 1 and (t & ~63) >= p0:          # window levels
+                m = t & 63
+                if m > 0:
+                    b = m * row + row + pc(t >> 6) * st
+                else:
+                    j = (t & -t).bit_length() - 1
+                    b = row + st + pc(t >> (j + 1)) * st
+                    if t - 64 >= p0:
+                        b += 64 * row + (j - 6) * st
+                    else:
+                        b += pc((t - 1) & ((1 << j) - 1)) * st + (st if s == 0 else 0)
+            elif t >= 1:                             # matrix levels after a load
+                b = (pc(t - 1) + (1 if s == 0 else 0) + 1) * st
+            else:
+                b = row
+            tot += b
+    return (tot * H + len(pos0) * H * small * steps) / steps
 
 
 # --------------------------------------------------------------------- CPU baseline

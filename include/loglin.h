@@ -261,12 +261,17 @@ LOGLIN_API loglin_status loglin_bwd_chunked(const void* q, const void* k, const 
  * every Fenwick bucket of the prefix keeps its own recurrent state, and the
  * live set holds at most ceil(log2 t + 1) + 1 of them): for nseq sequences x
  * H heads, Lmax level states of dk x dv (S = sum k v^T orientation) plus the
- * next position of each sequence.  Each
- * level is held as an fp32 matrix and a scalar log-scale (the state is the
- * matrix times exp(scale)), and level 0, which only ever holds the newest
- * token's k v^T, as the vectors k and v once a step has run; a step then
- * rewrites only the level it merges into.  loglin_state_export returns the
- * states themselves (dk x dv matrices).
+ * next position of each sequence.  Levels 7 and up are held as fp32 matrices
+ * with a scalar log-scale (the state is the matrix times exp(scale)).  Levels
+ * 0..6 of position t hold exactly the tokens of t's 64-token window
+ * [t & ~63, t]; loglin_decode_step keeps them as those tokens' raw k, v rows
+ * (with the running sum of a) and folds the window into a matrix level at
+ * each multiple of 64, so a step inside a window writes one row and reads the
+ * window and the matrix levels.  Loaded levels 0..6 are matrices and are kept
+ * as such until the next multiple of 64.  loglin_gdn_decode_step keeps every
+ * level as a matrix.  loglin_state_export returns the states themselves
+ * (dk x dv matrices) either way.  Memory: nseq*H*(Lmax*dk*dv +
+ * 64*(dk+dv+1) + dk+dv+Lmax) floats.
  * Allocates device memory (hipMalloc) and zeroes it on `stream`; every
  * sequence starts at position 0.  dk, dv in {16, 32, 64, 128};
  * 1 <= Lmax <= 48.  *st is set only on success.

@@ -75,6 +75,9 @@ struct DecodeParams {
     float* sigma;             // [nseq][H][Lmax] per-level log-scales
     float* raw;               // [nseq][H][dk + dv]: k and v of the newest token (level 0)
     int raw0;                 // level 0 is raw's k v^T (else the matrix in states)
+    float* win;               // [nseq][H][64][dk + dv]: the 64-token window's k, v rows
+    float* wc;                // [nseq][H][64]: sum of a from the window start to each token
+    int window;               // levels 0..6 live in the window (scalar-gated steps)
     const int64_t* base_pos;  // [nseq]: position of the first step after the last load
     int64_t step;             // steps taken since that load
     const void* q;            // [nseq][H][dk]

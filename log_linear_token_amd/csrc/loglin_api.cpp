@@ -587,6 +587,10 @@ struct loglin_state {
     float* levels;               // device [nseq][H][Lmax][dk][dv] matrices X
     float* sigma;                // device [nseq][H][Lmax] log-scales (state = exp(sigma) X)
     float* raw;                  // device [nseq][H][dk + dv]: level 0 as k, v once a step ran
+    float* win;                  // device [nseq][H][64][dk + dv]: the 64-token window's rows
+    float* wc;                   // device [nseq][H][64]: running sums of a over the window
+    int kind;                    // mixer stepping the state since the last load: 0 none,
+                                 // 1 scalar-gated (levels 0..6 in the window), 2 Gated DeltaNet
     int64_t* base_pos;           // device [nseq]
     std::vector<int64_t> host_base;  // host mirror of base_pos
     int64_t step;                // steps since the last load
@@ -608,6 +612,9 @@ DecodeParams decode_params(const loglin_state* st) {
     p.sigma = st->sigma;
     p.raw = st->raw;
     p.raw0 = st->step > 0;  // every step rewrites level 0 of every (sequence, head)
+    p.win = st->win;
+    p.wc = st->wc;
+    p.window = st->kind == 1;
     p.base_pos = st->base_pos;
     p.step = st->step;
     p.nseq = st->nseq;
@@ -676,6 +683,20 @@ loglin_status loglin_state_init(loglin_state** out, int nseq, int H, int dk, int
         delete st;
         return fail(LOGLIN_ENOMEM, "hipMalloc level 0 vectors: %s", hipGetErrorString(e));
     }
+    e = hipMalloc(&st->win, (size_t)nseq * H * 64 * (dk + dv) * sizeof(float));
+    if (e == hipSuccess) {
+        e = hipMalloc(&st->wc, (size_t)nseq * H * 64 * sizeof(float));
+        if (e != hipSuccess) (void)hipFree(st->win);
+    }
+    if (e != hipSuccess) {
+        (void)hipFree(st->levels);
+        (void)hipFree(st->base_pos);
+        (void)hipFree(st->sigma);
+        (void)hipFree(st->raw);
+        delete st;
+        return fail(LOGLIN_ENOMEM, "hipMalloc window rows: %s", hipGetErrorString(e));
+    }
+    st->kind = 0;
     hipStream_t s = static_cast<hipStream_t>(stream);
     e = hipMemsetAsync(st->levels, 0, bytes, s);
     if (e == hipSuccess) e = hipMemsetAsync(st->base_pos, 0, (size_t)nseq * sizeof(int64_t), s);
@@ -685,6 +706,8 @@ loglin_status loglin_state_init(loglin_state** out, int nseq, int H, int dk, int
         (void)hipFree(st->base_pos);
         (void)hipFree(st->sigma);
         (void)hipFree(st->raw);
+        (void)hipFree(st->win);
+        (void)hipFree(st->wc);
         delete st;
         return hip_fail(e, "loglin_state_init");
     }
@@ -703,8 +726,12 @@ loglin_status loglin_state_free(loglin_state* st) {
     hipError_t e2 = hipFree(st->base_pos);
     hipError_t e3 = hipFree(st->sigma);
     hipError_t e4 = hipFree(st->raw);
+    hipError_t e5 = hipFree(st->win);
+    hipError_t e6 = hipFree(st->wc);
     if (e2 == hipSuccess) e2 = e3;
     if (e2 == hipSuccess) e2 = e4;
+    if (e2 == hipSuccess) e2 = e5;
+    if (e2 == hipSuccess) e2 = e6;
     delete st;
     if (e != hipSuccess) return hip_fail(e, "loglin_state_free (synchronize)");
     if (e1 != hipSuccess) return hip_fail(e1, "loglin_state_free");
@@ -744,6 +771,7 @@ loglin_status loglin_state_load(loglin_state* st, const int64_t* pos_host, const
     if (e != hipSuccess) return hip_fail(e, "loglin_state_load (positions)");
     st->step = 0;
     st->max_base = mx;
+    st->kind = 0;
     return ok();
 }
 
@@ -775,6 +803,10 @@ loglin_status loglin_decode_step(loglin_state* st, const void* q, const void* k,
     if (t >= ((int64_t)1 << (st->Lmax - 1)))
         return fail(LOGLIN_ECAPACITY, "position %lld needs more than %d levels", (long long)t,
                     st->Lmax);
+    if (st->kind == 2)
+        return fail(LOGLIN_EINVAL, "the state was stepped by loglin_gdn_decode_step since its "
+                    "last load; one state serves one mixer");
+    st->kind = 1;
     DecodeParams p = decode_params(st);
     p.q = q;
     p.k = k;
@@ -803,6 +835,10 @@ loglin_status loglin_gdn_decode_step(loglin_state* st, const void* q, const void
     if (t >= ((int64_t)1 << (st->Lmax - 1)))
         return fail(LOGLIN_ECAPACITY, "position %lld needs more than %d levels", (long long)t,
                     st->Lmax);
+    if (st->kind == 1)
+        return fail(LOGLIN_EINVAL, "the state was stepped by loglin_decode_step since its last "
+                    "load; one state serves one mixer");
+    st->kind = 2;
     DecodeParams p = decode_params(st);
     p.q = q;
     p.k = k;

@@ -195,3 +195,93 @@ def test_decode_agrees_with_chunked_forward():
     want = ref.form_b(d["q"], d["k"], d["v"], d["a"], d["lam"])
     assert slice_rel_err(dec, want, 2) <= TOL_BF16
     assert slice_rel_err(fwd, want, 2) <= TOL_BF16
+
+
+def _tok(x, t):
+    return to_dev(np.ascontiguousarray(x[:, :, t]))
+
+
+@pytest.mark.parametrize("dk,dv", [(32, 16), (128, 128)])
+def test_window_export_matches_recurrence_states(dk, dv):
+    """Decode from empty with fp32 inputs; export the states inside a window,
+    at its last token and right after a boundary, and compare every level with
+    the oracle recurrence's states after the same tokens (levels 0..6 of the
+    window are summed from raw rows on export)."""
+    banner(f"decode window export dk={dk} dv={dv}")
+    rng = np.random.default_rng(dk + dv)
+    B, H, T = 1, 2, 200
+    L = (T - 1).bit_length() + 1
+    q = (rng.standard_normal((B, H, T, dk)) / np.sqrt(dk)).astype(np.float32)
+    k = (rng.standard_normal((B, H, T, dk)) / np.sqrt(dk)).astype(np.float32)
+    v = rng.standard_normal((B, H, T, dv)).astype(np.float32)
+    a = (-np.logaddexp(0, rng.standard_normal((B, H, T)) - 5)).astype(np.float32)
+    lam = rng.random((B, H, T, L)).astype(np.float32)
+    st = LL.loglin_state_init(B, H, dk, dv, L)
+    checks = {37, 63, 64, 65, 128, 129, 200}
+    for t in range(T):
+        LL.loglin_decode_step(st, _tok(q, t), _tok(k, t), _tok(v, t), _tok(a, t), _tok(lam, t))
+        n = t + 1
+        if n in checks:
+            pos, lv = LL.loglin_state_export(st)
+            assert int(pos[0]) == n
+            _, want = ref.form_b(q[:, :, :n], k[:, :, :n], v[:, :, :n], a[:, :, :n],
+                                 lam[:, :, :n], return_states=True)
+            err = state_rel_err(lv.cpu().numpy().reshape(B * H, L, dk, dv),
+                                want.reshape(B * H, L, dk, dv))
+            assert err <= TOL_F32, (n, err)
+            live = set(ref.live_slots(n))
+            got = lv.cpu().numpy()
+            for lev in range(L):
+                if lev not in live:
+                    assert not np.any(got[:, :, lev]), (n, lev)
+    LL.loglin_state_free(st)
+
+
+@pytest.mark.parametrize("stop", [40, 64, 100, 127])
+def test_export_load_resume_matches_uninterrupted(stop):
+    """Export mid-way (window rows become matrices), load into a new state,
+    continue: outputs match the uninterrupted decode and the oracle."""
+    banner(f"decode export/load/resume at {stop}")
+    rng = np.random.default_rng(stop)
+    B, H, T, dk, dv = 2, 2, 180, 64, 32
+    L = (T - 1).bit_length() + 1
+    q = (rng.standard_normal((B, H, T, dk)) / np.sqrt(dk)).astype(np.float32)
+    k = (rng.standard_normal((B, H, T, dk)) / np.sqrt(dk)).astype(np.float32)
+    v = rng.standard_normal((B, H, T, dv)).astype(np.float32)
+    a = (-np.logaddexp(0, rng.standard_normal((B, H, T)) - 5)).astype(np.float32)
+    lam = rng.random((B, H, T, L)).astype(np.float32)
+    st = LL.loglin_state_init(B, H, dk, dv, L)
+    outs = []
+    for t in range(stop):
+        outs.append(LL.loglin_decode_step(st, _tok(q, t), _tok(k, t), _tok(v, t), _tok(a, t),
+                                          _tok(lam, t)).cpu().numpy())
+    pos, lv = LL.loglin_state_export(st)
+    st2 = LL.loglin_state_init(B, H, dk, dv, L)
+    LL.loglin_state_load(st2, pos.numpy(), lv)
+    for t in range(stop, T):
+        o1 = LL.loglin_decode_step(st, _tok(q, t), _tok(k, t), _tok(v, t), _tok(a, t), _tok(lam, t))
+        o2 = LL.loglin_decode_step(st2, _tok(q, t), _tok(k, t), _tok(v, t), _tok(a, t), _tok(lam, t))
+        outs.append(o2.cpu().numpy())
+        assert np.allclose(o1.cpu().numpy(), o2.cpu().numpy(), rtol=1e-5, atol=1e-5), t
+    LL.loglin_state_free(st)
+    LL.loglin_state_free(st2)
+    got = np.stack(outs, axis=2)  # [B, H, T, dv]
+    want = ref.form_a(q, k, v, a, lam)
+    assert slice_rel_err(got, want, 2) <= TOL_F32
+
+
+def test_one_state_serves_one_mixer():
+    banner("decode state kind")
+    st = LL.loglin_state_init(1, 1, 16, 16, 6)
+    z = torch.zeros((1, 1, 16), device="cuda")
+    s1 = torch.zeros((1, 1), device="cuda")
+    lam = torch.zeros((1, 1, 6), device="cuda")
+    LL.loglin_decode_step(st, z, z, z, s1, lam)
+    with pytest.raises(LL.LoglinError) as ei:
+        LL.loglin_gdn_decode_step(st, z, z, z, s1, s1, lam)
+    assert ei.value.status == LL.LOGLIN_EINVAL
+    LL.loglin_state_load(st, [1])  # a load starts over
+    LL.loglin_gdn_decode_step(st, z, z, z, s1, s1, lam)
+    with pytest.raises(LL.LoglinError):
+        LL.loglin_decode_step(st, z, z, z, s1, lam)
+    LL.loglin_state_free(st)
