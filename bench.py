@@ -208,6 +208,107 @@ def decode_bytes(pos0: np.ndarray, H: int, dk: int, dv: int, Lmax: int, steps: i
     return (tot * H + len(pos0) * H * small * steps) / steps
 
 
+# --------------------------------------------------------------------- ceilings and sweeps
+
+def measure_ceilings() -> dict:
+    """The HBM rates a plain stream reaches on this GPU, measured in this run:
+    a 2 GiB device-to-device copy (read + write bytes) and a row-wise
+    reduction over 2 GiB (bytes read, 0.1 % written).  Kernels are reported against the
+    8 TB/s spec and against these."""
+    n = (2 << 30) // 4
+    src = torch.ones(n, device="cuda")
+    dst = torch.empty_like(src)
+    stream = torch.cuda.current_stream()
+    for _ in range(3):
+        dst.copy_(src)
+    ms_copy = timed(lambda: dst.copy_(src), 10, stream)
+    rows = torch.empty(n // 1024, device="cuda")
+    rsum = lambda: torch.sum(src.view(-1, 1024), dim=1, out=rows)  # noqa: E731
+    for _ in range(3):
+        rsum()
+    ms_read = timed(rsum, 10, stream)
+    copy = 2 * n * 4 / (ms_copy / 1e3) / 1e9
+    read = (n + n // 1024) * 4 / (ms_read / 1e3) / 1e9
+    log(f"ceilings: copy {copy:.0f} GB/s (read + write), read-only {read:.0f} GB/s")
+    del src, dst
+    torch.cuda.empty_cache()
+    return {"copy_GB/s": round(copy, 1), "read_GB/s": round(read, 1),
+            "spec_GB/s": HBM_PEAK_GBS,
+            "method": "torch copy_ of 2 GiB fp32 (bytes read + written) and torch.sum of "
+                      "2 GiB fp32 over rows of 1024 (bytes read + the row sums written), 10 "
+                      "timed launches each after 3 warm-ups"}
+
+
+def bench_sweep() -> dict:
+    """Scaling checks against the page's complexity claims (its opening:
+    O(T log T) training compute; section 3: the inter-chunk stage is
+    O(T log(T/C))).  Forward over T = 2K..64K at a fixed 2^18 tokens per
+    step (B = 2^18 / T, H = 16, dk = 128, dv = 64, C = 64, the 8K workload's
+    distributions); reports ms per step, ns per token-head and that time over
+    log2(T/C).  Decode: every sequence of the decode workload at the same
+    position t = 2^k - 1 + 64 u (u a few whole windows in), so the number of
+    live matrix levels is popcount(t >> 6); ms per step against the modelled
+    bytes."""
+    out = {"forward": [], "decode": []}
+    base = I.CONFIGS["fwd8k"]
+    stream = torch.cuda.current_stream()
+    for T in (2048, 4096, 8192, 16384, 32768, 65536):
+        cfg = base.scaled(B=(1 << 18) // T, T=T, L=(T - 1).bit_length() + 1)
+        g = torch.Generator(device="cuda")
+        g.manual_seed(cfg.seed + T)
+        shp = (cfg.B, cfg.H, T)
+        q = (torch.randn(shp + (cfg.dk,), device="cuda", generator=g) / cfg.dk ** 0.5).to(torch.bfloat16)
+        k = (torch.randn(shp + (cfg.dk,), device="cuda", generator=g) / cfg.dk ** 0.5).to(torch.bfloat16)
+        v = torch.randn(shp + (cfg.dv,), device="cuda", generator=g).to(torch.bfloat16)
+        a = -torch.nn.functional.softplus(-2.0 + 0.5 * torch.randn(shp, device="cuda", generator=g))
+        lam = torch.nn.functional.softplus(torch.randn(shp + (cfg.L,), device="cuda", generator=g))
+        ws = torch.empty(max(1, LL.loglin_fwd_workspace_bytes(cfg.B, cfg.H, T, cfg.dk, cfg.dv, cfg.C,
+                                                              torch.bfloat16)),
+                         dtype=torch.uint8, device="cuda")
+        o = torch.empty(shp + (cfg.dv,), device="cuda")
+        run = lambda: LL.loglin_fwd_chunked(q, k, v, a, lam, cfg.C, out=o, workspace=ws)  # noqa
+        for _ in range(20):
+            run()
+        ms = timed(run, 30, stream)
+        ns_th = ms * 1e6 / (cfg.B * cfg.H * T)
+        out["forward"].append({"T": T, "B": cfg.B, "ms": round(ms, 4),
+                               "ns_per_token_head": round(ns_th, 4),
+                               "ns_per_token_head_per_log2_T_over_C": round(ns_th / np.log2(T / cfg.C), 4)})
+        log(f"sweep T={T}: {ms:.3f} ms, {ns_th:.3f} ns per token-head")
+        del q, k, v, a, lam, ws, o
+    torch.cuda.empty_cache()
+    dc = I.CONFIGS["decode"]
+    nseq, H, dk, dv, Lmax = dc.nseq, dc.H, dc.dk, dc.dv, dc.Lmax
+    st = LL.loglin_state_init(nseq, H, dk, dv, Lmax)
+    g = torch.Generator(device="cuda")
+    g.manual_seed(dc.seed)
+    levels = torch.randn((nseq, H, Lmax, dk, dv), device="cuda", generator=g) / dk ** 0.5
+    qd = torch.randn((nseq, H, dk), device="cuda", generator=g).to(torch.bfloat16)
+    ad = -torch.nn.functional.softplus(torch.randn((nseq, H), device="cuda", generator=g))
+    ld = torch.rand((nseq, H, Lmax), device="cuda", generator=g)
+    od = torch.empty((nseq, H, dv), device="cuda")
+    for kbits in (7, 9, 11, 13, 15):
+        # position (2^kbits - 1) rounded down to a window start, then 2 windows
+        # of steps: the timed steps run inside windows, with popcount(t >> 6)
+        # matrix levels live
+        p0 = ((1 << kbits) - 1) & ~63
+        LL.loglin_state_load(st, np.full(nseq, p0, np.int64), levels)
+        steps = 128
+        it = iter(range(steps))
+        stp = lambda: (next(it), LL.loglin_decode_step(st, qd, qd, qd, ad, ld, out=od))  # noqa
+        ms = timed(stp, steps, stream)
+        pcs = [bin((p0 + s) >> 6).count("1") for s in range(steps)]
+        byts = decode_bytes(np.full(nseq, p0, np.int64), H, dk, dv, Lmax, steps)
+        out["decode"].append({"start_position": p0, "mean_live_matrix_levels": round(float(np.mean(pcs)), 3),
+                              "ms_per_step": round(ms, 4), "model_GB_per_step": round(byts / 1e9, 4),
+                              "GB/s": round(byts / (ms / 1e3) / 1e9, 1)})
+        log(f"sweep decode from {p0}: {ms:.3f} ms/step, {np.mean(pcs):.2f} matrix levels")
+    LL.loglin_state_free(st)
+    del levels
+    torch.cuda.empty_cache()
+    return out
+
+
 # --------------------------------------------------------------------- CPU baseline
 
 def cpu_baseline(cfg, d) -> dict:
@@ -240,6 +341,55 @@ def cpu_baseline(cfg, d) -> dict:
             "cpu_model": _cpu_model()}
 
 
+def cpu_baseline_other() -> dict:
+    """The oracle on bounded samples of the other workloads, scaled to each
+    workload's own unit: the 2K forward (all 16 slices, ten times), the 64K
+    forward (the first 8192 positions of eight slices: the recurrence's cost
+    per token grows only with the live levels, so this overstates its 64K
+    rate slightly), and decode (512 of the 4096 (sequence, head) pairs for
+    64 steps, scaled to steps of the whole batch)."""
+    from oracle import reference as ref
+    threads = ref.default_threads()
+    res = {}
+    c2 = I.CONFIGS["fwd2k"]
+    d2 = I.make_fwd(c2, "base")
+    reps = 10
+    t0 = time.perf_counter()
+    for _ in range(reps):
+        ref.form_b(d2["q"], d2["k"], d2["v"], d2["a"], d2["lam"], nthreads=threads)
+    dt = time.perf_counter() - t0
+    res["fwd2k"] = {"value": reps * c2.B * c2.T / dt, "unit": "tokens/s",
+                    "cores": min(threads, c2.B * c2.H), "kind": "oracle",
+                    "sample": f"fp64 recurrence over all {c2.B * c2.H} slices, {reps} times "
+                    f"({dt:.1f} s wall)"}
+    ns5, T5 = 8, 8192
+    c5 = I.CONFIGS["long64k"].scaled(B=1, H=ns5, T=T5, L=(T5 - 1).bit_length() + 1)
+    d5 = I.make_fwd(c5, "base")
+    t0 = time.perf_counter()
+    ref.form_b(d5["q"], d5["k"], d5["v"], d5["a"], d5["lam"], nthreads=threads)
+    dt = time.perf_counter() - t0
+    H5 = I.CONFIGS["long64k"].H
+    res["long64k"] = {"value": ns5 * T5 / H5 / dt, "unit": "tokens/s", "cores": min(threads, ns5),
+                      "kind": "oracle", "sample": f"fp64 recurrence over the first {T5} positions "
+                      f"of {ns5} of the 16 slices ({dt:.1f} s wall); tokens counted as slices*T/H"}
+    dc = I.CONFIGS["decode"].scaled(nseq=128, H=4, steps=64)
+    dd = I.make_decode(dc, "base", live_slots=ref.live_slots)
+    P = dc.nseq * dc.H
+    sel = lambda x: x.reshape((dc.steps, P) + x.shape[3:])  # noqa: E731
+    t0 = time.perf_counter()
+    ref.decode(dd["states"].reshape(P, dc.Lmax, dc.dk, dc.dv), np.repeat(dd["pos"], dc.H),
+               sel(dd["q"]), sel(dd["k"]), sel(dd["v"]), sel(dd["a"]), sel(dd["lam"]),
+               nthreads=threads)
+    dt = time.perf_counter() - t0
+    full = I.CONFIGS["decode"]
+    res["decode"] = {"value": dc.steps * P / (full.nseq * full.H) / dt, "unit": "steps/s",
+                     "cores": min(threads, P), "kind": "oracle",
+                     "sample": f"fp64 recurrence, {P} of the {full.nseq * full.H} (sequence, head) "
+                     f"pairs for {dc.steps} steps ({dt:.1f} s wall), scaled to steps of all pairs"}
+    log(f"cpu baseline other: {res}")
+    return res
+
+
 def _cpu_model() -> str:
     try:
         with open("/proc/cpuinfo") as f:
@@ -265,6 +415,8 @@ def main() -> int:
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-backward", action="store_true")
+    ap.add_argument("--no-sweep", action="store_true",
+                    help="skip the sequence-length and decode-popcount sweeps")
     ap.add_argument("--no-gdn", action="store_true",
                     help="skip the log-linear Gated DeltaNet forward and decode")
     ap.add_argument("--no-other", action="store_true",
@@ -300,6 +452,12 @@ def main() -> int:
                      dtype=torch.uint8, device="cuda")
     stream = torch.cuda.current_stream()
     fwd, sets = rotating_forward(cfg, q, k, v, a, lam, ws)
+
+    # Measured ceilings of this GPU (copy and read-only streams) and the
+    # sequence-length sweep run right before the headline timing, with the
+    # headline's inputs already resident (no host work in between).
+    ceilings = measure_ceilings()
+    sweep = None if args.no_sweep else bench_sweep()
 
     for _ in range(args.warmup):
         fwd()
@@ -343,6 +501,8 @@ def main() -> int:
     roof = {"kernel": dom, "bound": "hbm", "achieved": round(km["GB/s"], 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(km["GB/s"] / HBM_PEAK_GBS, 4),
             "traffic": measured_traffic(dom),
+            "frac_of_measured_copy": round(km["GB/s"] / ceilings["copy_GB/s"], 4),
+            "frac_of_measured_read": round(km["GB/s"] / ceilings["read_GB/s"], 4),
             "mfma": mfma_entry(km)}
 
     result = {
@@ -356,7 +516,10 @@ def main() -> int:
         "kernels": {n: {kk: (round(vv, 4) if isinstance(vv, float) else vv)
                         for kk, vv in m.items()} for n, m in kernels.items()},
         "plan": plan,
+        "ceilings": ceilings,
     }
+    if sweep is not None:
+        result["sweep"] = sweep
     result["prefill_states"] = bench_prefill(cfg, sets, stream, args.steps)
     if not args.no_backward:
         result["backward"] = bench_backward(cfg, sets, stream, max(5, args.steps // 4))
@@ -373,6 +536,7 @@ def main() -> int:
                                     "decode": bench_gdn_decode(args.decode_steps)}
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(cfg, d)
+        result["cpu_baseline_other"] = cpu_baseline_other()
     print(json.dumps(result), flush=True)
     return 0
 
