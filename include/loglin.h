@@ -188,10 +188,15 @@ LOGLIN_API loglin_status loglin_fwd_chunked_noalloc(const void* q, const void* k
  *   workspace  at least loglin_gdn_fwd_workspace_bytes(...) bytes, 256-byte
  *              aligned (NULL allowed when that is 0); contents on entry
  *              ignored, on return unspecified
- * Numerics: fp32 matrix cores throughout (bf16 inputs are widened exactly);
- * the delta rule's triangular system is inverted per chunk in fp32.  Keys of
- * unit norm keep the transition contractive; other keys are computed as
- * written.  B, H or T equal to 0 is a no-op.
+ * T may be at most 2^20 (14 levels of 64-token chunks).
+ * Numerics: fp32 inputs run on fp32 matrix cores throughout.  bf16 inputs
+ * run on bf16 matrix cores with fp32 accumulation; the products whose
+ * results carry from chunk to chunk (the chunk transitions and the level
+ * states) take each fp32 operand as two bf16 pieces (about 16 significant
+ * bits), the rest one piece.  The delta rule's triangular system is
+ * inverted per chunk in fp32.  Keys of unit norm keep the transition
+ * contractive; other keys are computed as written.  B, H or T equal to 0 is
+ * a no-op.
  */
 LOGLIN_API size_t loglin_gdn_fwd_workspace_bytes(int B, int H, int T, int dk, int dv, int C,
                                                  loglin_dtype in_dtype);

@@ -78,6 +78,54 @@ __device__ __forceinline__ float ld(const E* p) {
     return to_f32(*p);
 }
 
+// N = (I + A)^-1 in place for the strictly lower 64 x 64 matrix A held in T
+// (fp32, row pitch pc; the tiles above the diagonal are zero), by 16 x 16
+// blocks: the diagonal blocks by forward substitution (lane c of waves 0..3
+// holds column c of block w), then the blocks below them row by row,
+// N_ij = -N_ii sum_{k=j..i-1} A_ik N_kj on the fp32 matrix cores (temporaries
+// in G, [3][16][20]).  Called by all threads of a block of >= 4 waves.
+__device__ __forceinline__ void invert_unit_lower(float* T, int pc, float* G) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (wave < 4 && lane < 16) {
+        const int o = 16 * wave, c = lane;
+        float x[16];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            float s = r == c ? 1.f : 0.f;
+#pragma unroll
+            for (int u = 0; u < r; ++u) s -= T[(o + r) * pc + o + u] * x[u];
+            x[r] = s;
+        }
+#pragma unroll
+        for (int r = 0; r < 16; ++r) T[(o + r) * pc + o + c] = x[r];
+    }
+    __syncthreads();
+    for (int bi = 1; bi < 4; ++bi) {
+        // G_ij = sum_{k=j..i-1} A_ik N_kj into temp j (waves 0..i-1)
+        if (wave < bi) {
+            const int bj = wave;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int bk = bj; bk < bi; ++bk)
+                acc = mm_f32([&](int m, int k) { return T[(16 * bi + m) * pc + 16 * bk + k]; },
+                             [&](int k, int n) { return T[(16 * bk + k) * pc + 16 * bj + n]; }, 0,
+                             16, acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) G[(bj * 16 + (lane >> 4) * 4 + i) * 20 + (lane & 15)] = acc[i];
+        }
+        __syncthreads();
+        if (wave < bi) {
+            const int bj = wave;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = mm_f32([&](int m, int k) { return T[(16 * bi + m) * pc + 16 * bi + k]; },
+                         [&](int k, int n) { return G[(bj * 16 + k) * 20 + n]; }, 0, 16, acc);
+#pragma unroll
+            for (int i = 0; i < 4; ++i)
+                T[(16 * bi + (lane >> 4) * 4 + i) * pc + 16 * bj + (lane & 15)] = -acc[i];
+        }
+        __syncthreads();
+    }
+}
+
 template <typename E, int DK, int DV>
 struct ChunkSmem {
     static constexpr int PK = DK + 4, PV = DV + 4, PC = GC + 4;
@@ -181,47 +229,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_gdn_chunk(GdnParams p) {
     }
     __syncthreads();
 
-    // ---- N = (I + A)^-1 by 16 x 16 blocks: the diagonal blocks by forward
-    // substitution (lane c holds column c), then the blocks below them row by
-    // row: N_ij = -N_ii sum_{k=j..i-1} A_ik N_kj.
-    if (wave < 4 && lane < 16) {
-        const int o = 16 * wave, c = lane;
-        float x[16];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            float s = r == c ? 1.f : 0.f;
-#pragma unroll
-            for (int u = 0; u < r; ++u) s -= sT[(o + r) * PC + o + u] * x[u];
-            x[r] = s;
-        }
-#pragma unroll
-        for (int r = 0; r < 16; ++r) sT[(o + r) * PC + o + c] = x[r];
-    }
-    __syncthreads();
-    for (int bi = 1; bi < 4; ++bi) {
-        // G_ij = sum_{k=j..i-1} A_ik N_kj into temp j (waves 0..i-1)
-        if (wave < bi) {
-            const int bj = wave;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            for (int bk = bj; bk < bi; ++bk)
-                acc = mm_f32([&](int m, int k) { return sT[(16 * bi + m) * PC + 16 * bk + k]; },
-                             [&](int k, int n) { return sT[(16 * bk + k) * PC + 16 * bj + n]; }, 0,
-                             16, acc);
-#pragma unroll
-            for (int i = 0; i < 4; ++i) sG[(bj * 16 + (lane >> 4) * 4 + i) * 20 + (lane & 15)] = acc[i];
-        }
-        __syncthreads();
-        if (wave < bi) {
-            const int bj = wave;
-            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-            acc = mm_f32([&](int m, int k) { return sT[(16 * bi + m) * PC + 16 * bi + k]; },
-                         [&](int k, int n) { return sG[(bj * 16 + k) * 20 + n]; }, 0, 16, acc);
-#pragma unroll
-            for (int i = 0; i < 4; ++i)
-                sT[(16 * bi + (lane >> 4) * 4 + i) * PC + 16 * bj + (lane & 15)] = -acc[i];
-        }
-        __syncthreads();
-    }
+    invert_unit_lower(sT, PC, sG);
     // Tb = N diag(beta)
     for (int e = tid; e < GC * GC; e += kChunkThreads) {
         const int r = e / GC, c = e - r * GC;
@@ -478,6 +486,534 @@ __global__ __launch_bounds__(kLevelThreads) void k_gdn_levels(GdnParams p) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 inputs: the same two stages on the 16 x 16 x 32 bf16 matrix cores.
+//
+// Products whose results carry from chunk to chunk (W, F and the level states
+// of the walk) take each fp32 operand in two bf16 pieces, x = hi + lo with
+// hi = bf16(x) and lo = bf16(x - hi), and form A B as Ah Bh + Ah Bl + Al Bh
+// (about 16 significant bits; bf16 inputs are exact and need no lo piece).
+// The chunk's own block, its state U and the read-out queries take one bf16
+// piece (their rounding does not compound); the inverse stays in fp32.
+// Operands of the 16x16x32 MFMA are read 16 bytes per lane: A as rows m with
+// k contiguous, B as rows n with k contiguous (B transposed); every array has
+// a row pitch of its length plus 8 elements.
+//
+// Workspace (per bh, chunk), in the byte sizes of the fp32 stages:
+//   F   hi then lo, [DK*DK] bf16 each, in the A-operand order of the walk
+//   Qp  [64*DK] bf16, q' in the same order
+//   U   fp32 in the walk's accumulator order: [DV/16][DK/16][64 lanes][4]
+
+constexpr int P64 = GC + 8;         // pitch of rows of 64 elements
+constexpr int kMaxWalkLevels = kGdnMaxWalkLevelsBf;  // chunk levels the bf16 walk holds
+
+__device__ __forceinline__ f32x4 mm_bf(const bf16_t* A, int lda, const bf16_t* Bt, int ldb, int kb,
+                                       int ke, f32x4 acc) {
+    const int lane = threadIdx.x & 63, r = lane & 15, q = lane >> 4;
+    for (int k = kb; k < ke; k += 32) {
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(A + r * lda + k + 8 * q);
+        const bf16x8 b = *reinterpret_cast<const bf16x8*>(Bt + r * ldb + k + 8 * q);
+        acc = mma(a, b, acc);
+    }
+    return acc;
+}
+
+__device__ __forceinline__ bf16_t bf_of(float x) { return __builtin_bit_cast(bf16_t, (__bf16)x); }
+__device__ __forceinline__ void split_bf(float x, bf16_t& hi, bf16_t& lo) {
+    const __bf16 h = (__bf16)x;
+    hi = __builtin_bit_cast(bf16_t, h);
+    lo = bf_of(x - (float)h);
+}
+// four bf16 in one 8-byte store
+__device__ __forceinline__ void st4(bf16_t* dst, bf16_t a, bf16_t b, bf16_t c, bf16_t d) {
+    const uint2 v = make_uint2((uint32_t)a | ((uint32_t)b << 16), (uint32_t)c | ((uint32_t)d << 16));
+    *reinterpret_cast<uint2*>(dst) = v;
+}
+// index of (row m, col k) of a [rows][D] matrix in the A-operand order of the
+// 16x16x32 MFMA: tile of 16 rows, 32-wide k-step, lane, element
+__device__ __forceinline__ size_t frag16(int m, int k, int D) {
+    const int lane = (m & 15) + 16 * ((k & 31) >> 3);
+    return ((((size_t)(m >> 4) * (D / 32) + (k >> 5)) * 64 + lane) << 3) + (k & 7);
+}
+// contraction end of a lower-triangular row tile ti, rounded up to the k-step
+__device__ __forceinline__ int tri_end(int ti) { return min(GC, (16 * (ti + 1) + 31) & ~31); }
+
+template <int DK, int DV>
+struct ChunkBfSmem {
+    static constexpr int PK = DK + 8, PC = GC + 4;
+    static constexpr size_t q_off = 0;                                  // Q  [64][PK]
+    static constexpr size_t k_off = q_off + 2 * GC * PK;                 // K  [64][PK]
+    static constexpr size_t kt_off = k_off + 2 * GC * PK;                // K^T [DK][P64]
+    static constexpr size_t vt_off = kt_off + 2 * DK * P64;              // V^T [DV][P64]
+    static constexpr size_t yh_off = vt_off + 2 * DV * P64;              // Y (then P) [64][P64]
+    static constexpr size_t b_off = yh_off + 2 * GC * P64;               // b, beta, a [64] each
+    static constexpr size_t lam_off = b_off + 4 * 3 * GC;                // [64][8]
+    static constexpr size_t g_off = lam_off + 4 * GC * 8;                // inverse temps [3][16][20]
+    static constexpr size_t u_off = g_off + 4 * 3 * 16 * 20;             // union region
+    // phase 1: the system (fp32) and Tb, Tb diag(e^b) in two pieces, Tb^T
+    static constexpr size_t t_size = 4 * GC * PC;
+    static constexpr size_t tb_size = 2 * GC * P64;
+    static constexpr size_t phase1 = t_size + 5 * tb_size;
+    // phase 2: W^T, (diag(e^(g-b)) W)^T in two pieces, (diag(e^(g-b)) U0)^T in two
+    static constexpr size_t wt_size = 2 * DK * P64;
+    static constexpr size_t ut_size = 2 * DV * P64;
+    static constexpr size_t phase2 = 3 * wt_size + 2 * ut_size;
+    static constexpr size_t total = u_off + (phase1 > phase2 ? phase1 : phase2);
+};
+
+template <int DK, int DV>
+__global__ __launch_bounds__(kChunkThreads) void k_gdn_chunk_bf(GdnParams p) {
+    using S = ChunkBfSmem<DK, DV>;
+    constexpr int PK = S::PK, PC = S::PC;
+    constexpr int NWV = kChunkThreads / 64;
+    extern __shared__ __align__(16) char smem[];
+    bf16_t* sQ = reinterpret_cast<bf16_t*>(smem + S::q_off);
+    bf16_t* sK = reinterpret_cast<bf16_t*>(smem + S::k_off);
+    bf16_t* sKt = reinterpret_cast<bf16_t*>(smem + S::kt_off);
+    bf16_t* sVt = reinterpret_cast<bf16_t*>(smem + S::vt_off);
+    bf16_t* sYh = reinterpret_cast<bf16_t*>(smem + S::yh_off);
+    float* sb = reinterpret_cast<float*>(smem + S::b_off);
+    float* sbeta = sb + GC;
+    float* sa = sbeta + GC;
+    float* slam = reinterpret_cast<float*>(smem + S::lam_off);
+    float* sG = reinterpret_cast<float*>(smem + S::g_off);
+    char* un = smem + S::u_off;
+    float* sT = reinterpret_cast<float*>(un);
+    bf16_t* Tbh = reinterpret_cast<bf16_t*>(un + S::t_size);
+    bf16_t* Tbl = Tbh + GC * P64;
+    bf16_t* Tph = Tbl + GC * P64;
+    bf16_t* Tpl = Tph + GC * P64;
+    bf16_t* TbT = Tpl + GC * P64;
+    bf16_t* WTh = reinterpret_cast<bf16_t*>(un);
+    bf16_t* WpTh = WTh + DK * P64;
+    bf16_t* WpTl = WpTh + DK * P64;
+    bf16_t* U0h = WpTl + DK * P64;
+    bf16_t* U0l = U0h + DV * P64;
+
+    const int blk = xcd_local_block(blockIdx.x, gridDim.x);
+    const int bh = blk / p.N;
+    const int ci = blk - bh * p.N;
+    const int t0 = ci * GC;
+    const int nvalid = min(GC, p.T - t0);
+    const int tid = threadIdx.x;
+    const int wave = tid >> 6, lane = tid & 63, r16 = lane & 15, q4 = lane >> 4;
+    const size_t row0 = (size_t)bh * p.T + t0;
+
+    // ---- stage: q, k rows and k^T; v^T; a, beta, lambda 0..6
+    {
+        const bf16_t* q = static_cast<const bf16_t*>(p.q) + row0 * DK;
+        const bf16_t* k = static_cast<const bf16_t*>(p.k) + row0 * DK;
+        const bf16_t* v = static_cast<const bf16_t*>(p.v) + row0 * DV;
+        for (int e = tid; e < GC * DK / 8; e += kChunkThreads) {
+            const int r = e / (DK / 8), c8 = (e - r * (DK / 8)) * 8;
+            uint4 xq = make_uint4(0, 0, 0, 0), xk = xq;
+            if (r < nvalid) {
+                xq = *reinterpret_cast<const uint4*>(q + (size_t)r * DK + c8);
+                xk = *reinterpret_cast<const uint4*>(k + (size_t)r * DK + c8);
+            }
+            *reinterpret_cast<uint4*>(sQ + r * PK + c8) = xq;
+            *reinterpret_cast<uint4*>(sK + r * PK + c8) = xk;
+            const bf16_t* kk = reinterpret_cast<const bf16_t*>(&xk);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sKt[(c8 + i) * P64 + r] = kk[i];
+        }
+        for (int e = tid; e < GC * DV / 8; e += kChunkThreads) {
+            const int r = e / (DV / 8), c8 = (e - r * (DV / 8)) * 8;
+            uint4 xv = make_uint4(0, 0, 0, 0);
+            if (r < nvalid) xv = *reinterpret_cast<const uint4*>(v + (size_t)r * DV + c8);
+            const bf16_t* vv = reinterpret_cast<const bf16_t*>(&xv);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) sVt[(c8 + i) * P64 + r] = vv[i];
+        }
+        if (tid < GC) {
+            const bool ok = tid < nvalid;
+            sa[tid] = ok ? p.a[row0 + tid] : 0.f;
+            sbeta[tid] = ok ? p.beta[row0 + tid] : 0.f;
+        }
+        const int nl = min(p.L, 7);
+        for (int e = tid; e < GC * 8; e += kChunkThreads) {
+            const int r = e >> 3, l = e & 7;
+            slam[e] = (r < nvalid && l < nl) ? p.lam[(row0 + r) * p.L + l] : 0.f;
+        }
+        // tiles above the diagonal of Y and of the system stay zero
+        for (int e = tid; e < GC * GC; e += kChunkThreads) {
+            const int r = e / GC, c = e - r * GC;
+            if ((c >> 4) > (r >> 4)) {
+                sYh[r * P64 + c] = 0;
+                sT[r * PC + c] = 0.f;
+            }
+        }
+    }
+    __syncthreads();
+    if (wave == 0) wave_cumsum(sa, sb, GC);
+    __syncthreads();
+
+    // ---- Q K^T -> Y (one bf16 piece); K K^T -> the system (fp32)
+    for (int j = wave; j < 20; j += NWV) {
+        const bool isq = j < 10;
+        int ti, tj;
+        tri_tile(isq ? j : j - 10, ti, tj);
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mm_bf((isq ? sQ : sK) + 16 * ti * PK, PK, sK + 16 * tj * PK, PK, 0, DK, acc);
+        const int n = 16 * tj + r16;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int m = 16 * ti + q4 * 4 + i;
+            const float dec = m >= n ? __expf(sb[m] - sb[n]) : 0.f;
+            if (isq)
+                sYh[m * P64 + n] = bf_of(m >= n ? acc[i] * dec : 0.f);
+            else
+                sT[m * PC + n] = m > n ? sbeta[m] * acc[i] * dec : 0.f;
+        }
+    }
+    __syncthreads();
+    invert_unit_lower(sT, PC, sG);
+    // Tb = N diag(beta) and Tb diag(e^b), each in two pieces; Tb^T (one piece)
+    for (int e = tid; e < GC * GC; e += kChunkThreads) {
+        const int r = e / GC, c = e - r * GC;
+        const float tb = sT[r * PC + c] * sbeta[c];
+        bf16_t h, l;
+        split_bf(tb, h, l);
+        Tbh[r * P64 + c] = h;
+        Tbl[r * P64 + c] = l;
+        TbT[c * P64 + r] = h;
+        split_bf(tb * __expf(sb[c]), h, l);
+        Tph[r * P64 + c] = h;
+        Tpl[r * P64 + c] = l;
+    }
+    __syncthreads();
+
+    // ---- W = Tb diag(e^b) K, U0 = Tb V, P = (Y Tb) (.) Lambda -> registers
+    constexpr int NW = 4 * (DK / 16);
+    constexpr int NWW = NW / NWV;  // W tiles per wave
+    f32x4 w[NWW];
+#pragma unroll
+    for (int x = 0; x < NWW; ++x) {
+        const int j = wave + NWV * x;
+        const int ti = j / (DK / 16), tn = j % (DK / 16);
+        const int ke = tri_end(ti);
+        w[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+        w[x] = mm_bf(Tph + 16 * ti * P64, P64, sKt + 16 * tn * P64, P64, 0, ke, w[x]);
+        w[x] = mm_bf(Tpl + 16 * ti * P64, P64, sKt + 16 * tn * P64, P64, 0, ke, w[x]);
+    }
+    constexpr int NU = 4 * (DV / 16);
+    constexpr int NUW = (NU + NWV - 1) / NWV;
+    f32x4 u0[NUW];
+#pragma unroll
+    for (int x = 0; x < NUW; ++x) {
+        u0[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int j = wave + NWV * x;
+        if (j < NU) {
+            const int ti = j / (DV / 16), tn = j % (DV / 16);
+            const int ke = tri_end(ti);
+            u0[x] = mm_bf(Tbh + 16 * ti * P64, P64, sVt + 16 * tn * P64, P64, 0, ke, u0[x]);
+            u0[x] = mm_bf(Tbl + 16 * ti * P64, P64, sVt + 16 * tn * P64, P64, 0, ke, u0[x]);
+        }
+    }
+    f32x4 pt[2];
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+        pt[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+        const int j = wave + NWV * x;
+        if (j < 10) {
+            int ti, tj;
+            tri_tile(j, ti, tj);
+            pt[x] = mm_bf(sYh + 16 * ti * P64, P64, TbT + 16 * tj * P64, P64, (16 * tj) & ~31,
+                          tri_end(ti), pt[x]);
+            const int n = 16 * tj + r16;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = 16 * ti + q4 * 4 + i;
+                pt[x][i] = m >= n ? pt[x][i] * slam[m * 8 + fenwick_level((uint32_t)m, (uint32_t)n)] : 0.f;
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- W^T, (e^(g-b) W)^T in two pieces, (e^(g-b) U0)^T in two pieces
+    const float g = sb[GC - 1];
+#pragma unroll
+    for (int x = 0; x < NWW; ++x) {
+        const int j = wave + NWV * x;
+        const int ti = j / (DK / 16), tn = j % (DK / 16);
+        const int s0 = 16 * ti + q4 * 4, d = 16 * tn + r16;
+        bf16_t hh[4], ph[4], pl[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            hh[i] = bf_of(w[x][i]);
+            split_bf(w[x][i] * __expf(g - sb[s0 + i]), ph[i], pl[i]);
+        }
+        st4(WTh + d * P64 + s0, hh[0], hh[1], hh[2], hh[3]);
+        st4(WpTh + d * P64 + s0, ph[0], ph[1], ph[2], ph[3]);
+        st4(WpTl + d * P64 + s0, pl[0], pl[1], pl[2], pl[3]);
+    }
+#pragma unroll
+    for (int x = 0; x < NUW; ++x) {
+        const int j = wave + NWV * x;
+        if (j < NU) {
+            const int ti = j / (DV / 16), tn = j % (DV / 16);
+            const int s0 = 16 * ti + q4 * 4, c = 16 * tn + r16;
+            bf16_t ph[4], pl[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) split_bf(u0[x][i] * __expf(g - sb[s0 + i]), ph[i], pl[i]);
+            st4(U0h + c * P64 + s0, ph[0], ph[1], ph[2], ph[3]);
+            st4(U0l + c * P64 + s0, pl[0], pl[1], pl[2], pl[3]);
+        }
+    }
+    __syncthreads();
+
+    // ---- q' = e^b Q - Y W (read by the walk from chunk 1 on), F and U (for
+    // every chunk but the last)
+    // Each of q', F and the chunk output is formed transposed (operands
+    // swapped), so that a lane's four results are consecutive in the layout
+    // the walk reads and go out as one store.
+    if (ci > 0) {
+        bf16_t* Qp = reinterpret_cast<bf16_t*>(p.qp) + ((size_t)bh * p.N + ci) * GC * DK;
+#pragma unroll
+        for (int x = 0; x < NWW; ++x) {
+            const int j = wave + NWV * x;
+            const int td = j / 4, tt = j % 4;  // q'^T tile: rows d (16 td..), columns t (16 tt..)
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            // Y is lower triangular: token tile tt contracts over s < 16 (tt + 1)
+            acc = mm_bf(WTh + 16 * td * P64, P64, sYh + 16 * tt * P64, P64, 0, tri_end(tt), acc);
+            const int t = 16 * tt + r16, d0 = 16 * td + q4 * 4;
+            const float eb = __expf(sb[t]);
+            bf16_t h[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) h[i] = bf_of(eb * bf16_to_f32(sQ[t * PK + d0 + i]) - acc[i]);
+            st4(Qp + frag16(t, d0, DK), h[0], h[1], h[2], h[3]);
+        }
+    }
+    if (ci + 1 < p.N) {
+        bf16_t* Fh = reinterpret_cast<bf16_t*>(p.fmat) + ((size_t)bh * p.N + ci) * 2 * DK * DK;
+        bf16_t* Fl = Fh + DK * DK;
+        const float eg = __expf(g);
+        constexpr int NF = (DK / 16) * (DK / 16);
+        for (int j = wave; j < NF; j += NWV) {
+            const int tc = j / (DK / 16), tr = j % (DK / 16);  // F^T tile: rows d' (16 tc..), cols d
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = mm_bf(WpTh + 16 * tc * P64, P64, sKt + 16 * tr * P64, P64, 0, GC, acc);
+            acc = mm_bf(WpTl + 16 * tc * P64, P64, sKt + 16 * tr * P64, P64, 0, GC, acc);
+            const int d = 16 * tr + r16, e0 = 16 * tc + q4 * 4;  // F row d, columns e0..e0+3
+            bf16_t h[4], l[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) split_bf((d == e0 + i ? eg : 0.f) - acc[i], h[i], l[i]);
+            const size_t fi = frag16(d, e0, DK);
+            st4(Fh + fi, h[0], h[1], h[2], h[3]);
+            st4(Fl + fi, l[0], l[1], l[2], l[3]);
+        }
+        f32x4* U = reinterpret_cast<f32x4*>(p.ust + ((size_t)bh * p.N + ci) * DK * DV);
+        constexpr int NS = (DK / 16) * (DV / 16);
+        for (int j = wave; j < NS; j += NWV) {
+            const int ti = j % (DK / 16), tn = j / (DK / 16);
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+            acc = mm_bf(sKt + 16 * ti * P64, P64, U0h + 16 * tn * P64, P64, 0, GC, acc);
+            acc = mm_bf(sKt + 16 * ti * P64, P64, U0l + 16 * tn * P64, P64, 0, GC, acc);
+            U[((size_t)tn * (DK / 16) + ti) * 64 + lane] = acc;
+        }
+    }
+    __syncthreads();
+    // ---- P over Y, then the chunk's own output P V
+#pragma unroll
+    for (int x = 0; x < 2; ++x) {
+        const int j = wave + NWV * x;
+        if (j < 10) {
+            int ti, tj;
+            tri_tile(j, ti, tj);
+#pragma unroll
+            for (int i = 0; i < 4; ++i) sYh[(16 * ti + q4 * 4 + i) * P64 + 16 * tj + r16] = bf_of(pt[x][i]);
+        }
+    }
+    __syncthreads();
+    for (int j = wave; j < NU; j += NWV) {
+        const int tt = j / (DV / 16), tc = j % (DV / 16);  // O^T tile: rows c, columns t
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+        acc = mm_bf(sVt + 16 * tc * P64, P64, sYh + 16 * tt * P64, P64, 0, tri_end(tt), acc);
+        const int t = 16 * tt + r16;
+        if (t < nvalid)
+            *reinterpret_cast<f32x4*>(p.out + (row0 + t) * DV + 16 * tc + q4 * 4) = acc;
+    }
+}
+
+// Level walk for bf16 inputs: one block of 8 waves per (bh, 16 output
+// columns).  Each level state is kept transposed (16 columns x DK) in two
+// bf16 pieces; wave w < DK/16 carries rows 16w..16w+15 of every state through
+// F (three products per step), waves 0..3 read tokens 16w..16w+15 out.  The
+// next chunk's F, q', U and chunk output are loaded while this one is worked.
+template <int DK>
+__global__ __launch_bounds__(kChunkThreads) void k_gdn_levels_bf(GdnParams p) {
+    constexpr int XP = DK + 8;
+    constexpr int NKS = DK / 32;
+    constexpr int SLOT = 2 * kLevelCols * XP;  // bf16 elements of one level (hi, lo)
+    extern __shared__ __align__(16) char smem[];
+    bf16_t* sx = reinterpret_cast<bf16_t*>(smem);
+    float* slam0 = reinterpret_cast<float*>(smem + sizeof(bf16_t) * (size_t)p.nlev * SLOT);
+    const int nlev = p.nlev;
+    const int ncb = p.dv / kLevelCols;
+    const int blk = xcd_local_block(blockIdx.x, gridDim.x);
+    const int bh = blk / ncb, cb = blk - bh * ncb;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int r16 = lane & 15, q4 = lane >> 4;
+    const int col0 = cb * kLevelCols;
+    const int N = p.N;
+    constexpr int c6 = 6;  // chunk level p+1 is mask level 6+p+1
+    const bool trans = wave < DK / 16, reads = wave < 4;
+
+    // lambda of the coarse levels of a chunk: at most 64 * 14 values, two per
+    // thread, loaded with the chunk's other registers and stored to LDS later
+    constexpr int NLR = (GC * kMaxWalkLevels + kChunkThreads - 1) / kChunkThreads;
+    auto load_lam = [&](int ci, float (&lr)[NLR]) __attribute__((always_inline)) {
+        const size_t r0 = (size_t)bh * p.T + (size_t)ci * GC;
+        const int nv = min(GC, p.T - ci * GC);
+#pragma unroll
+        for (int u = 0; u < NLR; ++u) {
+            const int e = tid + u * kChunkThreads;
+            const int r = e / nlev, l = e - r * nlev;
+            const int lev = c6 + 1 + l;
+            lr[u] = (e < GC * nlev && r < nv && lev < p.L) ? p.lam[(r0 + r) * p.L + lev] : 0.f;
+        }
+    };
+    auto store_lam = [&](const float (&lr)[NLR], float* dst) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < NLR; ++u) {
+            const int e = tid + u * kChunkThreads;
+            if (e < GC * nlev) dst[e] = lr[u];
+        }
+    };
+    // registers of one chunk: F rows of this wave (two pieces), q' rows, U,
+    // chunk output, coarse lambda
+    struct Regs {
+        bf16x8 fh[NKS], fl[NKS], qf[NKS];
+        f32x4 u, o;
+        float lam[NLR];
+    };
+    auto load = [&](int ci, Regs& R) __attribute__((always_inline)) {
+        const size_t slot = (size_t)bh * N + ci;
+        if (trans && ci + 1 < N) {
+            const bf16x8* fh = reinterpret_cast<const bf16x8*>(p.fmat) + slot * 2 * DK * DK / 8;
+            const bf16x8* fl = fh + DK * DK / 8;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) {
+                R.fh[ks] = fh[((size_t)wave * NKS + ks) * 64 + lane];
+                R.fl[ks] = fl[((size_t)wave * NKS + ks) * 64 + lane];
+            }
+            R.u = reinterpret_cast<const f32x4*>(p.ust + slot * DK * p.dv)[((size_t)cb * (DK / 16) + wave) * 64 + lane];
+        }
+        load_lam(ci, R.lam);
+        if (reads && ci > 0) {
+            const bf16x8* qp = reinterpret_cast<const bf16x8*>(p.qp) + slot * GC * DK / 8;
+#pragma unroll
+            for (int ks = 0; ks < NKS; ++ks) R.qf[ks] = qp[((size_t)wave * NKS + ks) * 64 + lane];
+            const int nv = min(GC, p.T - ci * GC);
+            const size_t r0 = (size_t)bh * p.T + (size_t)ci * GC;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = 16 * wave + q4 * 4 + i;
+                R.o[i] = m < nv ? p.out[(r0 + m) * p.dv + col0 + r16] : 0.f;
+            }
+        }
+    };
+
+    for (int e = tid; e < nlev * SLOT; e += kChunkThreads) sx[e] = 0;
+    Regs cur, nxt;
+    load(0, nxt);
+    store_lam(nxt.lam, slam0);
+    __syncthreads();
+
+    for (int ci = 0; ci < N; ++ci) {
+        cur = nxt;
+        if (ci + 1 < N) load(ci + 1, nxt);
+        float* slam = slam0 + (ci & 1) * GC * nlev;
+        const int nvalid = min(GC, p.T - ci * GC);
+        const size_t row0 = (size_t)bh * p.T + (size_t)ci * GC;
+
+        // read-out of the live levels (bits of ci)
+        if (reads && ci > 0) {
+            f32x4 o = cur.o;
+            for (unsigned bits = (unsigned)ci; bits; bits &= bits - 1) {
+                const int l = __builtin_ctz(bits);
+                const bf16_t* Xh = sx + (size_t)l * SLOT + r16 * XP + 8 * q4;
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int ks = 0; ks < NKS; ++ks)
+                    acc = mma(cur.qf[ks], *reinterpret_cast<const bf16x8*>(Xh + 32 * ks), acc);
+#pragma unroll
+                for (int i = 0; i < 4; ++i) o[i] += slam[(16 * wave + q4 * 4 + i) * nlev + l] * acc[i];
+            }
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int m = 16 * wave + q4 * 4 + i;
+                if (m < nvalid) p.out[(row0 + m) * p.dv + col0 + r16] = o[i];
+            }
+        }
+        if (ci + 1 >= N) break;
+
+        // merge levels 1..j (slots 0..j-1) into slot j, in fp32 from the pieces
+        const int jm = __builtin_ctz((unsigned)(ci + 1));
+        for (int e = tid; e < kLevelCols * DK / 4; e += kChunkThreads) {
+            const int c = e / (DK / 4), d4 = (e - c * (DK / 4)) * 4;
+            float s4[4] = {0.f, 0.f, 0.f, 0.f};
+            for (int l = 0; l < jm; ++l) {
+                const bf16_t* h = sx + (size_t)l * SLOT + c * XP + d4;
+                const bf16_t* lo = h + kLevelCols * XP;
+#pragma unroll
+                for (int i = 0; i < 4; ++i) s4[i] += bf16_to_f32(h[i]) + bf16_to_f32(lo[i]);
+            }
+            bf16_t hh[4], ll[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) split_bf(s4[i], hh[i], ll[i]);
+            bf16_t* dh = sx + (size_t)jm * SLOT + c * XP + d4;
+            st4(dh, hh[0], hh[1], hh[2], hh[3]);
+            st4(dh + kLevelCols * XP, ll[0], ll[1], ll[2], ll[3]);
+        }
+        __syncthreads();
+
+        // carry: slot jm (the merged level, plus U) and the live slots above
+        const unsigned tbits = ((unsigned)ci >> jm) | 1u;
+        f32x4 nx[kMaxWalkLevels];
+        if (trans) {
+#pragma unroll
+            for (int x = 0; x < kMaxWalkLevels; ++x) {
+                nx[x] = f32x4{0.f, 0.f, 0.f, 0.f};
+                if ((tbits >> x) & 1u) {
+                    const bf16_t* Xh = sx + (size_t)(jm + x) * SLOT + r16 * XP + 8 * q4;
+                    const bf16_t* Xl = Xh + kLevelCols * XP;
+#pragma unroll
+                    for (int ks = 0; ks < NKS; ++ks) {
+                        const bf16x8 bh8 = *reinterpret_cast<const bf16x8*>(Xh + 32 * ks);
+                        const bf16x8 bl8 = *reinterpret_cast<const bf16x8*>(Xl + 32 * ks);
+                        nx[x] = mma(cur.fh[ks], bh8, nx[x]);
+                        nx[x] = mma(cur.fh[ks], bl8, nx[x]);
+                        nx[x] = mma(cur.fl[ks], bh8, nx[x]);
+                    }
+                    if (x == 0) {
+                        nx[x][0] += cur.u[0];
+                        nx[x][1] += cur.u[1];
+                        nx[x][2] += cur.u[2];
+                        nx[x][3] += cur.u[3];
+                    }
+                }
+            }
+        }
+        __syncthreads();
+        if (trans) {
+#pragma unroll
+            for (int x = 0; x < kMaxWalkLevels; ++x) {
+                if ((tbits >> x) & 1u) {
+                    bf16_t hh[4], ll[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) split_bf(nx[x][i], hh[i], ll[i]);
+                    bf16_t* dh = sx + (size_t)(jm + x) * SLOT + r16 * XP + 16 * wave + 4 * q4;
+                    st4(dh, hh[0], hh[1], hh[2], hh[3]);
+                    st4(dh + kLevelCols * XP, ll[0], ll[1], ll[2], ll[3]);
+                }
+            }
+        }
+        store_lam(nxt.lam, slam0 + ((ci + 1) & 1) * GC * nlev);
+        __syncthreads();
+    }
+}
+
 template <typename K>
 hipError_t set_smem(K kernel, size_t bytes) {
     return hipFuncSetAttribute(reinterpret_cast<const void*>(kernel),
@@ -505,6 +1041,37 @@ hipError_t launch_levels(const GdnParams& p, hipStream_t stream) {
     return hipGetLastError();
 }
 
+template <int DK, int DV>
+hipError_t launch_chunk_bf(const GdnParams& p, hipStream_t stream) {
+    constexpr size_t sm = ChunkBfSmem<DK, DV>::total;
+    static_assert(sm <= kGdnLdsMax, "chunk kernel LDS");
+    hipError_t e = set_smem(&k_gdn_chunk_bf<DK, DV>, sm);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_gdn_chunk_bf<DK, DV>), dim3((unsigned)(p.BH * p.N)), dim3(kChunkThreads),
+                       sm, stream, p);
+    return hipGetLastError();
+}
+
+template <int DK>
+hipError_t launch_levels_bf(const GdnParams& p, hipStream_t stream) {
+    const size_t sm = gdn_levels_smem_bf(DK, p.nlev);
+    hipError_t e = set_smem(&k_gdn_levels_bf<DK>, sm);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL((k_gdn_levels_bf<DK>), dim3((unsigned)(p.BH * (p.dv / kLevelCols))),
+                       dim3(kChunkThreads), sm, stream, p);
+    return hipGetLastError();
+}
+
+template <int DK>
+hipError_t launch_chunk_bf_dv(const GdnParams& p, hipStream_t stream) {
+    switch (p.dv) {
+        case 16: return launch_chunk_bf<DK, 16>(p, stream);
+        case 32: return launch_chunk_bf<DK, 32>(p, stream);
+        case 64: return launch_chunk_bf<DK, 64>(p, stream);
+    }
+    return hipErrorInvalidValue;
+}
+
 template <typename E, int DK>
 hipError_t launch_chunk_dv(const GdnParams& p, hipStream_t stream) {
     switch (p.dv) {
@@ -521,19 +1088,26 @@ size_t gdn_levels_smem(int dk, int nlev) {
     return sizeof(float) * ((size_t)nlev * dk * kXPitch + (size_t)GC * nlev);
 }
 
+size_t gdn_levels_smem_bf(int dk, int nlev) {
+    return sizeof(bf16_t) * (size_t)nlev * 2 * kLevelCols * (dk + 8) + sizeof(float) * 2 * GC * nlev;
+}
+
 hipError_t launch_gdn_fwd(const GdnParams& p, bool bf16, unsigned stages, hipStream_t stream) {
     hipError_t e = hipSuccess;
     if (stages & 1u) {
         if (bf16)
-            e = p.dk == 128 ? launch_chunk_dv<bf16_t, 128>(p, stream)
-                            : launch_chunk_dv<bf16_t, 64>(p, stream);
+            e = p.dk == 128 ? launch_chunk_bf_dv<128>(p, stream) : launch_chunk_bf_dv<64>(p, stream);
         else
             e = p.dk == 128 ? launch_chunk_dv<float, 128>(p, stream)
                             : launch_chunk_dv<float, 64>(p, stream);
         if (e != hipSuccess) return e;
     }
-    if ((stages & 2u) && p.N > 1)
-        e = p.dk == 128 ? launch_levels<128>(p, stream) : launch_levels<64>(p, stream);
+    if ((stages & 2u) && p.N > 1) {
+        if (bf16)
+            e = p.dk == 128 ? launch_levels_bf<128>(p, stream) : launch_levels_bf<64>(p, stream);
+        else
+            e = p.dk == 128 ? launch_levels<128>(p, stream) : launch_levels<64>(p, stream);
+    }
     return e;
 }
 

@@ -112,8 +112,11 @@ struct GdnParams {
     float* qp;           // [BH][N][64*dk] read-out queries (MFMA operand order)
     float* ust;          // [BH][N][dk][dv] each chunk's own state at its end
 };
-// LDS bytes of the level walk for head dim dk holding nlev levels
+// LDS bytes of the level walk for head dim dk holding nlev levels (fp32 and
+// bf16 inputs); the bf16 walk holds at most 14 levels
 size_t gdn_levels_smem(int dk, int nlev);
+size_t gdn_levels_smem_bf(int dk, int nlev);
+constexpr int kGdnMaxWalkLevelsBf = 14;
 // stages: bit 0 the per-chunk kernel, bit 1 the level walk
 hipError_t launch_gdn_fwd(const GdnParams& p, bool bf16, unsigned stages, hipStream_t stream);
 

@@ -359,7 +359,8 @@ loglin_status check_gdn_sizes(int B, int H, int T, int dk, int dv, int C) {
         return fail(LOGLIN_EUNSUPPORTED, "Gated DeltaNet forward: dv=%d must be 16, 32 or 64", dv);
     const long N = ((long)T + kGdnChunk - 1) / kGdnChunk;
     const int nlev = bit_length(N - 1);
-    if (gdn_levels_smem(dk, nlev) > kGdnLdsMax)
+    if (nlev > kGdnMaxWalkLevelsBf || gdn_levels_smem(dk, nlev) > kGdnLdsMax ||
+        gdn_levels_smem_bf(dk, nlev) > kGdnLdsMax)
         return fail(LOGLIN_EUNSUPPORTED, "Gated DeltaNet forward: T=%d needs %d chunk levels, "
                     "more than one block holds", T, nlev);
     return LOGLIN_OK;
