@@ -590,52 +590,79 @@ __global__ __launch_bounds__(kChunkThreads) void k_gdn_chunk_bf(GdnParams p) {
     bf16_t* U0h = WpTl + DK * P64;
     bf16_t* U0l = U0h + DV * P64;
 
-    const int blk = xcd_local_block(blockIdx.x, gridDim.x);
-    const int bh = blk / p.N;
-    const int ci = blk - bh * p.N;
-    const int t0 = ci * GC;
-    const int nvalid = min(GC, p.T - t0);
     const int tid = threadIdx.x;
     const int wave = tid >> 6, lane = tid & 63, r16 = lane & 15, q4 = lane >> 4;
-    const size_t row0 = (size_t)bh * p.T + t0;
+    const int total = p.BH * p.N;
 
-    // ---- stage: q, k rows and k^T; v^T; a, beta, lambda 0..6
-    {
-        const bf16_t* q = static_cast<const bf16_t*>(p.q) + row0 * DK;
-        const bf16_t* k = static_cast<const bf16_t*>(p.k) + row0 * DK;
-        const bf16_t* v = static_cast<const bf16_t*>(p.v) + row0 * DV;
-        for (int e = tid; e < GC * DK / 8; e += kChunkThreads) {
+    // A block works through chunks blockIdx.x, + gridDim.x, ...; the next
+    // chunk's inputs are loaded into registers while the current one is worked.
+    constexpr int NQK = GC * DK / 8 / kChunkThreads;                      // 16-byte pieces of q (k)
+    constexpr int NVV = (GC * DV / 8 + kChunkThreads - 1) / kChunkThreads;  // of v
+    static_assert(GC * 8 == kChunkThreads, "one lambda entry per thread");
+    struct In {
+        uint4 q[NQK], k[NQK], v[NVV];
+        float a, beta, lam;
+    };
+    auto fetch = [&](int cb, In& R) __attribute__((always_inline)) {
+        const int fbh = cb / p.N, fci = cb - fbh * p.N;
+        const int nv = min(GC, p.T - fci * GC);
+        const size_t r0 = (size_t)fbh * p.T + (size_t)fci * GC;
+        const bf16_t* q = static_cast<const bf16_t*>(p.q) + r0 * DK;
+        const bf16_t* k = static_cast<const bf16_t*>(p.k) + r0 * DK;
+        const bf16_t* v = static_cast<const bf16_t*>(p.v) + r0 * DV;
+#pragma unroll
+        for (int u = 0; u < NQK; ++u) {
+            const int e = tid + u * kChunkThreads;
             const int r = e / (DK / 8), c8 = (e - r * (DK / 8)) * 8;
-            uint4 xq = make_uint4(0, 0, 0, 0), xk = xq;
-            if (r < nvalid) {
-                xq = *reinterpret_cast<const uint4*>(q + (size_t)r * DK + c8);
-                xk = *reinterpret_cast<const uint4*>(k + (size_t)r * DK + c8);
+            R.q[u] = R.k[u] = make_uint4(0, 0, 0, 0);
+            if (r < nv) {
+                R.q[u] = *reinterpret_cast<const uint4*>(q + (size_t)r * DK + c8);
+                R.k[u] = *reinterpret_cast<const uint4*>(k + (size_t)r * DK + c8);
             }
-            *reinterpret_cast<uint4*>(sQ + r * PK + c8) = xq;
-            *reinterpret_cast<uint4*>(sK + r * PK + c8) = xk;
-            const bf16_t* kk = reinterpret_cast<const bf16_t*>(&xk);
+        }
+#pragma unroll
+        for (int u = 0; u < NVV; ++u) {
+            const int e = tid + u * kChunkThreads;
+            const int r = e / (DV / 8), c8 = (e - r * (DV / 8)) * 8;
+            R.v[u] = make_uint4(0, 0, 0, 0);
+            if (e < GC * DV / 8 && r < nv) R.v[u] = *reinterpret_cast<const uint4*>(v + (size_t)r * DV + c8);
+        }
+        R.a = R.beta = 0.f;
+        if (tid < nv) {
+            R.a = p.a[r0 + tid];
+            R.beta = p.beta[r0 + tid];
+        }
+        const int r = tid >> 3, l = tid & 7;
+        R.lam = (r < nv && l < min(p.L, 7)) ? p.lam[(r0 + r) * p.L + l] : 0.f;
+    };
+    // q, k rows and k^T; v^T; a, beta, lambda 0..6 to LDS; the tiles above the
+    // diagonal of Y and of the system zeroed
+    auto stage = [&](const In& R) __attribute__((always_inline)) {
+#pragma unroll
+        for (int u = 0; u < NQK; ++u) {
+            const int e = tid + u * kChunkThreads;
+            const int r = e / (DK / 8), c8 = (e - r * (DK / 8)) * 8;
+            *reinterpret_cast<uint4*>(sQ + r * PK + c8) = R.q[u];
+            *reinterpret_cast<uint4*>(sK + r * PK + c8) = R.k[u];
+            const bf16_t* kk = reinterpret_cast<const bf16_t*>(&R.k[u]);
 #pragma unroll
             for (int i = 0; i < 8; ++i) sKt[(c8 + i) * P64 + r] = kk[i];
         }
-        for (int e = tid; e < GC * DV / 8; e += kChunkThreads) {
-            const int r = e / (DV / 8), c8 = (e - r * (DV / 8)) * 8;
-            uint4 xv = make_uint4(0, 0, 0, 0);
-            if (r < nvalid) xv = *reinterpret_cast<const uint4*>(v + (size_t)r * DV + c8);
-            const bf16_t* vv = reinterpret_cast<const bf16_t*>(&xv);
 #pragma unroll
-            for (int i = 0; i < 8; ++i) sVt[(c8 + i) * P64 + r] = vv[i];
+        for (int u = 0; u < NVV; ++u) {
+            const int e = tid + u * kChunkThreads;
+            if (e < GC * DV / 8) {
+                const int r = e / (DV / 8), c8 = (e - r * (DV / 8)) * 8;
+                const bf16_t* vv = reinterpret_cast<const bf16_t*>(&R.v[u]);
+#pragma unroll
+                for (int i = 0; i < 8; ++i) sVt[(c8 + i) * P64 + r] = vv[i];
+            }
         }
         if (tid < GC) {
-            const bool ok = tid < nvalid;
-            sa[tid] = ok ? p.a[row0 + tid] : 0.f;
-            sbeta[tid] = ok ? p.beta[row0 + tid] : 0.f;
+            sa[tid] = R.a;
+            sbeta[tid] = R.beta;
         }
-        const int nl = min(p.L, 7);
-        for (int e = tid; e < GC * 8; e += kChunkThreads) {
-            const int r = e >> 3, l = e & 7;
-            slam[e] = (r < nvalid && l < nl) ? p.lam[(row0 + r) * p.L + l] : 0.f;
-        }
-        // tiles above the diagonal of Y and of the system stay zero
+        slam[tid] = R.lam;
         for (int e = tid; e < GC * GC; e += kChunkThreads) {
             const int r = e / GC, c = e - r * GC;
             if ((c >> 4) > (r >> 4)) {
@@ -643,7 +670,19 @@ __global__ __launch_bounds__(kChunkThreads) void k_gdn_chunk_bf(GdnParams p) {
                 sT[r * PC + c] = 0.f;
             }
         }
-    }
+    };
+
+    In nxt;
+    if ((int)blockIdx.x < total) fetch(blockIdx.x, nxt);
+    for (int blk = blockIdx.x; blk < total; blk += gridDim.x) {
+    const int bh = blk / p.N;
+    const int ci = blk - bh * p.N;
+    const int t0 = ci * GC;
+    const int nvalid = min(GC, p.T - t0);
+    const size_t row0 = (size_t)bh * p.T + t0;
+    __syncthreads();  // every wave is done with the previous chunk's LDS
+    stage(nxt);
+    if (blk + (int)gridDim.x < total) fetch(blk + gridDim.x, nxt);
     __syncthreads();
     if (wave == 0) wave_cumsum(sa, sb, GC);
     __syncthreads();
@@ -833,6 +872,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_gdn_chunk_bf(GdnParams p) {
         if (t < nvalid)
             *reinterpret_cast<f32x4*>(p.out + (row0 + t) * DV + 16 * tc + q4 * 4) = acc;
     }
+    }  // chunks of this block
 }
 
 // Level walk for bf16 inputs: one block of 8 waves per (bh, 16 output
@@ -1047,8 +1087,15 @@ hipError_t launch_chunk_bf(const GdnParams& p, hipStream_t stream) {
     static_assert(sm <= kGdnLdsMax, "chunk kernel LDS");
     hipError_t e = set_smem(&k_gdn_chunk_bf<DK, DV>, sm);
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL((k_gdn_chunk_bf<DK, DV>), dim3((unsigned)(p.BH * p.N)), dim3(kChunkThreads),
-                       sm, stream, p);
+    // one resident block per compute unit (the LDS of one block), each working
+    // through its share of the chunks
+    int dev = 0, ncu = 0;
+    e = hipGetDevice(&dev);
+    if (e == hipSuccess) e = hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev);
+    if (e != hipSuccess) return e;
+    const long total = (long)p.BH * p.N;
+    const unsigned grid = (unsigned)(total < ncu ? total : ncu);
+    hipLaunchKernelGGL((k_gdn_chunk_bf<DK, DV>), dim3(grid), dim3(kChunkThreads), sm, stream, p);
     return hipGetLastError();
 }
 
