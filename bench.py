@@ -735,8 +735,8 @@ def gdn_models(cfg) -> dict:
 
     Chunk kernel: reads q, k, v, a, beta and the 7 intra-chunk levels of
     lambda once; writes the chunk's output and, for every chunk but the last
-    of a sequence, its read-out queries q' (64 x dk), transition F (dk x dk)
-    and state U (dk x dv) in fp32.  Flops: the products of full 16 x 16
+    of a sequence, its read-out queries q' (64 x dk, bf16), transition F
+    (dk x dk, two bf16 pieces) and state U (dk x dv, fp32).  Flops: the products of full 16 x 16
     tiles it computes -- Q K^T and K K^T on the 10 lower tiles, the block
     inverse, W, U0, the chunk block Y Tb, P V, q', F and U.
     Level walk: reads q', F, U and the coarse lambda of every chunk once and
@@ -757,13 +757,13 @@ def gdn_models(cfg) -> dict:
              + 10 * 16 * tile * dv // 16 * 2  # U0 = Tb V and P V
              + 20 * 16 * tile)           # Y Tb on the lower tiles
     states = 64 * 2 * dk * dk + 64 * 2 * dk * dv
-    chunk_bytes = BH * T * (2 * (2 * dk + dv) + 8 + 4 * min(L, 7) + 4 * dv) \
-        + BH * nst * 4 * (64 * dk + dk * dk + dk * dv)
+    per_chunk = 2 * 64 * dk + 4 * dk * dk + 4 * dk * dv   # q' bf16, F hi + lo, U fp32
+    chunk_bytes = BH * T * (2 * (2 * dk + dv) + 8 + 4 * min(L, 7) + 4 * dv) + BH * nst * per_chunk
     walk_reads = sum(bin(i).count("1") for i in range(N))
     walk_trans = sum(1 + bin(i >> ((i + 1) & -(i + 1)).bit_length()).count("1")
                      for i in range(N - 1))
     lu = (T - 1).bit_length() + 1
-    walk_bytes = BH * nst * 4 * (64 * dk + dk * dk + dk * dv) + BH * T * (4 * max(0, lu - 7) + 8 * dv)
+    walk_bytes = BH * nst * per_chunk + BH * T * (4 * max(0, lu - 7) + 8 * dv)
     return {
         "gdn_chunk": {"bytes": chunk_bytes, "flops": BH * (N * intra + nst * states)},
         "gdn_levels": {"bytes": walk_bytes,

@@ -610,10 +610,12 @@ __global__ __launch_bounds__(kChunkThreads) void k_gdn_chunk_bf(GdnParams p) {
         const bf16_t* q = static_cast<const bf16_t*>(p.q) + r0 * DK;
         const bf16_t* k = static_cast<const bf16_t*>(p.k) + r0 * DK;
         const bf16_t* v = static_cast<const bf16_t*>(p.v) + r0 * DV;
+        // lane l of a wave takes token row l: the transposed copies below then
+        // write 64 consecutive tokens per store
 #pragma unroll
         for (int u = 0; u < NQK; ++u) {
             const int e = tid + u * kChunkThreads;
-            const int r = e / (DK / 8), c8 = (e - r * (DK / 8)) * 8;
+            const int r = e % GC, c8 = (e / GC) * 8;
             R.q[u] = R.k[u] = make_uint4(0, 0, 0, 0);
             if (r < nv) {
                 R.q[u] = *reinterpret_cast<const uint4*>(q + (size_t)r * DK + c8);
@@ -623,7 +625,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_gdn_chunk_bf(GdnParams p) {
 #pragma unroll
         for (int u = 0; u < NVV; ++u) {
             const int e = tid + u * kChunkThreads;
-            const int r = e / (DV / 8), c8 = (e - r * (DV / 8)) * 8;
+            const int r = e % GC, c8 = (e / GC) * 8;
             R.v[u] = make_uint4(0, 0, 0, 0);
             if (e < GC * DV / 8 && r < nv) R.v[u] = *reinterpret_cast<const uint4*>(v + (size_t)r * DV + c8);
         }
@@ -641,7 +643,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_gdn_chunk_bf(GdnParams p) {
 #pragma unroll
         for (int u = 0; u < NQK; ++u) {
             const int e = tid + u * kChunkThreads;
-            const int r = e / (DK / 8), c8 = (e - r * (DK / 8)) * 8;
+            const int r = e % GC, c8 = (e / GC) * 8;
             *reinterpret_cast<uint4*>(sQ + r * PK + c8) = R.q[u];
             *reinterpret_cast<uint4*>(sK + r * PK + c8) = R.k[u];
             const bf16_t* kk = reinterpret_cast<const bf16_t*>(&R.k[u]);
@@ -652,7 +654,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_gdn_chunk_bf(GdnParams p) {
         for (int u = 0; u < NVV; ++u) {
             const int e = tid + u * kChunkThreads;
             if (e < GC * DV / 8) {
-                const int r = e / (DV / 8), c8 = (e - r * (DV / 8)) * 8;
+                const int r = e % GC, c8 = (e / GC) * 8;
                 const bf16_t* vv = reinterpret_cast<const bf16_t*>(&R.v[u]);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) sVt[(c8 + i) * P64 + r] = vv[i];
