@@ -49,7 +49,14 @@ typedef enum {
     LOGLIN_EHIP = 5          /* the HIP runtime reported an error (see loglin_last_error) */
 } loglin_status;
 
-typedef enum { LOGLIN_F32 = 0, LOGLIN_BF16 = 1 } loglin_dtype;
+/* Element type of q, k, v.  Any other value is answered with LOGLIN_EINVAL; the
+ * last enumerator widens the type's value range to every int32 so that such a
+ * value is well defined on the C++ side too. */
+typedef enum {
+    LOGLIN_F32 = 0,
+    LOGLIN_BF16 = 1,
+    LOGLIN_DTYPE_RANGE_ = 0x7fffffff /* not a dtype */
+} loglin_dtype;
 
 typedef struct loglin_state loglin_state; /* opaque, owned by the library */
 

@@ -41,7 +41,10 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "loglin_oracle.c")
-_LIB = os.path.join(_HERE, "liblloracle.so")
+# LLO_SANITIZE=1 selects a build with AddressSanitizer and UndefinedBehaviorSanitizer
+# (the process must preload gcc's libasan; see tests/test_host_sanitizers.py)
+_SANITIZE = os.environ.get("LLO_SANITIZE") == "1"
+_LIB = os.path.join(_HERE, "liblloracle_san.so" if _SANITIZE else "liblloracle.so")
 
 LLO_OK, LLO_EARG, LLO_ECAP, LLO_ELIVE, LLO_ENOMEM = 0, 1, 2, 3, 4
 
@@ -50,8 +53,10 @@ def build(force: bool = False) -> str:
     """Compile the C part of the oracle with gcc (plain -O2, no tuning)."""
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp"
+        san = ["-fsanitize=address,undefined", "-fno-sanitize-recover=all", "-fno-omit-frame-pointer",
+               "-g"] if _SANITIZE else []
         subprocess.check_call(
-            ["gcc", "-O2", "-std=c99", "-shared", "-fPIC", _SRC, "-o", tmp, "-lm", "-lpthread"]
+            ["gcc", "-O2", "-std=c99", *san, "-shared", "-fPIC", _SRC, "-o", tmp, "-lm", "-lpthread"]
         )
         os.replace(tmp, _LIB)
     return _LIB
