@@ -127,3 +127,17 @@ def test_bwd_full_8k_workload_weak_decay():
     print("  " + " ".join(f"{n} {e:.2e}" for n, e in errs.items()), flush=True)
     for n, e in errs.items():
         assert e <= TOL_BF16, (n, e)
+
+
+def test_bwd_deterministic():
+    """Two backward passes over the same inputs give bit-identical gradients."""
+    banner("determinism bwd T=2047")
+    B, H, T, dk, dv, C = 1, 2, 2047, 64, 64, 64
+    L = (T - 1).bit_length() + 1
+    q, k, v, a, lam, g = _inputs(B, H, T, dk, dv, L, seed=9)
+    dev = [to_dev(x, torch.bfloat16) for x in (q, k, v)]
+    args = (*dev, to_dev(a), to_dev(lam), to_dev(g, torch.bfloat16), C)
+    r1 = [x.cpu().numpy() for x in LL.loglin_bwd_chunked(*args)]
+    r2 = [x.cpu().numpy() for x in LL.loglin_bwd_chunked(*args)]
+    for n, x, y in zip(NAMES, r1, r2):
+        assert np.array_equal(x, y), n

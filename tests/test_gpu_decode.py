@@ -285,3 +285,14 @@ def test_one_state_serves_one_mixer():
     with pytest.raises(LL.LoglinError):
         LL.loglin_decode_step(st, z, z, z, s1, lam)
     LL.loglin_state_free(st)
+
+
+def test_decode_deterministic():
+    """Two runs from the same state give bit-identical outputs and states."""
+    banner("determinism decode")
+    cfg = I.CONFIGS["decode"].scaled(nseq=2, H=2, steps=70)
+    d = I.make_decode(cfg, "base", seed=11, live_slots=ref.live_slots)
+    st = d["states"]
+    o1, p1, s1 = _decode_gpu(d, st)
+    o2, p2, s2 = _decode_gpu(d, st)
+    assert np.array_equal(o1, o2) and np.array_equal(p1, p2) and np.array_equal(s1, s2)

@@ -127,3 +127,15 @@ def test_prefill_with_many_slots_zeroes_dead_ones(T, dtype):
     err = state_rel_err(got.reshape(B * H, Lmax, dk, dv), want.reshape(B * H, Lmax, dk, dv))
     tol = TOL_F32 if dtype == torch.float32 else TOL_BF16
     assert err <= tol, err
+
+
+def test_prefill_deterministic():
+    """Two prefills of the same tokens give bit-identical states."""
+    banner("determinism prefill T=3000")
+    B, H, T, dk, dv = 1, 2, 3000, 128, 64
+    L = (T - 1).bit_length() + 1
+    _, k, v, a, _ = _inputs(B, H, T, dk, dv, L, seed=5)
+    kd, vd, ad = to_dev(k, torch.bfloat16), to_dev(v, torch.bfloat16), to_dev(a)
+    s1 = LL.loglin_prefill_states(kd, vd, ad, L).cpu().numpy()
+    s2 = LL.loglin_prefill_states(kd, vd, ad, L).cpu().numpy()
+    assert np.array_equal(s1, s2)
