@@ -38,6 +38,8 @@
 // region) and R in bf16 only: the operand form the dq and dk/dv kernels stage
 // (R^T is then read from R through LDS transpose reads).
 #include <algorithm>
+#include <cstdlib>
+#include <cstring>
 #include <type_traits>
 
 #include "chunk_stage.hpp"
@@ -1042,7 +1044,18 @@ hipError_t launch_bwd_typed(const BwdParams& p, hipStream_t stream) {
         if (err != hipSuccess) return err;
         hipLaunchKernelGGL((k_bwd_dq<E, C, DM, 0, 0>), dim3(nblk), dim3(C / 16 * 64), s1, stream, p1);
     }
-    if (p.N > 1) {
+    // R(j): one walk over the query chunks where it applies (LOGLIN_BWD_RSTATE=blocks
+    // keeps the block-per-R(j) kernel below), else one block per R(j)
+    bool walked = false;
+    if constexpr (sizeof(E) == 2 && C == 64) {
+        const char* mode = getenv("LOGLIN_BWD_RSTATE");
+        if (p.N > 1 && !(mode && strcmp(mode, "blocks") == 0) && bwd_rwalk_applies(p)) {
+            err = launch_bwd_rwalk(p, stream);
+            if (err != hipSuccess) return err;
+            walked = true;
+        }
+    }
+    if (p.N > 1 && !walked) {
         BwdParams p2 = p;
         p2.rs_nbuf = rstate_smem<E, C>(p.dk, p.dv, 2) <= kLdsMax ? 2 : 1;
         const size_t s2 = rstate_smem<E, C>(p.dk, p.dv, p2.rs_nbuf);

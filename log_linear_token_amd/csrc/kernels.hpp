@@ -146,6 +146,10 @@ struct BwdParams {
     int rs_nbuf;              // copies of the staged chunk the R(j) kernel keeps (1 or 2)
 };
 hipError_t launch_bwd_chunked(const BwdParams& p, bool bf16, hipStream_t stream);
+// R(j) of every block in one pass over the query chunks (bf16, C = 64,
+// d_v = 64, d_k in {64, 128}, N <= 256): whether it applies, and the launch
+bool bwd_rwalk_applies(const BwdParams& p);
+hipError_t launch_bwd_rwalk(const BwdParams& p, hipStream_t stream);
 
 // Fenwick level states after the T tokens of a prefill (the state a decode
 // step at position T reads)

@@ -141,3 +141,19 @@ def test_bwd_deterministic():
     r2 = [x.cpu().numpy() for x in LL.loglin_bwd_chunked(*args)]
     for n, x, y in zip(NAMES, r1, r2):
         assert np.array_equal(x, y), n
+
+
+@pytest.mark.parametrize("mode", ["walk", "blocks"])
+@pytest.mark.parametrize("B,H,T,dk,dv", [(1, 2, 2047, 64, 64), (1, 1, 3072, 128, 64),
+                                         (2, 2, 1000, 64, 64), (1, 1, 4100, 128, 64),
+                                         (1, 1, 10000, 64, 64)])
+def test_bwd_rstate_paths(monkeypatch, mode, B, H, T, dk, dv):
+    """The block states R(j) of the dk / dv stage built by one walk over the
+    query chunks (segments, parts of the blocks that span segments, a ragged
+    last chunk) and by one block per R(j): both give the oracle's gradients."""
+    if mode == "blocks":
+        monkeypatch.setenv("LOGLIN_BWD_RSTATE", "blocks")
+    else:
+        monkeypatch.delenv("LOGLIN_BWD_RSTATE", raising=False)
+    banner(f"bwd R(j) {mode} B={B} H={H} T={T} dk={dk} dv={dv}")
+    _check(B, H, T, dk, dv, 64, torch.bfloat16, seed=T, mu=-3.0)
