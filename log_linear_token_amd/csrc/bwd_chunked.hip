@@ -974,6 +974,73 @@ __global__ __launch_bounds__(256) void k_bwd_da(BwdParams p) {
     }
 }
 
+// A at the end of every chunk for the R(j) and dk / dv stages: one block per
+// (batch, head); each thread sums its chunk's a in fp32 (in token order), and
+// the chunk totals are summed in fp64, tile by tile, the earlier tiles' sum
+// carried.
+__global__ __launch_bounds__(256) void k_bwd_chunk_cum(BwdParams p) {
+    constexpr int NT = 256;
+    __shared__ double part[NT];
+    const int tid = threadIdx.x;
+    const size_t base = (size_t)blockIdx.x * p.T;
+    double carry = 0.0;
+    for (int c0 = 0; c0 < p.N; c0 += NT) {
+        const int c = c0 + tid;
+        float tot = 0.f;
+        if (c < p.N) {
+            const int t1 = min((c + 1) * p.C, p.T);
+            for (int t = c * p.C; t < t1; ++t) tot += p.a[base + t];
+        }
+        part[tid] = tot;
+        __syncthreads();
+        for (int off = 1; off < NT; off <<= 1) {  // inclusive prefix (Hillis-Steele)
+            const double y = tid >= off ? part[tid - off] : 0.0;
+            __syncthreads();
+            part[tid] += y;
+            __syncthreads();
+        }
+        // p.cum is read-only for the other stages; this kernel fills it
+        if (c < p.N) const_cast<double*>(p.cum)[(size_t)blockIdx.x * p.N + c] = carry + part[tid];
+        carry += part[NT - 1];
+        __syncthreads();  // part[] is rewritten by the next tile
+    }
+}
+
+// dlambda and q . dq summed over the column blocks of the fused dq pass.
+// One block per 64 tokens of one (batch, head): the level-major parts are
+// read a level at a time (64 consecutive tokens), transposed through LDS and
+// written as whole [token][L] rows.
+__global__ __launch_bounds__(256) void k_bwd_dlam_sum(BwdParams p, const float* __restrict__ dlp,
+                                                       const float* __restrict__ dqd, int ndvb,
+                                                       int lu) {
+    __shared__ float tile[64][65];
+    const int ntb = (p.T + 63) / 64;
+    const int bh = blockIdx.x / ntb;
+    const int t0 = (blockIdx.x % ntb) * 64;
+    const int nt = min(64, p.T - t0);
+    const size_t rows = (size_t)p.BH * p.T;
+    for (int e = threadIdx.x; e < 64 * lu; e += 256) {
+        const int l = e >> 6, t = e & 63;
+        float s = 0.f;
+        if (t < nt)
+            for (int b = 0; b < ndvb; ++b)
+                s += dlp[(((size_t)b * p.BH + bh) * lu + l) * p.T + t0 + t];
+        tile[t][l] = s;
+    }
+    __syncthreads();
+    float* g = p.glam + ((size_t)bh * p.T + t0) * p.L;
+    for (int e = threadIdx.x; e < nt * p.L; e += 256) {
+        const int t = e / p.L, l = e - t * p.L;
+        g[e] = l < lu ? tile[t][l] : 0.f;
+    }
+    if (threadIdx.x < nt) {
+        const size_t row = (size_t)bh * p.T + t0 + threadIdx.x;
+        float d = 0.f;
+        for (int b = 0; b < ndvb; ++b) d += dqd[(size_t)b * rows + row];
+        p.dA1[row] = d;
+    }
+}
+
 // LDS of the chunk's two staged matrices (head dims dk and dv)
 template <typename E, int C>
 size_t chunk_pair_elems(int dk, int dv) {
@@ -1034,8 +1101,10 @@ hipError_t launch_bwd_typed(const BwdParams& p, hipStream_t stream) {
     // where it does not fit the LDS, the generic kernel runs instead
     const long whole = (long)p.dk * (p.dv + kPadB);
     const bool f1 = FDK > 0 && e1 >= whole, f3 = FDK > 0 && e3 >= whole;
-    hipError_t err;
-    if (f1) {
+    hipError_t err = hipSuccess;
+    if (p.dq_done) {
+        // dq, dlambda and dA1 come from the fused dq pass
+    } else if (f1) {
         err = set_smem(&k_bwd_dq<E, C, DM, FDK, FDV>, s1);
         if (err != hipSuccess) return err;
         hipLaunchKernelGGL((k_bwd_dq<E, C, DM, FDK, FDV>), dim3(nblk), dim3(C / 16 * 64), s1, stream, p1);
@@ -1109,6 +1178,18 @@ hipError_t launch_bwd_e(const BwdParams& p, hipStream_t s) {
 }
 
 }  // namespace
+
+hipError_t launch_bwd_chunk_cum(const BwdParams& p, hipStream_t stream) {
+    hipLaunchKernelGGL(k_bwd_chunk_cum, dim3(p.BH), dim3(256), 0, stream, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_bwd_dlam_sum(const BwdParams& p, const float* dlp, const float* dqd, int ndvb,
+                               int lu, hipStream_t stream) {
+    const unsigned blocks = (unsigned)p.BH * ((p.T + 63) / 64);
+    hipLaunchKernelGGL(k_bwd_dlam_sum, dim3(blocks), dim3(256), 0, stream, p, dlp, dqd, ndvb, lu);
+    return hipGetLastError();
+}
 
 hipError_t launch_bwd_chunked(const BwdParams& p, bool bf16, hipStream_t stream) {
     return bf16 ? launch_bwd_e<bf16_t>(p, stream) : launch_bwd_e<float>(p, stream);

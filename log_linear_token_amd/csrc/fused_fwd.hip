@@ -96,19 +96,100 @@ __device__ __forceinline__ void score_block(int rb, int sb, const bf16_t* Qs, co
         *reinterpret_cast<bf16x4*>(Ps + t * PROW + 16 * (rb + 1) + 4 * g) = bf16x4{};
 }
 
+// The dq pass of the backward runs this kernel with the operands swapped
+// (queries dO, keys v, values k: dq = ((dO v^T) (.) M) k) and needs, besides
+// the weighted block, the gradient of lambda: for the levels inside the tile
+//   dlambda_t^(l) = sum over the keys s of level l of dP[t, s] S[t, s] e^(A_t - A_s)
+// with dP = dO v^T (the block's unweighted scores) and S = q k^T.  S is taken
+// over this column block's 64 columns of q and k only (k is the staged value
+// tile, q the extra tile Qo); the column blocks' partial sums add up.  Row
+// sums per level go to LDS: sDi[tau][row] for the blocks below the diagonal
+// (one level each), sDd[rb][level][row] for the diagonal blocks (levels 0..4).
+template <int DK, int DVW>
+__device__ __forceinline__ void score_block_bwd(int rb, int sb, const bf16_t* Qs, const bf16_t* Ks,
+                                                const bf16_t* Qo, const bf16_t* Vs, bf16_t* Ps,
+                                                const float* Aw, const float* lam_s, int L,
+                                                float* sDi, float* sDd) {
+    typedef HD<DK> H;
+    const int lane = threadIdx.x & 63, m16 = lane & 15, g = lane >> 4;
+    const int t = 16 * rb + m16;
+    typename H::frag kf[H::NKS], qf[H::NKS];
+#pragma unroll
+    for (int ks = 0; ks < H::NKS; ++ks) {
+        kf[ks] = ld8<DK>(Ks, 16 * sb + m16, ks * 32 + 8 * g);
+        qf[ks] = ld8<DK>(Qs, t, ks * 32 + 8 * g);
+    }
+    bf16x8 kf2[DVW / 32], qf2[DVW / 32];
+#pragma unroll
+    for (int ks = 0; ks < DVW / 32; ++ks) {
+        kf2[ks] = ld8<DVW>(Vs, 16 * sb + m16, ks * 32 + 8 * g);
+        qf2[ks] = ld8<DVW>(Qo, t, ks * 32 + 8 * g);
+    }
+    const float* lam_t = lam_s + t * L;
+    const float At = Aw[t];
+    const float4 As = *reinterpret_cast<const float4*>(Aw + 16 * sb + 4 * g);
+    int lev[4];
+    if (sb < rb) {
+        lev[0] = lev[1] = lev[2] = lev[3] = 5 + (31 - __builtin_clz(rb ^ sb));
+    } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) lev[i] = fenwick_level(t, 16 * sb + 4 * g + i);
+    }
+    float lam[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) lam[i] = lam_t[lev[i]];
+    __builtin_amdgcn_sched_barrier(0);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f}, acc2 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < H::NKS; ++ks) acc = mma(kf[ks], qf[ks], acc);
+#pragma unroll
+    for (int ks = 0; ks < DVW / 32; ++ks) acc2 = mma(kf2[ks], qf2[ks], acc2);
+    const float Asv[4] = {As.x, As.y, As.z, As.w};
+    float w[4], xd[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bool keep = sb < rb || 16 * sb + 4 * g + i <= t;
+        const float e = __expf(At - Asv[i]);
+        w[i] = keep ? acc[i] * lam[i] * e : 0.f;
+        xd[i] = keep ? acc[i] * acc2[i] * e : 0.f;
+    }
+    *reinterpret_cast<bf16x4*>(Ps + t * PROW + 16 * sb + 4 * g) = pack4(w[0], w[1], w[2], w[3]);
+    if (sb == rb && (rb & 1) == 0)
+        *reinterpret_cast<bf16x4*>(Ps + t * PROW + 16 * (rb + 1) + 4 * g) = bf16x4{};
+    if (sb < rb) {
+        const float v = sum_rows4(xd[0] + xd[1] + xd[2] + xd[3]);
+        if (g == 0) sDi[(rb * (rb + 1) / 2 + sb) * 16 + m16] = v;
+    } else {
+#pragma unroll
+        for (int l = 0; l < 5; ++l) {
+            float x = 0.f;
+#pragma unroll
+            for (int i = 0; i < 4; ++i) x += lev[i] == l ? xd[i] : 0.f;
+            const float v = sum_rows4(x);
+            if (g == 0) sDd[(rb * 5 + l) * 16 + m16] = v;
+        }
+    }
+}
+
 // The ten causal 16 x 16 score blocks of a tile.  With eight waves, waves
 // 0 and 1 take three blocks, waves 2 and 3 two and waves 4-7 none (those make
-// the tile copies and the output stores); otherwise they are dealt
+// the tile copies and the output stores); otherwise, and in the dq pass (whose
+// blocks carry a second product and the dlambda sums), they are dealt
 // round-robin.
-template <int DK, int NWT>
+template <int DK, int NWT, bool BWD = false, int DVW = 64>
 __device__ __forceinline__ void scores_for_wave(int wave, const bf16_t* Qs, const bf16_t* Ks,
                                                 bf16_t* Ps, const float* Aw, const float* lam_s,
-                                                int L) {
+                                                int L, const bf16_t* Qo = nullptr,
+                                                const bf16_t* Vs = nullptr, float* sDi = nullptr,
+                                                float* sDd = nullptr) {
     auto block = [&](int tau) __attribute__((always_inline)) {
         const int rb = tau < 1 ? 0 : tau < 3 ? 1 : tau < 6 ? 2 : 3;
-        score_block<DK>(rb, tau - rb * (rb + 1) / 2, Qs, Ks, Ps, Aw, lam_s, L);
+        if constexpr (BWD)
+            score_block_bwd<DK, DVW>(rb, tau - rb * (rb + 1) / 2, Qs, Ks, Qo, Vs, Ps, Aw, lam_s, L, sDi, sDd);
+        else
+            score_block<DK>(rb, tau - rb * (rb + 1) / 2, Qs, Ks, Ps, Aw, lam_s, L);
     };
-    if constexpr (NWT == 8) {
+    if constexpr (NWT == 8 && !BWD) {
         // one loop (a single call site): waves 0-3 take tau = w, w + 4 and
         // waves 0 and 1 also w + 8
         const int t1 = wave < 2 ? wave + 12 : wave < 4 ? wave + 8 : 0;
@@ -233,7 +314,11 @@ __global__ __launch_bounds__(NW * 64) void k_seg_state(FusedParams p) {
 //   MLOC    register-resident levels inside a segment (segments of <= 2^MLOC tiles)
 //   TOPMAX  levels above the segment held as bf16 fragments
 
-template <int DK, int NW, int NH, int MLOC, int TOPMAX>
+//   BWD     the dq pass of the backward (operands swapped, see score_block_bwd):
+//           also stages this column block's columns of q (p.qo) and writes
+//           the block's partial dlambda rows to p.dlp
+
+template <int DK, int NW, int NH, int MLOC, int TOPMAX, bool BWD>
 __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
     typedef HD<DK> H;
     constexpr int NWT = NW * NH;            // waves per block
@@ -260,6 +345,20 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
     __shared__ __align__(16) float sEw0[TC];
     __shared__ __align__(16) float sEw1[TC];
     __shared__ __align__(16) f32x4 sX[(NH > 1 ? NH * NW * NRB : 1) * 64];  // partial outputs
+    // dq pass: q's columns of this block, and the per-row dlambda partial sums
+    // (levels inside the tile from the score blocks; per wave and level slot
+    // for the levels above it: slot s < MLOC local level s, MLOC + q top level q)
+    constexpr int NLS = MLOC + TOPMAX;
+    static_assert(NRB == 4, "the four-row-block lane reductions");
+    __shared__ __align__(16) bf16_t sQo0[BWD ? TC * DVW : 8];
+    __shared__ __align__(16) bf16_t sQo1[BWD ? TC * DVW : 8];
+    __shared__ __align__(16) float sDl[BWD ? NLS * NWT * TC : 4];
+    __shared__ __align__(16) float sDi[BWD ? 10 * 16 : 4];
+    __shared__ __align__(16) float sDd[BWD ? NRB * 5 * 16 : 4];
+    // per wave q_t . (its part of dq_t), by tile parity: summed over the
+    // waves after the next tile's first barrier (q . dq from the dq this
+    // pass writes, the rounding the dk / dv stage sees as well)
+    __shared__ __align__(16) float sDq[BWD ? 2 * NWT * TC : 4];
     // sX slots hold the 64 lanes of a C-layout fragment; lane l of slab cs is
     // stored at l ^ ((l / 16 + 4 (cs & 1)) & 7), so that the whole-row reads
     // of the finishers (eight lanes over two slabs and four lane groups per
@@ -321,16 +420,18 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
     const bool dwave = wave == P1W0;  // copies a; computes each tile's decay
     TileCopy<DK, NIW> cqk;  // Q and K tiles share the layout
     TileCopy<DVW, NIW1> cv;
+    TileCopy<DVW, NIW1> cqo;  // dq pass: q's columns, laid out as the value tile
     cqk.init(DK, 0, iw);
     cv.init(p.dv, cb, i1);
+    if constexpr (BWD) cqo.init(p.dv, cb, i1);
 
     // Every tile input goes global -> LDS through the DMA path: 16-byte
     // copies where rows are whole and aligned, 4-byte copies of lambda and a
     // otherwise (entries past the sequence are stored as zeros).
     // part 0: Q and K (issuing waves iw); part 1: V, lambda and a (issuing
     // waves i1)
-    auto issue = [&](int il, int part, bf16_t* Qd, bf16_t* Kd, bf16_t* Vd, float* Ld, float* ad)
-        __attribute__((always_inline)) {
+    auto issue = [&](int il, int part, bf16_t* Qd, bf16_t* Kd, bf16_t* Vd, float* Ld, float* ad,
+                     bf16_t* Qod) __attribute__((always_inline)) {
         const int t0 = (tile0 + il) * TC;
         const int nvalid = min(TC, p.T - t0);
         const size_t r = row0 + t0;
@@ -348,6 +449,10 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
         }
         if (whole) cv.template issue<true>(p.v + r * p.dv, Vd, i1);
         else dma_tile<DVW, NIW1>(p.v + r * p.dv, p.dv, cb, nvalid, Vd, i1);
+        if constexpr (BWD) {
+            if (whole) cqo.template issue<true>(p.qo + r * p.dv, Qod, i1);
+            else dma_tile<DVW, NIW1>(p.qo + r * p.dv, p.dv, cb, nvalid, Qod, i1);
+        }
         // lambda from the last issuing wave down (those hold fewer Q/K/V jobs)
         const int lw = NIW1 - 1 - i1;
         if (whole && p.lam_dma) {
@@ -420,28 +525,48 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
         }
     };
     const bool finisher = NH > 1 && hh == NH - 1;
+    // dq pass: q . dq of tile il of the segment (its rows < T), this column
+    // block's part, summed over the waves' parts
+    auto finish_qdq = [&](int il) __attribute__((always_inline)) {
+        if constexpr (BWD) {
+            const int t = threadIdx.x;
+            const int t0 = (tile0 + il) * TC;
+            if (t < TC && t0 + t < p.T) {
+                float x = 0.f;
+#pragma unroll
+                for (int u = 0; u < NWT; ++u) x += sDq[((il & 1) * NWT + u) * TC + t];
+                p.dqd[((size_t)dvb * p.BH + bh) * p.T + t0 + t] = x;
+            }
+        }
+    };
 
     auto body = [&](int il, const bf16_t* Qc, const bf16_t* Kc, const bf16_t* Vc,
-                    const float* Lc, const float* Awc, const float* Ewc, bf16_t* Qn, bf16_t* Kn,
-                    bf16_t* Vn, float* Ln, float* an, float* Awn, float* Ewn)
-        __attribute__((always_inline)) {
+                    const float* Lc, const float* Awc, const float* Ewc, const bf16_t* Qoc,
+                    bf16_t* Qn, bf16_t* Kn, bf16_t* Vn, float* Ln, float* an, float* Awn,
+                    float* Ewn, bf16_t* Qon) __attribute__((always_inline)) {
         // tile il is in LDS and every wave is done with tile il - 1
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+        if constexpr (BWD) {
+            if (il > 0) finish_qdq(il - 1);
+        }
         if constexpr (NH > 1) {
             if (finisher && !issuer && prev_tile >= 0) finish_prev();
         }
         const int i = tile0 + il;
         const int nvalid = min(TC, p.T - i * TC);
         const float tot = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(Awc[TC - 1])));
-        scores_for_wave<DK, NWT>(wave, Qc, Kc, sP, Awc, Lc, LP);
+        if constexpr (BWD)
+            scores_for_wave<DK, NWT, true, DVW>(wave, Qc, Kc, sP, Awc, Lc, LP, Qoc, Vc, sDi, sDd);
+        else
+            scores_for_wave<DK, NWT>(wave, Qc, Kc, sP, Awc, Lc, LP);
         if (issuer) {
             if constexpr (NH > 1) {
                 if (finisher && prev_tile >= 0) finish_prev();
             }
-            if (il + 1 < ntl) issue(il + 1, 0, Qn, Kn, Vn, Ln, an);
+            if (il + 1 < ntl) issue(il + 1, 0, Qn, Kn, Vn, Ln, an, Qon);
         }
-        if (issuer1 && il + 1 < ntl) issue(il + 1, 1, Qn, Kn, Vn, Ln, an);
+        if (issuer1 && il + 1 < ntl) issue(il + 1, 1, Qn, Kn, Vn, Ln, an, Qon);
 
         // ---- level products (this wave's head-dim part, all rows), before the
         // barrier that publishes P: they do not need it.  The weight of level
@@ -462,7 +587,18 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
                 else qf[rb][ks] = ld4<DK>(Qc, 16 * rb + m16, 4 * g);
             }
         }
-        auto add_level = [&](const typename H::frag (&ga)[NKSH], int lev, float logd)
+        // dq pass: q at (row 16 rb + m16, columns c0 + 4g .. + 3), the columns
+        // of this lane's level-product outputs
+        float qv[BWD ? NRB : 1][4];
+        if constexpr (BWD) {
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb) {
+                const bf16x4 x = ld4<DVW>(Qoc, 16 * rb + m16, 16 * cs + 4 * g);
+#pragma unroll
+                for (int r = 0; r < 4; ++r) qv[rb][r] = (float)x[r];
+            }
+        }
+        auto add_level = [&](const typename H::frag (&ga)[NKSH], int lev, float logd, int slot)
             __attribute__((always_inline)) {
             const float d = __expf(logd);
             float w[NRB];
@@ -483,6 +619,17 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
                 lv[rb][2] += wr * y[rb][2];
                 lv[rb][3] += wr * y[rb][3];
             }
+            if constexpr (BWD) {
+                // this wave's part of q_t . (level product) e^(logd); e^(A_t)
+                // is applied when the parts are summed.  Lane (m16, g) ends
+                // with row block g's total for token 16 g + m16.
+                float x[NRB];
+#pragma unroll
+                for (int rb = 0; rb < NRB; ++rb)
+                    x[rb] = qv[rb][0] * y[rb][0] + qv[rb][1] * y[rb][1] + qv[rb][2] * y[rb][2] +
+                            qv[rb][3] * y[rb][3];
+                sDl[(slot * NWT + wave) * TC + lane] = d * sum_rows4_x4(x[0], x[1], x[2], x[3]);
+            }
         };
         // levels inside the segment
 #pragma unroll
@@ -494,14 +641,48 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
                     if constexpr (DK >= 32) ga[ks] = __builtin_shufflevector(G[s][2 * ks], G[s][2 * ks + 1], 0, 1, 2, 3, 4, 5, 6, 7);
                     else ga[ks] = G[s][ks];
                 }
-                add_level(ga, LOGTC + s + 1, logd_loc[s]);
+                add_level(ga, LOGTC + s + 1, logd_loc[s], s);
             }
         }
         // levels above the segment
 #pragma unroll
         for (int q = 0; q < TOPMAX; ++q)
-            if (q < p.ntop && ((seg >> q) & 1)) add_level(top[q], LOGTC + p.m + q + 1, logd_top[q]);
+            if (q < p.ntop && ((seg >> q) & 1)) add_level(top[q], LOGTC + p.m + q + 1, logd_top[q], MLOC + q);
         __syncthreads();
+        if constexpr (BWD) {
+            // the tile's dlambda for this column block, level-major ([LU][T]
+            // rows of dlp): wave w takes the levels w, w + NWT, ..., lane t the
+            // token; levels 0..4 from the diagonal score blocks, 5 and 6 from
+            // the blocks below it, the levels above the tile from the level
+            // products (summed over the waves' parts, times e^(A_t))
+            const int t = lane, rb = t >> 4, mm = t & 15;
+            float* dst = p.dlp + ((size_t)dvb * p.BH + bh) * (size_t)p.LU * p.T + (size_t)i * TC + t;
+            for (int l = wave; l < p.LU; l += NWT) {
+                float val = 0.f;
+                if (l <= 4) {
+                    val = sDd[(rb * 5 + l) * 16 + mm];
+                } else if (l == 5) {
+                    if (rb & 1) val = sDi[(rb * (rb + 1) / 2 + rb - 1) * 16 + mm];
+                } else if (l == 6) {
+                    if (rb >= 2) val = sDi[(rb * (rb + 1) / 2) * 16 + mm] + sDi[(rb * (rb + 1) / 2 + 1) * 16 + mm];
+                } else {
+                    const int sl = l - LOGTC - 1;
+                    int slot = -1;
+                    if (sl < p.m) {
+                        if (sl < MLOC && ((il >> sl) & 1)) slot = sl;
+                    } else if (sl - p.m < p.ntop && sl - p.m < TOPMAX && ((seg >> (sl - p.m)) & 1)) {
+                        slot = MLOC + sl - p.m;
+                    }
+                    if (slot >= 0) {
+                        float x = 0.f;
+#pragma unroll
+                        for (int u = 0; u < NWT; ++u) x += sDl[(slot * NWT + u) * TC + t];
+                        val = x * __expf(Awc[t]);
+                    }
+                }
+                if (t < nvalid) dst[(size_t)l * p.T] = val;
+            }
+        }
 
         // ---- intra-tile P V for the row blocks this wave writes
         bf16x8 vf[2];
@@ -533,6 +714,14 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
                 for (int sp = 0; sp <= rb / 2; ++sp) o[rb] = mma(vf[sp], pf[rb][sp], o[rb]);
         }
 
+        if constexpr (BWD) {
+            float x[NRB];
+#pragma unroll
+            for (int rb = 0; rb < NRB; ++rb)
+                x[rb] = qv[rb][0] * o[rb][0] + qv[rb][1] * o[rb][1] + qv[rb][2] * o[rb][2] +
+                        qv[rb][3] * o[rb][3];
+            sDq[((il & 1) * NWT + wave) * TC + lane] = sum_rows4_x4(x[0], x[1], x[2], x[3]);
+        }
         if constexpr (NH > 1) {
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb) sX[((hh * NW + cs) * NRB + rb) * 64 + xswz(lane, cs)] = o[rb];
@@ -589,20 +778,23 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
         }
     };
 
-    if (issuer) issue(0, 0, sQ0, sK0, sV0, sL0, sa0);
-    if (issuer1) issue(0, 1, sQ0, sK0, sV0, sL0, sa0);
+    if (issuer) issue(0, 0, sQ0, sK0, sV0, sL0, sa0, sQo0);
+    if (issuer1) issue(0, 1, sQ0, sK0, sV0, sL0, sa0, sQo0);
     if (dwave) {
         __builtin_amdgcn_s_waitcnt(0);
         tile_decay(sa0, sAw0, sEw0);
     }
     for (int il = 0; il < ntl; il += 2) {
-        body(il, sQ0, sK0, sV0, sL0, sAw0, sEw0, sQ1, sK1, sV1, sL1, sa1, sAw1, sEw1);
+        body(il, sQ0, sK0, sV0, sL0, sAw0, sEw0, sQo0, sQ1, sK1, sV1, sL1, sa1, sAw1, sEw1, sQo1);
         if (il + 1 < ntl)
-            body(il + 1, sQ1, sK1, sV1, sL1, sAw1, sEw1, sQ0, sK0, sV0, sL0, sa0, sAw0, sEw0);
+            body(il + 1, sQ1, sK1, sV1, sL1, sAw1, sEw1, sQo1, sQ0, sK0, sV0, sL0, sa0, sAw0, sEw0, sQo0);
     }
-    if constexpr (NH > 1) {
+    if constexpr (NH > 1 || BWD) {
         __syncthreads();
-        if (finisher) finish_prev();
+        if constexpr (NH > 1) {
+            if (finisher) finish_prev();
+        }
+        if constexpr (BWD) finish_qdq(ntl - 1);
     }
 }
 
@@ -685,7 +877,16 @@ template <int DK, int NW, int MLOC, int TOPMAX>
 hipError_t launch_main(const FusedParams& p, hipStream_t stream) {
     constexpr int NH = DK >= 64 ? 2 : 1;  // two waves share a column slab, each half of d_k
     const unsigned nblk = (unsigned)p.BH * p.nseg * p.ndvb;
-    hipLaunchKernelGGL((k_fused_fwd<DK, NW, NH, MLOC, TOPMAX>), dim3(nblk), dim3(NW * NH * 64), 0,
+    if (p.qo) {
+        // the backward's dq pass: d_v = 64 (the contraction here) only
+        if constexpr (DK == 64 && NW == 4) {
+            hipLaunchKernelGGL((k_fused_fwd<DK, NW, NH, MLOC, TOPMAX, true>), dim3(nblk),
+                               dim3(NW * NH * 64), 0, stream, p);
+            return hipGetLastError();
+        }
+        return hipErrorInvalidValue;
+    }
+    hipLaunchKernelGGL((k_fused_fwd<DK, NW, NH, MLOC, TOPMAX, false>), dim3(nblk), dim3(NW * NH * 64), 0,
                        stream, p);
     return hipGetLastError();
 }

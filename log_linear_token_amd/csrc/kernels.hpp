@@ -61,6 +61,12 @@ struct FusedParams {
     float* stot;                    // [BH][nseg]
     double* scum;                   // [BH][nseg]
     const bf16_t_storage* gfrag;    // bf16 MFMA fragments of the nodes (written by the scan)
+    // the backward's dq pass (q, k, v above are dO, v, k): the original q
+    // ([BH][T][dv], dv here being the original d_k) and the partial dlambda
+    // of each column block, level-major ([ndvb][BH][LU][T]); qo == nullptr otherwise
+    const bf16_t_storage* qo;
+    float* dlp;
+    float* dqd;                     // [ndvb][BH][T] each column block's part of q_t . dq_t
 };
 struct FusedPlan {
     int ok, m, nseg, ntop, dvw, ndvb, ntiles, combo, msub;
@@ -144,11 +150,18 @@ struct BwdParams {
     float* dA2;               // [BH][T] k_t . dk_t
     int st_elems;             // bf16 elements of the LDS buffer that stages one carried state
     int rs_nbuf;              // copies of the staged chunk the R(j) kernel keeps (1 or 2)
+    int dq_done;              // dq, dlambda and dA1 already written (fused dq pass)
 };
 hipError_t launch_bwd_chunked(const BwdParams& p, bool bf16, hipStream_t stream);
 // R(j) of every block in one pass over the query chunks (bf16, C = 64,
 // d_v = 64, d_k in {64, 128}, N <= 256): whether it applies, and the launch
 bool bwd_rwalk_applies(const BwdParams& p);
+// A at the end of every chunk ([BH][N] double, into p.cum) from a alone
+hipError_t launch_bwd_chunk_cum(const BwdParams& p, hipStream_t stream);
+// dlambda = the sum of the column blocks' parts dlp ([ndvb][BH][lu][T], the
+// levels past lu zero), and dA1_t = q_t . dq_t, the sum of their parts dqd ([ndvb][BH][T])
+hipError_t launch_bwd_dlam_sum(const BwdParams& p, const float* dlp, const float* dqd, int ndvb,
+                               int lu, hipStream_t stream);
 hipError_t launch_bwd_rwalk(const BwdParams& p, hipStream_t stream);
 
 // Fenwick level states after the T tokens of a prefill (the state a decode

@@ -155,6 +155,83 @@ Plan make_plan(long BH, int T, int dk, int dv, int C, loglin_dtype dt) {
     return pl;
 }
 
+// The fused path (segment states, their scan, the main kernel) for one
+// problem: q, k, v bf16 [BH][T][dk|dk|dv], out fp32 [BH][T][dv].  qo and dlp
+// select the backward's dq pass of the main kernel (nullptr for a forward).
+hipError_t launch_fused_path(const FusedPlan& f, const FwdWorkspace& w, char* base, const void* q,
+                             const void* k, const void* v, const float* log_decay,
+                             const float* lambda, float* out, long BH, int T, int dk, int dv,
+                             int L, int C, unsigned stage_mask, hipStream_t hs,
+                             const void* qo = nullptr, float* dlp = nullptr,
+                             float* dqd = nullptr) {
+    FwdParams p{};
+    p.q = q;
+    p.k = k;
+    p.v = v;
+    p.a = log_decay;
+    p.lam = lambda;
+    p.out = out;
+    p.BH = (int)BH;
+    p.T = T;
+    p.dk = dk;
+    p.dv = dv;
+    p.L = L;
+    p.C = C;
+    p.N = f.nseg;
+    p.nscan = f.nseg - 1;
+    if (w.total > 0) {
+        p.ust = reinterpret_cast<float*>(base + w.ust_off);
+        p.tot = reinterpret_cast<float*>(base + w.tot_off);
+        p.cum = reinterpret_cast<double*>(base + w.cum_off);
+    }
+    FusedParams fp{};
+    fp.q = static_cast<const bf16_t_storage*>(q);
+    fp.k = static_cast<const bf16_t_storage*>(k);
+    fp.v = static_cast<const bf16_t_storage*>(v);
+    fp.a = log_decay;
+    fp.lam = lambda;
+    fp.out = out;
+    fp.BH = (int)BH;
+    fp.T = T;
+    fp.dk = dk;
+    fp.dv = dv;
+    fp.L = L;
+    fp.LU = levels_needed(T);
+    fp.ntiles = f.ntiles;
+    fp.m = f.m;
+    fp.nseg = f.nseg;
+    fp.ntop = f.ntop;
+    fp.dvw = f.dvw;
+    fp.ndvb = f.ndvb;
+    fp.useg = p.ust;
+    fp.stot = p.tot;
+    fp.scum = p.cum;
+    fp.combo = f.combo;
+    // lambda rows are copied whole when they fit the kernel's staging area
+    // and every tile's rows start on a 16-byte boundary; otherwise the
+    // levels in use are loaded element by element
+    fp.lpitch = L <= kFusedMaxL ? L : fp.LU;
+    fp.lam_dma = L <= kFusedMaxL && ((long)T * L) % 4 == 0 &&
+                 reinterpret_cast<uintptr_t>(lambda) % 16 == 0;
+    fp.a_dma = T % 4 == 0 && reinterpret_cast<uintptr_t>(log_decay) % 16 == 0;
+    fp.msub = f.msub;
+    fp.qo = static_cast<const bf16_t_storage*>(qo);
+    fp.dlp = dlp;
+    fp.dqd = dqd;
+    if (w.total > 0) {
+        p.gfrag = reinterpret_cast<bf16_t_storage*>(base + w.frag_off);
+        fp.gfrag = p.gfrag;
+        if (f.m > f.msub) {  // segment states come in sub-ranges
+            fp.upart = reinterpret_cast<float*>(base + w.upart_off);
+            fp.tpart = reinterpret_cast<float*>(base + w.tpart_off);
+            p.upart = fp.upart;
+            p.tpart = fp.tpart;
+            p.nsub = 1 << (f.m - f.msub);
+        }
+    }
+    return launch_fused_fwd(fp, p, stage_mask, hs);
+}
+
 }  // namespace
 
 extern "C" {
@@ -243,77 +320,34 @@ loglin_status loglin_fwd_chunked_stages(const void* q, const void* k, const void
         reinterpret_cast<uintptr_t>(v) % 16 || reinterpret_cast<uintptr_t>(out) % 16)
         return fail(LOGLIN_EINVAL, "q, k, v and out must be 16-byte aligned");
 
-    // the chunk (or segment) state buffers, shared by both paths' scan
-    FwdParams p{};
-    p.q = q;
-    p.k = k;
-    p.v = v;
-    p.a = log_decay;
-    p.lam = lambda;
-    p.out = out;
-    p.BH = (int)BH;
-    p.T = T;
-    p.dk = dk;
-    p.dv = dv;
-    p.L = L;
-    p.C = C;
-    p.N = (int)pl.N;
-    p.nscan = (int)pl.N - 1;
-    if (w.total > 0) {
-        char* base = static_cast<char*>(workspace);
-        p.ust = reinterpret_cast<float*>(base + w.ust_off);
-        p.tot = reinterpret_cast<float*>(base + w.tot_off);
-        p.cum = reinterpret_cast<double*>(base + w.cum_off);
-    }
     hipStream_t hs = static_cast<hipStream_t>(stream);
     hipError_t e;
     if (pl.path == kPathFused) {
-        const FusedPlan& f = pl.fused;
-        FusedParams fp{};
-        fp.q = static_cast<const bf16_t_storage*>(q);
-        fp.k = static_cast<const bf16_t_storage*>(k);
-        fp.v = static_cast<const bf16_t_storage*>(v);
-        fp.a = log_decay;
-        fp.lam = lambda;
-        fp.out = out;
-        fp.BH = (int)BH;
-        fp.T = T;
-        fp.dk = dk;
-        fp.dv = dv;
-        fp.L = L;
-        fp.LU = levels_needed(T);
-        fp.ntiles = f.ntiles;
-        fp.m = f.m;
-        fp.nseg = f.nseg;
-        fp.ntop = f.ntop;
-        fp.dvw = f.dvw;
-        fp.ndvb = f.ndvb;
-        fp.useg = p.ust;
-        fp.stot = p.tot;
-        fp.scum = p.cum;
-        fp.combo = f.combo;
-        // lambda rows are copied whole when they fit the kernel's staging area
-        // and every tile's rows start on a 16-byte boundary; otherwise the
-        // levels in use are loaded element by element
-        fp.lpitch = L <= kFusedMaxL ? L : fp.LU;
-        fp.lam_dma = L <= kFusedMaxL && ((long)T * L) % 4 == 0 &&
-                     reinterpret_cast<uintptr_t>(lambda) % 16 == 0;
-        fp.a_dma = T % 4 == 0 && reinterpret_cast<uintptr_t>(log_decay) % 16 == 0;
-        fp.msub = f.msub;
+        e = launch_fused_path(pl.fused, w, static_cast<char*>(workspace), q, k, v, log_decay, lambda,
+                              out, BH, T, dk, dv, L, C, stage_mask, hs);
+    } else {
+        // the chunk state buffers of the chunked path
+        FwdParams p{};
+        p.q = q;
+        p.k = k;
+        p.v = v;
+        p.a = log_decay;
+        p.lam = lambda;
+        p.out = out;
+        p.BH = (int)BH;
+        p.T = T;
+        p.dk = dk;
+        p.dv = dv;
+        p.L = L;
+        p.C = C;
+        p.N = (int)pl.N;
+        p.nscan = (int)pl.N - 1;
         if (w.total > 0) {
             char* base = static_cast<char*>(workspace);
-            p.gfrag = reinterpret_cast<bf16_t_storage*>(base + w.frag_off);
-            fp.gfrag = p.gfrag;
-            if (f.m > f.msub) {  // segment states come in sub-ranges
-                fp.upart = reinterpret_cast<float*>(base + w.upart_off);
-                fp.tpart = reinterpret_cast<float*>(base + w.tpart_off);
-                p.upart = fp.upart;
-                p.tpart = fp.tpart;
-                p.nsub = 1 << (f.m - f.msub);
-            }
+            p.ust = reinterpret_cast<float*>(base + w.ust_off);
+            p.tot = reinterpret_cast<float*>(base + w.tot_off);
+            p.cum = reinterpret_cast<double*>(base + w.cum_off);
         }
-        e = launch_fused_fwd(fp, p, stage_mask, hs);
-    } else {
         e = launch_fwd_chunked(p, in_dtype == LOGLIN_BF16, stage_mask, hs);
     }
     if (e != hipSuccess) return hip_fail(e, "loglin_fwd_chunked launch");
@@ -447,20 +481,52 @@ loglin_status loglin_gdn_fwd_chunked(const void* q, const void* k, const void* v
 
 namespace {
 
-// workspace of the backward: the Fenwick nodes of k v^T over chunks (the
-// forward's chunk-state and scan buffers), the block states R and R^T, and
-// the two per-token dot products that make up the decay gradient
+// LOGLIN_BWD_DQ=chunked keeps the dq / dlambda stage of the backward on the
+// chunk-state path for bf16 inputs too (the fused dq pass is the default
+// where it applies).
+bool force_bwd_dq_chunked() {
+    const char* e = getenv("LOGLIN_BWD_DQ");
+    return e && strcmp(e, "chunked") == 0;
+}
+
+// Workspace of the backward.  dq / dlambda either by the fused path run on
+// the swapped problem (queries dO, keys v, values k; its segment states, the
+// per-column-block dlambda rows, the chunk-level decay prefix) or from the
+// Fenwick nodes of k v^T over chunks (the forward's chunk-state and scan
+// buffers); then the block states R and R^T and the two per-token dot
+// products that make up the decay gradient.
 struct BwdWorkspace {
-    FwdWorkspace nodes;
+    bool fused_dq;
+    FusedPlan fq;        // the fused dq pass's plan (fused_dq)
+    FwdWorkspace nodes;  // its segment buffers, or the chunk nodes
+    size_t dlp_off, dqd_off, ccum_off;
     size_t rst_off, rstT_off, da1_off, da2_off, total;
 };
 
-BwdWorkspace bwd_layout(long BH, int T, int dk, int dv, int C) {
+BwdWorkspace bwd_layout(long BH, int T, int dk, int dv, int C, loglin_dtype dt) {
     BwdWorkspace w{};
     const long N = ((long)T + C - 1) / C;
-    w.nodes = fwd_workspace_layout(BH, N, dk, dv, false, 1);
+    size_t off = 0;
+    if (dt == LOGLIN_BF16 && dv == 64 && (dk == 64 || dk == 128) && T > 0 && BH > 0 &&
+        !force_bwd_dq_chunked()) {
+        const FusedPlan f = plan_fused((int)BH, T, dv, dk, levels_needed(T), -1, -1);
+        if (f.ok) {
+            w.fused_dq = true;
+            w.fq = f;
+            w.nodes = fwd_workspace_layout(BH, f.nseg, dv, dk, true, 1 << (f.m - f.msub));
+            w.dlp_off = w.nodes.total;
+            // per column block: dlambda rows [ndvb][BH][T][levels the sequence
+            // uses] and the parts of q . dq [ndvb][BH][T]
+            w.dqd_off = align_up(w.dlp_off + (size_t)f.ndvb * BH * T * levels_needed(T) * sizeof(float));
+            w.ccum_off = align_up(w.dqd_off + (size_t)f.ndvb * BH * T * sizeof(float));
+            off = align_up(w.ccum_off + (size_t)BH * N * sizeof(double));
+        }
+    }
+    if (!w.fused_dq) {
+        w.nodes = fwd_workspace_layout(BH, N, dk, dv, false, 1);
+        off = w.nodes.total;
+    }
     const size_t st = N > 1 ? (size_t)BH * N * dk * dv * sizeof(float) : 0;
-    size_t off = w.nodes.total;
     w.rst_off = off;
     off = align_up(off + st);
     w.rstT_off = off;
@@ -483,7 +549,7 @@ size_t loglin_bwd_workspace_bytes(int B, int H, int T, int dk, int dv, int C, lo
         fail(LOGLIN_EINVAL, "in_dtype %d is neither LOGLIN_F32 nor LOGLIN_BF16", (int)in_dtype);
         return (size_t)-1;
     }
-    return bwd_layout((long)B * H, T, dk, dv, C).total;
+    return bwd_layout((long)B * H, T, dk, dv, C, in_dtype).total;
 }
 
 loglin_status loglin_bwd_chunked(const void* q, const void* k, const void* v, const float* log_decay,
@@ -507,7 +573,7 @@ loglin_status loglin_bwd_chunked(const void* q, const void* k, const void* v, co
                          reinterpret_cast<uintptr_t>(dv_out);
     if (al % 16) return fail(LOGLIN_EINVAL, "q, k, v, dout, dq, dk and dv must be 16-byte aligned");
     const long BH = (long)B * H;
-    const BwdWorkspace w = bwd_layout(BH, T, dk, dv, C);
+    const BwdWorkspace w = bwd_layout(BH, T, dk, dv, C, in_dtype);
     if (!workspace || workspace_bytes < w.total)
         return fail(LOGLIN_EINVAL, "workspace of %zu bytes needed, got %zu%s", w.total, workspace_bytes,
                     workspace ? "" : " (NULL)");
@@ -539,7 +605,27 @@ loglin_status loglin_bwd_chunked(const void* q, const void* k, const void* v, co
     bp.nlev = bit_length(N - 1);
     bp.dA1 = reinterpret_cast<float*>(base + w.da1_off);
     bp.dA2 = reinterpret_cast<float*>(base + w.da2_off);
-    if (N > 1) {
+    if (w.fused_dq) {
+        // dq = ((dO v^T) (.) M) k: the fused path over (dO, v, k), which also
+        // leaves each column block's dlambda rows and part of q . dq; then
+        // their sums
+        float* dlp = reinterpret_cast<float*>(base + w.dlp_off);
+        float* dqd = reinterpret_cast<float*>(base + w.dqd_off);
+        hipError_t e = launch_fused_path(w.fq, w.nodes, base, dout, v, k, log_decay, lambda, dq, BH, T,
+                                         dv, dk, L, C, kStageAll, hs, q, dlp, dqd);
+        if (e != hipSuccess) return hip_fail(e, "loglin_bwd_chunked dq launch");
+        e = launch_bwd_dlam_sum(bp, dlp, dqd, w.fq.ndvb, levels_needed(T), hs);
+        if (e != hipSuccess) return hip_fail(e, "loglin_bwd_chunked dlambda launch");
+        bp.dq_done = 1;
+        if (N > 1) {
+            bp.cum = reinterpret_cast<double*>(base + w.ccum_off);
+            e = launch_bwd_chunk_cum(bp, hs);
+            if (e != hipSuccess) return hip_fail(e, "loglin_bwd_chunked decay prefix launch");
+            bp.rst = reinterpret_cast<float*>(base + w.rst_off);
+            bp.rstT = reinterpret_cast<float*>(base + w.rstT_off);
+            bp.rst16 = reinterpret_cast<bf16_t_storage*>(base + w.rst_off);
+        }
+    } else if (N > 1) {
         // the forward's chunk states and node scan over k and v swapped: the
         // nodes come out as sum k v^T, [dk][dv]
         FwdParams fp{};

@@ -225,6 +225,30 @@ __device__ __forceinline__ bf16x4 cvt4(const f32x4& a) {
     return r;
 }
 
+// Sum over the four 16-lane rows of a wave, in every lane (lane l gets the
+// sum of lanes l % 16, + 16, + 32, + 48): the row-swap instructions of
+// gfx950 pair rows (0,1), (2,3), then halves, with no LDS traffic.
+__device__ __forceinline__ float sum_rows4(float x) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    x = __uint_as_float(a[0]) + __uint_as_float(a[1]);
+    const auto b = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(b[0]) + __uint_as_float(b[1]);
+}
+
+// Four values per lane (x[r] for 16-row block r of a tile, this lane's part
+// of token m = lane % 16) summed over the four 16-lane rows at once: row g
+// of the result holds the total of x[g] for token m.  Two row-pair swaps
+// fold (x0, x1) and (x2, x3) over rows (0,1) and (2,3); one half swap folds
+// the pairs over the halves.
+__device__ __forceinline__ float sum_rows4_x4(float x0, float x1, float x2, float x3) {
+    const auto a = __builtin_amdgcn_permlane16_swap(__float_as_uint(x0), __float_as_uint(x1), false, false);
+    const auto b = __builtin_amdgcn_permlane16_swap(__float_as_uint(x2), __float_as_uint(x3), false, false);
+    const float v = __uint_as_float(a[0]) + __uint_as_float(a[1]);  // rows: x0(01) x1(01) x0(23) x1(23)
+    const float u = __uint_as_float(b[0]) + __uint_as_float(b[1]);  // rows: x2(01) x3(01) x2(23) x3(23)
+    const auto c = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(u), false, false);
+    return __uint_as_float(c[0]) + __uint_as_float(c[1]);
+}
+
 __device__ __forceinline__ int xcd_block(int b, int nblocks) {
     if (nblocks % 8 != 0) return b;
     return (b % 8) * (nblocks / 8) + b / 8;

@@ -243,17 +243,49 @@ def _align(x):
     return (x + 255) // 256 * 256
 
 
+def _bwd_tail(BH, N, T, dk, dv, off):
+    """R and R^T (when N > 1), then the two per-token dot products."""
+    if N > 1:
+        off = _align(_align(off + BH * N * dk * dv * 4) + BH * N * dk * dv * 4)
+    return _align(_align(off + BH * T * 4) + BH * T * 4)
+
+
 @pytest.mark.parametrize("B,H,T,dk,dv,C", [(1, 1, 1, 16, 16, 16), (1, 2, 37, 16, 32, 16),
                                            (4, 16, 8192, 128, 64, 64), (1, 16, 65536, 128, 128, 128)])
-def test_bwd_workspace_bytes(lib, B, H, T, dk, dv, C):
+def test_bwd_workspace_bytes(lib, monkeypatch, B, H, T, dk, dv, C):
+    """The chunk-state layout: nodes, chunk totals, fp64 chunk ends, then R,
+    R^T and the dot products (fp32 inputs always; bf16 where the fused dq
+    pass does not apply or is switched off)."""
+    monkeypatch.setenv("LOGLIN_BWD_DQ", "chunked")
     BH, N = B * H, (T + C - 1) // C
-    want = 0
-    if N > 1:  # nodes, chunk totals, fp64 chunk ends, then R and R^T
-        want = _align(_align(_align(BH * N * dk * dv * 4) + BH * N * 4) + BH * N * 8)
-        want = _align(_align(want + BH * N * dk * dv * 4) + BH * N * dk * dv * 4)
-    want = _align(_align(want + BH * T * 4) + BH * T * 4)
+    off = 0
+    if N > 1:
+        off = _align(_align(_align(BH * N * dk * dv * 4) + BH * N * 4) + BH * N * 8)
+    want = _bwd_tail(BH, N, T, dk, dv, off)
     assert lib.loglin_bwd_workspace_bytes(B, H, T, dk, dv, C, 1) == want
     assert lib.loglin_bwd_workspace_bytes(B, H, T, dk, dv, C, 0) == want
+    monkeypatch.delenv("LOGLIN_BWD_DQ")
+    assert lib.loglin_bwd_workspace_bytes(B, H, T, dk, dv, C, 0) == want
+
+
+def test_bwd_workspace_bytes_fused_dq(lib, monkeypatch):
+    """bf16, d_v = 64: the fused dq pass's layout at the 8K workload's shape.
+    Its plan (swapped problem: d_k 64, d_v 128 in two column blocks of 64,
+    128 tiles, 64 (batch, head) pairs): segments of 32 tiles (every segment
+    length costs 64 serial tiles a compute unit; the longest wins), 4
+    segments, one sub-range each.  Segment nodes fp32 [64][4][128][64],
+    totals, fp64 ends, bf16 fragments; the dlambda parts [2][64][14][8192]
+    (positions below 8192 use levels 0..13) and the parts of q . dq [2][64][8192];
+    the fp64 chunk ends [64][128]; then R, R^T and the dot products."""
+    monkeypatch.delenv("LOGLIN_BWD_DQ", raising=False)
+    B, H, T, dk, dv, C = 4, 16, 8192, 128, 64, 64
+    BH, N, nseg, LU = B * H, T // C, 4, 14
+    off = _align(_align(_align(BH * nseg * dk * dv * 4) + BH * nseg * 4) + BH * nseg * 8)
+    off = _align(off + BH * nseg * dk * dv * 2)
+    off = _align(off + 2 * BH * T * LU * 4)
+    off = _align(off + 2 * BH * T * 4)
+    off = _align(off + BH * N * 8)
+    assert lib.loglin_bwd_workspace_bytes(B, H, T, dk, dv, C, 1) == _bwd_tail(BH, N, T, dk, dv, off)
 
 
 def _bwd(lib, B=1, H=1, T=64, dk=16, dv=16, L=8, C=16, dtype=1, ws=FAKE * 256, nws=1 << 30,

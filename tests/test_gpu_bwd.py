@@ -157,3 +157,20 @@ def test_bwd_rstate_paths(monkeypatch, mode, B, H, T, dk, dv):
         monkeypatch.delenv("LOGLIN_BWD_RSTATE", raising=False)
     banner(f"bwd R(j) {mode} B={B} H={H} T={T} dk={dk} dv={dv}")
     _check(B, H, T, dk, dv, 64, torch.bfloat16, seed=T, mu=-3.0)
+
+
+@pytest.mark.parametrize("mode", ["fused", "chunked"])
+@pytest.mark.parametrize("B,H,T,dk,C", [(1, 2, 1, 128, 64), (1, 2, 40, 64, 64), (2, 1, 777, 128, 64),
+                                        (1, 1, 3000, 128, 32), (1, 2, 2048, 64, 128),
+                                        (1, 1, 5000, 128, 64)])
+def test_bwd_dq_paths(monkeypatch, mode, B, H, T, dk, C):
+    """dq and dlambda from the fused pass over (dO, v, k) (which also gives
+    q . dq for the decay gradient) and from the chunk-state path: both give
+    the oracle's gradients (d_v = 64, one token, a partial tile, ragged
+    tails, every chunk size the other stages use)."""
+    if mode == "chunked":
+        monkeypatch.setenv("LOGLIN_BWD_DQ", "chunked")
+    else:
+        monkeypatch.delenv("LOGLIN_BWD_DQ", raising=False)
+    banner(f"bwd dq {mode} B={B} H={H} T={T} dk={dk} C={C}")
+    _check(B, H, T, dk, 64, C, torch.bfloat16, seed=T + dk, mu=-3.0)
