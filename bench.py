@@ -37,7 +37,7 @@ HBM_PEAK_GBS = 8000.0        # MI355X HBM3E, GB/s
 BF16_PEAK_TFLOPS = 2500.0    # dense bf16 MFMA, TFLOP/s
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "fwd8k_bwd8k_decode_hbm_traffic.txt")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "all_workloads_hbm_traffic.txt")
 
 
 def sources_hash(files: str) -> str:
@@ -590,7 +590,9 @@ def bench_fwd_other(name: str, steps: int, warmup: int) -> dict:
             "plan": plan,
             "roofline": {"kernel": name_out, "bound": "hbm", "achieved": round(km["GB/s"], 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                         "frac": round(km["GB/s"] / HBM_PEAK_GBS, 4), "mfma": mfma_entry(km)}}
+                         "frac": round(km["GB/s"] / HBM_PEAK_GBS, 4),
+                         "alg_bytes": m["bytes"], "traffic": measured_traffic(f"{name}_{name_out}"),
+                         "mfma": mfma_entry(km)}}
 
 
 def bench_prefill(cfg, sets, stream, steps: int) -> dict:
@@ -812,7 +814,8 @@ def bench_gdn_fwd(steps: int, warmup: int) -> dict:
         kernels[name] = {"ms": round(kms, 4), "TFLOP/s": round(tfl, 1),
                          "frac_fp32_mfma": round(tfl / FP32_PEAK_TFLOPS, 4),
                          "GB/s": round(gbs, 1), "frac_hbm": round(gbs / HBM_PEAK_GBS, 4),
-                         "alg_bytes": m["bytes"], "alg_flops": m["flops"]}
+                         "alg_bytes": m["bytes"], "alg_flops": m["flops"],
+                         "traffic": measured_traffic(name)}
         log(f"  {name}: {kms:.3f} ms, {tfl:.1f} TFLOP/s fp32, {gbs:.0f} GB/s")
     log(f"gdn8k forward: {ms:.3f} ms/step, {tps:.3e} tokens/s")
     del sets, ws, base
@@ -877,7 +880,7 @@ def bench_gdn_decode(steps: int) -> dict:
                        "dv": cfg.dv, "Lmax": cfg.Lmax},
             "roofline": {"kernel": "gdn_decode_step", "bound": "hbm", "achieved": round(gbs, 1),
                          "peak": HBM_PEAK_GBS, "unit": "GB/s", "frac": round(gbs / HBM_PEAK_GBS, 4),
-                         "alg_bytes_per_step": byts}}
+                         "alg_bytes_per_step": byts, "traffic": measured_traffic("gdn_decode_step")}}
 
 
 if __name__ == "__main__":
