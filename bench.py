@@ -441,7 +441,7 @@ def main() -> int:
                     help="only run a plain 1 GiB device-to-device copy (for scaling HBM counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py runs on one GPU only: this build has no multi-GPU path "
+        print("bench.py runs on one GPU only: the library has no multi-GPU path "
               f"(asked for --gpus {args.gpus})", file=sys.stderr)
         return 2
     if not torch.cuda.is_available():

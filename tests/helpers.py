@@ -15,7 +15,7 @@ _ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 # so that a run leaves its per-case margins behind (LOGLIN_PARITY_LOG=0 turns
 # this off).
 PARITY_LOG = os.environ.get("LOGLIN_PARITY_LOG",
-                            os.path.join(_ROOT, "gpurun_out", "parity_errors.tsv"))
+                            os.path.join(_ROOT, "test_logs", "parity_errors.tsv"))
 
 
 def record(kind: str, err: float) -> None:
