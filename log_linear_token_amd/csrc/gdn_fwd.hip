@@ -602,6 +602,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_gdn_chunk_bf(GdnParams p) {
     struct In {
         uint4 q[NQK], k[NQK], v[NVV];
         float a, beta, lam;
+        int nv;  // valid tokens of the chunk (rows past it are zeroed when staged)
     };
     auto fetch = [&](int cb, In& R) __attribute__((always_inline)) {
         const int fbh = cb / p.N, fci = cb - fbh * p.N;
@@ -611,42 +612,44 @@ __global__ __launch_bounds__(kChunkThreads) void k_gdn_chunk_bf(GdnParams p) {
         const bf16_t* k = static_cast<const bf16_t*>(p.k) + r0 * DK;
         const bf16_t* v = static_cast<const bf16_t*>(p.v) + r0 * DV;
         // lane l of a wave takes token row l: the transposed copies below then
-        // write 64 consecutive tokens per store
+        // write 64 consecutive tokens per store.  Every load is issued, rows
+        // past T reading the chunk's last valid row (zeroed when staged): a
+        // load under a branch leaves the compiler unsure how many memory
+        // operations follow it, and it then waits for all of them (the
+        // previous chunk's stores) before this chunk's data are used.  The
+        // loaded registers are not touched here, so the loads stay in flight.
+        R.nv = nv;
 #pragma unroll
         for (int u = 0; u < NQK; ++u) {
             const int e = tid + u * kChunkThreads;
-            const int r = e % GC, c8 = (e / GC) * 8;
-            R.q[u] = R.k[u] = make_uint4(0, 0, 0, 0);
-            if (r < nv) {
-                R.q[u] = *reinterpret_cast<const uint4*>(q + (size_t)r * DK + c8);
-                R.k[u] = *reinterpret_cast<const uint4*>(k + (size_t)r * DK + c8);
-            }
+            const int r = min(e % GC, nv - 1), c8 = (e / GC) * 8;
+            R.q[u] = *reinterpret_cast<const uint4*>(q + (size_t)r * DK + c8);
+            R.k[u] = *reinterpret_cast<const uint4*>(k + (size_t)r * DK + c8);
         }
 #pragma unroll
         for (int u = 0; u < NVV; ++u) {
-            const int e = tid + u * kChunkThreads;
-            const int r = e % GC, c8 = (e / GC) * 8;
-            R.v[u] = make_uint4(0, 0, 0, 0);
-            if (e < GC * DV / 8 && r < nv) R.v[u] = *reinterpret_cast<const uint4*>(v + (size_t)r * DV + c8);
+            const int e = min(tid + u * kChunkThreads, GC * DV / 8 - 1);
+            const int r = min(e % GC, nv - 1), c8 = (e / GC) * 8;
+            R.v[u] = *reinterpret_cast<const uint4*>(v + (size_t)r * DV + c8);
         }
-        R.a = R.beta = 0.f;
-        if (tid < nv) {
-            R.a = p.a[r0 + tid];
-            R.beta = p.beta[r0 + tid];
-        }
-        const int r = tid >> 3, l = tid & 7;
-        R.lam = (r < nv && l < min(p.L, 7)) ? p.lam[(r0 + r) * p.L + l] : 0.f;
+        const int tc = min(tid, nv - 1);
+        R.a = p.a[r0 + tc];
+        R.beta = p.beta[r0 + tc];
+        const int r = min(tid >> 3, nv - 1), l = min(tid & 7, min(p.L, 7) - 1);
+        R.lam = p.lam[(r0 + r) * p.L + l];
     };
     // q, k rows and k^T; v^T; a, beta, lambda 0..6 to LDS; the tiles above the
     // diagonal of Y and of the system zeroed
     auto stage = [&](const In& R) __attribute__((always_inline)) {
+        const uint4 z = make_uint4(0, 0, 0, 0);
 #pragma unroll
         for (int u = 0; u < NQK; ++u) {
             const int e = tid + u * kChunkThreads;
             const int r = e % GC, c8 = (e / GC) * 8;
-            *reinterpret_cast<uint4*>(sQ + r * PK + c8) = R.q[u];
-            *reinterpret_cast<uint4*>(sK + r * PK + c8) = R.k[u];
-            const bf16_t* kk = reinterpret_cast<const bf16_t*>(&R.k[u]);
+            const uint4 xq = r < R.nv ? R.q[u] : z, xk = r < R.nv ? R.k[u] : z;
+            *reinterpret_cast<uint4*>(sQ + r * PK + c8) = xq;
+            *reinterpret_cast<uint4*>(sK + r * PK + c8) = xk;
+            const bf16_t* kk = reinterpret_cast<const bf16_t*>(&xk);
 #pragma unroll
             for (int i = 0; i < 8; ++i) sKt[(c8 + i) * P64 + r] = kk[i];
         }
@@ -655,16 +658,17 @@ __global__ __launch_bounds__(kChunkThreads) void k_gdn_chunk_bf(GdnParams p) {
             const int e = tid + u * kChunkThreads;
             if (e < GC * DV / 8) {
                 const int r = e % GC, c8 = (e / GC) * 8;
-                const bf16_t* vv = reinterpret_cast<const bf16_t*>(&R.v[u]);
+                const uint4 xv = r < R.nv ? R.v[u] : z;
+                const bf16_t* vv = reinterpret_cast<const bf16_t*>(&xv);
 #pragma unroll
                 for (int i = 0; i < 8; ++i) sVt[(c8 + i) * P64 + r] = vv[i];
             }
         }
         if (tid < GC) {
-            sa[tid] = R.a;
-            sbeta[tid] = R.beta;
+            sa[tid] = tid < R.nv ? R.a : 0.f;
+            sbeta[tid] = tid < R.nv ? R.beta : 0.f;
         }
-        slam[tid] = R.lam;
+        slam[tid] = ((tid >> 3) < R.nv && (tid & 7) < min(p.L, 7)) ? R.lam : 0.f;
         for (int e = tid; e < GC * GC; e += kChunkThreads) {
             const int r = e / GC, c = e - r * GC;
             if ((c >> 4) > (r >> 4)) {
@@ -808,7 +812,11 @@ __global__ __launch_bounds__(kChunkThreads) void k_gdn_chunk_bf(GdnParams p) {
     // Each of q', F and the chunk output is formed transposed (operands
     // swapped), so that a lane's four results are consecutive in the layout
     // the walk reads and go out as one store.
-    if (ci > 0) {
+    // q', F and U are formed and stored for every chunk, also where the walk
+    // does not read them (q' of chunk 0, F and U of a sequence's last chunk:
+    // their workspace slots exist), so that every chunk issues the same
+    // stores and the wait for the next chunk's loads counts them exactly
+    {
         bf16_t* Qp = reinterpret_cast<bf16_t*>(p.qp) + ((size_t)bh * p.N + ci) * GC * DK;
 #pragma unroll
         for (int x = 0; x < NWW; ++x) {
@@ -825,12 +833,15 @@ __global__ __launch_bounds__(kChunkThreads) void k_gdn_chunk_bf(GdnParams p) {
             st4(Qp + frag16(t, d0, DK), h[0], h[1], h[2], h[3]);
         }
     }
-    if (ci + 1 < p.N) {
+    {
         bf16_t* Fh = reinterpret_cast<bf16_t*>(p.fmat) + ((size_t)bh * p.N + ci) * 2 * DK * DK;
         bf16_t* Fl = Fh + DK * DK;
         const float eg = __expf(g);
         constexpr int NF = (DK / 16) * (DK / 16);
-        for (int j = wave; j < NF; j += NWV) {
+        static_assert(NF % NWV == 0, "F tiles per wave");
+#pragma unroll 1
+        for (int x = 0; x < NF / NWV; ++x) {
+            const int j = wave + NWV * x;
             const int tc = j / (DK / 16), tr = j % (DK / 16);  // F^T tile: rows d' (16 tc..), cols d
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             acc = mm_bf(WpTh + 16 * tc * P64, P64, sKt + 16 * tr * P64, P64, 0, GC, acc);
@@ -845,7 +856,10 @@ __global__ __launch_bounds__(kChunkThreads) void k_gdn_chunk_bf(GdnParams p) {
         }
         f32x4* U = reinterpret_cast<f32x4*>(p.ust + ((size_t)bh * p.N + ci) * DK * DV);
         constexpr int NS = (DK / 16) * (DV / 16);
-        for (int j = wave; j < NS; j += NWV) {
+#pragma unroll 1
+        for (int x = 0; x < (NS + NWV - 1) / NWV; ++x) {
+            const int j = wave + NWV * x;
+            if (NS % NWV != 0 && j >= NS) break;
             const int ti = j % (DK / 16), tn = j / (DK / 16);
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
             acc = mm_bf(sKt + 16 * ti * P64, P64, U0h + 16 * tn * P64, P64, 0, GC, acc);
@@ -866,7 +880,10 @@ __global__ __launch_bounds__(kChunkThreads) void k_gdn_chunk_bf(GdnParams p) {
         }
     }
     __syncthreads();
-    for (int j = wave; j < NU; j += NWV) {
+#pragma unroll
+    for (int x = 0; x < (NU + NWV - 1) / NWV; ++x) {
+        const int j = wave + NWV * x;
+        if (NU % NWV != 0 && j >= NU) break;
         const int tt = j / (DV / 16), tc = j % (DV / 16);  // O^T tile: rows c, columns t
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
         acc = mm_bf(sVt + 16 * tc * P64, P64, sYh + 16 * tt * P64, P64, 0, tri_end(tt), acc);

@@ -373,10 +373,13 @@ struct GdnWorkspace {
     size_t f_off, q_off, u_off, total;
 };
 
+// one slot per chunk, a sequence's last chunk included: the bf16 chunk kernel
+// writes q', F and U for every chunk (the walk reads them from chunk 1 on,
+// and F, U up to the second-to-last chunk), so a single chunk needs them too
 GdnWorkspace gdn_layout(long BH, int T, int dk, int dv) {
     GdnWorkspace w{};
     const long N = ((long)T + kGdnChunk - 1) / kGdnChunk;
-    if (BH == 0 || N <= 1) return w;
+    if (BH == 0 || N < 1) return w;
     w.f_off = 0;
     w.q_off = align_up(w.f_off + (size_t)BH * N * dk * dk * sizeof(float));
     w.u_off = align_up(w.q_off + (size_t)BH * N * kGdnChunk * dk * sizeof(float));
