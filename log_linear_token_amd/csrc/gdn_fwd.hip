@@ -919,24 +919,32 @@ __global__ __launch_bounds__(kChunkThreads) void k_gdn_levels_bf(GdnParams p) {
     const bool trans = wave < DK / 16, reads = wave < 4;
 
     // lambda of the coarse levels of a chunk: at most 64 * 14 values, two per
-    // thread, loaded with the chunk's other registers and stored to LDS later
+    // thread, loaded with the chunk's other registers and stored to LDS later.
+    // Every load of a chunk is issued without a branch or a select on its
+    // value (indices clamped to valid memory): a select that consumed a load
+    // would make the compiler wait for it where it is issued, and a load
+    // under a branch leaves it unsure how many memory operations follow.
+    // Entries outside the chunk or the lambda row are zeroed when stored.
     constexpr int NLR = (GC * kMaxWalkLevels + kChunkThreads - 1) / kChunkThreads;
     auto load_lam = [&](int ci, float (&lr)[NLR]) __attribute__((always_inline)) {
         const size_t r0 = (size_t)bh * p.T + (size_t)ci * GC;
         const int nv = min(GC, p.T - ci * GC);
 #pragma unroll
         for (int u = 0; u < NLR; ++u) {
-            const int e = tid + u * kChunkThreads;
-            const int r = e / nlev, l = e - r * nlev;
-            const int lev = c6 + 1 + l;
-            lr[u] = (e < GC * nlev && r < nv && lev < p.L) ? p.lam[(r0 + r) * p.L + lev] : 0.f;
+            const int e = min(tid + u * kChunkThreads, GC * nlev - 1);
+            const int r = min(e / nlev, nv - 1), l = e - (e / nlev) * nlev;
+            const int lev = min(c6 + 1 + l, p.L - 1);
+            lr[u] = p.lam[(r0 + r) * p.L + lev];
         }
     };
-    auto store_lam = [&](const float (&lr)[NLR], float* dst) __attribute__((always_inline)) {
+    auto store_lam = [&](const float (&lr)[NLR], int nv, float* dst) __attribute__((always_inline)) {
 #pragma unroll
         for (int u = 0; u < NLR; ++u) {
             const int e = tid + u * kChunkThreads;
-            if (e < GC * nlev) dst[e] = lr[u];
+            if (e < GC * nlev) {
+                const int r = e / nlev, lev = c6 + 1 + (e - r * nlev);
+                dst[e] = (r < nv && lev < p.L) ? lr[u] : 0.f;
+            }
         }
     };
     // registers of one chunk: F rows of this wave (two pieces), q' rows, U,
@@ -945,10 +953,13 @@ __global__ __launch_bounds__(kChunkThreads) void k_gdn_levels_bf(GdnParams p) {
         bf16x8 fh[NKS], fl[NKS], qf[NKS];
         f32x4 u, o;
         float lam[NLR];
+        int nv;  // valid tokens of the chunk
     };
+    // the chunk kernel leaves q', F and U for every chunk, so the loads do not
+    // depend on the chunk index; each wave loads what its role uses
     auto load = [&](int ci, Regs& R) __attribute__((always_inline)) {
         const size_t slot = (size_t)bh * N + ci;
-        if (trans && ci + 1 < N) {
+        if (trans) {
             const bf16x8* fh = reinterpret_cast<const bf16x8*>(p.fmat) + slot * 2 * DK * DK / 8;
             const bf16x8* fl = fh + DK * DK / 8;
 #pragma unroll
@@ -959,16 +970,17 @@ __global__ __launch_bounds__(kChunkThreads) void k_gdn_levels_bf(GdnParams p) {
             R.u = reinterpret_cast<const f32x4*>(p.ust + slot * DK * p.dv)[((size_t)cb * (DK / 16) + wave) * 64 + lane];
         }
         load_lam(ci, R.lam);
-        if (reads && ci > 0) {
+        R.nv = min(GC, p.T - ci * GC);
+        if (reads) {
             const bf16x8* qp = reinterpret_cast<const bf16x8*>(p.qp) + slot * GC * DK / 8;
 #pragma unroll
             for (int ks = 0; ks < NKS; ++ks) R.qf[ks] = qp[((size_t)wave * NKS + ks) * 64 + lane];
-            const int nv = min(GC, p.T - ci * GC);
             const size_t r0 = (size_t)bh * p.T + (size_t)ci * GC;
+            // rows past the chunk read its last row; the read-out stores rows < nv only
 #pragma unroll
             for (int i = 0; i < 4; ++i) {
-                const int m = 16 * wave + q4 * 4 + i;
-                R.o[i] = m < nv ? p.out[(r0 + m) * p.dv + col0 + r16] : 0.f;
+                const int m = min(16 * wave + q4 * 4 + i, R.nv - 1);
+                R.o[i] = p.out[(r0 + m) * p.dv + col0 + r16];
             }
         }
     };
@@ -976,7 +988,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_gdn_levels_bf(GdnParams p) {
     for (int e = tid; e < nlev * SLOT; e += kChunkThreads) sx[e] = 0;
     Regs cur, nxt;
     load(0, nxt);
-    store_lam(nxt.lam, slam0);
+    store_lam(nxt.lam, nxt.nv, slam0);
     __syncthreads();
 
     for (int ci = 0; ci < N; ++ci) {
@@ -1068,7 +1080,7 @@ __global__ __launch_bounds__(kChunkThreads) void k_gdn_levels_bf(GdnParams p) {
                 }
             }
         }
-        store_lam(nxt.lam, slam0 + ((ci + 1) & 1) * GC * nlev);
+        store_lam(nxt.lam, nxt.nv, slam0 + ((ci + 1) & 1) * GC * nlev);
         __syncthreads();
     }
 }
