@@ -1115,11 +1115,16 @@ hipError_t launch_bwd_typed(const BwdParams& p, hipStream_t stream) {
     }
     // R(j): one walk over the query chunks where it applies (LOGLIN_BWD_RSTATE=blocks
     // keeps the block-per-R(j) kernel below), else one block per R(j)
-    bool walked = false;
+    // dk and dv: one reverse walk per segment where it applies (it builds the
+    // R(j) inside a segment itself; LOGLIN_BWD_DKV=chunks keeps the
+    // block-per-chunk kernel below)
+    bool walked = false, kvwalk = false;
     if constexpr (sizeof(E) == 2 && C == 64) {
         const char* mode = getenv("LOGLIN_BWD_RSTATE");
+        const char* kvmode = getenv("LOGLIN_BWD_DKV");
         if (p.N > 1 && !(mode && strcmp(mode, "blocks") == 0) && bwd_rwalk_applies(p)) {
-            err = launch_bwd_rwalk(p, stream);
+            kvwalk = !(kvmode && strcmp(kvmode, "chunks") == 0) && bwd_kvwalk_applies(p);
+            err = launch_bwd_rwalk(p, kvwalk, stream);
             if (err != hipSuccess) return err;
             walked = true;
         }
@@ -1133,7 +1138,10 @@ hipError_t launch_bwd_typed(const BwdParams& p, hipStream_t stream) {
         hipLaunchKernelGGL((k_bwd_rstate<E, C, DM, FDK, FDV>), dim3(p.BH * (p.N - 1)), dim3(256), s2, stream,
                            p2);
     }
-    if (f3) {
+    if (kvwalk) {
+        err = launch_bwd_kvwalk(p, stream);
+        if (err != hipSuccess) return err;
+    } else if (f3) {
         err = set_smem(&k_bwd_dkv<E, C, DM, FDK, FDV>, s3);
         if (err != hipSuccess) return err;
         hipLaunchKernelGGL((k_bwd_dkv<E, C, DM, FDK, FDV>), dim3(nblk), dim3(C / 16 * 64), s3, stream, p3);

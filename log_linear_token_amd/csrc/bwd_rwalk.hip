@@ -65,6 +65,8 @@ struct RwalkArgs {
     int m;          // chunks per segment = 2^m
     int nseg;       // segments per (batch*head)
     int ntop;       // levels p >= m that exist (nlev - m, or 0)
+    int pmin;       // levels p < pmin are not built (0, or m when the dk / dv
+                    // walk builds the levels inside a segment itself)
     int lam_dma;    // lambda rows of a whole chunk are 16-byte aligned
     int a_dma;      // a of a whole chunk is 16-byte aligned
     float* part;    // [BH][nseg][ntop][dk][dv] parts of the blocks of levels >= m
@@ -99,6 +101,14 @@ __global__ __launch_bounds__(kRwWaves * 64, 1) void k_bwd_rwalk(BwdParams p, Rwa
     const int blk = xcd_block(blockIdx.x, gridDim.x);
     const int seg = blk % w.nseg;
     const int bh = blk / w.nseg;
+    // levels pmin <= p < nlev only: a segment none of whose chunks has such a
+    // bit set (for p >= m: the segment index has none) has nothing to build
+    {
+        const int i0s = seg << w.m;
+        const int top = (1 << p.nlev) - 1;
+        const int low = w.pmin < w.m ? ((1 << w.m) - 1) & ~((1 << w.pmin) - 1) : 0;
+        if (((i0s & top) >> w.pmin) == 0 && low == 0) return;
+    }
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int lane = threadIdx.x & 63, m16 = lane & 15, g = lane >> 4;
     const int c0 = 16 * (wave & 3);           // this wave's d_v columns
@@ -184,7 +194,7 @@ __global__ __launch_bounds__(kRwWaves * 64, 1) void k_bwd_rwalk(BwdParams p, Rwa
     auto flush = [&](int i) __attribute__((always_inline)) {
 #pragma unroll
         for (int pl = 0; pl < NSLOT; ++pl) {
-            if (pl < w.m && pl < nlev && ((i >> pl) & 1)) {
+            if (pl >= w.pmin && pl < w.m && pl < nlev && ((i >> pl) & 1)) {
                 const int j = (i >> pl) << pl;
                 if (i + 1 == min(j + (1 << pl), N)) {
                     bf16_t* dst = rst + ((size_t)bh * N + j) * DK * DV;
@@ -218,7 +228,7 @@ __global__ __launch_bounds__(kRwWaves * 64, 1) void k_bwd_rwalk(BwdParams p, Rwa
             // lambda_t^(log2 C + pl + 1) e^(A_t - A(end of chunk j - 1))
             const int pl = wave;
             const float x = wave_inclusive_sum(ac[lane]);  // A_t - A(end of chunk i - 1)
-            if (pl < NSLOT && pl < nlev && ((i >> pl) & 1)) {
+            if (pl < NSLOT && pl >= w.pmin && pl < nlev && ((i >> pl) & 1)) {
                 const int j = (i >> pl) << pl;
                 const double cj = pl < w.m ? sCum[j - i0] : sTop[pl];
                 const float base = (float)(sCum[i - i0] - cj);
@@ -237,7 +247,7 @@ __global__ __launch_bounds__(kRwWaves * 64, 1) void k_bwd_rwalk(BwdParams p, Rwa
             for (int rb = 0; rb < NRBW; ++rb) bq[rb] = ld_tr8<DK>(Qc, 32 * ks, d0 + 16 * rb);
 #pragma unroll
             for (int pl = 0; pl < NSLOT; ++pl) {
-                if (pl < nlev && ((i >> pl) & 1)) {
+                if (pl >= w.pmin && pl < nlev && ((i >> pl) & 1)) {
                     const float4 w0 = *reinterpret_cast<const float4*>(&sW[pl][32 * ks + 8 * g]);
                     const float4 w1 = *reinterpret_cast<const float4*>(&sW[pl][32 * ks + 8 * g + 4]);
                     const bf16x8 sc = scale8(ao, w0, w1);
@@ -304,6 +314,397 @@ __global__ __launch_bounds__(256) void k_bwd_rcombine(BwdParams p, RwalkArgs w) 
     }
 }
 
+// ---------------------------------------------------------------------------
+// dk, dv and k_s . dk_s in one reverse walk per (batch*head, segment of 2^m
+// chunks) (bf16, 64-token chunks, d_k = 128, d_v = 64).
+//
+// Outside its own chunk i, key s meets the queries of the block of 2^p chunks
+// starting at j_p = ((i >> p) | 1) << p for each clear bit p of i, with the
+// block state R(j_p) of the R(j) walk above.  The key's side of the mask is a
+// decay alone, e^(-A_s), so the blocks combine before the products:
+//     dk_s += e^(A(end of i) - A_s) R~ v_s,   dv_s += e^(A(end of i) - A_s) R~^T k_s,
+//     R~(i) = sum over the clear bits p of e^(A(end of j_p - 1) - A(end of i)) R(j_p),
+// one pair of products per chunk whatever the number of blocks.  Walking the
+// segment's chunks from its last to its first, a block of level p < m inside
+// the segment is complete exactly when the walk reaches the 2^p chunks that
+// read it (they come right before it), so these blocks accumulate in fp32
+// registers as the walk passes their chunks: chunk i adds its queries to the
+// level-p block for each set bit p of i, the accumulator cleared when the walk
+// enters the next block of that level.  The blocks of levels p >= m lie in
+// later segments; their R(j) come from the R(j) walk, combined once at the
+// start with the weights e^(A(end of j - 1) - A(end of the segment)).
+// The chunk's own causal block adds (dP (.) M)^T Q to dk and ((Q K^T) (.) M)^T dO
+// to dv, with dP = dO v^T and M = lambda_t^(level) e^(A_t - A_s).
+//
+// Eight waves.  Wave w owns d_k columns 16 w .. 16 w + 15 of every block state
+// and of dk (all 64 keys), and dv columns 16 (w % 4) for the keys 32 (w / 4)
+// .. + 31.  The accumulated states are transposed (rows d_v, the dO operand
+// read with free column quads) so that each lane's fp32 entries are the
+// natural 8-wide d_v groups of the R~ operand of the dk product; the dv product
+// reads R~ back from LDS by transpose reads.  Chunks arrive by LDS-DMA one
+// ahead of use (two buffers); the results of a chunk are stored after the
+// next chunk's barrier, before that chunk's successor is requested.
+
+constexpr int kKvWaves = 8;
+constexpr int kKvMaxL = 24;   // lambda row length staged per token
+
+template <int DK, int DV>
+__global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_kvwalk(BwdParams p, RwalkArgs w) {
+    static_assert(DK == 16 * kKvWaves && DV == 64, "head dims of this kernel");
+    constexpr int MM = kRwMaxM;  // levels kept in registers: p < m <= MM
+    static_assert(MM + 3 <= kKvWaves, "one wave per level weight");
+    __shared__ __align__(16) bf16_t sQ[2][TC * DK];
+    __shared__ __align__(16) bf16_t sK[2][TC * DK];
+    __shared__ __align__(16) bf16_t sV[2][TC * DV];
+    __shared__ __align__(16) bf16_t sO[2][TC * DV];
+    __shared__ __align__(16) float sL[2][TC * kKvMaxL];
+    __shared__ __align__(16) float sa[2][TC];
+    __shared__ __align__(16) bf16_t sZ[TC * TC];   // (dP (.) M)^T: [key][query]
+    __shared__ __align__(16) bf16_t sP[TC * TC];   // ((Q K^T) (.) M)^T
+    __shared__ __align__(16) bf16_t sR[DK * DV];   // R~ of the chunk: [d_k][d_v]
+    __shared__ __align__(16) float sW[MM][TC];     // query weights of the levels the chunk feeds
+    __shared__ __align__(16) float sE[TC];         // e^(A(end of chunk) - A_s)
+    __shared__ __align__(16) float sAw[kKvWaves][TC];  // per wave: A_t - A(end of the chunk before)
+    __shared__ __align__(16) float sDa[kKvWaves][TC];  // per wave: its part of k_s . dk_s
+    __shared__ double sCum[(1 << kRwMaxM) + 1];
+
+    const int blk = xcd_block(blockIdx.x, gridDim.x);
+    const int seg = blk % w.nseg;
+    const int bh = blk / w.nseg;
+    const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+    const int lane = threadIdx.x & 63, n16 = lane & 15, g = lane >> 4;
+    const int N = p.N, L = p.L, T = p.T, nlev = p.nlev;
+    const int i0 = seg << w.m;
+    const int ntl = min(1 << w.m, N - i0);
+    const int mm = min(w.m, nlev);
+    const size_t row0 = (size_t)bh * T;
+    const double* cum = p.cum + (size_t)bh * N;
+    const bf16_t* q = reinterpret_cast<const bf16_t*>(p.q);
+    const bf16_t* k = reinterpret_cast<const bf16_t*>(p.k);
+    const bf16_t* v = reinterpret_cast<const bf16_t*>(p.v);
+    const bf16_t* dout = reinterpret_cast<const bf16_t*>(p.dout);
+    const bf16_t* rst = reinterpret_cast<const bf16_t*>(p.rst16);
+
+    typedef TileCopy<DK, kKvWaves> CK;
+    typedef TileCopy<DV, kKvWaves> CV;
+    CK ck;
+    CV cv;
+    ck.init(DK, 0, wave);
+    cv.init(DV, 0, wave);
+    // chunk il of the segment into buffer b; rows past T: q, k, v and dO
+    // repeat the last row (their weights are zero or their outputs unused),
+    // lambda and a are zero
+    auto issue = [&](int il, int b) __attribute__((always_inline)) {
+        const int t0 = (i0 + il) * TC;
+        const int nvalid = min(TC, T - t0);
+        const size_t r = row0 + t0;
+        if (nvalid == TC) {
+            ck.issue(q + r * DK, sQ[b], wave);
+            ck.issue(k + r * DK, sK[b], wave);
+            cv.issue(v + r * DV, sV[b], wave);
+            cv.issue(dout + r * DV, sO[b], wave);
+        } else {
+            dma_tile<DK, kKvWaves>(q + r * DK, DK, 0, nvalid, sQ[b], wave);
+            dma_tile<DK, kKvWaves>(k + r * DK, DK, 0, nvalid, sK[b], wave);
+            dma_tile<DV, kKvWaves>(v + r * DV, DV, 0, nvalid, sV[b], wave);
+            dma_tile<DV, kKvWaves>(dout + r * DV, DV, 0, nvalid, sO[b], wave);
+        }
+        float* Ld = sL[b];
+        if (nvalid == TC && w.lam_dma) {
+            const int nch = 16 * L;  // 64 rows x L floats in 16-byte pieces
+            for (int u = wave; u * 64 < nch; u += kKvWaves)
+                if (u * 64 + lane < nch) dma16o(p.lam + r * L, 16u * (u * 64 + lane), Ld + u * 256);
+        } else {
+            const int nel = nvalid * L;
+            for (int u = wave; u * 64 < TC * L; u += kKvWaves) {
+                const int x = u * 64 + lane;
+                if (x < nel) dma4(p.lam + r * L + x, Ld + u * 64);
+                else if (x < TC * L) Ld[x] = 0.f;
+            }
+        }
+        if (wave == kKvWaves - 1) {
+            if (nvalid == TC && w.a_dma) {
+                if (lane < TC / 4) dma16o(p.a + r, 16u * lane, sa[b]);
+            } else if (lane < nvalid) {
+                dma4(p.a + r + lane, sa[b]);
+            } else {
+                sa[b][lane] = 0.f;
+            }
+        }
+    };
+
+    // A at the end of chunks i0 - 1 .. i0 + ntl - 1 (sCum[x]: chunk i0 - 1 + x)
+    for (int x = threadIdx.x; x <= ntl; x += kKvWaves * 64)
+        sCum[x] = i0 + x >= 1 ? cum[i0 - 1 + x] : 0.0;
+    // the blocks of levels >= m after the segment, combined at its end: this
+    // lane's share, d_k row 16 w + n16, d_v 32 ks + 8 g + (0..7)
+    // (only a full segment that is not the last has such blocks; A at the end
+    // of the sequence's last chunk is never read)
+    f32x4 nc[2][2];
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) nc[ks][0] = nc[ks][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    bool coarse = false;
+    for (int pl = w.m; pl < nlev; ++pl) {
+        const int j = ((i0 >> pl) | 1) << pl;
+        if (((i0 >> pl) & 1) || j >= N) continue;
+        coarse = true;
+        const float wt = __expf((float)(cum[j - 1] - cum[i0 + ntl - 1]));
+        const bf16_t* R = rst + ((size_t)bh * N + j) * DK * DV + (size_t)(16 * wave + n16) * DV + 8 * g;
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) {
+            const bf16x8 x = *reinterpret_cast<const bf16x8*>(R + 32 * ks);
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                nc[ks][0][e] += wt * (float)x[e];
+                nc[ks][1][e] += wt * (float)x[4 + e];
+            }
+        }
+    }
+
+    f32x4 acc[MM][2][2];
+#pragma unroll
+    for (int pl = 0; pl < MM; ++pl)
+#pragma unroll
+        for (int ks = 0; ks < 2; ++ks) acc[pl][ks][0] = acc[pl][ks][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+    // results of the chunk last computed, stored after the next barrier
+    f32x4 dk4[4], dv2[2];
+    const int vb = wave & 3;          // this wave's d_v block
+    const int kb0 = 2 * (wave >> 2);  // and its first key block for dv
+
+    auto store = [&](int il, int zv) __attribute__((always_inline)) {
+        const int n16 = (lane & 15) + zv, g = (lane >> 4) + zv;
+        const int t0 = (i0 + il) * TC;
+        const int nvalid = min(TC, T - t0);
+        const size_t r = row0 + t0;
+        // uniform row base plus a 32-bit lane offset
+        float* gk = p.gk + r * DK;
+        float* gv = p.gv + r * DV;
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            const int s = 16 * kb + n16;
+            if (s < nvalid) *reinterpret_cast<f32x4*>(gk + (uint32_t)(s * DK + 16 * wave + 4 * g)) = dk4[kb];
+        }
+#pragma unroll
+        for (int jb = 0; jb < 2; ++jb) {
+            const int s = 16 * (kb0 + jb) + n16;
+            if (s < nvalid) *reinterpret_cast<f32x4*>(gv + (uint32_t)(s * DV + 16 * vb + 4 * g)) = dv2[jb];
+        }
+        if (wave == kKvWaves - 1) {
+            float d = 0.f;
+#pragma unroll
+            for (int u = 0; u < kKvWaves; ++u) d += sDa[u][lane];
+            if (lane < nvalid) p.dA2[r + lane] = d;
+        }
+    };
+
+    issue(ntl - 1, (ntl - 1) & 1);
+    for (int il = ntl - 1; il >= 0; --il) {
+        const int cur = il & 1;
+        wait_vm<0>();
+        __syncthreads();  // chunk il has landed; every wave is done with chunk il + 1
+        // the lane indices through an opaque zero: the per-lane address
+        // arithmetic of the body is then redone in place each chunk instead
+        // of being hoisted out of the loop, where it would be held (or
+        // spilled) beside the level accumulators
+        int zv;
+        asm volatile("v_mov_b32 %0, 0" : "=v"(zv));
+        const int n16 = (lane & 15) + zv, g = (lane >> 4) + zv;
+        if (il + 1 < ntl) store(il + 1, zv);
+        if (il > 0) issue(il - 1, cur ^ 1);
+        const bf16_t* Qs = sQ[cur];
+        const bf16_t* Ks = sK[cur];
+        const bf16_t* Vs = sV[cur];
+        const bf16_t* Os = sO[cur];
+        const float* Ls = sL[cur];
+        const int nvalid = min(TC, T - (i0 + il) * TC);
+
+        // this wave's copy of the chunk's decay: x_t = A_t - A(end of chunk il - 1)
+        const float x = wave_inclusive_sum(sa[cur][lane]);
+        const float xend = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+        sAw[wave][lane] = x;
+        // shared weights: e^(A(end) - A_s) (wave 2) and, wave 3 + p, the weights
+        // of the queries of this chunk in the level-p block it belongs to
+        if (wave == 2) {
+            sE[lane] = __expf(xend - x);
+        } else if (wave >= 3) {
+            const int pl = wave - 3;
+            if (pl < mm && ((il >> pl) & 1)) {
+                const int jb = (il >> pl) << pl;
+                const float base = (float)(sCum[il] - sCum[jb]);
+                const float lam = Ls[lane * L + kRwLogC + pl + 1];
+                sW[pl][lane] = lane < nvalid ? lam * __expf(x + base) : 0.f;
+            }
+        }
+
+        // the causal block: 16 x 16 blocks (query block rb >= key block sb),
+        // one or two per wave; lane (n16, g) holds query 16 rb + 4g + i, key 16 sb + n16
+        auto score = [&](int tau) __attribute__((always_inline)) {
+            const int rb = tau < 1 ? 0 : tau < 3 ? 1 : tau < 6 ? 2 : 3;
+            const int sb = tau - rb * (rb + 1) / 2;
+            bf16x8 of[2], vf[2], qf[4], kf[4];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                of[ks] = ld8<DV>(Os, 16 * rb + n16, 32 * ks + 8 * g);
+                vf[ks] = ld8<DV>(Vs, 16 * sb + n16, 32 * ks + 8 * g);
+            }
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) {
+                qf[ks] = ld8<DK>(Qs, 16 * rb + n16, 32 * ks + 8 * g);
+                kf[ks] = ld8<DK>(Ks, 16 * sb + n16, 32 * ks + 8 * g);
+            }
+            const int s = 16 * sb + n16;
+            const float As = sAw[wave][s];
+            const float4 At = *reinterpret_cast<const float4*>(&sAw[wave][16 * rb + 4 * g]);
+            __builtin_amdgcn_sched_barrier(0);
+            f32x4 dp = {0.f, 0.f, 0.f, 0.f}, sc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) dp = mma(of[ks], vf[ks], dp);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) sc = mma(qf[ks], kf[ks], sc);
+            const float Atv[4] = {At.x, At.y, At.z, At.w};
+            float z[4], pp[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const int t = 16 * rb + 4 * g + i;
+                const int lvl = sb < rb ? 5 + (31 - __builtin_clz(rb ^ sb)) : fenwick_level(t, s);
+                const float wt = Ls[t * L + lvl] * __expf(Atv[i] - As);
+                const bool keep = sb < rb || t >= s;
+                z[i] = keep ? dp[i] * wt : 0.f;
+                pp[i] = keep ? sc[i] * wt : 0.f;
+            }
+            *reinterpret_cast<bf16x4*>(sZ + toff<TC>(s, 16 * rb + 4 * g)) = pack4(z[0], z[1], z[2], z[3]);
+            *reinterpret_cast<bf16x4*>(sP + toff<TC>(s, 16 * rb + 4 * g)) = pack4(pp[0], pp[1], pp[2], pp[3]);
+            if (sb == rb && (rb & 1) == 0) {
+                // the block past the diagonal (keys of block rb + 1, queries of
+                // block rb), which the 32-query products pair with this one
+                *reinterpret_cast<bf16x4*>(sZ + toff<TC>(s + 16, 16 * rb + 4 * g)) = bf16x4{};
+                *reinterpret_cast<bf16x4*>(sP + toff<TC>(s + 16, 16 * rb + 4 * g)) = bf16x4{};
+            }
+        };
+        score(wave);
+        if (wave < 2) score(wave + 8);
+
+        // R~ share of this wave (d_k row 16 w + n16, d_v 32 ks + 8 g + 0..7):
+        // operand of the dk product in registers, and to LDS for the dv product
+        bf16x8 rf[2];
+        {
+            const float wc = coarse ? __expf((float)(sCum[ntl] - sCum[il + 1])) : 0.f;
+            f32x4 r[2][2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) r[ks][h] = wc * nc[ks][h];
+#pragma unroll
+            for (int pl = 0; pl < MM; ++pl) {
+                const int jr = ((il >> pl) | 1) << pl;
+                if (pl < mm && !((il >> pl) & 1) && jr < ntl) {
+                    const float c = __expf((float)(sCum[jr] - sCum[il + 1]));
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) r[ks][h] += c * acc[pl][ks][h];
+                }
+            }
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) {
+                rf[ks] = cvt8(r[ks][0], r[ks][1]);
+                *reinterpret_cast<bf16x8*>(sR + toff<DV>(16 * wave + n16, 32 * ks + 8 * g)) = rf[ks];
+            }
+        }
+        __syncthreads();  // the chunk's weights, (dP (.) M)^T, ((Q K^T) (.) M)^T and R~
+
+        // dk^T (rows d_k 16 w + 4g + i, column key 16 kb + n16): the causal
+        // block, then e^(A(end) - A_s) R~ v_s
+        bf16x8 qT[2];
+#pragma unroll
+        for (int sp = 0; sp < 2; ++sp) qT[sp] = ld_tr8<DK>(Qs, 32 * sp + zv, 16 * wave);
+#pragma unroll
+        for (int kb = 0; kb < 4; ++kb) {
+            f32x4 a = {0.f, 0.f, 0.f, 0.f}, t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int sp = 0; sp < 2; ++sp)
+                if (kb < 2 || sp == 1) a = mma(qT[sp], ld8<TC>(sZ, 16 * kb + n16, 32 * sp + 8 * g), a);
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks) t = mma(rf[ks], ld8<DV>(Vs, 16 * kb + n16, 32 * ks + 8 * g), t);
+            const float e = sE[16 * kb + n16];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) dk4[kb][i] = a[i] + e * t[i];
+            // one key block's operands in registers at a time
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        // dv^T (rows d_v 16 vb + 4g + i, column key 16 kb + n16) for two key blocks
+        {
+            bf16x8 oT[2], rT[4];
+#pragma unroll
+            for (int sp = 0; sp < 2; ++sp) oT[sp] = ld_tr8<DV>(Os, 32 * sp + zv, 16 * vb);
+#pragma unroll
+            for (int ks = 0; ks < 4; ++ks) rT[ks] = ld_tr8<DV>(sR, 32 * ks + zv, 16 * vb);
+#pragma unroll
+            for (int jb = 0; jb < 2; ++jb) {
+                const int kb = kb0 + jb;
+                f32x4 a = {0.f, 0.f, 0.f, 0.f}, t = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int sp = 0; sp < 2; ++sp)
+                    if (kb < 2 || sp == 1) a = mma(oT[sp], ld8<TC>(sP, 16 * kb + n16, 32 * sp + 8 * g), a);
+#pragma unroll
+                for (int ks = 0; ks < 4; ++ks) t = mma(rT[ks], ld8<DK>(Ks, 16 * kb + n16, 32 * ks + 8 * g), t);
+                const float e = sE[16 * kb + n16];
+#pragma unroll
+                for (int i = 0; i < 4; ++i) dv2[jb][i] = a[i] + e * t[i];
+                __builtin_amdgcn_sched_barrier(0);
+            }
+        }
+        // this wave's part of k_s . dk_s (its 16 d_k columns), summed over the
+        // lane rows: lane 16 g + n16 gets key 16 g + n16
+        {
+            float xk[4];
+#pragma unroll
+            for (int kb = 0; kb < 4; ++kb) {
+                const bf16x4 kk = ld4<DK>(Ks, 16 * kb + n16, 16 * wave + 4 * g);
+                xk[kb] = (float)kk[0] * dk4[kb][0] + (float)kk[1] * dk4[kb][1] +
+                         (float)kk[2] * dk4[kb][2] + (float)kk[3] * dk4[kb][3];
+            }
+            sDa[wave][lane] = sum_rows4_x4(xk[0], xk[1], xk[2], xk[3]);
+        }
+
+        // the chunk's queries into the blocks it belongs to (set bits p < m):
+        // R^T[d_v][d_k] += dO^T diag(weights) Q, d_v rows in column quads
+#pragma unroll
+        for (int pl = 0; pl < MM; ++pl) {
+            if (pl < mm && ((il >> pl) & 1) && (((il + 1) & ((2 << pl) - 1)) == 0)) {
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks) acc[pl][ks][0] = acc[pl][ks][1] = f32x4{0.f, 0.f, 0.f, 0.f};
+            }
+        }
+#pragma unroll
+        for (int sp = 0; sp < 2; ++sp) {
+            bf16x8 oq[2][2];
+#pragma unroll
+            for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                for (int h = 0; h < 2; ++h) oq[ks][h] = ld_tr8_q<DV>(Os, 32 * sp + zv, 32 * ks + 4 * h);
+#pragma unroll
+            for (int pl = 0; pl < MM; ++pl) {
+                if (pl < mm && ((il >> pl) & 1)) {
+                    const float4 w0 = *reinterpret_cast<const float4*>(&sW[pl][32 * sp + 8 * g]);
+                    const float4 w1 = *reinterpret_cast<const float4*>(&sW[pl][32 * sp + 8 * g + 4]);
+                    const bf16x8 bs = scale8(qT[sp], w0, w1);
+#pragma unroll
+                    for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                        for (int h = 0; h < 2; ++h) acc[pl][ks][h] = mma(oq[ks][h], bs, acc[pl][ks][h]);
+                }
+            }
+        }
+    }
+    __syncthreads();  // the last chunk's k . dk parts
+    store(0, 0);
+}
+
+bool kvwalk_applies(const BwdParams& p, const RwalkArgs& w) {
+    return p.dk == 16 * kKvWaves && p.dv == 64 && p.L <= kKvMaxL && w.m <= kRwMaxM;
+}
+
 template <int DK>
 hipError_t launch_rwalk_dk(const BwdParams& p, const RwalkArgs& w, hipStream_t stream) {
     if (p.nlev <= 7)
@@ -353,10 +754,23 @@ bool bwd_rwalk_applies(const BwdParams& p) {
     return rwalk_plan(p, w);
 }
 
-hipError_t launch_bwd_rwalk(const BwdParams& p, hipStream_t stream) {
+bool bwd_kvwalk_applies(const BwdParams& p) {
+    RwalkArgs w{};
+    return rwalk_plan(p, w) && kvwalk_applies(p, w);
+}
+
+hipError_t launch_bwd_rwalk(const BwdParams& p, bool coarse_only, hipStream_t stream) {
     RwalkArgs w{};
     if (!rwalk_plan(p, w)) return hipErrorInvalidValue;
+    w.pmin = coarse_only ? w.m : 0;
     return p.dk == 128 ? launch_rwalk_dk<128>(p, w, stream) : launch_rwalk_dk<64>(p, w, stream);
+}
+
+hipError_t launch_bwd_kvwalk(const BwdParams& p, hipStream_t stream) {
+    RwalkArgs w{};
+    if (!rwalk_plan(p, w) || !kvwalk_applies(p, w)) return hipErrorInvalidValue;
+    hipLaunchKernelGGL((k_bwd_kvwalk<128, 64>), dim3(p.BH * w.nseg), dim3(kKvWaves * 64), 0, stream, p, w);
+    return hipGetLastError();
 }
 
 }  // namespace loglin

@@ -162,7 +162,13 @@ hipError_t launch_bwd_chunk_cum(const BwdParams& p, hipStream_t stream);
 // levels past lu zero), and dA1_t = q_t . dq_t, the sum of their parts dqd ([ndvb][BH][T])
 hipError_t launch_bwd_dlam_sum(const BwdParams& p, const float* dlp, const float* dqd, int ndvb,
                                int lu, hipStream_t stream);
-hipError_t launch_bwd_rwalk(const BwdParams& p, hipStream_t stream);
+// coarse_only: only the blocks of levels >= m (those spanning segments), for
+// the dk / dv walk, which builds the levels inside a segment itself
+hipError_t launch_bwd_rwalk(const BwdParams& p, bool coarse_only, hipStream_t stream);
+// dk, dv and k . dk in one reverse walk per segment (bf16, C = 64, d_k = 128,
+// d_v = 64; after launch_bwd_rwalk with coarse_only): whether it applies, and the launch
+bool bwd_kvwalk_applies(const BwdParams& p);
+hipError_t launch_bwd_kvwalk(const BwdParams& p, hipStream_t stream);
 
 // Fenwick level states after the T tokens of a prefill (the state a decode
 // step at position T reads)

@@ -174,3 +174,22 @@ def test_bwd_dq_paths(monkeypatch, mode, B, H, T, dk, C):
         monkeypatch.delenv("LOGLIN_BWD_DQ", raising=False)
     banner(f"bwd dq {mode} B={B} H={H} T={T} dk={dk} C={C}")
     _check(B, H, T, dk, 64, C, torch.bfloat16, seed=T + dk, mu=-3.0)
+
+
+@pytest.mark.parametrize("mode", ["walk", "chunks"])
+@pytest.mark.parametrize("B,H,T,mu", [(1, 1, 100, -1.0), (2, 1, 777, -3.0), (1, 2, 2112, -8.0),
+                                      (1, 1, 3072, -3.0), (1, 1, 4100, -1.0), (1, 1, 8192, -8.0)])
+def test_bwd_dkv_paths(monkeypatch, mode, B, H, T, mu):
+    """dk and dv by the reverse walk over each segment's chunks (block states
+    of the levels inside a segment built in registers, the blocks of every
+    clear bit combined before the products, the levels spanning segments
+    from the R(j) walk) and by one block per chunk: both give the oracle's
+    gradients, over two chunks, ragged tails, odd chunk counts and many
+    coarse levels, under weak decay too (the full 8K workload test runs
+    whole 32-chunk segments)."""
+    if mode == "chunks":
+        monkeypatch.setenv("LOGLIN_BWD_DKV", "chunks")
+    else:
+        monkeypatch.delenv("LOGLIN_BWD_DKV", raising=False)
+    banner(f"bwd dk/dv {mode} B={B} H={H} T={T} mu={mu}")
+    _check(B, H, T, 128, 64, 64, torch.bfloat16, seed=T + 1, mu=mu)
