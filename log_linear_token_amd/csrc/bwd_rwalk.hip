@@ -365,8 +365,13 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_kvwalk(BwdParams p, Rw
     __shared__ __align__(16) float sW[MM][TC];     // query weights of the levels the chunk feeds
     __shared__ __align__(16) float sE[TC];         // e^(A(end of chunk) - A_s)
     __shared__ __align__(16) float sAw[kKvWaves][TC];  // per wave: A_t - A(end of the chunk before)
-    __shared__ __align__(16) float sDa[kKvWaves][TC];  // per wave: its part of k_s . dk_s
-    __shared__ double sCum[(1 << kRwMaxM) + 1];
+    __shared__ __align__(16) float sDa[2][kKvWaves][TC];  // per wave: its part of k_s . dk_s
+    // per chunk of the segment: the weights of the blocks that make R~ (level
+    // p, and the blocks after the segment at MM; zero where not used), and
+    // the offsets A(end of chunk - 1) - A(end of block start - 1) of the query
+    // weights of the blocks the chunk feeds
+    __shared__ float sCw[1 << kRwMaxM][MM + 1];
+    __shared__ float sBw[1 << kRwMaxM][MM];
 
     const int blk = xcd_block(blockIdx.x, gridDim.x);
     const int seg = blk % w.nseg;
@@ -391,51 +396,55 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_kvwalk(BwdParams p, Rw
     CV cv;
     ck.init(DK, 0, wave);
     cv.init(DV, 0, wave);
-    // chunk il of the segment into buffer b; rows past T: q, k, v and dO
-    // repeat the last row (their weights are zero or their outputs unused),
-    // lambda and a are zero
-    auto issue = [&](int il, int b) __attribute__((always_inline)) {
+    // chunk il of the segment into buffer b, in four parts (q; k; v and dO;
+    // lambda and a) that the body issues between its computations, so that
+    // the copies of the eight waves do not queue up at once; rows past T: q,
+    // k, v and dO repeat the last row (their weights are zero or their
+    // outputs unused), lambda and a are zero
+    auto issue = [&](int il, int b, int part) __attribute__((always_inline)) {
         const int t0 = (i0 + il) * TC;
         const int nvalid = min(TC, T - t0);
         const size_t r = row0 + t0;
-        if (nvalid == TC) {
-            ck.issue(q + r * DK, sQ[b], wave);
-            ck.issue(k + r * DK, sK[b], wave);
-            cv.issue(v + r * DV, sV[b], wave);
-            cv.issue(dout + r * DV, sO[b], wave);
-        } else {
-            dma_tile<DK, kKvWaves>(q + r * DK, DK, 0, nvalid, sQ[b], wave);
-            dma_tile<DK, kKvWaves>(k + r * DK, DK, 0, nvalid, sK[b], wave);
-            dma_tile<DV, kKvWaves>(v + r * DV, DV, 0, nvalid, sV[b], wave);
-            dma_tile<DV, kKvWaves>(dout + r * DV, DV, 0, nvalid, sO[b], wave);
-        }
-        float* Ld = sL[b];
-        if (nvalid == TC && w.lam_dma) {
-            const int nch = 16 * L;  // 64 rows x L floats in 16-byte pieces
-            for (int u = wave; u * 64 < nch; u += kKvWaves)
-                if (u * 64 + lane < nch) dma16o(p.lam + r * L, 16u * (u * 64 + lane), Ld + u * 256);
-        } else {
-            const int nel = nvalid * L;
-            for (int u = wave; u * 64 < TC * L; u += kKvWaves) {
-                const int x = u * 64 + lane;
-                if (x < nel) dma4(p.lam + r * L + x, Ld + u * 64);
-                else if (x < TC * L) Ld[x] = 0.f;
-            }
-        }
-        if (wave == kKvWaves - 1) {
-            if (nvalid == TC && w.a_dma) {
-                if (lane < TC / 4) dma16o(p.a + r, 16u * lane, sa[b]);
-            } else if (lane < nvalid) {
-                dma4(p.a + r + lane, sa[b]);
+        if (part == 0) {
+            if (nvalid == TC) ck.issue(q + r * DK, sQ[b], wave);
+            else dma_tile<DK, kKvWaves>(q + r * DK, DK, 0, nvalid, sQ[b], wave);
+        } else if (part == 1) {
+            if (nvalid == TC) ck.issue(k + r * DK, sK[b], wave);
+            else dma_tile<DK, kKvWaves>(k + r * DK, DK, 0, nvalid, sK[b], wave);
+        } else if (part == 2) {
+            if (nvalid == TC) {
+                cv.issue(v + r * DV, sV[b], wave);
+                cv.issue(dout + r * DV, sO[b], wave);
             } else {
-                sa[b][lane] = 0.f;
+                dma_tile<DV, kKvWaves>(v + r * DV, DV, 0, nvalid, sV[b], wave);
+                dma_tile<DV, kKvWaves>(dout + r * DV, DV, 0, nvalid, sO[b], wave);
+            }
+        } else {
+            float* Ld = sL[b];
+            if (nvalid == TC && w.lam_dma) {
+                const int nch = 16 * L;  // 64 rows x L floats in 16-byte pieces
+                for (int u = wave; u * 64 < nch; u += kKvWaves)
+                    if (u * 64 + lane < nch) dma16o(p.lam + r * L, 16u * (u * 64 + lane), Ld + u * 256);
+            } else {
+                const int nel = nvalid * L;
+                for (int u = wave; u * 64 < TC * L; u += kKvWaves) {
+                    const int x = u * 64 + lane;
+                    if (x < nel) dma4(p.lam + r * L + x, Ld + u * 64);
+                    else if (x < TC * L) Ld[x] = 0.f;
+                }
+            }
+            if (wave == kKvWaves - 1) {
+                if (nvalid == TC && w.a_dma) {
+                    if (lane < TC / 4) dma16o(p.a + r, 16u * lane, sa[b]);
+                } else if (lane < nvalid) {
+                    dma4(p.a + r + lane, sa[b]);
+                } else {
+                    sa[b][lane] = 0.f;
+                }
             }
         }
     };
 
-    // A at the end of chunks i0 - 1 .. i0 + ntl - 1 (sCum[x]: chunk i0 - 1 + x)
-    for (int x = threadIdx.x; x <= ntl; x += kKvWaves * 64)
-        sCum[x] = i0 + x >= 1 ? cum[i0 - 1 + x] : 0.0;
     // the blocks of levels >= m after the segment, combined at its end: this
     // lane's share, d_k row 16 w + n16, d_v 32 ks + 8 g + (0..7)
     // (only a full segment that is not the last has such blocks; A at the end
@@ -461,6 +470,26 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_kvwalk(BwdParams p, Rw
         }
     }
 
+    for (int x = threadIdx.x; x < ntl * (MM + 1); x += kKvWaves * 64) {
+        const int il = x / (MM + 1), pl = x - il * (MM + 1);
+        float c = 0.f;
+        if (pl == MM) {
+            if (coarse) c = __expf((float)(cum[i0 + ntl - 1] - cum[i0 + il]));
+        } else {
+            const int jr = ((il >> pl) | 1) << pl;
+            if (pl < mm && !((il >> pl) & 1) && jr < ntl)
+                c = __expf((float)(cum[i0 + jr - 1] - cum[i0 + il]));
+        }
+        sCw[il][pl] = c;
+    }
+    for (int x = threadIdx.x; x < ntl * MM; x += kKvWaves * 64) {
+        const int il = x / MM, pl = x - il * MM;
+        const int jb = (il >> pl) << pl;
+        const double ce = i0 + il >= 1 ? cum[i0 + il - 1] : 0.0;
+        const double cb = i0 + jb >= 1 ? cum[i0 + jb - 1] : 0.0;
+        sBw[il][pl] = (float)(ce - cb);
+    }
+
     f32x4 acc[MM][2][2];
 #pragma unroll
     for (int pl = 0; pl < MM; ++pl)
@@ -471,33 +500,34 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_kvwalk(BwdParams p, Rw
     const int vb = wave & 3;          // this wave's d_v block
     const int kb0 = 2 * (wave >> 2);  // and its first key block for dv
 
-    auto store = [&](int il, int zv) __attribute__((always_inline)) {
+    // results of chunk il: dk rows of key block kb (this wave's 16 columns),
+    // dv rows of its key block kb0 + jb, and k . dk (the last wave)
+    auto store_dk = [&](int il, int kb, int zv) __attribute__((always_inline)) {
         const int n16 = (lane & 15) + zv, g = (lane >> 4) + zv;
         const int t0 = (i0 + il) * TC;
-        const int nvalid = min(TC, T - t0);
-        const size_t r = row0 + t0;
-        // uniform row base plus a 32-bit lane offset
-        float* gk = p.gk + r * DK;
-        float* gv = p.gv + r * DV;
-#pragma unroll
-        for (int kb = 0; kb < 4; ++kb) {
-            const int s = 16 * kb + n16;
-            if (s < nvalid) *reinterpret_cast<f32x4*>(gk + (uint32_t)(s * DK + 16 * wave + 4 * g)) = dk4[kb];
-        }
-#pragma unroll
-        for (int jb = 0; jb < 2; ++jb) {
-            const int s = 16 * (kb0 + jb) + n16;
-            if (s < nvalid) *reinterpret_cast<f32x4*>(gv + (uint32_t)(s * DV + 16 * vb + 4 * g)) = dv2[jb];
-        }
+        const int s = 16 * kb + n16;
+        float* gk = p.gk + (row0 + t0) * DK;  // uniform row base plus a 32-bit lane offset
+        if (s < T - t0) *reinterpret_cast<f32x4*>(gk + (uint32_t)(s * DK + 16 * wave + 4 * g)) = dk4[kb];
+    };
+    auto store_dv = [&](int il, int jb, int zv) __attribute__((always_inline)) {
+        const int n16 = (lane & 15) + zv, g = (lane >> 4) + zv;
+        const int t0 = (i0 + il) * TC;
+        const int s = 16 * (kb0 + jb) + n16;
+        float* gv = p.gv + (row0 + t0) * DV;
+        if (s < T - t0) *reinterpret_cast<f32x4*>(gv + (uint32_t)(s * DV + 16 * vb + 4 * g)) = dv2[jb];
+    };
+    auto store_da = [&](int il) __attribute__((always_inline)) {
         if (wave == kKvWaves - 1) {
+            const int t0 = (i0 + il) * TC;
             float d = 0.f;
 #pragma unroll
-            for (int u = 0; u < kKvWaves; ++u) d += sDa[u][lane];
-            if (lane < nvalid) p.dA2[r + lane] = d;
+            for (int u = 0; u < kKvWaves; ++u) d += sDa[il & 1][u][lane];
+            if (lane < T - t0) p.dA2[row0 + t0 + lane] = d;
         }
     };
 
-    issue(ntl - 1, (ntl - 1) & 1);
+#pragma unroll
+    for (int part = 0; part < 4; ++part) issue(ntl - 1, (ntl - 1) & 1, part);
     for (int il = ntl - 1; il >= 0; --il) {
         const int cur = il & 1;
         wait_vm<0>();
@@ -509,8 +539,7 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_kvwalk(BwdParams p, Rw
         int zv;
         asm volatile("v_mov_b32 %0, 0" : "=v"(zv));
         const int n16 = (lane & 15) + zv, g = (lane >> 4) + zv;
-        if (il + 1 < ntl) store(il + 1, zv);
-        if (il > 0) issue(il - 1, cur ^ 1);
+        if (il > 0) issue(il - 1, cur ^ 1, 0);
         const bf16_t* Qs = sQ[cur];
         const bf16_t* Ks = sK[cur];
         const bf16_t* Vs = sV[cur];
@@ -529,8 +558,7 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_kvwalk(BwdParams p, Rw
         } else if (wave >= 3) {
             const int pl = wave - 3;
             if (pl < mm && ((il >> pl) & 1)) {
-                const int jb = (il >> pl) << pl;
-                const float base = (float)(sCum[il] - sCum[jb]);
+                const float base = sBw[il][pl];
                 const float lam = Ls[lane * L + kRwLogC + pl + 1];
                 sW[pl][lane] = lane < nvalid ? lam * __expf(x + base) : 0.f;
             }
@@ -581,14 +609,16 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_kvwalk(BwdParams p, Rw
                 *reinterpret_cast<bf16x4*>(sP + toff<TC>(s + 16, 16 * rb + 4 * g)) = bf16x4{};
             }
         };
+        if (il > 0) issue(il - 1, cur ^ 1, 1);
         score(wave);
         if (wave < 2) score(wave + 8);
+        if (il > 0) issue(il - 1, cur ^ 1, 2);
 
         // R~ share of this wave (d_k row 16 w + n16, d_v 32 ks + 8 g + 0..7):
         // operand of the dk product in registers, and to LDS for the dv product
         bf16x8 rf[2];
         {
-            const float wc = coarse ? __expf((float)(sCum[ntl] - sCum[il + 1])) : 0.f;
+            const float wc = sCw[il][MM];
             f32x4 r[2][2];
 #pragma unroll
             for (int ks = 0; ks < 2; ++ks)
@@ -598,7 +628,7 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_kvwalk(BwdParams p, Rw
             for (int pl = 0; pl < MM; ++pl) {
                 const int jr = ((il >> pl) | 1) << pl;
                 if (pl < mm && !((il >> pl) & 1) && jr < ntl) {
-                    const float c = __expf((float)(sCum[jr] - sCum[il + 1]));
+                    const float c = sCw[il][pl];
 #pragma unroll
                     for (int ks = 0; ks < 2; ++ks)
 #pragma unroll
@@ -611,7 +641,12 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_kvwalk(BwdParams p, Rw
                 *reinterpret_cast<bf16x8*>(sR + toff<DV>(16 * wave + n16, 32 * ks + 8 * g)) = rf[ks];
             }
         }
+        if (il > 0) issue(il - 1, cur ^ 1, 3);
         __syncthreads();  // the chunk's weights, (dP (.) M)^T, ((Q K^T) (.) M)^T and R~
+        // the previous chunk's results go out block by block between this
+        // chunk's products (each right before its registers are reused)
+        const bool prev = il + 1 < ntl;
+        if (prev) store_da(il + 1);
 
         // dk^T (rows d_k 16 w + 4g + i, column key 16 kb + n16): the causal
         // block, then e^(A(end) - A_s) R~ v_s
@@ -620,6 +655,7 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_kvwalk(BwdParams p, Rw
         for (int sp = 0; sp < 2; ++sp) qT[sp] = ld_tr8<DK>(Qs, 32 * sp + zv, 16 * wave);
 #pragma unroll
         for (int kb = 0; kb < 4; ++kb) {
+            if (prev) store_dk(il + 1, kb, zv);
             f32x4 a = {0.f, 0.f, 0.f, 0.f}, t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int sp = 0; sp < 2; ++sp)
@@ -641,6 +677,7 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_kvwalk(BwdParams p, Rw
             for (int ks = 0; ks < 4; ++ks) rT[ks] = ld_tr8<DV>(sR, 32 * ks + zv, 16 * vb);
 #pragma unroll
             for (int jb = 0; jb < 2; ++jb) {
+                if (prev) store_dv(il + 1, jb, zv);
                 const int kb = kb0 + jb;
                 f32x4 a = {0.f, 0.f, 0.f, 0.f}, t = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
@@ -664,7 +701,7 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_kvwalk(BwdParams p, Rw
                 xk[kb] = (float)kk[0] * dk4[kb][0] + (float)kk[1] * dk4[kb][1] +
                          (float)kk[2] * dk4[kb][2] + (float)kk[3] * dk4[kb][3];
             }
-            sDa[wave][lane] = sum_rows4_x4(xk[0], xk[1], xk[2], xk[3]);
+            sDa[il & 1][wave][lane] = sum_rows4_x4(xk[0], xk[1], xk[2], xk[3]);
         }
 
         // the chunk's queries into the blocks it belongs to (set bits p < m):
@@ -698,7 +735,11 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_kvwalk(BwdParams p, Rw
         }
     }
     __syncthreads();  // the last chunk's k . dk parts
-    store(0, 0);
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) store_dk(0, kb, 0);
+#pragma unroll
+    for (int jb = 0; jb < 2; ++jb) store_dv(0, jb, 0);
+    store_da(0);
 }
 
 bool kvwalk_applies(const BwdParams& p, const RwalkArgs& w) {
