@@ -160,14 +160,18 @@ __device__ __forceinline__ void score_block_bwd(int rb, int sb, const bf16_t* Qs
         const float v = sum_rows4(xd[0] + xd[1] + xd[2] + xd[3]);
         if (g == 0) sDi[(rb * (rb + 1) / 2 + sb) * 16 + m16] = v;
     } else {
+        // levels 0..4 of the diagonal block: 0..3 in one four-way row
+        // reduction (lane (m16, g) ends with level g of token m16), 4 alone
+        float x[5];
 #pragma unroll
         for (int l = 0; l < 5; ++l) {
-            float x = 0.f;
+            x[l] = 0.f;
 #pragma unroll
-            for (int i = 0; i < 4; ++i) x += lev[i] == l ? xd[i] : 0.f;
-            const float v = sum_rows4(x);
-            if (g == 0) sDd[(rb * 5 + l) * 16 + m16] = v;
+            for (int i = 0; i < 4; ++i) x[l] += lev[i] == l ? xd[i] : 0.f;
         }
+        sDd[(rb * 5 + g) * 16 + m16] = sum_rows4_x4(x[0], x[1], x[2], x[3]);
+        const float v4 = sum_rows4(x[4]);
+        if (g == 0) sDd[(rb * 5 + 4) * 16 + m16] = v4;
     }
 }
 
@@ -194,6 +198,16 @@ __device__ __forceinline__ void scores_for_wave(int wave, const bf16_t* Qs, cons
         // waves 0 and 1 also w + 8
         const int t1 = wave < 2 ? wave + 12 : wave < 4 ? wave + 8 : 0;
         for (int tau = wave; tau < t1; tau += 4) block(tau);
+    } else if constexpr (NWT == 8 && BWD) {
+        // the diagonal blocks (tau 0, 2, 5, 9: five levels of dlambda sums)
+        // cost about twice the others: one each for waves 2-5, which also
+        // issue copies; waves 0 and 1 (no copies) take two of the others
+        // (1, 3 and 4, 6), waves 6 and 7 one (7, 8)
+        constexpr unsigned kFirst = 0x87952041u;   // 4 bits per wave
+        constexpr unsigned kSecond = 0x63u;
+        const int n = wave < 2 ? 2 : 1;
+#pragma unroll 1  // one call site of the block (unrolled, the two copies spill)
+        for (int x = 0; x < n; ++x) block((int)(((x ? kSecond : kFirst) >> (4 * wave)) & 15u));
     } else {
         for (int tau = wave; tau < NRB * (NRB + 1) / 2; tau += NWT) block(tau);
     }
@@ -556,11 +570,20 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
         const int i = tile0 + il;
         const int nvalid = min(TC, p.T - i * TC);
         const float tot = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(Awc[TC - 1])));
+        // dq pass: the issuing waves of Q and K store and copy before their
+        // scores, so that their queue stalls overlap the other waves' scores
+        // and not the waves 2 and 3 copying V, q, lambda and a after theirs
+        if (BWD && issuer) {
+            if constexpr (NH > 1) {
+                if (finisher && prev_tile >= 0) finish_prev();
+            }
+            if (il + 1 < ntl) issue(il + 1, 0, Qn, Kn, Vn, Ln, an, Qon);
+        }
         if constexpr (BWD)
             scores_for_wave<DK, NWT, true, DVW>(wave, Qc, Kc, sP, Awc, Lc, LP, Qoc, Vc, sDi, sDd);
         else
             scores_for_wave<DK, NWT>(wave, Qc, Kc, sP, Awc, Lc, LP);
-        if (issuer) {
+        if (!BWD && issuer) {
             if constexpr (NH > 1) {
                 if (finisher && prev_tile >= 0) finish_prev();
             }
