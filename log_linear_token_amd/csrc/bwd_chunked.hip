@@ -974,6 +974,65 @@ __global__ __launch_bounds__(256) void k_bwd_da(BwdParams p) {
     }
 }
 
+// The same suffix sums over more blocks (the one-block-per-head kernel above
+// walks the sequence serially): pieces of 1024 tokens per (batch, head).
+// First each piece's total, then each piece's suffix sums plus the totals of
+// the later pieces; fp64 throughout.
+constexpr int kDaPiece = 1024;
+
+__global__ __launch_bounds__(256) void k_bwd_da_part(BwdParams p, double* __restrict__ parts, int np) {
+    constexpr int NT = 256, PT = kDaPiece / NT;
+    __shared__ double red[NT / 64];
+    const int bh = blockIdx.x / np, pc = blockIdx.x - bh * np;
+    const size_t base = (size_t)bh * p.T;
+    const int t0 = pc * kDaPiece + threadIdx.x * PT;
+    double sum = 0.0;
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+        const int t = t0 + j;
+        if (t < p.T) sum += (double)p.dA1[base + t] - (double)p.dA2[base + t];
+    }
+    for (int o = 32; o >= 1; o >>= 1) sum += __shfl_xor(sum, o);
+    if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = sum;
+    __syncthreads();
+    if (threadIdx.x == 0) parts[blockIdx.x] = red[0] + red[1] + red[2] + red[3];
+}
+
+__global__ __launch_bounds__(256) void k_bwd_da_scan(BwdParams p, const double* __restrict__ parts, int np) {
+    constexpr int NT = 256, PT = kDaPiece / NT;
+    __shared__ double part[NT];
+    const int tid = threadIdx.x;
+    const int bh = blockIdx.x / np, pc = blockIdx.x - bh * np;
+    const size_t base = (size_t)bh * p.T;
+    const int t0 = pc * kDaPiece + tid * PT;
+    // the later pieces of this (batch, head)
+    double carry = 0.0;
+    for (int u = pc + 1; u < np; ++u) carry += parts[(size_t)bh * np + u];
+    double x[PT];
+    double sum = 0.0;
+#pragma unroll
+    for (int j = 0; j < PT; ++j) {
+        const int t = t0 + j;
+        x[j] = t < p.T ? (double)p.dA1[base + t] - (double)p.dA2[base + t] : 0.0;
+        sum += x[j];
+    }
+    part[tid] = sum;
+    __syncthreads();
+    for (int off = 1; off < NT; off <<= 1) {  // inclusive suffix scan over the threads
+        const double y = tid + off < NT ? part[tid + off] : 0.0;
+        __syncthreads();
+        part[tid] += y;
+        __syncthreads();
+    }
+    double run = carry + part[tid] - sum;  // the later threads and pieces
+#pragma unroll
+    for (int j = PT - 1; j >= 0; --j) {
+        const int t = t0 + j;
+        run += x[j];
+        if (t < p.T) p.ga[base + t] = (float)run;
+    }
+}
+
 // A at the end of every chunk for the R(j) and dk / dv stages: one block per
 // (batch, head); each thread sums its chunk's a in fp32 (in token order), and
 // the chunk totals are summed in fp64, tile by tile, the earlier tiles' sum
@@ -1150,7 +1209,17 @@ hipError_t launch_bwd_typed(const BwdParams& p, hipStream_t stream) {
         if (err != hipSuccess) return err;
         hipLaunchKernelGGL((k_bwd_dkv<E, C, DM, 0, 0>), dim3(nblk), dim3(C / 16 * 64), s3, stream, p3);
     }
-    hipLaunchKernelGGL(k_bwd_da, dim3(p.BH), dim3(256), 0, stream, p);
+    if (p.cum && (long)((p.T + kDaPiece - 1) / kDaPiece) <= (long)p.N) {
+        // the piece totals go to the chunk-decay region ([BH][N] doubles), which
+        // nothing reads after the dk / dv stage
+        const int np = (p.T + kDaPiece - 1) / kDaPiece;
+        double* parts = const_cast<double*>(p.cum);
+        hipLaunchKernelGGL(k_bwd_da_part, dim3(p.BH * np), dim3(256), 0, stream, p, parts, np);
+        hipLaunchKernelGGL(k_bwd_da_scan, dim3(p.BH * np), dim3(256), 0, stream, p,
+                           static_cast<const double*>(parts), np);
+    } else {
+        hipLaunchKernelGGL(k_bwd_da, dim3(p.BH), dim3(256), 0, stream, p);
+    }
     return hipGetLastError();
 }
 

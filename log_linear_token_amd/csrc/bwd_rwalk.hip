@@ -388,7 +388,6 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_kvwalk(BwdParams p, Rw
     const bf16_t* k = reinterpret_cast<const bf16_t*>(p.k);
     const bf16_t* v = reinterpret_cast<const bf16_t*>(p.v);
     const bf16_t* dout = reinterpret_cast<const bf16_t*>(p.dout);
-    const bf16_t* rst = reinterpret_cast<const bf16_t*>(p.rst16);
 
     typedef TileCopy<DK, kKvWaves> CK;
     typedef TileCopy<DV, kKvWaves> CV;
@@ -446,9 +445,11 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_kvwalk(BwdParams p, Rw
     };
 
     // the blocks of levels >= m after the segment, combined at its end: this
-    // lane's share, d_k row 16 w + n16, d_v 32 ks + 8 g + (0..7)
-    // (only a full segment that is not the last has such blocks; A at the end
-    // of the sequence's last chunk is never read)
+    // lane's share, d_k row 16 w + n16, d_v 32 ks + 8 g + (0..7).  Each such
+    // block is the sum of the fp32 parts the R(j) walk left for the segments
+    // it covers (all relative to the block's start).  Only a full segment that
+    // is not the last has such blocks (A at the end of the sequence's last
+    // chunk is never read).
     f32x4 nc[2][2];
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) nc[ks][0] = nc[ks][1] = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -458,14 +459,19 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_kvwalk(BwdParams p, Rw
         if (((i0 >> pl) & 1) || j >= N) continue;
         coarse = true;
         const float wt = __expf((float)(cum[j - 1] - cum[i0 + ntl - 1]));
-        const bf16_t* R = rst + ((size_t)bh * N + j) * DK * DV + (size_t)(16 * wave + n16) * DV + 8 * g;
+        const int s0 = j >> w.m, s1 = min(s0 + (1 << (pl - w.m)), w.nseg);
+        for (int sg = s0; sg < s1; ++sg) {
+            const float* R = w.part + (((size_t)bh * w.nseg + sg) * w.ntop + (pl - w.m)) * DK * DV +
+                             (size_t)(16 * wave + n16) * DV + 8 * g;
 #pragma unroll
-        for (int ks = 0; ks < 2; ++ks) {
-            const bf16x8 x = *reinterpret_cast<const bf16x8*>(R + 32 * ks);
+            for (int ks = 0; ks < 2; ++ks) {
+                const f32x4 x0 = *reinterpret_cast<const f32x4*>(R + 32 * ks);
+                const f32x4 x1 = *reinterpret_cast<const f32x4*>(R + 32 * ks + 4);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                nc[ks][0][e] += wt * (float)x[e];
-                nc[ks][1][e] += wt * (float)x[4 + e];
+                for (int e = 0; e < 4; ++e) {
+                    nc[ks][0][e] += wt * x0[e];
+                    nc[ks][1][e] += wt * x1[e];
+                }
             }
         }
     }
@@ -752,7 +758,8 @@ hipError_t launch_rwalk_dk(const BwdParams& p, const RwalkArgs& w, hipStream_t s
         hipLaunchKernelGGL((k_bwd_rwalk<DK, 64, 7>), dim3(p.BH * w.nseg), dim3(kRwWaves * 64), 0, stream, p, w);
     else
         hipLaunchKernelGGL((k_bwd_rwalk<DK, 64, 8>), dim3(p.BH * w.nseg), dim3(kRwWaves * 64), 0, stream, p, w);
-    if (w.ntop > 0) {
+    // (with pmin = m the dk / dv walk sums the parts of the blocks itself)
+    if (w.ntop > 0 && w.pmin < w.m) {
         long nj = 0;
         for (int pp = w.m; pp < p.nlev; ++pp) {
             const int first = 1 << pp;
