@@ -1034,23 +1034,51 @@ __global__ __launch_bounds__(256) void k_bwd_da_scan(BwdParams p, const double* 
 }
 
 // A at the end of every chunk for the R(j) and dk / dv stages: one block per
-// (batch, head); each thread sums its chunk's a in fp32 (in token order), and
-// the chunk totals are summed in fp64, tile by tile, the earlier tiles' sum
-// carried.
+// (batch, head), walking the sequence in tiles of 8192 tokens.  Each thread
+// sums two strips of 16 consecutive tokens (fp32, in token order; 16-byte
+// loads where the strip is whole and aligned), a chunk's total is the sum of
+// its strips in order (C is a multiple of 16; at most 256 chunks a tile), and the chunk totals are
+// summed in fp64, the earlier tiles' sum carried.
 __global__ __launch_bounds__(256) void k_bwd_chunk_cum(BwdParams p) {
-    constexpr int NT = 256;
+    constexpr int NT = 256, S = 16, NS = 2 * NT;  // strips per tile
+    __shared__ float strip[NS];
     __shared__ double part[NT];
     const int tid = threadIdx.x;
     const size_t base = (size_t)blockIdx.x * p.T;
+    const int spc = p.C / S;        // strips per chunk
+    const int cpt = min(NS / spc, NT);  // chunks per tile
+    const bool vec = (p.T % 4) == 0 && (reinterpret_cast<uintptr_t>(p.a) % 16) == 0;
     double carry = 0.0;
-    for (int c0 = 0; c0 < p.N; c0 += NT) {
-        const int c = c0 + tid;
-        float tot = 0.f;
-        if (c < p.N) {
-            const int t1 = min((c + 1) * p.C, p.T);
-            for (int t = c * p.C; t < t1; ++t) tot += p.a[base + t];
+    for (int c0 = 0; c0 < p.N; c0 += cpt) {
+        const int tt0 = c0 * p.C;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+            const int sidx = u * NT + tid;
+            if (sidx >= cpt * spc) break;
+            const int t = tt0 + sidx * S;
+            float tot = 0.f;
+            if (vec && t + S <= p.T) {
+                const float4* src = reinterpret_cast<const float4*>(p.a + base + t);
+#pragma unroll
+                for (int k = 0; k < S / 4; ++k) {
+                    const float4 y = src[k];
+                    tot += y.x;
+                    tot += y.y;
+                    tot += y.z;
+                    tot += y.w;
+                }
+            } else {
+                for (int k = 0; k < S; ++k)
+                    if (t + k < p.T) tot += p.a[base + t + k];
+            }
+            strip[sidx] = tot;
         }
-        part[tid] = tot;
+        __syncthreads();
+        const int c = c0 + tid;
+        float ct = 0.f;
+        if (tid < cpt && c < p.N)
+            for (int k = 0; k < spc; ++k) ct += strip[tid * spc + k];
+        part[tid] = ct;
         __syncthreads();
         for (int off = 1; off < NT; off <<= 1) {  // inclusive prefix (Hillis-Steele)
             const double y = tid >= off ? part[tid - off] : 0.0;
@@ -1059,9 +1087,9 @@ __global__ __launch_bounds__(256) void k_bwd_chunk_cum(BwdParams p) {
             __syncthreads();
         }
         // p.cum is read-only for the other stages; this kernel fills it
-        if (c < p.N) const_cast<double*>(p.cum)[(size_t)blockIdx.x * p.N + c] = carry + part[tid];
-        carry += part[NT - 1];
-        __syncthreads();  // part[] is rewritten by the next tile
+        if (tid < cpt && c < p.N) const_cast<double*>(p.cum)[(size_t)blockIdx.x * p.N + c] = carry + part[tid];
+        carry += part[cpt - 1];
+        __syncthreads();  // strip[] and part[] are rewritten by the next tile
     }
 }
 

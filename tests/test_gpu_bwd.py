@@ -160,7 +160,7 @@ def test_bwd_rstate_paths(monkeypatch, mode, B, H, T, dk, dv):
 
 
 @pytest.mark.parametrize("mode", ["fused", "chunked"])
-@pytest.mark.parametrize("B,H,T,dk,C", [(1, 2, 1, 128, 64), (1, 2, 40, 64, 64), (2, 1, 777, 128, 64),
+@pytest.mark.parametrize("B,H,T,dk,C", [(1, 2, 1, 128, 64), (1, 2, 40, 64, 64), (2, 1, 777, 128, 64), (1, 1, 700, 64, 16),
                                         (1, 1, 3000, 128, 32), (1, 2, 2048, 64, 128),
                                         (1, 1, 5000, 128, 64)])
 def test_bwd_dq_paths(monkeypatch, mode, B, H, T, dk, C):
