@@ -635,6 +635,7 @@ def bench_prefill(cfg, sets, stream, steps: int) -> dict:
         state["i"] += 1
         LL.loglin_prefill_states(kk, vv, aa, Lmax, out=out, workspace=ws)
 
+    settle(run)
     for _ in range(5):
         run()
     ms = timed(run, max(5, steps // 4), stream)
@@ -689,6 +690,7 @@ def bench_backward(cfg, sets, stream, steps: int) -> dict:
         state["i"] += 1
         LL.loglin_bwd_chunked(qq, kk, vv, aa, ll, douts[j], cfg.C, grads=grads, workspace=ws)
 
+    settle(run)
     for _ in range(10):
         run()
     ms = timed(run, steps, stream)
