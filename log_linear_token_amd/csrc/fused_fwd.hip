@@ -198,7 +198,7 @@ __device__ __forceinline__ void scores_for_wave(int wave, const bf16_t* Qs, cons
         // waves 0 and 1 also w + 8
         const int t1 = wave < 2 ? wave + 12 : wave < 4 ? wave + 8 : 0;
         for (int tau = wave; tau < t1; tau += 4) block(tau);
-    } else if constexpr (NWT == 8 && BWD) {
+    } else if constexpr (NWT == 8 && BWD && DVW == 64) {
         // the diagonal blocks (tau 0, 2, 5, 9: five levels of dlambda sums)
         // cost about twice the others: one each for waves 2-5, which also
         // issue copies; waves 0 and 1 (no copies) take two of the others
@@ -424,11 +424,15 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
     // With eight waves, waves 4-7 (no score blocks) store the output and copy
     // Q and K, and waves 2 and 3 (two score blocks) copy V, lambda and a;
     // otherwise every wave does its share of everything.
+    // The dq pass as one block of 128 columns (one wave per 16-column slab,
+    // NH = 1): its V and q tiles are 16 KB each, so waves 0-3 copy those,
+    // lambda and a, and waves 4-7 Q and K; every wave stores its own rows.
+    constexpr bool WIDE = BWD && NH == 1 && NWT == 8;
     constexpr int NIW = NWT == 8 ? 4 : NWT;      // Q/K copies and stores
     const bool issuer = wave >= NWT - NIW;
     const int iw = issuer ? wave - (NWT - NIW) : 0;
-    constexpr int NIW1 = NWT == 8 ? 2 : NIW;     // V, lambda and a copies
-    constexpr int P1W0 = NWT == 8 ? 2 : NWT - NIW;
+    constexpr int NIW1 = WIDE ? 4 : NWT == 8 ? 2 : NIW;  // V, lambda and a copies
+    constexpr int P1W0 = WIDE ? 0 : NWT == 8 ? 2 : NWT - NIW;
     const bool issuer1 = wave >= P1W0 && wave < P1W0 + NIW1;
     const int i1 = issuer1 ? wave - P1W0 : 0;
     const bool dwave = wave == P1W0;  // copies a; computes each tile's decay
@@ -601,25 +605,32 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
         // Q fragments of the level products (this wave's head-dim part, all
         // row blocks): 8 consecutive head-dim rows per lane group, the order in
         // which tile_state lays out the register states.  Read once per tile.
-        typename H::frag qf[NRB][NKSH];
+        // (the one-block dq pass reads them from LDS at each use instead: its
+        // register levels cover all of d_k, and kept here they would spill)
+        typename H::frag qf[WIDE ? 1 : NRB][NKSH];
+        auto qfrag = [&](int rb, int ks) __attribute__((always_inline)) {
+            typename H::frag x;
+            if constexpr (DK >= 32) x = ld8<DK>(Qc, 16 * rb + m16, 32 * (ks0 + ks) + 8 * g);
+            else x = ld4<DK>(Qc, 16 * rb + m16, 4 * g);
+            return x;
+        };
+        if constexpr (!WIDE) {
 #pragma unroll
-        for (int rb = 0; rb < NRB; ++rb) {
+            for (int rb = 0; rb < NRB; ++rb)
 #pragma unroll
-            for (int ks = 0; ks < NKSH; ++ks) {
-                if constexpr (DK >= 32) qf[rb][ks] = ld8<DK>(Qc, 16 * rb + m16, 32 * (ks0 + ks) + 8 * g);
-                else qf[rb][ks] = ld4<DK>(Qc, 16 * rb + m16, 4 * g);
-            }
+                for (int ks = 0; ks < NKSH; ++ks) qf[rb][ks] = qfrag(rb, ks);
         }
         // dq pass: q at (row 16 rb + m16, columns c0 + 4g .. + 3), the columns
         // of this lane's level-product outputs
-        float qv[BWD ? NRB : 1][4];
-        if constexpr (BWD) {
+        float qv[BWD && !WIDE ? NRB : 1][4];
+        auto qval = [&](int rb, float (&x)[4]) __attribute__((always_inline)) {
+            const bf16x4 y = ld4<DVW>(Qoc, 16 * rb + m16, 16 * cs + 4 * g);
 #pragma unroll
-            for (int rb = 0; rb < NRB; ++rb) {
-                const bf16x4 x = ld4<DVW>(Qoc, 16 * rb + m16, 16 * cs + 4 * g);
+            for (int r = 0; r < 4; ++r) x[r] = (float)y[r];
+        };
+        if constexpr (BWD && !WIDE) {
 #pragma unroll
-                for (int r = 0; r < 4; ++r) qv[rb][r] = (float)x[r];
-            }
+            for (int rb = 0; rb < NRB; ++rb) qval(rb, qv[rb]);
         }
         auto add_level = [&](const typename H::frag (&ga)[NKSH], int lev, float logd, int slot)
             __attribute__((always_inline)) {
@@ -632,7 +643,10 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
             for (int rb = 0; rb < NRB; ++rb) {
                 y[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                for (int ks = 0; ks < NKSH; ++ks) y[rb] = mma(ga[ks], qf[rb][ks], y[rb]);
+                for (int ks = 0; ks < NKSH; ++ks) {
+                    if constexpr (WIDE) y[rb] = mma(ga[ks], qfrag(rb, ks), y[rb]);
+                    else y[rb] = mma(ga[ks], qf[rb][ks], y[rb]);
+                }
             }
 #pragma unroll
             for (int rb = 0; rb < NRB; ++rb) {
@@ -648,9 +662,12 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
                 // with row block g's total for token 16 g + m16.
                 float x[NRB];
 #pragma unroll
-                for (int rb = 0; rb < NRB; ++rb)
-                    x[rb] = qv[rb][0] * y[rb][0] + qv[rb][1] * y[rb][1] + qv[rb][2] * y[rb][2] +
-                            qv[rb][3] * y[rb][3];
+                for (int rb = 0; rb < NRB; ++rb) {
+                    float qq[4];
+                    if constexpr (WIDE) qval(rb, qq);
+                    else for (int r = 0; r < 4; ++r) qq[r] = qv[rb][r];
+                    x[rb] = qq[0] * y[rb][0] + qq[1] * y[rb][1] + qq[2] * y[rb][2] + qq[3] * y[rb][3];
+                }
                 sDl[(slot * NWT + wave) * TC + lane] = d * sum_rows4_x4(x[0], x[1], x[2], x[3]);
             }
         };
@@ -740,9 +757,12 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
         if constexpr (BWD) {
             float x[NRB];
 #pragma unroll
-            for (int rb = 0; rb < NRB; ++rb)
-                x[rb] = qv[rb][0] * o[rb][0] + qv[rb][1] * o[rb][1] + qv[rb][2] * o[rb][2] +
-                        qv[rb][3] * o[rb][3];
+            for (int rb = 0; rb < NRB; ++rb) {
+                float qq[4];
+                if constexpr (WIDE) qval(rb, qq);
+                else for (int r = 0; r < 4; ++r) qq[r] = qv[rb][r];
+                x[rb] = qq[0] * o[rb][0] + qq[1] * o[rb][1] + qq[2] * o[rb][2] + qq[3] * o[rb][3];
+            }
             sDq[((il & 1) * NWT + wave) * TC + lane] = sum_rows4_x4(x[0], x[1], x[2], x[3]);
         }
         if constexpr (NH > 1) {
@@ -844,10 +864,10 @@ int bit_len(long x) {
 
 }  // namespace
 
-FusedPlan plan_fused(int BH, int T, int dk, int dv, int lu, int force_m, int force_split) {
+FusedPlan plan_fused(int BH, int T, int dk, int dv, int lu, int force_m, int force_split, int max_dvw) {
     FusedPlan pl{};
     if (lu > kFusedMaxL) return pl;  // lambda levels staged per token
-    const int dvw = dv >= 64 ? 64 : dv;
+    const int dvw = dv >= max_dvw ? max_dvw : dv >= 64 ? 64 : dv;
     pl.dvw = dvw;
     pl.ndvb = dv / dvw;
     pl.ntiles = (T + TC - 1) / TC;
@@ -898,20 +918,35 @@ namespace {
 
 template <int DK, int NW, int MLOC, int TOPMAX>
 hipError_t launch_main(const FusedParams& p, hipStream_t stream) {
-    constexpr int NH = DK >= 64 ? 2 : 1;  // two waves share a column slab, each half of d_k
     const unsigned nblk = (unsigned)p.BH * p.nseg * p.ndvb;
-    if (p.qo) {
-        // the backward's dq pass: d_v = 64 (the contraction here) only
-        if constexpr (DK == 64 && NW == 4) {
-            hipLaunchKernelGGL((k_fused_fwd<DK, NW, NH, MLOC, TOPMAX, true>), dim3(nblk),
-                               dim3(NW * NH * 64), 0, stream, p);
-            return hipGetLastError();
+    if constexpr (NW == 8) {
+        // 128 columns in one block: only the backward's dq pass (d_k' = 64,
+        // one wave per 16-column slab holding all of d_k') with five register
+        // levels and two above the segment (the 8K plan; other plans use
+        // two 64-column blocks)
+        if constexpr (DK == 64 && MLOC == 5 && TOPMAX == 2) {
+            if (p.qo) {
+                hipLaunchKernelGGL((k_fused_fwd<DK, 8, 1, MLOC, TOPMAX, true>), dim3(nblk), dim3(8 * 64), 0,
+                                   stream, p);
+                return hipGetLastError();
+            }
         }
         return hipErrorInvalidValue;
+    } else {
+        constexpr int NH = DK >= 64 ? 2 : 1;  // two waves share a column slab, each half of d_k
+        if (p.qo) {
+            // the backward's dq pass: d_v = 64 (the contraction here) only
+            if constexpr (DK == 64 && NW == 4) {
+                hipLaunchKernelGGL((k_fused_fwd<DK, NW, NH, MLOC, TOPMAX, true>), dim3(nblk),
+                                   dim3(NW * NH * 64), 0, stream, p);
+                return hipGetLastError();
+            }
+            return hipErrorInvalidValue;
+        }
+        hipLaunchKernelGGL((k_fused_fwd<DK, NW, NH, MLOC, TOPMAX, false>), dim3(nblk), dim3(NW * NH * 64), 0,
+                           stream, p);
+        return hipGetLastError();
     }
-    hipLaunchKernelGGL((k_fused_fwd<DK, NW, NH, MLOC, TOPMAX, false>), dim3(nblk), dim3(NW * NH * 64), 0,
-                       stream, p);
-    return hipGetLastError();
 }
 
 template <int DK, int NW>
@@ -948,6 +983,9 @@ hipError_t launch_fused_dk(const FusedParams& p, const FwdParams& scan, unsigned
         case 16: return launch_fused_t<DK, 1>(p, scan, stages, s);
         case 32: return launch_fused_t<DK, 2>(p, scan, stages, s);
         case 64: return launch_fused_t<DK, 4>(p, scan, stages, s);
+        case 128:
+            if constexpr (DK == 64) return launch_fused_t<DK, 8>(p, scan, stages, s);
+            break;
     }
     return hipErrorInvalidValue;
 }

@@ -71,8 +71,11 @@ struct FusedParams {
 struct FusedPlan {
     int ok, m, nseg, ntop, dvw, ndvb, ntiles, combo, msub;
 };
-// force_m >= 0 asks for segments of 2^force_m tiles (plan fails if that does not fit)
-FusedPlan plan_fused(int BH, int T, int dk, int dv, int lu, int force_m, int force_split);
+// force_m >= 0 asks for segments of 2^force_m tiles (plan fails if that does not fit);
+// max_dvw: widest column block (64, or 128 for the backward's dq pass, whose
+// one-block kernel exists only for d_k = 64 with combination {5, 2})
+FusedPlan plan_fused(int BH, int T, int dk, int dv, int lu, int force_m, int force_split,
+                     int max_dvw = 64);
 hipError_t launch_fused_fwd(const FusedParams& p, const FwdParams& scan, unsigned stages,
                             hipStream_t stream);
 

@@ -491,6 +491,12 @@ bool force_bwd_dq_chunked() {
     const char* e = getenv("LOGLIN_BWD_DQ");
     return e && strcmp(e, "chunked") == 0;
 }
+// LOGLIN_BWD_DQ=fused64: the fused dq pass in two 64-column blocks even where
+// the one-block kernel applies
+bool force_bwd_dq_two_blocks() {
+    const char* e = getenv("LOGLIN_BWD_DQ");
+    return e && strcmp(e, "fused64") == 0;
+}
 
 // Workspace of the backward.  dq / dlambda either by the fused path run on
 // the swapped problem (queries dO, keys v, values k; its segment states, the
@@ -512,7 +518,15 @@ BwdWorkspace bwd_layout(long BH, int T, int dk, int dv, int C, loglin_dtype dt) 
     size_t off = 0;
     if (dt == LOGLIN_BF16 && dv == 64 && (dk == 64 || dk == 128) && T > 0 && BH > 0 &&
         !force_bwd_dq_chunked()) {
-        const FusedPlan f = plan_fused((int)BH, T, dv, dk, levels_needed(T), -1, -1);
+        // d_v' = d_k = 128: one block of 128 columns (the score tile of dO v^T
+        // computed once, dO, v, lambda and a read once) where the plan has
+        // five register levels and two above the segment, the combination
+        // that kernel is built for; two 64-column blocks otherwise
+        FusedPlan f = plan_fused((int)BH, T, dv, dk, levels_needed(T), -1, -1);
+        if (f.ok && dv == 64 && dk == 128 && !force_bwd_dq_two_blocks()) {
+            const FusedPlan w1 = plan_fused((int)BH, T, dv, dk, levels_needed(T), -1, -1, 128);
+            if (w1.ok && w1.ndvb == 1 && w1.combo == 2) f = w1;
+        }
         if (f.ok) {
             w.fused_dq = true;
             w.fq = f;

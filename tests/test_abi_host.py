@@ -268,24 +268,37 @@ def test_bwd_workspace_bytes(lib, monkeypatch, B, H, T, dk, dv, C):
     assert lib.loglin_bwd_workspace_bytes(B, H, T, dk, dv, C, 0) == want
 
 
+def _fused_dq_layout(BH, N, T, dk, dv, nseg, LU, ncb, nsub):
+    off = _align(_align(_align(BH * nseg * dk * dv * 4) + BH * nseg * 4) + BH * nseg * 8)
+    off = _align(off + BH * nseg * dk * dv * 2)
+    if nsub > 1:  # sub-range states and totals
+        off = _align(_align(off + BH * nseg * nsub * dk * dv * 4) + BH * nseg * nsub * 4)
+    off = _align(off + ncb * BH * T * LU * 4)
+    off = _align(off + ncb * BH * T * 4)
+    off = _align(off + BH * N * 8)
+    return _bwd_tail(BH, N, T, dk, dv, off)
+
+
 def test_bwd_workspace_bytes_fused_dq(lib, monkeypatch):
     """bf16, d_v = 64: the fused dq pass's layout at the 8K workload's shape.
-    Its plan (swapped problem: d_k 64, d_v 128 in two column blocks of 64,
-    128 tiles, 64 (batch, head) pairs): segments of 32 tiles (every segment
-    length costs 64 serial tiles a compute unit; the longest wins), 4
-    segments, one sub-range each.  Segment nodes fp32 [64][4][128][64],
-    totals, fp64 ends, bf16 fragments; the dlambda parts [2][64][14][8192]
-    (positions below 8192 use levels 0..13) and the parts of q . dq [2][64][8192];
-    the fp64 chunk ends [64][128]; then R, R^T and the dot products."""
+    Its plan (swapped problem: d_k 64, d_v 128, 128 tiles, 64 (batch, head)
+    pairs): segments of 32 tiles (every segment length costs the same serial
+    tiles per compute unit; the longest wins), 4 segments, five register
+    levels and two above the segment, so the 128 columns run as one block;
+    with 64 pairs the segment states come in two sub-ranges (3 x 64 blocks
+    would leave compute units idle).  Segment nodes fp32 [64][4][128][64],
+    totals, fp64 ends, bf16 fragments, the sub-range states [64][4][2][128][64]
+    and totals; the dlambda parts [1][64][14][8192] (positions
+    below 8192 use levels 0..13) and the parts of q . dq [1][64][8192]; the
+    fp64 chunk ends [64][128]; then R, R^T and the dot products.  With
+    LOGLIN_BWD_DQ=fused64 the pass keeps two 64-column blocks: two parts
+    of each, and the segment states in one sub-range (3 x 128 blocks)."""
     monkeypatch.delenv("LOGLIN_BWD_DQ", raising=False)
     B, H, T, dk, dv, C = 4, 16, 8192, 128, 64, 64
     BH, N, nseg, LU = B * H, T // C, 4, 14
-    off = _align(_align(_align(BH * nseg * dk * dv * 4) + BH * nseg * 4) + BH * nseg * 8)
-    off = _align(off + BH * nseg * dk * dv * 2)
-    off = _align(off + 2 * BH * T * LU * 4)
-    off = _align(off + 2 * BH * T * 4)
-    off = _align(off + BH * N * 8)
-    assert lib.loglin_bwd_workspace_bytes(B, H, T, dk, dv, C, 1) == _bwd_tail(BH, N, T, dk, dv, off)
+    assert lib.loglin_bwd_workspace_bytes(B, H, T, dk, dv, C, 1) == _fused_dq_layout(BH, N, T, dk, dv, nseg, LU, 1, 2)
+    monkeypatch.setenv("LOGLIN_BWD_DQ", "fused64")
+    assert lib.loglin_bwd_workspace_bytes(B, H, T, dk, dv, C, 1) == _fused_dq_layout(BH, N, T, dk, dv, nseg, LU, 2, 1)
 
 
 def _bwd(lib, B=1, H=1, T=64, dk=16, dv=16, L=8, C=16, dtype=1, ws=FAKE * 256, nws=1 << 30,

@@ -103,15 +103,22 @@ def test_bwd_empty_is_noop():
     assert all(x.numel() == 0 for x in out)
 
 
-def test_bwd_full_8k_workload_weak_decay():
+@pytest.mark.parametrize("dq_blocks", ["one", "two"])
+def test_bwd_full_8k_workload_weak_decay(monkeypatch, dq_blocks):
     """The 8K-token workload at full size (B=4, H=16, T=8192, d_k=128, d_v=64,
     C=64, L=15), launched as the benchmark launches it, with the weak decay
     (a = -softplus(N(-8, 0.5))) so that every coarse level carries weight:
-    the last (batch, head) slice against the oracle's gradients in full."""
+    the last (batch, head) slice against the oracle's gradients in full.  The
+    dq pass runs as one block of 128 columns (the benchmark's launch) and, with
+    LOGLIN_BWD_DQ=fused64, as two 64-column blocks."""
     from log_linear_token_amd import inputs as I
 
+    if dq_blocks == "two":
+        monkeypatch.setenv("LOGLIN_BWD_DQ", "fused64")
+    else:
+        monkeypatch.delenv("LOGLIN_BWD_DQ", raising=False)
     cfg = I.CONFIGS["fwd8k"]
-    banner(f"bwd full fwd8k weak B={cfg.B} H={cfg.H} T={cfg.T} dk={cfg.dk} dv={cfg.dv} C={cfg.C}")
+    banner(f"bwd full fwd8k weak dq blocks={dq_blocks} B={cfg.B} H={cfg.H} T={cfg.T} dk={cfg.dk} dv={cfg.dv} C={cfg.C}")
     d = I.make_fwd(cfg, "weak")
     g = np.random.default_rng(cfg.seed + 5).standard_normal((cfg.B, cfg.H, cfg.T, cfg.dv)).astype(np.float32)
     dt = torch.bfloat16
