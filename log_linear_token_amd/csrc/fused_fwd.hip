@@ -558,6 +558,7 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
         }
     };
 
+    const int lane_k = lane, m16_k = m16, g_k = g;  // the body's lane indices (see there)
     auto body = [&](int il, const bf16_t* Qc, const bf16_t* Kc, const bf16_t* Vc,
                     const float* Lc, const float* Awc, const float* Ewc, const bf16_t* Qoc,
                     bf16_t* Qn, bf16_t* Kn, bf16_t* Vn, float* Ln, float* an, float* Awn,
@@ -565,6 +566,14 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
         // tile il is in LDS and every wave is done with tile il - 1
         __builtin_amdgcn_s_waitcnt(0);
         __syncthreads();
+        // one-block dq pass: the lane indices through an opaque zero, so that
+        // the body's per-lane address arithmetic is redone in place each tile
+        // instead of being hoisted out of the loop and spilled (a spill
+        // reload there makes the copying waves wait for their own copies)
+        int zv = 0;
+        if constexpr (WIDE) asm volatile("v_mov_b32 %0, 0" : "=v"(zv));
+        const int lane = WIDE ? (int)(threadIdx.x & 63) + zv : lane_k;
+        const int m16 = WIDE ? lane & 15 : m16_k, g = WIDE ? lane >> 4 : g_k;
         if constexpr (BWD) {
             if (il > 0) finish_qdq(il - 1);
         }
