@@ -39,6 +39,7 @@ constexpr int kRwSlots = 8;   // levels p < 8, i.e. at most 256 chunks
 constexpr int kRwMaxL = 32;   // lambda row length staged per token
 constexpr int kRwLogC = 6;    // 64-token chunks
 constexpr int kRwMaxM = 5;    // at most 32 chunks per segment
+constexpr int kRwCoarse = 2;  // slots of the walk that builds only the levels spanning segments
 
 // s_waitcnt with only the vector-memory counter bounded: at most N vector
 // memory operations of this wave still outstanding (expcnt, lgkmcnt at their maxima)
@@ -67,31 +68,35 @@ struct RwalkArgs {
     int ntop;       // levels p >= m that exist (nlev - m, or 0)
     int pmin;       // levels p < pmin are not built (0, or m when the dk / dv
                     // walk builds the levels inside a segment itself)
+    int pm, pnseg, pntop;  // the dk / dv walk: segment log2, count and levels of the
+                           // parts the R(j) walk left (its m, nseg, ntop)
     int lam_dma;    // lambda rows of a whole chunk are 16-byte aligned
     int a_dma;      // a of a whole chunk is 16-byte aligned
     float* part;    // [BH][nseg][ntop][dk][dv] parts of the blocks of levels >= m
                     // (nseg ntop <= N: within an fp32 [BH][N][dk][dv] region)
 };
 
-// NSLOT: levels p < NSLOT (at most 2^NSLOT chunks)
-template <int DK, int DV, int NSLOT>
-__global__ __launch_bounds__(kRwWaves * 64, 1) void k_bwd_rwalk(BwdParams p, RwalkArgs w) {
+// NSLOT: levels p < NSLOT (at most 2^NSLOT chunks); NB chunk buffers: three
+// (chunks il + 1 and il + 2 in flight while il is used, one block per compute
+// unit) or two (il + 1 in flight; 65 KB, so that two blocks share a compute
+// unit: the walk that builds only the blocks spanning segments runs twice
+// as many shorter segments)
+// COARSE: only the levels p >= pmin, all of which span segments (pmin > m):
+// slot s accumulates level pmin + s, whose set bits are those of the
+// segment's first chunk for all its chunks; with NSLOT = 2 slots the
+// accumulators fit two blocks per compute unit (four waves per SIMD, the
+// second launch bound).
+template <int DK, int DV, int NSLOT, int NB, bool COARSE>
+__global__ __launch_bounds__(kRwWaves * 64, COARSE ? 4 : 1) void k_bwd_rwalk(BwdParams p, RwalkArgs w) {
     static_assert(DV == 64 && (DK == 64 || DK == 128), "head dims of this kernel");
     static_assert(NSLOT <= kRwSlots, "one wave per level for the weights");
+    static_assert(NB == 2 || NB == 3, "chunk buffers");
+    auto lvl = [&](int s) __attribute__((always_inline)) { return COARSE ? w.pmin + s : s; };
     constexpr int NRBW = DK / 32;  // 16-row blocks of d_k per wave
-    // three chunk buffers: chunks il + 1 and il + 2 are in flight while il is used
-    __shared__ __align__(16) bf16_t sQ0[TC * DK];
-    __shared__ __align__(16) bf16_t sQ1[TC * DK];
-    __shared__ __align__(16) bf16_t sQ2[TC * DK];
-    __shared__ __align__(16) bf16_t sO0[TC * DV];
-    __shared__ __align__(16) bf16_t sO1[TC * DV];
-    __shared__ __align__(16) bf16_t sO2[TC * DV];
-    __shared__ __align__(16) float sL0[TC * kRwMaxL];
-    __shared__ __align__(16) float sL1[TC * kRwMaxL];
-    __shared__ __align__(16) float sL2[TC * kRwMaxL];
-    __shared__ __align__(16) float sa0[TC];
-    __shared__ __align__(16) float sa1[TC];
-    __shared__ __align__(16) float sa2[TC];
+    __shared__ __align__(16) bf16_t sQ[NB][TC * DK];
+    __shared__ __align__(16) bf16_t sO[NB][TC * DV];
+    __shared__ __align__(16) float sL[NB][TC * kRwMaxL];
+    __shared__ __align__(16) float sa[NB][TC];
     __shared__ __align__(16) float sW[kRwSlots][TC];  // per-token weights of each level
     // A at the end of chunks i0 - 1 .. i0 + 2^m - 1 (sCum[k]: chunk i0 - 1 + k),
     // and at the end of chunk j - 1 for the blocks of levels >= m
@@ -173,7 +178,7 @@ __global__ __launch_bounds__(kRwWaves * 64, 1) void k_bwd_rwalk(BwdParams p, Rwa
     // would make the compiler wait for every copy in flight
     for (int k = threadIdx.x; k <= ntl; k += kRwWaves * 64)
         sCum[k] = i0 + k >= 1 ? cum[i0 - 1 + k] : 0.0;
-    if (threadIdx.x < NSLOT) {
+    if (threadIdx.x < kRwSlots) {
         const int pl = threadIdx.x;
         const int j = (i0 >> pl) << pl;
         sTop[pl] = (pl >= w.m && pl < nlev && ((i0 >> pl) & 1)) ? cum[j - 1] : 0.0;
@@ -192,6 +197,7 @@ __global__ __launch_bounds__(kRwWaves * 64, 1) void k_bwd_rwalk(BwdParams p, Rwa
     // so that these stores are older than the copies the next wait is for.
     // Lane (m16, g) holds R[d0 + 16 rb + m16][c0 + 4g .. c0 + 4g + 3].
     auto flush = [&](int i) __attribute__((always_inline)) {
+        if constexpr (COARSE) return;
 #pragma unroll
         for (int pl = 0; pl < NSLOT; ++pl) {
             if (pl >= w.pmin && pl < w.m && pl < nlev && ((i >> pl) & 1)) {
@@ -216,23 +222,29 @@ __global__ __launch_bounds__(kRwWaves * 64, 1) void k_bwd_rwalk(BwdParams p, Rwa
         // this wave's copies of chunk il have landed (at least KMIN copies of
         // il + 1, issued after them, may still be in flight); after the
         // barrier every wave's have, and every wave is done with chunk il - 1
-        if (il + 1 < ntl) wait_vm<KMIN>();
-        else wait_vm<0>();
+        if constexpr (NB == 3) {
+            if (il + 1 < ntl) wait_vm<KMIN>();
+            else wait_vm<0>();
+        } else {
+            wait_vm<0>();
+        }
         __syncthreads();
         const int i = i0 + il;
         if (il > 0) flush(i - 1);
-        if (il + 2 < ntl) issue(il + 2, Qn2, On2, Ln2, an2);
+        // the next copies go to the buffer every wave has finished with: that
+        // of chunk il - 1 (three buffers: chunk il + 2; two: chunk il + 1)
+        if (il + NB - 1 < ntl) issue(il + NB - 1, Qn2, On2, Ln2, an2);
         const int nvalid = min(TC, T - i * TC);
         {
             // wave pl: the weights of level pl for the chunk's 64 tokens,
             // lambda_t^(log2 C + pl + 1) e^(A_t - A(end of chunk j - 1))
-            const int pl = wave;
+            const int pl = wave, lv = lvl(pl);
             const float x = wave_inclusive_sum(ac[lane]);  // A_t - A(end of chunk i - 1)
-            if (pl < NSLOT && pl >= w.pmin && pl < nlev && ((i >> pl) & 1)) {
-                const int j = (i >> pl) << pl;
-                const double cj = pl < w.m ? sCum[j - i0] : sTop[pl];
+            if (pl < NSLOT && lv >= w.pmin && lv < nlev && ((i >> lv) & 1)) {
+                const int j = (i >> lv) << lv;
+                const double cj = lv < w.m ? sCum[j - i0] : sTop[lv];
                 const float base = (float)(sCum[i - i0] - cj);
-                const float lam = Lc[lane * L + kRwLogC + pl + 1];
+                const float lam = Lc[lane * L + kRwLogC + lv + 1];
                 sW[pl][lane] = lane < nvalid ? lam * __expf(x + base) : 0.f;
             }
         }
@@ -247,7 +259,8 @@ __global__ __launch_bounds__(kRwWaves * 64, 1) void k_bwd_rwalk(BwdParams p, Rwa
             for (int rb = 0; rb < NRBW; ++rb) bq[rb] = ld_tr8<DK>(Qc, 32 * ks, d0 + 16 * rb);
 #pragma unroll
             for (int pl = 0; pl < NSLOT; ++pl) {
-                if (pl >= w.pmin && pl < nlev && ((i >> pl) & 1)) {
+                const int lv = lvl(pl);
+                if (lv >= w.pmin && lv < nlev && ((i >> lv) & 1)) {
                     const float4 w0 = *reinterpret_cast<const float4*>(&sW[pl][32 * ks + 8 * g]);
                     const float4 w1 = *reinterpret_cast<const float4*>(&sW[pl][32 * ks + 8 * g + 4]);
                     const bf16x8 sc = scale8(ao, w0, w1);
@@ -258,19 +271,29 @@ __global__ __launch_bounds__(kRwWaves * 64, 1) void k_bwd_rwalk(BwdParams p, Rwa
         }
     };
 
-    issue(0, sQ0, sO0, sL0, sa0);
-    if (ntl > 1) issue(1, sQ1, sO1, sL1, sa1);
-    for (int il = 0; il < ntl; il += 3) {
-        body(il, sQ0, sO0, sL0, sa0, sQ2, sO2, sL2, sa2);
-        if (il + 1 < ntl) body(il + 1, sQ1, sO1, sL1, sa1, sQ0, sO0, sL0, sa0);
-        if (il + 2 < ntl) body(il + 2, sQ2, sO2, sL2, sa2, sQ1, sO1, sL1, sa1);
+    if constexpr (NB == 3) {
+        issue(0, sQ[0], sO[0], sL[0], sa[0]);
+        if (ntl > 1) issue(1, sQ[1], sO[1], sL[1], sa[1]);
+        for (int il = 0; il < ntl; il += 3) {
+            body(il, sQ[0], sO[0], sL[0], sa[0], sQ[NB - 1], sO[NB - 1], sL[NB - 1], sa[NB - 1]);
+            if (il + 1 < ntl) body(il + 1, sQ[1], sO[1], sL[1], sa[1], sQ[0], sO[0], sL[0], sa[0]);
+            if (il + 2 < ntl)
+                body(il + 2, sQ[NB - 1], sO[NB - 1], sL[NB - 1], sa[NB - 1], sQ[1], sO[1], sL[1], sa[1]);
+        }
+    } else {
+        issue(0, sQ[0], sO[0], sL[0], sa[0]);
+        for (int il = 0; il < ntl; il += 2) {
+            body(il, sQ[0], sO[0], sL[0], sa[0], sQ[1], sO[1], sL[1], sa[1]);
+            if (il + 1 < ntl) body(il + 1, sQ[1], sO[1], sL[1], sa[1], sQ[0], sO[0], sL[0], sa[0]);
+        }
     }
     flush(i0 + ntl - 1);
     // this segment's parts of the blocks of levels >= m that it belongs to
 #pragma unroll
     for (int pl = 0; pl < NSLOT; ++pl) {
-        if (pl >= w.m && pl < nlev && ((i0 >> pl) & 1)) {
-            float* dst = w.part + (((size_t)bh * w.nseg + seg) * w.ntop + (pl - w.m)) * DK * DV;
+        const int lv = lvl(pl);
+        if (lv >= w.m && lv >= w.pmin && lv < nlev && ((i0 >> lv) & 1)) {
+            float* dst = w.part + (((size_t)bh * w.nseg + seg) * w.ntop + (lv - w.m)) * DK * DV;
 #pragma unroll
             for (int rb = 0; rb < NRBW; ++rb)
                 *reinterpret_cast<f32x4*>(dst + (size_t)(d0 + 16 * rb + m16) * DV + c0 + 4 * g) = acc[pl][rb];
@@ -444,6 +467,11 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_kvwalk(BwdParams p, Rw
         }
     };
 
+    // the walk's first chunk (the segment's last) is requested before the
+    // prologue's own loads, so that their latencies overlap
+#pragma unroll
+    for (int part = 0; part < 4; ++part) issue(ntl - 1, (ntl - 1) & 1, part);
+
     // the blocks of levels >= m after the segment, combined at its end: this
     // lane's share, d_k row 16 w + n16, d_v 32 ks + 8 g + (0..7).  Each such
     // block is the sum of the fp32 parts the R(j) walk left for the segments
@@ -459,19 +487,32 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_kvwalk(BwdParams p, Rw
         if (((i0 >> pl) & 1) || j >= N) continue;
         coarse = true;
         const float wt = __expf((float)(cum[j - 1] - cum[i0 + ntl - 1]));
-        const int s0 = j >> w.m, s1 = min(s0 + (1 << (pl - w.m)), w.nseg);
-        for (int sg = s0; sg < s1; ++sg) {
-            const float* R = w.part + (((size_t)bh * w.nseg + sg) * w.ntop + (pl - w.m)) * DK * DV +
-                             (size_t)(16 * wave + n16) * DV + 8 * g;
+        const int s0 = j >> w.pm, s1 = min(s0 + (1 << (pl - w.pm)), w.pnseg);
+        // four parts' loads in flight at once (past the last part: the last
+        // one again, weighted zero)
+        for (int sb = s0; sb < s1; sb += 4) {
+            f32x4 x[4][2][2];
 #pragma unroll
-            for (int ks = 0; ks < 2; ++ks) {
-                const f32x4 x0 = *reinterpret_cast<const f32x4*>(R + 32 * ks);
-                const f32x4 x1 = *reinterpret_cast<const f32x4*>(R + 32 * ks + 4);
+            for (int u = 0; u < 4; ++u) {
+                const int sg = min(sb + u, s1 - 1);
+                const float* R = w.part + (((size_t)bh * w.pnseg + sg) * w.pntop + (pl - w.pm)) * DK * DV +
+                                 (size_t)(16 * wave + n16) * DV + 8 * g;
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    nc[ks][0][e] += wt * x0[e];
-                    nc[ks][1][e] += wt * x1[e];
+                for (int ks = 0; ks < 2; ++ks) {
+                    x[u][ks][0] = *reinterpret_cast<const f32x4*>(R + 32 * ks);
+                    x[u][ks][1] = *reinterpret_cast<const f32x4*>(R + 32 * ks + 4);
                 }
+            }
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const float wu = sb + u < s1 ? wt : 0.f;
+#pragma unroll
+                for (int ks = 0; ks < 2; ++ks)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        nc[ks][0][e] += wu * x[u][ks][0][e];
+                        nc[ks][1][e] += wu * x[u][ks][1][e];
+                    }
             }
         }
     }
@@ -532,8 +573,6 @@ __global__ __launch_bounds__(kKvWaves * 64, 1) void k_bwd_kvwalk(BwdParams p, Rw
         }
     };
 
-#pragma unroll
-    for (int part = 0; part < 4; ++part) issue(ntl - 1, (ntl - 1) & 1, part);
     for (int il = ntl - 1; il >= 0; --il) {
         const int cur = il & 1;
         wait_vm<0>();
@@ -754,10 +793,15 @@ bool kvwalk_applies(const BwdParams& p, const RwalkArgs& w) {
 
 template <int DK>
 hipError_t launch_rwalk_dk(const BwdParams& p, const RwalkArgs& w, hipStream_t stream) {
-    if (p.nlev <= 7)
-        hipLaunchKernelGGL((k_bwd_rwalk<DK, 64, 7>), dim3(p.BH * w.nseg), dim3(kRwWaves * 64), 0, stream, p, w);
+    if (w.pmin > w.m)  // the spanning levels alone, segments shorter than the dk / dv walk's
+        hipLaunchKernelGGL((k_bwd_rwalk<DK, 64, kRwCoarse, 2, true>), dim3(p.BH * w.nseg), dim3(kRwWaves * 64),
+                           0, stream, p, w);
+    else if (p.nlev <= 7)
+        hipLaunchKernelGGL((k_bwd_rwalk<DK, 64, 7, 3, false>), dim3(p.BH * w.nseg), dim3(kRwWaves * 64), 0,
+                           stream, p, w);
     else
-        hipLaunchKernelGGL((k_bwd_rwalk<DK, 64, 8>), dim3(p.BH * w.nseg), dim3(kRwWaves * 64), 0, stream, p, w);
+        hipLaunchKernelGGL((k_bwd_rwalk<DK, 64, 8, 3, false>), dim3(p.BH * w.nseg), dim3(kRwWaves * 64), 0,
+                           stream, p, w);
     // (with pmin = m the dk / dv walk sums the parts of the blocks itself)
     if (w.ntop > 0 && w.pmin < w.m) {
         long nj = 0;
@@ -797,6 +841,26 @@ bool rwalk_plan(const BwdParams& p, RwalkArgs& w) {
 }
 }  // namespace
 
+// The R(j) walk that leaves only the parts of the blocks of levels >= m of
+// the dk / dv walk (w: that walk's plan): segments of 2^(m-1) chunks where
+// those levels fit the coarse kernel's slots and the parts their region (two
+// blocks per compute unit, twice the blocks), else the dk / dv walk's own.
+RwalkArgs coarse_plan(const BwdParams& p, const RwalkArgs& w) {
+    RwalkArgs r = w;
+    r.pmin = w.m;
+    const int mr = w.m - 1;
+    if (mr >= 2 && p.nlev - w.m <= kRwCoarse) {
+        const int nseg = (p.N + (1 << mr) - 1) >> mr;
+        const int ntop = p.nlev - mr;
+        if ((long)nseg * ntop <= p.N) {
+            r.m = mr;
+            r.nseg = nseg;
+            r.ntop = ntop;
+        }
+    }
+    return r;
+}
+
 bool bwd_rwalk_applies(const BwdParams& p) {
     RwalkArgs w{};
     return rwalk_plan(p, w);
@@ -810,13 +874,18 @@ bool bwd_kvwalk_applies(const BwdParams& p) {
 hipError_t launch_bwd_rwalk(const BwdParams& p, bool coarse_only, hipStream_t stream) {
     RwalkArgs w{};
     if (!rwalk_plan(p, w)) return hipErrorInvalidValue;
-    w.pmin = coarse_only ? w.m : 0;
+    w.pmin = 0;
+    if (coarse_only) w = coarse_plan(p, w);
     return p.dk == 128 ? launch_rwalk_dk<128>(p, w, stream) : launch_rwalk_dk<64>(p, w, stream);
 }
 
 hipError_t launch_bwd_kvwalk(const BwdParams& p, hipStream_t stream) {
     RwalkArgs w{};
     if (!rwalk_plan(p, w) || !kvwalk_applies(p, w)) return hipErrorInvalidValue;
+    const RwalkArgs r = coarse_plan(p, w);
+    w.pm = r.m;
+    w.pnseg = r.nseg;
+    w.pntop = r.ntop;
     hipLaunchKernelGGL((k_bwd_kvwalk<128, 64>), dim3(p.BH * w.nseg), dim3(kKvWaves * 64), 0, stream, p, w);
     return hipGetLastError();
 }

@@ -200,3 +200,26 @@ def test_bwd_dkv_paths(monkeypatch, mode, B, H, T, mu):
         monkeypatch.delenv("LOGLIN_BWD_DKV", raising=False)
     banner(f"bwd dk/dv {mode} B={B} H={H} T={T} mu={mu}")
     _check(B, H, T, 128, 64, 64, torch.bfloat16, seed=T + 1, mu=mu)
+
+
+def test_bwd_many_heads_coarse_walk():
+    """64 (batch, head) pairs of 4096 tokens (B=4, H=16, d_k=128, d_v=64,
+    C=64, weak decay): the dk / dv walk runs 16-chunk segments and the R(j)
+    walk builds only the two levels spanning them, in 8-chunk segments of
+    its own (two blocks per compute unit), whose parts the dk / dv walk sums.
+    The first and the last (batch, head) slices against the oracle."""
+    B, H, T, dk, dv, C = 4, 16, 4096, 128, 64, 64
+    L = (T - 1).bit_length() + 1
+    banner(f"bwd coarse walk B={B} H={H} T={T}")
+    q, k, v, a, lam, g = _inputs(B, H, T, dk, dv, L, seed=41, mu=-8.0)
+    dt = torch.bfloat16
+    got = LL.loglin_bwd_chunked(to_dev(q, dt), to_dev(k, dt), to_dev(v, dt), to_dev(a), to_dev(lam),
+                                to_dev(g, dt), C)
+    torch.cuda.synchronize()
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        sl = lambda x: x[b, h][None, None]
+        want = ref.form_a_grads(*(_round(sl(x), dt) for x in (q, k, v)), sl(a), sl(lam), _round(sl(g), dt))
+        errs = {n: slice_rel_err(x[b, h][None, None].cpu().numpy(), y, 2) for n, x, y in zip(NAMES, got, want)}
+        print("  " + " ".join(f"{n} {e:.2e}" for n, e in errs.items()), flush=True)
+        for n, e in errs.items():
+            assert e <= TOL_BF16, (n, b, h, e)
