@@ -336,6 +336,8 @@ template <int DK, int NW, int NH, int MLOC, int TOPMAX, bool BWD>
 __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
     typedef HD<DK> H;
     constexpr int NWT = NW * NH;            // waves per block
+    // the backward's dq pass as one block of 128 columns (one wave per slab)
+    constexpr bool WIDE = BWD && NH == 1 && NWT == 8;
     constexpr int DVW = NW * 16;
     constexpr int NKSH = H::NKS / NH;       // contraction steps of this wave's head-dim part
     constexpr int NDTH = H::NDT / NH;       // 16-row state blocks of this wave's part
@@ -373,6 +375,9 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
     // waves after the next tile's first barrier (q . dq from the dq this
     // pass writes, the rounding the dk / dv stage sees as well)
     __shared__ __align__(16) float sDq[BWD ? 2 * NWT * TC : 4];
+    // one-block dq pass writing dlambda rows: the tile's [token][L] block, by
+    // tile parity, stored after the next tile's first barrier
+    __shared__ __align__(16) float sGl[WIDE ? 2 * TC * kFusedMaxL : 4];
     // sX slots hold the 64 lanes of a C-layout fragment; lane l of slab cs is
     // stored at l ^ ((l / 16 + 4 (cs & 1)) & 7), so that the whole-row reads
     // of the finishers (eight lanes over two slabs and four lane groups per
@@ -427,7 +432,6 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
     // The dq pass as one block of 128 columns (one wave per 16-column slab,
     // NH = 1): its V and q tiles are 16 KB each, so waves 0-3 copy those,
     // lambda and a, and waves 4-7 Q and K; every wave stores its own rows.
-    constexpr bool WIDE = BWD && NH == 1 && NWT == 8;
     constexpr int NIW = NWT == 8 ? 4 : NWT;      // Q/K copies and stores
     const bool issuer = wave >= NWT - NIW;
     const int iw = issuer ? wave - (NWT - NIW) : 0;
@@ -554,6 +558,15 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
 #pragma unroll
                 for (int u = 0; u < NWT; ++u) x += sDq[((il & 1) * NWT + u) * TC + t];
                 p.dqd[((size_t)dvb * p.BH + bh) * p.T + t0 + t] = x;
+            }
+            if constexpr (WIDE) {
+                // the tile's dlambda rows: nvalid x L consecutive floats
+                if (p.dlam_rows) {
+                    const int n = min(TC, p.T - t0) * p.L;
+                    float* dst = p.dlam_rows + ((size_t)bh * p.T + t0) * p.L;
+                    const float* src = sGl + (il & 1) * TC * kFusedMaxL;
+                    for (int x = threadIdx.x; x < n; x += NWT * 64) dst[x] = src[x];
+                }
             }
         }
     };
@@ -706,9 +719,12 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
             // products (summed over the waves' parts, times e^(A_t))
             const int t = lane, rb = t >> 4, mm = t & 15;
             float* dst = p.dlp + ((size_t)dvb * p.BH + bh) * (size_t)p.LU * p.T + (size_t)i * TC + t;
-            for (int l = wave; l < p.LU; l += NWT) {
+            // (written as rows: every level of the row, zero past LU)
+            const int lend = WIDE && p.dlam_rows ? p.L : p.LU;
+            for (int l = wave; l < lend; l += NWT) {
                 float val = 0.f;
-                if (l <= 4) {
+                if (l >= p.LU) {
+                } else if (l <= 4) {
                     val = sDd[(rb * 5 + l) * 16 + mm];
                 } else if (l == 5) {
                     if (rb & 1) val = sDi[(rb * (rb + 1) / 2 + rb - 1) * 16 + mm];
@@ -729,7 +745,12 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
                         val = x * __expf(Awc[t]);
                     }
                 }
-                if (t < nvalid) dst[(size_t)l * p.T] = val;
+                if constexpr (WIDE) {
+                    if (p.dlam_rows) sGl[(il & 1) * TC * kFusedMaxL + t * p.L + l] = val;
+                    else if (t < nvalid) dst[(size_t)l * p.T] = val;
+                } else {
+                    if (t < nvalid) dst[(size_t)l * p.T] = val;
+                }
             }
         }
 

@@ -67,6 +67,10 @@ struct FusedParams {
     const bf16_t_storage* qo;
     float* dlp;
     float* dqd;                     // [ndvb][BH][T] each column block's part of q_t . dq_t
+    // one-block dq pass (ndvb = 1, L <= kFusedMaxL): dlambda written here as
+    // whole [BH][T][L] rows (levels past LU zero) instead of dlp, and dqd is
+    // then q_t . dq_t itself; nullptr otherwise
+    float* dlam_rows;
 };
 struct FusedPlan {
     int ok, m, nseg, ntop, dvw, ndvb, ntiles, combo, msub;

@@ -163,7 +163,7 @@ hipError_t launch_fused_path(const FusedPlan& f, const FwdWorkspace& w, char* ba
                              const float* lambda, float* out, long BH, int T, int dk, int dv,
                              int L, int C, unsigned stage_mask, hipStream_t hs,
                              const void* qo = nullptr, float* dlp = nullptr,
-                             float* dqd = nullptr) {
+                             float* dqd = nullptr, float* dlam_rows = nullptr) {
     FwdParams p{};
     p.q = q;
     p.k = k;
@@ -218,6 +218,7 @@ hipError_t launch_fused_path(const FusedPlan& f, const FwdWorkspace& w, char* ba
     fp.qo = static_cast<const bf16_t_storage*>(qo);
     fp.dlp = dlp;
     fp.dqd = dqd;
+    fp.dlam_rows = dlam_rows;
     if (w.total > 0) {
         p.gfrag = reinterpret_cast<bf16_t_storage*>(base + w.frag_off);
         fp.gfrag = p.gfrag;
@@ -628,11 +629,18 @@ loglin_status loglin_bwd_chunked(const void* q, const void* k, const void* v, co
         // their sums
         float* dlp = reinterpret_cast<float*>(base + w.dlp_off);
         float* dqd = reinterpret_cast<float*>(base + w.dqd_off);
+        // the one-block (128-column) pass with lambda rows that fit its LDS
+        // tile writes dlambda rows and q . dq (dA1) itself; else the column
+        // blocks' parts are summed and transposed by the dlambda kernel
+        const bool rows = w.fq.dvw == 128 && L <= kFusedMaxL;
         hipError_t e = launch_fused_path(w.fq, w.nodes, base, dout, v, k, log_decay, lambda, dq, BH, T,
-                                         dv, dk, L, C, kStageAll, hs, q, dlp, dqd);
+                                         dv, dk, L, C, kStageAll, hs, q, dlp, rows ? bp.dA1 : dqd,
+                                         rows ? dlambda : nullptr);
         if (e != hipSuccess) return hip_fail(e, "loglin_bwd_chunked dq launch");
-        e = launch_bwd_dlam_sum(bp, dlp, dqd, w.fq.ndvb, levels_needed(T), hs);
-        if (e != hipSuccess) return hip_fail(e, "loglin_bwd_chunked dlambda launch");
+        if (!rows) {
+            e = launch_bwd_dlam_sum(bp, dlp, dqd, w.fq.ndvb, levels_needed(T), hs);
+            if (e != hipSuccess) return hip_fail(e, "loglin_bwd_chunked dlambda launch");
+        }
         bp.dq_done = 1;
         if (N > 1) {
             bp.cum = reinterpret_cast<double*>(base + w.ccum_off);
