@@ -559,14 +559,23 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
                 for (int u = 0; u < NWT; ++u) x += sDq[((il & 1) * NWT + u) * TC + t];
                 p.dqd[((size_t)dvb * p.BH + bh) * p.T + t0 + t] = x;
             }
-            if constexpr (WIDE) {
-                // the tile's dlambda rows: nvalid x L consecutive floats
-                if (p.dlam_rows) {
-                    const int n = min(TC, p.T - t0) * p.L;
-                    float* dst = p.dlam_rows + ((size_t)bh * p.T + t0) * p.L;
-                    const float* src = sGl + (il & 1) * TC * kFusedMaxL;
-                    for (int x = threadIdx.x; x < n; x += NWT * 64) dst[x] = src[x];
-                }
+        }
+    };
+    // one-block dq pass: the dlambda rows of tile il of the segment, nvalid x
+    // L consecutive floats
+    auto store_rows = [&](int il) __attribute__((always_inline)) {
+        if constexpr (WIDE) {
+            if (p.dlam_rows) {
+                const int t0 = (tile0 + il) * TC;
+                const int n = min(TC, p.T - t0) * p.L;
+                float* dst = p.dlam_rows + ((size_t)bh * p.T + t0) * p.L;
+                const float* src = sGl + (il & 1) * TC * kFusedMaxL;
+                // 16-byte stores where the rows start on 16 bytes (t0 is a
+                // multiple of 64, so T L % 4 == 0 decides it)
+                const int n4 = (p.T * p.L) % 4 == 0 ? n >> 2 : 0;
+                for (int x = threadIdx.x; x < n4; x += NWT * 64)
+                    reinterpret_cast<f32x4*>(dst)[x] = reinterpret_cast<const f32x4*>(src)[x];
+                for (int x = 4 * n4 + threadIdx.x; x < n; x += NWT * 64) dst[x] = src[x];
             }
         }
     };
@@ -589,6 +598,7 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
         const int m16 = WIDE ? lane & 15 : m16_k, g = WIDE ? lane >> 4 : g_k;
         if constexpr (BWD) {
             if (il > 0) finish_qdq(il - 1);
+            if (il > 0) store_rows(il - 1);
         }
         if constexpr (NH > 1) {
             if (finisher && !issuer && prev_tile >= 0) finish_prev();
@@ -719,12 +729,10 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
             // products (summed over the waves' parts, times e^(A_t))
             const int t = lane, rb = t >> 4, mm = t & 15;
             float* dst = p.dlp + ((size_t)dvb * p.BH + bh) * (size_t)p.LU * p.T + (size_t)i * TC + t;
-            // (written as rows: every level of the row, zero past LU)
-            const int lend = WIDE && p.dlam_rows ? p.L : p.LU;
-            for (int l = wave; l < lend; l += NWT) {
+            // (written as rows: the levels past LU stay zero from the start)
+            for (int l = wave; l < p.LU; l += NWT) {
                 float val = 0.f;
-                if (l >= p.LU) {
-                } else if (l <= 4) {
+                if (l <= 4) {
                     val = sDd[(rb * 5 + l) * 16 + mm];
                 } else if (l == 5) {
                     if (rb & 1) val = sDi[(rb * (rb + 1) / 2 + rb - 1) * 16 + mm];
@@ -851,6 +859,11 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
         }
     };
 
+    if constexpr (WIDE) {
+        // dlambda rows: levels LU..L-1 of every staged row are zero
+        if (p.dlam_rows)
+            for (int x = threadIdx.x; x < 2 * TC * kFusedMaxL; x += NWT * 64) sGl[x] = 0.f;
+    }
     if (issuer) issue(0, 0, sQ0, sK0, sV0, sL0, sa0, sQo0);
     if (issuer1) issue(0, 1, sQ0, sK0, sV0, sL0, sa0, sQo0);
     if (dwave) {
@@ -867,7 +880,10 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
         if constexpr (NH > 1) {
             if (finisher) finish_prev();
         }
-        if constexpr (BWD) finish_qdq(ntl - 1);
+        if constexpr (BWD) {
+            finish_qdq(ntl - 1);
+            store_rows(ntl - 1);
+        }
     }
 }
 
