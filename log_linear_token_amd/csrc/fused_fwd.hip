@@ -217,9 +217,10 @@ __device__ __forceinline__ void scores_for_wave(int wave, const bf16_t* Qs, cons
 
 // ---------------------------------------------------------------------------
 // Segment states: for each (bh, segment except the last, column block) the
-// decayed sum of k v^T over the segment, fp32 [d_v][d_k] at the segment's end.
+// decayed sum of k v^T over the segment, fp32 [d_v][d_k] at the segment's end
+// (TR: stored as [d_k][d_v], the state of the problem with k and v swapped).
 
-template <int DK, int NW>
+template <int DK, int NW, bool TR = false>
 __global__ __launch_bounds__(NW * 64) void k_seg_state(FusedParams p) {
     constexpr int DVW = NW * 16;
     constexpr int NDT = DK / 16;
@@ -313,8 +314,13 @@ __global__ __launch_bounds__(NW * 64) void k_seg_state(FusedParams p) {
     for (int kt = 0; kt < NDT; ++kt) {
         // row of u[kt] (see tile_state): 32 (kt / 2) + 8g + 4 (kt % 2), or 4g for d_k = 16
         const int row = DK >= 32 ? 32 * (kt / 2) + 8 * g + 4 * (kt % 2) : 4 * g;
-        *reinterpret_cast<float4*>(dst + (size_t)c * DK + row) =
-            make_float4(u[kt][0], u[kt][1], u[kt][2], u[kt][3]);
+        if constexpr (TR) {
+#pragma unroll
+            for (int r = 0; r < 4; ++r) dst[(size_t)(row + r) * p.dv + c] = u[kt][r];
+        } else {
+            *reinterpret_cast<float4*>(dst + (size_t)c * DK + row) =
+                make_float4(u[kt][0], u[kt][1], u[kt][2], u[kt][3]);
+        }
     }
     if (threadIdx.x == 0 && dvb == 0) (nsub == 1 ? p.stot : p.tpart)[slot] = total;
 }
@@ -1001,7 +1007,21 @@ hipError_t launch_fused_t(const FusedParams& p, const FwdParams& scan, unsigned 
     hipError_t err;
     if (p.nseg > 1 && (stages & kStageChunkState)) {
         const unsigned nblk = (unsigned)p.BH * (p.nseg - 1) * (1u << (p.m - p.msub)) * p.ndvb;
-        hipLaunchKernelGGL((k_seg_state<DK, NW>), dim3(nblk), dim3(NW * 64), 0, stream, p);
+        if constexpr (DK == 64 && NW == 8) {
+            // the one-block dq pass (keys v, d_k' = 64; values k, 128 columns):
+            // its states sum v k^T, the transpose of the forward's k v^T over
+            // the same segments, so the forward's kernel (keys k, values v in
+            // one 64-column block) builds them and stores them transposed;
+            // the scan over them is elementwise
+            FusedParams sp = p;
+            sp.k = p.v;
+            sp.v = p.k;
+            sp.dv = 64;
+            sp.ndvb = 1;
+            hipLaunchKernelGGL((k_seg_state<128, 4, true>), dim3(nblk), dim3(4 * 64), 0, stream, sp);
+        } else {
+            hipLaunchKernelGGL((k_seg_state<DK, NW>), dim3(nblk), dim3(NW * 64), 0, stream, p);
+        }
         err = hipGetLastError();
         if (err != hipSuccess) return err;
     }
