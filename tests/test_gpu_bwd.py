@@ -202,6 +202,31 @@ def test_bwd_dkv_paths(monkeypatch, mode, B, H, T, mu):
     _check(B, H, T, 128, 64, 64, torch.bfloat16, seed=T + 1, mu=mu)
 
 
+def test_bwd_one_block_dq_ragged_rows():
+    """The one-block dq pass (64 (batch, head) pairs, so that its plan takes
+    segments of 16 tiles) on a ragged sequence: T = 4095 leaves 63 tokens in
+    the last tile, and L = 15 levels against the 13 the sequence uses makes
+    T L odd (the dlambda rows go out with 4-byte stores from unaligned
+    starts) and leaves two levels whose gradient must be exactly zero.  The
+    first and the last (batch, head) slices against the oracle."""
+    B, H, T, dk, dv, C, L = 4, 16, 4095, 128, 64, 64, 15
+    banner(f"bwd one-block dq ragged B={B} H={H} T={T} L={L}")
+    q, k, v, a, lam, g = _inputs(B, H, T, dk, dv, L, seed=43, mu=-3.0)
+    dt = torch.bfloat16
+    got = LL.loglin_bwd_chunked(to_dev(q, dt), to_dev(k, dt), to_dev(v, dt), to_dev(a), to_dev(lam),
+                                to_dev(g, dt), C)
+    torch.cuda.synchronize()
+    lu = (T - 1).bit_length() + 1
+    assert not got[4][..., lu:].any().item()
+    for b, h in ((0, 0), (B - 1, H - 1)):
+        sl = lambda x: x[b, h][None, None]
+        want = ref.form_a_grads(*(_round(sl(x), dt) for x in (q, k, v)), sl(a), sl(lam), _round(sl(g), dt))
+        errs = {n: slice_rel_err(x[b, h][None, None].cpu().numpy(), y, 2) for n, x, y in zip(NAMES, got, want)}
+        print("  " + " ".join(f"{n} {e:.2e}" for n, e in errs.items()), flush=True)
+        for n, e in errs.items():
+            assert e <= TOL_BF16, (n, b, h, e)
+
+
 def test_bwd_many_heads_coarse_walk():
     """64 (batch, head) pairs of 4096 tokens (B=4, H=16, d_k=128, d_v=64,
     C=64, weak decay): the dk / dv walk runs 16-chunk segments and the R(j)
