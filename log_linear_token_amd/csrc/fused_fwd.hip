@@ -576,9 +576,11 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
                 const int n = min(TC, p.T - t0) * p.L;
                 float* dst = p.dlam_rows + ((size_t)bh * p.T + t0) * p.L;
                 const float* src = sGl + (il & 1) * TC * kFusedMaxL;
-                // 16-byte stores where the rows start on 16 bytes (t0 is a
-                // multiple of 64, so T L % 4 == 0 decides it)
-                const int n4 = (p.T * p.L) % 4 == 0 ? n >> 2 : 0;
+                // 16-byte stores where the rows start on 16 bytes: the
+                // output on 16 bytes and T L % 4 == 0 (t0 is a multiple of 64)
+                const bool al16 = (reinterpret_cast<uintptr_t>(p.dlam_rows) & 15) == 0 &&
+                                  ((long)p.T * p.L) % 4 == 0;
+                const int n4 = al16 ? n >> 2 : 0;
                 for (int x = threadIdx.x; x < n4; x += NWT * 64)
                     reinterpret_cast<f32x4*>(dst)[x] = reinterpret_cast<const f32x4*>(src)[x];
                 for (int x = 4 * n4 + threadIdx.x; x < n; x += NWT * 64) dst[x] = src[x];

@@ -227,6 +227,32 @@ def test_bwd_one_block_dq_ragged_rows():
             assert e <= TOL_BF16, (n, b, h, e)
 
 
+def test_bwd_unaligned_gradient_outputs():
+    """dlambda and dlog_decay may start anywhere on 4 bytes: the one-block dq
+    pass (64 (batch, head) pairs, T = 4096, T L a multiple of 4) then writes
+    the dlambda rows with 4-byte stores.  The gradients are bitwise those of
+    a call with 16-byte aligned outputs."""
+    B, H, T, dk, dv, C = 4, 16, 4096, 128, 64, 64
+    L = (T - 1).bit_length() + 1
+    banner(f"bwd unaligned dlambda B={B} H={H} T={T} L={L}")
+    q, k, v, a, lam, g = _inputs(B, H, T, dk, dv, L, seed=47, mu=-3.0)
+    dt = torch.bfloat16
+    args = (to_dev(q, dt), to_dev(k, dt), to_dev(v, dt), to_dev(a), to_dev(lam), to_dev(g, dt), C)
+    want = LL.loglin_bwd_chunked(*args)
+    dev = want[0].device
+    shapes = [x.shape for x in want]
+    grads = [torch.full(sh, float("nan"), dtype=torch.float32, device=dev) for sh in shapes[:3]]
+    for sh in shapes[3:]:
+        n = int(np.prod(sh))
+        buf = torch.full((n + 1,), float("nan"), dtype=torch.float32, device=dev)
+        grads.append(buf[1:].view(sh))
+    assert grads[4].data_ptr() % 16 == 4 and grads[3].data_ptr() % 16 == 4
+    got = LL.loglin_bwd_chunked(*args, grads=tuple(grads))
+    torch.cuda.synchronize()
+    for n, x, y in zip(NAMES, got, want):
+        assert torch.equal(x, y), n
+
+
 def test_bwd_many_heads_coarse_walk():
     """64 (batch, head) pairs of 4096 tokens (B=4, H=16, d_k=128, d_v=64,
     C=64, weak decay): the dk / dv walk runs 16-chunk segments and the R(j)
