@@ -254,10 +254,13 @@ LOGLIN_API size_t loglin_bwd_workspace_bytes(int B, int H, int T, int dk, int dv
  *   workspace  device buffer of at least loglin_bwd_workspace_bytes(...)
  *              bytes, 256-byte aligned; contents on entry ignored, on
  *              return unspecified
- * q, k, v, dout, dq, dk_out and dv_out must be 16-byte aligned.  B, H or T
+ * q, k, v, dout, dq, dk_out and dv_out must be 16-byte aligned; log_decay,
+ * lambda, dlog_decay and dlambda need only 4-byte alignment.  B, H or T
  * equal to 0 is a no-op.  Errors as for loglin_fwd_chunked; nothing is
  * launched when an argument is rejected.  Numerics: bf16 in_dtype feeds
- * bf16 matrix cores (16-deep steps) with fp32 accumulation, the carried
+ * bf16 matrix cores with fp32 accumulation (32-deep steps in the fused dq
+ * pass and the two walks, which cover C = 64, d_k = 128, d_v = 64; 16-deep
+ * in the block-per-chunk kernels that serve the other shapes), the carried
  * states and the masked score tiles rounded to bf16 as operands; the decay
  * gradient's suffix sums run in fp64.
  */
