@@ -74,32 +74,59 @@ __global__ __launch_bounds__(NW * 64) void k_prefill_job(PrefillParams p) {
     const bf16_t* kg = reinterpret_cast<const bf16_t*>(p.k);
     const bf16_t* vg = reinterpret_cast<const bf16_t*>(p.v);
 
-    // decay from the end of the job to position T - 1 (read after a barrier)
-    // (eight independent partial sums, so that eight loads are in flight)
+    // decay from the end of the job to position T - 1 (read after a barrier):
+    // 16-byte loads from the first 16-byte boundary on, eight in flight per
+    // thread, the up to three floats before it and the rest after them one by one
     float part = 0.f;
     {
         constexpr int NT = NW * 64;
         const int n = p.T - jb.s1;
         const float* ap = p.a + row0 + jb.s1;
-        float ps[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-        int r = threadIdx.x;
-        for (; r + 7 * NT < n; r += 8 * NT) {
+        const int head = min(n, (int)((16u - (uint32_t)(reinterpret_cast<uintptr_t>(ap) & 15u)) & 15u) / 4);
+        const int n4 = (n - head) >> 2;
+        const float4* ap4 = reinterpret_cast<const float4*>(ap + head);
+        float4 ps[8];
 #pragma unroll
-            for (int j = 0; j < 8; ++j) ps[j] += ap[r + j * NT];
+        for (int j = 0; j < 8; ++j) ps[j] = make_float4(0.f, 0.f, 0.f, 0.f);
+        int r = threadIdx.x;
+        for (; r + 7 * NT < n4; r += 8 * NT) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const float4 x = ap4[r + j * NT];
+                ps[j].x += x.x; ps[j].y += x.y; ps[j].z += x.z; ps[j].w += x.w;
+            }
         }
-        for (; r < n; r += NT) ps[0] += ap[r];
-        part = ((ps[0] + ps[1]) + (ps[2] + ps[3])) + ((ps[4] + ps[5]) + (ps[6] + ps[7]));
+        for (; r < n4; r += NT) {
+            const float4 x = ap4[r];
+            ps[0].x += x.x; ps[0].y += x.y; ps[0].z += x.z; ps[0].w += x.w;
+        }
+        const int rest = n - head - 4 * n4;  // 0..3
+        if ((int)threadIdx.x < head) ps[1].x += ap[threadIdx.x];
+        if ((int)threadIdx.x < rest) ps[2].x += ap[head + 4 * n4 + threadIdx.x];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) part += (ps[j].x + ps[j].y) + (ps[j].z + ps[j].w);
     }
     for (int o = 32; o >= 1; o >>= 1) part += __shfl_xor(part, o);
     if (lane == 0) sred[wave] = part;
 
     const int t0 = jb.s0 / TC, t1 = (jb.s1 - 1) / TC;  // the job's tiles
+    // whole tiles by the forward's copy plan (one scalar base, precomputed
+    // lane offsets), the sequence's partial last tile row by row
+    TileCopy<DK, NW> ck;
+    TileCopy<DVW, NW> cv;
+    ck.init(DK, 0, wave);
+    cv.init(p.dv, cb, wave);
     auto issue = [&](int tile, bf16_t* Kd, bf16_t* Vd, float* ad) __attribute__((always_inline)) {
         const int base = tile * TC;
         const int nvalid = min(TC, p.T - base);
         const size_t r = row0 + base;
-        dma_tile<DK, NW>(kg + r * DK, DK, 0, nvalid, Kd, wave);
-        dma_tile<DVW, NW>(vg + r * p.dv, p.dv, cb, nvalid, Vd, wave);
+        if (nvalid == TC) {
+            ck.issue(kg + r * DK, Kd, wave);
+            cv.issue(vg + r * p.dv, Vd, wave);
+        } else {
+            dma_tile<DK, NW>(kg + r * DK, DK, 0, nvalid, Kd, wave);
+            dma_tile<DVW, NW>(vg + r * p.dv, p.dv, cb, nvalid, Vd, wave);
+        }
         if (wave == 0) {
             if (lane < nvalid) dma4(p.a + r + lane, ad);
             else ad[lane] = 0.f;
