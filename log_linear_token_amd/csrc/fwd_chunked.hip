@@ -161,6 +161,108 @@ struct ScanLoad {
     }
 };
 
+// Decay total of chunk (segment) i, summed as ScanLoad::combine sums it.
+template <int NSUB>
+__device__ __forceinline__ float chunk_total(const FwdParams& p, int bh, int i) {
+    if constexpr (NSUB == 1) {
+        return p.tot[(size_t)bh * p.N + i];
+    } else {
+        const float* t = p.tpart + ((size_t)bh * p.N + i) * NSUB;
+        float after = t[NSUB - 1];
+#pragma unroll
+        for (int s = NSUB - 2; s >= 0; --s) after += t[s];
+        return after;
+    }
+}
+
+// Where node i's four elements e4 go: the fp32 node over ust, the bf16 copies
+// (row order, or the fused kernel's fragment order; see k_fenwick_scan).
+__device__ __forceinline__ size_t node_frag_offset(const FwdParams& p, int e4) {
+    const int e = 4 * e4;
+    const int col = e / p.dk, d0 = e % p.dk;
+    const int cblk = col >> 4, m = col & 15;
+    if (p.dk >= 32) {
+        const int j = d0 >> 5, w32 = d0 & 31, g = w32 >> 3, half = (w32 >> 2) & 1;
+        return (((size_t)cblk * (p.dk / 32) + j) * 64 + 16 * g + m) * 8 + 4 * half;
+    }
+    return ((size_t)cblk * 64 + 16 * (d0 >> 2) + m) * 4;
+}
+__device__ __forceinline__ void store_node(const FwdParams& p, int bh, int e4, int per4, int i,
+                                           const float4& acc) {
+    if (!p.nodes16_only)
+        reinterpret_cast<float4*>(p.ust)[((size_t)bh * p.N + i) * per4 + e4] = acc;
+    bf16x4 h;
+    h[0] = (__bf16)acc.x; h[1] = (__bf16)acc.y; h[2] = (__bf16)acc.z; h[3] = (__bf16)acc.w;
+    if (p.gnode16)
+        *reinterpret_cast<bf16x4*>(p.gnode16 + ((size_t)bh * p.N + i) * per4 * 4 + 4 * e4) = h;
+    if (p.gfrag) {
+        const size_t fstride = (size_t)p.dv * p.dk;
+        *reinterpret_cast<bf16x4*>(reinterpret_cast<bf16_t*>(p.gfrag) + ((size_t)bh * p.N + i) * fstride +
+                                   node_frag_offset(p, e4)) = h;
+    }
+}
+
+// The nodes over chunks formed independently, one thread per (bh, node,
+// 4 state elements): node i is the decayed sum, to the end of chunk i, of
+// the states of the 2^lssb(i + 1) chunks ending at i, here by Horner's rule
+// over them (the scan below reaches the same sums through its running
+// levels).  It reads each state once per node that covers it instead of
+// once, so it serves where the scan's walk, one thread per (bh, 4 elements),
+// would leave most of the GPU idle; and only with sub-range states
+// (NSUB > 1), since the nodes then do not overwrite the states they read.
+template <int NSUB>
+__global__ __launch_bounds__(256) void k_fenwick_nodes(FwdParams p) {
+    static_assert(NSUB > 1, "the nodes would overwrite the chunk states in place");
+    const int per4 = p.dv * p.dk / 4;
+    const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
+    const long per_bh = (long)p.nscan * per4;
+    const int bh = (int)(gid / per_bh);
+    if (bh >= p.BH) return;
+    const long rem = gid - (long)bh * per_bh;
+    const int i = (int)(rem / per4);
+    const int e4 = (int)(rem - (long)i * per4);
+    const int r0 = i + 1 - (1 << lssb((uint64_t)i + 1));
+    const int width = i + 1 - r0;
+    // the node's states, kDepth loads in flight (issued before the totals)
+    constexpr int kDepth = 4;
+    ScanLoad<NSUB> ring[kDepth];
+#pragma unroll
+    for (int d = 0; d < kDepth; ++d)
+        if (d < width) ring[d].issue(p, bh, e4, per4, r0 + d);
+    // decay total up to the end of each chunk, in fp64 as the scan forms it
+    // (the totals before the node loaded eight at a time, summed in order)
+    double c = 0.0;
+    int r = 0;
+    for (; r + 8 <= r0; r += 8) {
+        float t[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) t[u] = chunk_total<NSUB>(p, bh, r + u);
+#pragma unroll
+        for (int u = 0; u < 8; ++u) c += (double)t[u];
+    }
+    for (; r < r0; ++r) c += (double)chunk_total<NSUB>(p, bh, r);
+    float4 acc = make_float4(0.f, 0.f, 0.f, 0.f);
+    for (int k0 = 0; k0 < width; k0 += kDepth) {
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) {
+            const int k = k0 + d;
+            if (k < width) {
+                float total;
+                const float4 st = ring[d].combine(p, bh, r0 + k, &total);
+                if (k + kDepth < width) ring[d].issue(p, bh, e4, per4, r0 + k + kDepth);
+                const float w = k == 0 ? 0.f : __expf(total);  // chunk r0 + k's decay onto the sum
+                acc.x = w * acc.x + st.x;
+                acc.y = w * acc.y + st.y;
+                acc.z = w * acc.z + st.z;
+                acc.w = w * acc.w + st.w;
+                c += (double)total;
+            }
+        }
+    }
+    store_node(p, bh, e4, per4, i, acc);
+    if (e4 == 0) p.cum[(size_t)bh * p.N + i] = c;
+}
+
 template <int NSUB>
 __global__ __launch_bounds__(256) void k_fenwick_scan(FwdParams p) {
     constexpr int DEPTH = NSUB >= 8 ? 1 : kScanDepth / NSUB;  // segments kept in flight
@@ -180,18 +282,8 @@ __global__ __launch_bounds__(256) void k_fenwick_scan(FwdParams p) {
     bf16_t* frag = nullptr;
     size_t fstride = 0;
     if (p.gfrag) {
-        const int e = 4 * e4;
-        const int col = e / p.dk, d0 = e % p.dk;
-        const int cblk = col >> 4, m = col & 15;
-        size_t off;
-        if (p.dk >= 32) {
-            const int j = d0 >> 5, w32 = d0 & 31, g = w32 >> 3, half = (w32 >> 2) & 1;
-            off = (((size_t)cblk * (p.dk / 32) + j) * 64 + 16 * g + m) * 8 + 4 * half;
-        } else {
-            off = ((size_t)cblk * 64 + 16 * (d0 >> 2) + m) * 4;
-        }
         fstride = (size_t)p.dv * p.dk;
-        frag = reinterpret_cast<bf16_t*>(p.gfrag) + (size_t)bh * p.N * fstride + off;
+        frag = reinterpret_cast<bf16_t*>(p.gfrag) + (size_t)bh * p.N * fstride + node_frag_offset(p, e4);
     }
     float4 live[kScanLevels];
     double lcum[kScanLevels];
@@ -435,6 +527,18 @@ hipError_t launch_fenwick_scan(const FwdParams& p, hipStream_t stream) {
     if (p.nscan <= 0) return hipSuccess;
     const long threads = (long)p.BH * (p.dv * p.dk / 4);
     const dim3 grid((unsigned)((threads + 255) / 256));
+    if (p.upart && p.nsub > 1 && p.nscan >= 4 && grid.x < 256) {
+        // the walk would run on fewer blocks than the GPU has compute units:
+        // every node by a thread of its own
+        const dim3 g2((unsigned)((threads * p.nscan + 255) / 256));
+        switch (p.nsub) {
+            case 2: hipLaunchKernelGGL(k_fenwick_nodes<2>, g2, dim3(256), 0, stream, p); break;
+            case 4: hipLaunchKernelGGL(k_fenwick_nodes<4>, g2, dim3(256), 0, stream, p); break;
+            case 8: hipLaunchKernelGGL(k_fenwick_nodes<8>, g2, dim3(256), 0, stream, p); break;
+            default: return hipErrorInvalidValue;
+        }
+        return hipGetLastError();
+    }
     switch (p.upart ? p.nsub : 1) {
         case 1: hipLaunchKernelGGL(k_fenwick_scan<1>, grid, dim3(256), 0, stream, p); break;
         case 2: hipLaunchKernelGGL(k_fenwick_scan<2>, grid, dim3(256), 0, stream, p); break;
