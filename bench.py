@@ -164,8 +164,8 @@ def fwd_models(cfg, plan) -> dict:
             "seg_state": {"bytes": BH * tiles_pre * tile * (2 * (dk + dv) + 4)
                           + BH * (nseg - 1) * nsub * (st + 4),
                           "flops": BH * tiles_pre * tile * 2 * dk * dv},
-            # reads the sub-range states, writes each node in fp32 and bf16
-            "fenwick_scan": {"bytes": BH * (nseg - 1) * (nsub * (st + 4) + st + st // 2 + 8),
+            # reads the sub-range states, writes each node as bf16 fragments
+            "fenwick_scan": {"bytes": BH * (nseg - 1) * (nsub * (st + 4) + st // 2 + 8),
                              "flops": 0},
             "fused_fwd": {"bytes": BH * T * (tok_in + tok_out) + BH * (nseg - 1) * (st + 8),
                           "flops": BH * (ntiles * intra + (states + local_reads + top_reads)

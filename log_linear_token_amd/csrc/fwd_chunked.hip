@@ -208,11 +208,11 @@ __device__ __forceinline__ void store_node(const FwdParams& p, int bh, int e4, i
 // over them (the scan below reaches the same sums through its running
 // levels).  It reads each state once per node that covers it instead of
 // once, so it serves where the scan's walk, one thread per (bh, 4 elements),
-// would leave most of the GPU idle; and only with sub-range states
-// (NSUB > 1), since the nodes then do not overwrite the states they read.
+// would leave most of the GPU idle; and only where no node overwrites a
+// state another thread reads: sub-range states (NSUB > 1), or no fp32 copy
+// of the nodes (nodes16_only).
 template <int NSUB>
 __global__ __launch_bounds__(256) void k_fenwick_nodes(FwdParams p) {
-    static_assert(NSUB > 1, "the nodes would overwrite the chunk states in place");
     const int per4 = p.dv * p.dk / 4;
     const long gid = (long)blockIdx.x * blockDim.x + threadIdx.x;
     const long per_bh = (long)p.nscan * per4;
@@ -527,11 +527,13 @@ hipError_t launch_fenwick_scan(const FwdParams& p, hipStream_t stream) {
     if (p.nscan <= 0) return hipSuccess;
     const long threads = (long)p.BH * (p.dv * p.dk / 4);
     const dim3 grid((unsigned)((threads + 255) / 256));
-    if (p.upart && p.nsub > 1 && p.nscan >= 4 && grid.x < 256) {
+    const int nsub = p.upart ? p.nsub : 1;
+    if ((nsub > 1 || p.nodes16_only) && p.nscan >= 4 && grid.x < 256) {
         // the walk would run on fewer blocks than the GPU has compute units:
         // every node by a thread of its own
         const dim3 g2((unsigned)((threads * p.nscan + 255) / 256));
-        switch (p.nsub) {
+        switch (nsub) {
+            case 1: hipLaunchKernelGGL(k_fenwick_nodes<1>, g2, dim3(256), 0, stream, p); break;
             case 2: hipLaunchKernelGGL(k_fenwick_nodes<2>, g2, dim3(256), 0, stream, p); break;
             case 4: hipLaunchKernelGGL(k_fenwick_nodes<4>, g2, dim3(256), 0, stream, p); break;
             case 8: hipLaunchKernelGGL(k_fenwick_nodes<8>, g2, dim3(256), 0, stream, p); break;

@@ -22,7 +22,8 @@ struct FwdParams {
     double* cum;         // workspace [BH][N]
     bf16_t_storage* gfrag;  // optional bf16 copy of the nodes in MFMA fragment order
     bf16_t_storage* gnode16;  // optional bf16 copy of the nodes in the order of ust
-    bool nodes16_only;        // with gnode16: the fp32 nodes are not written back to ust
+    bool nodes16_only;        // the fp32 nodes are not written back to ust (only the bf16
+                              // copies: gnode16 and / or gfrag)
     const float* upart;  // optional [BH][N][nsub][dv][dk] states of sub-ranges (then tpart)
     const float* tpart;  // [BH][N][nsub] decay totals of the sub-ranges
     int nsub;            // sub-ranges per chunk (1, 2, 4 or 8) when upart is set

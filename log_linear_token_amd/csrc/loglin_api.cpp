@@ -184,6 +184,9 @@ hipError_t launch_fused_path(const FusedPlan& f, const FwdWorkspace& w, char* ba
         p.tot = reinterpret_cast<float*>(base + w.tot_off);
         p.cum = reinterpret_cast<double*>(base + w.cum_off);
     }
+    // the output kernel reads the nodes only as bf16 fragments: the scan
+    // writes no fp32 copy (the segment states stay in place)
+    p.nodes16_only = true;
     FusedParams fp{};
     fp.q = static_cast<const bf16_t_storage*>(q);
     fp.k = static_cast<const bf16_t_storage*>(k);
