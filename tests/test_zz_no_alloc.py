@@ -82,3 +82,32 @@ def test_noalloc_rejects_what_the_forward_rejects():
     with pytest.raises(LL.LoglinError) as ei:
         LL.loglin_fwd_chunked_noalloc(q, q, q, a, lam[..., :3].contiguous(), 16)  # too few levels
     assert ei.value.status == LL.LOGLIN_EINVAL
+
+
+def test_noalloc_forward_replayed_from_a_graph():
+    """The allocation-free forward captured once in a HIP graph
+    (torch.cuda.CUDAGraph) and replayed four times, with an eager forward of
+    other inputs (which reuses the shared scratch array) and host
+    synchronisations between the replays: every replay writes the eager
+    output bit for bit into the captured output tensor."""
+    banner("no-alloc forward replayed from a graph")
+    cfg = I.CONFIGS["fwd8k"].scaled(B=2, H=4)
+    q, k, v, a, lam = _dev_inputs(cfg, "weak", seed=21)
+    ocfg = I.CONFIGS["fwd2k"].scaled(B=1, H=4, T=1000)
+    other = _dev_inputs(ocfg, "base", seed=22)
+    want = LL.loglin_fwd_chunked_noalloc(q, k, v, a, lam, cfg.C)  # also the scratch's set-up
+    other_want = LL.loglin_fwd_chunked_noalloc(*other, ocfg.C)
+    torch.cuda.synchronize()
+    out = torch.full_like(want, float("nan"))
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        LL.loglin_fwd_chunked_noalloc(q, k, v, a, lam, cfg.C, out=out)
+    torch.cuda.synchronize()
+    for r in range(4):
+        out.fill_(float("nan"))
+        got_other = LL.loglin_fwd_chunked_noalloc(*other, ocfg.C)
+        torch.cuda.synchronize()
+        assert torch.equal(got_other, other_want), r
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out, want), (r, float((out - want).abs().nan_to_num(1e30).max()))
