@@ -589,6 +589,11 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
     };
 
     const int lane_k = lane, m16_k = m16, g_k = g;  // the body's lane indices (see there)
+    // dq pass: A at the end of each tile of the segment (fp64), from A before it
+    double run_cum = 0.0;
+    if constexpr (BWD) {
+        if (p.ccum && seg > 0) run_cum = p.scum[(size_t)bh * p.nseg + seg - 1];
+    }
     auto body = [&](int il, const bf16_t* Qc, const bf16_t* Kc, const bf16_t* Vc,
                     const float* Lc, const float* Awc, const float* Ewc, const bf16_t* Qoc,
                     bf16_t* Qn, bf16_t* Kn, bf16_t* Vn, float* Ln, float* an, float* Awn,
@@ -614,6 +619,12 @@ __global__ __launch_bounds__(NW * NH * 64, 1) void k_fused_fwd(FusedParams p) {
         const int i = tile0 + il;
         const int nvalid = min(TC, p.T - i * TC);
         const float tot = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(Awc[TC - 1])));
+        if constexpr (BWD) {
+            if (p.ccum) {
+                run_cum += (double)tot;
+                if (threadIdx.x == 0 && dvb == 0) p.ccum[(size_t)bh * p.ntiles + i] = run_cum;
+            }
+        }
         // dq pass: the issuing waves of Q and K store and copy before their
         // scores, so that their queue stalls overlap the other waves' scores
         // and not the waves 2 and 3 copying V, q, lambda and a after theirs

@@ -72,6 +72,10 @@ struct FusedParams {
     // whole [BH][T][L] rows (levels past LU zero) instead of dlp, and dqd is
     // then q_t . dq_t itself; nullptr otherwise
     float* dlam_rows;
+    // dq pass with 64-token chunks: A at the end of every tile, fp64
+    // ([BH][ntiles]; the segment scan's value before the segment plus the
+    // tiles' totals in order), for the dk / dv stage; nullptr otherwise
+    double* ccum;
 };
 struct FusedPlan {
     int ok, m, nseg, ntop, dvw, ndvb, ntiles, combo, msub;

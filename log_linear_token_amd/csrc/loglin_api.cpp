@@ -163,7 +163,8 @@ hipError_t launch_fused_path(const FusedPlan& f, const FwdWorkspace& w, char* ba
                              const float* lambda, float* out, long BH, int T, int dk, int dv,
                              int L, int C, unsigned stage_mask, hipStream_t hs,
                              const void* qo = nullptr, float* dlp = nullptr,
-                             float* dqd = nullptr, float* dlam_rows = nullptr) {
+                             float* dqd = nullptr, float* dlam_rows = nullptr,
+                             double* ccum = nullptr) {
     FwdParams p{};
     p.q = q;
     p.k = k;
@@ -222,6 +223,7 @@ hipError_t launch_fused_path(const FusedPlan& f, const FwdWorkspace& w, char* ba
     fp.dlp = dlp;
     fp.dqd = dqd;
     fp.dlam_rows = dlam_rows;
+    fp.ccum = ccum;
     if (w.total > 0) {
         p.gfrag = reinterpret_cast<bf16_t_storage*>(base + w.frag_off);
         fp.gfrag = p.gfrag;
@@ -636,9 +638,13 @@ loglin_status loglin_bwd_chunked(const void* q, const void* k, const void* v, co
         // tile writes dlambda rows and q . dq (dA1) itself; else the column
         // blocks' parts are summed and transposed by the dlambda kernel
         const bool rows = w.fq.dvw == 128 && L <= kFusedMaxL;
+        // with 64-token chunks (the pass's tiles) the pass also leaves A at
+        // the end of every chunk for the dk / dv stage
+        double* ccum = reinterpret_cast<double*>(base + w.ccum_off);
+        const bool cum_by_pass = C == 64 && N > 1;
         hipError_t e = launch_fused_path(w.fq, w.nodes, base, dout, v, k, log_decay, lambda, dq, BH, T,
                                          dv, dk, L, C, kStageAll, hs, q, dlp, rows ? bp.dA1 : dqd,
-                                         rows ? dlambda : nullptr);
+                                         rows ? dlambda : nullptr, cum_by_pass ? ccum : nullptr);
         if (e != hipSuccess) return hip_fail(e, "loglin_bwd_chunked dq launch");
         if (!rows) {
             e = launch_bwd_dlam_sum(bp, dlp, dqd, w.fq.ndvb, levels_needed(T), hs);
@@ -646,9 +652,11 @@ loglin_status loglin_bwd_chunked(const void* q, const void* k, const void* v, co
         }
         bp.dq_done = 1;
         if (N > 1) {
-            bp.cum = reinterpret_cast<double*>(base + w.ccum_off);
-            e = launch_bwd_chunk_cum(bp, hs);
-            if (e != hipSuccess) return hip_fail(e, "loglin_bwd_chunked decay prefix launch");
+            bp.cum = ccum;
+            if (!cum_by_pass) {
+                e = launch_bwd_chunk_cum(bp, hs);
+                if (e != hipSuccess) return hip_fail(e, "loglin_bwd_chunked decay prefix launch");
+            }
             bp.rst = reinterpret_cast<float*>(base + w.rst_off);
             bp.rstT = reinterpret_cast<float*>(base + w.rstT_off);
             bp.rst16 = reinterpret_cast<bf16_t_storage*>(base + w.rst_off);
