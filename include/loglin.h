@@ -23,6 +23,19 @@
  *    The text of the last error of the calling thread is loglin_last_error().
  *  - Documented but not checked: lambda >= 0 and log_decay <= 0 (other values
  *    are computed as written, with the overflow that implies).
+ *
+ * Environment variables (read at each call; for tests and profiling, every
+ * setting computes the same result by other kernels):
+ *   LOGLIN_FWD_PATH=chunked       bf16 forward on the chunked path
+ *   LOGLIN_FUSED_SEGMENT=<tiles>  fused path: segments of 1, 2, 4, 8, 16 or 32
+ *                                 64-token tiles (else the planner chooses)
+ *   LOGLIN_FUSED_SPLIT=<n>        fused path: segment states in 1, 2, 4 or 8
+ *                                 sub-ranges (else the planner chooses)
+ *   LOGLIN_BWD_DQ=chunked         backward dq by the chunk-state kernels
+ *   LOGLIN_BWD_DQ=fused64         backward dq pass in 64-column blocks
+ *   LOGLIN_BWD_RSTATE=blocks      backward R(j) states one block each
+ *   LOGLIN_BWD_DKV=chunks         backward dk / dv one block per chunk
+ *   LOGLIN_TEST_FAIL_ALLOC=1      loglin_state_init fails as if out of memory
  */
 #ifndef LOGLIN_H
 #define LOGLIN_H
