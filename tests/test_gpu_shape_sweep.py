@@ -1,9 +1,11 @@
 """Seeded sweep of sequence lengths, batch and head counts, lambda row lengths
 and decay strengths, on the (dtype, chunk size, head dims) combinations the
 other GPU tests name, against the oracle: the forward against the
-materialised mask (Form A), the backward against its chain-rule gradients.
-The cases are drawn once, from a fixed seed, when the module is collected,
-so every run checks the same ones."""
+materialised mask (Form A), the backward against its chain-rule gradients,
+the log-linear Gated DeltaNet forward against its masked form, and the
+prefill hand-over against the recurrence's level states (slots that are not
+live exactly zero).  The cases are drawn once, from fixed seeds, when the
+module is collected, so every run checks the same ones."""
 import numpy as np
 import pytest
 import torch
@@ -11,7 +13,7 @@ import torch
 from log_linear_token_amd import inputs as I
 from log_linear_token_amd import loglin as LL
 from oracle import reference as ref
-from tests.helpers import TOL_BF16, TOL_F32, banner, in_dtype, slice_rel_err, to_dev
+from tests.helpers import TOL_BF16, TOL_F32, banner, in_dtype, slice_rel_err, state_rel_err, to_dev
 
 pytestmark = pytest.mark.gpu
 
@@ -96,3 +98,77 @@ def test_backward_shape_sweep(case):
     print("  " + " ".join(f"{n} {e:.2e}" for n, e in errs.items()), flush=True)
     for n, e in errs.items():
         assert e <= tol, (n, e)
+
+
+# the log-linear Gated DeltaNet forward: (dtype, dk, dv) of its other tests
+GDN_KINDS = [("f32", 64, 64), ("f32", 64, 16), ("f32", 128, 32), ("f32", 128, 64), ("f32", 64, 32),
+             ("bf16", 128, 64), ("bf16", 64, 64), ("bf16", 128, 16), ("bf16", 64, 32)]
+
+
+def _draw_gdn(n, tmax, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dtype, dk, dv = GDN_KINDS[int(rng.integers(len(GDN_KINDS)))]
+        out.append((i, dtype, dk, dv, int(rng.integers(1, tmax + 1)), int(rng.integers(1, 3)),
+                    int(rng.integers(1, 3)), int(rng.integers(0, 3)),
+                    str(rng.choice(["base", "unit", "weak"]))))
+    return out
+
+
+GDN_CASES = _draw_gdn(8, 1800, 20261205)
+
+
+@pytest.mark.parametrize("case", GDN_CASES,
+                         ids=lambda c: f"{c[0]}-{c[1]}-d{c[2]}x{c[3]}-T{c[4]}-B{c[5]}H{c[6]}-L+{c[7]}-{c[8]}")
+def test_gdn_forward_shape_sweep(case):
+    i, dtype, dk, dv, T, B, H, extra, variant = case
+    banner(f"sweep gdn {case}")
+    L = (T - 1).bit_length() + 1 + extra
+    cfg = I.CONFIGS["gdn2k"].scaled(B=B, H=H, T=T, dk=dk, dv=dv, C=64, L=L, dtype=dtype)
+    d = I.make_gdn(cfg, variant, seed=900 + i)
+    dt = in_dtype(dtype)
+    out = LL.loglin_gdn_fwd_chunked(to_dev(d["q"], dt), to_dev(d["k"], dt), to_dev(d["v"], dt),
+                                    to_dev(d["a"]), to_dev(d["beta"]), to_dev(d["lam"]), 64)
+    torch.cuda.synchronize()
+    want = ref.gdn_form_a(d["q"], d["k"], d["v"], d["a"], d["beta"], d["lam"])
+    err = slice_rel_err(out.cpu().numpy(), want, 2)
+    print(f"  out {err:.2e}", flush=True)
+    assert err <= (TOL_BF16 if dtype == "bf16" else TOL_F32), err
+
+
+# the prefill -> decode hand-over: (dtype, dk, dv) of its other tests
+PF_KINDS = [("f32", 16, 16), ("f32", 16, 32), ("f32", 32, 16), ("f32", 64, 64), ("bf16", 64, 64),
+            ("bf16", 128, 64), ("f32", 32, 32), ("bf16", 32, 32), ("bf16", 128, 128)]
+
+
+def _draw_pf(n, tmax, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dtype, dk, dv = PF_KINDS[int(rng.integers(len(PF_KINDS)))]
+        out.append((i, dtype, dk, dv, int(rng.integers(1, tmax + 1)), int(rng.integers(1, 3)),
+                    int(rng.integers(1, 3)), float(rng.choice([-1.0, -8.0]))))
+    return out
+
+
+PF_CASES = _draw_pf(8, 3000, 20261206)
+
+
+@pytest.mark.parametrize("case", PF_CASES,
+                         ids=lambda c: f"{c[0]}-{c[1]}-d{c[2]}x{c[3]}-T{c[4]}-B{c[5]}H{c[6]}-mu{c[7]:g}")
+def test_prefill_shape_sweep(case):
+    i, dtype, dk, dv, T, B, H, mu = case
+    banner(f"sweep prefill {case}")
+    L = (T - 1).bit_length() + 1
+    q, k, v, a, lam, _ = _inputs(B, H, T, dk, dv, L, mu, seed=1100 + i)
+    dt = in_dtype(dtype)
+    got = LL.loglin_prefill_states(to_dev(k, dt), to_dev(v, dt), to_dev(a), L).cpu().numpy()
+    _, want = ref.form_b(q, _round(k, dt), _round(v, dt), a, lam, return_states=True)
+    err = state_rel_err(got.reshape(B * H, L, dk, dv), want.reshape(B * H, L, dk, dv))
+    print(f"  states {err:.2e}", flush=True)
+    assert err <= (TOL_BF16 if dtype == "bf16" else TOL_F32), err
+    live = set(ref.live_slots(T))
+    for lv in range(L):
+        if lv not in live:
+            assert not np.any(got[:, :, lv]), lv
