@@ -2,9 +2,10 @@
 and decay strengths, on the (dtype, chunk size, head dims) combinations the
 other GPU tests name, against the oracle: the forward against the
 materialised mask (Form A), the backward against its chain-rule gradients,
-the log-linear Gated DeltaNet forward against its masked form, and the
-prefill hand-over against the recurrence's level states (slots that are not
-live exactly zero).  The cases are drawn once, from fixed seeds, when the
+the log-linear Gated DeltaNet forward against its masked form, the prefill
+hand-over against the recurrence's level states (slots that are not live
+exactly zero), and decode steps from pre-filled states against the
+recurrence.  The cases are drawn once, from fixed seeds, when the
 module is collected, so every run checks the same ones."""
 import numpy as np
 import pytest
@@ -172,3 +173,49 @@ def test_prefill_shape_sweep(case):
     for lv in range(L):
         if lv not in live:
             assert not np.any(got[:, :, lv]), lv
+
+
+# decode steps from synthetic pre-filled states: (dk, dv) of its other tests
+DEC_KINDS = [(16, 16), (32, 64), (128, 128), (64, 16), (32, 16)]
+
+
+def _draw_dec(n, seed):
+    rng = np.random.default_rng(seed)
+    out = []
+    for i in range(n):
+        dk, dv = DEC_KINDS[int(rng.integers(len(DEC_KINDS)))]
+        nseq, H, Lmax = int(rng.integers(1, 7)), int(rng.integers(1, 4)), int(rng.integers(10, 17))
+        steps, max_prefill = int(rng.integers(20, 131)), int(rng.integers(1, 2000))
+        # every position reached must fit the levels (t < 2^(Lmax - 1))
+        Lmax = max(Lmax, (max_prefill + steps).bit_length() + 1)
+        out.append((i, dk, dv, nseq, H, Lmax, steps, max_prefill, str(rng.choice(["base", "unit"]))))
+    return out
+
+
+DEC_CASES = _draw_dec(6, 20261207)
+
+
+@pytest.mark.parametrize("case", DEC_CASES,
+                         ids=lambda c: f"{c[0]}-d{c[1]}x{c[2]}-n{c[3]}H{c[4]}-L{c[5]}-s{c[6]}-p{c[7]}-{c[8]}")
+def test_decode_shape_sweep(case):
+    """Steps from pre-filled states (prefill lengths up to the drawn bound,
+    steps crossing 64-token window ends): outputs, positions and level
+    states against the oracle recurrence, dead slots empty."""
+    from tests.test_gpu_decode import _decode_gpu, _live_mask_ok, _oracle
+    i, dk, dv, nseq, H, Lmax, steps, max_prefill, variant = case
+    banner(f"sweep decode {case}")
+    cfg = I.CONFIGS["decode"].scaled(nseq=nseq, H=H, dk=dk, dv=dv, Lmax=Lmax, steps=steps,
+                                     max_prefill=max_prefill)
+    d = I.make_decode(cfg, variant, seed=1300 + i, live_slots=ref.live_slots)
+    out, pos, lv = _decode_gpu(d, d["states"])
+    pairs = [(s, h) for s in range(nseq) for h in range(H)]
+    o_ref, st_ref, pos_ref = _oracle(d, d["states"], pairs, steps)
+    got = out.reshape(steps, -1, dv).transpose(1, 0, 2)
+    err = slice_rel_err(got, o_ref.transpose(1, 0, 2), 1)
+    serr = state_rel_err(lv.reshape(-1, Lmax, dk, dv), st_ref)
+    print(f"  out {err:.2e} states {serr:.2e}", flush=True)
+    assert err <= TOL_BF16, err
+    assert np.array_equal(pos, pos_ref.reshape(nseq, H)[:, 0])
+    assert serr <= TOL_BF16, serr
+    ok, where = _live_mask_ok(lv, pos, Lmax)
+    assert ok, where
